@@ -1,0 +1,220 @@
+"""TetraJet-v2 NVFP4 linear layer on AMD MI355X: Python binding of libtj2.
+
+Thin wrappers over the C ABI (include/tj2.h): they take torch tensors that
+live on the GPU, pass their device pointers and the current HIP stream, and
+check the returned status.  Every step of the path runs in the library's HIP
+kernels; there is no Python or CPU implementation here.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI_INIT, OSCI_WINDOW_END, RTN, SR,
+                   Tj2Error, check, lib)
+
+__all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "linear_fwd", "linear_bwd", "linear_bwd_workspace",
+           "osci_reset_step", "channel_sumsq", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
+           "GROUP_ROW", "GROUP_COL", "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END"]
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+class QTensor:
+    """A quantized operand of `rows` x `len` elements grouped along `len` (device storage).
+
+    codes    uint8 [rows, nb*64] (NVFP4) or [rows, nb*128] (FP8), nb = ceil(len/128)
+    scale16  uint8 [rows, nb*8] E4M3 (NVFP4 only)
+    scale128 float32 [rows, nb]
+    """
+
+    def __init__(self, fmt: int, rows: int, length: int, device="cuda"):
+        if length % 16 or length <= 0 or rows <= 0:
+            raise ValueError("len must be a positive multiple of 16 and rows positive")
+        self.fmt, self.rows, self.len = fmt, rows, length
+        nb = (length + 127) // 128
+        self.nb = nb
+        self.codes = torch.empty((rows, nb * (64 if fmt == NVFP4 else 128)), dtype=torch.uint8, device=device)
+        self.scale16 = torch.empty((rows, nb * 8), dtype=torch.uint8, device=device) if fmt == NVFP4 else None
+        self.scale128 = torch.empty((rows, nb), dtype=torch.float32, device=device)
+
+    def c(self) -> _lib.QTensorC:
+        return _lib.QTensorC(self.codes.data_ptr(), 0 if self.scale16 is None else self.scale16.data_ptr(),
+                             self.scale128.data_ptr(), self.rows, self.len, self.fmt, 0)
+
+    # host views of the unpadded content (for tests)
+    def host(self):
+        codes = self.codes.cpu().numpy()
+        if self.fmt == NVFP4:
+            return (codes[:, : self.len // 2], self.scale16.cpu().numpy()[:, : self.len // 16],
+                    self.scale128.cpu().numpy())
+        return codes[:, : self.len], None, self.scale128.cpu().numpy()
+
+
+@dataclass
+class OutlierPlan:
+    outliers: torch.Tensor  # int32 device, ascending
+    rest: torch.Tensor  # int32 device, ascending
+
+    @staticmethod
+    def from_indices(K: int, outliers, device="cuda") -> "OutlierPlan":
+        o = sorted(int(i) for i in outliers)
+        mask = [True] * K
+        for i in o:
+            mask[i] = False
+        rest = [i for i in range(K) if mask[i]]
+        return OutlierPlan(torch.tensor(o, dtype=torch.int32, device=device),
+                           torch.tensor(rest, dtype=torch.int32, device=device))
+
+    @property
+    def n(self) -> int:
+        return int(self.outliers.numel())
+
+    def c(self) -> _lib.PlanC:
+        return _lib.PlanC(self.outliers.data_ptr(), self.rest.data_ptr(), self.n, 0)
+
+
+def rht_signs(seed: int, offset: int) -> int:
+    return int(lib().tj2_rht_signs(seed, offset))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def quantize(x, *, grouping: int = GROUP_ROW, rounding: int = RTN, rht: bool = False, signs: int = 0,
+             seed: int = 0, offset: int = 0, out_fmt: int = NVFP4, col_idx: torch.Tensor | None = None,
+             out: QTensor | None = None) -> QTensor:
+    """Quantize a dense bf16/fp32 tensor [rows, cols] or a QTensor (dequantized first)."""
+    if isinstance(x, QTensor):
+        rows, cols = x.rows, x.len
+        xp, xd, xq = None, x.fmt, ctypes.byref(x.c())
+    else:
+        rows, cols = x.shape
+        xp, xd, xq = x, _dtype_code(x), None
+    n = int(col_idx.numel()) if col_idx is not None else cols
+    if out is None:
+        out = QTensor(out_fmt, rows, n) if grouping == GROUP_ROW else QTensor(out_fmt, cols, rows)
+    oc = out.c()
+    st = lib().nvfp4_quantize(_ptr(xp), xd, xq, rows, cols, _ptr(col_idx), n if col_idx is not None else 0,
+                              grouping, rounding, 1 if rht else 0, signs, seed, offset, ctypes.byref(oc), _stream())
+    check("nvfp4_quantize", st)
+    return out
+
+
+def gemm(A: QTensor, B: QTensor, A2: QTensor | None = None, B2: QTensor | None = None, *,
+         out: torch.Tensor | None = None, out_dtype=torch.float32, col_map: torch.Tensor | None = None,
+         accumulate: bool = False) -> torch.Tensor:
+    """C = A B^T (+ A2 B2^T) on packed operands; C[i, col_map[j]] if col_map is given."""
+    if out is None:
+        out = torch.empty((A.rows, B.rows), dtype=out_dtype, device=A.codes.device)
+    ac, bc = A.c(), B.c()
+    a2 = ctypes.byref(A2.c()) if A2 is not None else None
+    b2 = ctypes.byref(B2.c()) if B2 is not None else None
+    st = lib().nvfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), a2, b2, _ptr(out), _dtype_code(out), out.stride(0),
+                          _ptr(col_map), 1 if accumulate else 0, None, 0, _stream())
+    check("nvfp4_gemm", st)
+    return out
+
+
+def linear_fwd(X: torch.Tensor, W_master: torch.Tensor | None, N: int, *, Wq: QTensor | None = None,
+               W8: QTensor | None = None, plan: OutlierPlan | None = None, y_dtype=torch.bfloat16,
+               Y: torch.Tensor | None = None):
+    """Y = X W^T with NVFP4 operands; returns (Y, saved) with saved = dict(Xq, X8, Wq, W8)."""
+    M, K = X.shape
+    K1 = K - (plan.n if plan else 0)
+    Xq = QTensor(NVFP4, M, K1)
+    X8 = QTensor(FP8, M, plan.n) if plan else None
+    if Wq is None:
+        Wq = QTensor(NVFP4, N, K1)
+    if plan and W8 is None:
+        W8 = QTensor(FP8, N, plan.n)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=y_dtype, device=X.device)
+    pc = plan.c() if plan else None
+    w8c = W8.c() if W8 is not None else None
+    x8c = X8.c() if X8 is not None else None
+    wqc, xqc = Wq.c(), Xq.c()
+    st = lib().nvfp4_linear_fwd(_ptr(X), M, K, N, _ptr(W_master), ctypes.byref(wqc),
+                                ctypes.byref(w8c) if w8c is not None else None,
+                                ctypes.byref(pc) if pc is not None else None, ctypes.byref(xqc),
+                                ctypes.byref(x8c) if x8c is not None else None, _ptr(Y), _dtype_code(Y), _stream())
+    check("nvfp4_linear_fwd", st)
+    return Y, {"Xq": Xq, "X8": X8, "Wq": Wq, "W8": W8}
+
+
+def linear_bwd_workspace(M: int, N: int, K: int, n_outliers: int = 0, device="cuda") -> torch.Tensor:
+    n = int(lib().nvfp4_linear_bwd_workspace_size(M, N, K, n_outliers))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def linear_bwd(dY: torch.Tensor, saved: dict, K: int, *, seed: int, offset: int, rht: bool = True,
+               plan: OutlierPlan | None = None, dx_dtype=torch.bfloat16, keep_operands: bool = False,
+               workspace: torch.Tensor | None = None, dX: torch.Tensor | None = None,
+               dW: torch.Tensor | None = None):
+    """Returns (dX, dW, operands-or-None)."""
+    M, N = dY.shape
+    no = plan.n if plan else 0
+    K1 = K - no
+    if dX is None:
+        dX = torch.empty((M, K), dtype=dx_dtype, device=dY.device)
+    if dW is None:
+        dW = torch.empty((N, K), dtype=torch.float32, device=dY.device)
+    ops = None
+    opsc = None
+    if keep_operands:
+        ops = {"dYq": QTensor(NVFP4, M, N), "dYt": QTensor(NVFP4, N, M), "Wt": QTensor(NVFP4, K1, N),
+               "Xt": QTensor(NVFP4, K1, M)}
+        if plan:
+            ops["W8t"] = QTensor(FP8, no, N)
+            ops["X8t"] = QTensor(FP8, no, M)
+        empty = _lib.QTensorC()
+        opsc = _lib.BwdOperandsC(ops["dYq"].c(), ops["dYt"].c(), ops["Wt"].c(), ops["Xt"].c(),
+                                 ops["W8t"].c() if plan else empty, ops["X8t"].c() if plan else empty)
+    elif workspace is None:
+        workspace = linear_bwd_workspace(M, N, K, no, dY.device)
+    pc = plan.c() if plan else None
+    xqc, wqc = saved["Xq"].c(), saved["Wq"].c()
+    x8c = saved["X8"].c() if saved.get("X8") is not None else None
+    w8c = saved["W8"].c() if saved.get("W8") is not None else None
+    st = lib().nvfp4_linear_bwd(_ptr(dY), M, N, K, ctypes.byref(xqc), ctypes.byref(x8c) if x8c else None,
+                                ctypes.byref(wqc), ctypes.byref(w8c) if w8c else None,
+                                ctypes.byref(pc) if pc else None, 1 if rht else 0, seed, offset, _ptr(dX),
+                                _dtype_code(dX), _ptr(dW), ctypes.byref(opsc) if opsc is not None else None,
+                                _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
+    check("nvfp4_linear_bwd", st)
+    return dX, dW, ops
+
+
+def osci_reset_step(W, W_prev, Q_prev, dQ, dM, *, mode: int, tau: float = 4.0, reset_enabled: bool = False,
+                    Wq_out: QTensor | None = None, reset_count: torch.Tensor | None = None) -> None:
+    N, K = W.shape
+    wqc = Wq_out.c() if Wq_out is not None else None
+    st = lib().osci_reset_step(_ptr(W), _ptr(W_prev), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K, mode,
+                               ctypes.c_float(tau), 1 if reset_enabled else 0,
+                               ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count), _stream())
+    check("osci_reset_step", st)
+
+
+def channel_sumsq(X: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:
+    M, K = X.shape
+    check("tj2_channel_sumsq", lib().tj2_channel_sumsq(_ptr(X), M, K, _ptr(acc), _stream()))
+    return acc
+
+
+def n_outliers(K: int, p: float) -> int:
+    return int(math.ceil(p * K / 16.0)) * 16

@@ -1,0 +1,92 @@
+"""ctypes declarations of libtj2.so (the C ABI in include/tj2.h).
+
+The library is loaded from this package directory only; there is no fallback:
+if it is missing, every call raises.  torch is imported first so the HIP
+runtime it ships is the one the library binds to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime before libtj2)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtj2.so")
+
+TJ2_OK, TJ2_ERR_ARG, TJ2_ERR_SHAPE, TJ2_ERR_ALIGN, TJ2_ERR_HIP, TJ2_ERR_UNSUPPORTED = range(6)
+BF16, F32, NVFP4, FP8 = 0, 1, 2, 3
+GROUP_ROW, GROUP_COL = 0, 1
+RTN, SR = 0, 1
+OSCI_INIT, OSCI_ACCUM, OSCI_WINDOW_END = 0, 1, 2
+
+STATUS_NAMES = {0: "TJ2_OK", 1: "TJ2_ERR_ARG", 2: "TJ2_ERR_SHAPE", 3: "TJ2_ERR_ALIGN", 4: "TJ2_ERR_HIP",
+                5: "TJ2_ERR_UNSUPPORTED"}
+
+
+class QTensorC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scale16", ctypes.c_void_p), ("scale128", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("len", ctypes.c_int64), ("fmt", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class PlanC(ctypes.Structure):
+    _fields_ = [("outliers", ctypes.c_void_p), ("rest", ctypes.c_void_p), ("n_outliers", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class BwdOperandsC(ctypes.Structure):
+    _fields_ = [("dYq", QTensorC), ("dYt", QTensorC), ("Wt", QTensorC), ("Xt", QTensorC), ("W8t", QTensorC),
+                ("X8t", QTensorC)]
+
+
+class Tj2Error(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+I64 = ctypes.c_int64
+U32 = ctypes.c_uint32
+U64 = ctypes.c_uint64
+SZ = ctypes.c_size_t
+QP = ctypes.POINTER(QTensorC)
+
+SIGNATURES = {
+    "tj2_last_error": (ctypes.c_char_p, []),
+    "tj2_version": (ctypes.c_char_p, []),
+    "tj2_qtensor_bytes": (I32, [I32, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+    "tj2_rht_signs": (U32, [U64, U64]),
+    "nvfp4_quantize": (I32, [P, I32, QP, I64, I64, P, I64, I32, I32, I32, U32, U64, U64, QP, P]),
+    "nvfp4_gemm": (I32, [QP, QP, QP, QP, P, I32, I64, P, I32, P, SZ, P]),
+    "nvfp4_gemm_workspace_size": (SZ, [I64, I64, I64]),
+    "nvfp4_linear_fwd": (I32, [P, I64, I64, I64, P, QP, QP, ctypes.POINTER(PlanC), QP, QP, P, I32, P]),
+    "nvfp4_linear_bwd": (I32, [P, I64, I64, I64, QP, QP, QP, QP, ctypes.POINTER(PlanC), I32, U64, U64, P, I32, P,
+                               ctypes.POINTER(BwdOperandsC), P, SZ, P]),
+    "nvfp4_linear_bwd_workspace_size": (SZ, [I64, I64, I64, I32]),
+    "osci_reset_step": (I32, [P, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, QP, P, P]),
+    "tj2_channel_sumsq": (I32, [P, I64, I64, P, P]),
+}
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_fully_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != TJ2_OK:
+        raise Tj2Error(fn, status, lib().tj2_last_error().decode())

@@ -1,0 +1,404 @@
+// C ABI of libtj2 (declared in include/tj2.h): argument validation and the
+// orchestration of the linear layer's forward and backward passes over the
+// quantizer, product and OsciReset kernels.  All device work is enqueued on
+// the caller's stream; no device memory is allocated here.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "tj2_internal.h"
+
+using namespace tj2;
+
+namespace {
+
+thread_local std::string g_err;
+
+tj2_status fail(tj2_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tj2_status fail(tj2_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+tj2_status ok() {
+  g_err.clear();
+  return TJ2_OK;
+}
+
+tj2_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TJ2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return TJ2_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define TJ2_TRY(expr)                 \
+  do {                                \
+    tj2_status st_ = (expr);          \
+    if (st_ != TJ2_OK) return st_;    \
+  } while (0)
+
+tj2_status check_qtensor(const tj2_qtensor* q, const char* name, int fmt, int64_t rows, int64_t len) {
+  if (!q) return fail(TJ2_ERR_ARG, "%s is NULL", name);
+  if (q->fmt != fmt) return fail(TJ2_ERR_ARG, "%s has format %d, expected %d", name, q->fmt, fmt);
+  if (q->rows != rows || q->len != len)
+    return fail(TJ2_ERR_SHAPE, "%s is [%lld, %lld], expected [%lld, %lld]", name, (long long)q->rows,
+                (long long)q->len, (long long)rows, (long long)len);
+  if (len <= 0 || len % 16) return fail(TJ2_ERR_SHAPE, "%s: len %lld is not a positive multiple of 16", name, (long long)len);
+  if (rows <= 0) return fail(TJ2_ERR_SHAPE, "%s: rows must be positive", name);
+  if (!q->codes || !q->scale128 || (fmt == TJ2_NVFP4 && !q->scale16))
+    return fail(TJ2_ERR_ARG, "%s: NULL array", name);
+  if (!aligned16(q->codes) || !aligned16(q->scale128) || (fmt == TJ2_NVFP4 && !aligned16(q->scale16)))
+    return fail(TJ2_ERR_ALIGN, "%s: arrays must be 16-byte aligned", name);
+  return TJ2_OK;
+}
+
+tj2_status check_dims(int64_t v, const char* name) {
+  if (v <= 0 || v % 16) return fail(TJ2_ERR_SHAPE, "%s = %lld must be a positive multiple of 16", name, (long long)v);
+  if (v > (int64_t)1 << 30) return fail(TJ2_ERR_SHAPE, "%s = %lld is too large", name, (long long)v);
+  return TJ2_OK;
+}
+
+size_t qbytes(int fmt, int64_t rows, int64_t len, size_t* c, size_t* s16, size_t* s128) {
+  const int64_t nb = (len + 127) / 128;
+  *c = (size_t)(rows * nb * (fmt == TJ2_FP8 ? 128 : 64));
+  *s16 = fmt == TJ2_FP8 ? 0 : (size_t)(rows * nb * 8);
+  *s128 = (size_t)(rows * nb * 4);
+  return *c + *s16 + *s128;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Carve a tj2_qtensor out of a workspace cursor.
+tj2_qtensor carve(uint8_t*& cur, int fmt, int64_t rows, int64_t len) {
+  size_t c, s16, s128;
+  qbytes(fmt, rows, len, &c, &s16, &s128);
+  tj2_qtensor q;
+  q.codes = cur;
+  cur += align256(c);
+  q.scale16 = s16 ? cur : nullptr;
+  cur += align256(s16);
+  q.scale128 = reinterpret_cast<float*>(cur);
+  cur += align256(s128);
+  q.rows = rows;
+  q.len = len;
+  q.fmt = fmt;
+  q.reserved = 0;
+  return q;
+}
+
+size_t carve_size(int fmt, int64_t rows, int64_t len) {
+  size_t c, s16, s128;
+  qbytes(fmt, rows, len, &c, &s16, &s128);
+  return align256(c) + align256(s16) + align256(s128);
+}
+
+tj2_status run_quant(const void* x, int x_dtype, const tj2_qtensor* x_q, int64_t rows, int64_t cols,
+                     const int32_t* idx, int64_t n_idx, int grouping, int rounding, int rht, uint32_t mask,
+                     uint64_t seed, uint64_t offset, const tj2_qtensor* out, hipStream_t s) {
+  QuantParams p;
+  memset(&p, 0, sizeof(p));
+  p.in_dtype = x_dtype;
+  p.x = x;
+  p.ld_x = cols;
+  if (x_q) p.xq = make_view(*x_q);
+  p.rows = rows;
+  p.cols = cols;
+  p.idx = idx;
+  p.n_idx = n_idx;
+  p.grouping = grouping;
+  p.rounding = rounding;
+  p.rht = rht;
+  p.rht_mask = mask & 0xFFFFu;
+  p.seed = seed;
+  p.offset = offset;
+  p.out = make_view(*out);
+  return hip_check(launch_quant(p, s), "quantize launch");
+}
+
+tj2_status run_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2, const tj2_qtensor* B2,
+                    void* C, int c_dtype, int64_t ldc, const int32_t* col_map, int accumulate, hipStream_t s) {
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.seg[0].a = make_view(*A);
+  p.seg[0].b = make_view(*B);
+  p.seg[0].K = A->len;
+  p.nseg = 1;
+  if (A2 && B2) {
+    p.seg[1].a = make_view(*A2);
+    p.seg[1].b = make_view(*B2);
+    p.seg[1].K = A2->len;
+    p.nseg = 2;
+  }
+  p.I = A->rows;
+  p.J = B->rows;
+  p.C = C;
+  p.c_dtype = c_dtype;
+  p.ldc = ldc;
+  p.col_map = col_map;
+  p.accumulate = accumulate;
+  return hip_check(launch_gemm(p, s), "gemm launch");
+}
+
+uint32_t philox_word0(uint64_t seed, uint64_t offset) {
+  uint32_t c0 = 0xFFFFFFFFu, c1 = 0xFFFFFFFFu, c2 = (uint32_t)offset, c3 = (uint32_t)(offset >> 32);
+  uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  for (int r = 0; r < 10; ++r) {
+    uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+    uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+tj2_status check_plan(const tj2_outlier_plan* plan, int64_t K) {
+  if (!plan) return TJ2_OK;
+  if (!plan->outliers || !plan->rest) return fail(TJ2_ERR_ARG, "plan arrays are NULL");
+  if (!aligned16(plan->outliers) || !aligned16(plan->rest)) return fail(TJ2_ERR_ALIGN, "plan arrays must be 16-byte aligned");
+  if (plan->n_outliers <= 0 || plan->n_outliers % 16 || plan->n_outliers >= K)
+    return fail(TJ2_ERR_SHAPE, "plan n_outliers = %d must be a positive multiple of 16 below K", plan->n_outliers);
+  return TJ2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tj2_last_error(void) { return g_err.c_str(); }
+
+const char* tj2_version(void) { return "tj2 0.1.0 gfx950"; }
+
+tj2_status tj2_qtensor_bytes(int32_t fmt, int64_t rows, int64_t len, size_t* codes_bytes, size_t* scale16_bytes,
+                             size_t* scale128_bytes) {
+  if (fmt != TJ2_NVFP4 && fmt != TJ2_FP8) return fail(TJ2_ERR_ARG, "format must be TJ2_NVFP4 or TJ2_FP8");
+  if (rows <= 0 || len <= 0 || len % 16) return fail(TJ2_ERR_SHAPE, "rows > 0 and len a positive multiple of 16 required");
+  size_t c, s16, s128;
+  qbytes(fmt, rows, len, &c, &s16, &s128);
+  if (codes_bytes) *codes_bytes = c;
+  if (scale16_bytes) *scale16_bytes = s16;
+  if (scale128_bytes) *scale128_bytes = s128;
+  return ok();
+}
+
+uint32_t tj2_rht_signs(uint64_t seed, uint64_t offset) { return philox_word0(seed, offset) & 0xFFFFu; }
+
+tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q, int64_t rows, int64_t cols,
+                          const int32_t* col_idx, int64_t n_idx, int32_t grouping, int32_t rounding, int32_t rht,
+                          uint32_t rht_signs, uint64_t seed, uint64_t offset, tj2_qtensor* out, void* stream) {
+  if (grouping != TJ2_GROUP_ROW && grouping != TJ2_GROUP_COL) return fail(TJ2_ERR_ARG, "bad grouping %d", grouping);
+  if (rounding != TJ2_RTN && rounding != TJ2_SR) return fail(TJ2_ERR_ARG, "bad rounding %d", rounding);
+  if (!out) return fail(TJ2_ERR_ARG, "out is NULL");
+  if (out->fmt != TJ2_NVFP4 && out->fmt != TJ2_FP8) return fail(TJ2_ERR_ARG, "out format must be NVFP4 or FP8");
+  if (rows <= 0 || cols <= 0) return fail(TJ2_ERR_SHAPE, "rows and cols must be positive");
+  if (rows > (int64_t)1 << 30 || cols > (int64_t)1 << 30) return fail(TJ2_ERR_SHAPE, "dimension too large");
+  const bool dense = x_dtype == TJ2_BF16 || x_dtype == TJ2_F32;
+  if (dense) {
+    if (!x) return fail(TJ2_ERR_ARG, "x is NULL");
+    if (!aligned16(x)) return fail(TJ2_ERR_ALIGN, "x must be 16-byte aligned");
+  } else if (x_dtype == TJ2_NVFP4 || x_dtype == TJ2_FP8) {
+    TJ2_TRY(check_qtensor(x_q, "x_q", x_dtype, rows, cols));
+  } else {
+    return fail(TJ2_ERR_ARG, "bad x_dtype %d", x_dtype);
+  }
+  if (col_idx) {
+    if (grouping != TJ2_GROUP_ROW || !dense) return fail(TJ2_ERR_UNSUPPORTED, "col_idx needs row grouping and a dense input");
+    if (!aligned16(col_idx)) return fail(TJ2_ERR_ALIGN, "col_idx must be 16-byte aligned");
+    if (n_idx <= 0 || n_idx % 16 || n_idx > cols) return fail(TJ2_ERR_SHAPE, "n_idx must be a positive multiple of 16 <= cols");
+  }
+  if (grouping == TJ2_GROUP_ROW) {
+    if (!dense) return fail(TJ2_ERR_UNSUPPORTED, "row grouping of a quantized input is not implemented");
+    const int64_t n = col_idx ? n_idx : cols;
+    if (n % 16) return fail(TJ2_ERR_SHAPE, "grouped length %lld is not a multiple of 16", (long long)n);
+    if (cols % 8) return fail(TJ2_ERR_SHAPE, "cols must be a multiple of 8");
+    TJ2_TRY(check_qtensor(out, "out", out->fmt, rows, n));
+    const int64_t nb = (n + 127) / 128;
+    if (rows * nb * 8 >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
+  } else {
+    if (rows % 16 || cols % 16) return fail(TJ2_ERR_SHAPE, "column grouping needs rows and cols multiples of 16");
+    TJ2_TRY(check_qtensor(out, "out", out->fmt, cols, rows));
+  }
+  return run_quant(x, x_dtype, x_q, rows, cols, col_idx, n_idx, grouping, rounding, rht ? 1 : 0, rht_signs, seed,
+                   offset, out, (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
+}
+
+size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K) {
+  (void)I; (void)J; (void)K;
+  return 0;
+}
+
+tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2, const tj2_qtensor* B2,
+                      void* C, int32_t c_dtype, int64_t ldc, const int32_t* col_map, int32_t accumulate,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace; (void)ws_bytes;
+  if (!A || !B) return fail(TJ2_ERR_ARG, "A and B are required");
+  if ((A2 == nullptr) != (B2 == nullptr)) return fail(TJ2_ERR_ARG, "A2 and B2 must be given together");
+  TJ2_TRY(check_qtensor(A, "A", A->fmt, A->rows, A->len));
+  TJ2_TRY(check_qtensor(B, "B", B->fmt, B->rows, A->len));
+  if (A2) {
+    TJ2_TRY(check_qtensor(A2, "A2", A2->fmt, A->rows, A2->len));
+    TJ2_TRY(check_qtensor(B2, "B2", B2->fmt, B->rows, A2->len));
+  }
+  if (!C) return fail(TJ2_ERR_ARG, "C is NULL");
+  if (c_dtype != TJ2_F32 && c_dtype != TJ2_BF16) return fail(TJ2_ERR_ARG, "c_dtype must be TJ2_F32 or TJ2_BF16");
+  if (accumulate && c_dtype != TJ2_F32) return fail(TJ2_ERR_UNSUPPORTED, "accumulate needs an fp32 output");
+  if (!col_map && ldc < B->rows) return fail(TJ2_ERR_SHAPE, "ldc < J");
+  if (ldc <= 0) return fail(TJ2_ERR_SHAPE, "ldc must be positive");
+  if (A->rows > ((int64_t)1 << 24) * 128 || B->rows > ((int64_t)1 << 24) * 128) return fail(TJ2_ERR_SHAPE, "too many rows");
+  return run_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate, (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
+}
+
+tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, const float* W_master, tj2_qtensor* Wq,
+                            tj2_qtensor* W8, const tj2_outlier_plan* plan, tj2_qtensor* Xq, tj2_qtensor* X8, void* Y,
+                            int32_t y_dtype, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  TJ2_TRY(check_dims(M, "M"));
+  TJ2_TRY(check_dims(K, "K"));
+  TJ2_TRY(check_dims(N, "N"));
+  if (!X || !Y) return fail(TJ2_ERR_ARG, "X and Y are required");
+  if (!aligned16(X) || !aligned16(Y) || (W_master && !aligned16(W_master))) return fail(TJ2_ERR_ALIGN, "X, Y, W_master must be 16-byte aligned");
+  if (y_dtype != TJ2_BF16 && y_dtype != TJ2_F32) return fail(TJ2_ERR_ARG, "y_dtype must be TJ2_BF16 or TJ2_F32");
+  TJ2_TRY(check_plan(plan, K));
+  const int64_t no = plan ? plan->n_outliers : 0;
+  const int64_t K1 = K - no;
+  TJ2_TRY(check_qtensor(Xq, "Xq", TJ2_NVFP4, M, K1));
+  TJ2_TRY(check_qtensor(Wq, "Wq", TJ2_NVFP4, N, K1));
+  if (plan) {
+    TJ2_TRY(check_qtensor(X8, "X8", TJ2_FP8, M, no));
+    TJ2_TRY(check_qtensor(W8, "W8", TJ2_FP8, N, no));
+  }
+  const int32_t* rest = plan ? plan->rest : nullptr;
+  TJ2_TRY(run_quant(X, TJ2_BF16, nullptr, M, K, rest, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Xq, s));
+  if (plan) TJ2_TRY(run_quant(X, TJ2_BF16, nullptr, M, K, plan->outliers, no, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, X8, s));
+  if (W_master) {
+    TJ2_TRY(run_quant(W_master, TJ2_F32, nullptr, N, K, rest, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Wq, s));
+    if (plan) TJ2_TRY(run_quant(W_master, TJ2_F32, nullptr, N, K, plan->outliers, no, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, W8, s));
+  }
+  TJ2_TRY(run_gemm(Xq, Wq, plan ? X8 : nullptr, plan ? W8 : nullptr, Y, y_dtype, N, nullptr, 0, s));
+  return ok();
+}
+
+size_t nvfp4_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers) {
+  if (M <= 0 || N <= 0 || K <= 0 || n_outliers < 0 || n_outliers >= K) return 0;
+  const int64_t K1 = K - n_outliers;
+  size_t t = carve_size(TJ2_NVFP4, M, N) + carve_size(TJ2_NVFP4, N, M) + carve_size(TJ2_NVFP4, K1, N) +
+             carve_size(TJ2_NVFP4, K1, M);
+  if (n_outliers) t += carve_size(TJ2_FP8, n_outliers, N) + carve_size(TJ2_FP8, n_outliers, M);
+  return t + 256;
+}
+
+tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, const tj2_qtensor* Xq,
+                            const tj2_qtensor* X8, const tj2_qtensor* Wq, const tj2_qtensor* W8,
+                            const tj2_outlier_plan* plan, int32_t rht, uint64_t seed, uint64_t offset, void* dX,
+                            int32_t dx_dtype, float* dW, tj2_bwd_operands* ops, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  TJ2_TRY(check_dims(M, "M"));
+  TJ2_TRY(check_dims(K, "K"));
+  TJ2_TRY(check_dims(N, "N"));
+  if (!dY || !dX || !dW) return fail(TJ2_ERR_ARG, "dY, dX and dW are required");
+  if (!aligned16(dY) || !aligned16(dX) || !aligned16(dW)) return fail(TJ2_ERR_ALIGN, "dY, dX, dW must be 16-byte aligned");
+  if (dx_dtype != TJ2_BF16 && dx_dtype != TJ2_F32) return fail(TJ2_ERR_ARG, "dx_dtype must be TJ2_BF16 or TJ2_F32");
+  TJ2_TRY(check_plan(plan, K));
+  const int64_t no = plan ? plan->n_outliers : 0;
+  const int64_t K1 = K - no;
+  TJ2_TRY(check_qtensor(Xq, "Xq", TJ2_NVFP4, M, K1));
+  TJ2_TRY(check_qtensor(Wq, "Wq", TJ2_NVFP4, N, K1));
+  if (plan) {
+    TJ2_TRY(check_qtensor(X8, "X8", TJ2_FP8, M, no));
+    TJ2_TRY(check_qtensor(W8, "W8", TJ2_FP8, N, no));
+  }
+  tj2_bwd_operands local;
+  tj2_bwd_operands* o = ops;
+  if (!o) {
+    const size_t need = nvfp4_linear_bwd_workspace_size(M, N, K, (int32_t)no);
+    if (!workspace || ws_bytes < need)
+      return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    uint8_t* cur = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
+    local.dYq = carve(cur, TJ2_NVFP4, M, N);
+    local.dYt = carve(cur, TJ2_NVFP4, N, M);
+    local.Wt = carve(cur, TJ2_NVFP4, K1, N);
+    local.Xt = carve(cur, TJ2_NVFP4, K1, M);
+    if (plan) {
+      local.W8t = carve(cur, TJ2_FP8, no, N);
+      local.X8t = carve(cur, TJ2_FP8, no, M);
+    }
+    o = &local;
+  } else {
+    TJ2_TRY(check_qtensor(&o->dYq, "ops.dYq", TJ2_NVFP4, M, N));
+    TJ2_TRY(check_qtensor(&o->dYt, "ops.dYt", TJ2_NVFP4, N, M));
+    TJ2_TRY(check_qtensor(&o->Wt, "ops.Wt", TJ2_NVFP4, K1, N));
+    TJ2_TRY(check_qtensor(&o->Xt, "ops.Xt", TJ2_NVFP4, K1, M));
+    if (plan) {
+      TJ2_TRY(check_qtensor(&o->W8t, "ops.W8t", TJ2_FP8, no, N));
+      TJ2_TRY(check_qtensor(&o->X8t, "ops.X8t", TJ2_FP8, no, M));
+    }
+  }
+  const int r = rht ? 1 : 0;
+  const uint32_t mdx = r ? tj2_rht_signs(seed, offset + 0) : 0u;
+  const uint32_t mdw = r ? tj2_rht_signs(seed, offset + 2) : 0u;
+  TJ2_TRY(run_quant(dY, TJ2_BF16, nullptr, M, N, nullptr, 0, TJ2_GROUP_ROW, TJ2_SR, r, mdx, seed, offset + 0, &o->dYq, s));
+  TJ2_TRY(run_quant(nullptr, TJ2_NVFP4, Wq, N, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 1, &o->Wt, s));
+  TJ2_TRY(run_quant(dY, TJ2_BF16, nullptr, M, N, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 2, &o->dYt, s));
+  TJ2_TRY(run_quant(nullptr, TJ2_NVFP4, Xq, M, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 3, &o->Xt, s));
+  const int32_t* rest = plan ? plan->rest : nullptr;
+  TJ2_TRY(run_gemm(&o->dYq, &o->Wt, nullptr, nullptr, dX, dx_dtype, K, rest, 0, s));
+  TJ2_TRY(run_gemm(&o->dYt, &o->Xt, nullptr, nullptr, dW, TJ2_F32, K, rest, 0, s));
+  if (plan) {
+    TJ2_TRY(run_quant(nullptr, TJ2_FP8, W8, N, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 4, &o->W8t, s));
+    TJ2_TRY(run_quant(nullptr, TJ2_FP8, X8, M, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 5, &o->X8t, s));
+    TJ2_TRY(run_gemm(&o->dYq, &o->W8t, nullptr, nullptr, dX, dx_dtype, K, plan->outliers, 0, s));
+    TJ2_TRY(run_gemm(&o->dYt, &o->X8t, nullptr, nullptr, dW, TJ2_F32, K, plan->outliers, 0, s));
+  }
+  return ok();
+}
+
+tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N, int64_t K,
+                           int32_t mode, float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
+                           void* stream) {
+  if (!W || !W_prev || !Q_prev || !dQ || !dM) return fail(TJ2_ERR_ARG, "W and the state arrays are required");
+  if (!aligned16(W) || !aligned16(W_prev) || !aligned16(Q_prev) || !aligned16(dQ) || !aligned16(dM))
+    return fail(TJ2_ERR_ALIGN, "arrays must be 16-byte aligned");
+  if (N <= 0 || N > ((int64_t)1 << 30)) return fail(TJ2_ERR_SHAPE, "N must be positive");
+  TJ2_TRY(check_dims(K, "K"));
+  if (mode != TJ2_OSCI_INIT && mode != TJ2_OSCI_ACCUM && mode != TJ2_OSCI_WINDOW_END) return fail(TJ2_ERR_ARG, "bad mode %d", mode);
+  if (!(tau >= 0.0f)) return fail(TJ2_ERR_ARG, "tau must be >= 0");
+  const int64_t nb = (K + 127) / 128;
+  if (N * nb * 8 >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
+  OsciParams p;
+  memset(&p, 0, sizeof(p));
+  p.W = W; p.W_prev = W_prev; p.Q_prev = Q_prev; p.dQ = dQ; p.dM = dM;
+  p.N = N; p.K = K; p.mode = mode; p.tau = tau; p.reset_enabled = reset_enabled ? 1 : 0;
+  if (Wq_out) {
+    TJ2_TRY(check_qtensor(Wq_out, "Wq_out", TJ2_NVFP4, N, K));
+    p.wq = make_view(*Wq_out);
+    p.have_wq = 1;
+  }
+  p.reset_count = reinterpret_cast<unsigned long long*>(reset_count);
+  TJ2_TRY(hip_check(launch_osci(p, (hipStream_t)stream), "osci launch"));
+  return ok();
+}
+
+tj2_status tj2_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, void* stream) {
+  if (!X || !acc) return fail(TJ2_ERR_ARG, "X and acc are required");
+  if (!aligned16(X)) return fail(TJ2_ERR_ALIGN, "X must be 16-byte aligned");
+  if (M <= 0) return fail(TJ2_ERR_SHAPE, "M must be positive");
+  TJ2_TRY(check_dims(K, "K"));
+  TJ2_TRY(hip_check(launch_channel_sumsq(X, M, K, acc, (hipStream_t)stream), "sumsq launch"));
+  return ok();
+}
+
+}  // extern "C"

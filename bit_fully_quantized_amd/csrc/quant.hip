@@ -1,0 +1,370 @@
+// Double-block NVFP4 / per-128 FP8 quantizers for gfx950.
+//
+// TetraJet-v2 technical summary, section 2.A (double-block quantization:
+// 128-element outer blocks with an FP32 scale over 16-element inner blocks with
+// an 8-bit scale; round-to-nearest forward, stochastic rounding backward; 1x16
+// weight groups whose transpose is re-grouped) and section 2.C (Hadamard
+// transform on the backward operands; FP8 outlier channels).
+//
+// Two kernels, both HBM-bound streaming passes with no global reduction:
+//  * quant_row: groups along the contiguous dimension.  One lane owns one
+//    16-element group; the 8 lanes of an outer block reduce its amax with DPP.
+//  * quant_col: groups along rows, output stored transposed.  One lane owns a
+//    16-row x 8-column patch (8 groups, one per column); the 8 lanes stacked
+//    along rows form a 128-row outer block.  A row of the patch is one 16-byte
+//    (bf16) load, so lanes with neighbouring column patches read contiguous
+//    128-byte segments; the Philox block of 8 consecutive input elements of a
+//    row is used whole by one lane.
+#include "tj2_device.h"
+#include "tj2_internal.h"
+
+namespace tj2 {
+
+namespace {
+
+// ----------------------------------------------------------------------------
+// loading helpers
+// ----------------------------------------------------------------------------
+template <int IN>
+struct Dense;
+
+template <>
+struct Dense<TJ2_BF16> {
+  using T = uint16_t;
+  // 16 consecutive elements
+  static __device__ __forceinline__ void load16(const T* p, float v[16]) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    uint4 a = q[0], b = q[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ float load1(const T* p) { return __uint_as_float((uint32_t)(*p) << 16); }
+};
+
+template <>
+struct Dense<TJ2_F32> {
+  using T = float;
+  static __device__ __forceinline__ void load16(const T* p, float v[16]) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4 a = q[i];
+      v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+    }
+  }
+  static __device__ __forceinline__ float load1(const T* p) { return *p; }
+};
+
+__device__ __forceinline__ float e2m1_value(uint32_t n) {
+  // magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} from the bit fields
+  uint32_t e = (n >> 1) & 3u, m = n & 1u;
+  float mag = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
+  return (n & 8u) ? -mag : mag;
+}
+
+// ----------------------------------------------------------------------------
+// Per-group quantization of 16 values v (already transformed if RHT), given
+// the outer amax a_o.  Writes 8 bytes (NVFP4) or 16 bytes (FP8) of codes.
+// ----------------------------------------------------------------------------
+template <bool FP8OUT, bool SR>
+__device__ __forceinline__ void quantize_group(const float v[16], float a_o, float a_j, const uint32_t u[16],
+                                               uint32_t codes[4], uint32_t* s_code, float* S_out) {
+  if (!FP8OUT) {
+    GroupScale g = nvfp4_group_scale(a_o, a_j);
+    *s_code = g.s_code;
+    *S_out = g.S;
+    codes[0] = codes[1] = 0u;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float y = nvfp4_scaled(v[t], g.inv);
+      uint32_t c = SR ? e2m1_sr(y, u[t]) : e2m1_rtn(y);
+      codes[t >> 3] |= c << (4 * (t & 7));
+    }
+  } else {
+    float S = 0.0f, inv = 0.0f;
+    if (a_o >= kTiny) {
+      S = a_o / kFp8Div;
+      inv = 1.0f / S;
+    }
+    *s_code = 0u;
+    *S_out = S;
+    codes[0] = codes[1] = codes[2] = codes[3] = 0u;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float y = fp8_scaled(v[t], inv);
+      uint32_t c = SR ? e4m3_sr(y, u[t]) : e4m3_rne(y);
+      codes[t >> 2] |= c << (8 * (t & 3));
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Row grouping: one lane per 16-element group.
+// ----------------------------------------------------------------------------
+template <int IN, bool GATHER, bool FP8OUT, bool SR, bool RHT>
+__global__ __launch_bounds__(256) void quant_row_kernel(const typename Dense<IN>::T* __restrict__ x,
+                                                        int64_t ld_x, const int32_t* __restrict__ idx,
+                                                        int32_t rows, int32_t L, int32_t groups_per_row,
+                                                        QView out, uint32_t rht_mask, uint64_t seed,
+                                                        uint64_t offset) {
+  const uint32_t g = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t row = g / (uint32_t)groups_per_row;
+  if (row >= (uint32_t)rows) return;  // groups_per_row is a multiple of 8: whole outer blocks exit
+  const uint32_t j = g - row * (uint32_t)groups_per_row;
+  const bool valid = (int32_t)(j * 16u) < L;
+
+  float v[16];
+  if (valid) {
+    const typename Dense<IN>::T* xr = x + (int64_t)row * ld_x;
+    if (GATHER) {
+      const int4* ip = reinterpret_cast<const int4*>(idx + j * 16u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int4 c = ip[q];
+        v[4 * q + 0] = Dense<IN>::load1(xr + c.x);
+        v[4 * q + 1] = Dense<IN>::load1(xr + c.y);
+        v[4 * q + 2] = Dense<IN>::load1(xr + c.z);
+        v[4 * q + 3] = Dense<IN>::load1(xr + c.w);
+      }
+    } else {
+      Dense<IN>::load16(xr + j * 16u, v);
+    }
+    if (RHT) rht16(v, rht_mask);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) v[t] = 0.0f;
+  }
+
+  float a_j = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
+  const float a_o = max8_lanes(a_j);
+
+  uint32_t u[16];
+  if (SR && valid) {
+    const uint64_t e0 = (uint64_t)row * (uint64_t)L + j * 16u;
+    draws8(e0 >> 3, seed, offset, u);
+    draws8((e0 >> 3) + 1, seed, offset, u + 8);
+  }
+  uint32_t codes[4], s_code;
+  float S;
+  quantize_group<FP8OUT, SR>(v, a_o, a_j, u, codes, &s_code, &S);
+
+  if (!FP8OUT) {
+    *reinterpret_cast<uint2*>(out.codes + (int64_t)row * out.ld_codes + j * 8u) = make_uint2(codes[0], codes[1]);
+    out.s16[(int64_t)row * out.ld_s16 + j] = (uint8_t)s_code;
+  } else {
+    *reinterpret_cast<uint4*>(out.codes + (int64_t)row * out.ld_codes + j * 16u) =
+        make_uint4(codes[0], codes[1], codes[2], codes[3]);
+  }
+  if ((j & 7u) == 0u) out.s128[(int64_t)row * out.ld_s128 + (j >> 3)] = S;
+}
+
+// ----------------------------------------------------------------------------
+// Column grouping (16x1), output transposed.  Lane (cg, rs) of a wave owns
+// columns c0..c0+7 and rows r0..r0+15 of the input; lanes rs = 0..7 of one cg
+// are consecutive, so the 128-row outer amax is an 8-lane DPP reduction.
+// ----------------------------------------------------------------------------
+template <int IN>
+struct ColPatch;
+
+template <>
+struct ColPatch<TJ2_BF16> {
+  uint32_t w[16][4];
+  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
+    const uint16_t* x = reinterpret_cast<const uint16_t*>(p.x);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      uint4 a = *reinterpret_cast<const uint4*>(x + (r0 + t) * p.ld_x + c0);
+      w[t][0] = a.x; w[t][1] = a.y; w[t][2] = a.z; w[t][3] = a.w;
+    }
+  }
+  __device__ __forceinline__ float get(int t, int k) const {
+    uint32_t x = w[t][k >> 1];
+    return __uint_as_float((k & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  }
+};
+
+template <>
+struct ColPatch<TJ2_F32> {
+  float w[16][8];
+  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
+    const float* x = reinterpret_cast<const float*>(p.x);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float4 a = *reinterpret_cast<const float4*>(x + (r0 + t) * p.ld_x + c0);
+      float4 b = *reinterpret_cast<const float4*>(x + (r0 + t) * p.ld_x + c0 + 4);
+      w[t][0] = a.x; w[t][1] = a.y; w[t][2] = a.z; w[t][3] = a.w;
+      w[t][4] = b.x; w[t][5] = b.y; w[t][6] = b.z; w[t][7] = b.w;
+    }
+  }
+  __device__ __forceinline__ float get(int t, int k) const { return w[t][k]; }
+};
+
+// NVFP4 input: dequantized value (q * s) * S in fp32 (the forward's X-hat / W-hat).
+template <>
+struct ColPatch<TJ2_NVFP4> {
+  uint32_t codes[16];
+  float qs_scale[16];  // s (E4M3 inner scale of the 16-group holding the 8 columns)
+  float S[16];
+  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
+    const QView& q = p.xq;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int64_t r = r0 + t;
+      codes[t] = *reinterpret_cast<const uint32_t*>(q.codes + r * q.ld_codes + (c0 >> 1));
+      qs_scale[t] = e4m3_decode(q.s16[r * q.ld_s16 + (c0 >> 4)]);
+      S[t] = q.s128[r * q.ld_s128 + (c0 >> 7)];
+    }
+  }
+  __device__ __forceinline__ float get(int t, int k) const {
+    float qv = e2m1_value((codes[t] >> (4 * k)) & 15u);
+    return (qv * qs_scale[t]) * S[t];
+  }
+};
+
+template <>
+struct ColPatch<TJ2_FP8> {
+  uint32_t codes[16][2];
+  float S[16];
+  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
+    const QView& q = p.xq;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int64_t r = r0 + t;
+      uint2 a = *reinterpret_cast<const uint2*>(q.codes + r * q.ld_codes + c0);
+      codes[t][0] = a.x; codes[t][1] = a.y;
+      S[t] = q.s128[r * q.ld_s128 + (c0 >> 7)];
+    }
+  }
+  __device__ __forceinline__ float get(int t, int k) const {
+    return e4m3_decode((codes[t][k >> 2] >> (8 * (k & 3))) & 0xFFu) * S[t];
+  }
+};
+
+template <int IN, bool FP8OUT, bool SR, bool RHT>
+__global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int cg = lane >> 3, rs = lane & 7;
+  const int64_t c0 = ((int64_t)blockIdx.x * 4 + wave) * 64 + cg * 8;
+  if (c0 >= p.cols) return;  // all 8 lanes of this column patch exit together
+  const int64_t r0 = (int64_t)blockIdx.y * 128 + rs * 16;
+  const bool valid = r0 < p.rows;
+  const int64_t R = p.rows, C = p.cols;
+
+  ColPatch<IN> patch;
+  if (valid) patch.load(p, r0, c0);
+
+  uint32_t words[16][4];
+  if (SR && valid) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint64_t b = ((uint64_t)(r0 + t) * (uint64_t)C + (uint64_t)c0) >> 3;
+      u32x4 w = philox10((uint32_t)b, (uint32_t)(b >> 32), (uint32_t)p.offset, (uint32_t)(p.offset >> 32),
+                         (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+      words[t][0] = w.x; words[t][1] = w.y; words[t][2] = w.z; words[t][3] = w.w;
+    }
+  }
+
+  const QView& o = p.out;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float v[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) v[t] = valid ? patch.get(t, k) : 0.0f;
+    if (RHT && valid) rht16(v, p.rht_mask);
+    float a_j = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
+    const float a_o = max8_lanes(a_j);
+    uint32_t u[16];
+    if (SR && valid) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) u[t] = (words[t][k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+    }
+    uint32_t codes[4], s_code;
+    float S;
+    quantize_group<FP8OUT, SR>(v, a_o, a_j, u, codes, &s_code, &S);
+    const int64_t orow = c0 + k;
+    if (!FP8OUT) {
+      *reinterpret_cast<uint2*>(o.codes + orow * o.ld_codes + (r0 >> 1)) = make_uint2(codes[0], codes[1]);
+      o.s16[orow * o.ld_s16 + (r0 >> 4)] = (uint8_t)s_code;
+    } else {
+      *reinterpret_cast<uint4*>(o.codes + orow * o.ld_codes + r0) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+    }
+    if (rs == 0) o.s128[orow * o.ld_s128 + blockIdx.y] = S;
+  }
+  (void)R;
+}
+
+template <int IN, bool GATHER, bool FP8OUT, bool SR, bool RHT>
+hipError_t run_row(const QuantParams& p, hipStream_t s) {
+  const int64_t L = p.out.len;
+  const int64_t gpr = p.out.nb * 8;
+  const int64_t threads = p.rows * gpr;
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL((quant_row_kernel<IN, GATHER, FP8OUT, SR, RHT>), dim3((uint32_t)blocks), dim3(256), 0, s,
+                     reinterpret_cast<const typename Dense<IN>::T*>(p.x), p.ld_x, p.idx, (int32_t)p.rows,
+                     (int32_t)L, (int32_t)gpr, p.out, p.rht_mask, p.seed, p.offset);
+  return hipGetLastError();
+}
+
+template <int IN, bool FP8OUT, bool SR, bool RHT>
+hipError_t run_col(const QuantParams& p, hipStream_t s) {
+  const int64_t nbR = (p.rows + 127) / 128;
+  dim3 grid((uint32_t)((p.cols + 255) / 256), (uint32_t)nbR);
+  hipLaunchKernelGGL((quant_col_kernel<IN, FP8OUT, SR, RHT>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int IN, bool GATHER, bool FP8OUT>
+hipError_t dispatch_row_rs(const QuantParams& p, hipStream_t s) {
+  const bool sr = p.rounding == TJ2_SR, rht = p.rht != 0;
+  if (sr) return rht ? run_row<IN, GATHER, FP8OUT, true, true>(p, s) : run_row<IN, GATHER, FP8OUT, true, false>(p, s);
+  return rht ? run_row<IN, GATHER, FP8OUT, false, true>(p, s) : run_row<IN, GATHER, FP8OUT, false, false>(p, s);
+}
+
+template <int IN, bool FP8OUT>
+hipError_t dispatch_col_rs(const QuantParams& p, hipStream_t s) {
+  const bool sr = p.rounding == TJ2_SR, rht = p.rht != 0;
+  if (sr) return rht ? run_col<IN, FP8OUT, true, true>(p, s) : run_col<IN, FP8OUT, true, false>(p, s);
+  return rht ? run_col<IN, FP8OUT, false, true>(p, s) : run_col<IN, FP8OUT, false, false>(p, s);
+}
+
+template <int IN>
+hipError_t dispatch_row(const QuantParams& p, hipStream_t s) {
+  const bool fp8 = p.out.fmt == TJ2_FP8;
+  if (p.idx) return fp8 ? dispatch_row_rs<IN, true, true>(p, s) : dispatch_row_rs<IN, true, false>(p, s);
+  return fp8 ? dispatch_row_rs<IN, false, true>(p, s) : dispatch_row_rs<IN, false, false>(p, s);
+}
+
+template <int IN>
+hipError_t dispatch_col(const QuantParams& p, hipStream_t s) {
+  return p.out.fmt == TJ2_FP8 ? dispatch_col_rs<IN, true>(p, s) : dispatch_col_rs<IN, false>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_quant(const QuantParams& p, hipStream_t s) {
+  if (p.grouping == TJ2_GROUP_ROW) {
+    switch (p.in_dtype) {
+      case TJ2_BF16: return dispatch_row<TJ2_BF16>(p, s);
+      case TJ2_F32: return dispatch_row<TJ2_F32>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (p.in_dtype) {
+    case TJ2_BF16: return dispatch_col<TJ2_BF16>(p, s);
+    case TJ2_F32: return dispatch_col<TJ2_F32>(p, s);
+    case TJ2_NVFP4: return dispatch_col<TJ2_NVFP4>(p, s);
+    case TJ2_FP8: return dispatch_col<TJ2_FP8>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tj2

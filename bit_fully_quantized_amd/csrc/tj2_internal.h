@@ -1,0 +1,85 @@
+// Host-side declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tj2.h"
+
+namespace tj2 {
+
+// Padded storage of a quantized operand: every row holds whole 128-element
+// outer blocks (nb = ceil(len/128)); the padding is written as zeros.
+struct QView {
+  uint8_t* codes;
+  uint8_t* s16;
+  float* s128;
+  int64_t rows, len, nb;
+  int64_t ld_codes, ld_s16, ld_s128;  // row strides in bytes, bytes, floats
+  int fmt;
+};
+
+inline QView make_view(const tj2_qtensor& q) {
+  QView v;
+  v.codes = q.codes;
+  v.s16 = q.scale16;
+  v.s128 = q.scale128;
+  v.rows = q.rows;
+  v.len = q.len;
+  v.nb = (q.len + 127) / 128;
+  v.fmt = q.fmt;
+  v.ld_codes = q.fmt == TJ2_FP8 ? v.nb * 128 : v.nb * 64;
+  v.ld_s16 = v.nb * 8;
+  v.ld_s128 = v.nb;
+  return v;
+}
+
+struct QuantParams {
+  int in_dtype;          // TJ2_BF16, TJ2_F32, TJ2_NVFP4, TJ2_FP8
+  const void* x;         // dense input (BF16/F32), row-major [rows, ld_x]
+  int64_t ld_x;
+  QView xq;              // quantized input (NVFP4/FP8)
+  int64_t rows, cols;    // logical input shape
+  const int32_t* idx;    // optional column gather (row grouping)
+  int64_t n_idx;
+  int grouping, rounding, rht;
+  uint32_t rht_mask;
+  uint64_t seed, offset;
+  QView out;
+};
+
+hipError_t launch_quant(const QuantParams& p, hipStream_t s);
+
+struct GemmSeg {
+  QView a, b;  // a: [I, K], b: [J, K] grouped along K
+  int64_t K;
+};
+
+struct GemmParams {
+  GemmSeg seg[2];
+  int nseg;
+  int64_t I, J;
+  void* C;
+  int c_dtype;       // TJ2_F32 or TJ2_BF16
+  int64_t ldc;
+  const int32_t* col_map;
+  int accumulate;
+};
+
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+
+struct OsciParams {
+  float *W, *W_prev, *Q_prev, *dQ, *dM;
+  int64_t N, K;
+  int mode;
+  float tau;
+  int reset_enabled;
+  QView wq;          // codes.rows==0 -> no codes output
+  int have_wq;
+  unsigned long long* reset_count;
+};
+
+hipError_t launch_osci(const OsciParams& p, hipStream_t s);
+
+hipError_t launch_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, hipStream_t s);
+
+}  // namespace tj2

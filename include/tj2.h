@@ -1,0 +1,247 @@
+/*
+ * tj2.h -- C ABI of libtj2: the TetraJet-v2 NVFP4 double-block quantized linear
+ * layer, OsciReset and OutControl outlier channels on AMD Instinct MI355X (gfx950).
+ *
+ * Method source: "TetraJet-v2: Accurate NVFP4 Training for Large Language Models
+ * with Oscillation Suppression and Outlier Control" as summarised on the
+ * gist.science technical-summary pages (sections cited per entry point below).
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates device memory.  Host-side descriptors (tj2_qtensor, tj2_outlier_plan)
+ *    are read during the call only.
+ *  - Dense tensors are row-major and contiguous.  bf16 is passed as raw 16-bit
+ *    words.  Device pointers must be 16-byte aligned.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as void*;
+ *    NULL = the default stream).  Calls return once the work is enqueued.
+ *  - Return value: TJ2_OK, or an error code with a message in tj2_last_error()
+ *    (thread-local).  Argument checks happen before any launch, so an error
+ *    other than TJ2_ERR_HIP means nothing was enqueued.
+ *  - Data-dependent conditions (NaN/Inf inputs) are not checked; results for
+ *    them are unspecified.
+ *  - Calls that share output buffers must be ordered by the caller (streams).
+ */
+#ifndef TJ2_H_
+#define TJ2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tj2_status;
+#define TJ2_OK 0
+#define TJ2_ERR_ARG 1         /* null pointer, bad enum, out-of-range value     */
+#define TJ2_ERR_SHAPE 2       /* dimension not a multiple of 16, mismatch        */
+#define TJ2_ERR_ALIGN 3       /* device pointer not 16-byte aligned              */
+#define TJ2_ERR_HIP 4         /* launch or runtime error reported by HIP         */
+#define TJ2_ERR_UNSUPPORTED 5 /* valid but unimplemented combination             */
+
+/* element / storage types */
+#define TJ2_BF16 0
+#define TJ2_F32 1
+#define TJ2_NVFP4 2
+#define TJ2_FP8 3
+
+/* grouping of a quantizer */
+#define TJ2_GROUP_ROW 0 /* 1x16 groups along the contiguous (column) dimension   */
+#define TJ2_GROUP_COL 1 /* 16x1 groups along rows; the output is stored transposed */
+
+/* element rounding */
+#define TJ2_RTN 0 /* round to nearest, ties to even (forward pass)            */
+#define TJ2_SR 1  /* stochastic rounding with Philox4x32-10 draws (backward)  */
+
+/* OsciReset modes */
+#define TJ2_OSCI_INIT 0
+#define TJ2_OSCI_ACCUM 1
+#define TJ2_OSCI_WINDOW_END 2
+
+/*
+ * A quantized operand with `rows` rows of `len` elements, grouped along `len`
+ * (TetraJet-v2 technical summary, section 2.A: 16-element inner blocks with an
+ * 8-bit scale, 128-element outer blocks with an FP32 scale).
+ *
+ * Storage, with nb = ceil(len / 128):
+ *   TJ2_NVFP4: codes    uint8 [rows][nb*64]  E2M1, element 2i in the low nibble of byte i
+ *              scale16  uint8 [rows][nb*8]   E4M3FN, one per 16 elements
+ *              scale128 float [rows][nb]     one per 128 elements
+ *   TJ2_FP8:   codes    uint8 [rows][nb*128] E4M3FN
+ *              scale16  unused (may be NULL)
+ *              scale128 float [rows][nb]
+ * Element positions beyond `len` in each row are padding; producers write
+ * them as zero.  `len` must be a positive multiple of 16.
+ * E2M1 code: bit 3 sign, bits 2..0 index into {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ */
+typedef struct {
+  uint8_t* codes;
+  uint8_t* scale16;
+  float* scale128;
+  int64_t rows;
+  int64_t len;
+  int32_t fmt;
+  int32_t reserved;
+} tj2_qtensor;
+
+/*
+ * Static outlier channels (OutControl; technical summary, section 2.C): the
+ * input channels kept in FP8 and the complement kept in NVFP4.  Both are
+ * DEVICE int32 arrays in ascending order that together list every channel
+ * 0..K-1 once.  n_outliers must be a positive multiple of 16.
+ */
+typedef struct {
+  const int32_t* outliers;
+  const int32_t* rest;
+  int32_t n_outliers;
+  int32_t reserved;
+} tj2_outlier_plan;
+
+/* Buffers for the backward operands (optional argument of nvfp4_linear_bwd). */
+typedef struct {
+  tj2_qtensor dYq;  /* [M, N] NVFP4, groups along N (RHT_N, SR)       */
+  tj2_qtensor dYt;  /* [N, M] NVFP4, groups along M (RHT_M, SR)       */
+  tj2_qtensor Wt;   /* [K1, N] NVFP4, re-grouped dequantized weights  */
+  tj2_qtensor Xt;   /* [K1, M] NVFP4, re-grouped dequantized inputs   */
+  tj2_qtensor W8t;  /* [n_outliers, N] FP8 (plan only)                */
+  tj2_qtensor X8t;  /* [n_outliers, M] FP8 (plan only)                */
+} tj2_bwd_operands;
+
+/* Message describing the last error of the calling thread ("" if none). */
+const char* tj2_last_error(void);
+
+/* Library version string. */
+const char* tj2_version(void);
+
+/*
+ * Bytes needed by each array of a tj2_qtensor of the given format and shape
+ * (see the storage table above).  Host-only; returns TJ2_ERR_ARG / _SHAPE for
+ * a bad format or a len that is not a positive multiple of 16.
+ */
+tj2_status tj2_qtensor_bytes(int32_t fmt, int64_t rows, int64_t len, size_t* codes_bytes,
+                             size_t* scale16_bytes, size_t* scale128_bytes);
+
+/*
+ * 16-bit sign mask of the random Hadamard transform for one product (bit j set
+ * = position j of every 16-chunk is negated).  Host function, no device work:
+ * low 16 bits of word 0 of Philox4x32-10 with key (lo seed, hi seed) and counter
+ * (0xFFFFFFFF, 0xFFFFFFFF, lo offset, hi offset).  (Section 2.C: RHT on dX, dW.)
+ */
+uint32_t tj2_rht_signs(uint64_t seed, uint64_t offset);
+
+/*
+ * Double-block quantizer (section 2.A; FP8 output for the OutControl channels,
+ * section 2.C).
+ *
+ * Input: a logical [rows, cols] tensor, either dense (x_dtype TJ2_BF16 / TJ2_F32,
+ * `x` points to rows*cols elements, x_q ignored) or quantized (x_dtype TJ2_NVFP4
+ * / TJ2_FP8, `x` ignored, *x_q describes rows x cols grouped along cols), in
+ * which case it is dequantized first ((q*s)*S, or e*S8, in fp32).
+ *
+ * col_idx (optional, device int32[n_idx], TJ2_GROUP_ROW with dense input only):
+ * quantize the gathered columns x[:, col_idx] instead of all columns.
+ *
+ * grouping TJ2_GROUP_ROW: groups along cols; *out is [rows, n] with n = n_idx or cols.
+ * grouping TJ2_GROUP_COL: groups along rows (16x1); *out is [cols, rows] (transposed).
+ * The grouped length must be a multiple of 16; for TJ2_GROUP_COL, cols too.
+ *
+ * rht != 0: apply the 16-wide Hadamard transform with sign mask rht_signs along
+ * the grouping dimension before quantizing.
+ * rounding TJ2_SR: element e (row-major index in the, possibly gathered, input)
+ * draws 16 bits from Philox4x32-10 block e>>3 (counter (lo, hi of e>>3, lo, hi of
+ * offset), key seed), word (e>>1)&3, half e&1.
+ *
+ * out->fmt selects NVFP4 (scale = amax/2688 per 128, E4M3 round-up per 16) or FP8
+ * (E4M3FN elements, scale = amax/448 per 128).  out->rows/len must match.
+ */
+tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q, int64_t rows,
+                          int64_t cols, const int32_t* col_idx, int64_t n_idx, int32_t grouping,
+                          int32_t rounding, int32_t rht, uint32_t rht_signs, uint64_t seed,
+                          uint64_t offset, tj2_qtensor* out, void* stream);
+
+/*
+ * Product on packed operands (section 2: every linear-layer product runs on the
+ * quantized tensors).  C[i, col(j)] (+)= sum_k A[i,k] B[j,k] + sum_k A2[i,k] B2[j,k]
+ * with A [I, K] and B [J, K] grouped along K, each NVFP4 or FP8; the optional
+ * second segment (A2, B2: [I, K2], [J, K2]) adds another reduction range.
+ * The result is accumulated in fp32 with one FP32 promotion per 128-element
+ * outer block.  c_dtype TJ2_F32 or TJ2_BF16 (round to nearest even); ldc in
+ * elements.  col_map (optional, device int32[J]) gives the output column of B
+ * row j.  accumulate != 0 adds into C (TJ2_F32 only).  workspace may be NULL
+ * when nvfp4_gemm_workspace_size() returns 0.
+ */
+tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2,
+                      const tj2_qtensor* B2, void* C, int32_t c_dtype, int64_t ldc,
+                      const int32_t* col_map, int32_t accumulate, void* workspace, size_t ws_bytes,
+                      void* stream);
+size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K);
+
+/*
+ * Forward of the NVFP4 linear layer Y = X W^T (section 2.A), X [M, K] bf16,
+ * W [N, K].
+ *   W_master != NULL: quantize the fp32 masters into *Wq (and *W8 with a plan);
+ *   W_master == NULL: use *Wq (*W8) as given (e.g. codes emitted by osci_reset_step).
+ *   plan == NULL: Xq [M, K], Wq [N, K] NVFP4 (RTN, 1x16 along K); X8/W8 unused.
+ *   plan != NULL: Xq [M, K1], Wq [N, K1] hold the compacted non-outlier channels
+ *     (K1 = K - n_outliers) in NVFP4; X8 [M, n_outliers], W8 [N, n_outliers] the
+ *     outlier channels in FP8 (round to nearest even); Y adds both products.
+ * Xq/X8 are saved for the backward and stay owned by the caller.
+ * Y [M, N]: y_dtype TJ2_BF16 or TJ2_F32.  M, K, N multiples of 16.
+ */
+tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, const float* W_master,
+                            tj2_qtensor* Wq, tj2_qtensor* W8, const tj2_outlier_plan* plan,
+                            tj2_qtensor* Xq, tj2_qtensor* X8, void* Y, int32_t y_dtype,
+                            void* stream);
+
+/*
+ * Backward of the NVFP4 linear layer (sections 2.A and 2.C).  Uses the forward's
+ * quantized tensors (X-hat / W-hat alignment), a 16-wide random Hadamard
+ * transform along the reduction dimension of each product (signs
+ * tj2_rht_signs(seed, offset+0) for dX, (seed, offset+2) for dW; rht == 0 skips
+ * it) and stochastic rounding with Philox offsets
+ *   offset+0 dY (groups along N), offset+1 W-hat re-grouped along N,
+ *   offset+2 dY re-grouped along M, offset+3 X-hat re-grouped along M,
+ *   offset+4 FP8 W-hat outliers, offset+5 FP8 X-hat outliers.
+ * The caller advances offset by 8 per call.
+ *   dX [M, K] (dx_dtype TJ2_BF16 or TJ2_F32) = Q(dY T) . Q(T^T W-hat)
+ *   dW [N, K] fp32                           = Q(dY^T T) . Q(T^T X-hat)
+ * With a plan, outlier columns of dX / dW come from the FP8 operands and are
+ * scattered back to their original channel positions.
+ * ops (optional): caller buffers for the intermediate operands (shapes in
+ * tj2_bwd_operands); NULL = carve them from `workspace`, which must then hold
+ * nvfp4_linear_bwd_workspace_size(M, N, K, n_outliers) bytes.
+ */
+tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, const tj2_qtensor* Xq,
+                            const tj2_qtensor* X8, const tj2_qtensor* Wq, const tj2_qtensor* W8,
+                            const tj2_outlier_plan* plan, int32_t rht, uint64_t seed,
+                            uint64_t offset, void* dX, int32_t dx_dtype, float* dW,
+                            tj2_bwd_operands* ops, void* workspace, size_t ws_bytes, void* stream);
+size_t nvfp4_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers);
+
+/*
+ * OsciReset (section 2.B) on fp32 masters W [N, K] and its state arrays (all
+ * fp32 [N, K], caller-owned).  Q(w) is the forward quantizer (RTN, 1x16 along K)
+ * dequantized in fp32.
+ *   TJ2_OSCI_INIT:       W_prev = W, Q_prev = Q(W), dQ = dM = 0.
+ *   TJ2_OSCI_ACCUM:      dQ += |Q(W) - Q_prev|, dM += |W - W_prev|, Q_prev = Q(W), W_prev = W.
+ *   TJ2_OSCI_WINDOW_END: as ACCUM; then where reset_enabled and dQ > tau*dM:
+ *                        W = Q(W), W_prev = Q(W); then dQ = dM = 0.
+ * Wq_out (optional, NVFP4 [N, K]): forward codes of the final W.
+ * reset_count (optional, device uint64): incremented by the number of resets.
+ * K must be a multiple of 16.
+ */
+tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N,
+                           int64_t K, int32_t mode, float tau, int32_t reset_enabled,
+                           tj2_qtensor* Wq_out, uint64_t* reset_count, void* stream);
+
+/*
+ * OutControl calibration helper (section 2.C: top p% channels from a short
+ * calibration window): acc[k] += sum over rows of X[m, k]^2 (fp32, bf16 input
+ * [M, K]).  The caller zeroes acc once and ranks the channels on the host.
+ */
+tj2_status tj2_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TJ2_H_ */

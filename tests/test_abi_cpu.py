@@ -1,0 +1,121 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/tj2.h, and rejects bad arguments on the host (before any
+device work) with the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import philox
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tj2.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from bit_fully_quantized_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libtj2.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_linear_fwd", "nvfp4_linear_bwd", "osci_reset_step",
+              "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes"]:
+        assert n in names
+
+
+def test_exports_every_declared_symbol(L):
+    from bit_fully_quantized_amd import _lib
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} not exported"
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature"
+
+
+def test_version_and_rht_signs_match_oracle(L):
+    assert b"gfx950" in L.tj2_version()
+    for seed, off in [(0, 0), (0, 2), (1234, 8), (2 ** 63 + 5, 2 ** 40 + 3)]:
+        assert L.tj2_rht_signs(seed, off) == philox.rht_signs(seed, off)
+
+
+def test_qtensor_bytes(L):
+    from bit_fully_quantized_amd import _lib
+    c, s16, s128 = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.tj2_qtensor_bytes(_lib.NVFP4, 3, 144, ctypes.byref(c), ctypes.byref(s16), ctypes.byref(s128)) == 0
+    assert (c.value, s16.value, s128.value) == (3 * 2 * 64, 3 * 2 * 8, 3 * 2 * 4)
+    assert L.tj2_qtensor_bytes(_lib.FP8, 2, 128, ctypes.byref(c), ctypes.byref(s16), ctypes.byref(s128)) == 0
+    assert (c.value, s16.value, s128.value) == (256, 0, 8)
+    assert L.tj2_qtensor_bytes(_lib.NVFP4, 2, 100, None, None, None) == _lib.TJ2_ERR_SHAPE
+    assert L.tj2_qtensor_bytes(7, 2, 128, None, None, None) == _lib.TJ2_ERR_ARG
+    assert b"format" in L.tj2_last_error()
+
+
+def fake_q(fmt, rows, length, base=0x10000):
+    from bit_fully_quantized_amd import _lib
+    return _lib.QTensorC(base, base + 0x1000 if fmt == _lib.NVFP4 else 0, base + 0x2000, rows, length, fmt, 0)
+
+
+def test_quantize_argument_errors(L):
+    from bit_fully_quantized_amd import _lib
+    out = fake_q(_lib.NVFP4, 32, 64)
+    q = lambda *a: L.nvfp4_quantize(*a)
+    # bad grouping / rounding / null out / bad dtype
+    assert q(0x1000, _lib.BF16, None, 32, 64, None, 0, 9, 0, 0, 0, 0, 0, ctypes.byref(out), None) == _lib.TJ2_ERR_ARG
+    assert q(0x1000, _lib.BF16, None, 32, 64, None, 0, 0, 5, 0, 0, 0, 0, ctypes.byref(out), None) == _lib.TJ2_ERR_ARG
+    assert q(0x1000, _lib.BF16, None, 32, 64, None, 0, 0, 0, 0, 0, 0, 0, None, None) == _lib.TJ2_ERR_ARG
+    assert q(0x1000, 9, None, 32, 64, None, 0, 0, 0, 0, 0, 0, 0, ctypes.byref(out), None) == _lib.TJ2_ERR_ARG
+    # misaligned input
+    assert q(0x1002, _lib.BF16, None, 32, 64, None, 0, 0, 0, 0, 0, 0, 0, ctypes.byref(out), None) == _lib.TJ2_ERR_ALIGN
+    # grouped length not a multiple of 16
+    bad = fake_q(_lib.NVFP4, 32, 64)
+    assert q(0x1000, _lib.BF16, None, 32, 40, None, 0, 0, 0, 0, 0, 0, 0, ctypes.byref(bad), None) == _lib.TJ2_ERR_SHAPE
+    # output shape mismatch (column grouping transposes)
+    assert q(0x1000, _lib.BF16, None, 32, 64, None, 0, 1, 0, 0, 0, 0, 0, ctypes.byref(out), None) == _lib.TJ2_ERR_SHAPE
+    assert b"expected" in L.tj2_last_error()
+    # gather with column grouping is unsupported
+    assert q(0x1000, _lib.BF16, None, 32, 64, 0x3000, 16, 1, 0, 0, 0, 0, 0, ctypes.byref(out), None) == _lib.TJ2_ERR_UNSUPPORTED
+
+
+def test_gemm_and_linear_argument_errors(L):
+    from bit_fully_quantized_amd import _lib
+    A = fake_q(_lib.NVFP4, 64, 128)
+    B = fake_q(_lib.NVFP4, 32, 96)
+    assert L.nvfp4_gemm(ctypes.byref(A), ctypes.byref(B), None, None, 0x5000, _lib.F32, 32, None, 0, None, 0, None) == _lib.TJ2_ERR_SHAPE
+    B = fake_q(_lib.NVFP4, 32, 128)
+    assert L.nvfp4_gemm(ctypes.byref(A), ctypes.byref(B), ctypes.byref(A), None, 0x5000, _lib.F32, 32, None, 0, None, 0, None) == _lib.TJ2_ERR_ARG
+    assert L.nvfp4_gemm(ctypes.byref(A), ctypes.byref(B), None, None, 0x5000, _lib.BF16, 32, None, 1, None, 0, None) == _lib.TJ2_ERR_UNSUPPORTED
+    assert L.nvfp4_gemm(ctypes.byref(A), ctypes.byref(B), None, None, 0x5000, _lib.F32, 16, None, 0, None, 0, None) == _lib.TJ2_ERR_SHAPE
+    Xq = fake_q(_lib.NVFP4, 64, 128)
+    Wq = fake_q(_lib.NVFP4, 32, 128)
+    # M not a multiple of 16
+    assert L.nvfp4_linear_fwd(0x1000, 60, 128, 32, None, ctypes.byref(Wq), None, None, ctypes.byref(Xq), None,
+                              0x9000, _lib.BF16, None) == _lib.TJ2_ERR_SHAPE
+    # plan with a bad outlier count
+    plan = _lib.PlanC(0x7000, 0x8000, 8, 0)
+    assert L.nvfp4_linear_fwd(0x1000, 64, 128, 32, None, ctypes.byref(Wq), None, ctypes.byref(plan),
+                              ctypes.byref(Xq), None, 0x9000, _lib.BF16, None) == _lib.TJ2_ERR_SHAPE
+    # backward without workspace
+    assert L.nvfp4_linear_bwd(0x1000, 64, 32, 128, ctypes.byref(Xq), None, ctypes.byref(Wq), None, None, 1, 0, 0,
+                              0x9000, _lib.BF16, 0xA000, None, None, 0, None) == _lib.TJ2_ERR_ARG
+    assert b"workspace" in L.tj2_last_error()
+    assert L.nvfp4_linear_bwd_workspace_size(64, 32, 128, 0) > 0
+
+
+def test_osci_argument_errors(L):
+    from bit_fully_quantized_amd import _lib
+    p = [0x1000 * (i + 1) for i in range(5)]
+    assert L.osci_reset_step(*p, 16, 100, 1, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_SHAPE
+    assert L.osci_reset_step(*p, 16, 128, 7, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step(*p, 16, 128, 1, ctypes.c_float(-1.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step(None, *p[1:], 16, 128, 1, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.tj2_channel_sumsq(0x1000, 64, 100, 0x2000, None) == _lib.TJ2_ERR_SHAPE

@@ -1,0 +1,80 @@
+"""GPU parity of the packed-operand products (relative Frobenius error <= 1e-3 vs
+the oracle's fp64 product of the same dequantized operands, which are first
+checked bit-exact against the oracle's own quantizers)."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import gemm as ogemm, quant
+
+import _helpers as H
+
+pytestmark = pytest.mark.gpu
+
+tj2 = pytest.importorskip("bit_fully_quantized_amd")
+
+
+def _operands(I, J, K, seed, fmt_b="nvfp4", sr=False):
+    a_bits = synthetic.normal_bf16((I, K), 1.0, seed)
+    b = synthetic.normal_f32((J, K), 0.02, seed + 1)
+    ga = tj2.quantize(H.bf16_to_device(a_bits), rounding=tj2.SR if sr else tj2.RTN, seed=seed, offset=0)
+    gb = tj2.quantize(H.f32_to_device(b), out_fmt=tj2.FP8 if fmt_b == "fp8" else tj2.NVFP4)
+    ra = quant.quantize(H.bf16_values(a_bits), rounding="sr" if sr else "rtn", seed=seed, offset=0)
+    rb = quant.quantize(b, fmt=fmt_b)
+    H.assert_q_equal(ga, ra, what="A")
+    H.assert_q_equal(gb, rb, what="B")
+    return ga, gb, ra, rb
+
+
+@pytest.mark.parametrize("I,J,K", [(256, 512, 512), (208, 144, 400), (16, 16, 16), (128, 384, 1024),
+                                   (300, 130, 272), (512, 256, 2048)])
+def test_gemm_nvfp4(I, J, K):
+    ga, gb, ra, rb = _operands(I, J, K, seed=I + J + K)
+    c = tj2.gemm(ga, gb).cpu().numpy()
+    ref = ogemm.gemm_nt_f64(ra, rb)
+    assert H.rel_fro(c, ref) <= H.GEMM_TOL
+    assert H.rel_fro(c, ref) < 1e-5  # fp32 accumulation of exact products
+
+
+def test_gemm_mixed_fp8_segment_and_scatter():
+    I, J, K = 192, 160, 256
+    ga, gb8, ra, rb8 = _operands(I, J, K, seed=5, fmt_b="fp8", sr=True)
+    c = tj2.gemm(ga, gb8).cpu().numpy()
+    assert H.rel_fro(c, ogemm.gemm_nt_f64(ra, rb8)) < 1e-5
+    # two segments (NVFP4 x NVFP4 + FP8 x FP8) into a column-scattered output
+    ga2, gb2, ra2, rb2 = _operands(I, J, 112, seed=6)
+    a8 = tj2.quantize(H.bf16_to_device(synthetic.normal_bf16((I, 112), 1.0, 60)), out_fmt=tj2.FP8)
+    ra8 = H.oracle_qtensor_from_gpu(a8)
+    b8 = tj2.quantize(H.f32_to_device(synthetic.normal_f32((J, 112), 0.02, 61)), out_fmt=tj2.FP8)
+    rb8b = H.oracle_qtensor_from_gpu(b8)
+    perm = np.random.default_rng(0).permutation(J + 32)[:J].astype(np.int32)
+    out = torch.full((I, J + 32), 7.0, device="cuda")
+    tj2.gemm(ga2, gb2, a8, b8, out=out, col_map=torch.from_numpy(perm).cuda())
+    ref = ogemm.gemm_nt_f64(ra2, rb2) + ogemm.gemm_nt_f64(ra8, rb8b)
+    got = out.cpu().numpy()
+    assert H.rel_fro(got[:, perm], ref) < 1e-5
+    untouched = np.setdiff1d(np.arange(J + 32), perm)
+    assert np.all(got[:, untouched] == 7.0)
+    # accumulate into fp32
+    tj2.gemm(ga2, gb2, out=out, col_map=torch.from_numpy(perm).cuda(), accumulate=True)
+    assert H.rel_fro(out.cpu().numpy()[:, perm], ref + ogemm.gemm_nt_f64(ra2, rb2)) < 1e-5
+
+
+def test_gemm_bf16_output():
+    ga, gb, ra, rb = _operands(256, 256, 512, seed=9)
+    c = tj2.gemm(ga, gb, out_dtype=torch.bfloat16)
+    assert H.bf16_ulp_ok(c, ogemm.gemm_nt_f64(ra, rb))
+
+
+def test_gemm_heterogeneous_scales():
+    """Rows / blocks whose outer scales differ by many binades: the per-128 promotion keeps them exact."""
+    I, J, K = 128, 128, 512
+    rng = np.random.default_rng(3)
+    a = (rng.standard_normal((I, K)) * np.exp2(rng.integers(-40, 40, size=(I, K // 128))).repeat(128, 1)).astype(np.float32)
+    b = (rng.standard_normal((J, K)) * np.exp2(rng.integers(-40, 40, size=(J, K // 128))).repeat(128, 1)).astype(np.float32)
+    ga, gb = tj2.quantize(H.f32_to_device(a)), tj2.quantize(H.f32_to_device(b))
+    ra, rb = quant.quantize(a), quant.quantize(b)
+    H.assert_q_equal(ga, ra); H.assert_q_equal(gb, rb)
+    c = tj2.gemm(ga, gb).cpu().numpy()
+    assert H.rel_fro(c, ogemm.gemm_nt_f64(ra, rb)) < 1e-5
