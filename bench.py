@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the TetraJet-v2 NVFP4 linear-layer path on one MI355X.
+
+One step = the whole hot path over one batch of the OLMo-2-370M-style linear
+workload: for each of the 16 layers x 5 linears (QKV 1024->3072, O 1024->1024,
+gate/up 1024->4096, down 4096->1024) with 16384 tokens,
+  forward   RTN quantization of X (NVFP4 + FP8 outlier channels) and of the
+            fp32 masters, product on the packed operands;
+  backward  SR + Hadamard quantization of dY (both groupings), re-grouping of
+            W-hat and X-hat (NVFP4 + FP8 outliers), dX and dW products;
+  OsciReset accumulation step on every fp32 master.
+Inputs are synthetic and resident in HBM before timing: X[t, c] = z * g_c with
+z ~ N(0, 1) and fixed heavy-tailed channel gains g_c = exp(1.5 * zeta_c); the
+static FP8 channels are the top 10% of 8 calibration batches; W ~ N(0, 0.02)
+fp32; dY ~ N(0, 0.01) bf16.
+
+value = algorithmic product flops per step (6 * M * N * K summed over the
+linears) / step time, in TFLOP/s.  Also reported: the product kernel's
+roofline (HIP events on its launch stream), the quantizer sweep on the
+8192x4096 bf16 tensor (GB/s of algorithmic bytes), OsciReset GB/s, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+SEED = 0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_gen(seed):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return g
+
+
+class LinearState:
+    """Device buffers of one linear layer of the workload."""
+
+    def __init__(self, tj2, layer, spec, M, p_outliers, seed):
+        import torch
+        self.name, self.K, self.N = spec.name, spec.K, spec.N
+        K, N = self.K, self.N
+        g = make_gen(seed)
+        self.gains = torch.exp(1.5 * torch.randn(K, generator=g, device="cuda"))
+        self.X = (torch.randn(M, K, generator=g, device="cuda") * self.gains).to(torch.bfloat16)
+        self.W = (torch.randn(N, K, generator=g, device="cuda") * 0.02).float().contiguous()
+        self.dY = (torch.randn(M, N, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+        # static outlier channels from 8 calibration batches (fresh z, same gains)
+        from bit_fully_quantized_amd import outcontrol
+        calib = ((torch.randn(M // 8, K, generator=g, device="cuda") * self.gains).to(torch.bfloat16)
+                 for _ in range(8))
+        self.plan = outcontrol.calibrate(calib, p_outliers)
+        no = self.plan.n
+        self.K1 = K - no
+        self.Xq = tj2.QTensor(tj2.NVFP4, M, self.K1)
+        self.X8 = tj2.QTensor(tj2.FP8, M, no)
+        self.Wq = tj2.QTensor(tj2.NVFP4, N, self.K1)
+        self.W8 = tj2.QTensor(tj2.FP8, N, no)
+        self.Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        self.dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        self.dW = torch.empty(N, K, dtype=torch.float32, device="cuda")
+        self.state = [torch.empty_like(self.W) for _ in range(4)]
+        tj2.osci_reset_step(self.W, *self.state, mode=tj2.OSCI_INIT)
+        self.saved = None
+
+
+def run_step(tj2, lins, ws, it):
+    for li in lins:
+        _, li.saved = tj2.linear_fwd(li.X, li.W, li.N, Wq=li.Wq, W8=li.W8, plan=li.plan, Y=li.Y, Xq=li.Xq,
+                                     X8=li.X8)
+    for idx in range(len(lins) - 1, -1, -1):
+        li = lins[idx]
+        tj2.linear_bwd(li.dY, li.saved, li.K, seed=SEED, offset=8 * (it * len(lins) + idx), plan=li.plan,
+                       dX=li.dX, dW=li.dW, workspace=ws)
+    for li in lins:
+        tj2.osci_reset_step(li.W, *li.state, mode=tj2.OSCI_ACCUM, tau=4.0)
+
+
+def time_launches(fn, reps):
+    """Average duration (s) of fn() over reps launches, HIP events on the current stream."""
+    import torch
+    fn()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / 1e3 / reps
+
+
+def gemm_roofline(tj2, lins, layers, M, reps=10):
+    """Average duration and flops of the product launches of one step (one layer's linears x layers)."""
+    tot_flops = 0.0
+    tot_time = 0.0
+    launches = 0
+    per = {}
+    for li in lins[:5]:
+        _, _, ops = tj2.linear_bwd(li.dY, li.saved, li.K, seed=SEED, offset=0, plan=li.plan, dX=li.dX, dW=li.dW,
+                                   keep_operands=True)
+        no, K1, K, N = li.plan.n, li.K1, li.K, li.N
+        calls = [
+            ("fwd", 2.0 * M * N * K, lambda: tj2.gemm(li.Xq, li.Wq, li.X8, li.W8, out=li.Y)),
+            ("dX", 2.0 * M * K1 * N, lambda: tj2.gemm(ops["dYq"], ops["Wt"], out=li.dX, col_map=li.plan.rest)),
+            ("dX8", 2.0 * M * no * N, lambda: tj2.gemm(ops["dYq"], ops["W8t"], out=li.dX, col_map=li.plan.outliers)),
+            ("dW", 2.0 * N * K1 * M, lambda: tj2.gemm(ops["dYt"], ops["Xt"], out=li.dW, col_map=li.plan.rest)),
+            ("dW8", 2.0 * N * no * M, lambda: tj2.gemm(ops["dYt"], ops["X8t"], out=li.dW, col_map=li.plan.outliers)),
+        ]
+        for name, fl, fn in calls:
+            t = time_launches(fn, reps)
+            per[f"{li.name}.{name}"] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 1)}
+            tot_flops += fl * layers
+            tot_time += t * layers
+            launches += layers
+    return tot_flops, tot_time, launches, per
+
+
+def quant_sweep(tj2, reps=24, nbuf=8):
+    """8192x4096 bf16 N(0,1), 1% of columns x64; buffers rotated to defeat the 256 MB last-level cache."""
+    import torch
+    import synthetic
+    R, C = synthetic.QUANT_SWEEP_SHAPE
+    g = make_gen(77)
+    cols = torch.randperm(C, generator=g, device="cuda")[: round(0.01 * C)]
+    xs = []
+    for _ in range(nbuf):
+        x = torch.randn(R, C, generator=g, device="cuda")
+        x[:, cols] *= 64.0
+        xs.append(x.to(torch.bfloat16))
+    outs_r = [tj2.QTensor(tj2.NVFP4, R, C) for _ in range(nbuf)]
+    outs_c = [tj2.QTensor(tj2.NVFP4, C, R) for _ in range(nbuf)]
+    bytes_per_call = R * C * (2 + 0.5 + 1 / 16 + 4 / 128)  # read bf16; write codes, E4M3, FP32 scales
+    signs = tj2.rht_signs(0, 0)
+    variants = {
+        "row_rtn": dict(grouping=tj2.GROUP_ROW, rounding=tj2.RTN, rht=False),
+        "row_sr": dict(grouping=tj2.GROUP_ROW, rounding=tj2.SR, rht=False),
+        "row_sr_rht": dict(grouping=tj2.GROUP_ROW, rounding=tj2.SR, rht=True),
+        "col_rtn": dict(grouping=tj2.GROUP_COL, rounding=tj2.RTN, rht=False),
+        "col_sr_rht": dict(grouping=tj2.GROUP_COL, rounding=tj2.SR, rht=True),
+    }
+    res = {}
+    for name, kw in variants.items():
+        outs = outs_r if kw["grouping"] == tj2.GROUP_ROW else outs_c
+        state = {"i": 0}
+
+        def fn():
+            i = state["i"] % nbuf
+            state["i"] += 1
+            tj2.quantize(xs[i], signs=signs, seed=0, offset=i, out=outs[i], **kw)
+
+        t = time_launches(fn, reps)
+        gbs = bytes_per_call / t / 1e9
+        res[name] = {"us": round(t * 1e6, 2), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 3)}
+    del xs, outs_r, outs_c
+    torch.cuda.empty_cache()
+    return res, bytes_per_call
+
+
+def cpu_baseline(M=256, K=1024, N=3072, p=0.10):
+    """The oracle (fp64 products, numpy quantizers) on one QKV-shaped linear with M tokens."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import synthetic
+    from oracle import calib as ocalib, linear as olinear
+    gains = synthetic.lognormal_channel_gains(K, 1.5, 11)
+    X = synthetic.bf16_bits_to_f32(synthetic.heavy_tailed_acts_bf16(M, gains, 12))
+    W = synthetic.normal_f32((N, K), 0.02, 13)
+    dY = synthetic.bf16_bits_to_f32(synthetic.normal_bf16((M, N), 0.01, 14))
+    plan = olinear.Plan.from_outliers(K, ocalib.select_outliers(ocalib.channel_scores([X]), p))
+    t0 = time.perf_counter()
+    fwd = olinear.linear_fwd(X, W, plan)
+    olinear.linear_bwd(dY, fwd, seed=0, offset=0, plan=plan)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    flops = 6.0 * M * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one QKV-shaped linear (K={K}, N={N}) with M={M} tokens and {plan.outliers.size} FP8 "
+                      f"outlier channels: forward + backward incl. every quantizer, fp64 products; "
+                      f"{dt:.2f} s for {flops / 1e9:.2f} GFLOP",
+            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU figures are not produced",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import bit_fully_quantized_amd as tj2
+    import synthetic
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = synthetic.OLMO370M
+    M, layers = wl.M, wl.layers
+    log(f"setting up {wl.name}: {layers} layers x {len(wl.linears)} linears, M={M}")
+    lins = []
+    for l in range(layers):
+        for j, spec in enumerate(wl.linears):
+            lins.append(LinearState(tj2, l, spec, M, 0.10, seed=1000 * l + j))
+    max_ws = max(int(tj2.lib().nvfp4_linear_bwd_workspace_size(M, li.N, li.K, li.plan.n)) for li in lins)
+    ws = torch.empty(max_ws, dtype=torch.uint8, device="cuda")
+    flops_step = wl.gemm_flops_per_step()
+    torch.cuda.synchronize()
+    log(f"setup done; warmup {args.warmup} steps")
+
+    for it in range(args.warmup):
+        run_step(tj2, lins, ws, it)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for it in range(args.steps):
+        run_step(tj2, lins, ws, args.warmup + it)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_s = wall / args.steps
+    step_ev = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    log(f"step {step_s * 1e3:.2f} ms (events {step_ev * 1e3:.2f} ms)")
+
+    log("product roofline pass")
+    g_flops, g_time, g_launches, per = gemm_roofline(tj2, lins, layers, M)
+    achieved = g_flops / g_time / 1e12
+    log("OsciReset pass")
+    n_params = sum(li.N * li.K for li in lins)
+    osci_t = time_launches(lambda: [tj2.osci_reset_step(li.W, *li.state, mode=tj2.OSCI_ACCUM, tau=4.0)
+                                    for li in lins], 3)
+    osci_bytes = n_params * 36.0  # read W, W_prev, Q_prev, dQ, dM; write W_prev, Q_prev, dQ, dM (fp32)
+    del lins, ws
+    torch.cuda.empty_cache()
+
+    sweep, sweep_bytes = ({}, 0) if args.no_sweep else quant_sweep(tj2)
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+
+    out = {
+        "metric": "NVFP4 linear fwd+bwd TFLOP/s at 370M shapes; quantizer GB/s (% of peak)",
+        "value": round(flops_step / step_s / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4",
+        "data": "synthetic",
+        "config": {
+            "workload": "OLMo-2-370M-style linears: d_model 1024, SwiGLU ffn 4096, 16 layers x "
+                        "(QKV, O, gate, up, down), 16384 tokens/step, heavy-tailed channels "
+                        "(lognormal sigma 1.5), OutControl top-10% FP8 channels, OsciReset accumulate",
+            "tokens": M, "layers": layers, "linears": len(wl.linears) * layers,
+            "gemm_tflop_per_step": round(flops_step / 1e12, 3), "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "gemm_nt_kernel (packed NVFP4/FP8 products: fwd, dX, dW)",
+            "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+            "avg_launch_us": round(g_time / g_launches * 1e6, 2), "launches_per_step": g_launches,
+            "gemm_share_of_step": round(g_time / step_s, 3), "per_launch": per,
+        },
+        "quantizer_sweep": {"tensor": "bf16 8192x4096 N(0,1), 1% columns x64", "algorithmic_MB_per_call":
+                            round(sweep_bytes / 1e6, 2), "hbm_peak_GB_s": HBM_PEAK_GBS, **sweep},
+        "osci_reset": {"GB_s": round(osci_bytes / osci_t / 1e9, 1),
+                       "frac_hbm": round(osci_bytes / osci_t / 1e9 / HBM_PEAK_GBS, 3),
+                       "ms_per_step": round(osci_t * 1e3, 3), "params": n_params},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

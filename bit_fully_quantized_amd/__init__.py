@@ -133,12 +133,16 @@ def gemm(A: QTensor, B: QTensor, A2: QTensor | None = None, B2: QTensor | None =
 
 def linear_fwd(X: torch.Tensor, W_master: torch.Tensor | None, N: int, *, Wq: QTensor | None = None,
                W8: QTensor | None = None, plan: OutlierPlan | None = None, y_dtype=torch.bfloat16,
-               Y: torch.Tensor | None = None):
-    """Y = X W^T with NVFP4 operands; returns (Y, saved) with saved = dict(Xq, X8, Wq, W8)."""
+               Y: torch.Tensor | None = None, Xq: QTensor | None = None, X8: QTensor | None = None):
+    """Y = X W^T with NVFP4 operands; returns (Y, saved) with saved = dict(Xq, X8, Wq, W8).
+
+    Output / saved buffers may be passed in (Y, Xq, X8, Wq, W8) to avoid allocations."""
     M, K = X.shape
     K1 = K - (plan.n if plan else 0)
-    Xq = QTensor(NVFP4, M, K1)
-    X8 = QTensor(FP8, M, plan.n) if plan else None
+    if Xq is None:
+        Xq = QTensor(NVFP4, M, K1)
+    if plan and X8 is None:
+        X8 = QTensor(FP8, M, plan.n)
     if Wq is None:
         Wq = QTensor(NVFP4, N, K1)
     if plan and W8 is None:
