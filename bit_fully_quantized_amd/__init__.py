@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI_INIT, OSCI_WINDOW_END, RTN, SR,
                    Tj2Error, check, lib)
 
-__all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "linear_fwd", "linear_bwd", "linear_bwd_workspace",
+__all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "gemm_workspace", "linear_fwd", "linear_bwd", "linear_bwd_workspace",
            "osci_reset_step", "channel_sumsq", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
            "GROUP_ROW", "GROUP_COL", "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END"]
 
@@ -116,17 +116,28 @@ def quantize(x, *, grouping: int = GROUP_ROW, rounding: int = RTN, rht: bool = F
     return out
 
 
+def gemm_workspace(I: int, J: int, K: int, device="cuda") -> torch.Tensor | None:
+    n = int(lib().nvfp4_gemm_workspace_size(I, J, K))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def gemm(A: QTensor, B: QTensor, A2: QTensor | None = None, B2: QTensor | None = None, *,
          out: torch.Tensor | None = None, out_dtype=torch.float32, col_map: torch.Tensor | None = None,
-         accumulate: bool = False) -> torch.Tensor:
-    """C = A B^T (+ A2 B2^T) on packed operands; C[i, col_map[j]] if col_map is given."""
+         accumulate: bool = False, workspace: torch.Tensor | None = None, split_k: bool = True) -> torch.Tensor:
+    """C = A B^T (+ A2 B2^T) on packed operands; C[i, col_map[j]] if col_map is given.
+
+    With split_k (default) a workspace for K-split partial sums is allocated when the library asks
+    for one (nvfp4_gemm_workspace_size); pass `workspace` to reuse a buffer."""
     if out is None:
         out = torch.empty((A.rows, B.rows), dtype=out_dtype, device=A.codes.device)
+    if workspace is None and split_k:
+        workspace = gemm_workspace(A.rows, B.rows, A.len + (A2.len if A2 is not None else 0), A.codes.device)
     ac, bc = A.c(), B.c()
     a2 = ctypes.byref(A2.c()) if A2 is not None else None
     b2 = ctypes.byref(B2.c()) if B2 is not None else None
     st = lib().nvfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), a2, b2, _ptr(out), _dtype_code(out), out.stride(0),
-                          _ptr(col_map), 1 if accumulate else 0, None, 0, _stream())
+                          _ptr(col_map), 1 if accumulate else 0, _ptr(workspace),
+                          0 if workspace is None else workspace.numel(), _stream())
     check("nvfp4_gemm", st)
     return out
 
@@ -189,7 +200,7 @@ def linear_bwd(dY: torch.Tensor, saved: dict, K: int, *, seed: int, offset: int,
         empty = _lib.QTensorC()
         opsc = _lib.BwdOperandsC(ops["dYq"].c(), ops["dYt"].c(), ops["Wt"].c(), ops["Xt"].c(),
                                  ops["W8t"].c() if plan else empty, ops["X8t"].c() if plan else empty)
-    elif workspace is None:
+    if workspace is None:
         workspace = linear_bwd_workspace(M, N, K, no, dY.device)
     pc = plan.c() if plan else None
     xqc, wqc = saved["Xq"].c(), saved["Wq"].c()

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "tj2_internal.h"
@@ -124,7 +125,8 @@ tj2_status run_quant(const void* x, int x_dtype, const tj2_qtensor* x_q, int64_t
 }
 
 tj2_status run_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2, const tj2_qtensor* B2,
-                    void* C, int c_dtype, int64_t ldc, const int32_t* col_map, int accumulate, hipStream_t s) {
+                    void* C, int c_dtype, int64_t ldc, const int32_t* col_map, int accumulate, void* ws,
+                    size_t ws_bytes, hipStream_t s) {
   GemmParams p;
   memset(&p, 0, sizeof(p));
   p.seg[0].a = make_view(*A);
@@ -144,6 +146,8 @@ tj2_status run_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtenso
   p.ldc = ldc;
   p.col_map = col_map;
   p.accumulate = accumulate;
+  p.partial = reinterpret_cast<float*>(ws);
+  p.partial_bytes = ws ? ws_bytes : 0;
   return hip_check(launch_gemm(p, s), "gemm launch");
 }
 
@@ -163,6 +167,18 @@ uint32_t philox_word0(uint64_t seed, uint64_t offset) {
     k1 += 0xBB67AE85u;
   }
   return c0;
+}
+
+// Split-K workspace shared (sequentially) by the products of one backward call.
+size_t bwd_gemm_ws(int64_t M, int64_t N, int64_t K1, int64_t no) {
+  const int64_t cn = (N + 127) / 128, cm = (M + 127) / 128;
+  size_t w = gemm_workspace_bytes(M, K1, cn);
+  w = std::max(w, gemm_workspace_bytes(N, K1, cm));
+  if (no) {
+    w = std::max(w, gemm_workspace_bytes(M, no, cn));
+    w = std::max(w, gemm_workspace_bytes(N, no, cm));
+  }
+  return align256(w);
 }
 
 tj2_status check_plan(const tj2_outlier_plan* plan, int64_t K) {
@@ -236,15 +252,15 @@ tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q
 }
 
 size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K) {
-  (void)I; (void)J; (void)K;
-  return 0;
+  if (I <= 0 || J <= 0 || K <= 0) return 0;
+  return gemm_workspace_bytes(I, J, (K + 127) / 128);
 }
 
 tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2, const tj2_qtensor* B2,
                       void* C, int32_t c_dtype, int64_t ldc, const int32_t* col_map, int32_t accumulate,
                       void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes;
   if (!A || !B) return fail(TJ2_ERR_ARG, "A and B are required");
+  if (workspace && !aligned16(workspace)) return fail(TJ2_ERR_ALIGN, "workspace must be 16-byte aligned");
   if ((A2 == nullptr) != (B2 == nullptr)) return fail(TJ2_ERR_ARG, "A2 and B2 must be given together");
   TJ2_TRY(check_qtensor(A, "A", A->fmt, A->rows, A->len));
   TJ2_TRY(check_qtensor(B, "B", B->fmt, B->rows, A->len));
@@ -258,7 +274,8 @@ tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qten
   if (!col_map && ldc < B->rows) return fail(TJ2_ERR_SHAPE, "ldc < J");
   if (ldc <= 0) return fail(TJ2_ERR_SHAPE, "ldc must be positive");
   if (A->rows > ((int64_t)1 << 24) * 128 || B->rows > ((int64_t)1 << 24) * 128) return fail(TJ2_ERR_SHAPE, "too many rows");
-  return run_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate, (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
+  return run_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate, workspace, workspace ? ws_bytes : 0,
+                  (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
 }
 
 tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, const float* W_master, tj2_qtensor* Wq,
@@ -287,7 +304,7 @@ tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, cons
     TJ2_TRY(run_quant(W_master, TJ2_F32, nullptr, N, K, rest, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Wq, s));
     if (plan) TJ2_TRY(run_quant(W_master, TJ2_F32, nullptr, N, K, plan->outliers, no, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, W8, s));
   }
-  TJ2_TRY(run_gemm(Xq, Wq, plan ? X8 : nullptr, plan ? W8 : nullptr, Y, y_dtype, N, nullptr, 0, s));
+  TJ2_TRY(run_gemm(Xq, Wq, plan ? X8 : nullptr, plan ? W8 : nullptr, Y, y_dtype, N, nullptr, 0, nullptr, 0, s));
   return ok();
 }
 
@@ -297,7 +314,7 @@ size_t nvfp4_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t 
   size_t t = carve_size(TJ2_NVFP4, M, N) + carve_size(TJ2_NVFP4, N, M) + carve_size(TJ2_NVFP4, K1, N) +
              carve_size(TJ2_NVFP4, K1, M);
   if (n_outliers) t += carve_size(TJ2_FP8, n_outliers, N) + carve_size(TJ2_FP8, n_outliers, M);
-  return t + 256;
+  return t + 256 + bwd_gemm_ws(M, N, K1, n_outliers);
 }
 
 tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, const tj2_qtensor* Xq,
@@ -323,11 +340,15 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
   }
   tj2_bwd_operands local;
   tj2_bwd_operands* o = ops;
+  const size_t gws = bwd_gemm_ws(M, N, K1, no);
+  void* gemm_ws = nullptr;
   if (!o) {
     const size_t need = nvfp4_linear_bwd_workspace_size(M, N, K, (int32_t)no);
     if (!workspace || ws_bytes < need)
       return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
     uint8_t* cur = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
+    gemm_ws = gws ? cur : nullptr;
+    cur += gws;
     local.dYq = carve(cur, TJ2_NVFP4, M, N);
     local.dYt = carve(cur, TJ2_NVFP4, N, M);
     local.Wt = carve(cur, TJ2_NVFP4, K1, N);
@@ -338,6 +359,7 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
     }
     o = &local;
   } else {
+    if (workspace && ws_bytes >= gws && aligned16(workspace)) gemm_ws = gws ? workspace : nullptr;
     TJ2_TRY(check_qtensor(&o->dYq, "ops.dYq", TJ2_NVFP4, M, N));
     TJ2_TRY(check_qtensor(&o->dYt, "ops.dYt", TJ2_NVFP4, N, M));
     TJ2_TRY(check_qtensor(&o->Wt, "ops.Wt", TJ2_NVFP4, K1, N));
@@ -355,13 +377,13 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
   TJ2_TRY(run_quant(dY, TJ2_BF16, nullptr, M, N, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 2, &o->dYt, s));
   TJ2_TRY(run_quant(nullptr, TJ2_NVFP4, Xq, M, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 3, &o->Xt, s));
   const int32_t* rest = plan ? plan->rest : nullptr;
-  TJ2_TRY(run_gemm(&o->dYq, &o->Wt, nullptr, nullptr, dX, dx_dtype, K, rest, 0, s));
-  TJ2_TRY(run_gemm(&o->dYt, &o->Xt, nullptr, nullptr, dW, TJ2_F32, K, rest, 0, s));
+  TJ2_TRY(run_gemm(&o->dYq, &o->Wt, nullptr, nullptr, dX, dx_dtype, K, rest, 0, gemm_ws, gws, s));
+  TJ2_TRY(run_gemm(&o->dYt, &o->Xt, nullptr, nullptr, dW, TJ2_F32, K, rest, 0, gemm_ws, gws, s));
   if (plan) {
     TJ2_TRY(run_quant(nullptr, TJ2_FP8, W8, N, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 4, &o->W8t, s));
     TJ2_TRY(run_quant(nullptr, TJ2_FP8, X8, M, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 5, &o->X8t, s));
-    TJ2_TRY(run_gemm(&o->dYq, &o->W8t, nullptr, nullptr, dX, dx_dtype, K, plan->outliers, 0, s));
-    TJ2_TRY(run_gemm(&o->dYt, &o->X8t, nullptr, nullptr, dW, TJ2_F32, K, plan->outliers, 0, s));
+    TJ2_TRY(run_gemm(&o->dYq, &o->W8t, nullptr, nullptr, dX, dx_dtype, K, plan->outliers, 0, gemm_ws, gws, s));
+    TJ2_TRY(run_gemm(&o->dYt, &o->X8t, nullptr, nullptr, dW, TJ2_F32, K, plan->outliers, 0, gemm_ws, gws, s));
   }
   return ok();
 }

@@ -20,9 +20,14 @@
 // row-half of A and of B (packed codes + scales), decodes it to f16 with
 // v_cvt_scalef32_pk_f16_fp4 / _fp8 (scale 1.0: exact) and v_pk_mul_f16 by the
 // inner scale, and writes it to LDS (rows padded to 272 bytes: conflict-free
-// 16-byte accesses).  The next chunk's packed operands are fetched into
-// registers while the current chunk runs on MFMA; two workgroups per CU
-// overlap one's decode with the other's MFMA.
+// 16-byte accesses).  Packed operands are prefetched two chunks ahead into
+// registers; the eight 16-deep K steps of a chunk are unrolled with the LDS
+// fragments of step k+1 read during step k; two workgroups per CU overlap one's
+// decode with the other's MFMA.  Operand formats are template parameters (no
+// runtime format branches); rows past the edge are clamped to the last row
+// (their results are never stored), so loads never diverge.  Workgroups are
+// numbered so that each of the 8 XCDs (own L2) gets a contiguous range of
+// output tiles, N-fastest: consecutive tiles on one XCD share their A rows.
 #include "tj2_device.h"
 #include "tj2_internal.h"
 
@@ -32,13 +37,13 @@ namespace {
 
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int LDS_STRIDE = BK + 8;  // f16 elements per LDS row
+constexpr int F_NONE = -1;
 
 struct OperandK {
   const uint8_t* codes;
   const uint8_t* s16;
   const float* s128;
   int64_t ld_codes, ld_s16, ld_s128;
-  int fmt;
 };
 
 struct SegK {
@@ -49,8 +54,10 @@ struct SegK {
 
 struct GemmKArgs {
   SegK seg[2];
-  int nseg;
-  int nchunks;
+  int nchunks;           // seg[0].nchunks + seg[1].nchunks
+  int chunks_per_split;  // chunk range of split z: [z*cps, min((z+1)*cps, nchunks))
+  int tiles_m, tiles_n, split;
+  float* partial;        // split > 1: fp32 [split][I][J] partial sums
   int64_t I, J;
   void* C;
   int64_t ldc;
@@ -59,187 +66,264 @@ struct GemmKArgs {
   int accumulate;
 };
 
-// Packed operand slice of one thread: 64 consecutive K elements of one row.
-struct Slice {
-  uint4 c[4];      // NVFP4 uses c[0..1] (32 bytes), FP8 c[0..3] (64 bytes)
-  uint32_t s16;    // four E4M3 inner scales (NVFP4)
-  float S;         // outer scale of the chunk
+// Packed slice of one thread: 64 consecutive K elements of one operand row.
+template <int F>
+struct Op;
+
+template <>
+struct Op<TJ2_NVFP4> {
+  struct Slice {
+    uint4 c0, c1;   // 64 E2M1 codes
+    uint32_t s16;   // four E4M3 inner scales
+    float S;        // outer scale of the chunk
+  };
+  static __device__ __forceinline__ void load(const OperandK& o, int64_t row, int kc, int half, Slice& s) {
+    const uint8_t* cp = o.codes + row * o.ld_codes + kc * 64 + half * 32;
+    s.c0 = *reinterpret_cast<const uint4*>(cp);
+    s.c1 = *reinterpret_cast<const uint4*>(cp + 16);
+    s.s16 = *reinterpret_cast<const uint32_t*>(o.s16 + row * o.ld_s16 + kc * 8 + half * 4);
+    s.S = o.s128[row * o.ld_s128 + kc];
+  }
+  template <int BYTE>
+  static __device__ __forceinline__ uint32_t q2(uint32_t word, half2_t sc) {
+    half2_t q = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, BYTE) * sc;
+    return __builtin_bit_cast(uint32_t, q);
+  }
+  // 64 f16 values q * s (exact) to dst (16-byte aligned)
+  static __device__ __forceinline__ void decode(const Slice& s, _Float16* dst) {
+    uint4* out = reinterpret_cast<uint4*>(dst);
+    const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.s16, 1.0f, false);
+    const half2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.s16, 1.0f, true);
+    const half2_t sg[4] = {half2_t{s01[0], s01[0]}, half2_t{s01[1], s01[1]}, half2_t{s23[0], s23[0]},
+                           half2_t{s23[1], s23[1]}};
+    const uint32_t w[8] = {s.c0.x, s.c0.y, s.c0.z, s.c0.w, s.c1.x, s.c1.y, s.c1.z, s.c1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const half2_t sc = sg[i >> 1];
+      out[i] = make_uint4(q2<0>(w[i], sc), q2<1>(w[i], sc), q2<2>(w[i], sc), q2<3>(w[i], sc));
+    }
+  }
 };
 
-__device__ __forceinline__ void load_slice(const OperandK& o, int64_t row, bool valid, int kc, int half,
-                                           Slice& s) {
-  if (!valid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s.c[i] = make_uint4(0, 0, 0, 0);
-    s.s16 = 0u;
-    s.S = 0.0f;
-    return;
-  }
-  if (o.fmt == TJ2_NVFP4) {
-    const uint4* p = reinterpret_cast<const uint4*>(o.codes + row * o.ld_codes + kc * 64 + half * 32);
-    s.c[0] = p[0];
-    s.c[1] = p[1];
-    s.s16 = *reinterpret_cast<const uint32_t*>(o.s16 + row * o.ld_s16 + kc * 8 + half * 4);
-  } else {
+template <>
+struct Op<TJ2_FP8> {
+  struct Slice {
+    uint4 c[4];     // 64 E4M3 codes
+    float S;
+  };
+  static __device__ __forceinline__ void load(const OperandK& o, int64_t row, int kc, int half, Slice& s) {
     const uint4* p = reinterpret_cast<const uint4*>(o.codes + row * o.ld_codes + kc * 128 + half * 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s.c[i] = p[i];
-    s.s16 = 0u;
+    s.S = o.s128[row * o.ld_s128 + kc];
   }
-  s.S = o.s128[row * o.ld_s128 + kc];
-}
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t e2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
+  static __device__ __forceinline__ void decode(const Slice& s, _Float16* dst) {
+    uint4* out = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = make_uint4(e2<false>(s.c[i].x), e2<true>(s.c[i].x), e2<false>(s.c[i].y), e2<true>(s.c[i].y));
+      out[2 * i + 1] = make_uint4(e2<false>(s.c[i].z), e2<true>(s.c[i].z), e2<false>(s.c[i].w), e2<true>(s.c[i].w));
+    }
+  }
+};
 
-// Decode 64 elements to f16 and store them at dst (64 halves, 16-byte aligned).
-__device__ __forceinline__ void decode_slice(int fmt, const Slice& s, _Float16* dst) {
-  uint4* out = reinterpret_cast<uint4*>(dst);
-  if (fmt == TJ2_NVFP4) {
-    // inner scales as f16 pairs {s0, s1}, {s2, s3}
-    half2_t sc01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.s16, 1.0f, false);
-    half2_t sc23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.s16, 1.0f, true);
-    const uint32_t w[8] = {s.c[0].x, s.c[0].y, s.c[0].z, s.c[0].w, s.c[1].x, s.c[1].y, s.c[1].z, s.c[1].w};
+struct TileCtx {
+  int64_t rowA, rowB;   // clamped source rows of this thread's loads
+  int lr, lh, lane, wm, wn;
+  _Float16* lds_a;
+  _Float16* lds_b;
+  float* sa;
+  float* sb;
+};
+
+__device__ __forceinline__ half8_t ld8(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
+
+// MFMA over one decoded chunk (nk 16-deep steps) and promotion into acc.
+__device__ __forceinline__ void chunk_mfma(const TileCtx& t, int nk, float16_t (&acc)[2][2]) {
+  const _Float16* ab = t.lds_a + (t.wm * 64 + (t.lane & 31)) * LDS_STRIDE + (t.lane >> 5) * 8;
+  const _Float16* bb = t.lds_b + (t.wn * 64 + (t.lane & 31)) * LDS_STRIDE + (t.lane >> 5) * 8;
+  float16_t part[2][2];
+  if (nk == BK / 16) {
+    half8_t fa[2][2], fb[2][2];
+    fa[0][0] = ld8(ab);
+    fa[0][1] = ld8(ab + 32 * LDS_STRIDE);
+    fb[0][0] = ld8(bb);
+    fb[0][1] = ld8(bb + 32 * LDS_STRIDE);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const half2_t sg = g == 0 ? half2_t{sc01[0], sc01[0]}
-                       : g == 1 ? half2_t{sc01[1], sc01[1]}
-                       : g == 2 ? half2_t{sc23[0], sc23[0]}
-                                : half2_t{sc23[1], sc23[1]};
-      uint32_t r[8];
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const uint32_t word = w[2 * g + d];
-        half2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sg;
-        half2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sg;
-        half2_t q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sg;
-        half2_t q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sg;
-        r[4 * d + 0] = __builtin_bit_cast(uint32_t, q0);
-        r[4 * d + 1] = __builtin_bit_cast(uint32_t, q1);
-        r[4 * d + 2] = __builtin_bit_cast(uint32_t, q2);
-        r[4 * d + 3] = __builtin_bit_cast(uint32_t, q3);
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int cb = ks & 1, nb = cb ^ 1;
+      if (ks + 1 < BK / 16) {
+        fa[nb][0] = ld8(ab + (ks + 1) * 16);
+        fa[nb][1] = ld8(ab + 32 * LDS_STRIDE + (ks + 1) * 16);
+        fb[nb][0] = ld8(bb + (ks + 1) * 16);
+        fb[nb][1] = ld8(bb + 32 * LDS_STRIDE + (ks + 1) * 16);
       }
-      out[2 * g + 0] = make_uint4(r[0], r[1], r[2], r[3]);
-      out[2 * g + 1] = make_uint4(r[4], r[5], r[6], r[7]);
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn)
+          part[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[cb][tm], fb[cb][tn],
+                                                                ks == 0 ? float16_t{} : part[tm][tn], 0, 0, 0);
     }
   } else {
-    const uint32_t w[16] = {s.c[0].x, s.c[0].y, s.c[0].z, s.c[0].w, s.c[1].x, s.c[1].y, s.c[1].z, s.c[1].w,
-                            s.c[2].x, s.c[2].y, s.c[2].z, s.c[2].w, s.c[3].x, s.c[3].y, s.c[3].z, s.c[3].w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      half2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * i], 1.0f, false);
-      half2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * i], 1.0f, true);
-      half2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * i + 1], 1.0f, false);
-      half2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * i + 1], 1.0f, true);
-      out[i] = make_uint4(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
-                          __builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1));
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+        part[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ld8(ab + tm * 32 * LDS_STRIDE),
+                                                              ld8(bb + tn * 32 * LDS_STRIDE), float16_t{}, 0, 0, 0);
+    for (int ks = 1; ks < nk; ++ks) {
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn)
+          part[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ld8(ab + tm * 32 * LDS_STRIDE + ks * 16),
+                                                                ld8(bb + tn * 32 * LDS_STRIDE + ks * 16),
+                                                                part[tm][tn], 0, 0, 0);
+    }
+  }
+  // promotion: acc += part * (S_A[row] * S_B[col]); rows t&3 of a lane are consecutive
+  float rb[2];
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn) rb[tn] = t.sb[t.wn * 64 + tn * 32 + (t.lane & 31)];
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 ra = *reinterpret_cast<const float4*>(t.sa + t.wm * 64 + tm * 32 + 8 * g + 4 * (t.lane >> 5));
+      const float r4[4] = {ra.x, ra.y, ra.z, ra.w};
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[tm][tn][4 * g + q] = fmaf(part[tm][tn][4 * g + q], r4[q] * rb[tn], acc[tm][tn][4 * g + q]);
     }
   }
 }
 
-__device__ __forceinline__ void chunk_of(const GemmKArgs& p, int c, int& seg, int& kc) {
-  seg = (p.nseg > 1 && c >= p.seg[0].nchunks) ? 1 : 0;
-  kc = seg ? c - p.seg[0].nchunks : c;
+template <int FA, int FB>
+__device__ __forceinline__ void stage_chunk(const TileCtx& t, const typename Op<FA>::Slice& a,
+                                            const typename Op<FB>::Slice& b) {
+  __syncthreads();  // the previous chunk's LDS reads are done
+  Op<FA>::decode(a, t.lds_a + t.lr * LDS_STRIDE + t.lh * 64);
+  Op<FB>::decode(b, t.lds_b + t.lr * LDS_STRIDE + t.lh * 64);
+  if (t.lh == 0) {
+    t.sa[t.lr] = a.S;
+    t.sb[t.lr] = b.S;
+  }
+  __syncthreads();
 }
 
+// Chunks [kc0, kc1) of one segment, with a two-deep register prefetch.
+template <int FA, int FB>
+__device__ __forceinline__ void run_segment(const TileCtx& t, const SegK& g, int kc0, int kc1,
+                                            float16_t (&acc)[2][2]) {
+  if (kc0 >= kc1) return;
+  typename Op<FA>::Slice a0, a1;
+  typename Op<FB>::Slice b0, b1;
+  Op<FA>::load(g.a, t.rowA, kc0, t.lh, a0);
+  Op<FB>::load(g.b, t.rowB, kc0, t.lh, b0);
+  if (kc0 + 1 < kc1) {
+    Op<FA>::load(g.a, t.rowA, kc0 + 1, t.lh, a1);
+    Op<FB>::load(g.b, t.rowB, kc0 + 1, t.lh, b1);
+  }
+  for (int kc = kc0; kc < kc1; kc += 2) {
+    stage_chunk<FA, FB>(t, a0, b0);
+    if (kc + 2 < kc1) {
+      Op<FA>::load(g.a, t.rowA, kc + 2, t.lh, a0);
+      Op<FB>::load(g.b, t.rowB, kc + 2, t.lh, b0);
+    }
+    int64_t krem = g.K - (int64_t)kc * BK;
+    chunk_mfma(t, (int)((krem < BK ? krem : BK) >> 4), acc);
+    if (kc + 1 >= kc1) break;
+    stage_chunk<FA, FB>(t, a1, b1);
+    if (kc + 3 < kc1) {
+      Op<FA>::load(g.a, t.rowA, kc + 3, t.lh, a1);
+      Op<FB>::load(g.b, t.rowB, kc + 3, t.lh, b1);
+    }
+    krem = g.K - (int64_t)(kc + 1) * BK;
+    chunk_mfma(t, (int)((krem < BK ? krem : BK) >> 4), acc);
+  }
+}
+
+template <int FA0, int FB0, int FA1, int FB1>
 __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(GemmKArgs p) {
   __shared__ __attribute__((aligned(16))) _Float16 lds_a[BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) _Float16 lds_b[BN * LDS_STRIDE];
-  __shared__ float sa[BM], sb[BN];
+  __shared__ __attribute__((aligned(16))) float sa[BM];
+  __shared__ __attribute__((aligned(16))) float sb[BN];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int lr = tid >> 1, lh = tid & 1;
-  const int64_t rowA = m0 + lr, rowB = n0 + lr;
-  const bool vA = rowA < p.I, vB = rowB < p.J;
+  // XCD-aware numbering: workgroup id w runs on XCD w % 8; give each XCD a
+  // contiguous range of (tile, split) indices, tiles N-fastest.
+  const uint32_t nwg = gridDim.x;
+  uint32_t id = blockIdx.x;
+  const uint32_t per_xcd = nwg / 8;
+  if (id < per_xcd * 8) id = (id % 8) * per_xcd + id / 8;
+  const uint32_t tiles = (uint32_t)(p.tiles_m * p.tiles_n);
+  const uint32_t tile = id % tiles, z = id / tiles;
+  const int64_t m0 = (int64_t)(tile / p.tiles_n) * BM, n0 = (int64_t)(tile % p.tiles_n) * BN;
+
+  TileCtx t;
+  const int tid = threadIdx.x;
+  t.lane = tid & 63;
+  const int wave = tid >> 6;
+  t.wm = wave >> 1;
+  t.wn = wave & 1;
+  t.lr = tid >> 1;
+  t.lh = tid & 1;
+  t.rowA = min(m0 + t.lr, p.I - 1);
+  t.rowB = min(n0 + t.lr, p.J - 1);
+  t.lds_a = lds_a;
+  t.lds_b = lds_b;
+  t.sa = sa;
+  t.sb = sb;
 
   float16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int t = 0; t < 16; ++t) acc[i][j][t] = 0.0f;
-  const float16_t zero = acc[0][0];
+    for (int j = 0; j < 2; ++j) acc[i][j] = float16_t{};
 
-  Slice pa, pb;
-  {
-    int seg, kc;
-    chunk_of(p, 0, seg, kc);
-    load_slice(p.seg[seg].a, rowA, vA, kc, lh, pa);
-    load_slice(p.seg[seg].b, rowB, vB, kc, lh, pb);
-  }
+  const int c_begin = (int)z * p.chunks_per_split;
+  const int c_end = min(c_begin + p.chunks_per_split, p.nchunks);
+  const int n0c = p.seg[0].nchunks;
+  run_segment<FA0, FB0>(t, p.seg[0], c_begin, min(c_end, n0c), acc);
+  if constexpr (FA1 != F_NONE) run_segment<FA1, FB1>(t, p.seg[1], max(c_begin, n0c) - n0c, c_end - n0c, acc);
 
-  for (int c = 0; c < p.nchunks; ++c) {
-    int seg, kc;
-    chunk_of(p, c, seg, kc);
-    const SegK& g = p.seg[seg];
-    __syncthreads();  // previous chunk's LDS reads are done
-    decode_slice(g.a.fmt, pa, lds_a + lr * LDS_STRIDE + lh * 64);
-    decode_slice(g.b.fmt, pb, lds_b + lr * LDS_STRIDE + lh * 64);
-    if (lh == 0) {
-      sa[lr] = pa.S;
-      sb[lr] = pb.S;
-    }
-    __syncthreads();
-    if (c + 1 < p.nchunks) {
-      int seg2, kc2;
-      chunk_of(p, c + 1, seg2, kc2);
-      load_slice(p.seg[seg2].a, rowA, vA, kc2, lh, pa);
-      load_slice(p.seg[seg2].b, rowB, vB, kc2, lh, pb);
-    }
-    const int64_t krem = g.K - (int64_t)kc * BK;
-    const int nk = (int)((krem < BK ? krem : BK) >> 4);
-
-    float16_t part[2][2];
-    const _Float16* a_base = lds_a + (wm * 64 + (lane & 31)) * LDS_STRIDE + (lane >> 5) * 8;
-    const _Float16* b_base = lds_b + (wn * 64 + (lane & 31)) * LDS_STRIDE + (lane >> 5) * 8;
-    {
-      half8_t a0 = *reinterpret_cast<const half8_t*>(a_base);
-      half8_t a1 = *reinterpret_cast<const half8_t*>(a_base + 32 * LDS_STRIDE);
-      half8_t b0 = *reinterpret_cast<const half8_t*>(b_base);
-      half8_t b1 = *reinterpret_cast<const half8_t*>(b_base + 32 * LDS_STRIDE);
-      part[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, zero, 0, 0, 0);
-      part[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, zero, 0, 0, 0);
-      part[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, zero, 0, 0, 0);
-      part[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, zero, 0, 0, 0);
-    }
-    for (int ks = 1; ks < nk; ++ks) {
-      half8_t a0 = *reinterpret_cast<const half8_t*>(a_base + ks * 16);
-      half8_t a1 = *reinterpret_cast<const half8_t*>(a_base + 32 * LDS_STRIDE + ks * 16);
-      half8_t b0 = *reinterpret_cast<const half8_t*>(b_base + ks * 16);
-      half8_t b1 = *reinterpret_cast<const half8_t*>(b_base + 32 * LDS_STRIDE + ks * 16);
-      part[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, part[0][0], 0, 0, 0);
-      part[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, part[0][1], 0, 0, 0);
-      part[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, part[1][0], 0, 0, 0);
-      part[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, part[1][1], 0, 0, 0);
-    }
-    // promote: acc += part * (S_A[row] * S_B[col])
+  const int lane = t.lane;
+  if (p.partial) {
+    float* part_out = p.partial + (int64_t)z * p.I * p.J;
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn) {
-      const float rb = sb[wn * 64 + tn * 32 + (lane & 31)];
+      const int64_t col = n0 + t.wn * 64 + tn * 32 + (lane & 31);
+      if (col >= p.J) continue;
 #pragma unroll
       for (int tm = 0; tm < 2; ++tm) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int r = wm * 64 + tm * 32 + 8 * (t >> 2) + 4 * (lane >> 5) + (t & 3);
-          acc[tm][tn][t] = fmaf(part[tm][tn][t], sa[r] * rb, acc[tm][tn][t]);
+        for (int e = 0; e < 16; ++e) {
+          const int64_t row = m0 + t.wm * 64 + tm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if (row < p.I) part_out[row * p.J + col] = acc[tm][tn][e];
         }
       }
     }
+    return;
   }
-
-  // epilogue
 #pragma unroll
   for (int tn = 0; tn < 2; ++tn) {
-    const int64_t col = n0 + wn * 64 + tn * 32 + (lane & 31);
+    const int64_t col = n0 + t.wn * 64 + tn * 32 + (lane & 31);
     if (col >= p.J) continue;
     const int64_t ccol = p.col_map ? (int64_t)p.col_map[col] : col;
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int64_t row = m0 + wm * 64 + tm * 32 + 8 * (t >> 2) + 4 * (lane >> 5) + (t & 3);
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + t.wm * 64 + tm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (row >= p.I) continue;
-        const float v = acc[tm][tn][t];
+        const float v = acc[tm][tn][e];
         if (p.c_bf16) {
           reinterpret_cast<uint16_t*>(p.C)[row * p.ldc + ccol] = (uint16_t)f32_to_bf16(v);
         } else {
@@ -247,6 +331,43 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(GemmKArgs p) {
           *cp = p.accumulate ? *cp + v : v;
         }
       }
+    }
+  }
+}
+
+// C[i, map(j)] (+)= sum_z partial[z][i][j]; one thread per 4 consecutive j.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int split, int64_t I,
+                                                            int64_t J, void* C, int64_t ldc,
+                                                            const int32_t* __restrict__ col_map, int c_bf16,
+                                                            int accumulate) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t jq = (J + 3) / 4;
+  const int64_t i = q / jq;
+  if (i >= I) return;
+  const int64_t j0 = (q - i * jq) * 4;
+  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t stride = I * J;
+  const float* p = partial + i * J + j0;
+  if (j0 + 4 <= J && (J & 3) == 0) {
+    for (int z = 0; z < split; ++z) {
+      float4 v = *reinterpret_cast<const float4*>(p + z * stride);
+      s[0] += v.x; s[1] += v.y; s[2] += v.z; s[3] += v.w;
+    }
+  } else {
+    for (int z = 0; z < split; ++z)
+      for (int t = 0; t < 4; ++t)
+        if (j0 + t < J) s[t] += p[z * stride + t];
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t j = j0 + t;
+    if (j >= J) break;
+    const int64_t cj = col_map ? (int64_t)col_map[j] : j;
+    if (c_bf16) {
+      reinterpret_cast<uint16_t*>(C)[i * ldc + cj] = (uint16_t)f32_to_bf16(s[t]);
+    } else {
+      float* cp = reinterpret_cast<float*>(C) + i * ldc + cj;
+      *cp = accumulate ? *cp + s[t] : s[t];
     }
   }
 }
@@ -259,15 +380,49 @@ OperandK operand_of(const QView& v) {
   o.ld_codes = v.ld_codes;
   o.ld_s16 = v.ld_s16;
   o.ld_s128 = v.ld_s128;
-  o.fmt = v.fmt;
   return o;
+}
+
+typedef void (*GemmKernel)(GemmKArgs);
+
+GemmKernel pick_kernel(const GemmParams& p) {
+  const int fa = p.seg[0].a.fmt, fb = p.seg[0].b.fmt;
+  if (p.nseg == 2) {
+    if (fa == TJ2_NVFP4 && fb == TJ2_NVFP4 && p.seg[1].a.fmt == TJ2_FP8 && p.seg[1].b.fmt == TJ2_FP8)
+      return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, TJ2_FP8, TJ2_FP8>;
+    if (fa == TJ2_NVFP4 && fb == TJ2_NVFP4 && p.seg[1].a.fmt == TJ2_NVFP4 && p.seg[1].b.fmt == TJ2_NVFP4)
+      return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, TJ2_NVFP4, TJ2_NVFP4>;
+    return nullptr;
+  }
+  if (fa == TJ2_NVFP4 && fb == TJ2_NVFP4) return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, F_NONE, F_NONE>;
+  if (fa == TJ2_NVFP4 && fb == TJ2_FP8) return gemm_nt_kernel<TJ2_NVFP4, TJ2_FP8, F_NONE, F_NONE>;
+  if (fa == TJ2_FP8 && fb == TJ2_NVFP4) return gemm_nt_kernel<TJ2_FP8, TJ2_NVFP4, F_NONE, F_NONE>;
+  if (fa == TJ2_FP8 && fb == TJ2_FP8) return gemm_nt_kernel<TJ2_FP8, TJ2_FP8, F_NONE, F_NONE>;
+  return nullptr;
 }
 
 }  // namespace
 
+int gemm_split(int64_t I, int64_t J, int64_t nchunks) {
+  const int64_t tiles = ((I + BM - 1) / BM) * ((J + BN - 1) / BN);
+  const int64_t target = 1024;  // workgroups: about two rounds of two per CU
+  if (tiles >= target / 2 || nchunks < 8) return 1;
+  int64_t split = (target + tiles - 1) / tiles;
+  const int64_t max_by_depth = nchunks / 4;  // keep >= 4 chunks per split
+  if (split > max_by_depth) split = max_by_depth;
+  if (split > 64) split = 64;
+  return split < 2 ? 1 : (int)split;
+}
+
+size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t nchunks) {
+  const int split = gemm_split(I, J, nchunks);
+  return split > 1 ? (size_t)split * (size_t)I * (size_t)J * sizeof(float) : 0;
+}
+
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+  GemmKernel kern = pick_kernel(p);
+  if (!kern) return hipErrorInvalidValue;
   GemmKArgs k;
-  k.nseg = p.nseg;
   k.nchunks = 0;
   for (int i = 0; i < 2; ++i) {
     if (i < p.nseg) {
@@ -288,8 +443,21 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   k.col_map = p.col_map;
   k.c_bf16 = p.c_dtype == TJ2_BF16;
   k.accumulate = p.accumulate;
-  dim3 grid((uint32_t)((p.J + BN - 1) / BN), (uint32_t)((p.I + BM - 1) / BM));
-  hipLaunchKernelGGL(gemm_nt_kernel, grid, dim3(256), 0, s, k);
+  int split = gemm_split(p.I, p.J, k.nchunks);
+  if (split > 1 && (!p.partial || p.partial_bytes < (size_t)split * p.I * p.J * sizeof(float))) split = 1;
+  k.chunks_per_split = (k.nchunks + split - 1) / split;
+  split = (k.nchunks + k.chunks_per_split - 1) / k.chunks_per_split;  // no empty splits
+  k.partial = split > 1 ? p.partial : nullptr;
+  k.tiles_m = (int)((p.I + BM - 1) / BM);
+  k.tiles_n = (int)((p.J + BN - 1) / BN);
+  k.split = split;
+  const uint32_t nwg = (uint32_t)k.tiles_m * (uint32_t)k.tiles_n * (uint32_t)split;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, s, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || split == 1) return e;
+  const int64_t threads = p.I * ((p.J + 3) / 4);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, s, p.partial, split,
+                     p.I, p.J, p.C, p.ldc, p.col_map, p.c_dtype == TJ2_BF16 ? 1 : 0, p.accumulate);
   return hipGetLastError();
 }
 

@@ -63,7 +63,14 @@ struct GemmParams {
   int64_t ldc;
   const int32_t* col_map;
   int accumulate;
+  float* partial;        // split-K workspace (fp32 [split][I][J]); NULL -> no split
+  size_t partial_bytes;
 };
+
+// Number of K splits used for a product of I x J outputs over nchunks 128-element
+// chunks, and the workspace it needs (0 when no split).
+int gemm_split(int64_t I, int64_t J, int64_t nchunks);
+size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t nchunks);
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 

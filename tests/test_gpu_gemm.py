@@ -78,3 +78,20 @@ def test_gemm_heterogeneous_scales():
     H.assert_q_equal(ga, ra); H.assert_q_equal(gb, rb)
     c = tj2.gemm(ga, gb).cpu().numpy()
     assert H.rel_fro(c, ogemm.gemm_nt_f64(ra, rb)) < 1e-5
+
+
+@pytest.mark.parametrize("I,J,K", [(256, 128, 8192), (200, 112, 4096), (16384 // 8, 112, 3072)])
+def test_gemm_split_k(I, J, K):
+    """Few output tiles and a long reduction: K is split over workgroups, partials reduced in order."""
+    ga, gb, ra, rb = _operands(I, J, K, seed=I + K)
+    ws = tj2.gemm_workspace(I, J, K)
+    assert ws is not None and ws.numel() > 0
+    ref = ogemm.gemm_nt_f64(ra, rb)
+    c = tj2.gemm(ga, gb, workspace=ws).cpu().numpy()
+    assert H.rel_fro(c, ref) < 1e-5
+    c1 = tj2.gemm(ga, gb, split_k=False).cpu().numpy()
+    assert H.rel_fro(c1, ref) < 1e-5
+    # scattered bf16 output through the reduce pass
+    perm = np.random.default_rng(1).permutation(J).astype(np.int32)
+    cb = tj2.gemm(ga, gb, out_dtype=torch.bfloat16, col_map=torch.from_numpy(perm).cuda(), workspace=ws)
+    assert H.bf16_ulp_ok(cb[:, perm], ref)

@@ -69,6 +69,13 @@ def test_linear_with_outliers():
     _check_linear(256, 384, K, seed=3, rht=True, plan_idx=outl, offset=16)
 
 
+def test_linear_long_reduction_split_k():
+    """M = 2048 tokens: the dW products (reduction over M) run split over K."""
+    K = 512
+    outl = calib.select_outliers(np.exp(np.random.default_rng(2).standard_normal(K) * 1.5), 0.1)
+    _check_linear(2048, 256, K, seed=5, rht=True, plan_idx=outl, offset=32)
+
+
 def test_linear_with_outliers_partial_blocks():
     K = 1024
     outl = calib.select_outliers(np.exp(np.random.default_rng(1).standard_normal(K) * 1.5), 0.1)  # 112 channels
