@@ -147,9 +147,10 @@ uint32_t tj2_rht_signs(uint64_t seed, uint64_t offset);
  *
  * rht != 0: apply the 16-wide Hadamard transform with sign mask rht_signs along
  * the grouping dimension before quantizing.
- * rounding TJ2_SR: element e (row-major index in the, possibly gathered, input)
- * draws 16 bits from Philox4x32-10 block e>>3 (counter (lo, hi of e>>3, lo, hi of
- * offset), key seed), word (e>>1)&3, half e&1.
+ * rounding TJ2_SR: element e (row-major index in the output, i.e. in the grouped
+ * layout: for TJ2_GROUP_COL, output row = input column) draws 16 bits from
+ * Philox4x32-10 block e>>3 (counter (lo, hi of e>>3, lo, hi of offset), key seed),
+ * word (e>>1)&3, half e&1 (0 = low half).
  *
  * out->fmt selects NVFP4 (scale = amax/2688 per 128, E4M3 round-up per 16) or FP8
  * (E4M3FN elements, scale = amax/448 per 128).  out->rows/len must match.

@@ -11,9 +11,11 @@ the standard Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw,
 * the key is bumped by (0x9E3779B9, 0xBB67AE85) between rounds.
 
 Per-element draw (reading): the element with row-major index e in the
-quantizer's *input* array uses block b = e >> 3 with counter
+quantizer's *output* array (the grouped layout: for a transposed 16x1
+quantization, output row = input column) uses block b = e >> 3 with counter
 (lo32 b, hi32 b, lo32 offset, hi32 offset) and key (lo32 seed, hi32 seed);
 its 16-bit draw is half (e & 1) (0 = low half) of output word (e >> 1) & 3.
+Every 16-element group therefore consumes exactly two whole Philox blocks.
 
 RHT signs for one GEMM pair: the low 16 bits of word 0 of the block with
 counter (0xFFFFFFFF, 0xFFFFFFFF, lo32 offset, hi32 offset); bit j set means

@@ -165,7 +165,8 @@ def quantize(x: np.ndarray, *, grouping: str = "row", fmt: str = "nvfp4", roundi
     grouping "col": groups run along R (16x1), the result is stored transposed, [C, R].
     rht_mask: if given, the 16-wide Hadamard transform with that sign mask is
     applied along the grouping dimension before quantizing.
-    Stochastic draws are indexed by the element's row-major position in x.
+    Stochastic draws are indexed by the element's row-major position in the
+    (grouped, possibly transposed) output.
     """
     x = np.asarray(x, dtype=np.float32)
     R, C = x.shape
@@ -176,10 +177,7 @@ def quantize(x: np.ndarray, *, grouping: str = "row", fmt: str = "nvfp4", roundi
     else:
         raise ValueError(grouping)
     y = rht.rht_along_last(xg, rht_mask) if rht_mask is not None else xg
-    u16 = None
-    if rounding == "sr":
-        draws = philox.sr_draws_for_shape((R, C), seed, offset)
-        u16 = draws if grouping == "row" else np.ascontiguousarray(draws.T)
+    u16 = philox.sr_draws_for_shape(y.shape, seed, offset) if rounding == "sr" else None
     if fmt == "nvfp4":
         return nvfp4_quantize_rows(y, rounding, u16)
     if fmt == "fp8":

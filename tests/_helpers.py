@@ -74,7 +74,7 @@ def oracle_cols(x_cols: np.ndarray, col_ids, n_cols_total: int, fmt: str, roundi
                 rht_mask=None) -> quant.QTensor:
     """Oracle column-grouped quantization of selected input columns (x_cols: [R, len(col_ids)]).
 
-    Returns the transposed rows [len(col_ids), R]; draws use the input index r * C + c.
+    Returns the transposed rows [len(col_ids), R]; draws use the output index c * R + r.
     """
     from oracle import rht
     y = np.ascontiguousarray(np.asarray(x_cols, dtype=np.float32).T)
@@ -83,8 +83,8 @@ def oracle_cols(x_cols: np.ndarray, col_ids, n_cols_total: int, fmt: str, roundi
     u16 = None
     if rounding == "sr":
         R = y.shape[1]
-        idx = (np.arange(R, dtype=np.uint64)[None, :] * np.uint64(n_cols_total)
-               + np.asarray(col_ids, dtype=np.uint64)[:, None])
+        idx = (np.asarray(col_ids, dtype=np.uint64)[:, None] * np.uint64(R)
+               + np.arange(R, dtype=np.uint64)[None, :])
         u16 = philox.sr_draws_u16(idx, seed, offset)
     if fmt == "nvfp4":
         return quant.nvfp4_quantize_rows(y, rounding, u16)

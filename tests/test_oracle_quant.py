@@ -106,7 +106,7 @@ def test_col_grouping_is_row_grouping_of_transpose():
     qc = quant.quantize(x, grouping="col", rounding="sr", rht_mask=0x1357, seed=9, offset=4)
     from oracle import rht
     y = rht.rht_along_last(np.ascontiguousarray(x.T), 0x1357)
-    u = philox.sr_draws_for_shape(x.shape, 9, 4).T
+    u = philox.sr_draws_for_shape(y.shape, 9, 4)  # draws follow the output (grouped) layout
     qr = quant.nvfp4_quantize_rows(y, "sr", u)
     assert np.array_equal(qc.codes, qr.codes) and np.array_equal(qc.s16, qr.s16)
     assert np.array_equal(qc.s128, qr.s128) and (qc.rows, qc.L) == (48, 96)
