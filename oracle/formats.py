@@ -17,9 +17,13 @@ Element rounding rules (readings where the pages are silent):
   whose mantissa bit is 0 (IEEE-style ties-to-even); the sign of the input is
   kept, so -0 encodes as code 8.
 * stochastic rounding (backward pass, E[round(x)] = x per section 2.A): with
-  lo <= |v| < hi the neighbouring grid values, round up iff a 16-bit uniform
-  draw u satisfies float(u) < (|v| - lo) / (hi - lo) * 65536.  Every step of
-  that expression is exact in fp32.
+  lo <= |v| < hi the neighbouring grid values and t = (|v| - lo) / (hi - lo)
+  * 65536 (exact in fp32), round up iff a 16-bit uniform draw u satisfies
+  u + floor(t) >= 65536, i.e. the fraction plus u / 65536 reaches the next
+  grid value.  P(up) = floor(t) / 65536, within 2^-16 of the exact fraction.
+  The pages fix only unbiasedness; this form of the rule is what gfx950's
+  stochastic conversion instructions compute when the draw occupies the top
+  16 bits of their random operand.
 """
 from __future__ import annotations
 
@@ -73,7 +77,7 @@ def e2m1_sr(v, u16) -> np.ndarray:
     with np.errstate(invalid="ignore", divide="ignore"):
         p = np.where(gap > 0, (a - lo_v) / np.where(gap > 0, gap, np.float32(1)), np.float32(0)).astype(np.float32)
     t = (p * np.float32(65536.0)).astype(np.float32)
-    up = np.asarray(u16, dtype=np.uint16).astype(np.float32) < t
+    up = np.asarray(u16, dtype=np.uint16).astype(np.int64) + np.floor(t).astype(np.int64) >= 65536
     idx = np.where(up, hi, lo).astype(np.uint8)
     return idx | (np.signbit(v).astype(np.uint8) << 3)
 
@@ -129,6 +133,6 @@ def e4m3_sr(v, u16) -> np.ndarray:
     with np.errstate(invalid="ignore", divide="ignore"):
         p = np.where(gap > 0, (a - lo_v) / np.where(gap > 0, gap, np.float32(1)), np.float32(0)).astype(np.float32)
     t = (p * np.float32(65536.0)).astype(np.float32)
-    up = np.asarray(u16, dtype=np.uint16).astype(np.float32) < t
+    up = np.asarray(u16, dtype=np.uint16).astype(np.int64) + np.floor(t).astype(np.int64) >= 65536
     idx = np.where(up, hi, lo).astype(np.uint8)
     return idx | (np.signbit(v).astype(np.uint8) << 7)

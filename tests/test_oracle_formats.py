@@ -81,11 +81,16 @@ def test_e2m1_sr_unbiased(x):
 
 
 def test_e2m1_sr_exact_probability():
-    # with all 65536 draws the up-fraction equals ceil(t)/65536 exactly
+    # with all 65536 draws the up-fraction equals floor(t)/65536 exactly, and the draws that
+    # round up are the largest ones (u >= 65536 - floor(t))
     u = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-    v = np.float32(1.2)  # between 1 and 1.5; p = 0.4 -> t = 26214.4
+    v = np.float32(1.2)  # between 1 and 1.5; fraction 0.4 -> t = 26214.4
     out = formats.e2m1_decode(formats.e2m1_sr(np.full(65536, v), u))
-    assert (out == 1.5).sum() == 26215
+    assert (out == 1.5).sum() == 26214
+    assert np.all(out[65536 - 26214:] == 1.5) and np.all(out[: 65536 - 26214] == 1.0)
+    # a fraction of exactly one half: the top half of the draws rounds up
+    out = formats.e2m1_decode(formats.e2m1_sr(np.full(65536, np.float32(1.25)), u))
+    assert (out == 1.5).sum() == 32768 and out[32768] == 1.5 and out[32767] == 1.0
 
 
 def test_e4m3_decode_vs_torch_and_constants():
