@@ -49,11 +49,13 @@ __device__ __forceinline__ void fwd_quant16(const float w[16], bool valid, uint3
   const float a_o = max8_lanes(a_j);
   GroupScale g = nvfp4_group_scale(a_o, a_j);
   const float s = e4m3_decode(g.s_code);
-  codes[0] = codes[1] = 0u;
+  float y[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) y[t] = (valid ? w[t] : 0.0f) * g.inv;
+  e2m1_rtn16(y, codes);
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    const uint32_t c = e2m1_rtn(nvfp4_scaled(valid ? w[t] : 0.0f, g.inv));
-    codes[t >> 3] |= c << (4 * (t & 7));
+    const uint32_t c = (codes[t >> 3] >> (4 * (t & 7))) & 15u;
     q[t] = (e2m1_val(c) * s) * g.S;
   }
   *s_code = g.s_code;

@@ -13,8 +13,8 @@
 //    16-row x 8-column patch (8 groups, one per column); the 8 lanes stacked
 //    along rows form a 128-row outer block.  A row of the patch is one 16-byte
 //    (bf16) load, so lanes with neighbouring column patches read contiguous
-//    128-byte segments; the Philox block of 8 consecutive input elements of a
-//    row is used whole by one lane.
+//    128-byte segments.  Stochastic draws follow the output position, so each
+//    16-element group uses two whole Philox blocks generated on the spot.
 #include "tj2_device.h"
 #include "tj2_internal.h"
 
@@ -68,22 +68,23 @@ __device__ __forceinline__ float e2m1_value(uint32_t n) {
 
 // ----------------------------------------------------------------------------
 // Per-group quantization of 16 values v (already transformed if RHT), given
-// the outer amax a_o.  Writes 8 bytes (NVFP4) or 16 bytes (FP8) of codes.
+// the outer amax a_o and, for SR, the draws r (top-aligned 16-bit).  Writes 8
+// bytes (NVFP4) or 16 bytes (FP8) of codes.
 // ----------------------------------------------------------------------------
 template <bool FP8OUT, bool SR>
-__device__ __forceinline__ void quantize_group(const float v[16], float a_o, float a_j, const uint32_t u[16],
+__device__ __forceinline__ void quantize_group(const float v[16], float a_o, float a_j, const uint32_t r[16],
                                                uint32_t codes[4], uint32_t* s_code, float* S_out) {
   if (!FP8OUT) {
     GroupScale g = nvfp4_group_scale(a_o, a_j);
     *s_code = g.s_code;
     *S_out = g.S;
-    codes[0] = codes[1] = 0u;
+    // both conversions saturate at +-6 and y * 0 keeps the sign of y, so an
+    // empty group (inv = 0) encodes signed zeros
+    float y[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float y = nvfp4_scaled(v[t], g.inv);
-      uint32_t c = SR ? e2m1_sr(y, u[t]) : e2m1_rtn(y);
-      codes[t >> 3] |= c << (4 * (t & 7));
-    }
+    for (int t = 0; t < 16; ++t) y[t] = v[t] * g.inv;
+    if (SR) e2m1_sr16(y, r, codes);
+    else e2m1_rtn16(y, codes);
   } else {
     float S = 0.0f, inv = 0.0f;
     if (a_o >= kTiny) {
@@ -92,12 +93,15 @@ __device__ __forceinline__ void quantize_group(const float v[16], float a_o, flo
     }
     *s_code = 0u;
     *S_out = S;
-    codes[0] = codes[1] = codes[2] = codes[3] = 0u;
+    float y[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float y = fp8_scaled(v[t], inv);
-      uint32_t c = SR ? e4m3_sr(y, u[t]) : e4m3_rne(y);
-      codes[t >> 2] |= c << (8 * (t & 3));
+    for (int t = 0; t < 16; ++t) y[t] = fp8_scaled(v[t], inv);
+    if (SR) {
+      e4m3_sr16(y, r, codes);
+    } else {
+      codes[0] = codes[1] = codes[2] = codes[3] = 0u;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) codes[t >> 2] |= e4m3_rne(y[t]) << (8 * (t & 3));
     }
   }
 }
@@ -255,25 +259,14 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
   if (c0 >= p.cols) return;  // all 8 lanes of this column patch exit together
   const int64_t r0 = (int64_t)blockIdx.y * 128 + rs * 16;
   const bool valid = r0 < p.rows;
-  const int64_t R = p.rows, C = p.cols;
+  const int64_t R = p.rows;
 
   ColPatch<IN> patch;
   if (valid) patch.load(p, r0, c0);
 
-  uint32_t words[16][4];
-  if (SR && valid) {
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint64_t b = ((uint64_t)(r0 + t) * (uint64_t)C + (uint64_t)c0) >> 3;
-      u32x4 w = philox10((uint32_t)b, (uint32_t)(b >> 32), (uint32_t)p.offset, (uint32_t)(p.offset >> 32),
-                         (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-      words[t][0] = w.x; words[t][1] = w.y; words[t][2] = w.z; words[t][3] = w.w;
-    }
-  }
-
   const QView& o = p.out;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  static_for<8>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
     float v[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) v[t] = valid ? patch.get(t, k) : 0.0f;
@@ -282,15 +275,17 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
     const float a_o = max8_lanes(a_j);
+    const int64_t orow = c0 + k;  // output row = input column
     uint32_t u[16];
     if (SR && valid) {
-#pragma unroll
-      for (int t = 0; t < 16; ++t) u[t] = (words[t][k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+      // draws follow the output position orow * R + r0 + t: two whole Philox blocks
+      const uint64_t b = ((uint64_t)orow * (uint64_t)R + (uint64_t)r0) >> 3;
+      draws8(b, p.seed, p.offset, u);
+      draws8(b + 1, p.seed, p.offset, u + 8);
     }
     uint32_t codes[4], s_code;
     float S;
     quantize_group<FP8OUT, SR>(v, a_o, a_j, u, codes, &s_code, &S);
-    const int64_t orow = c0 + k;
     if (!FP8OUT) {
       *reinterpret_cast<uint2*>(o.codes + orow * o.ld_codes + (r0 >> 1)) = make_uint2(codes[0], codes[1]);
       o.s16[orow * o.ld_s16 + (r0 >> 4)] = (uint8_t)s_code;
@@ -298,8 +293,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
       *reinterpret_cast<uint4*>(o.codes + orow * o.ld_codes + r0) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
     }
     if (rs == 0) o.s128[orow * o.ld_s128 + blockIdx.y] = S;
-  }
-  (void)R;
+  });
 }
 
 template <int IN, bool GATHER, bool FP8OUT, bool SR, bool RHT>

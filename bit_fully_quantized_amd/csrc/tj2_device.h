@@ -9,7 +9,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace tj2 {
+
+// Compile-time loop: f(std::integral_constant<int, 0>{}) ... f(<N-1>), so that
+// register arrays are only ever indexed with constants.
+template <class F, int... Ks>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Ks...>) {
+  (f(std::integral_constant<int, Ks>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -67,29 +81,60 @@ __device__ __forceinline__ uint32_t e2m1_rtn(float v) {
   return idx | sign;
 }
 
-// Stochastic rounding with a 16-bit draw u: up iff float(u) < (|v|-lo)/(hi-lo)*65536.
-__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u) {
-  uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
-  float a = fabsf(v);
-  float lo, scale;
-  uint32_t idx;
-  if (a < 1.0f) {
-    lo = floorf(a * 2.0f) * 0.5f;
-    idx = (uint32_t)(lo * 2.0f);
-    scale = 131072.0f;                  // 65536 / 0.5
-  } else {
-    uint32_t b = __float_as_uint(a) & 0xFFC00000u;  // truncate to one mantissa bit
-    lo = __uint_as_float(b);
-    idx = (b >> 22) - 252u;
-    scale = __uint_as_float((271u - (b >> 23)) << 23);  // 65536 / 2^(e-1)
-  }
-  float t = (a - lo) * scale;           // exact
-  uint32_t up = ((float)u < t && idx < 7u) ? 1u : 0u;
-  return (idx + up) | sign;
+// Round-to-nearest of 16 scaled values (v = y * inv, unclamped) into 8 bytes of
+// E2M1 codes (element 2i in the low nibble of byte i).  gfx950's
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to nearest-even, saturates at
+// +-6 (the clamp) and keeps the sign of zero: the same rule as e2m1_rtn, checked
+// exhaustively against it.
+__device__ __forceinline__ void e2m1_rtn16(const float y[16], uint32_t out[2]) {
+  uint32_t c0 = 0u, c1 = 0u;
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, y[0], y[1], 1.0f, 0);
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, y[2], y[3], 1.0f, 1);
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, y[4], y[5], 1.0f, 2);
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, y[6], y[7], 1.0f, 3);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, y[8], y[9], 1.0f, 0);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, y[10], y[11], 1.0f, 1);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, y[12], y[13], 1.0f, 2);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, y[14], y[15], 1.0f, 3);
+  out[0] = c0;
+  out[1] = c1;
+}
+
+// Stochastic rounding of 16 scaled values with 16-bit draws r[t] held in the
+// top half of a 32-bit word (low half zero).  Rule: with t = 65536 * (position of
+// |y| inside its grid gap), round up iff u + floor(t) >= 65536.  gfx950's
+// v_cvt_scalef32_sr_pk_fp4_f32 rounds up iff the gap fraction plus r / 2^32
+// reaches 1, which with r = u << 16 is exactly that rule (checked bit-exactly
+// at every threshold against the CPU rule); it also saturates at +-6.  One
+// element per instruction (the second slot converts 0.0, code 0), so every
+// element gets its own draw.  The instruction leaves bytes 1..3 of its result
+// undefined (it does not merge into an old value), so only byte 0 is used:
+// pairs are merged with a shift-or, then bytes are gathered with v_perm.
+__device__ __forceinline__ uint32_t e2m1_sr1(float y, uint32_t r) {
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, float2_t{y, 0.0f}, r, 1.0f, 0);
+}
+
+__device__ __forceinline__ uint32_t e2m1_sr8(const float* y, const uint32_t* r) {
+  // byte 0 of each pair word = code(2i) | code(2i+1) << 4; upper bytes are don't-care
+  const uint32_t p0 = e2m1_sr1(y[0], r[0]) | (e2m1_sr1(y[1], r[1]) << 4);
+  const uint32_t p1 = e2m1_sr1(y[2], r[2]) | (e2m1_sr1(y[3], r[3]) << 4);
+  const uint32_t p2 = e2m1_sr1(y[4], r[4]) | (e2m1_sr1(y[5], r[5]) << 4);
+  const uint32_t p3 = e2m1_sr1(y[6], r[6]) | (e2m1_sr1(y[7], r[7]) << 4);
+  // v_perm_b32(a, b, sel): selector bytes 0-3 pick bytes of b, 4-7 bytes of a
+  const uint32_t lo = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);  // [p0.b0, p1.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);  // [0, 0, p2.b0, p3.b0]
+  return lo | hi;
+}
+
+__device__ __forceinline__ void e2m1_sr16(const float y[16], const uint32_t r[16], uint32_t out[2]) {
+  out[0] = e2m1_sr8(y, r);
+  out[1] = e2m1_sr8(y + 8, r + 8);
 }
 
 // ---------------------------------------------------------------------------
-// E4M3FN element rounding (|v| <= 448) for the FP8 outlier channels.
+// E4M3FN element rounding (|v| <= 448) for the FP8 outlier channels:
+// nearest, ties to even code, sign kept.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t e4m3_rne(float v) {
   uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
@@ -100,23 +145,19 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
   return sign | ((b >> 20) - 960u);
 }
 
-__device__ __forceinline__ uint32_t e4m3_sr(float v, uint32_t u) {
-  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  float a = fabsf(v);
-  uint32_t code;
-  float t;
-  if (a < 0x1p-6f) {
-    float x = a * 512.0f;
-    float lo = floorf(x);
-    code = (uint32_t)lo;
-    t = (x - lo) * 65536.0f;
-  } else {
-    uint32_t b = __float_as_uint(a) & 0xFFF00000u;
-    code = (b >> 20) - 960u;
-    t = (a - __uint_as_float(b)) * __uint_as_float((273u - (b >> 23)) << 23);  // 65536 / 2^(e-3)
+// Same rule on the E4M3 grid with v_cvt_scalef32_sr_fp8_f32 (one element per
+// instruction, byte `sel` of the destination).  The instruction does not
+// saturate, so inputs are clamped to +-448 by the caller.
+__device__ __forceinline__ void e4m3_sr16(const float y[16], const uint32_t r[16], uint32_t out[4]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t d = 0u;
+    d = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d, y[4 * w + 0], r[4 * w + 0], 1.0f, 0);
+    d = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d, y[4 * w + 1], r[4 * w + 1], 1.0f, 1);
+    d = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d, y[4 * w + 2], r[4 * w + 2], 1.0f, 2);
+    d = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(d, y[4 * w + 3], r[4 * w + 3], 1.0f, 3);
+    out[w] = d;
   }
-  uint32_t up = ((float)u < t && code < 0x7Eu) ? 1u : 0u;
-  return sign | (code + up);
 }
 
 // ---------------------------------------------------------------------------
@@ -144,14 +185,15 @@ __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2,
   return {c0, c1, c2, c3};
 }
 
-// Eight 16-bit draws of the 8-element block b.
-__device__ __forceinline__ void draws8(uint64_t b, uint64_t seed, uint64_t offset, uint32_t u[8]) {
+// Eight 16-bit draws of the 8-element block b, each placed in the top half of
+// a 32-bit word (the form the stochastic conversions take).
+__device__ __forceinline__ void draws8(uint64_t b, uint64_t seed, uint64_t offset, uint32_t r[8]) {
   u32x4 w = philox10((uint32_t)b, (uint32_t)(b >> 32), (uint32_t)offset, (uint32_t)(offset >> 32),
                      (uint32_t)seed, (uint32_t)(seed >> 32));
-  u[0] = w.x & 0xFFFFu; u[1] = w.x >> 16;
-  u[2] = w.y & 0xFFFFu; u[3] = w.y >> 16;
-  u[4] = w.z & 0xFFFFu; u[5] = w.z >> 16;
-  u[6] = w.w & 0xFFFFu; u[7] = w.w >> 16;
+  r[0] = w.x << 16; r[1] = w.x & 0xFFFF0000u;
+  r[2] = w.y << 16; r[3] = w.y & 0xFFFF0000u;
+  r[4] = w.z << 16; r[5] = w.z & 0xFFFF0000u;
+  r[6] = w.w << 16; r[7] = w.w & 0xFFFF0000u;
 }
 
 // ---------------------------------------------------------------------------
@@ -214,14 +256,13 @@ __device__ __forceinline__ GroupScale nvfp4_group_scale(float a_o, float a_j) {
   return g;
 }
 
-// Scaled element: clamp(y * inv, -6, 6); an empty group keeps only the sign.
+// Scaled element: clamp(y * inv, -6, 6).  An empty group has inv = 0, and
+// y * 0 is a zero with the sign of y, so it encodes the sign only.
 __device__ __forceinline__ float nvfp4_scaled(float y, float inv) {
-  if (inv == 0.0f) return __uint_as_float(__float_as_uint(y) & 0x80000000u);
   return fminf(fmaxf(y * inv, -6.0f), 6.0f);
 }
 
 __device__ __forceinline__ float fp8_scaled(float y, float inv) {
-  if (inv == 0.0f) return __uint_as_float(__float_as_uint(y) & 0x80000000u);
   return fminf(fmaxf(y * inv, -448.0f), 448.0f);
 }
 

@@ -152,3 +152,37 @@ def test_sr_unbiased_on_gpu():
     err_sr = np.abs(acc / n - x).mean()
     err_rtn = np.abs(quant.dequantize(quant.quantize(x)) - x).mean()
     assert err_sr < 0.2 * err_rtn
+
+
+def test_rtn_exhaustive_unit_step():
+    """Every fp32 magnitude in [2^-8, 6], both signs, placed where the element step is exactly 1
+    (outer max 2688 -> S = 1; every test group also holds a 6 -> s = 1): each code must equal
+    round-to-nearest-even onto the E2M1 grid, computed independently with torch.round (half to even)."""
+    lo = int(np.float32(2.0 ** -8).view(np.int32))
+    hi = int(np.float32(6.0).view(np.int32))
+    bits = torch.arange(lo, hi + 1, dtype=torch.int64, device="cuda").to(torch.int32)
+    vals = bits.view(torch.float32)
+    vals = torch.where(torch.arange(vals.numel(), device="cuda") % 2 == 0, vals, -vals)
+    per_row = 7 * 15
+    rows = (vals.numel() + per_row - 1) // per_row
+    X = torch.zeros(rows, 128, dtype=torch.float32, device="cuda")
+    X[:, 0] = 2688.0
+    slots = torch.zeros(rows * per_row, dtype=torch.float32, device="cuda")
+    slots[: vals.numel()] = vals
+    body = X[:, 16:].view(rows, 7, 16)
+    body[:, :, 0] = 6.0
+    body[:, :, 1:] = slots.view(rows, 7, 15)
+    q = tj2.quantize(X)
+    assert torch.all(q.scale128[:, 0] == 1.0)
+    assert torch.all(q.scale16[:, 1:8] == 0x38)  # E4M3 1.0
+    c = q.codes[:, :64].view(rows, 64)
+    nib = torch.stack([c & 15, c >> 4], dim=-1).view(rows, 128)[:, 16:].reshape(rows, 7, 16)[:, :, 1:].reshape(-1)
+    nib = nib[: vals.numel()].to(torch.int64)
+    a = vals.abs().double()
+    step = torch.where(a < 2, 0.5, torch.where(a < 4, 1.0, 2.0))
+    ref_mag = torch.clamp(torch.round(a / step) * step, max=6.0)
+    grid = torch.tensor([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=torch.float64, device="cuda")
+    ref_idx = torch.searchsorted(grid, ref_mag)
+    ref = ref_idx | (torch.signbit(vals).to(torch.int64) << 3)
+    bad = (nib != ref).sum().item()
+    assert bad == 0, f"{bad} mismatches"
