@@ -173,7 +173,7 @@ def quant_sweep(tj2, reps=24, nbuf=8):
     return res, bytes_per_call
 
 
-def cpu_baseline(M=256, K=1024, N=3072, p=0.10):
+def cpu_baseline(M=4096, K=1024, N=3072, p=0.10):
     """The oracle (fp64 products, numpy quantizers) on one QKV-shaped linear with M tokens."""
     import numpy as np
     from threadpoolctl import threadpool_info
