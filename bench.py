@@ -106,10 +106,18 @@ def time_launches(fn, reps):
     return s.elapsed_time(e) / 1e3 / reps
 
 
+def q_bytes(q):
+    """Algorithmic bytes of a packed operand: codes, inner and outer scales of its len (not the padding)."""
+    per = 0.5 + 1 / 16 + 4 / 128 if q.scale16 is not None else 1 + 4 / 128
+    return q.rows * q.len * per
+
+
 def gemm_roofline(tj2, lins, layers, M, reps=10):
-    """Average duration and flops of the product launches of one step (one layer's linears x layers)."""
+    """Average duration, flops and algorithmic bytes of the product launches of one step
+    (one layer's five linears, each product weighted by the number of layers)."""
     tot_flops = 0.0
     tot_time = 0.0
+    tot_bytes = 0.0
     launches = 0
     per = {}
     for li in lins[:5]:
@@ -117,19 +125,72 @@ def gemm_roofline(tj2, lins, layers, M, reps=10):
                                    keep_operands=True)
         no, K1, K, N = li.plan.n, li.K1, li.K, li.N
         calls = [
-            ("fwd", 2.0 * M * N * K, lambda: tj2.gemm(li.Xq, li.Wq, li.X8, li.W8, out=li.Y)),
-            ("dX", 2.0 * M * K1 * N, lambda: tj2.gemm(ops["dYq"], ops["Wt"], out=li.dX, col_map=li.plan.rest)),
-            ("dX8", 2.0 * M * no * N, lambda: tj2.gemm(ops["dYq"], ops["W8t"], out=li.dX, col_map=li.plan.outliers)),
-            ("dW", 2.0 * N * K1 * M, lambda: tj2.gemm(ops["dYt"], ops["Xt"], out=li.dW, col_map=li.plan.rest)),
-            ("dW8", 2.0 * N * no * M, lambda: tj2.gemm(ops["dYt"], ops["X8t"], out=li.dW, col_map=li.plan.outliers)),
+            ("fwd", 2.0 * M * N * K, q_bytes(li.Xq) + q_bytes(li.Wq) + q_bytes(li.X8) + q_bytes(li.W8) + 2 * M * N,
+             lambda: tj2.gemm(li.Xq, li.Wq, li.X8, li.W8, out=li.Y)),
+            ("dX", 2.0 * M * K1 * N, q_bytes(ops["dYq"]) + q_bytes(ops["Wt"]) + 2 * M * K1,
+             lambda: tj2.gemm(ops["dYq"], ops["Wt"], out=li.dX, col_map=li.plan.rest)),
+            ("dX8", 2.0 * M * no * N, q_bytes(ops["dYq"]) + q_bytes(ops["W8t"]) + 2 * M * no,
+             lambda: tj2.gemm(ops["dYq"], ops["W8t"], out=li.dX, col_map=li.plan.outliers)),
+            ("dW", 2.0 * N * K1 * M, q_bytes(ops["dYt"]) + q_bytes(ops["Xt"]) + 4 * N * K1,
+             lambda: tj2.gemm(ops["dYt"], ops["Xt"], out=li.dW, col_map=li.plan.rest)),
+            ("dW8", 2.0 * N * no * M, q_bytes(ops["dYt"]) + q_bytes(ops["X8t"]) + 4 * N * no,
+             lambda: tj2.gemm(ops["dYt"], ops["X8t"], out=li.dW, col_map=li.plan.outliers)),
         ]
-        for name, fl, fn in calls:
+        for name, fl, by, fn in calls:
             t = time_launches(fn, reps)
             per[f"{li.name}.{name}"] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 1)}
             tot_flops += fl * layers
             tot_time += t * layers
+            tot_bytes += by * layers
             launches += layers
-    return tot_flops, tot_time, launches, per
+    return tot_flops, tot_time, tot_bytes, launches, per
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain elementwise copy kernel of known size (bf16 negation, 1 GiB read + 1 GiB written per launch).
+
+    Under `rocprofv3 --pmc FETCH_SIZE` / `WRITE_SIZE` its per-dispatch counters give the factor between
+    the counters and bytes moved, which scales the product kernel's counters into HBM bytes."""
+    import torch
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    del x, y
+    torch.cuda.empty_cache()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_kernel_olmo370m_linears_traffic.txt")
+GEMM_SOURCES = [os.path.join(ROOT, "bit_fully_quantized_amd", "csrc", f)
+                for f in ("gemm.hip", "tj2_device.h", "tj2_internal.h")]
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per product launch from the committed counter summary, or None when it is missing or
+    was taken on a different version of the product kernel's sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def quant_sweep(tj2, reps=24, nbuf=8):
@@ -173,7 +234,7 @@ def quant_sweep(tj2, reps=24, nbuf=8):
     return res, bytes_per_call
 
 
-def cpu_baseline(M=4096, K=1024, N=3072, p=0.10):
+def cpu_baseline(M=8192, K=1024, N=3072, p=0.10):
     """The oracle (fp64 products, numpy quantizers) on one QKV-shaped linear with M tokens."""
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -247,8 +308,9 @@ def main():
     log(f"step {step_s * 1e3:.2f} ms (events {step_ev * 1e3:.2f} ms)")
 
     log("product roofline pass")
-    g_flops, g_time, g_launches, per = gemm_roofline(tj2, lins, layers, M)
+    g_flops, g_time, g_bytes, g_launches, per = gemm_roofline(tj2, lins, layers, M)
     achieved = g_flops / g_time / 1e12
+    copy_calibration()
     log("OsciReset pass")
     n_params = sum(li.N * li.K for li in lins)
     osci_t = time_launches(lambda: [tj2.osci_reset_step(li.W, *li.state, mode=tj2.OSCI_ACCUM, tau=4.0)
@@ -283,7 +345,9 @@ def main():
         "roofline": {
             "kernel": "gemm_nt_kernel (packed NVFP4/FP8 products: fwd, dX, dW)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",
+            "algorithmic_bytes_per_launch": round(g_bytes / g_launches),
             "avg_launch_us": round(g_time / g_launches * 1e6, 2), "launches_per_step": g_launches,
             "gemm_share_of_step": round(g_time / step_s, 3), "per_launch": per,
         },

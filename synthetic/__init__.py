@@ -23,9 +23,14 @@ import numpy as np
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round finite fp32 values to bf16 (round-to-nearest-even); returns uint16 bits."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    bias = np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))
-    return ((b + bias) >> np.uint64(16)).astype(np.uint16)
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    out = np.empty(b.shape, np.uint16)
+    flat_b, flat_o = b.reshape(-1), out.reshape(-1)
+    step = 1 << 22  # chunks keep the temporaries small; finite inputs never overflow 32 bits
+    for i in range(0, flat_b.size, step):
+        c = flat_b[i:i + step]
+        flat_o[i:i + step] = (c + (np.uint32(0x7FFF) + ((c >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    return out
 
 
 def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
