@@ -35,7 +35,7 @@ namespace tj2 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int BM = 256, BN = 128, BK = 128;
 constexpr int LDS_STRIDE = BK + 8;  // f16 elements per LDS row
 constexpr int F_NONE = -1;
 
@@ -66,196 +66,336 @@ struct GemmKArgs {
   int accumulate;
 };
 
-// Packed slice of one thread: 64 consecutive K elements of one operand row.
+// Packed slice of one thread, in a layout shared by both formats:
+//  * A operand: 64 consecutive K elements (half of a 128-chunk) of one row.
+//    NVFP4 uses q[0..1] (codes) and q[2].x (four inner scales); FP8 q[0..3].
+//  * B operand: 32 consecutive K elements (a quarter chunk) of one row.
+//    NVFP4 uses q[0] (codes) and q[1].x (two inner scales); FP8 q[0..1].
+struct Slice {
+  uint4 q[4];
+  float S;  // outer scale of the chunk
+};
+
 template <int F>
 struct Op;
 
 template <>
 struct Op<TJ2_NVFP4> {
-  struct Slice {
-    uint4 c0, c1;   // 64 E2M1 codes
-    uint32_t s16;   // four E4M3 inner scales
-    float S;        // outer scale of the chunk
-  };
-  static __device__ __forceinline__ void load(const OperandK& o, int64_t row, int kc, int half, Slice& s) {
-    const uint8_t* cp = o.codes + row * o.ld_codes + kc * 64 + half * 32;
-    s.c0 = *reinterpret_cast<const uint4*>(cp);
-    s.c1 = *reinterpret_cast<const uint4*>(cp + 16);
-    s.s16 = *reinterpret_cast<const uint32_t*>(o.s16 + row * o.ld_s16 + kc * 8 + half * 4);
-    s.S = o.s128[row * o.ld_s128 + kc];
+  // rn = row * (outer blocks per row): codes at rn * 64 bytes, inner scales at rn * 8, outer at rn
+  static __device__ __forceinline__ void load_half(const OperandK& o, uint32_t rn, int kc, int half, Slice& s) {
+    const uint8_t* cp = o.codes + (size_t)kc * 64 + (rn * 64 + half * 32);
+    s.q[0] = *reinterpret_cast<const uint4*>(cp);
+    s.q[1] = *reinterpret_cast<const uint4*>(cp + 16);
+    s.q[2].x = *reinterpret_cast<const uint32_t*>(o.s16 + (size_t)kc * 8 + (rn * 8 + half * 4));
+    s.S = (o.s128 + kc)[rn];
+  }
+  static __device__ __forceinline__ void load_quarter(const OperandK& o, uint32_t rn, int kc, int qt, Slice& s) {
+    s.q[0] = *reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 64 + (rn * 64 + qt * 16));
+    s.q[1].x = *reinterpret_cast<const uint16_t*>(o.s16 + (size_t)kc * 8 + (rn * 8 + qt * 2));
+    s.S = (o.s128 + kc)[rn];
   }
   template <int BYTE>
   static __device__ __forceinline__ uint32_t q2(uint32_t word, half2_t sc) {
     half2_t q = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, BYTE) * sc;
     return __builtin_bit_cast(uint32_t, q);
   }
-  // 64 f16 values q * s (exact) to dst (16-byte aligned)
-  static __device__ __forceinline__ void decode(const Slice& s, _Float16* dst) {
-    uint4* out = reinterpret_cast<uint4*>(dst);
-    const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.s16, 1.0f, false);
-    const half2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.s16, 1.0f, true);
-    const half2_t sg[4] = {half2_t{s01[0], s01[0]}, half2_t{s01[1], s01[1]}, half2_t{s23[0], s23[0]},
-                           half2_t{s23[1], s23[1]}};
-    const uint32_t w[8] = {s.c0.x, s.c0.y, s.c0.z, s.c0.w, s.c1.x, s.c1.y, s.c1.z, s.c1.w};
+  // 8 codes (one word) times their inner scale: 8 exact f16 values
+  static __device__ __forceinline__ half8_t dec8(uint32_t w, half2_t sc) {
+    return __builtin_bit_cast(half8_t, make_uint4(q2<0>(w, sc), q2<1>(w, sc), q2<2>(w, sc), q2<3>(w, sc)));
+  }
+  static __device__ __forceinline__ void scales(uint32_t s16, half2_t (&sg)[4]) {
+    const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s16, 1.0f, false);
+    const half2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s16, 1.0f, true);
+    sg[0] = half2_t{s01[0], s01[0]};
+    sg[1] = half2_t{s01[1], s01[1]};
+    sg[2] = half2_t{s23[0], s23[0]};
+    sg[3] = half2_t{s23[1], s23[1]};
+  }
+  // piecewise decode used by the pipelined kernel: scale preparation, then one
+  // 8-element fragment (A half slice) or unit (B quarter slice) at a time
+  static __device__ __forceinline__ void prep_a(const Slice& s, half2_t (&sg)[4]) { scales(s.q[2].x, sg); }
+  static __device__ __forceinline__ void prep_b(const Slice& s, half2_t (&sg)[4]) { scales(s.q[1].x, sg); }
+  template <int F>
+  static __device__ __forceinline__ half8_t frag_a(const Slice& s, const half2_t (&sg)[4]) {
+    const uint4& v = s.q[F >> 2];
+    const uint32_t w = (F & 3) == 0 ? v.x : (F & 3) == 1 ? v.y : (F & 3) == 2 ? v.z : v.w;
+    return dec8(w, sg[F >> 1]);
+  }
+  template <int U>
+  static __device__ __forceinline__ half8_t unit_b(const Slice& s, const half2_t (&sg)[4]) {
+    const uint4& v = s.q[0];
+    const uint32_t w = U == 0 ? v.x : U == 1 ? v.y : U == 2 ? v.z : v.w;
+    return dec8(w, sg[U >> 1]);
+  }
+  // half slice -> fragments f[i] = elements 8i..8i+7
+  static __device__ __forceinline__ void decode_half(const Slice& s, half8_t (&f)[8]) {
+    half2_t sg[4];
+    scales(s.q[2].x, sg);
+    const uint32_t w[8] = {s.q[0].x, s.q[0].y, s.q[0].z, s.q[0].w, s.q[1].x, s.q[1].y, s.q[1].z, s.q[1].w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const half2_t sc = sg[i >> 1];
-      out[i] = make_uint4(q2<0>(w[i], sc), q2<1>(w[i], sc), q2<2>(w[i], sc), q2<3>(w[i], sc));
-    }
+    for (int i = 0; i < 8; ++i) f[i] = dec8(w[i], sg[i >> 1]);
+  }
+  // quarter slice -> 32 f16 values at dst (16-byte aligned)
+  static __device__ __forceinline__ void decode_quarter(const Slice& s, _Float16* dst) {
+    half2_t sg[4];
+    scales(s.q[1].x, sg);
+    half8_t* out = reinterpret_cast<half8_t*>(dst);
+    out[0] = dec8(s.q[0].x, sg[0]);
+    out[1] = dec8(s.q[0].y, sg[0]);
+    out[2] = dec8(s.q[0].z, sg[1]);
+    out[3] = dec8(s.q[0].w, sg[1]);
   }
 };
 
 template <>
 struct Op<TJ2_FP8> {
-  struct Slice {
-    uint4 c[4];     // 64 E4M3 codes
-    float S;
-  };
-  static __device__ __forceinline__ void load(const OperandK& o, int64_t row, int kc, int half, Slice& s) {
-    const uint4* p = reinterpret_cast<const uint4*>(o.codes + row * o.ld_codes + kc * 128 + half * 64);
+  // rn = row * (outer blocks per row): codes at rn * 128 bytes, outer scales at rn
+  static __device__ __forceinline__ void load_half(const OperandK& o, uint32_t rn, int kc, int half, Slice& s) {
+    const uint4* p = reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 128 + (rn * 128 + half * 64));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s.c[i] = p[i];
-    s.S = o.s128[row * o.ld_s128 + kc];
+    for (int i = 0; i < 4; ++i) s.q[i] = p[i];
+    s.S = (o.s128 + kc)[rn];
+  }
+  static __device__ __forceinline__ void load_quarter(const OperandK& o, uint32_t rn, int kc, int qt, Slice& s) {
+    const uint4* p = reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 128 + (rn * 128 + qt * 32));
+    s.q[0] = p[0];
+    s.q[1] = p[1];
+    s.S = (o.s128 + kc)[rn];
   }
   template <bool HI>
   static __device__ __forceinline__ uint32_t e2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
   }
-  static __device__ __forceinline__ void decode(const Slice& s, _Float16* dst) {
-    uint4* out = reinterpret_cast<uint4*>(dst);
+  static __device__ __forceinline__ half8_t dec8(uint32_t w0, uint32_t w1) {
+    return __builtin_bit_cast(half8_t, make_uint4(e2<false>(w0), e2<true>(w0), e2<false>(w1), e2<true>(w1)));
+  }
+  static __device__ __forceinline__ void prep_a(const Slice&, half2_t (&)[4]) {}
+  static __device__ __forceinline__ void prep_b(const Slice&, half2_t (&)[4]) {}
+  template <int F>
+  static __device__ __forceinline__ half8_t frag_a(const Slice& s, const half2_t (&)[4]) {
+    const uint4& v = s.q[F >> 1];
+    return (F & 1) ? dec8(v.z, v.w) : dec8(v.x, v.y);
+  }
+  template <int U>
+  static __device__ __forceinline__ half8_t unit_b(const Slice& s, const half2_t (&)[4]) {
+    const uint4& v = s.q[U >> 1];
+    return (U & 1) ? dec8(v.z, v.w) : dec8(v.x, v.y);
+  }
+  static __device__ __forceinline__ void decode_half(const Slice& s, half8_t (&f)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      out[2 * i] = make_uint4(e2<false>(s.c[i].x), e2<true>(s.c[i].x), e2<false>(s.c[i].y), e2<true>(s.c[i].y));
-      out[2 * i + 1] = make_uint4(e2<false>(s.c[i].z), e2<true>(s.c[i].z), e2<false>(s.c[i].w), e2<true>(s.c[i].w));
+      f[2 * i] = dec8(s.q[i].x, s.q[i].y);
+      f[2 * i + 1] = dec8(s.q[i].z, s.q[i].w);
     }
   }
-};
-
-struct TileCtx {
-  int64_t rowA, rowB;   // clamped source rows of this thread's loads
-  int lr, lh, lane, wm, wn;
-  _Float16* lds_a;
-  _Float16* lds_b;
-  float* sa;
-  float* sb;
+  static __device__ __forceinline__ void decode_quarter(const Slice& s, _Float16* dst) {
+    half8_t* out = reinterpret_cast<half8_t*>(dst);
+    out[0] = dec8(s.q[0].x, s.q[0].y);
+    out[1] = dec8(s.q[0].z, s.q[0].w);
+    out[2] = dec8(s.q[1].x, s.q[1].y);
+    out[3] = dec8(s.q[1].z, s.q[1].w);
+  }
 };
 
 __device__ __forceinline__ half8_t ld8(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
 
-// MFMA over one decoded chunk (nk 16-deep steps) and promotion into acc.
-__device__ __forceinline__ void chunk_mfma(const TileCtx& t, int nk, float16_t (&acc)[2][2]) {
-  const _Float16* ab = t.lds_a + (t.wm * 64 + (t.lane & 31)) * LDS_STRIDE + (t.lane >> 5) * 8;
-  const _Float16* bb = t.lds_b + (t.wn * 64 + (t.lane & 31)) * LDS_STRIDE + (t.lane >> 5) * 8;
-  float16_t part[2][2];
-  if (nk == BK / 16) {
-    half8_t fa[2][2], fb[2][2];
-    fa[0][0] = ld8(ab);
-    fa[0][1] = ld8(ab + 32 * LDS_STRIDE);
-    fb[0][0] = ld8(bb);
-    fb[0][1] = ld8(bb + 32 * LDS_STRIDE);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cb = ks & 1, nb = cb ^ 1;
-      if (ks + 1 < BK / 16) {
-        fa[nb][0] = ld8(ab + (ks + 1) * 16);
-        fa[nb][1] = ld8(ab + 32 * LDS_STRIDE + (ks + 1) * 16);
-        fb[nb][0] = ld8(bb + (ks + 1) * 16);
-        fb[nb][1] = ld8(bb + 32 * LDS_STRIDE + (ks + 1) * 16);
-      }
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn)
-          part[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[cb][tm], fb[cb][tn],
-                                                                ks == 0 ? float16_t{} : part[tm][tn], 0, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
-        part[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ld8(ab + tm * 32 * LDS_STRIDE),
-                                                              ld8(bb + tn * 32 * LDS_STRIDE), float16_t{}, 0, 0, 0);
-    for (int ks = 1; ks < nk; ++ks) {
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn)
-          part[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ld8(ab + tm * 32 * LDS_STRIDE + ks * 16),
-                                                                ld8(bb + tn * 32 * LDS_STRIDE + ks * 16),
-                                                                part[tm][tn], 0, 0, 0);
-    }
-  }
-  // promotion: acc += part * (S_A[row] * S_B[col]); rows t&3 of a lane are consecutive
-  float rb[2];
-#pragma unroll
-  for (int tn = 0; tn < 2; ++tn) rb[tn] = t.sb[t.wn * 64 + tn * 32 + (t.lane & 31)];
-#pragma unroll
-  for (int tm = 0; tm < 2; ++tm) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 ra = *reinterpret_cast<const float4*>(t.sa + t.wm * 64 + tm * 32 + 8 * g + 4 * (t.lane >> 5));
-      const float r4[4] = {ra.x, ra.y, ra.z, ra.w};
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          acc[tm][tn][4 * g + q] = fmaf(part[tm][tn][4 * g + q], r4[q] * rb[tn], acc[tm][tn][4 * g + q]);
-    }
-  }
-}
+typedef float float16v_t __attribute__((ext_vector_type(16)));
 
-template <int FA, int FB>
-__device__ __forceinline__ void stage_chunk(const TileCtx& t, const typename Op<FA>::Slice& a,
-                                            const typename Op<FB>::Slice& b) {
-  __syncthreads();  // the previous chunk's LDS reads are done
-  Op<FA>::decode(a, t.lds_a + t.lr * LDS_STRIDE + t.lh * 64);
-  Op<FB>::decode(b, t.lds_b + t.lr * LDS_STRIDE + t.lh * 64);
-  if (t.lh == 0) {
-    t.sa[t.lr] = a.S;
-    t.sb[t.lr] = b.S;
-  }
-  __syncthreads();
-}
+// Shared memory: two decoded f16 stages of the B tile and four-deep rings of
+// the outer scales of both operands (a chunk's scales are read one chunk later).
+struct Smem {
+  _Float16 b[2][BN * LDS_STRIDE];
+  float sa[4][BM];
+  float sb[4][BN];
+};
 
-// Chunks [kc0, kc1) of one segment, with a two-deep register prefetch.
-template <int FA, int FB>
-__device__ __forceinline__ void run_segment(const TileCtx& t, const SegK& g, int kc0, int kc1,
-                                            float16_t (&acc)[2][2]) {
-  if (kc0 >= kc1) return;
-  typename Op<FA>::Slice a0, a1;
-  typename Op<FB>::Slice b0, b1;
-  Op<FA>::load(g.a, t.rowA, kc0, t.lh, a0);
-  Op<FB>::load(g.b, t.rowB, kc0, t.lh, b0);
-  if (kc0 + 1 < kc1) {
-    Op<FA>::load(g.a, t.rowA, kc0 + 1, t.lh, a1);
-    Op<FB>::load(g.b, t.rowB, kc0 + 1, t.lh, b1);
-  }
-  for (int kc = kc0; kc < kc1; kc += 2) {
-    stage_chunk<FA, FB>(t, a0, b0);
-    if (kc + 2 < kc1) {
-      Op<FA>::load(g.a, t.rowA, kc + 2, t.lh, a0);
-      Op<FB>::load(g.b, t.rowB, kc + 2, t.lh, b0);
-    }
-    int64_t krem = g.K - (int64_t)kc * BK;
-    chunk_mfma(t, (int)((krem < BK ? krem : BK) >> 4), acc);
-    if (kc + 1 >= kc1) break;
-    stage_chunk<FA, FB>(t, a1, b1);
-    if (kc + 3 < kc1) {
-      Op<FA>::load(g.a, t.rowA, kc + 3, t.lh, a1);
-      Op<FB>::load(g.b, t.rowB, kc + 3, t.lh, b1);
-    }
-    krem = g.K - (int64_t)(kc + 1) * BK;
-    chunk_mfma(t, (int)((krem < BK ? krem : BK) >> 4), acc);
-  }
-}
+// Per-thread roles.  Wave w owns output rows 32w..32w+31 of the 256x128 tile
+// and all 128 columns (four 32x32 blocks).  A rows go global -> registers ->
+// MFMA: lane l loads row 32w + (l & 31), K half h = l >> 5 of each chunk, and
+// MFMA step ks consumes K elements 64h + 8ks .. 64h + 8ks + 7 (the same
+// permutation of K is applied to B, so the sum is unchanged).  B rows are
+// decoded once per workgroup into LDS: thread t stages row t >> 2, quarter t & 3.
+struct Ctx {
+  uint32_t arn[2], brn[2];  // clamped source row * outer blocks per row, per segment
+  int ah, bq;               // A half, B quarter
+  int lane, w;
+  int n0c;                  // chunks of segment 0
+  int c_begin;              // first chunk of this workgroup
+};
 
 template <int FA0, int FB0, int FA1, int FB1>
-__global__ __launch_bounds__(256, 2) void gemm_nt_kernel(GemmKArgs p) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds_a[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) _Float16 lds_b[BN * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) float sa[BM];
-  __shared__ __attribute__((aligned(16))) float sb[BN];
+struct Fmt {
+  // the A slice / B slice of workgroup-local chunk `it` (if it exists)
+  // (an index past the range reloads the last chunk: branch-free, the data is unused)
+  static __device__ __forceinline__ void fetch_a(const GemmKArgs& p, const Ctx& t, int it, int n, Slice& a) {
+    const int g = t.c_begin + min(it, n - 1);
+    if (FA1 == F_NONE || g < t.n0c) Op<FA0>::load_half(p.seg[0].a, t.arn[0], g, t.ah, a);
+    else if constexpr (FA1 != F_NONE) Op<FA1>::load_half(p.seg[1].a, t.arn[1], g - t.n0c, t.ah, a);
+  }
+  static __device__ __forceinline__ void fetch_b(const GemmKArgs& p, const Ctx& t, int it, int n, Slice& b) {
+    const int g = t.c_begin + min(it, n - 1);
+    if (FA1 == F_NONE || g < t.n0c) Op<FB0>::load_quarter(p.seg[0].b, t.brn[0], g, t.bq, b);
+    else if constexpr (FA1 != F_NONE) Op<FB1>::load_quarter(p.seg[1].b, t.brn[1], g - t.n0c, t.bq, b);
+  }
+};
+
+// Outer scales of one 32x32 output block of a chunk, as this lane needs them:
+// S_B of its column and S_A of its 16 rows (rows 8g + 4*(lane/32) + q hold
+// element 4g + q).
+struct Scl {
+  float rb;
+  float4 ra[4];
+};
+
+__device__ __forceinline__ void read_scl(const Smem& sm, const Ctx& t, int slot, int tn, Scl& c) {
+  c.rb = sm.sb[slot][tn * 32 + (t.lane & 31)];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    c.ra[g] = *reinterpret_cast<const float4*>(&sm.sa[slot][t.w * 32 + 8 * g + 4 * (t.lane >> 5)]);
+}
+
+template <int E>
+__device__ __forceinline__ void promote_elem(const Scl& c, const float16v_t& part, float (&acc)[16]) {
+  const float4& r = c.ra[E >> 2];
+  const float ra = (E & 3) == 0 ? r.x : (E & 3) == 1 ? r.y : (E & 3) == 2 ? r.z : r.w;
+  acc[E] = fmaf(part[E], ra * c.rb, acc[E]);
+}
+
+__device__ __forceinline__ void barrier_lds() {
+  // LDS writes of this wave are complete; global prefetches may stay in flight
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// Operand formats of the two K segments: the A slice of a chunk and the B
+// quarter staged for the next chunk are in segment 1 when the flag says so.
+template <int FA0, int FB0, int FA1, int FB1>
+struct Fmts {
+  static constexpr bool kMixedA = FA1 != F_NONE && FA1 != FA0;
+  static constexpr bool kMixedB = FA1 != F_NONE && FB1 != FB0;
+  static constexpr int kFA1 = FA1 == F_NONE ? FA0 : FA1;
+  static constexpr int kFB1 = FA1 == F_NONE ? FB0 : FB1;
+  static __device__ __forceinline__ void prep_a(const Slice& a, half2_t (&sg)[4]) { Op<FA0>::prep_a(a, sg); }
+  static __device__ __forceinline__ void prep_b(const Slice& b, half2_t (&sg)[4]) { Op<FB0>::prep_b(b, sg); }
+  template <int F>
+  static __device__ __forceinline__ half8_t frag_a(const Slice& a, const half2_t (&sg)[4], bool seg1) {
+    if constexpr (kMixedA) {
+      if (seg1) return Op<kFA1>::template frag_a<F>(a, sg);
+    }
+    return Op<FA0>::template frag_a<F>(a, sg);
+  }
+  template <int U>
+  static __device__ __forceinline__ half8_t unit_b(const Slice& b, const half2_t (&sg)[4], bool seg1) {
+    if constexpr (kMixedB) {
+      if (seg1) return Op<kFB1>::template unit_b<U>(b, sg);
+    }
+    return Op<FB0>::template unit_b<U>(b, sg);
+  }
+};
+
+// One chunk as 32 issue slots (block tn = q / 8, K step ks = q % 8).  Slot q:
+// in block 0 decodes A fragment q of this chunk from the wave's A slice (the
+// previous chunk's last MFMA reading that fragment has issued), reads the B
+// fragment of slot q + 2, issues one MFMA into the block's partial (blocks
+// alternate between two partials), promotes a share of the previous block
+// (block 3 of the previous chunk during block 0; before the first chunk that
+// partial and its scales are zero), and stages the next chunk's B quarter into
+// the other LDS stage at slots 4, 12, 20, 28 and its B outer scales at slot 5
+// (after the last chunk this writes unused data).  At slot 8 the A slice is
+// refilled with the next chunk (fetch_a).  The promotion reads S_B of the block
+// at its step 0 and the lane's 16 S_A values at steps 0-1 of blocks 0 (previous
+// chunk) and 1 (this chunk).  A scheduling barrier after each slot keeps this
+// order.  Chunks past the end of a segment's K are zero in the padded operands,
+// so every chunk runs all steps.
+template <class FM, class FETCH_A, class SYNC>
+__device__ __forceinline__ void chunk(Smem& sm, const Ctx& t, int it, bool aseg1, bool bseg1, half8_t (&af)[8],
+                                      half8_t (&bf)[4], float (&acc)[4][16], float16v_t (&part)[2], Slice& a,
+                                      const Slice& nb, FETCH_A&& fetch_a, SYNC&& sync) {
+  const _Float16* bb = sm.b[it & 1] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
+  const _Float16* bn = sm.b[(it + 1) & 1] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
+  _Float16* bdst = sm.b[(it + 1) & 1] + (threadIdx.x >> 2) * LDS_STRIDE + t.bq * 32;
+  const float* sa_row = &sm.sa[0][t.w * 32 + 4 * (t.lane >> 5)];
+  Scl scl;
+  half2_t sga[4], sgb[4];
+  FM::prep_a(a, sga);
+  sm.sa[it & 3][t.w * 32 + (t.lane & 31)] = a.S;  // read back by this wave only
+  static_for<32>([&](auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    constexpr int tn = q / 8, ks = q % 8;
+    if constexpr (q < 8) af[q] = FM::template frag_a<q>(a, sga, aseg1);
+    if constexpr (q == 8) fetch_a(a);
+    // B fragments three slots ahead; the workgroup barrier sits in slot 29, once
+    // the next chunk's stage is written and this chunk's last fragment read has
+    // been issued, so slots 29-31 already read the next chunk's first fragments
+    if constexpr (q == 29) sync();
+    if constexpr (q + 3 < 32) bf[(q + 3) & 3] = ld8(bb + ((q + 3) / 8) * 32 * LDS_STRIDE + ((q + 3) % 8) * 8);
+    else bf[(q + 3) & 3] = ld8(bn + (q + 3 - 32) * 8);
+    part[tn & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks], bf[q & 3], ks == 0 ? float16v_t{} : part[tn & 1],
+                                                          0, 0, 0);
+    {
+      // the previous block's elements 4g..4g+3 are promoted at step g + 3 (its last MFMA has completed)
+      constexpr int pb = tn > 0 ? tn - 1 : 3;
+      if constexpr (ks == 0) scl.rb = sm.sb[tn > 0 ? it & 3 : (it - 1) & 3][pb * 32 + (t.lane & 31)];
+      if constexpr (tn <= 1 && ks <= 1) {
+        const float* src = sa_row + (tn == 0 ? (it - 1) & 3 : it & 3) * BM;
+        scl.ra[2 * ks] = *reinterpret_cast<const float4*>(src + 16 * ks);
+        scl.ra[2 * ks + 1] = *reinterpret_cast<const float4*>(src + 16 * ks + 8);
+      }
+      if constexpr (ks >= 3 && ks <= 6) {
+        static_for<4>([&](auto i) __attribute__((always_inline)) {
+          promote_elem<4 * (ks - 3) + decltype(i)::value>(scl, part[pb & 1], acc[pb]);
+        });
+      }
+    }
+    if constexpr (q == 3) FM::prep_b(nb, sgb);
+    if constexpr (q % 8 == 4) *reinterpret_cast<half8_t*>(bdst + tn * 8) = FM::template unit_b<tn>(nb, sgb, bseg1);
+    if constexpr (q == 5) sm.sb[(it + 1) & 3][threadIdx.x >> 2] = nb.S;
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// Stage the B quarter of the first chunk of the range (format FB).
+template <int FB>
+__device__ __forceinline__ void stage_first_b(Smem& sm, const Ctx& t, const Slice& b) {
+  Op<FB>::decode_quarter(b, sm.b[0] + (threadIdx.x >> 2) * LDS_STRIDE + t.bq * 32);
+  sm.sb[0][threadIdx.x >> 2] = b.S;
+}
+
+// A chunk of the second K segment (the FP8 outlier channels, at most a few
+// chunks per tile): loaded, decoded and multiplied without pipelining, each
+// block promoted right after its eight K steps.
+template <int FA, int FB>
+__device__ __forceinline__ void tail_chunk(const GemmKArgs& p, Smem& sm, const Ctx& t, int g, float (&acc)[4][16]) {
+  Slice a, b;
+  Op<FA>::load_half(p.seg[1].a, t.arn[1], g, t.ah, a);
+  Op<FB>::load_quarter(p.seg[1].b, t.brn[1], g, t.bq, b);
+  barrier_lds();  // every wave is done with the previous chunk's stage and scales
+  Op<FB>::decode_quarter(b, sm.b[0] + (threadIdx.x >> 2) * LDS_STRIDE + t.bq * 32);
+  sm.sb[0][threadIdx.x >> 2] = b.S;
+  sm.sa[0][t.w * 32 + (t.lane & 31)] = a.S;
+  half8_t af[8];
+  Op<FA>::decode_half(a, af);
+  barrier_lds();
+  const _Float16* bb = sm.b[0] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
+  Scl scl;
+  read_scl(sm, t, 0, 0, scl);
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
+    float16v_t part = float16v_t{};
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
+      part = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks], ld8(bb + tn * 32 * LDS_STRIDE + ks * 8), part, 0, 0, 0);
+    scl.rb = sm.sb[0][tn * 32 + (t.lane & 31)];
+    static_for<16>([&](auto e) __attribute__((always_inline)) {
+      promote_elem<decltype(e)::value>(scl, part, acc[tn]);
+    });
+  }
+}
+
+// Workgroup: 512 threads (8 waves), one 256x128 output tile, the chunk range of split z.
+template <int FA0, int FB0, int FA1, int FB1>
+__global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
 
   // XCD-aware numbering: workgroup id w runs on XCD w % 8; give each XCD a
   // contiguous range of (tile, split) indices, tiles N-fastest.
@@ -267,69 +407,105 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(GemmKArgs p) {
   const uint32_t tile = id % tiles, z = id / tiles;
   const int64_t m0 = (int64_t)(tile / p.tiles_n) * BM, n0 = (int64_t)(tile % p.tiles_n) * BN;
 
-  TileCtx t;
-  const int tid = threadIdx.x;
-  t.lane = tid & 63;
-  const int wave = tid >> 6;
-  t.wm = wave >> 1;
-  t.wn = wave & 1;
-  t.lr = tid >> 1;
-  t.lh = tid & 1;
-  t.rowA = min(m0 + t.lr, p.I - 1);
-  t.rowB = min(n0 + t.lr, p.J - 1);
-  t.lds_a = lds_a;
-  t.lds_b = lds_b;
-  t.sa = sa;
-  t.sb = sb;
-
-  float16_t acc[2][2];
+  Ctx t;
+  t.lane = threadIdx.x & 63;
+  t.w = threadIdx.x >> 6;
+  t.ah = t.lane >> 5;
+  t.bq = threadIdx.x & 3;
+  const uint32_t arow = (uint32_t)min(m0 + t.w * 32 + (t.lane & 31), p.I - 1);
+  const uint32_t brow = (uint32_t)min(n0 + (int64_t)(threadIdx.x >> 2), p.J - 1);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = float16_t{};
+  for (int sgi = 0; sgi < 2; ++sgi) {
+    t.arn[sgi] = arow * (uint32_t)p.seg[sgi].a.ld_s128;
+    t.brn[sgi] = brow * (uint32_t)p.seg[sgi].b.ld_s128;
+  }
+  t.n0c = p.seg[0].nchunks;
+  t.c_begin = (int)z * p.chunks_per_split;
+  const int n = min(t.c_begin + p.chunks_per_split, p.nchunks) - t.c_begin;
 
-  const int c_begin = (int)z * p.chunks_per_split;
-  const int c_end = min(c_begin + p.chunks_per_split, p.nchunks);
-  const int n0c = p.seg[0].nchunks;
-  run_segment<FA0, FB0>(t, p.seg[0], c_begin, min(c_end, n0c), acc);
-  if constexpr (FA1 != F_NONE) run_segment<FA1, FB1>(t, p.seg[1], max(c_begin, n0c) - n0c, c_end - n0c, acc);
+  float acc[4][16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+
+  // chunks [0, s1) of the range are segment 0 (pipelined), [s1, n) segment 1
+  const int s1 = FA1 == F_NONE ? n : min(max(t.n0c - t.c_begin, 0), n);
+  if (s1 > 0) {
+    using F = Fmt<FA0, FB0, F_NONE, F_NONE>;
+    Slice a, b1, b2;
+    half8_t af[8];
+    float16v_t part[2];
+    part[1] = float16v_t{};
+    // ring slot 3 stands for "chunk -1": zero scales for the first chunk's promotion of part[1]
+    sm.sb[3][threadIdx.x >> 2] = 0.0f;
+    sm.sa[3][t.w * 32 + (t.lane & 31)] = 0.0f;
+    F::fetch_a(p, t, 0, s1, a);
+    F::fetch_b(p, t, 0, s1, b1);
+    stage_first_b<FB0>(sm, t, b1);
+    F::fetch_b(p, t, 1, s1, b1);
+    F::fetch_b(p, t, 2, s1, b2);
+    barrier_lds();
+    half8_t bf[4];
+    {
+      const _Float16* bb = sm.b[0] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
+      bf[0] = ld8(bb);
+      bf[1] = ld8(bb + 8);
+      bf[2] = ld8(bb + 16);
+    }
+    // b1 holds the B slice of the chunk to stage next, b2 the one after it
+    for (int it = 0; it < s1; ++it) {
+      auto fa = [&](Slice& sl) __attribute__((always_inline)) { F::fetch_a(p, t, it + 1, s1, sl); };
+      auto sync = [&]() __attribute__((always_inline)) {
+        b1 = b2;
+        F::fetch_b(p, t, it + 3, s1, b2);
+        barrier_lds();  // chunk it+1's B staged; this chunk's stage may be refilled
+      };
+      chunk<Fmts<FA0, FB0, F_NONE, F_NONE>>(sm, t, it, false, false, af, bf, acc, part, a, b1, fa, sync);
+    }
+    Scl scl;
+    read_scl(sm, t, (s1 - 1) & 3, 3, scl);
+    static_for<16>([&](auto e) __attribute__((always_inline)) {
+      promote_elem<decltype(e)::value>(scl, part[1], acc[3]);
+    });
+  }
+  if constexpr (FA1 != F_NONE) {
+    for (int it = s1; it < n; ++it) tail_chunk<FA1, FB1>(p, sm, t, t.c_begin + it - t.n0c, acc);
+  }
 
   const int lane = t.lane;
+  const int64_t r0 = m0 + t.w * 32 + 4 * (lane >> 5);
+  const int64_t c0 = n0 + (lane & 31);
+  const bool full = m0 + BM <= p.I && n0 + BN <= p.J;
   if (p.partial) {
-    float* part_out = p.partial + (int64_t)z * p.I * p.J;
+    float* base = p.partial + (int64_t)z * p.I * p.J + r0 * p.J + c0;
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
-      const int64_t col = n0 + t.wn * 64 + tn * 32 + (lane & 31);
-      if (col >= p.J) continue;
+    for (int tn = 0; tn < 4; ++tn) {
+      if (!full && c0 + tn * 32 >= p.J) continue;
 #pragma unroll
-      for (int tm = 0; tm < 2; ++tm) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t row = m0 + t.wm * 64 + tm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          if (row < p.I) part_out[row * p.J + col] = acc[tm][tn][e];
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int dr = 8 * (e >> 2) + (e & 3);
+        if (full || r0 + dr < p.I) base[dr * p.J + tn * 32] = acc[tn][e];
       }
     }
     return;
   }
 #pragma unroll
-  for (int tn = 0; tn < 2; ++tn) {
-    const int64_t col = n0 + t.wn * 64 + tn * 32 + (lane & 31);
-    if (col >= p.J) continue;
+  for (int tn = 0; tn < 4; ++tn) {
+    const int64_t col = c0 + tn * 32;
+    if (!full && col >= p.J) continue;
     const int64_t ccol = p.col_map ? (int64_t)p.col_map[col] : col;
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + t.wm * 64 + tm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (row >= p.I) continue;
-        const float v = acc[tm][tn][e];
-        if (p.c_bf16) {
-          reinterpret_cast<uint16_t*>(p.C)[row * p.ldc + ccol] = (uint16_t)f32_to_bf16(v);
-        } else {
-          float* cp = reinterpret_cast<float*>(p.C) + row * p.ldc + ccol;
-          *cp = p.accumulate ? *cp + v : v;
-        }
+    for (int e = 0; e < 16; ++e) {
+      const int dr = 8 * (e >> 2) + (e & 3);
+      if (!full && r0 + dr >= p.I) continue;
+      const int64_t off = (r0 + dr) * p.ldc + ccol;
+      const float v = acc[tn][e];
+      if (p.c_bf16) {
+        reinterpret_cast<uint16_t*>(p.C)[off] = (uint16_t)f32_to_bf16(v);
+      } else {
+        float* cp = reinterpret_cast<float*>(p.C) + off;
+        *cp = p.accumulate ? *cp + v : v;
       }
     }
   }
@@ -405,7 +581,7 @@ GemmKernel pick_kernel(const GemmParams& p) {
 
 int gemm_split(int64_t I, int64_t J, int64_t nchunks) {
   const int64_t tiles = ((I + BM - 1) / BM) * ((J + BN - 1) / BN);
-  const int64_t target = 1024;  // workgroups: about two rounds of two per CU
+  const int64_t target = 512;  // workgroups: about two rounds of one per CU
   if (tiles >= target / 2 || nchunks < 8) return 1;
   int64_t split = (target + tiles - 1) / tiles;
   const int64_t max_by_depth = nchunks / 4;  // keep >= 4 chunks per split
@@ -452,7 +628,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   k.tiles_n = (int)((p.J + BN - 1) / BN);
   k.split = split;
   const uint32_t nwg = (uint32_t)k.tiles_m * (uint32_t)k.tiles_n * (uint32_t)split;
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, s, k);
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(512), 0, s, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split == 1) return e;
   const int64_t threads = p.I * ((p.J + 3) / 4);
