@@ -199,6 +199,15 @@ struct Op<TJ2_FP8> {
 
 __device__ __forceinline__ half8_t ld8(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
 
+// B fragments are read kFragAhead MFMA slots before use (ring of kFragRing;
+// 32 % kFragRing == 0 so ring positions carry over between chunks)
+#ifndef TJ2_FRAG_AHEAD
+#define TJ2_FRAG_AHEAD 5
+#endif
+constexpr int kFragAhead = TJ2_FRAG_AHEAD;
+constexpr int kFragRing = kFragAhead < 4 ? 4 : 8;
+static_assert(kFragAhead < kFragRing && 32 % kFragRing == 0, "fragment ring");
+
 typedef float float16v_t __attribute__((ext_vector_type(16)));
 
 // Shared memory: two decoded f16 stages of the B tile and four-deep rings of
@@ -296,20 +305,23 @@ struct Fmts {
 // One chunk as 32 issue slots (block tn = q / 8, K step ks = q % 8).  Slot q:
 // in block 0 decodes A fragment q of this chunk from the wave's A slice (the
 // previous chunk's last MFMA reading that fragment has issued), reads the B
-// fragment of slot q + 2, issues one MFMA into the block's partial (blocks
-// alternate between two partials), promotes a share of the previous block
-// (block 3 of the previous chunk during block 0; before the first chunk that
-// partial and its scales are zero), and stages the next chunk's B quarter into
-// the other LDS stage at slots 4, 12, 20, 28 and its B outer scales at slot 5
-// (after the last chunk this writes unused data).  At slot 8 the A slice is
-// refilled with the next chunk (fetch_a).  The promotion reads S_B of the block
-// at its step 0 and the lane's 16 S_A values at steps 0-1 of blocks 0 (previous
-// chunk) and 1 (this chunk).  A scheduling barrier after each slot keeps this
+// fragment of slot q + kFragAhead, issues one MFMA into the block's partial
+// (blocks alternate between two partials), promotes a share of the previous
+// block (block 3 of the previous chunk during block 0; before the first chunk
+// that partial and its scales are zero), and stages the next chunk's B quarter
+// into the other LDS stage at slots 2, 8, 14, 20 and its B outer scales at
+// slot 3 (after the last chunk this writes unused data).  At slot 8 the A
+// slice is refilled with the next chunk (fetch_a).  The promotion reads S_B of
+// the block at its step 0 and the lane's 16 S_A values at steps 0-1 of blocks
+// 0 (previous chunk) and 1 (this chunk).  The workgroup barrier (sync) sits in
+// slot 32 - kFragAhead, once the next stage is written and this chunk's last
+// fragment read has been issued, so the last slots already read the next
+// chunk's first fragments.  A scheduling barrier after each slot keeps this
 // order.  Chunks past the end of a segment's K are zero in the padded operands,
 // so every chunk runs all steps.
 template <class FM, class FETCH_A, class SYNC>
 __device__ __forceinline__ void chunk(Smem& sm, const Ctx& t, int it, bool aseg1, bool bseg1, half8_t (&af)[8],
-                                      half8_t (&bf)[4], float (&acc)[4][16], float16v_t (&part)[2], Slice& a,
+                                      half8_t (&bf)[kFragRing], float (&acc)[4][16], float16v_t (&part)[2], Slice& a,
                                       const Slice& nb, FETCH_A&& fetch_a, SYNC&& sync) {
   const _Float16* bb = sm.b[it & 1] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
   const _Float16* bn = sm.b[(it + 1) & 1] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
@@ -324,13 +336,11 @@ __device__ __forceinline__ void chunk(Smem& sm, const Ctx& t, int it, bool aseg1
     constexpr int tn = q / 8, ks = q % 8;
     if constexpr (q < 8) af[q] = FM::template frag_a<q>(a, sga, aseg1);
     if constexpr (q == 8) fetch_a(a);
-    // B fragments three slots ahead; the workgroup barrier sits in slot 29, once
-    // the next chunk's stage is written and this chunk's last fragment read has
-    // been issued, so slots 29-31 already read the next chunk's first fragments
-    if constexpr (q == 29) sync();
-    if constexpr (q + 3 < 32) bf[(q + 3) & 3] = ld8(bb + ((q + 3) / 8) * 32 * LDS_STRIDE + ((q + 3) % 8) * 8);
-    else bf[(q + 3) & 3] = ld8(bn + (q + 3 - 32) * 8);
-    part[tn & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks], bf[q & 3], ks == 0 ? float16v_t{} : part[tn & 1],
+    if constexpr (q == 32 - kFragAhead) sync();
+    constexpr int qf = q + kFragAhead;  // fragment read in this slot
+    if constexpr (qf < 32) bf[qf % kFragRing] = ld8(bb + (qf / 8) * 32 * LDS_STRIDE + (qf % 8) * 8);
+    else bf[qf % kFragRing] = ld8(bn + (qf - 32) * 8);
+    part[tn & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks], bf[q % kFragRing], ks == 0 ? float16v_t{} : part[tn & 1],
                                                           0, 0, 0);
     {
       // the previous block's elements 4g..4g+3 are promoted at step g + 3 (its last MFMA has completed)
@@ -347,9 +357,12 @@ __device__ __forceinline__ void chunk(Smem& sm, const Ctx& t, int it, bool aseg1
         });
       }
     }
-    if constexpr (q == 3) FM::prep_b(nb, sgb);
-    if constexpr (q % 8 == 4) *reinterpret_cast<half8_t*>(bdst + tn * 8) = FM::template unit_b<tn>(nb, sgb, bseg1);
-    if constexpr (q == 5) sm.sb[(it + 1) & 3][threadIdx.x >> 2] = nb.S;
+    if constexpr (q == 1) FM::prep_b(nb, sgb);
+    if constexpr (q % 6 == 2 && q <= 20) {
+      constexpr int u = q / 6;
+      *reinterpret_cast<half8_t*>(bdst + u * 8) = FM::template unit_b<u>(nb, sgb, bseg1);
+    }
+    if constexpr (q == 3) sm.sb[(it + 1) & 3][threadIdx.x >> 2] = nb.S;
     __builtin_amdgcn_sched_barrier(0);
   });
 }
@@ -446,12 +459,12 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     F::fetch_b(p, t, 1, s1, b1);
     F::fetch_b(p, t, 2, s1, b2);
     barrier_lds();
-    half8_t bf[4];
+    half8_t bf[kFragRing];
     {
       const _Float16* bb = sm.b[0] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
-      bf[0] = ld8(bb);
-      bf[1] = ld8(bb + 8);
-      bf[2] = ld8(bb + 16);
+      static_for<kFragAhead>([&](auto f) __attribute__((always_inline)) {
+        bf[decltype(f)::value] = ld8(bb + decltype(f)::value * 8);
+      });
     }
     // b1 holds the B slice of the chunk to stage next, b2 the one after it
     for (int it = 0; it < s1; ++it) {
