@@ -142,6 +142,23 @@ def gemm(A: QTensor, B: QTensor, A2: QTensor | None = None, B2: QTensor | None =
     return out
 
 
+def gemm_outlier_cols(A: QTensor, B: QTensor, B8: QTensor, plan: "OutlierPlan", *, out: torch.Tensor | None = None,
+                      out_dtype=torch.float32, accumulate: bool = False,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One product over all K output columns of a plan: C[:, rest[j]] = A B[j]^T, C[:, outliers[j]] = A B8[j]^T."""
+    J = B.rows + B8.rows
+    if out is None:
+        out = torch.empty((A.rows, J), dtype=out_dtype, device=A.codes.device)
+    if workspace is None:
+        workspace = gemm_workspace(A.rows, J, A.len, A.codes.device)
+    ac, bc, b8c, pc = A.c(), B.c(), B8.c(), plan.c()
+    st = lib().nvfp4_gemm_outlier_cols(ctypes.byref(ac), ctypes.byref(bc), ctypes.byref(b8c), ctypes.byref(pc),
+                                       _ptr(out), _dtype_code(out), out.stride(0), 1 if accumulate else 0,
+                                       _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
+    check("nvfp4_gemm_outlier_cols", st)
+    return out
+
+
 def linear_fwd(X: torch.Tensor, W_master: torch.Tensor | None, N: int, *, Wq: QTensor | None = None,
                W8: QTensor | None = None, plan: OutlierPlan | None = None, y_dtype=torch.bfloat16,
                Y: torch.Tensor | None = None, Xq: QTensor | None = None, X8: QTensor | None = None):

@@ -151,6 +151,31 @@ tj2_status run_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtenso
   return hip_check(launch_gemm(p, s), "gemm launch");
 }
 
+// C[:, rest[j]] = A . B[j]^T and C[:, outliers[i]] = A . B8[i]^T in one product.
+tj2_status run_gemm_outl(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* B8,
+                         const tj2_outlier_plan* plan, void* C, int c_dtype, int64_t ldc, int accumulate, void* ws,
+                         size_t ws_bytes, hipStream_t s) {
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.seg[0].a = make_view(*A);
+  p.seg[0].b = make_view(*B);
+  p.seg[0].K = A->len;
+  p.nseg = 1;
+  p.b8 = make_view(*B8);
+  p.outl = plan->outliers;
+  p.rest = plan->rest;
+  p.n_outl = plan->n_outliers;
+  p.I = A->rows;
+  p.J = B->rows + B8->rows;
+  p.C = C;
+  p.c_dtype = c_dtype;
+  p.ldc = ldc;
+  p.accumulate = accumulate;
+  p.partial = reinterpret_cast<float*>(ws);
+  p.partial_bytes = ws ? ws_bytes : 0;
+  return hip_check(launch_gemm(p, s), "gemm launch");
+}
+
 uint32_t philox_word0(uint64_t seed, uint64_t offset) {
   uint32_t c0 = 0xFFFFFFFFu, c1 = 0xFFFFFFFFu, c2 = (uint32_t)offset, c3 = (uint32_t)(offset >> 32);
   uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
@@ -171,13 +196,10 @@ uint32_t philox_word0(uint64_t seed, uint64_t offset) {
 
 // Split-K workspace shared (sequentially) by the products of one backward call.
 size_t bwd_gemm_ws(int64_t M, int64_t N, int64_t K1, int64_t no) {
+  // with a plan, dX and dW are each one outlier-column product over all K1 + no columns
   const int64_t cn = (N + 127) / 128, cm = (M + 127) / 128;
-  size_t w = gemm_workspace_bytes(M, K1, cn);
-  w = std::max(w, gemm_workspace_bytes(N, K1, cm));
-  if (no) {
-    w = std::max(w, gemm_workspace_bytes(M, no, cn));
-    w = std::max(w, gemm_workspace_bytes(N, no, cm));
-  }
+  size_t w = gemm_workspace_bytes(M, K1 + no, cn);
+  w = std::max(w, gemm_workspace_bytes(N, K1 + no, cm));
   return align256(w);
 }
 
@@ -278,6 +300,28 @@ tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qten
                   (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
 }
 
+tj2_status nvfp4_gemm_outlier_cols(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* B8,
+                                   const tj2_outlier_plan* plan, void* C, int32_t c_dtype, int64_t ldc,
+                                   int32_t accumulate, void* workspace, size_t ws_bytes, void* stream) {
+  if (!A || !B || !B8 || !plan) return fail(TJ2_ERR_ARG, "A, B, B8 and plan are required");
+  if (workspace && !aligned16(workspace)) return fail(TJ2_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (A->fmt != TJ2_NVFP4 || B->fmt != TJ2_NVFP4 || B8->fmt != TJ2_FP8)
+    return fail(TJ2_ERR_UNSUPPORTED, "A and B must be NVFP4, B8 FP8");
+  const int64_t J = B->rows + B8->rows;
+  TJ2_TRY(check_plan(plan, J));
+  if (plan->n_outliers != B8->rows) return fail(TJ2_ERR_SHAPE, "B8 rows (%lld) != n_outliers (%d)", (long long)B8->rows, plan->n_outliers);
+  TJ2_TRY(check_qtensor(A, "A", TJ2_NVFP4, A->rows, A->len));
+  TJ2_TRY(check_qtensor(B, "B", TJ2_NVFP4, B->rows, A->len));
+  TJ2_TRY(check_qtensor(B8, "B8", TJ2_FP8, B8->rows, A->len));
+  if (!C) return fail(TJ2_ERR_ARG, "C is NULL");
+  if (c_dtype != TJ2_F32 && c_dtype != TJ2_BF16) return fail(TJ2_ERR_ARG, "c_dtype must be TJ2_F32 or TJ2_BF16");
+  if (accumulate && c_dtype != TJ2_F32) return fail(TJ2_ERR_UNSUPPORTED, "accumulate needs an fp32 output");
+  if (ldc < J) return fail(TJ2_ERR_SHAPE, "ldc < J");
+  if (A->rows > ((int64_t)1 << 24) * 128 || J > ((int64_t)1 << 24) * 128) return fail(TJ2_ERR_SHAPE, "too many rows");
+  return run_gemm_outl(A, B, B8, plan, C, c_dtype, ldc, accumulate, workspace, workspace ? ws_bytes : 0,
+                       (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
+}
+
 tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, const float* W_master, tj2_qtensor* Wq,
                             tj2_qtensor* W8, const tj2_outlier_plan* plan, tj2_qtensor* Xq, tj2_qtensor* X8, void* Y,
                             int32_t y_dtype, void* stream) {
@@ -376,15 +420,15 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
   TJ2_TRY(run_quant(nullptr, TJ2_NVFP4, Wq, N, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 1, &o->Wt, s));
   TJ2_TRY(run_quant(dY, TJ2_BF16, nullptr, M, N, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 2, &o->dYt, s));
   TJ2_TRY(run_quant(nullptr, TJ2_NVFP4, Xq, M, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 3, &o->Xt, s));
-  const int32_t* rest = plan ? plan->rest : nullptr;
-  TJ2_TRY(run_gemm(&o->dYq, &o->Wt, nullptr, nullptr, dX, dx_dtype, K, rest, 0, gemm_ws, gws, s));
-  TJ2_TRY(run_gemm(&o->dYt, &o->Xt, nullptr, nullptr, dW, TJ2_F32, K, rest, 0, gemm_ws, gws, s));
-  if (plan) {
-    TJ2_TRY(run_quant(nullptr, TJ2_FP8, W8, N, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 4, &o->W8t, s));
-    TJ2_TRY(run_quant(nullptr, TJ2_FP8, X8, M, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 5, &o->X8t, s));
-    TJ2_TRY(run_gemm(&o->dYq, &o->W8t, nullptr, nullptr, dX, dx_dtype, K, plan->outliers, 0, gemm_ws, gws, s));
-    TJ2_TRY(run_gemm(&o->dYt, &o->X8t, nullptr, nullptr, dW, TJ2_F32, K, plan->outliers, 0, gemm_ws, gws, s));
+  if (!plan) {
+    TJ2_TRY(run_gemm(&o->dYq, &o->Wt, nullptr, nullptr, dX, dx_dtype, K, nullptr, 0, gemm_ws, gws, s));
+    TJ2_TRY(run_gemm(&o->dYt, &o->Xt, nullptr, nullptr, dW, TJ2_F32, K, nullptr, 0, gemm_ws, gws, s));
+    return ok();
   }
+  TJ2_TRY(run_quant(nullptr, TJ2_FP8, W8, N, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 4, &o->W8t, s));
+  TJ2_TRY(run_quant(nullptr, TJ2_FP8, X8, M, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 5, &o->X8t, s));
+  TJ2_TRY(run_gemm_outl(&o->dYq, &o->Wt, &o->W8t, plan, dX, dx_dtype, K, 0, gemm_ws, gws, s));
+  TJ2_TRY(run_gemm_outl(&o->dYt, &o->Xt, &o->X8t, plan, dW, TJ2_F32, K, 0, gemm_ws, gws, s));
   return ok();
 }
 

@@ -64,6 +64,13 @@ struct GemmKArgs {
   const int32_t* col_map;
   int c_bf16;
   int accumulate;
+  // outlier-column products: J output columns in original order; column
+  // outl[i] (sorted) takes B row i of b8 (FP8), the other columns in order take
+  // the rows of seg[0].b (NVFP4); rest lists those other columns
+  OperandK b8;
+  const int32_t* outl;
+  const int32_t* rest;
+  int n_outl;
 };
 
 // Packed slice of one thread, in a layout shared by both formats:
@@ -199,14 +206,12 @@ struct Op<TJ2_FP8> {
 
 __device__ __forceinline__ half8_t ld8(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
 
-// B fragments are read kFragAhead MFMA slots before use (ring of kFragRing;
-// 32 % kFragRing == 0 so ring positions carry over between chunks)
-#ifndef TJ2_FRAG_AHEAD
-#define TJ2_FRAG_AHEAD 5
-#endif
-constexpr int kFragAhead = TJ2_FRAG_AHEAD;
-constexpr int kFragRing = kFragAhead < 4 ? 4 : 8;
-static_assert(kFragAhead < kFragRing && 32 % kFragRing == 0, "fragment ring");
+// B fragments are read D MFMA slots before use, in a ring of frag_ring(D)
+// registers (32 % ring == 0 so ring positions carry over between chunks):
+// D = 5 in general, 3 for outlier-column products (fewer registers).
+constexpr int frag_ring(int d) { return d < 4 ? 4 : 8; }
+template <bool MIXB>
+constexpr int kFragAheadFor = MIXB ? 5 : 5;
 
 typedef float float16v_t __attribute__((ext_vector_type(16)));
 
@@ -226,6 +231,7 @@ struct Smem {
 // decoded once per workgroup into LDS: thread t stages row t >> 2, quarter t & 3.
 struct Ctx {
   uint32_t arn[2], brn[2];  // clamped source row * outer blocks per row, per segment
+  bool b8;                  // outlier-column products: this thread stages an FP8 row (from p.b8)
   int ah, bq;               // A half, B quarter
   int lane, w;
   int n0c;                  // chunks of segment 0
@@ -245,6 +251,26 @@ struct Fmt {
     const int g = t.c_begin + min(it, n - 1);
     if (FA1 == F_NONE || g < t.n0c) Op<FB0>::load_quarter(p.seg[0].b, t.brn[0], g, t.bq, b);
     else if constexpr (FA1 != F_NONE) Op<FB1>::load_quarter(p.seg[1].b, t.brn[1], g - t.n0c, t.bq, b);
+  }
+};
+
+// Outlier-column products: A NVFP4; B rows NVFP4 (seg[0].b) or FP8 (b8) per thread.
+struct FmtMixB {
+  static __device__ __forceinline__ void fetch_a(const GemmKArgs& p, const Ctx& t, int it, int n, Slice& a) {
+    Op<TJ2_NVFP4>::load_half(p.seg[0].a, t.arn[0], t.c_begin + min(it, n - 1), t.ah, a);
+  }
+  // Branch-free: every thread issues the same loads from addresses selected by its
+  // format (an NVFP4 thread's second 16 bytes and an FP8 thread's inner scales
+  // are read from valid addresses and ignored).
+  static __device__ __forceinline__ void fetch_b(const GemmKArgs& p, const Ctx& t, int it, int n, Slice& b) {
+    const int g = t.c_begin + min(it, n - 1);
+    const uint8_t* c4 = p.seg[0].b.codes + (size_t)g * 64 + (t.brn[0] * 64 + t.bq * 16);
+    const uint8_t* c8 = p.b8.codes + (size_t)g * 128 + (t.brn[1] * 128 + t.bq * 32);
+    const uint8_t* c = t.b8 ? c8 : c4;
+    b.q[0] = *reinterpret_cast<const uint4*>(c);
+    b.q[1] = *reinterpret_cast<const uint4*>(t.b8 ? c8 + 16 : c4);
+    b.q[2].x = *reinterpret_cast<const uint16_t*>(p.seg[0].b.s16 + (size_t)g * 8 + (t.brn[0] * 8 + t.bq * 2));
+    b.S = t.b8 ? (p.b8.s128 + g)[t.brn[1]] : (p.seg[0].b.s128 + g)[t.brn[0]];
   }
 };
 
@@ -302,6 +328,25 @@ struct Fmts {
   }
 };
 
+struct FmtsMixB {
+  static __device__ __forceinline__ void prep_a(const Slice& a, half2_t (&sg)[4]) { Op<TJ2_NVFP4>::prep_a(a, sg); }
+  // the NVFP4 inner scales sit in q[2].x of a B slice here (q[1] holds FP8 codes)
+  static __device__ __forceinline__ void prep_b(const Slice& b, half2_t (&sg)[4]) {
+    Op<TJ2_NVFP4>::scales(b.q[2].x, sg);
+  }
+  template <int F>
+  static __device__ __forceinline__ half8_t frag_a(const Slice& a, const half2_t (&sg)[4], bool) {
+    return Op<TJ2_NVFP4>::template frag_a<F>(a, sg);
+  }
+  // both decodes, selected per lane (no divergent branch)
+  template <int U>
+  static __device__ __forceinline__ half8_t unit_b(const Slice& b, const half2_t (&sg)[4], bool fp8) {
+    const half8_t v8 = Op<TJ2_FP8>::template unit_b<U>(b, sg);
+    const half8_t v4 = Op<TJ2_NVFP4>::template unit_b<U>(b, sg);
+    return fp8 ? v8 : v4;
+  }
+};
+
 // One chunk as 32 issue slots (block tn = q / 8, K step ks = q % 8).  Slot q:
 // in block 0 decodes A fragment q of this chunk from the wave's A slice (the
 // previous chunk's last MFMA reading that fragment has issued), reads the B
@@ -319,14 +364,15 @@ struct Fmts {
 // chunk's first fragments.  A scheduling barrier after each slot keeps this
 // order.  Chunks past the end of a segment's K are zero in the padded operands,
 // so every chunk runs all steps.
-template <class FM, class FETCH_A, class SYNC>
+template <class FM, int kFragAhead, class FETCH_A, class SYNC>
 __device__ __forceinline__ void chunk(Smem& sm, const Ctx& t, int it, bool aseg1, bool bseg1, half8_t (&af)[8],
-                                      half8_t (&bf)[kFragRing], float (&acc)[4][16], float16v_t (&part)[2], Slice& a,
+                                      half8_t (&bf)[frag_ring(kFragAhead)], float (&acc)[4][16], float16v_t (&part)[2], Slice& a,
                                       const Slice& nb, FETCH_A&& fetch_a, SYNC&& sync) {
   const _Float16* bb = sm.b[it & 1] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
   const _Float16* bn = sm.b[(it + 1) & 1] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
   _Float16* bdst = sm.b[(it + 1) & 1] + (threadIdx.x >> 2) * LDS_STRIDE + t.bq * 32;
   const float* sa_row = &sm.sa[0][t.w * 32 + 4 * (t.lane >> 5)];
+  constexpr int kFragRing = frag_ring(kFragAhead);
   Scl scl;
   half2_t sga[4], sgb[4];
   FM::prep_a(a, sga);
@@ -406,7 +452,18 @@ __device__ __forceinline__ void tail_chunk(const GemmKArgs& p, Smem& sm, const C
 }
 
 // Workgroup: 512 threads (8 waves), one 256x128 output tile, the chunk range of split z.
-template <int FA0, int FB0, int FA1, int FB1>
+// first index i in [0, n) with a[i] >= v (a sorted ascending), n if none
+__device__ __forceinline__ int lower_bound(const int32_t* a, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+template <int FA0, int FB0, int FA1, int FB1, bool MIXB>
 __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
 
@@ -432,6 +489,24 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     t.arn[sgi] = arow * (uint32_t)p.seg[sgi].a.ld_s128;
     t.brn[sgi] = brow * (uint32_t)p.seg[sgi].b.ld_s128;
   }
+  t.b8 = false;
+  // Outlier-column products: the tile's output columns [n0, n0 + ncols) are
+  // staged as LDS rows [0, c1) = its non-outlier columns in order (B rows r0..),
+  // then rows [c1, ncols) = its outlier columns (FP8 rows lo..), so at most one
+  // wave mixes the two formats; the epilogue maps rows back to columns.
+  int lo = 0, c1 = BN, r0 = 0, ncols = BN;
+  if constexpr (MIXB) {
+    lo = lower_bound(p.outl, p.n_outl, (int)n0);
+    const int hi = lower_bound(p.outl, p.n_outl, (int)min(n0 + BN, p.J));
+    ncols = (int)min((int64_t)BN, p.J - n0);
+    c1 = ncols - (hi - lo);
+    r0 = (int)n0 - lo;
+    const int rho = threadIdx.x >> 2;
+    t.b8 = rho >= c1 && rho < ncols;
+    const int64_t n1 = p.J - p.n_outl;  // rows of the NVFP4 B operand
+    t.brn[0] = (uint32_t)min((int64_t)(r0 + rho), n1 - 1) * (uint32_t)p.seg[0].b.ld_s128;
+    t.brn[1] = (uint32_t)min(lo + max(rho - c1, 0), p.n_outl - 1) * (uint32_t)p.b8.ld_s128;
+  }
   t.n0c = p.seg[0].nchunks;
   t.c_begin = (int)z * p.chunks_per_split;
   const int n = min(t.c_begin + p.chunks_per_split, p.nchunks) - t.c_begin;
@@ -445,7 +520,8 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
   // chunks [0, s1) of the range are segment 0 (pipelined), [s1, n) segment 1
   const int s1 = FA1 == F_NONE ? n : min(max(t.n0c - t.c_begin, 0), n);
   if (s1 > 0) {
-    using F = Fmt<FA0, FB0, F_NONE, F_NONE>;
+    using F = std::conditional_t<MIXB, FmtMixB, Fmt<FA0, FB0, F_NONE, F_NONE>>;
+    using FM = std::conditional_t<MIXB, FmtsMixB, Fmts<FA0, FB0, F_NONE, F_NONE>>;
     Slice a, b1, b2;
     half8_t af[8];
     float16v_t part[2];
@@ -455,11 +531,23 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     sm.sa[3][t.w * 32 + (t.lane & 31)] = 0.0f;
     F::fetch_a(p, t, 0, s1, a);
     F::fetch_b(p, t, 0, s1, b1);
-    stage_first_b<FB0>(sm, t, b1);
+    if constexpr (MIXB) {
+      half2_t sg[4];
+      FM::prep_b(b1, sg);
+      half8_t* out = reinterpret_cast<half8_t*>(sm.b[0] + (threadIdx.x >> 2) * LDS_STRIDE + t.bq * 32);
+      out[0] = FM::template unit_b<0>(b1, sg, t.b8);
+      out[1] = FM::template unit_b<1>(b1, sg, t.b8);
+      out[2] = FM::template unit_b<2>(b1, sg, t.b8);
+      out[3] = FM::template unit_b<3>(b1, sg, t.b8);
+      sm.sb[0][threadIdx.x >> 2] = b1.S;
+    } else {
+      stage_first_b<FB0>(sm, t, b1);
+    }
     F::fetch_b(p, t, 1, s1, b1);
     F::fetch_b(p, t, 2, s1, b2);
     barrier_lds();
-    half8_t bf[kFragRing];
+    constexpr int kFragAhead = kFragAheadFor<MIXB>;
+    half8_t bf[frag_ring(kFragAhead)];
     {
       const _Float16* bb = sm.b[0] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
       static_for<kFragAhead>([&](auto f) __attribute__((always_inline)) {
@@ -474,7 +562,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
         F::fetch_b(p, t, it + 3, s1, b2);
         barrier_lds();  // chunk it+1's B staged; this chunk's stage may be refilled
       };
-      chunk<Fmts<FA0, FB0, F_NONE, F_NONE>>(sm, t, it, false, false, af, bf, acc, part, a, b1, fa, sync);
+      chunk<FM, kFragAhead>(sm, t, it, false, t.b8, af, bf, acc, part, a, b1, fa, sync);
     }
     Scl scl;
     read_scl(sm, t, (s1 - 1) & 3, 3, scl);
@@ -486,33 +574,47 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     for (int it = s1; it < n; ++it) tail_chunk<FA1, FB1>(p, sm, t, t.c_begin + it - t.n0c, acc);
   }
 
+  // Output: lane holds rows 8g + 4*(lane/32) + q (element 4g + q) of the wave's
+  // 32 rows, column tn*32 + (lane & 31) of block tn (staged LDS row; for
+  // outlier-column products mapped back to the original column).
   const int lane = t.lane;
-  const int64_t r0 = m0 + t.w * 32 + 4 * (lane >> 5);
-  const int64_t c0 = n0 + (lane & 31);
-  const bool full = m0 + BM <= p.I && n0 + BN <= p.J;
+  const int64_t rw = m0 + t.w * 32 + 4 * (lane >> 5);
+  const bool full_rows = m0 + BM <= p.I;
+  int64_t ocol[4];
+  bool ok[4];
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
+    const int rho = tn * 32 + (lane & 31);
+    if constexpr (MIXB) {
+      ok[tn] = rho < ncols;
+      ocol[tn] = !ok[tn] ? 0 : rho < c1 ? (int64_t)p.rest[r0 + rho] : (int64_t)p.outl[lo + rho - c1];
+    } else {
+      ocol[tn] = n0 + rho;
+      ok[tn] = ocol[tn] < p.J;
+    }
+  }
   if (p.partial) {
-    float* base = p.partial + (int64_t)z * p.I * p.J + r0 * p.J + c0;
+    float* base = p.partial + (int64_t)z * p.I * p.J + rw * p.J;
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn) {
-      if (!full && c0 + tn * 32 >= p.J) continue;
+      if (!ok[tn]) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int dr = 8 * (e >> 2) + (e & 3);
-        if (full || r0 + dr < p.I) base[dr * p.J + tn * 32] = acc[tn][e];
+        if (full_rows || rw + dr < p.I) base[dr * p.J + ocol[tn]] = acc[tn][e];
       }
     }
     return;
   }
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn) {
-    const int64_t col = c0 + tn * 32;
-    if (!full && col >= p.J) continue;
-    const int64_t ccol = p.col_map ? (int64_t)p.col_map[col] : col;
+    if (!ok[tn]) continue;
+    const int64_t ccol = (!MIXB && p.col_map) ? (int64_t)p.col_map[ocol[tn]] : ocol[tn];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int dr = 8 * (e >> 2) + (e & 3);
-      if (!full && r0 + dr >= p.I) continue;
-      const int64_t off = (r0 + dr) * p.ldc + ccol;
+      if (!full_rows && rw + dr >= p.I) continue;
+      const int64_t off = (rw + dr) * p.ldc + ccol;
       const float v = acc[tn][e];
       if (p.c_bf16) {
         reinterpret_cast<uint16_t*>(p.C)[off] = (uint16_t)f32_to_bf16(v);
@@ -576,17 +678,22 @@ typedef void (*GemmKernel)(GemmKArgs);
 
 GemmKernel pick_kernel(const GemmParams& p) {
   const int fa = p.seg[0].a.fmt, fb = p.seg[0].b.fmt;
-  if (p.nseg == 2) {
-    if (fa == TJ2_NVFP4 && fb == TJ2_NVFP4 && p.seg[1].a.fmt == TJ2_FP8 && p.seg[1].b.fmt == TJ2_FP8)
-      return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, TJ2_FP8, TJ2_FP8>;
-    if (fa == TJ2_NVFP4 && fb == TJ2_NVFP4 && p.seg[1].a.fmt == TJ2_NVFP4 && p.seg[1].b.fmt == TJ2_NVFP4)
-      return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, TJ2_NVFP4, TJ2_NVFP4>;
+  if (p.outl) {
+    if (p.nseg == 1 && fa == TJ2_NVFP4 && fb == TJ2_NVFP4 && p.b8.fmt == TJ2_FP8)
+      return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, F_NONE, F_NONE, true>;
     return nullptr;
   }
-  if (fa == TJ2_NVFP4 && fb == TJ2_NVFP4) return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, F_NONE, F_NONE>;
-  if (fa == TJ2_NVFP4 && fb == TJ2_FP8) return gemm_nt_kernel<TJ2_NVFP4, TJ2_FP8, F_NONE, F_NONE>;
-  if (fa == TJ2_FP8 && fb == TJ2_NVFP4) return gemm_nt_kernel<TJ2_FP8, TJ2_NVFP4, F_NONE, F_NONE>;
-  if (fa == TJ2_FP8 && fb == TJ2_FP8) return gemm_nt_kernel<TJ2_FP8, TJ2_FP8, F_NONE, F_NONE>;
+  if (p.nseg == 2) {
+    if (fa == TJ2_NVFP4 && fb == TJ2_NVFP4 && p.seg[1].a.fmt == TJ2_FP8 && p.seg[1].b.fmt == TJ2_FP8)
+      return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, TJ2_FP8, TJ2_FP8, false>;
+    if (fa == TJ2_NVFP4 && fb == TJ2_NVFP4 && p.seg[1].a.fmt == TJ2_NVFP4 && p.seg[1].b.fmt == TJ2_NVFP4)
+      return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, TJ2_NVFP4, TJ2_NVFP4, false>;
+    return nullptr;
+  }
+  if (fa == TJ2_NVFP4 && fb == TJ2_NVFP4) return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, F_NONE, F_NONE, false>;
+  if (fa == TJ2_NVFP4 && fb == TJ2_FP8) return gemm_nt_kernel<TJ2_NVFP4, TJ2_FP8, F_NONE, F_NONE, false>;
+  if (fa == TJ2_FP8 && fb == TJ2_NVFP4) return gemm_nt_kernel<TJ2_FP8, TJ2_NVFP4, F_NONE, F_NONE, false>;
+  if (fa == TJ2_FP8 && fb == TJ2_FP8) return gemm_nt_kernel<TJ2_FP8, TJ2_FP8, F_NONE, F_NONE, false>;
   return nullptr;
 }
 
@@ -632,6 +739,10 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   k.col_map = p.col_map;
   k.c_bf16 = p.c_dtype == TJ2_BF16;
   k.accumulate = p.accumulate;
+  k.outl = p.outl;
+  k.rest = p.rest;
+  k.n_outl = p.n_outl;
+  k.b8 = p.outl ? operand_of(p.b8) : k.seg[0].b;
   int split = gemm_split(p.I, p.J, k.nchunks);
   if (split > 1 && (!p.partial || p.partial_bytes < (size_t)split * p.I * p.J * sizeof(float))) split = 1;
   k.chunks_per_split = (k.nchunks + split - 1) / split;

@@ -65,6 +65,13 @@ struct GemmParams {
   int accumulate;
   float* partial;        // split-K workspace (fp32 [split][I][J]); NULL -> no split
   size_t partial_bytes;
+  // outlier-column product (outl != NULL): J output columns; column outl[i]
+  // (sorted, n_outl of them) takes row i of b8, the others (rest, sorted) take
+  // the rows of seg[0].b in order
+  QView b8;
+  const int32_t* outl;
+  const int32_t* rest;
+  int n_outl;
 };
 
 // Number of K splits used for a product of I x J outputs over nchunks 128-element

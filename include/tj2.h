@@ -178,6 +178,23 @@ tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qten
 size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K);
 
 /*
+ * Product whose output columns are split by a static outlier plan (OutControl,
+ * TetraJet-v2 technical summary, section 2.C), in one launch: with
+ * J = B->rows + B8->rows output columns,
+ *   C[i, plan->rest[j]]     = sum_k A[i,k] B[j,k]    (B NVFP4, j < B->rows)
+ *   C[i, plan->outliers[j]] = sum_k A[i,k] B8[j,k]   (B8 FP8, j < n_outliers)
+ * This is how the backward forms dX (B = re-grouped W-hat of the non-outlier
+ * channels, B8 = its FP8 outlier channels) and dW (B, B8 = re-grouped X-hat).
+ * A [I, K] NVFP4; B [J - n, K] NVFP4; B8 [n, K] FP8 with n = plan->n_outliers;
+ * plan arrays sorted ascending, device int32, 16-byte aligned, rest listing the
+ * J - n columns not in outliers.  C, ldc (>= J), c_dtype, accumulate and the
+ * workspace (nvfp4_gemm_workspace_size(I, J, K) bytes) as for nvfp4_gemm.
+ */
+tj2_status nvfp4_gemm_outlier_cols(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* B8,
+                                   const tj2_outlier_plan* plan, void* C, int32_t c_dtype, int64_t ldc,
+                                   int32_t accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Forward of the NVFP4 linear layer Y = X W^T (section 2.A), X [M, K] bf16,
  * W [N, K].
  *   W_master != NULL: quantize the fp32 masters into *Wq (and *W8 with a plan);

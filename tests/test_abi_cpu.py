@@ -30,7 +30,7 @@ def L():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_linear_fwd", "nvfp4_linear_bwd", "osci_reset_step",
+    for n in ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_outlier_cols", "nvfp4_linear_fwd", "nvfp4_linear_bwd", "osci_reset_step",
               "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes"]:
         assert n in names
 
@@ -95,6 +95,18 @@ def test_gemm_and_linear_argument_errors(L):
     assert L.nvfp4_gemm(ctypes.byref(A), ctypes.byref(B), ctypes.byref(A), None, 0x5000, _lib.F32, 32, None, 0, None, 0, None) == _lib.TJ2_ERR_ARG
     assert L.nvfp4_gemm(ctypes.byref(A), ctypes.byref(B), None, None, 0x5000, _lib.BF16, 32, None, 1, None, 0, None) == _lib.TJ2_ERR_UNSUPPORTED
     assert L.nvfp4_gemm(ctypes.byref(A), ctypes.byref(B), None, None, 0x5000, _lib.F32, 16, None, 0, None, 0, None) == _lib.TJ2_ERR_SHAPE
+    # outlier-column product: plan / B8 consistency is checked on the host
+    B8 = fake_q(_lib.FP8, 16, 128)
+    plan = _lib.PlanC(0x7000, 0x8000, 16, 0)
+    assert L.nvfp4_gemm_outlier_cols(ctypes.byref(A), ctypes.byref(B), ctypes.byref(B8), None, 0x5000, _lib.F32,
+                                     48, 0, None, 0, None) == _lib.TJ2_ERR_ARG
+    bad = _lib.PlanC(0x7000, 0x8000, 32, 0)
+    assert L.nvfp4_gemm_outlier_cols(ctypes.byref(A), ctypes.byref(B), ctypes.byref(B8), ctypes.byref(bad), 0x5000,
+                                     _lib.F32, 48, 0, None, 0, None) == _lib.TJ2_ERR_SHAPE
+    assert L.nvfp4_gemm_outlier_cols(ctypes.byref(A), ctypes.byref(B), ctypes.byref(B8), ctypes.byref(plan), 0x5000,
+                                     _lib.F32, 32, 0, None, 0, None) == _lib.TJ2_ERR_SHAPE
+    assert L.nvfp4_gemm_outlier_cols(ctypes.byref(A), ctypes.byref(B8), ctypes.byref(B), ctypes.byref(plan), 0x5000,
+                                     _lib.F32, 48, 0, None, 0, None) == _lib.TJ2_ERR_UNSUPPORTED
     Xq = fake_q(_lib.NVFP4, 64, 128)
     Wq = fake_q(_lib.NVFP4, 32, 128)
     # M not a multiple of 16

@@ -44,10 +44,14 @@ def test_gemm_mixed_fp8_segment_and_scatter():
     assert H.rel_fro(c, ogemm.gemm_nt_f64(ra, rb8)) < 1e-5
     # two segments (NVFP4 x NVFP4 + FP8 x FP8) into a column-scattered output
     ga2, gb2, ra2, rb2 = _operands(I, J, 112, seed=6)
-    a8 = tj2.quantize(H.bf16_to_device(synthetic.normal_bf16((I, 112), 1.0, 60)), out_fmt=tj2.FP8)
-    ra8 = H.oracle_qtensor_from_gpu(a8)
-    b8 = tj2.quantize(H.f32_to_device(synthetic.normal_f32((J, 112), 0.02, 61)), out_fmt=tj2.FP8)
-    rb8b = H.oracle_qtensor_from_gpu(b8)
+    a8_bits = synthetic.normal_bf16((I, 112), 1.0, 60)
+    b8_f = synthetic.normal_f32((J, 112), 0.02, 61)
+    a8 = tj2.quantize(H.bf16_to_device(a8_bits), out_fmt=tj2.FP8)
+    b8 = tj2.quantize(H.f32_to_device(b8_f), out_fmt=tj2.FP8)
+    ra8 = quant.quantize(H.bf16_values(a8_bits), fmt="fp8")
+    rb8b = quant.quantize(b8_f, fmt="fp8")
+    H.assert_q_equal(a8, ra8, what="A8")
+    H.assert_q_equal(b8, rb8b, what="B8")
     perm = np.random.default_rng(0).permutation(J + 32)[:J].astype(np.int32)
     out = torch.full((I, J + 32), 7.0, device="cuda")
     tj2.gemm(ga2, gb2, a8, b8, out=out, col_map=torch.from_numpy(perm).cuda())
@@ -95,3 +99,45 @@ def test_gemm_split_k(I, J, K):
     perm = np.random.default_rng(1).permutation(J).astype(np.int32)
     cb = tj2.gemm(ga, gb, out_dtype=torch.bfloat16, col_map=torch.from_numpy(perm).cuda(), workspace=ws)
     assert H.bf16_ulp_ok(cb[:, perm], ref)
+
+
+def _plan_cases():
+    rng = np.random.default_rng(11)
+    return [
+        ("random", 256, 400, 256, np.sort(rng.choice(400, 48, replace=False))),
+        ("tile-of-outliers", 300, 384, 384, np.concatenate([np.arange(128), np.arange(368, 384)])),
+        ("strided", 128, 256, 512, np.arange(0, 256, 8)),
+        ("edges", 64, 272, 128, np.concatenate([np.arange(8), np.arange(264, 272)])),
+        ("split-k", 256, 208, 8192, np.sort(rng.choice(208, 32, replace=False))),
+    ]
+
+
+@pytest.mark.parametrize("name,I,J,K,outl", _plan_cases(), ids=[c[0] for c in _plan_cases()])
+def test_gemm_outlier_cols(name, I, J, K, outl):
+    """One product over all J output columns of a plan: NVFP4 rows for the non-outlier
+    columns, FP8 rows for the outlier columns (backward dX / dW with OutControl)."""
+    outl = np.asarray(outl, dtype=np.int64)
+    rest = np.setdiff1d(np.arange(J), outl)
+    a_bits = synthetic.normal_bf16((I, K), 1.0, 70 + I)
+    b = synthetic.normal_f32((J, K), 0.02, 71 + J)
+    ga = tj2.quantize(H.bf16_to_device(a_bits))
+    gb = tj2.quantize(H.f32_to_device(b[rest]))
+    gb8 = tj2.quantize(H.f32_to_device(b[outl]), out_fmt=tj2.FP8)
+    ra = quant.quantize(H.bf16_values(a_bits))
+    rb = quant.quantize(np.ascontiguousarray(b[rest]))
+    rb8 = quant.quantize(np.ascontiguousarray(b[outl]), fmt="fp8")
+    H.assert_q_equal(ga, ra, what="A")
+    H.assert_q_equal(gb, rb, what="B")
+    H.assert_q_equal(gb8, rb8, what="B8")
+    ref = np.zeros((I, J))
+    ref[:, rest] = ogemm.gemm_nt_f64(ra, rb)
+    ref[:, outl] = ogemm.gemm_nt_f64(ra, rb8)
+    plan = tj2.OutlierPlan.from_indices(J, outl)
+    c = tj2.gemm_outlier_cols(ga, gb, gb8, plan).cpu().numpy()
+    assert H.rel_fro(c, ref) < 1e-5
+    cb = tj2.gemm_outlier_cols(ga, gb, gb8, plan, out_dtype=torch.bfloat16)
+    assert H.bf16_ulp_ok(cb, ref)
+    # accumulate into an fp32 output
+    out = torch.from_numpy(c).cuda()
+    tj2.gemm_outlier_cols(ga, gb, gb8, plan, out=out, accumulate=True)
+    assert H.rel_fro(out.cpu().numpy(), 2 * ref) < 1e-5
