@@ -173,11 +173,11 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const typename Dense<IN>
 // columns c0..c0+7 and rows r0..r0+15 of the input; lanes rs = 0..7 of one cg
 // are consecutive, so the 128-row outer amax is an 8-lane DPP reduction.
 // ----------------------------------------------------------------------------
-template <int IN>
+template <int IN, int CPL = 8>
 struct ColPatch;
 
 template <>
-struct ColPatch<TJ2_BF16> {
+struct ColPatch<TJ2_BF16, 8> {
   uint32_t w[16][4];
   __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
     const uint16_t* x = reinterpret_cast<const uint16_t*>(p.x);
@@ -194,7 +194,7 @@ struct ColPatch<TJ2_BF16> {
 };
 
 template <>
-struct ColPatch<TJ2_F32> {
+struct ColPatch<TJ2_F32, 8> {
   float w[16][8];
   __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
     const float* x = reinterpret_cast<const float*>(p.x);
@@ -211,7 +211,7 @@ struct ColPatch<TJ2_F32> {
 
 // NVFP4 input: dequantized value (q * s) * S in fp32 (the forward's X-hat / W-hat).
 template <>
-struct ColPatch<TJ2_NVFP4> {
+struct ColPatch<TJ2_NVFP4, 8> {
   uint32_t codes[16];
   float qs_scale[16];  // s (E4M3 inner scale of the 16-group holding the 8 columns)
   float S[16];
@@ -232,7 +232,7 @@ struct ColPatch<TJ2_NVFP4> {
 };
 
 template <>
-struct ColPatch<TJ2_FP8> {
+struct ColPatch<TJ2_FP8, 8> {
   uint32_t codes[16][2];
   float S[16];
   __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
@@ -250,22 +250,66 @@ struct ColPatch<TJ2_FP8> {
   }
 };
 
+// Packed inputs (the forward's NVFP4 / FP8 operands, re-grouped for the
+// backward) hold few bytes per element: lanes take 2 columns each, so the
+// transpose of an operand of a few thousand columns still fills the GPU.
+template <>
+struct ColPatch<TJ2_NVFP4, 2> {
+  uint32_t codes[16];  // one byte (two E2M1 codes) per row
+  float qs_scale[16];
+  float S[16];
+  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
+    const QView& q = p.xq;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int64_t r = r0 + t;
+      codes[t] = q.codes[r * q.ld_codes + (c0 >> 1)];
+      qs_scale[t] = e4m3_decode(q.s16[r * q.ld_s16 + (c0 >> 4)]);
+      S[t] = q.s128[r * q.ld_s128 + (c0 >> 7)];
+    }
+  }
+  __device__ __forceinline__ float get(int t, int k) const {
+    float qv = e2m1_value((codes[t] >> (4 * k)) & 15u);
+    return (qv * qs_scale[t]) * S[t];
+  }
+};
+
+template <>
+struct ColPatch<TJ2_FP8, 2> {
+  uint32_t codes[16];  // two bytes per row
+  float S[16];
+  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
+    const QView& q = p.xq;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int64_t r = r0 + t;
+      codes[t] = *reinterpret_cast<const uint16_t*>(q.codes + r * q.ld_codes + c0);
+      S[t] = q.s128[r * q.ld_s128 + (c0 >> 7)];
+    }
+  }
+  __device__ __forceinline__ float get(int t, int k) const { return e4m3_decode((codes[t] >> (8 * k)) & 0xFFu) * S[t]; }
+};
+
+template <int IN>
+constexpr int kColsPerLane = (IN == TJ2_NVFP4 || IN == TJ2_FP8) ? 2 : 8;
+
 template <int IN, bool FP8OUT, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
+  constexpr int CPL = kColsPerLane<IN>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int cg = lane >> 3, rs = lane & 7;
-  const int64_t c0 = ((int64_t)blockIdx.x * 4 + wave) * 64 + cg * 8;
+  const int64_t c0 = ((int64_t)blockIdx.x * 4 + wave) * (8 * CPL) + cg * CPL;
   if (c0 >= p.cols) return;  // all 8 lanes of this column patch exit together
   const int64_t r0 = (int64_t)blockIdx.y * 128 + rs * 16;
   const bool valid = r0 < p.rows;
   const int64_t R = p.rows;
 
-  ColPatch<IN> patch;
+  ColPatch<IN, CPL> patch;
   if (valid) patch.load(p, r0, c0);
 
   const QView& o = p.out;
-  static_for<8>([&](auto kc) {
+  static_for<CPL>([&](auto kc) {
     constexpr int k = decltype(kc)::value;
     float v[16];
 #pragma unroll
@@ -311,7 +355,8 @@ hipError_t run_row(const QuantParams& p, hipStream_t s) {
 template <int IN, bool FP8OUT, bool SR, bool RHT>
 hipError_t run_col(const QuantParams& p, hipStream_t s) {
   const int64_t nbR = (p.rows + 127) / 128;
-  dim3 grid((uint32_t)((p.cols + 255) / 256), (uint32_t)nbR);
+  const int64_t cols_per_block = 4 * 8 * kColsPerLane<IN>;
+  dim3 grid((uint32_t)((p.cols + cols_per_block - 1) / cols_per_block), (uint32_t)nbR);
   hipLaunchKernelGGL((quant_col_kernel<IN, FP8OUT, SR, RHT>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
