@@ -173,11 +173,11 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const typename Dense<IN>
 // columns c0..c0+7 and rows r0..r0+15 of the input; lanes rs = 0..7 of one cg
 // are consecutive, so the 128-row outer amax is an 8-lane DPP reduction.
 // ----------------------------------------------------------------------------
-template <int IN, int CPL = 8>
+template <int IN>
 struct ColPatch;
 
 template <>
-struct ColPatch<TJ2_BF16, 8> {
+struct ColPatch<TJ2_BF16> {
   uint32_t w[16][4];
   __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
     const uint16_t* x = reinterpret_cast<const uint16_t*>(p.x);
@@ -194,7 +194,7 @@ struct ColPatch<TJ2_BF16, 8> {
 };
 
 template <>
-struct ColPatch<TJ2_F32, 8> {
+struct ColPatch<TJ2_F32> {
   float w[16][8];
   __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
     const float* x = reinterpret_cast<const float*>(p.x);
@@ -209,93 +209,9 @@ struct ColPatch<TJ2_F32, 8> {
   __device__ __forceinline__ float get(int t, int k) const { return w[t][k]; }
 };
 
-// NVFP4 input: dequantized value (q * s) * S in fp32 (the forward's X-hat / W-hat).
-template <>
-struct ColPatch<TJ2_NVFP4, 8> {
-  uint32_t codes[16];
-  float qs_scale[16];  // s (E4M3 inner scale of the 16-group holding the 8 columns)
-  float S[16];
-  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
-    const QView& q = p.xq;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int64_t r = r0 + t;
-      codes[t] = *reinterpret_cast<const uint32_t*>(q.codes + r * q.ld_codes + (c0 >> 1));
-      qs_scale[t] = e4m3_decode(q.s16[r * q.ld_s16 + (c0 >> 4)]);
-      S[t] = q.s128[r * q.ld_s128 + (c0 >> 7)];
-    }
-  }
-  __device__ __forceinline__ float get(int t, int k) const {
-    float qv = e2m1_value((codes[t] >> (4 * k)) & 15u);
-    return (qv * qs_scale[t]) * S[t];
-  }
-};
-
-template <>
-struct ColPatch<TJ2_FP8, 8> {
-  uint32_t codes[16][2];
-  float S[16];
-  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
-    const QView& q = p.xq;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int64_t r = r0 + t;
-      uint2 a = *reinterpret_cast<const uint2*>(q.codes + r * q.ld_codes + c0);
-      codes[t][0] = a.x; codes[t][1] = a.y;
-      S[t] = q.s128[r * q.ld_s128 + (c0 >> 7)];
-    }
-  }
-  __device__ __forceinline__ float get(int t, int k) const {
-    return e4m3_decode((codes[t][k >> 2] >> (8 * (k & 3))) & 0xFFu) * S[t];
-  }
-};
-
-// Packed inputs (the forward's NVFP4 / FP8 operands, re-grouped for the
-// backward) hold few bytes per element: lanes take 2 columns each, so the
-// transpose of an operand of a few thousand columns still fills the GPU.
-template <>
-struct ColPatch<TJ2_NVFP4, 2> {
-  uint32_t codes[16];  // one byte (two E2M1 codes) per row
-  float qs_scale[16];
-  float S[16];
-  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
-    const QView& q = p.xq;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int64_t r = r0 + t;
-      codes[t] = q.codes[r * q.ld_codes + (c0 >> 1)];
-      qs_scale[t] = e4m3_decode(q.s16[r * q.ld_s16 + (c0 >> 4)]);
-      S[t] = q.s128[r * q.ld_s128 + (c0 >> 7)];
-    }
-  }
-  __device__ __forceinline__ float get(int t, int k) const {
-    float qv = e2m1_value((codes[t] >> (4 * k)) & 15u);
-    return (qv * qs_scale[t]) * S[t];
-  }
-};
-
-template <>
-struct ColPatch<TJ2_FP8, 2> {
-  uint32_t codes[16];  // two bytes per row
-  float S[16];
-  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
-    const QView& q = p.xq;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int64_t r = r0 + t;
-      codes[t] = *reinterpret_cast<const uint16_t*>(q.codes + r * q.ld_codes + c0);
-      S[t] = q.s128[r * q.ld_s128 + (c0 >> 7)];
-    }
-  }
-  __device__ __forceinline__ float get(int t, int k) const { return e4m3_decode((codes[t] >> (8 * k)) & 0xFFu) * S[t]; }
-};
-
-template <int IN>
-constexpr int kColsPerLane = (IN == TJ2_NVFP4 || IN == TJ2_FP8) ? 2 : 8;
-
 template <int IN, bool FP8OUT, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
-  constexpr int CPL = kColsPerLane<IN>;
+  constexpr int CPL = 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int cg = lane >> 3, rs = lane & 7;
@@ -305,7 +221,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
   const bool valid = r0 < p.rows;
   const int64_t R = p.rows;
 
-  ColPatch<IN, CPL> patch;
+  ColPatch<IN> patch;
   if (valid) patch.load(p, r0, c0);
 
   const QView& o = p.out;
@@ -340,6 +256,124 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
   });
 }
 
+// Packed inputs (NVFP4 / FP8: the forward's operands re-grouped for the
+// backward) through LDS: a workgroup stages a 128-row x 64-column tile with
+// coalesced row reads, then each lane takes 2 columns x 16 rows of it, as the
+// lane layout above (wave w: tile columns 16w..16w+15).
+template <int IN>
+struct PackedTile;
+
+template <>
+struct PackedTile<TJ2_NVFP4> {
+  static constexpr int kRowBytes = 32 + 4;  // codes of 64 columns, padded
+  uint8_t codes[128 * kRowBytes];
+  uint8_t s16[128 * 4];
+  float S[128];
+  __device__ __forceinline__ void load(const QuantParams& p, int64_t rb, int64_t c0) {
+    const QView& q = p.xq;
+    const int t = threadIdx.x, row = t >> 1, half = t & 1;
+    const int64_t r = rb + row;
+    const bool in = r < p.rows;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (in) v = *reinterpret_cast<const uint4*>(q.codes + r * q.ld_codes + (c0 >> 1) + half * 16);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * kRowBytes + half * 16);
+    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    if (half == 0) {
+      const uint32_t w = in ? *reinterpret_cast<const uint32_t*>(q.s16 + r * q.ld_s16 + (c0 >> 4)) : 0u;
+      *reinterpret_cast<uint32_t*>(s16 + row * 4) = w;
+    } else {
+      S[row] = in ? q.s128[r * q.ld_s128 + (c0 >> 7)] : 0.0f;
+    }
+  }
+  // values of tile row `row`, tile columns col, col + 1 (col even): (q * s) * S in fp32,
+  // the forward's X-hat / W-hat
+  __device__ __forceinline__ void get2(int row, int col, float& v0, float& v1) const {
+    const uint32_t b = codes[row * kRowBytes + (col >> 1)];
+    const float s = e4m3_decode(s16[row * 4 + (col >> 4)]);
+    const float Sr = S[row];
+    v0 = (e2m1_value(b & 15u) * s) * Sr;
+    v1 = (e2m1_value(b >> 4) * s) * Sr;
+  }
+};
+
+template <>
+struct PackedTile<TJ2_FP8> {
+  static constexpr int kRowBytes = 64 + 4;
+  uint8_t codes[128 * kRowBytes];
+  float S[128];
+  __device__ __forceinline__ void load(const QuantParams& p, int64_t rb, int64_t c0) {
+    const QView& q = p.xq;
+    const int t = threadIdx.x, row = t >> 1, half = t & 1;
+    const int64_t r = rb + row;
+    const bool in = r < p.rows;
+    uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
+    if (in) {
+      const uint4* src = reinterpret_cast<const uint4*>(q.codes + r * q.ld_codes + c0 + half * 32);
+      v0 = src[0];
+      v1 = src[1];
+    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * kRowBytes + half * 32);
+    dst[0] = v0.x; dst[1] = v0.y; dst[2] = v0.z; dst[3] = v0.w;
+    dst[4] = v1.x; dst[5] = v1.y; dst[6] = v1.z; dst[7] = v1.w;
+    if (half == 0) S[row] = in ? q.s128[r * q.ld_s128 + (c0 >> 7)] : 0.0f;
+  }
+  __device__ __forceinline__ void get2(int row, int col, float& v0, float& v1) const {
+    const uint32_t b = *reinterpret_cast<const uint16_t*>(codes + row * kRowBytes + col);
+    const float Sr = S[row];
+    v0 = e4m3_decode(b & 0xFFu) * Sr;
+    v1 = e4m3_decode(b >> 8) * Sr;
+  }
+};
+
+template <int IN, bool FP8OUT, bool SR, bool RHT>
+__global__ __launch_bounds__(256) void quant_col_packed_kernel(QuantParams p) {
+  __shared__ PackedTile<IN> tile;
+  const int64_t c_tile = (int64_t)blockIdx.x * 64;
+  const int64_t rb = (int64_t)blockIdx.y * 128;
+  tile.load(p, rb, c_tile);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int cg = lane >> 3, rs = lane & 7;
+  const int cl = wave * 16 + cg * 2;  // first of this lane's two tile columns
+  const int64_t c0 = c_tile + cl;
+  if (c0 >= p.cols) return;  // all 8 lanes of this column pair exit together
+  const int64_t r0 = rb + rs * 16;
+  const bool valid = r0 < p.rows;
+  const int64_t R = p.rows;
+  const QView& o = p.out;
+  float vv[2][16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) tile.get2(rs * 16 + t, cl, vv[0][t], vv[1][t]);
+  static_for<2>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    float* v = vv[k];
+    if (RHT && valid) rht16(v, p.rht_mask);
+    float a_j = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
+    const float a_o = max8_lanes(a_j);
+    const int64_t orow = c0 + k;  // output row = input column
+    uint32_t u[16];
+    if (SR && valid) {
+      const uint64_t b = ((uint64_t)orow * (uint64_t)R + (uint64_t)r0) >> 3;
+      draws8(b, p.seed, p.offset, u);
+      draws8(b + 1, p.seed, p.offset, u + 8);
+    }
+    uint32_t codes[4], s_code;
+    float S;
+    quantize_group<FP8OUT, SR>(v, a_o, a_j, u, codes, &s_code, &S);
+    // groups past the last row are the zero padding of the output's last block
+    if (!FP8OUT) {
+      *reinterpret_cast<uint2*>(o.codes + orow * o.ld_codes + (r0 >> 1)) = make_uint2(codes[0], codes[1]);
+      o.s16[orow * o.ld_s16 + (r0 >> 4)] = (uint8_t)s_code;
+    } else {
+      *reinterpret_cast<uint4*>(o.codes + orow * o.ld_codes + r0) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+    }
+    if (rs == 0) o.s128[orow * o.ld_s128 + blockIdx.y] = S;
+  });
+}
+
 template <int IN, bool GATHER, bool FP8OUT, bool SR, bool RHT>
 hipError_t run_row(const QuantParams& p, hipStream_t s) {
   const int64_t L = p.out.len;
@@ -355,9 +389,13 @@ hipError_t run_row(const QuantParams& p, hipStream_t s) {
 template <int IN, bool FP8OUT, bool SR, bool RHT>
 hipError_t run_col(const QuantParams& p, hipStream_t s) {
   const int64_t nbR = (p.rows + 127) / 128;
-  const int64_t cols_per_block = 4 * 8 * kColsPerLane<IN>;
-  dim3 grid((uint32_t)((p.cols + cols_per_block - 1) / cols_per_block), (uint32_t)nbR);
-  hipLaunchKernelGGL((quant_col_kernel<IN, FP8OUT, SR, RHT>), grid, dim3(256), 0, s, p);
+  if constexpr (IN == TJ2_NVFP4 || IN == TJ2_FP8) {
+    dim3 grid((uint32_t)((p.cols + 63) / 64), (uint32_t)nbR);
+    hipLaunchKernelGGL((quant_col_packed_kernel<IN, FP8OUT, SR, RHT>), grid, dim3(256), 0, s, p);
+  } else {
+    dim3 grid((uint32_t)((p.cols + 255) / 256), (uint32_t)nbR);
+    hipLaunchKernelGGL((quant_col_kernel<IN, FP8OUT, SR, RHT>), grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
