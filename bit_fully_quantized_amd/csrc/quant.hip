@@ -59,13 +59,6 @@ struct Dense<TJ2_F32> {
   static __device__ __forceinline__ float load1(const T* p) { return *p; }
 };
 
-__device__ __forceinline__ float e2m1_value(uint32_t n) {
-  // magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} from the bit fields
-  uint32_t e = (n >> 1) & 3u, m = n & 1u;
-  float mag = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
-  return (n & 8u) ? -mag : mag;
-}
-
 // ----------------------------------------------------------------------------
 // Per-group quantization of 16 values v (already transformed if RHT), given
 // the outer amax a_o and, for SR, the draws r (top-aligned 16-bit).  Writes 8
@@ -148,8 +141,10 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const typename Dense<IN>
   for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
   const float a_o = max8_lanes(a_j);
 
+  // padding groups take draws as well: their values are zero, which every draw
+  // rounds to zero, and no branch keeps the draws' registers apart
   uint32_t u[16];
-  if (SR && valid) {
+  if (SR) {
     const uint64_t e0 = (uint64_t)row * (uint64_t)L + j * 16u;
     draws8(e0 >> 3, seed, offset, u);
     draws8((e0 >> 3) + 1, seed, offset, u + 8);
@@ -237,7 +232,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
     const float a_o = max8_lanes(a_j);
     const int64_t orow = c0 + k;  // output row = input column
     uint32_t u[16];
-    if (SR && valid) {
+    if (SR) {  // groups past the last row are zeros: any draw keeps them zero
       // draws follow the output position orow * R + r0 + t: two whole Philox blocks
       const uint64_t b = ((uint64_t)orow * (uint64_t)R + (uint64_t)r0) >> 3;
       draws8(b, p.seed, p.offset, u);
@@ -288,11 +283,13 @@ struct PackedTile<TJ2_NVFP4> {
   // values of tile row `row`, tile columns col, col + 1 (col even): (q * s) * S in fp32,
   // the forward's X-hat / W-hat
   __device__ __forceinline__ void get2(int row, int col, float& v0, float& v1) const {
+    typedef float float2_t __attribute__((ext_vector_type(2)));
     const uint32_t b = codes[row * kRowBytes + (col >> 1)];
     const float s = e4m3_decode(s16[row * 4 + (col >> 4)]);
     const float Sr = S[row];
-    v0 = (e2m1_value(b & 15u) * s) * Sr;
-    v1 = (e2m1_value(b >> 4) * s) * Sr;
+    const float2_t q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b, 1.0f, 0);  // exact E2M1 values
+    v0 = (q.x * s) * Sr;
+    v1 = (q.y * s) * Sr;
   }
 };
 
@@ -318,10 +315,12 @@ struct PackedTile<TJ2_FP8> {
     if (half == 0) S[row] = in ? q.s128[r * q.ld_s128 + (c0 >> 7)] : 0.0f;
   }
   __device__ __forceinline__ void get2(int row, int col, float& v0, float& v1) const {
+    typedef float float2_t __attribute__((ext_vector_type(2)));
     const uint32_t b = *reinterpret_cast<const uint16_t*>(codes + row * kRowBytes + col);
     const float Sr = S[row];
-    v0 = e4m3_decode(b & 0xFFu) * Sr;
-    v1 = e4m3_decode(b >> 8) * Sr;
+    const float2_t q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b, 1.0f, false);  // exact E4M3 values
+    v0 = q.x * Sr;
+    v1 = q.y * Sr;
   }
 };
 
@@ -355,7 +354,7 @@ __global__ __launch_bounds__(256) void quant_col_packed_kernel(QuantParams p) {
     const float a_o = max8_lanes(a_j);
     const int64_t orow = c0 + k;  // output row = input column
     uint32_t u[16];
-    if (SR && valid) {
+    if (SR) {  // groups past the last row are zeros: any draw keeps them zero
       const uint64_t b = ((uint64_t)orow * (uint64_t)R + (uint64_t)r0) >> 3;
       draws8(b, p.seed, p.offset, u);
       draws8(b + 1, p.seed, p.offset, u + 8);

@@ -57,10 +57,12 @@ __device__ __forceinline__ float e4m3_round_up(float r, uint32_t* code) {
   return __uint_as_float(b);
 }
 
+// Value of an E4M3FN byte (finite codes).  gfx950's v_cvt_scalef32_pk_f32_fp8
+// with scale 1.0 is exact on them: every E4M3 value is an fp32 value.
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  return (c & 0x80u) ? -mag : mag;
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  const float2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false);
+  return v.x;
 }
 
 // ---------------------------------------------------------------------------
@@ -109,10 +111,11 @@ __device__ __forceinline__ void e2m1_rtn16(const float y[16], uint32_t out[2]) {
 // element per instruction (the second slot converts 0.0, code 0), so every
 // element gets its own draw.  The instruction leaves bytes 1..3 of its result
 // undefined (it does not merge into an old value), so only byte 0 is used:
-// pairs are merged with a shift-or, then bytes are gathered with v_perm.
+// pairs are merged with a shift-or, then bytes are gathered with v_perm.  The
+// draw doubles as the old value, so no register is cleared for it.
 __device__ __forceinline__ uint32_t e2m1_sr1(float y, uint32_t r) {
   typedef float float2_t __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, float2_t{y, 0.0f}, r, 1.0f, 0);
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(r, float2_t{y, 0.0f}, r, 1.0f, 0);
 }
 
 __device__ __forceinline__ uint32_t e2m1_sr8(const float* y, const uint32_t* r) {
@@ -173,8 +176,9 @@ __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2,
   for (int r = 0; r < 10; ++r) {
     uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
     uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
-    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-input xor in one instruction (truth table 0x96)
+    uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -220,18 +224,16 @@ __device__ __forceinline__ void rht16(float v[16], uint32_t mask) {
 
 // ---------------------------------------------------------------------------
 // Max over the 8 consecutive lanes of an aligned group (DPP: quad swaps, then
-// the half-row mirror, which pairs each lane with one in the other quad).
+// the half-row mirror, which pairs each lane with one in the other quad).  The
+// inputs are amaxes (>= 0, never NaN), whose fp32 bit patterns order as
+// unsigned integers, so each step is one integer max with a DPP operand.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float max8_lanes(float x) {
-  int xi = __float_as_int(x);
-  int y = __builtin_amdgcn_update_dpp(xi, xi, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-  x = fmaxf(x, __int_as_float(y));
-  xi = __float_as_int(x);
-  y = __builtin_amdgcn_update_dpp(xi, xi, 0x4E, 0xF, 0xF, false);       // quad_perm [2,3,0,1]
-  x = fmaxf(x, __int_as_float(y));
-  xi = __float_as_int(x);
-  y = __builtin_amdgcn_update_dpp(xi, xi, 0x141, 0xF, 0xF, false);      // row_half_mirror
-  return fmaxf(x, __int_as_float(y));
+  uint32_t xi = __float_as_uint(x);
+  xi = max(xi, (uint32_t)__builtin_amdgcn_mov_dpp((int)xi, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  xi = max(xi, (uint32_t)__builtin_amdgcn_mov_dpp((int)xi, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  xi = max(xi, (uint32_t)__builtin_amdgcn_mov_dpp((int)xi, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  return __uint_as_float(xi);
 }
 
 // ---------------------------------------------------------------------------
