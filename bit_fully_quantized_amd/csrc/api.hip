@@ -124,6 +124,28 @@ tj2_status run_quant(const void* x, int x_dtype, const tj2_qtensor* x_q, int64_t
   return hip_check(launch_quant(p, s), "quantize launch");
 }
 
+// One read of X (or W) into its NVFP4 rest columns and FP8 outlier columns.
+// Rows wider than 32 KB go through the two gathering row quantizations.
+tj2_status run_split(const void* x, int x_dtype, int64_t rows, int64_t K, const tj2_outlier_plan* plan,
+                     const tj2_qtensor* q4, const tj2_qtensor* q8, hipStream_t s) {
+  const int64_t no = plan->n_outliers, K1 = K - no;
+  if (K * (x_dtype == TJ2_BF16 ? 2 : 4) > 32768) {
+    TJ2_TRY(run_quant(x, x_dtype, nullptr, rows, K, plan->rest, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, q4, s));
+    return run_quant(x, x_dtype, nullptr, rows, K, plan->outliers, no, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, q8, s);
+  }
+  SplitParams p;
+  memset(&p, 0, sizeof(p));
+  p.in_dtype = x_dtype;
+  p.x = x;
+  p.rows = rows;
+  p.cols = K;
+  p.rest = plan->rest;
+  p.outl = plan->outliers;
+  p.q4 = make_view(*q4);
+  p.q8 = make_view(*q8);
+  return hip_check(launch_quant_split(p, s), "split quantize launch");
+}
+
 tj2_status run_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2, const tj2_qtensor* B2,
                     void* C, int c_dtype, int64_t ldc, const int32_t* col_map, int accumulate, void* ws,
                     size_t ws_bytes, hipStream_t s) {
@@ -341,12 +363,12 @@ tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, cons
     TJ2_TRY(check_qtensor(X8, "X8", TJ2_FP8, M, no));
     TJ2_TRY(check_qtensor(W8, "W8", TJ2_FP8, N, no));
   }
-  const int32_t* rest = plan ? plan->rest : nullptr;
-  TJ2_TRY(run_quant(X, TJ2_BF16, nullptr, M, K, rest, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Xq, s));
-  if (plan) TJ2_TRY(run_quant(X, TJ2_BF16, nullptr, M, K, plan->outliers, no, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, X8, s));
-  if (W_master) {
-    TJ2_TRY(run_quant(W_master, TJ2_F32, nullptr, N, K, rest, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Wq, s));
-    if (plan) TJ2_TRY(run_quant(W_master, TJ2_F32, nullptr, N, K, plan->outliers, no, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, W8, s));
+  if (plan) {
+    TJ2_TRY(run_split(X, TJ2_BF16, M, K, plan, Xq, X8, s));
+    if (W_master) TJ2_TRY(run_split(W_master, TJ2_F32, N, K, plan, Wq, W8, s));
+  } else {
+    TJ2_TRY(run_quant(X, TJ2_BF16, nullptr, M, K, nullptr, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Xq, s));
+    if (W_master) TJ2_TRY(run_quant(W_master, TJ2_F32, nullptr, N, K, nullptr, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Wq, s));
   }
   TJ2_TRY(run_gemm(Xq, Wq, plan ? X8 : nullptr, plan ? W8 : nullptr, Y, y_dtype, N, nullptr, 0, nullptr, 0, s));
   return ok();

@@ -15,6 +15,8 @@
 //    (bf16) load, so lanes with neighbouring column patches read contiguous
 //    128-byte segments.  Stochastic draws follow the output position, so each
 //    16-element group uses two whole Philox blocks generated on the spot.
+#include <algorithm>
+
 #include "tj2_device.h"
 #include "tj2_internal.h"
 
@@ -92,9 +94,7 @@ __device__ __forceinline__ void quantize_group(const float v[16], float a_o, flo
     if (SR) {
       e4m3_sr16(y, r, codes);
     } else {
-      codes[0] = codes[1] = codes[2] = codes[3] = 0u;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) codes[t >> 2] |= e4m3_rne(y[t]) << (8 * (t & 3));
+      e4m3_rne16(y, codes);
     }
   }
 }
@@ -164,102 +164,65 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const typename Dense<IN>
 }
 
 // ----------------------------------------------------------------------------
-// Column grouping (16x1), output transposed.  Lane (cg, rs) of a wave owns
-// columns c0..c0+7 and rows r0..r0+15 of the input; lanes rs = 0..7 of one cg
-// are consecutive, so the 128-row outer amax is an 8-lane DPP reduction.
+// Column grouping (16x1), output transposed.  A workgroup stages a 128-row x
+// 64-column tile of the input in LDS with coalesced row reads; lane (cg, rs) of
+// wave w then takes tile columns 16w + 2cg, +1 and rows 16rs..16rs+15, one
+// 16-element group per column.  Lanes rs = 0..7 of one cg are consecutive, so
+// the 128-row outer amax is an 8-lane DPP reduction.  Inputs: bf16 / fp32
+// activations and gradients, or the forward's packed NVFP4 / FP8 operands
+// (X-hat, W-hat, the FP8 slices) re-grouped for the backward.
 // ----------------------------------------------------------------------------
 template <int IN>
-struct ColPatch;
+struct ColTile;
 
 template <>
-struct ColPatch<TJ2_BF16> {
-  uint32_t w[16][4];
-  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
+struct ColTile<TJ2_BF16> {
+  static constexpr int kRowWords = 32 + 1;  // 64 bf16, padded
+  uint32_t w[128 * kRowWords];
+  __device__ __forceinline__ void load(const QuantParams& p, int64_t rb, int64_t c_tile) {
     const uint16_t* x = reinterpret_cast<const uint16_t*>(p.x);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      uint4 a = *reinterpret_cast<const uint4*>(x + (r0 + t) * p.ld_x + c0);
-      w[t][0] = a.x; w[t][1] = a.y; w[t][2] = a.z; w[t][3] = a.w;
+    for (int i = 0; i < 4; ++i) {
+      const int idx = threadIdx.x + 256 * i, row = idx >> 3, seg = idx & 7;
+      const int64_t r = rb + row, c = c_tile + seg * 8;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < p.rows && c < p.cols) v = *reinterpret_cast<const uint4*>(x + r * p.ld_x + c);
+      uint32_t* d = w + row * kRowWords + seg * 4;
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
   }
-  __device__ __forceinline__ float get(int t, int k) const {
-    uint32_t x = w[t][k >> 1];
-    return __uint_as_float((k & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  __device__ __forceinline__ void get2(int row, int col, float& v0, float& v1) const {
+    const uint32_t b = w[row * kRowWords + (col >> 1)];
+    v0 = __uint_as_float(b << 16);
+    v1 = __uint_as_float(b & 0xFFFF0000u);
   }
 };
 
 template <>
-struct ColPatch<TJ2_F32> {
-  float w[16][8];
-  __device__ __forceinline__ void load(const QuantParams& p, int64_t r0, int64_t c0) {
+struct ColTile<TJ2_F32> {
+  static constexpr int kRowWords = 64 + 2;  // padded, rows stay 8-byte aligned
+  float w[128 * kRowWords];
+  __device__ __forceinline__ void load(const QuantParams& p, int64_t rb, int64_t c_tile) {
     const float* x = reinterpret_cast<const float*>(p.x);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float4 a = *reinterpret_cast<const float4*>(x + (r0 + t) * p.ld_x + c0);
-      float4 b = *reinterpret_cast<const float4*>(x + (r0 + t) * p.ld_x + c0 + 4);
-      w[t][0] = a.x; w[t][1] = a.y; w[t][2] = a.z; w[t][3] = a.w;
-      w[t][4] = b.x; w[t][5] = b.y; w[t][6] = b.z; w[t][7] = b.w;
+    for (int i = 0; i < 8; ++i) {
+      const int idx = threadIdx.x + 256 * i, row = idx >> 4, seg = idx & 15;
+      const int64_t r = rb + row, c = c_tile + seg * 4;
+      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (r < p.rows && c < p.cols) v = *reinterpret_cast<const float4*>(x + r * p.ld_x + c);
+      float* d = w + row * kRowWords + seg * 4;
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
   }
-  __device__ __forceinline__ float get(int t, int k) const { return w[t][k]; }
+  __device__ __forceinline__ void get2(int row, int col, float& v0, float& v1) const {
+    const float2 b = *reinterpret_cast<const float2*>(w + row * kRowWords + col);
+    v0 = b.x;
+    v1 = b.y;
+  }
 };
 
-template <int IN, bool FP8OUT, bool SR, bool RHT>
-__global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
-  constexpr int CPL = 8;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int cg = lane >> 3, rs = lane & 7;
-  const int64_t c0 = ((int64_t)blockIdx.x * 4 + wave) * (8 * CPL) + cg * CPL;
-  if (c0 >= p.cols) return;  // all 8 lanes of this column patch exit together
-  const int64_t r0 = (int64_t)blockIdx.y * 128 + rs * 16;
-  const bool valid = r0 < p.rows;
-  const int64_t R = p.rows;
-
-  ColPatch<IN> patch;
-  if (valid) patch.load(p, r0, c0);
-
-  const QView& o = p.out;
-  static_for<CPL>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    float v[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) v[t] = valid ? patch.get(t, k) : 0.0f;
-    if (RHT && valid) rht16(v, p.rht_mask);
-    float a_j = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
-    const float a_o = max8_lanes(a_j);
-    const int64_t orow = c0 + k;  // output row = input column
-    uint32_t u[16];
-    if (SR) {  // groups past the last row are zeros: any draw keeps them zero
-      // draws follow the output position orow * R + r0 + t: two whole Philox blocks
-      const uint64_t b = ((uint64_t)orow * (uint64_t)R + (uint64_t)r0) >> 3;
-      draws8(b, p.seed, p.offset, u);
-      draws8(b + 1, p.seed, p.offset, u + 8);
-    }
-    uint32_t codes[4], s_code;
-    float S;
-    quantize_group<FP8OUT, SR>(v, a_o, a_j, u, codes, &s_code, &S);
-    if (!FP8OUT) {
-      *reinterpret_cast<uint2*>(o.codes + orow * o.ld_codes + (r0 >> 1)) = make_uint2(codes[0], codes[1]);
-      o.s16[orow * o.ld_s16 + (r0 >> 4)] = (uint8_t)s_code;
-    } else {
-      *reinterpret_cast<uint4*>(o.codes + orow * o.ld_codes + r0) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
-    }
-    if (rs == 0) o.s128[orow * o.ld_s128 + blockIdx.y] = S;
-  });
-}
-
-// Packed inputs (NVFP4 / FP8: the forward's operands re-grouped for the
-// backward) through LDS: a workgroup stages a 128-row x 64-column tile with
-// coalesced row reads, then each lane takes 2 columns x 16 rows of it, as the
-// lane layout above (wave w: tile columns 16w..16w+15).
-template <int IN>
-struct PackedTile;
-
 template <>
-struct PackedTile<TJ2_NVFP4> {
+struct ColTile<TJ2_NVFP4> {
   static constexpr int kRowBytes = 32 + 4;  // codes of 64 columns, padded
   uint8_t codes[128 * kRowBytes];
   uint8_t s16[128 * 4];
@@ -294,7 +257,7 @@ struct PackedTile<TJ2_NVFP4> {
 };
 
 template <>
-struct PackedTile<TJ2_FP8> {
+struct ColTile<TJ2_FP8> {
   static constexpr int kRowBytes = 64 + 4;
   uint8_t codes[128 * kRowBytes];
   float S[128];
@@ -325,8 +288,8 @@ struct PackedTile<TJ2_FP8> {
 };
 
 template <int IN, bool FP8OUT, bool SR, bool RHT>
-__global__ __launch_bounds__(256) void quant_col_packed_kernel(QuantParams p) {
-  __shared__ PackedTile<IN> tile;
+__global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
+  __shared__ ColTile<IN> tile;
   const int64_t c_tile = (int64_t)blockIdx.x * 64;
   const int64_t rb = (int64_t)blockIdx.y * 128;
   tile.load(p, rb, c_tile);
@@ -387,14 +350,8 @@ hipError_t run_row(const QuantParams& p, hipStream_t s) {
 
 template <int IN, bool FP8OUT, bool SR, bool RHT>
 hipError_t run_col(const QuantParams& p, hipStream_t s) {
-  const int64_t nbR = (p.rows + 127) / 128;
-  if constexpr (IN == TJ2_NVFP4 || IN == TJ2_FP8) {
-    dim3 grid((uint32_t)((p.cols + 63) / 64), (uint32_t)nbR);
-    hipLaunchKernelGGL((quant_col_packed_kernel<IN, FP8OUT, SR, RHT>), grid, dim3(256), 0, s, p);
-  } else {
-    dim3 grid((uint32_t)((p.cols + 255) / 256), (uint32_t)nbR);
-    hipLaunchKernelGGL((quant_col_kernel<IN, FP8OUT, SR, RHT>), grid, dim3(256), 0, s, p);
-  }
+  dim3 grid((uint32_t)((p.cols + 63) / 64), (uint32_t)((p.rows + 127) / 128));
+  hipLaunchKernelGGL((quant_col_kernel<IN, FP8OUT, SR, RHT>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -425,6 +382,117 @@ hipError_t dispatch_col(const QuantParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+// ----------------------------------------------------------------------------
+// Forward split with an outlier plan (TetraJet-v2 technical summary, section
+// 2.C): a workgroup stages R whole input rows in LDS with coalesced reads, then
+// each lane takes 16-element groups (8 nb(rest) NVFP4 and 8 nb(outl) FP8 ones
+// per row) and gathers their columns from LDS.  Groups of one outer block are 8
+// consecutive lanes, as in the row kernel, so their amax is a DPP reduction.
+// ----------------------------------------------------------------------------
+template <int IN>
+__global__ __launch_bounds__(256) void quant_split_kernel(SplitParams p, int R) {
+  extern __shared__ uint32_t rows_lds[];
+  using T = typename Dense<IN>::T;
+  const int64_t r_base = (int64_t)blockIdx.x * R;
+  const int nrows = (int)min((int64_t)R, p.rows - r_base);
+  const int units = (int)(p.cols * (int64_t)sizeof(T) / 16);  // 16-byte units per row
+  {
+    // the rows are contiguous and hold at most 32 KB: eight 16-byte loads per
+    // lane, all in flight before the LDS writes
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(p.x) + r_base * p.cols);
+    uint4* dst = reinterpret_cast<uint4*>(rows_lds);
+    const int n = nrows * units;
+    uint4 t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int u = i * 256 + (int)threadIdx.x;
+      t[i] = u < n ? src[u] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int u = i * 256 + (int)threadIdx.x;
+      if (u < n) dst[u] = t[i];
+    }
+  }
+  __syncthreads();
+  const T* xs = reinterpret_cast<const T*>(rows_lds);
+  // the NVFP4 groups of all rows first, then the FP8 groups, so that only one
+  // wave holds both kinds
+  const int G4 = (int)p.q4.nb * 8, G8 = (int)p.q8.nb * 8;
+  const int total4 = nrows * G4, total = total4 + nrows * G8;  // multiples of 8
+  for (int g = threadIdx.x; g < total; g += 256) {
+    const bool fp8 = g >= total4;
+    const int Gk = fp8 ? G8 : G4, gk = fp8 ? g - total4 : g;
+    const int row = gk / Gk, jj = gk - row * Gk;
+    const int64_t len = fp8 ? p.q8.len : p.q4.len;
+    const int32_t* idx = fp8 ? p.outl : p.rest;
+    const bool valid = (int64_t)jj * 16 < len;
+    float v[16];
+    if (valid) {
+      const int4* ip = reinterpret_cast<const int4*>(idx + jj * 16);
+      const T* xr = xs + (int64_t)row * p.cols;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int4 c = ip[q];
+        v[4 * q + 0] = Dense<IN>::load1(xr + c.x);
+        v[4 * q + 1] = Dense<IN>::load1(xr + c.y);
+        v[4 * q + 2] = Dense<IN>::load1(xr + c.z);
+        v[4 * q + 3] = Dense<IN>::load1(xr + c.w);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) v[t] = 0.0f;
+    }
+    float a_j = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
+    const float a_o = max8_lanes(a_j);
+    const int64_t orow = r_base + row;
+    uint32_t codes[4], s_code;
+    float S;
+    if (!fp8) {
+      quantize_group<false, false>(v, a_o, a_j, nullptr, codes, &s_code, &S);
+      const QView& o = p.q4;
+      *reinterpret_cast<uint2*>(o.codes + orow * o.ld_codes + jj * 8) = make_uint2(codes[0], codes[1]);
+      o.s16[orow * o.ld_s16 + jj] = (uint8_t)s_code;
+      if ((jj & 7) == 0) o.s128[orow * o.ld_s128 + (jj >> 3)] = S;
+    } else {
+      quantize_group<true, false>(v, a_o, a_j, nullptr, codes, &s_code, &S);
+      const QView& o = p.q8;
+      *reinterpret_cast<uint4*>(o.codes + orow * o.ld_codes + jj * 16) =
+          make_uint4(codes[0], codes[1], codes[2], codes[3]);
+      if ((jj & 7) == 0) o.s128[orow * o.ld_s128 + (jj >> 3)] = S;
+    }
+  }
+}
+
+// Rows per workgroup: the groups of R rows fill whole 256-lane passes as well
+// as possible, within 32 KB of LDS (several workgroups per CU).
+int split_rows_per_wg(int64_t cols, int esize, int64_t groups_per_row) {
+  const int64_t rmax = std::max<int64_t>(1, std::min<int64_t>(16, 32768 / (cols * esize)));
+  int best = 1;
+  double best_eff = 0.0;
+  for (int64_t r = 1; r <= rmax; ++r) {
+    const int64_t work = r * groups_per_row, passes = (work + 255) / 256;
+    const double eff = (double)work / (double)(passes * 256);
+    if (eff > best_eff + 1e-9) { best_eff = eff; best = (int)r; }
+  }
+  return best;
+}
+
+hipError_t launch_quant_split(const SplitParams& p, hipStream_t s) {
+  const int esize = p.in_dtype == TJ2_BF16 ? 2 : 4;
+  if (p.cols * esize > 32768) return hipErrorInvalidValue;  // the kernel stages at most 32 KB
+  const int R = split_rows_per_wg(p.cols, esize, (p.q4.nb + p.q8.nb) * 8);
+  const uint32_t blocks = (uint32_t)((p.rows + R - 1) / R);
+  const size_t lds = (size_t)R * p.cols * esize;
+  if (p.in_dtype == TJ2_BF16)
+    hipLaunchKernelGGL(quant_split_kernel<TJ2_BF16>, dim3(blocks), dim3(256), lds, s, p, R);
+  else
+    hipLaunchKernelGGL(quant_split_kernel<TJ2_F32>, dim3(blocks), dim3(256), lds, s, p, R);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant(const QuantParams& p, hipStream_t s) {
   if (p.grouping == TJ2_GROUP_ROW) {

@@ -49,6 +49,20 @@ struct QuantParams {
 
 hipError_t launch_quant(const QuantParams& p, hipStream_t s);
 
+// Forward split of a dense row-major input with an outlier plan: the columns
+// in `rest` quantized to NVFP4 (q4) and the columns in `outl` to FP8 (q8), both
+// round-to-nearest along rows, from one read of the input.
+struct SplitParams {
+  int in_dtype;  // TJ2_BF16 or TJ2_F32
+  const void* x;
+  int64_t rows, cols;
+  const int32_t* rest;
+  const int32_t* outl;
+  QView q4, q8;
+};
+
+hipError_t launch_quant_split(const SplitParams& p, hipStream_t s);
+
 struct GemmSeg {
   QView a, b;  // a: [I, K], b: [J, K] grouped along K
   int64_t K;
