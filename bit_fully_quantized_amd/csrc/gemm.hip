@@ -77,7 +77,8 @@ struct GemmKArgs {
 //  * A operand: 64 consecutive K elements (half of a 128-chunk) of one row.
 //    NVFP4 uses q[0..1] (codes) and q[2].x (four inner scales); FP8 q[0..3].
 //  * B operand: 32 consecutive K elements (a quarter chunk) of one row.
-//    NVFP4 uses q[0] (codes) and q[1].x (two inner scales); FP8 q[0..1].
+//    NVFP4 uses q[0] (codes), q[1].x (the aligned word holding its two inner
+//    scales) and q[1].y (their bit offset in it); FP8 q[0..1].
 struct Slice {
   uint4 q[4];
   float S;  // outer scale of the chunk
@@ -98,7 +99,10 @@ struct Op<TJ2_NVFP4> {
   }
   static __device__ __forceinline__ void load_quarter(const OperandK& o, uint32_t rn, int kc, int qt, Slice& s) {
     s.q[0] = *reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 64 + (rn * 64 + qt * 16));
-    s.q[1].x = *reinterpret_cast<const uint16_t*>(o.s16 + (size_t)kc * 8 + (rn * 8 + qt * 2));
+    // the aligned word holding this quarter's two inner scales, and its shift: a
+    // full-word load lands in the slice's own register (no extension on use)
+    s.q[1].x = *reinterpret_cast<const uint32_t*>(o.s16 + (size_t)kc * 8 + (rn * 8 + (qt >> 1) * 4));
+    s.q[1].y = (uint32_t)(qt & 1) * 16u;
     s.S = (o.s128 + kc)[rn];
   }
   template <int BYTE>
@@ -121,7 +125,7 @@ struct Op<TJ2_NVFP4> {
   // piecewise decode used by the pipelined kernel: scale preparation, then one
   // 8-element fragment (A half slice) or unit (B quarter slice) at a time
   static __device__ __forceinline__ void prep_a(const Slice& s, half2_t (&sg)[4]) { scales(s.q[2].x, sg); }
-  static __device__ __forceinline__ void prep_b(const Slice& s, half2_t (&sg)[4]) { scales(s.q[1].x, sg); }
+  static __device__ __forceinline__ void prep_b(const Slice& s, half2_t (&sg)[4]) { scales(s.q[1].x >> s.q[1].y, sg); }
   template <int F>
   static __device__ __forceinline__ half8_t frag_a(const Slice& s, const half2_t (&sg)[4]) {
     const uint4& v = s.q[F >> 2];
@@ -145,7 +149,7 @@ struct Op<TJ2_NVFP4> {
   // quarter slice -> 32 f16 values at dst (16-byte aligned)
   static __device__ __forceinline__ void decode_quarter(const Slice& s, _Float16* dst) {
     half2_t sg[4];
-    scales(s.q[1].x, sg);
+    scales(s.q[1].x >> s.q[1].y, sg);
     half8_t* out = reinterpret_cast<half8_t*>(dst);
     out[0] = dec8(s.q[0].x, sg[0]);
     out[1] = dec8(s.q[0].y, sg[0]);
@@ -269,7 +273,8 @@ struct FmtMixB {
     const uint8_t* c = t.b8 ? c8 : c4;
     b.q[0] = *reinterpret_cast<const uint4*>(c);
     b.q[1] = *reinterpret_cast<const uint4*>(t.b8 ? c8 + 16 : c4);
-    b.q[2].x = *reinterpret_cast<const uint16_t*>(p.seg[0].b.s16 + (size_t)g * 8 + (t.brn[0] * 8 + t.bq * 2));
+    b.q[2].x = *reinterpret_cast<const uint32_t*>(p.seg[0].b.s16 + (size_t)g * 8 + (t.brn[0] * 8 + (t.bq >> 1) * 4));
+    b.q[2].y = (uint32_t)(t.bq & 1) * 16u;
     b.S = t.b8 ? (p.b8.s128 + g)[t.brn[1]] : (p.seg[0].b.s128 + g)[t.brn[0]];
   }
 };
@@ -332,7 +337,7 @@ struct FmtsMixB {
   static __device__ __forceinline__ void prep_a(const Slice& a, half2_t (&sg)[4]) { Op<TJ2_NVFP4>::prep_a(a, sg); }
   // the NVFP4 inner scales sit in q[2].x of a B slice here (q[1] holds FP8 codes)
   static __device__ __forceinline__ void prep_b(const Slice& b, half2_t (&sg)[4]) {
-    Op<TJ2_NVFP4>::scales(b.q[2].x, sg);
+    Op<TJ2_NVFP4>::scales(b.q[2].x >> b.q[2].y, sg);
   }
   template <int F>
   static __device__ __forceinline__ half8_t frag_a(const Slice& a, const half2_t (&sg)[4], bool) {
@@ -529,7 +534,6 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     // ring slot 3 stands for "chunk -1": zero scales for the first chunk's promotion of part[1]
     sm.sb[3][threadIdx.x >> 2] = 0.0f;
     sm.sa[3][t.w * 32 + (t.lane & 31)] = 0.0f;
-    F::fetch_a(p, t, 0, s1, a);
     F::fetch_b(p, t, 0, s1, b1);
     if constexpr (MIXB) {
       half2_t sg[4];
@@ -543,7 +547,13 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     } else {
       stage_first_b<FB0>(sm, t, b1);
     }
+    // loads in flight enter the loop in the order the loop keeps them (the B
+    // slice staged next, the A slice, the B slice after), so the wait counts
+    // the compiler derives for the loop body hold on its first pass too
     F::fetch_b(p, t, 1, s1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    F::fetch_a(p, t, 0, s1, a);
+    __builtin_amdgcn_sched_barrier(0);
     F::fetch_b(p, t, 2, s1, b2);
     barrier_lds();
     constexpr int kFragAhead = kFragAheadFor<MIXB>;
@@ -554,16 +564,24 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
         bf[decltype(f)::value] = ld8(bb + decltype(f)::value * 8);
       });
     }
-    // b1 holds the B slice of the chunk to stage next, b2 the one after it
-    for (int it = 0; it < s1; ++it) {
+    // Chunk it stages the B slice of chunk it + 1 from b1 (it even) or b2 (it
+    // odd) and, once that staging is done (its sync slot), refills the same
+    // slice with chunk it + 3.  Two chunks per loop iteration keep the slices
+    // in fixed registers, so no copy at the back edge waits on a fresh load.
+    auto run = [&](int it, Slice& nb) __attribute__((always_inline)) {
       auto fa = [&](Slice& sl) __attribute__((always_inline)) { F::fetch_a(p, t, it + 1, s1, sl); };
       auto sync = [&]() __attribute__((always_inline)) {
-        b1 = b2;
-        F::fetch_b(p, t, it + 3, s1, b2);
+        F::fetch_b(p, t, it + 3, s1, nb);
         barrier_lds();  // chunk it+1's B staged; this chunk's stage may be refilled
       };
-      chunk<FM, kFragAhead>(sm, t, it, false, t.b8, af, bf, acc, part, a, b1, fa, sync);
+      chunk<FM, kFragAhead>(sm, t, it, false, t.b8, af, bf, acc, part, a, nb, fa, sync);
+    };
+    int it = 0;
+    for (; it + 1 < s1; it += 2) {
+      run(it, b1);
+      run(it + 1, b2);
     }
+    if (it < s1) run(it, b1);
     Scl scl;
     read_scl(sm, t, (s1 - 1) & 3, 3, scl);
     static_for<16>([&](auto e) __attribute__((always_inline)) {

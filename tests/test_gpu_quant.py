@@ -186,3 +186,35 @@ def test_rtn_exhaustive_unit_step():
     ref = ref_idx | (torch.signbit(vals).to(torch.int64) << 3)
     bad = (nib != ref).sum().item()
     assert bad == 0, f"{bad} mismatches"
+
+
+def test_fp8_rtn_exhaustive_unit_step():
+    """Every fp32 magnitude in [2^-10, 448], both signs, quantized to FP8 where the element step is
+    1 (outer max 448 -> S = 1): each code must equal round-to-nearest-even onto the E4M3 grid,
+    computed independently with torch.round (half to even) on the grid step of each binade."""
+    lo = int(np.float32(2.0 ** -10).view(np.int32))
+    hi = int(np.float32(448.0).view(np.int32))
+    bits = torch.arange(lo, hi + 1, dtype=torch.int64, device="cuda").to(torch.int32)
+    vals = bits.view(torch.float32)
+    vals = torch.where(torch.arange(vals.numel(), device="cuda") % 2 == 0, vals, -vals)
+    per_row = 127
+    rows = (vals.numel() + per_row - 1) // per_row
+    X = torch.zeros(rows, 128, dtype=torch.float32, device="cuda")
+    X[:, 0] = 448.0
+    slots = torch.zeros(rows * per_row, dtype=torch.float32, device="cuda")
+    slots[: vals.numel()] = vals
+    X[:, 1:] = slots.view(rows, per_row)
+    q = tj2.quantize(X, out_fmt=tj2.FP8)
+    assert torch.all(q.scale128[:, 0] == 1.0)
+    got = q.codes[:, 1:128].reshape(-1)[: vals.numel()].to(torch.int64)
+    a = vals.abs().double()
+    # grid step: 2^-9 below 2^-6 (subnormals), else 2^(e - 3) in the binade [2^e, 2^(e+1))
+    e = torch.frexp(torch.clamp(a, min=2.0 ** -6)).exponent.double() - 1  # a in [2^e, 2^(e+1))
+    step = torch.where(a < 2.0 ** -6, 2.0 ** -9, torch.exp2(e - 3))
+    mag = torch.clamp(torch.round(a / step) * step, max=448.0)
+    me = torch.frexp(torch.clamp(mag, min=2.0 ** -6)).exponent.double() - 1
+    normal = mag >= 2.0 ** -6
+    code = torch.where(normal, ((me + 7) * 8 + (mag / torch.exp2(me) - 1) * 8), mag / 2.0 ** -9).round().to(torch.int64)
+    ref = code | (torch.signbit(vals).to(torch.int64) << 7)
+    bad = (got != ref).sum().item()
+    assert bad == 0, f"{bad} mismatches"
