@@ -18,12 +18,6 @@ namespace tj2 {
 
 namespace {
 
-__device__ __forceinline__ float e2m1_val(uint32_t n) {
-  uint32_t e = (n >> 1) & 3u, m = n & 1u;
-  float mag = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
-  return (n & 8u) ? -mag : mag;
-}
-
 __device__ __forceinline__ void load16f(const float* p, float v[16]) {
   const float4* q = reinterpret_cast<const float4*>(p);
 #pragma unroll
@@ -53,10 +47,16 @@ __device__ __forceinline__ void fwd_quant16(const float w[16], bool valid, uint3
 #pragma unroll
   for (int t = 0; t < 16; ++t) y[t] = (valid ? w[t] : 0.0f) * g.inv;
   e2m1_rtn16(y, codes);
+  typedef float float2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const uint32_t c = (codes[t >> 3] >> (4 * (t & 7))) & 15u;
-    q[t] = (e2m1_val(c) * s) * g.S;
+  for (int b = 0; b < 8; ++b) {  // byte b holds elements 2b, 2b+1; exact E2M1 values
+    const uint32_t word = codes[b >> 2];
+    const float2_t v = (b & 3) == 0   ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0)
+                       : (b & 3) == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1)
+                       : (b & 3) == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2)
+                                      : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+    q[2 * b] = (v.x * s) * g.S;
+    q[2 * b + 1] = (v.y * s) * g.S;
   }
   *s_code = g.s_code;
   *S = g.S;
@@ -70,9 +70,18 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t groups_
   const bool valid = (int64_t)j * 16 < p.K;
   const int64_t base = (int64_t)row * p.K + (int64_t)j * 16;
 
-  float w[16], q[16];
-  if (valid) load16f(p.W + base, w);
-  else {
+  // every load of the lane is issued before the quantization work (few waves per
+  // SIMD for these sizes, so one exposed latency instead of two)
+  float w[16], q[16], wp[16], qp[16], dq[16], dm[16];
+  if (valid) {
+    load16f(p.W + base, w);
+    if (p.mode != TJ2_OSCI_INIT) {
+      load16f(p.W_prev + base, wp);
+      load16f(p.Q_prev + base, qp);
+      load16f(p.dQ + base, dq);
+      load16f(p.dM + base, dm);
+    }
+  } else {
 #pragma unroll
     for (int t = 0; t < 16; ++t) w[t] = 0.0f;
   }
@@ -92,11 +101,6 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t groups_
       store16f(p.dQ + base, z);
       store16f(p.dM + base, z);
     } else {
-      float wp[16], qp[16], dq[16], dm[16];
-      load16f(p.W_prev + base, wp);
-      load16f(p.Q_prev + base, qp);
-      load16f(p.dQ + base, dq);
-      load16f(p.dM + base, dm);
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         dq[t] = dq[t] + fabsf(q[t] - qp[t]);

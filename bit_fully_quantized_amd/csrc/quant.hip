@@ -290,8 +290,17 @@ struct ColTile<TJ2_FP8> {
 template <int IN, bool FP8OUT, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
   __shared__ ColTile<IN> tile;
-  const int64_t c_tile = (int64_t)blockIdx.x * 64;
-  const int64_t rb = (int64_t)blockIdx.y * 128;
+  // Packed inputs: row blocks fastest, so the column tiles of one row block run
+  // on one XCD (and its L2) close together and a cache line holding several of
+  // their packed rows is fetched from HBM once.  Dense inputs: column tiles
+  // fastest (a tile row is a whole 128-byte line; neighbours share DRAM pages).
+  constexpr bool kRowsFastest = IN == TJ2_NVFP4 || IN == TJ2_FP8;
+  const uint32_t nbR = (uint32_t)((p.rows + 127) / 128);
+  const uint32_t nbC = (uint32_t)((p.cols + 63) / 64);
+  const uint32_t rbi = kRowsFastest ? blockIdx.x % nbR : blockIdx.x / nbC;
+  const uint32_t cti = kRowsFastest ? blockIdx.x / nbR : blockIdx.x % nbC;
+  const int64_t c_tile = (int64_t)cti * 64;
+  const int64_t rb = (int64_t)rbi * 128;
   tile.load(p, rb, c_tile);
   __syncthreads();
   const int lane = threadIdx.x & 63;
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
     } else {
       *reinterpret_cast<uint4*>(o.codes + orow * o.ld_codes + r0) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
     }
-    if (rs == 0) o.s128[orow * o.ld_s128 + blockIdx.y] = S;
+    if (rs == 0) o.s128[orow * o.ld_s128 + rbi] = S;
   });
 }
 
@@ -350,8 +359,9 @@ hipError_t run_row(const QuantParams& p, hipStream_t s) {
 
 template <int IN, bool FP8OUT, bool SR, bool RHT>
 hipError_t run_col(const QuantParams& p, hipStream_t s) {
-  dim3 grid((uint32_t)((p.cols + 63) / 64), (uint32_t)((p.rows + 127) / 128));
-  hipLaunchKernelGGL((quant_col_kernel<IN, FP8OUT, SR, RHT>), grid, dim3(256), 0, s, p);
+  const int64_t blocks = (p.cols + 63) / 64 * ((p.rows + 127) / 128);
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_col_kernel<IN, FP8OUT, SR, RHT>), dim3((uint32_t)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
