@@ -717,15 +717,25 @@ GemmKernel pick_kernel(const GemmParams& p) {
 
 }  // namespace
 
+// K splits of a product: one workgroup per CU at a time (256 CUs), so the time
+// is about (rounds of workgroups) x (chunks per workgroup); a split adds about
+// one chunk's worth of time per workgroup for its fp32 partial tile (written
+// here, read by the reduction).  The smallest split with the least estimated
+// time wins; splits keep at least four chunks each.
 int gemm_split(int64_t I, int64_t J, int64_t nchunks) {
+  constexpr int64_t kCUs = 256;
   const int64_t tiles = ((I + BM - 1) / BM) * ((J + BN - 1) / BN);
-  const int64_t target = 512;  // workgroups: about two rounds of one per CU
-  if (tiles >= target / 2 || nchunks < 8) return 1;
-  int64_t split = (target + tiles - 1) / tiles;
-  const int64_t max_by_depth = nchunks / 4;  // keep >= 4 chunks per split
-  if (split > max_by_depth) split = max_by_depth;
-  if (split > 64) split = 64;
-  return split < 2 ? 1 : (int)split;
+  if (tiles >= kCUs || nchunks < 8) return 1;
+  int64_t best = 1, best_cost = -1;
+  for (int64_t s = 1; s <= 64 && nchunks / s >= 4; ++s) {
+    const int64_t cps = (nchunks + s - 1) / s;
+    const int64_t splits = (nchunks + cps - 1) / cps;  // as launched: no empty splits
+    if (splits != s) continue;
+    const int64_t rounds = (tiles * s + kCUs - 1) / kCUs;
+    const int64_t cost = rounds * (cps + (s > 1 ? 1 : 0));
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = s; }
+  }
+  return (int)best;
 }
 
 size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t nchunks) {
