@@ -101,9 +101,9 @@ size_t carve_size(int fmt, int64_t rows, int64_t len) {
   return align256(c) + align256(s16) + align256(s128);
 }
 
-tj2_status run_quant(const void* x, int x_dtype, const tj2_qtensor* x_q, int64_t rows, int64_t cols,
-                     const int32_t* idx, int64_t n_idx, int grouping, int rounding, int rht, uint32_t mask,
-                     uint64_t seed, uint64_t offset, const tj2_qtensor* out, hipStream_t s) {
+QuantParams quant_params(const void* x, int x_dtype, const tj2_qtensor* x_q, int64_t rows, int64_t cols,
+                         const int32_t* idx, int64_t n_idx, int grouping, int rounding, int rht, uint32_t mask,
+                         uint64_t seed, uint64_t offset, const tj2_qtensor* out) {
   QuantParams p;
   memset(&p, 0, sizeof(p));
   p.in_dtype = x_dtype;
@@ -121,6 +121,14 @@ tj2_status run_quant(const void* x, int x_dtype, const tj2_qtensor* x_q, int64_t
   p.seed = seed;
   p.offset = offset;
   p.out = make_view(*out);
+  return p;
+}
+
+tj2_status run_quant(const void* x, int x_dtype, const tj2_qtensor* x_q, int64_t rows, int64_t cols,
+                     const int32_t* idx, int64_t n_idx, int grouping, int rounding, int rht, uint32_t mask,
+                     uint64_t seed, uint64_t offset, const tj2_qtensor* out, hipStream_t s) {
+  const QuantParams p =
+      quant_params(x, x_dtype, x_q, rows, cols, idx, n_idx, grouping, rounding, rht, mask, seed, offset, out);
   return hip_check(launch_quant(p, s), "quantize launch");
 }
 
@@ -439,16 +447,23 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
   const uint32_t mdx = r ? tj2_rht_signs(seed, offset + 0) : 0u;
   const uint32_t mdw = r ? tj2_rht_signs(seed, offset + 2) : 0u;
   TJ2_TRY(run_quant(dY, TJ2_BF16, nullptr, M, N, nullptr, 0, TJ2_GROUP_ROW, TJ2_SR, r, mdx, seed, offset + 0, &o->dYq, s));
-  TJ2_TRY(run_quant(nullptr, TJ2_NVFP4, Wq, N, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 1, &o->Wt, s));
-  TJ2_TRY(run_quant(dY, TJ2_BF16, nullptr, M, N, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 2, &o->dYt, s));
-  TJ2_TRY(run_quant(nullptr, TJ2_NVFP4, Xq, M, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 3, &o->Xt, s));
+  // the column (re-grouped, transposed) operands of both products in one launch,
+  // the small FP8 slices first so their latency hides behind the large problems
+  QuantParams cols[kColMultiMax];
+  int nc = 0;
+  if (plan) {
+    cols[nc++] = quant_params(nullptr, TJ2_FP8, X8, M, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 5, &o->X8t);
+    cols[nc++] = quant_params(nullptr, TJ2_FP8, W8, N, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 4, &o->W8t);
+  }
+  cols[nc++] = quant_params(nullptr, TJ2_NVFP4, Wq, N, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 1, &o->Wt);
+  cols[nc++] = quant_params(nullptr, TJ2_NVFP4, Xq, M, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 3, &o->Xt);
+  cols[nc++] = quant_params(dY, TJ2_BF16, nullptr, M, N, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 2, &o->dYt);
+  TJ2_TRY(hip_check(launch_quant_col_multi(cols, nc, s), "column quantize launch"));
   if (!plan) {
     TJ2_TRY(run_gemm(&o->dYq, &o->Wt, nullptr, nullptr, dX, dx_dtype, K, nullptr, 0, gemm_ws, gws, s));
     TJ2_TRY(run_gemm(&o->dYt, &o->Xt, nullptr, nullptr, dW, TJ2_F32, K, nullptr, 0, gemm_ws, gws, s));
     return ok();
   }
-  TJ2_TRY(run_quant(nullptr, TJ2_FP8, W8, N, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 4, &o->W8t, s));
-  TJ2_TRY(run_quant(nullptr, TJ2_FP8, X8, M, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 5, &o->X8t, s));
   TJ2_TRY(run_gemm_outl(&o->dYq, &o->Wt, &o->W8t, plan, dX, dx_dtype, K, 0, gemm_ws, gws, s));
   TJ2_TRY(run_gemm_outl(&o->dYt, &o->Xt, &o->X8t, plan, dW, TJ2_F32, K, 0, gemm_ws, gws, s));
   return ok();

@@ -16,6 +16,7 @@
 //    128-byte segments.  Stochastic draws follow the output position, so each
 //    16-element group uses two whole Philox blocks generated on the spot.
 #include <algorithm>
+#include <cstring>
 
 #include "tj2_device.h"
 #include "tj2_internal.h"
@@ -287,9 +288,9 @@ struct ColTile<TJ2_FP8> {
   }
 };
 
+// One 128-row x 64-column tile (number `bid` of the problem's tiles).
 template <int IN, bool FP8OUT, bool SR, bool RHT>
-__global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
-  __shared__ ColTile<IN> tile;
+__device__ __forceinline__ void col_tile(const QuantParams& p, uint32_t bid, ColTile<IN>& tile) {
   // Packed inputs: row blocks fastest, so the column tiles of one row block run
   // on one XCD (and its L2) close together and a cache line holding several of
   // their packed rows is fetched from HBM once.  Dense inputs: column tiles
@@ -297,8 +298,8 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
   constexpr bool kRowsFastest = IN == TJ2_NVFP4 || IN == TJ2_FP8;
   const uint32_t nbR = (uint32_t)((p.rows + 127) / 128);
   const uint32_t nbC = (uint32_t)((p.cols + 63) / 64);
-  const uint32_t rbi = kRowsFastest ? blockIdx.x % nbR : blockIdx.x / nbC;
-  const uint32_t cti = kRowsFastest ? blockIdx.x / nbR : blockIdx.x % nbC;
+  const uint32_t rbi = kRowsFastest ? bid % nbR : bid / nbC;
+  const uint32_t cti = kRowsFastest ? bid / nbR : bid % nbC;
   const int64_t c_tile = (int64_t)cti * 64;
   const int64_t rb = (int64_t)rbi * 128;
   tile.load(p, rb, c_tile);
@@ -343,6 +344,38 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
     }
     if (rs == 0) o.s128[orow * o.ld_s128 + rbi] = S;
   });
+}
+
+template <int IN, bool FP8OUT, bool SR, bool RHT>
+__global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
+  __shared__ ColTile<IN> tile;
+  col_tile<IN, FP8OUT, SR, RHT>(p, blockIdx.x, tile);
+}
+
+// Several independent column quantizations in one launch (the backward's
+// re-grouped operands): workgroups [begin[i], begin[i+1]) take problem i, so
+// small, latency-bound problems run beside the large ones instead of after
+// them.  Combinations: bf16 -> NVFP4, NVFP4 -> NVFP4, FP8 -> FP8.
+struct ColMulti {
+  QuantParams p[kColMultiMax];
+  uint32_t begin[kColMultiMax + 1];
+  int n;
+};
+
+template <bool SR, bool RHT>
+__global__ __launch_bounds__(256) void quant_col_multi_kernel(ColMulti m) {
+  __shared__ union {
+    ColTile<TJ2_BF16> b;
+    ColTile<TJ2_NVFP4> n;
+    ColTile<TJ2_FP8> e;
+  } tile;
+  int i = 0;
+  while (i + 1 < m.n && blockIdx.x >= m.begin[i + 1]) ++i;  // uniform per workgroup
+  const QuantParams& p = m.p[i];
+  const uint32_t bid = blockIdx.x - m.begin[i];
+  if (p.in_dtype == TJ2_BF16) col_tile<TJ2_BF16, false, SR, RHT>(p, bid, tile.b);
+  else if (p.in_dtype == TJ2_NVFP4) col_tile<TJ2_NVFP4, false, SR, RHT>(p, bid, tile.n);
+  else col_tile<TJ2_FP8, true, SR, RHT>(p, bid, tile.e);
 }
 
 template <int IN, bool GATHER, bool FP8OUT, bool SR, bool RHT>
@@ -501,6 +534,37 @@ hipError_t launch_quant_split(const SplitParams& p, hipStream_t s) {
     hipLaunchKernelGGL(quant_split_kernel<TJ2_BF16>, dim3(blocks), dim3(256), lds, s, p, R);
   else
     hipLaunchKernelGGL(quant_split_kernel<TJ2_F32>, dim3(blocks), dim3(256), lds, s, p, R);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_col_multi(const QuantParams* ps, int n, hipStream_t s) {
+  if (n < 1 || n > kColMultiMax) return hipErrorInvalidValue;
+  ColMulti m;
+  memset(&m, 0, sizeof(m));
+  m.n = n;
+  int64_t total = 0;
+  bool sr = ps[0].rounding == TJ2_SR, rht = ps[0].rht != 0;
+  for (int i = 0; i < n; ++i) {
+    const QuantParams& p = ps[i];
+    const bool ok = p.grouping == TJ2_GROUP_COL && (p.rounding == TJ2_SR) == sr && (p.rht != 0) == rht &&
+                    ((p.in_dtype == TJ2_BF16 && p.out.fmt == TJ2_NVFP4) ||
+                     (p.in_dtype == TJ2_NVFP4 && p.out.fmt == TJ2_NVFP4) ||
+                     (p.in_dtype == TJ2_FP8 && p.out.fmt == TJ2_FP8));
+    if (!ok) return hipErrorInvalidValue;
+    m.p[i] = p;
+    m.begin[i] = (uint32_t)total;
+    total += (p.cols + 63) / 64 * ((p.rows + 127) / 128);
+  }
+  if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  m.begin[n] = (uint32_t)total;
+  const dim3 grid((uint32_t)total);
+  if (sr) {
+    if (rht) hipLaunchKernelGGL((quant_col_multi_kernel<true, true>), grid, dim3(256), 0, s, m);
+    else hipLaunchKernelGGL((quant_col_multi_kernel<true, false>), grid, dim3(256), 0, s, m);
+  } else {
+    if (rht) hipLaunchKernelGGL((quant_col_multi_kernel<false, true>), grid, dim3(256), 0, s, m);
+    else hipLaunchKernelGGL((quant_col_multi_kernel<false, false>), grid, dim3(256), 0, s, m);
+  }
   return hipGetLastError();
 }
 

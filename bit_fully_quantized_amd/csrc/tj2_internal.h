@@ -49,6 +49,12 @@ struct QuantParams {
 
 hipError_t launch_quant(const QuantParams& p, hipStream_t s);
 
+// Up to kColMultiMax column (16x1, transposed) quantizations in one launch; every
+// problem shares rounding and the Hadamard switch, and is bf16 -> NVFP4,
+// NVFP4 -> NVFP4 or FP8 -> FP8.
+constexpr int kColMultiMax = 6;
+hipError_t launch_quant_col_multi(const QuantParams* ps, int n, hipStream_t s);
+
 // Forward split of a dense row-major input with an outlier plan: the columns
 // in `rest` quantized to NVFP4 (q4) and the columns in `outl` to FP8 (q8), both
 // round-to-nearest along rows, from one read of the input.
