@@ -6,9 +6,10 @@
 // risk dQ / dM exceeds tau (while the learning rate is low: host switch) are
 // reset to the centre of their current bin, Q(w).  Q is the forward quantizer
 // (round to nearest, 1x16 groups along K), so the pass also emits the codes the
-// next forward consumes.  One lane owns 16 consecutive elements of a row; the 8
-// lanes of a 128-element outer block reduce its amax with DPP.  The pass is
-// element-wise and HBM-bound: 5 fp32 reads, 4-5 fp32 writes per element.
+// next forward consumes.  One lane owns 8 consecutive elements of a row (half
+// a 16-element group); the 16 lanes of a 128-element outer block reduce its
+// amax with DPP.  The pass is element-wise and HBM-bound: 5 fp32 reads, 4-5
+// fp32 writes per element.
 //
 // Calibration (section 2.C): per-channel sum of squares of the activations.
 #include "tj2_device.h"
@@ -18,91 +19,111 @@ namespace tj2 {
 
 namespace {
 
-__device__ __forceinline__ void load16f(const float* p, float v[16]) {
+__device__ __forceinline__ void load8f(const float* p, float v[8]) {
   const float4* q = reinterpret_cast<const float4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float4 a = q[i];
-    v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
-  }
+  const float4 a = q[0], b = q[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-__device__ __forceinline__ void store16f(float* p, const float v[16]) {
+__device__ __forceinline__ void store8f(float* p, const float v[8]) {
   float4* q = reinterpret_cast<float4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) q[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  q[0] = make_float4(v[0], v[1], v[2], v[3]);
+  q[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// Forward quantization of one 16-element group: codes and dequantized values.
-__device__ __forceinline__ void fwd_quant16(const float w[16], bool valid, uint32_t codes[2], uint32_t* s_code,
-                                            float* S, float q[16]) {
-  float a_j = 0.0f;
+// Max over the 16 consecutive lanes of an aligned outer block (non-negative
+// inputs: their fp32 bit patterns order as unsigned integers).
+__device__ __forceinline__ float max16_lanes(float x) {
+  uint32_t xi = __float_as_uint(x);
+  xi = max(xi, (uint32_t)__builtin_amdgcn_mov_dpp((int)xi, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  xi = max(xi, (uint32_t)__builtin_amdgcn_mov_dpp((int)xi, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  xi = max(xi, (uint32_t)__builtin_amdgcn_mov_dpp((int)xi, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  xi = max(xi, (uint32_t)__builtin_amdgcn_mov_dpp((int)xi, 0x140, 0xF, 0xF, false));  // row_mirror
+  return __uint_as_float(xi);
+}
+
+// Forward quantization of this lane's half (8 elements) of a 16-element group:
+// the group's amax pairs the two lanes, the outer block's spans 16 lanes.
+// Returns the lane's 8 codes (one word), the group's E4M3 code and S, and the
+// dequantized values Q(w).
+__device__ __forceinline__ void fwd_quant8(const float w[8], bool valid, uint32_t* code, uint32_t* s_code, float* S,
+                                           float q[8]) {
+  float a_h = 0.0f;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(w[t]));
-  if (!valid) a_j = 0.0f;
-  const float a_o = max8_lanes(a_j);
+  for (int t = 0; t < 8; ++t) a_h = fmaxf(a_h, fabsf(w[t]));
+  if (!valid) a_h = 0.0f;
+  uint32_t ai = __float_as_uint(a_h);
+  ai = max(ai, (uint32_t)__builtin_amdgcn_mov_dpp((int)ai, 0xB1, 0xF, 0xF, false));  // the group's other half
+  const float a_j = __uint_as_float(ai);
+  const float a_o = max16_lanes(a_j);
   GroupScale g = nvfp4_group_scale(a_o, a_j);
   const float s = e4m3_decode(g.s_code);
-  float y[16];
+  float y[8];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) y[t] = (valid ? w[t] : 0.0f) * g.inv;
-  e2m1_rtn16(y, codes);
+  for (int t = 0; t < 8; ++t) y[t] = (valid ? w[t] : 0.0f) * g.inv;
+  uint32_t c = 0u;
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[0], y[1], 1.0f, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[2], y[3], 1.0f, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[4], y[5], 1.0f, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[6], y[7], 1.0f, 3);
   typedef float float2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {  // byte b holds elements 2b, 2b+1; exact E2M1 values
-    const uint32_t word = codes[b >> 2];
-    const float2_t v = (b & 3) == 0   ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0)
-                       : (b & 3) == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1)
-                       : (b & 3) == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2)
-                                      : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+  for (int b = 0; b < 4; ++b) {  // byte b holds elements 2b, 2b+1; exact E2M1 values
+    const float2_t v = b == 0   ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0)
+                       : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1)
+                       : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2)
+                                : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
     q[2 * b] = (v.x * s) * g.S;
     q[2 * b + 1] = (v.y * s) * g.S;
   }
+  *code = c;
   *s_code = g.s_code;
   *S = g.S;
 }
 
-__global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t groups_per_row) {
+// One lane per half group (8 consecutive elements of a row); the 16 lanes of
+// a 128-element outer block are consecutive.  All loads of the lane are issued
+// before the quantization work.
+__global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_per_row) {
   const uint32_t g = blockIdx.x * 256u + threadIdx.x;
-  const uint32_t row = g / (uint32_t)groups_per_row;
+  const uint32_t row = g / (uint32_t)halves_per_row;
   if (row >= (uint32_t)p.N) return;  // whole outer blocks exit together
-  const uint32_t j = g - row * (uint32_t)groups_per_row;
+  const uint32_t jh = g - row * (uint32_t)halves_per_row;
+  const uint32_t j = jh >> 1;  // 16-element group
   const bool valid = (int64_t)j * 16 < p.K;
-  const int64_t base = (int64_t)row * p.K + (int64_t)j * 16;
+  const int64_t base = (int64_t)row * p.K + (int64_t)jh * 8;
 
-  // every load of the lane is issued before the quantization work (few waves per
-  // SIMD for these sizes, so one exposed latency instead of two)
-  float w[16], q[16], wp[16], qp[16], dq[16], dm[16];
+  float w[8], q[8], wp[8], qp[8], dq[8], dm[8];
   if (valid) {
-    load16f(p.W + base, w);
+    load8f(p.W + base, w);
     if (p.mode != TJ2_OSCI_INIT) {
-      load16f(p.W_prev + base, wp);
-      load16f(p.Q_prev + base, qp);
-      load16f(p.dQ + base, dq);
-      load16f(p.dM + base, dm);
+      load8f(p.W_prev + base, wp);
+      load8f(p.Q_prev + base, qp);
+      load8f(p.dQ + base, dq);
+      load8f(p.dM + base, dm);
     }
   } else {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) w[t] = 0.0f;
+    for (int t = 0; t < 8; ++t) w[t] = 0.0f;
   }
-  uint32_t codes[2], s_code;
+  uint32_t code, s_code;
   float S;
-  fwd_quant16(w, valid, codes, &s_code, &S, q);
+  fwd_quant8(w, valid, &code, &s_code, &S, q);
 
   uint32_t n_reset = 0;
-  bool any_reset = false;
   if (valid) {
     if (p.mode == TJ2_OSCI_INIT) {
-      float z[16];
+      float z[8];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) z[t] = 0.0f;
-      store16f(p.W_prev + base, w);
-      store16f(p.Q_prev + base, q);
-      store16f(p.dQ + base, z);
-      store16f(p.dM + base, z);
+      for (int t = 0; t < 8; ++t) z[t] = 0.0f;
+      store8f(p.W_prev + base, w);
+      store8f(p.Q_prev + base, q);
+      store8f(p.dQ + base, z);
+      store8f(p.dM + base, z);
     } else {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < 8; ++t) {
         dq[t] = dq[t] + fabsf(q[t] - qp[t]);
         dm[t] = dm[t] + fabsf(w[t] - wp[t]);
         wp[t] = w[t];
@@ -110,31 +131,31 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t groups_
       if (p.mode == TJ2_OSCI_WINDOW_END) {
         if (p.reset_enabled) {
 #pragma unroll
-          for (int t = 0; t < 16; ++t) {
+          for (int t = 0; t < 8; ++t) {
             if (dq[t] > p.tau * dm[t]) {
               w[t] = q[t];
               wp[t] = q[t];
               ++n_reset;
             }
           }
-          if (n_reset) store16f(p.W + base, w);
+          if (n_reset) store8f(p.W + base, w);
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) { dq[t] = 0.0f; dm[t] = 0.0f; }
+        for (int t = 0; t < 8; ++t) { dq[t] = 0.0f; dm[t] = 0.0f; }
       }
-      store16f(p.W_prev + base, wp);
-      store16f(p.Q_prev + base, q);
-      store16f(p.dQ + base, dq);
-      store16f(p.dM + base, dm);
+      store8f(p.W_prev + base, wp);
+      store8f(p.Q_prev + base, q);
+      store8f(p.dQ + base, dq);
+      store8f(p.dM + base, dm);
     }
   }
-  any_reset = max8_lanes(n_reset ? 1.0f : 0.0f) > 0.0f;
+  const bool any_reset = max16_lanes(n_reset ? 1.0f : 0.0f) > 0.0f;  // uniform over the outer block
   if (p.have_wq) {
-    if (any_reset) fwd_quant16(w, valid, codes, &s_code, &S, q);  // scales may change after a reset
+    if (any_reset) fwd_quant8(w, valid, &code, &s_code, &S, q);  // scales may change after a reset
     const QView& o = p.wq;
-    *reinterpret_cast<uint2*>(o.codes + (int64_t)row * o.ld_codes + j * 8u) = make_uint2(codes[0], codes[1]);
-    o.s16[(int64_t)row * o.ld_s16 + j] = (uint8_t)s_code;
-    if ((j & 7u) == 0u) o.s128[(int64_t)row * o.ld_s128 + (j >> 3)] = S;
+    *reinterpret_cast<uint32_t*>(o.codes + (int64_t)row * o.ld_codes + jh * 4u) = code;
+    if ((jh & 1u) == 0u) o.s16[(int64_t)row * o.ld_s16 + j] = (uint8_t)s_code;
+    if ((jh & 15u) == 0u) o.s128[(int64_t)row * o.ld_s128 + (j >> 3)] = S;
   }
   if (p.reset_count && n_reset) atomicAdd(p.reset_count, (unsigned long long)n_reset);
 }
@@ -178,9 +199,9 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const uint16_t* __restrict__
 
 hipError_t launch_osci(const OsciParams& p, hipStream_t s) {
   const int64_t nb = (p.K + 127) / 128;
-  const int64_t gpr = nb * 8;
-  const int64_t blocks = (p.N * gpr + 255) / 256;
-  hipLaunchKernelGGL(osci_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)gpr);
+  const int64_t hpr = nb * 16;  // half groups per row
+  const int64_t blocks = (p.N * hpr + 255) / 256;
+  hipLaunchKernelGGL(osci_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
   return hipGetLastError();
 }
 
