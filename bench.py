@@ -312,6 +312,14 @@ def main():
     osci_t = time_launches(lambda: [tj2.osci_reset_step(li.W, *li.state, mode=tj2.OSCI_ACCUM, tau=4.0)
                                     for li in lins], 3)
     osci_bytes = n_params * 36.0  # read W, W_prev, Q_prev, dQ, dM; write W_prev, Q_prev, dQ, dM (fp32)
+    log("fused master-weight pass")
+    for li in lins:
+        li.m, li.v = torch.zeros_like(li.W), torch.zeros_like(li.W)
+    master_t = time_launches(lambda: [tj2.master_update_step(li.W, li.m, li.v, li.dW, *li.state[1:], lr=1e-6,
+                                                             bias_correction1=0.1, bias_correction2=0.05,
+                                                             mode=tj2.OSCI_ACCUM, tau=4.0) for li in lins], 3)
+    # read W, m, v, grad, Q_prev, dQ, dM; write W, m, v, Q_prev, dQ, dM (fp32)
+    master_bytes = n_params * 52.0
     del lins, ws
     torch.cuda.empty_cache()
 
@@ -352,6 +360,10 @@ def main():
         "osci_reset": {"GB_s": round(osci_bytes / osci_t / 1e9, 1),
                        "frac_hbm": round(osci_bytes / osci_t / 1e9 / HBM_PEAK_GBS, 3),
                        "ms_per_step": round(osci_t * 1e3, 3), "params": n_params},
+        "master_update": {"what": "fused AdamW + OsciReset accumulate over all masters (52 B/param)",
+                          "GB_s": round(master_bytes / master_t / 1e9, 1),
+                          "frac_hbm": round(master_bytes / master_t / 1e9 / HBM_PEAK_GBS, 3),
+                          "ms_per_step": round(master_t * 1e3, 3), "params": n_params},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -18,7 +18,7 @@ from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI
                    Tj2Error, check, lib)
 
 __all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "gemm_workspace", "linear_fwd", "linear_bwd", "linear_bwd_workspace",
-           "osci_reset_step", "channel_sumsq", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
+           "osci_reset_step", "master_update_step", "channel_sumsq", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
            "GROUP_ROW", "GROUP_COL", "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END"]
 
 
@@ -240,6 +240,22 @@ def osci_reset_step(W, W_prev, Q_prev, dQ, dM, *, mode: int, tau: float = 4.0, r
                                ctypes.c_float(tau), 1 if reset_enabled else 0,
                                ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count), _stream())
     check("osci_reset_step", st)
+
+
+def master_update_step(W, m, v, grad, Q_prev, dQ, dM, *, lr: float, bias_correction1: float,
+                       bias_correction2: float, beta1: float = 0.9, beta2: float = 0.95, eps: float = 1e-8,
+                       weight_decay: float = 0.1, mode: int = OSCI_ACCUM, tau: float = 4.0,
+                       reset_enabled: bool = False, Wq_out: QTensor | None = None,
+                       reset_count: torch.Tensor | None = None) -> None:
+    """Fused master-weight pass: AdamW on W, then OsciReset (ACCUM / WINDOW_END) with the
+    pre-update master as W_prev, then the forward codes (Wq_out)."""
+    N, K = W.shape
+    ap = _lib.AdamWC(lr, beta1, beta2, eps, weight_decay, bias_correction1, bias_correction2)
+    wqc = Wq_out.c() if Wq_out is not None else None
+    st = lib().master_update_step(_ptr(W), _ptr(m), _ptr(v), _ptr(grad), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K,
+                                  ctypes.byref(ap), mode, ctypes.c_float(tau), 1 if reset_enabled else 0,
+                                  ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count), _stream())
+    check("master_update_step", st)
 
 
 def channel_sumsq(X: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:

@@ -55,6 +55,13 @@ U64 = ctypes.c_uint64
 SZ = ctypes.c_size_t
 QP = ctypes.POINTER(QTensorC)
 
+
+class AdamWC(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("bias_correction1", ctypes.c_float), ("bias_correction2", ctypes.c_float)]
+
+
 SIGNATURES = {
     "tj2_last_error": (ctypes.c_char_p, []),
     "tj2_version": (ctypes.c_char_p, []),
@@ -69,6 +76,8 @@ SIGNATURES = {
                                ctypes.POINTER(BwdOperandsC), P, SZ, P]),
     "nvfp4_linear_bwd_workspace_size": (SZ, [I64, I64, I64, I32]),
     "osci_reset_step": (I32, [P, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, QP, P, P]),
+    "master_update_step": (I32, [P, P, P, P, P, P, P, I64, I64, ctypes.POINTER(AdamWC), I32, ctypes.c_float, I32,
+                                 QP, P, P]),
     "tj2_channel_sumsq": (I32, [P, I64, I64, P, P]),
 }
 

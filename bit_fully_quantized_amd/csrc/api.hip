@@ -469,6 +469,39 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
   return ok();
 }
 
+tj2_status master_update_step(float* W, float* m, float* v, const float* grad, float* Q_prev, float* dQ, float* dM,
+                              int64_t N, int64_t K, const tj2_adamw_params* adam, int32_t mode, float tau,
+                              int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count, void* stream) {
+  if (!W || !m || !v || !grad || !Q_prev || !dQ || !dM) return fail(TJ2_ERR_ARG, "W, m, v, grad and the state arrays are required");
+  if (!adam) return fail(TJ2_ERR_ARG, "adam parameters are required");
+  if (!aligned16(W) || !aligned16(m) || !aligned16(v) || !aligned16(grad) || !aligned16(Q_prev) || !aligned16(dQ) ||
+      !aligned16(dM))
+    return fail(TJ2_ERR_ALIGN, "arrays must be 16-byte aligned");
+  if (N <= 0 || N > ((int64_t)1 << 30)) return fail(TJ2_ERR_SHAPE, "N must be positive");
+  TJ2_TRY(check_dims(K, "K"));
+  if (mode != TJ2_OSCI_ACCUM && mode != TJ2_OSCI_WINDOW_END) return fail(TJ2_ERR_ARG, "mode must be ACCUM or WINDOW_END");
+  if (!(tau >= 0.0f)) return fail(TJ2_ERR_ARG, "tau must be >= 0");
+  const int64_t nb = (K + 127) / 128;
+  if (N * nb * 16 >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
+  MasterParams p;
+  memset(&p, 0, sizeof(p));
+  p.W = W; p.m = m; p.v = v; p.grad = grad; p.Q_prev = Q_prev; p.dQ = dQ; p.dM = dM;
+  p.N = N; p.K = K;
+  p.lr = adam->lr; p.beta1 = adam->beta1; p.beta2 = adam->beta2; p.eps = adam->eps;
+  p.weight_decay = adam->weight_decay; p.bc1 = adam->bias_correction1; p.bc2 = adam->bias_correction2;
+  p.window_end = mode == TJ2_OSCI_WINDOW_END ? 1 : 0;
+  p.tau = tau;
+  p.reset_enabled = reset_enabled ? 1 : 0;
+  if (Wq_out) {
+    TJ2_TRY(check_qtensor(Wq_out, "Wq_out", TJ2_NVFP4, N, K));
+    p.wq = make_view(*Wq_out);
+    p.have_wq = 1;
+  }
+  p.reset_count = reinterpret_cast<unsigned long long*>(reset_count);
+  TJ2_TRY(hip_check(launch_master(p, (hipStream_t)stream), "master update launch"));
+  return ok();
+}
+
 tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N, int64_t K,
                            int32_t mode, float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
                            void* stream) {
@@ -480,7 +513,7 @@ tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, fl
   if (mode != TJ2_OSCI_INIT && mode != TJ2_OSCI_ACCUM && mode != TJ2_OSCI_WINDOW_END) return fail(TJ2_ERR_ARG, "bad mode %d", mode);
   if (!(tau >= 0.0f)) return fail(TJ2_ERR_ARG, "tau must be >= 0");
   const int64_t nb = (K + 127) / 128;
-  if (N * nb * 8 >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
+  if (N * nb * 16 >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
   OsciParams p;
   memset(&p, 0, sizeof(p));
   p.W = W; p.W_prev = W_prev; p.Q_prev = Q_prev; p.dQ = dQ; p.dM = dM;

@@ -160,6 +160,89 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_
   if (p.reset_count && n_reset) atomicAdd(p.reset_count, (unsigned long long)n_reset);
 }
 
+// Fused master-weight pass (one read of the masters, their AdamW moments and the
+// OsciReset state): AdamW with decoupled weight decay in fp32, one rounded
+// operation at a time (the builder's optimizer: the pages use fp32 masters and
+// apply OsciReset after the update, section 2.B, without naming the optimizer),
+// then the OsciReset update of the new masters with the pre-update master as
+// W_prev (the distance the master travels is the update), then the forward
+// codes.  Lane layout as osci_kernel.
+__global__ __launch_bounds__(256) void master_kernel(MasterParams p, int32_t halves_per_row) {
+  const uint32_t g = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t row = g / (uint32_t)halves_per_row;
+  if (row >= (uint32_t)p.N) return;  // whole outer blocks exit together
+  const uint32_t jh = g - row * (uint32_t)halves_per_row;
+  const uint32_t j = jh >> 1;
+  const bool valid = (int64_t)j * 16 < p.K;
+  const int64_t base = (int64_t)row * p.K + (int64_t)jh * 8;
+
+  float w[8], m[8], v[8], gr[8], qp[8], dq[8], dm[8];
+  if (valid) {
+    load8f(p.W + base, w);
+    load8f(p.m + base, m);
+    load8f(p.v + base, v);
+    load8f(p.grad + base, gr);
+    load8f(p.Q_prev + base, qp);
+    load8f(p.dQ + base, dq);
+    load8f(p.dM + base, dm);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) w[t] = 0.0f;
+  }
+  const float omb1 = 1.0f - p.beta1, omb2 = 1.0f - p.beta2;
+  const float decay = 1.0f - p.lr * p.weight_decay;
+  float w1[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float m1 = p.beta1 * m[t] + omb1 * gr[t];
+    const float v1 = p.beta2 * v[t] + omb2 * (gr[t] * gr[t]);
+    const float u = (m1 / p.bc1) / (sqrtf(v1 / p.bc2) + p.eps);
+    w1[t] = valid ? w[t] * decay - p.lr * u : 0.0f;
+    m[t] = m1;
+    v[t] = v1;
+  }
+  uint32_t code, s_code;
+  float S;
+  float q[8];
+  fwd_quant8(w1, valid, &code, &s_code, &S, q);
+  uint32_t n_reset = 0;
+  if (valid) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      dq[t] = dq[t] + fabsf(q[t] - qp[t]);
+      dm[t] = dm[t] + fabsf(w1[t] - w[t]);
+    }
+    if (p.window_end) {
+      if (p.reset_enabled) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          if (dq[t] > p.tau * dm[t]) {
+            w1[t] = q[t];
+            ++n_reset;
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) { dq[t] = 0.0f; dm[t] = 0.0f; }
+    }
+    store8f(p.W + base, w1);
+    store8f(p.m + base, m);
+    store8f(p.v + base, v);
+    store8f(p.Q_prev + base, q);
+    store8f(p.dQ + base, dq);
+    store8f(p.dM + base, dm);
+  }
+  const bool any_reset = max16_lanes(n_reset ? 1.0f : 0.0f) > 0.0f;  // uniform over the outer block
+  if (p.have_wq) {
+    if (any_reset) fwd_quant8(w1, valid, &code, &s_code, &S, q);  // scales may change after a reset
+    const QView& o = p.wq;
+    *reinterpret_cast<uint32_t*>(o.codes + (int64_t)row * o.ld_codes + jh * 4u) = code;
+    if ((jh & 1u) == 0u) o.s16[(int64_t)row * o.ld_s16 + j] = (uint8_t)s_code;
+    if ((jh & 15u) == 0u) o.s128[(int64_t)row * o.ld_s128 + (j >> 3)] = S;
+  }
+  if (p.reset_count && n_reset) atomicAdd(p.reset_count, (unsigned long long)n_reset);
+}
+
 // acc[k] += sum_m X[m, k]^2.  Thread: 8 columns x 64 rows; 8 row slices per block
 // are reduced in LDS, then one atomic per column per block.
 __global__ __launch_bounds__(256) void sumsq_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
@@ -196,6 +279,14 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const uint16_t* __restrict__
 }
 
 }  // namespace
+
+hipError_t launch_master(const MasterParams& p, hipStream_t s) {
+  const int64_t nb = (p.K + 127) / 128;
+  const int64_t hpr = nb * 16;  // half groups per row
+  const int64_t blocks = (p.N * hpr + 255) / 256;
+  hipLaunchKernelGGL(master_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
+  return hipGetLastError();
+}
 
 hipError_t launch_osci(const OsciParams& p, hipStream_t s) {
   const int64_t nb = (p.K + 127) / 128;

@@ -114,6 +114,24 @@ struct OsciParams {
 
 hipError_t launch_osci(const OsciParams& p, hipStream_t s);
 
+// Fused master-weight pass: AdamW on the masters, then OsciReset (ACCUM or
+// WINDOW_END) with the pre-update master as W_prev, then the forward codes.
+struct MasterParams {
+  float *W, *m, *v;
+  const float* grad;
+  float *Q_prev, *dQ, *dM;
+  int64_t N, K;
+  float lr, beta1, beta2, eps, weight_decay, bc1, bc2;
+  int window_end;
+  float tau;
+  int reset_enabled;
+  QView wq;
+  int have_wq;
+  unsigned long long* reset_count;
+};
+
+hipError_t launch_master(const MasterParams& p, hipStream_t s);
+
 hipError_t launch_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, hipStream_t s);
 
 }  // namespace tj2

@@ -253,6 +253,38 @@ tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, fl
                            tj2_qtensor* Wq_out, uint64_t* reset_count, void* stream);
 
 /*
+ * AdamW hyper-parameters of one optimizer step on the fp32 masters (the pages
+ * train with fp32 masters but do not name the optimizer; AdamW with decoupled
+ * weight decay is this library's choice).  bias_correction1 = 1 - beta1^t and
+ * bias_correction2 = 1 - beta2^t for step t >= 1, computed by the caller.
+ */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay, bias_correction1, bias_correction2;
+} tj2_adamw_params;
+
+/*
+ * Fused master-weight pass: one AdamW step on the fp32 masters W [N, K], then
+ * OsciReset (section 2.B) of the updated masters, then their forward codes, in
+ * one pass over W, the moments m, v, the gradient grad and the OsciReset state
+ * Q_prev, dQ, dM (all fp32 [N, K], caller-owned, updated in place except grad).
+ * Per element, fp32, each operation rounded to nearest (no fused multiply-add):
+ *   m' = beta1*m + (1-beta1)*g;  v' = beta2*v + (1-beta2)*(g*g)
+ *   u  = (m'/bc1) / (sqrt(v'/bc2) + eps)
+ *   W' = W*(1 - lr*wd) - lr*u
+ *   then OsciReset on W' with W_prev = W (the pre-update master, so no W_prev
+ *   array): mode TJ2_OSCI_ACCUM or TJ2_OSCI_WINDOW_END as in osci_reset_step
+ *   (TJ2_OSCI_INIT is osci_reset_step's; its W_prev is not read here).
+ * Wq_out (optional, NVFP4 [N, K]): forward codes of the final W.
+ * reset_count (optional, device uint64): incremented by the number of resets.
+ * K must be a multiple of 16; arrays 16-byte aligned.  Errors: TJ2_ERR_ARG
+ * (NULL array or params, bad mode, tau < 0), TJ2_ERR_SHAPE, TJ2_ERR_ALIGN.
+ */
+tj2_status master_update_step(float* W, float* m, float* v, const float* grad, float* Q_prev, float* dQ,
+                              float* dM, int64_t N, int64_t K, const tj2_adamw_params* adam, int32_t mode,
+                              float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
+                              void* stream);
+
+/*
  * OutControl calibration helper (section 2.C: top p% channels from a short
  * calibration window): acc[k] += sum over rows of X[m, k]^2 (fp32, bf16 input
  * [M, K]).  The caller zeroes acc once and ranks the channels on the host.

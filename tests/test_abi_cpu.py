@@ -31,7 +31,7 @@ def L():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_outlier_cols", "nvfp4_linear_fwd", "nvfp4_linear_bwd", "osci_reset_step",
-              "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes"]:
+              "master_update_step", "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes"]:
         assert n in names
 
 
@@ -131,3 +131,20 @@ def test_osci_argument_errors(L):
     assert L.osci_reset_step(*p, 16, 128, 1, ctypes.c_float(-1.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
     assert L.osci_reset_step(None, *p[1:], 16, 128, 1, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
     assert L.tj2_channel_sumsq(0x1000, 64, 100, 0x2000, None) == _lib.TJ2_ERR_SHAPE
+
+
+def test_master_update_argument_errors(L):
+    from bit_fully_quantized_amd import _lib
+    p = [0x1000 * (i + 1) for i in range(7)]
+    ap = _lib.AdamWC(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
+    f4 = ctypes.c_float(4.0)
+    assert L.master_update_step(*p, 16, 100, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None) == _lib.TJ2_ERR_SHAPE
+    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_INIT, f4, 0, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.master_update_step(*p, 16, 128, None, _lib.OSCI_ACCUM, f4, 0, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, ctypes.c_float(-1.0), 0, None, None,
+                                None) == _lib.TJ2_ERR_ARG
+    assert L.master_update_step(None, *p[1:], 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None,
+                                None) == _lib.TJ2_ERR_ARG
+    q = list(p)
+    q[3] = 0x3008  # grad not 16-byte aligned
+    assert L.master_update_step(*q, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None) == _lib.TJ2_ERR_ALIGN
