@@ -225,9 +225,44 @@ def quant_sweep(tj2, reps=24, nbuf=8):
         t = time_launches(fn, reps)
         gbs = bytes_per_call / t / 1e9
         res[name] = {"us": round(t * 1e6, 2), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 3)}
-    del xs, outs_r, outs_c
+    # achievable reference on the same rotated buffers: a plain elementwise copy (bf16 negation,
+    # 64 MiB read + 64 MiB written per call), and each variant's rate as a fraction of it
+    ys = [torch.empty_like(xs[0]) for _ in range(2)]
+    state = {"i": 0}
+
+    def copy_fn():
+        i = state["i"]
+        state["i"] += 1
+        torch.neg(xs[i % nbuf], out=ys[i % 2])
+
+    t = time_launches(copy_fn, reps)
+    copy_gbs = 2 * xs[0].numel() * 2 / t / 1e9
+    res["copy_reference"] = {"what": "torch bf16 negation on the same buffers (read + write)", "us": round(t * 1e6, 2),
+                             "GB_s": round(copy_gbs, 1), "frac_hbm": round(copy_gbs / HBM_PEAK_GBS, 3)}
+    for name in variants:
+        res[name]["frac_of_copy"] = round(res[name]["GB_s"] / copy_gbs, 3)
+    del xs, ys, outs_r, outs_c
     torch.cuda.empty_cache()
     return res, bytes_per_call
+
+
+def library_gemm_reference(M, shapes, reps=10):
+    """Achievable dense f16-class MFMA rate on this part, as the vendor library reaches it: torch's bf16
+    matrix product (hipBLASLt) on plain contiguous operands of the workload's forward shapes."""
+    import torch
+    g = make_gen(5)
+    res, flops, secs = {}, 0.0, 0.0
+    for name, K, N in shapes:
+        a = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
+        b = torch.randn(K, N, generator=g, device="cuda").to(torch.bfloat16).contiguous()
+        c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        t = time_launches(lambda: torch.mm(a, b, out=c), reps)
+        res[name] = round(2.0 * M * N * K / t / 1e12, 1)
+        flops += 2.0 * M * N * K
+        secs += t
+        del a, b, c
+    torch.cuda.empty_cache()
+    return res, flops / secs / 1e12
 
 
 def cpu_baseline(M=8192, K=1024, N=3072, p=0.10):
@@ -323,6 +358,8 @@ def main():
     del lins, ws
     torch.cuda.empty_cache()
 
+    log("library bf16 product reference")
+    lib_ref, lib_all = library_gemm_reference(M, [(f"{spec.name}.fwd", spec.K, spec.N) for spec in wl.linears])
     sweep, sweep_bytes = ({}, 0) if args.no_sweep else quant_sweep(tj2)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
@@ -354,6 +391,12 @@ def main():
             "algorithmic_bytes_per_launch": round(g_bytes / g_launches),
             "avg_launch_us": round(g_time / g_launches * 1e6, 2), "launches_per_step": g_launches,
             "gemm_share_of_step": round(g_time / step_s, 3), "per_launch": per,
+            "library_bf16_reference": {"what": "torch.mm bf16 (hipBLASLt) on plain operands of each linear's "
+                                               "forward shape, TFLOP/s: the achievable dense rate as a vendor "
+                                               "library reaches it, without decode or per-128 promotion",
+                                       "per_shape": lib_ref, "all_shapes": round(lib_all, 1),
+                                       "frac_of_peak": round(lib_all / MFMA_F16_PEAK_TFLOPS, 3),
+                                       "products_frac_of_it": round(achieved / lib_all, 3)},
         },
         "quantizer_sweep": {"tensor": "bf16 8192x4096 N(0,1), 1% columns x64", "algorithmic_MB_per_call":
                             round(sweep_bytes / 1e6, 2), "hbm_peak_GB_s": HBM_PEAK_GBS, **sweep},
