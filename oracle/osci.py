@@ -27,6 +27,20 @@ One call per optimizer step, after the master update, in one of three modes:
               W = Q and W_prev = Q; finally dQ = dM = 0.
 
 The call also returns the forward codes of the final W for the next forward.
+
+Oscillation diagnostics (optional, `diag` dict).  Section 1 of the technical
+summary names the failure mode these measure: small master updates that make
+the quantized weight flip back and forth between adjacent bins.
+
+* flips: per accum / window_end call, the number of elements whose quantized
+  value Q(W) differs from Q_prev (compared as fp32 values, so +0 and -0 are the
+  same bin); summed by the caller over a window this is the window's flip count.
+* risk_hist (window_end only): the window's risk dQ / dM of every element,
+  taken before the reset decision and the zeroing, counted into RISK_BINS
+  bins:  bin 0: dQ == 0;  bin 31: dQ > 0 and dM == 0;  otherwise with
+  r = fl32(dQ / dM) and e = floor(log2 r) (the exponent of r), bin
+  clamp(e + 16, 1, 30), so bin b in 2..29 holds r in [2^(b-16), 2^(b-15)) and
+  bins 1 and 30 also take everything below 2^-14 and from 2^14 up.
 """
 from __future__ import annotations
 
@@ -57,12 +71,44 @@ def osci_init(W: np.ndarray) -> tuple[OsciState, QTensor]:
     return OsciState(W.copy(), Q, z.copy(), z.copy()), Wq
 
 
-def osci_step(W: np.ndarray, st: OsciState, tau: float, window_end: bool, reset_enabled: bool):
-    """Returns (W_new, state_new, Wq of W_new, number of resets)."""
+RISK_BINS = 32
+
+
+def flip_count(Q: np.ndarray, Q_prev: np.ndarray) -> int:
+    """Elements whose quantized value changed since the previous step."""
+    return int(np.count_nonzero(np.asarray(Q, np.float32) != np.asarray(Q_prev, np.float32)))
+
+
+def risk_bin(dQ: np.ndarray, dM: np.ndarray) -> np.ndarray:
+    """Per-element risk bin (see the module docstring) of the window's distances."""
+    dQ = np.asarray(dQ, np.float32)
+    dM = np.asarray(dM, np.float32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        r = (dQ / dM).astype(np.float32)
+    # exponent field of the non-negative fp32 quotient: floor(log2 r) for normal r
+    e = ((r.view(np.uint32) >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int64) - 127
+    b = np.clip(e + 16, 1, 30)
+    b = np.where(dM == 0, 31, b)
+    return np.where(dQ == 0, 0, b).astype(np.int64)
+
+
+def risk_histogram(dQ: np.ndarray, dM: np.ndarray) -> np.ndarray:
+    return np.bincount(risk_bin(dQ, dM).ravel(), minlength=RISK_BINS).astype(np.int64)
+
+
+def osci_step(W: np.ndarray, st: OsciState, tau: float, window_end: bool, reset_enabled: bool,
+              diag: dict | None = None):
+    """Returns (W_new, state_new, Wq of W_new, number of resets).  With diag, adds this
+    call's flip count to diag["flips"] and, at a window end, the risk histogram to
+    diag["risk_hist"] (both created when missing)."""
     W = np.asarray(W, dtype=np.float32).copy()
     Q, _ = fwd_quant(W)
     dQ = (st.dQ + np.abs((Q - st.Q_prev).astype(np.float32))).astype(np.float32)
     dM = (st.dM + np.abs((W - st.W_prev).astype(np.float32))).astype(np.float32)
+    if diag is not None:
+        diag["flips"] = diag.get("flips", 0) + flip_count(Q, st.Q_prev)
+        if window_end:
+            diag["risk_hist"] = diag.get("risk_hist", np.zeros(RISK_BINS, np.int64)) + risk_histogram(dQ, dM)
     Q_prev = Q.copy()
     W_prev = W.copy()
     n_reset = 0
