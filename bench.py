@@ -355,6 +355,23 @@ def main():
                                                              mode=tj2.OSCI_ACCUM, tau=4.0) for li in lins], 3)
     # read W, m, v, grad, Q_prev, dQ, dM; write W, m, v, Q_prev, dQ, dM (fp32)
     master_bytes = n_params * 52.0
+    log("oscillation diagnostics")
+    flips = torch.zeros(1, dtype=torch.int64, device="cuda")
+    hist = torch.zeros(tj2.RISK_BINS, dtype=torch.int64, device="cuda")
+
+    def master_diag(mode, h):
+        for li in lins:
+            tj2.master_update_step(li.W, li.m, li.v, li.dW, *li.state[1:], lr=1e-6, bias_correction1=0.1,
+                                   bias_correction2=0.05, mode=mode, tau=4.0, flips=flips, risk_hist=h)
+
+    diag_accum_t = time_launches(lambda: master_diag(tj2.OSCI_ACCUM, None), 3)
+    flips.zero_()
+    master_diag(tj2.OSCI_ACCUM, None)
+    flips_per_pass = int(flips.item())
+    hist.zero_()
+    master_diag(tj2.OSCI_WINDOW_END, hist)  # the window so far: every master pass since the state's INIT
+    risk_hist = [int(x) for x in hist.cpu().tolist()]
+    diag_end_t = time_launches(lambda: master_diag(tj2.OSCI_WINDOW_END, hist), 2)
     del lins, ws
     torch.cuda.empty_cache()
 
@@ -407,6 +424,13 @@ def main():
                           "GB_s": round(master_bytes / master_t / 1e9, 1),
                           "frac_hbm": round(master_bytes / master_t / 1e9 / HBM_PEAK_GBS, 3),
                           "ms_per_step": round(master_t * 1e3, 3), "params": n_params},
+        "osci_diagnostics": {"what": "fused master pass with oscillation diagnostics: per-pass flip count (ACCUM), "
+                                     "window risk histogram in 32 log2 bins (WINDOW_END)",
+                             "accum_with_flips_ms": round(diag_accum_t * 1e3, 3),
+                             "accum_with_flips_GB_s": round(master_bytes / diag_accum_t / 1e9, 1),
+                             "window_end_with_hist_ms": round(diag_end_t * 1e3, 3),
+                             "window_end_with_hist_GB_s": round(master_bytes / diag_end_t / 1e9, 1),
+                             "flips_per_pass": flips_per_pass, "risk_hist_one_window_end": risk_hist},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -14,12 +14,12 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI_INIT, OSCI_WINDOW_END, RTN, SR,
-                   Tj2Error, check, lib)
+from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI_INIT, OSCI_WINDOW_END, RISK_BINS, RTN,
+                   SR, Tj2Error, check, lib)
 
 __all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "gemm_workspace", "linear_fwd", "linear_bwd", "linear_bwd_workspace",
            "osci_reset_step", "master_update_step", "channel_sumsq", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
-           "GROUP_ROW", "GROUP_COL", "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END"]
+           "GROUP_ROW", "GROUP_COL", "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END", "RISK_BINS"]
 
 
 def _stream():
@@ -232,13 +232,29 @@ def linear_bwd(dY: torch.Tensor, saved: dict, K: int, *, seed: int, offset: int,
     return dX, dW, ops
 
 
+def _diag(flips: torch.Tensor | None, risk_hist: torch.Tensor | None):
+    """Oscillation-diagnostic counters (device int64 / uint64; risk_hist holds RISK_BINS), or None."""
+    if flips is None and risk_hist is None:
+        return None
+    for name, t, n in (("flips", flips, 1), ("risk_hist", risk_hist, RISK_BINS)):
+        if t is not None and (not t.is_cuda or t.dtype not in (torch.int64, torch.uint64) or t.numel() < n
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device int64 tensor of at least {n} elements")
+    return ctypes.byref(_lib.OsciDiagC(_ptr(flips), _ptr(risk_hist)))
+
+
 def osci_reset_step(W, W_prev, Q_prev, dQ, dM, *, mode: int, tau: float = 4.0, reset_enabled: bool = False,
-                    Wq_out: QTensor | None = None, reset_count: torch.Tensor | None = None) -> None:
+                    Wq_out: QTensor | None = None, reset_count: torch.Tensor | None = None,
+                    flips: torch.Tensor | None = None, risk_hist: torch.Tensor | None = None) -> None:
+    """OsciReset step; flips / risk_hist (optional device counters) receive the oscillation
+    diagnostics: the number of elements whose quantized value changed, and at a window end the
+    risk histogram (RISK_BINS bins, see include/tj2.h)."""
     N, K = W.shape
     wqc = Wq_out.c() if Wq_out is not None else None
     st = lib().osci_reset_step(_ptr(W), _ptr(W_prev), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K, mode,
                                ctypes.c_float(tau), 1 if reset_enabled else 0,
-                               ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count), _stream())
+                               ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count),
+                               _diag(flips, risk_hist), _stream())
     check("osci_reset_step", st)
 
 
@@ -246,15 +262,17 @@ def master_update_step(W, m, v, grad, Q_prev, dQ, dM, *, lr: float, bias_correct
                        bias_correction2: float, beta1: float = 0.9, beta2: float = 0.95, eps: float = 1e-8,
                        weight_decay: float = 0.1, mode: int = OSCI_ACCUM, tau: float = 4.0,
                        reset_enabled: bool = False, Wq_out: QTensor | None = None,
-                       reset_count: torch.Tensor | None = None) -> None:
+                       reset_count: torch.Tensor | None = None, flips: torch.Tensor | None = None,
+                       risk_hist: torch.Tensor | None = None) -> None:
     """Fused master-weight pass: AdamW on W, then OsciReset (ACCUM / WINDOW_END) with the
-    pre-update master as W_prev, then the forward codes (Wq_out)."""
+    pre-update master as W_prev, then the forward codes (Wq_out); diagnostics as osci_reset_step."""
     N, K = W.shape
     ap = _lib.AdamWC(lr, beta1, beta2, eps, weight_decay, bias_correction1, bias_correction2)
     wqc = Wq_out.c() if Wq_out is not None else None
     st = lib().master_update_step(_ptr(W), _ptr(m), _ptr(v), _ptr(grad), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K,
                                   ctypes.byref(ap), mode, ctypes.c_float(tau), 1 if reset_enabled else 0,
-                                  ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count), _stream())
+                                  ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count),
+                                  _diag(flips, risk_hist), _stream())
     check("master_update_step", st)
 
 

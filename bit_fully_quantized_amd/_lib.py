@@ -62,6 +62,12 @@ class AdamWC(ctypes.Structure):
                 ("bias_correction1", ctypes.c_float), ("bias_correction2", ctypes.c_float)]
 
 
+class OsciDiagC(ctypes.Structure):
+    _fields_ = [("flips", P), ("risk_hist", P)]
+
+
+RISK_BINS = 32
+
 SIGNATURES = {
     "tj2_last_error": (ctypes.c_char_p, []),
     "tj2_version": (ctypes.c_char_p, []),
@@ -75,9 +81,10 @@ SIGNATURES = {
     "nvfp4_linear_bwd": (I32, [P, I64, I64, I64, QP, QP, QP, QP, ctypes.POINTER(PlanC), I32, U64, U64, P, I32, P,
                                ctypes.POINTER(BwdOperandsC), P, SZ, P]),
     "nvfp4_linear_bwd_workspace_size": (SZ, [I64, I64, I64, I32]),
-    "osci_reset_step": (I32, [P, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, QP, P, P]),
+    "osci_reset_step": (I32, [P, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, QP, P, ctypes.POINTER(OsciDiagC),
+                              P]),
     "master_update_step": (I32, [P, P, P, P, P, P, P, I64, I64, ctypes.POINTER(AdamWC), I32, ctypes.c_float, I32,
-                                 QP, P, P]),
+                                 QP, P, ctypes.POINTER(OsciDiagC), P]),
     "tj2_channel_sumsq": (I32, [P, I64, I64, P, P]),
 }
 

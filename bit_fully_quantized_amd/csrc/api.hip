@@ -61,6 +61,18 @@ tj2_status check_qtensor(const tj2_qtensor* q, const char* name, int fmt, int64_
   return TJ2_OK;
 }
 
+// Device counters of the oscillation diagnostics (NULL diag or members: off).
+tj2_status diag_pointers(const tj2_osci_diag* d, unsigned long long** flips, unsigned long long** hist) {
+  *flips = nullptr;
+  *hist = nullptr;
+  if (!d) return TJ2_OK;
+  if ((reinterpret_cast<uintptr_t>(d->flips) & 7u) || (reinterpret_cast<uintptr_t>(d->risk_hist) & 7u))
+    return fail(TJ2_ERR_ALIGN, "diagnostic counters must be 8-byte aligned");
+  *flips = reinterpret_cast<unsigned long long*>(d->flips);
+  *hist = reinterpret_cast<unsigned long long*>(d->risk_hist);
+  return TJ2_OK;
+}
+
 tj2_status check_dims(int64_t v, const char* name) {
   if (v <= 0 || v % 16) return fail(TJ2_ERR_SHAPE, "%s = %lld must be a positive multiple of 16", name, (long long)v);
   if (v > (int64_t)1 << 30) return fail(TJ2_ERR_SHAPE, "%s = %lld is too large", name, (long long)v);
@@ -471,7 +483,8 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
 
 tj2_status master_update_step(float* W, float* m, float* v, const float* grad, float* Q_prev, float* dQ, float* dM,
                               int64_t N, int64_t K, const tj2_adamw_params* adam, int32_t mode, float tau,
-                              int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count, void* stream) {
+                              int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
+                              const tj2_osci_diag* diag, void* stream) {
   if (!W || !m || !v || !grad || !Q_prev || !dQ || !dM) return fail(TJ2_ERR_ARG, "W, m, v, grad and the state arrays are required");
   if (!adam) return fail(TJ2_ERR_ARG, "adam parameters are required");
   if (!aligned16(W) || !aligned16(m) || !aligned16(v) || !aligned16(grad) || !aligned16(Q_prev) || !aligned16(dQ) ||
@@ -498,13 +511,14 @@ tj2_status master_update_step(float* W, float* m, float* v, const float* grad, f
     p.have_wq = 1;
   }
   p.reset_count = reinterpret_cast<unsigned long long*>(reset_count);
+  TJ2_TRY(diag_pointers(diag, &p.flips, &p.risk_hist));
   TJ2_TRY(hip_check(launch_master(p, (hipStream_t)stream), "master update launch"));
   return ok();
 }
 
 tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N, int64_t K,
                            int32_t mode, float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
-                           void* stream) {
+                           const tj2_osci_diag* diag, void* stream) {
   if (!W || !W_prev || !Q_prev || !dQ || !dM) return fail(TJ2_ERR_ARG, "W and the state arrays are required");
   if (!aligned16(W) || !aligned16(W_prev) || !aligned16(Q_prev) || !aligned16(dQ) || !aligned16(dM))
     return fail(TJ2_ERR_ALIGN, "arrays must be 16-byte aligned");
@@ -524,6 +538,7 @@ tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, fl
     p.have_wq = 1;
   }
   p.reset_count = reinterpret_cast<unsigned long long*>(reset_count);
+  TJ2_TRY(diag_pointers(diag, &p.flips, &p.risk_hist));
   TJ2_TRY(hip_check(launch_osci(p, (hipStream_t)stream), "osci launch"));
   return ok();
 }

@@ -11,6 +11,13 @@
 // amax with DPP.  The pass is element-wise and HBM-bound: 5 fp32 reads, 4-5
 // fp32 writes per element.
 //
+// Oscillation diagnostics (section 1 names the phenomenon: quantized weights
+// flipping between adjacent bins under small master updates): per call, the
+// number of elements whose E2M1 code differs from the previous master's (the
+// previous master is quantized once more for it), and at a window end the histogram of
+// the window's risk dQ / dM, reduced per workgroup in LDS and added to device
+// counters with one atomic per workgroup and counter.
+//
 // Calibration (section 2.C): per-channel sum of squares of the activations.
 #include "tj2_device.h"
 #include "tj2_internal.h"
@@ -82,16 +89,66 @@ __device__ __forceinline__ void fwd_quant8(const float w[8], bool valid, uint32_
   *S = g.S;
 }
 
+// Risk bin of one element from its window distances: 0 if dq == 0, 31 if only
+// dm == 0, else the binary exponent e of r = dq / dm (fp32, correctly rounded)
+// as min(max(e + 16, 1), 30).
+__device__ __forceinline__ uint32_t risk_bin(float dq, float dm) {
+  if (dq == 0.0f) return 0u;
+  if (dm == 0.0f) return (uint32_t)(kRiskBins - 1);
+  const float r = dq / dm;
+  const int e = (int)((__float_as_uint(r) >> 23) & 0xFFu) - 127;
+  return (uint32_t)min(max(e + 16, 1), kRiskBins - 2);
+}
+
+// Bin changes between two words of 8 E2M1 codes (sign bit 3 of each nibble);
+// +0 and -0 are one bin.
+__device__ __forceinline__ uint32_t code_flips(uint32_t c, uint32_t cp) {
+  uint32_t n = 0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t a = (c >> (4 * t)) & 15u, b = (cp >> (4 * t)) & 15u;
+    n += (a != b && ((a | b) & 7u) != 0u) ? 1u : 0u;
+  }
+  return n;
+}
+
+struct DiagSmem {
+  uint32_t flips;
+  uint32_t hist[kRiskBins];
+};
+
+// Adds the workgroup's flip count and (with bins) risk histogram to the device
+// counters.  Called by every thread of the workgroup under a condition that is
+// uniform over the grid (kernel parameters), so the barriers are reached by all.
+__device__ __forceinline__ void add_diag(DiagSmem& sm, unsigned long long* flips, unsigned long long* hist,
+                                         uint32_t n_flip, bool with_bins, const uint32_t (&bins)[8]) {
+  if (threadIdx.x == 0) sm.flips = 0u;
+  if (threadIdx.x < kRiskBins) sm.hist[threadIdx.x] = 0u;
+  __syncthreads();
+  if (n_flip) atomicAdd(&sm.flips, n_flip);
+  if (with_bins) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) atomicAdd(&sm.hist[bins[t]], 1u);
+  }
+  __syncthreads();
+  if (flips && threadIdx.x == 0 && sm.flips) atomicAdd(flips, (unsigned long long)sm.flips);
+  if (hist && threadIdx.x < kRiskBins && sm.hist[threadIdx.x])
+    atomicAdd(hist + threadIdx.x, (unsigned long long)sm.hist[threadIdx.x]);
+}
+
 // One lane per half group (8 consecutive elements of a row); the 16 lanes of
 // a 128-element outer block are consecutive.  All loads of the lane are issued
-// before the quantization work.
+// before the quantization work.  Lanes past the last row stay (no early exit,
+// the diagnostics use workgroup barriers) but touch no memory.
+template <bool DIAG>
 __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_per_row) {
+  __shared__ DiagSmem dsm;
   const uint32_t g = blockIdx.x * 256u + threadIdx.x;
   const uint32_t row = g / (uint32_t)halves_per_row;
-  if (row >= (uint32_t)p.N) return;  // whole outer blocks exit together
+  const bool live = row < (uint32_t)p.N;  // whole outer blocks are live or not
   const uint32_t jh = g - row * (uint32_t)halves_per_row;
   const uint32_t j = jh >> 1;  // 16-element group
-  const bool valid = (int64_t)j * 16 < p.K;
+  const bool valid = live && (int64_t)j * 16 < p.K;
   const int64_t base = (int64_t)row * p.K + (int64_t)jh * 8;
 
   float w[8], q[8], wp[8], qp[8], dq[8], dm[8];
@@ -110,8 +167,18 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_
   uint32_t code, s_code;
   float S;
   fwd_quant8(w, valid, &code, &s_code, &S, q);
+  uint32_t code_prev = 0;  // diagnostics: the previous master's codes (a flip is a change of bin)
+  if (DIAG && p.mode != TJ2_OSCI_INIT) {
+    float x[8], qx[8], Sx;
+    uint32_t sx;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x[t] = valid ? wp[t] : 0.0f;
+    fwd_quant8(x, valid, &code_prev, &sx, &Sx, qx);
+  }
 
-  uint32_t n_reset = 0;
+  uint32_t n_reset = 0, n_flip = 0;
+  uint32_t bins[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const bool want_bins = DIAG && p.risk_hist && p.mode == TJ2_OSCI_WINDOW_END;
   if (valid) {
     if (p.mode == TJ2_OSCI_INIT) {
       float z[8];
@@ -122,6 +189,7 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_
       store8f(p.dQ + base, z);
       store8f(p.dM + base, z);
     } else {
+      if (DIAG) n_flip = code_flips(code, code_prev);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         dq[t] = dq[t] + fabsf(q[t] - qp[t]);
@@ -129,6 +197,10 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_
         wp[t] = w[t];
       }
       if (p.mode == TJ2_OSCI_WINDOW_END) {
+        if (want_bins) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) bins[t] = risk_bin(dq[t], dm[t]);
+        }
         if (p.reset_enabled) {
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
@@ -150,7 +222,7 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_
     }
   }
   const bool any_reset = max16_lanes(n_reset ? 1.0f : 0.0f) > 0.0f;  // uniform over the outer block
-  if (p.have_wq) {
+  if (p.have_wq && live) {
     if (any_reset) fwd_quant8(w, valid, &code, &s_code, &S, q);  // scales may change after a reset
     const QView& o = p.wq;
     *reinterpret_cast<uint32_t*>(o.codes + (int64_t)row * o.ld_codes + jh * 4u) = code;
@@ -158,6 +230,7 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_
     if ((jh & 15u) == 0u) o.s128[(int64_t)row * o.ld_s128 + (j >> 3)] = S;
   }
   if (p.reset_count && n_reset) atomicAdd(p.reset_count, (unsigned long long)n_reset);
+  if constexpr (DIAG) add_diag(dsm, p.flips, want_bins ? p.risk_hist : nullptr, n_flip, want_bins && valid, bins);
 }
 
 // Fused master-weight pass (one read of the masters, their AdamW moments and the
@@ -167,13 +240,15 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_
 // then the OsciReset update of the new masters with the pre-update master as
 // W_prev (the distance the master travels is the update), then the forward
 // codes.  Lane layout as osci_kernel.
+template <bool DIAG>
 __global__ __launch_bounds__(256) void master_kernel(MasterParams p, int32_t halves_per_row) {
+  __shared__ DiagSmem dsm;
   const uint32_t g = blockIdx.x * 256u + threadIdx.x;
   const uint32_t row = g / (uint32_t)halves_per_row;
-  if (row >= (uint32_t)p.N) return;  // whole outer blocks exit together
+  const bool live = row < (uint32_t)p.N;  // as osci_kernel: no early exit
   const uint32_t jh = g - row * (uint32_t)halves_per_row;
   const uint32_t j = jh >> 1;
-  const bool valid = (int64_t)j * 16 < p.K;
+  const bool valid = live && (int64_t)j * 16 < p.K;
   const int64_t base = (int64_t)row * p.K + (int64_t)jh * 8;
 
   float w[8], m[8], v[8], gr[8], qp[8], dq[8], dm[8];
@@ -205,14 +280,27 @@ __global__ __launch_bounds__(256) void master_kernel(MasterParams p, int32_t hal
   float S;
   float q[8];
   fwd_quant8(w1, valid, &code, &s_code, &S, q);
-  uint32_t n_reset = 0;
+  uint32_t code_prev = 0;  // diagnostics: codes of the pre-update master
+  if (DIAG) {
+    float qx[8], Sx;
+    uint32_t sx;
+    fwd_quant8(w, valid, &code_prev, &sx, &Sx, qx);
+  }
+  uint32_t n_reset = 0, n_flip = 0;
+  uint32_t bins[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const bool want_bins = DIAG && p.risk_hist && p.window_end;
   if (valid) {
+    if (DIAG) n_flip = code_flips(code, code_prev);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       dq[t] = dq[t] + fabsf(q[t] - qp[t]);
       dm[t] = dm[t] + fabsf(w1[t] - w[t]);
     }
     if (p.window_end) {
+      if (want_bins) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) bins[t] = risk_bin(dq[t], dm[t]);
+      }
       if (p.reset_enabled) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -233,7 +321,7 @@ __global__ __launch_bounds__(256) void master_kernel(MasterParams p, int32_t hal
     store8f(p.dM + base, dm);
   }
   const bool any_reset = max16_lanes(n_reset ? 1.0f : 0.0f) > 0.0f;  // uniform over the outer block
-  if (p.have_wq) {
+  if (p.have_wq && live) {
     if (any_reset) fwd_quant8(w1, valid, &code, &s_code, &S, q);  // scales may change after a reset
     const QView& o = p.wq;
     *reinterpret_cast<uint32_t*>(o.codes + (int64_t)row * o.ld_codes + jh * 4u) = code;
@@ -241,6 +329,7 @@ __global__ __launch_bounds__(256) void master_kernel(MasterParams p, int32_t hal
     if ((jh & 15u) == 0u) o.s128[(int64_t)row * o.ld_s128 + (j >> 3)] = S;
   }
   if (p.reset_count && n_reset) atomicAdd(p.reset_count, (unsigned long long)n_reset);
+  if constexpr (DIAG) add_diag(dsm, p.flips, want_bins ? p.risk_hist : nullptr, n_flip, want_bins && valid, bins);
 }
 
 // acc[k] += sum_m X[m, k]^2.  Thread: 8 columns x 64 rows; 8 row slices per block
@@ -284,7 +373,10 @@ hipError_t launch_master(const MasterParams& p, hipStream_t s) {
   const int64_t nb = (p.K + 127) / 128;
   const int64_t hpr = nb * 16;  // half groups per row
   const int64_t blocks = (p.N * hpr + 255) / 256;
-  hipLaunchKernelGGL(master_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
+  if (p.flips || p.risk_hist)
+    hipLaunchKernelGGL(master_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
+  else
+    hipLaunchKernelGGL(master_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
   return hipGetLastError();
 }
 
@@ -292,7 +384,10 @@ hipError_t launch_osci(const OsciParams& p, hipStream_t s) {
   const int64_t nb = (p.K + 127) / 128;
   const int64_t hpr = nb * 16;  // half groups per row
   const int64_t blocks = (p.N * hpr + 255) / 256;
-  hipLaunchKernelGGL(osci_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
+  if (p.flips || p.risk_hist)
+    hipLaunchKernelGGL(osci_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
+  else
+    hipLaunchKernelGGL(osci_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
   return hipGetLastError();
 }
 

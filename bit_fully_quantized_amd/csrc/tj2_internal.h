@@ -110,7 +110,11 @@ struct OsciParams {
   QView wq;          // codes.rows==0 -> no codes output
   int have_wq;
   unsigned long long* reset_count;
+  unsigned long long* flips;      // oscillation diagnostics, NULL = off
+  unsigned long long* risk_hist;  // [kRiskBins], WINDOW_END only
 };
+
+constexpr int kRiskBins = 32;
 
 hipError_t launch_osci(const OsciParams& p, hipStream_t s);
 
@@ -128,6 +132,8 @@ struct MasterParams {
   QView wq;
   int have_wq;
   unsigned long long* reset_count;
+  unsigned long long* flips;      // as OsciParams
+  unsigned long long* risk_hist;
 };
 
 hipError_t launch_master(const MasterParams& p, hipStream_t s);

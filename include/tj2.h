@@ -237,6 +237,32 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
 size_t nvfp4_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers);
 
 /*
+ * Oscillation diagnostics (optional in osci_reset_step and master_update_step).
+ * Section 1 of the TetraJet-v2 technical summary names the failure mode they
+ * measure: small master updates that flip the quantized weight back and forth
+ * between adjacent bins; section 2.B defines the risk dist_Q / dist_M.  Both
+ * members are device uint64 counters that the call adds to (the caller zeroes
+ * them, e.g. at a window start); NULL members are skipped, as is a NULL diag.
+ *   flips:     ACCUM / WINDOW_END: the number of elements whose E2M1 code (bin
+ *              and sign) in the forward quantization of W differs from that of
+ *              the previous master (W_prev; for master_update_step the master
+ *              before the update), before any reset; +0 and -0 are one bin.
+ *              Codes are compared, not Q values: a block's FP32 scale moves with
+ *              its largest element, which changes Q without a change of bin.
+ *   risk_hist: [TJ2_RISK_BINS], WINDOW_END only: each element's window risk,
+ *              with dQ and dM as accumulated up to this step (before the reset
+ *              decision and the zeroing): bin 0 if dQ == 0; bin 31 if dQ > 0 and
+ *              dM == 0; otherwise, with r = dQ / dM rounded to fp32 and e its
+ *              binary exponent (floor(log2 r)), bin min(max(e + 16, 1), 30).
+ * Both pointers must be 8-byte aligned (TJ2_ERR_ALIGN).
+ */
+#define TJ2_RISK_BINS 32
+typedef struct {
+  uint64_t* flips;
+  uint64_t* risk_hist;
+} tj2_osci_diag;
+
+/*
  * OsciReset (section 2.B) on fp32 masters W [N, K] and its state arrays (all
  * fp32 [N, K], caller-owned).  Q(w) is the forward quantizer (RTN, 1x16 along K)
  * dequantized in fp32.
@@ -246,11 +272,13 @@ size_t nvfp4_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t 
  *                        W = Q(W), W_prev = Q(W); then dQ = dM = 0.
  * Wq_out (optional, NVFP4 [N, K]): forward codes of the final W.
  * reset_count (optional, device uint64): incremented by the number of resets.
+ * diag (optional): oscillation diagnostics (tj2_osci_diag).
  * K must be a multiple of 16.
  */
 tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N,
                            int64_t K, int32_t mode, float tau, int32_t reset_enabled,
-                           tj2_qtensor* Wq_out, uint64_t* reset_count, void* stream);
+                           tj2_qtensor* Wq_out, uint64_t* reset_count, const tj2_osci_diag* diag,
+                           void* stream);
 
 /*
  * AdamW hyper-parameters of one optimizer step on the fp32 masters (the pages
@@ -276,13 +304,14 @@ typedef struct {
  *   (TJ2_OSCI_INIT is osci_reset_step's; its W_prev is not read here).
  * Wq_out (optional, NVFP4 [N, K]): forward codes of the final W.
  * reset_count (optional, device uint64): incremented by the number of resets.
+ * diag (optional): oscillation diagnostics of the updated masters (tj2_osci_diag).
  * K must be a multiple of 16; arrays 16-byte aligned.  Errors: TJ2_ERR_ARG
  * (NULL array or params, bad mode, tau < 0), TJ2_ERR_SHAPE, TJ2_ERR_ALIGN.
  */
 tj2_status master_update_step(float* W, float* m, float* v, const float* grad, float* Q_prev, float* dQ,
                               float* dM, int64_t N, int64_t K, const tj2_adamw_params* adam, int32_t mode,
                               float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
-                              void* stream);
+                              const tj2_osci_diag* diag, void* stream);
 
 /*
  * OutControl calibration helper (section 2.C: top p% channels from a short

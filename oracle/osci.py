@@ -32,9 +32,13 @@ Oscillation diagnostics (optional, `diag` dict).  Section 1 of the technical
 summary names the failure mode these measure: small master updates that make
 the quantized weight flip back and forth between adjacent bins.
 
-* flips: per accum / window_end call, the number of elements whose quantized
-  value Q(W) differs from Q_prev (compared as fp32 values, so +0 and -0 are the
-  same bin); summed by the caller over a window this is the window's flip count.
+* flips: per accum / window_end call, the number of elements whose E2M1 code
+  (the bin, with its sign) in the forward quantization of W differs from the
+  code of the previous master W_prev, before any reset; +0 and -0 are one bin.
+  Codes rather than dequantized values are compared because the per-128 scale
+  moves with every update of a block's largest element, which changes Q(w) of
+  the whole block without moving any element to another bin.  Summed by the
+  caller over a window this is the window's flip count.
 * risk_hist (window_end only): the window's risk dQ / dM of every element,
   taken before the reset decision and the zeroing, counted into RISK_BINS
   bins:  bin 0: dQ == 0;  bin 31: dQ > 0 and dM == 0;  otherwise with
@@ -48,7 +52,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .quant import QTensor, dequantize, quantize
+from .quant import QTensor, dequantize, quantize, unpack_nibbles
 
 
 @dataclass
@@ -74,9 +78,16 @@ def osci_init(W: np.ndarray) -> tuple[OsciState, QTensor]:
 RISK_BINS = 32
 
 
-def flip_count(Q: np.ndarray, Q_prev: np.ndarray) -> int:
-    """Elements whose quantized value changed since the previous step."""
-    return int(np.count_nonzero(np.asarray(Q, np.float32) != np.asarray(Q_prev, np.float32)))
+def fwd_codes(W: np.ndarray) -> np.ndarray:
+    """E2M1 code (sign bit 3, magnitude bits 0-2) of every element of the forward quantization of W."""
+    return unpack_nibbles(fwd_quant(W)[1].codes)[:, : np.asarray(W).shape[1]]
+
+
+def flip_count(W: np.ndarray, W_prev: np.ndarray) -> int:
+    """Elements whose bin changed between the masters W_prev and W (+0 and -0 are one bin)."""
+    c, cp = fwd_codes(W), fwd_codes(W_prev)
+    same = (c == cp) | (((c & 7) == 0) & ((cp & 7) == 0))
+    return int(np.count_nonzero(~same))
 
 
 def risk_bin(dQ: np.ndarray, dM: np.ndarray) -> np.ndarray:
@@ -106,7 +117,7 @@ def osci_step(W: np.ndarray, st: OsciState, tau: float, window_end: bool, reset_
     dQ = (st.dQ + np.abs((Q - st.Q_prev).astype(np.float32))).astype(np.float32)
     dM = (st.dM + np.abs((W - st.W_prev).astype(np.float32))).astype(np.float32)
     if diag is not None:
-        diag["flips"] = diag.get("flips", 0) + flip_count(Q, st.Q_prev)
+        diag["flips"] = diag.get("flips", 0) + flip_count(W, st.W_prev)
         if window_end:
             diag["risk_hist"] = diag.get("risk_hist", np.zeros(RISK_BINS, np.int64)) + risk_histogram(dQ, dM)
     Q_prev = Q.copy()

@@ -126,10 +126,10 @@ def test_gemm_and_linear_argument_errors(L):
 def test_osci_argument_errors(L):
     from bit_fully_quantized_amd import _lib
     p = [0x1000 * (i + 1) for i in range(5)]
-    assert L.osci_reset_step(*p, 16, 100, 1, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_SHAPE
-    assert L.osci_reset_step(*p, 16, 128, 7, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
-    assert L.osci_reset_step(*p, 16, 128, 1, ctypes.c_float(-1.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
-    assert L.osci_reset_step(None, *p[1:], 16, 128, 1, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step(*p, 16, 100, 1, ctypes.c_float(4.0), 1, None, None, None, None) == _lib.TJ2_ERR_SHAPE
+    assert L.osci_reset_step(*p, 16, 128, 7, ctypes.c_float(4.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step(*p, 16, 128, 1, ctypes.c_float(-1.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step(None, *p[1:], 16, 128, 1, ctypes.c_float(4.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
     assert L.tj2_channel_sumsq(0x1000, 64, 100, 0x2000, None) == _lib.TJ2_ERR_SHAPE
 
 
@@ -138,13 +138,28 @@ def test_master_update_argument_errors(L):
     p = [0x1000 * (i + 1) for i in range(7)]
     ap = _lib.AdamWC(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
     f4 = ctypes.c_float(4.0)
-    assert L.master_update_step(*p, 16, 100, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None) == _lib.TJ2_ERR_SHAPE
-    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_INIT, f4, 0, None, None, None) == _lib.TJ2_ERR_ARG
-    assert L.master_update_step(*p, 16, 128, None, _lib.OSCI_ACCUM, f4, 0, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.master_update_step(*p, 16, 100, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None, None) == _lib.TJ2_ERR_SHAPE
+    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_INIT, f4, 0, None, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.master_update_step(*p, 16, 128, None, _lib.OSCI_ACCUM, f4, 0, None, None, None, None) == _lib.TJ2_ERR_ARG
     assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, ctypes.c_float(-1.0), 0, None, None,
-                                None) == _lib.TJ2_ERR_ARG
+                                None, None) == _lib.TJ2_ERR_ARG
     assert L.master_update_step(None, *p[1:], 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None,
-                                None) == _lib.TJ2_ERR_ARG
+                                None, None) == _lib.TJ2_ERR_ARG
     q = list(p)
     q[3] = 0x3008  # grad not 16-byte aligned
-    assert L.master_update_step(*q, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None) == _lib.TJ2_ERR_ALIGN
+    assert L.master_update_step(*q, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None, None) == _lib.TJ2_ERR_ALIGN
+
+
+def test_diag_counter_alignment(L):
+    # misaligned diagnostic counters are rejected on the host, before any launch
+    from bit_fully_quantized_amd import _lib
+    p = [0x1000 * (i + 1) for i in range(7)]
+    ap = _lib.AdamWC(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
+    f4 = ctypes.c_float(4.0)
+    d = _lib.OsciDiagC(0x5004, None)
+    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, ctypes.byref(d),
+                                None) == _lib.TJ2_ERR_ALIGN
+    assert b"8-byte" in L.tj2_last_error()
+    d = _lib.OsciDiagC(None, 0x5002)
+    assert L.osci_reset_step(*p[:5], 16, 128, _lib.OSCI_WINDOW_END, f4, 1, None, None, ctypes.byref(d),
+                             None) == _lib.TJ2_ERR_ALIGN

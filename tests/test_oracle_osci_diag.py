@@ -116,3 +116,26 @@ def test_histogram_invariants():
     # doubling dQ (exact) moves every element up by one bin, away from the clamped ends
     h2 = osci.risk_histogram((dQ * 2).astype(np.float32), dM)
     np.testing.assert_array_equal(h2[1:], h[:-1])
+
+
+def test_scale_drift_is_not_a_flip():
+    # Growing a block's largest element moves its FP32 outer scale, and with it the dequantized
+    # value of every element of the block, but no element changes bin: no flips.
+    r = np.random.default_rng(5)
+    W = (r.standard_normal((16, 128)) * 0.02).astype(np.float32)
+    W[:, 7] = 0.5  # the largest element of every row's single outer block
+    st, _ = osci.osci_init(W)
+    W1 = W.copy()
+    W1[:, 7] = np.float32(0.5 * (1 + 2 ** -20))
+    diag = {}
+    _, st1, _, _ = osci.osci_step(W1, st, tau=4.0, window_end=False, reset_enabled=False, diag=diag)
+    assert np.count_nonzero(st1.Q_prev != st.Q_prev) > 1000  # the values moved...
+    assert diag["flips"] == 0  # ...the bins did not
+    # one element pushed across a bin edge is one flip
+    W2 = W1.copy()
+    q1 = osci.fwd_codes(W1)
+    i = int(np.argmax((q1[0] & 7) == 2))  # an element of row 0 at the grid value 1 (in its group's steps)
+    W2[0, i] = np.float32(W1[0, i] * 1.6)
+    diag = {}
+    osci.osci_step(W2, st1, tau=4.0, window_end=False, reset_enabled=False, diag=diag)
+    assert diag["flips"] == int(np.count_nonzero(osci.fwd_codes(W2) != q1)) >= 1
