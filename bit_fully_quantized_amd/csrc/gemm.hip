@@ -356,11 +356,12 @@ struct FmtsMixB {
 // in block 0 decodes A fragment q of this chunk from the wave's A slice (the
 // previous chunk's last MFMA reading that fragment has issued), reads the B
 // fragment of slot q + kFragAhead, issues one MFMA into the block's partial
-// (blocks alternate between two partials), promotes a share of the previous
-// block (block 3 of the previous chunk during block 0; before the first chunk
-// that partial and its scales are zero), and stages the next chunk's B quarter
-// into the other LDS stage at slots 2, 8, 14, 20 and its B outer scales at
-// slot 3 (after the last chunk this writes unused data).  At slot 8 the A
+// (blocks alternate between two partials), promotes two or three elements of
+// the previous block at K-steps 2-7 (block 3 of the previous chunk during
+// block 0; before the first chunk that partial and its scales are zero), and
+// stages the next chunk's B quarter into the other LDS stage at slots 9, 15,
+// 20, 25, away from block 0's A decode, and its B outer scales at slot 3
+// (after the last chunk this writes unused data).  At slot 8 the A
 // slice is refilled with the next chunk (fetch_a).  The promotion reads S_B of
 // the block at its step 0 and the lane's 16 S_A values at steps 0-1 of blocks
 // 0 (previous chunk) and 1 (this chunk).  The workgroup barrier (sync) sits in
@@ -394,7 +395,7 @@ __device__ __forceinline__ void chunk(Smem& sm, const Ctx& t, int it, bool aseg1
     part[tn & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks], bf[q % kFragRing], ks == 0 ? float16v_t{} : part[tn & 1],
                                                           0, 0, 0);
     {
-      // the previous block's elements 4g..4g+3 are promoted at step g + 3 (its last MFMA has completed)
+      // the previous block's elements are promoted over steps 2-7 (its last MFMA has completed)
       constexpr int pb = tn > 0 ? tn - 1 : 3;
       if constexpr (ks == 0) scl.rb = sm.sb[tn > 0 ? it & 3 : (it - 1) & 3][pb * 32 + (t.lane & 31)];
       if constexpr (tn <= 1 && ks <= 1) {
@@ -402,15 +403,17 @@ __device__ __forceinline__ void chunk(Smem& sm, const Ctx& t, int it, bool aseg1
         scl.ra[2 * ks] = *reinterpret_cast<const float4*>(src + 16 * ks);
         scl.ra[2 * ks + 1] = *reinterpret_cast<const float4*>(src + 16 * ks + 8);
       }
-      if constexpr (ks >= 3 && ks <= 6) {
-        static_for<4>([&](auto i) __attribute__((always_inline)) {
-          promote_elem<4 * (ks - 3) + decltype(i)::value>(scl, part[pb & 1], acc[pb]);
+      if constexpr (ks >= 2) {
+        // elements [lo, hi) of the previous block at K-step ks (2..7): 3,3,3,3,2,2
+        constexpr int lo = ks <= 6 ? 3 * (ks - 2) : 14, hi = ks < 6 ? lo + 3 : lo + 2;
+        static_for<hi - lo>([&](auto i) __attribute__((always_inline)) {
+          promote_elem<lo + decltype(i)::value>(scl, part[pb & 1], acc[pb]);
         });
       }
     }
     if constexpr (q == 1) FM::prep_b(nb, sgb);
-    if constexpr (q % 6 == 2 && q <= 20) {
-      constexpr int u = q / 6;
+    if constexpr (q == 9 || q == 15 || q == 20 || q == 25) {
+      constexpr int u = q == 9 ? 0 : q == 15 ? 1 : q == 20 ? 2 : 3;
       *reinterpret_cast<half8_t*>(bdst + u * 8) = FM::template unit_b<u>(nb, sgb, bseg1);
     }
     if constexpr (q == 3) sm.sb[(it + 1) & 3][threadIdx.x >> 2] = nb.S;
