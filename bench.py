@@ -163,11 +163,17 @@ GEMM_SOURCES = [os.path.join(ROOT, "bit_fully_quantized_amd", "csrc", f)
 
 
 def gemm_source_hash():
+    """Hash of the product kernel's code: its sources with // comments and blank lines removed,
+    so that a change of comments alone does not invalidate the counter summary."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            for line in fh:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -15,19 +15,21 @@
 // block-scaled MFMA takes E8M0 scales per 32 elements, which cannot express an
 // E4M3 scale per 16, hence the f16 decode.
 //
-// Kernel: 128x128 output tile per 256-thread workgroup (2x2 waves of 64x64,
-// each 2x2 v_mfma_f32_32x32x16_f16).  Per 128-K chunk every thread loads one
-// row-half of A and of B (packed codes + scales), decodes it to f16 with
-// v_cvt_scalef32_pk_f16_fp4 / _fp8 (scale 1.0: exact) and v_pk_mul_f16 by the
-// inner scale, and writes it to LDS (rows padded to 272 bytes: conflict-free
-// 16-byte accesses).  Packed operands are prefetched two chunks ahead into
-// registers; the eight 16-deep K steps of a chunk are unrolled with the LDS
-// fragments of step k+1 read during step k; two workgroups per CU overlap one's
-// decode with the other's MFMA.  Operand formats are template parameters (no
-// runtime format branches); rows past the edge are clamped to the last row
-// (their results are never stored), so loads never diverge.  Workgroups are
-// numbered so that each of the 8 XCDs (own L2) gets a contiguous range of
-// output tiles, N-fastest: consecutive tiles on one XCD share their A rows.
+// Kernel: a 256x128 output tile per 512-thread workgroup (one per CU); wave w
+// owns rows 32w..32w+31 and all 128 columns (four 32x32 blocks of
+// v_mfma_f32_32x32x16_f16).  A goes global -> registers -> MFMA: each wave
+// decodes its own 32 rows (v_cvt_scalef32_pk_f16_fp4 / _fp8 at scale 1.0,
+// exact, then v_pk_mul_f16 by the inner scale).  B (128 rows) is decoded once
+// per workgroup into a double-buffered f16 LDS stage (rows padded to 272
+// bytes: conflict-free 16-byte fragment reads) and read by all eight waves.
+// Packed slices are prefetched one (A) and two to three (B) chunks ahead; a
+// chunk is 32 MFMA issue slots per wave in a fixed order that spreads the
+// decode, the promotion and the B staging over the slots, with one workgroup
+// barrier per chunk.  Operand formats are template parameters (no runtime
+// format branches); rows past the edge are clamped to the last row (their
+// results are never stored), so loads never diverge.  Workgroups are numbered
+// so that each of the 8 XCDs (own L2) gets a contiguous range of output tiles,
+// N-fastest: consecutive tiles on one XCD share their A rows.
 #include "tj2_device.h"
 #include "tj2_internal.h"
 
