@@ -355,8 +355,9 @@ struct FmtsMixB {
 };
 
 // One chunk as 32 issue slots (block tn = q / 8, K step ks = q % 8).  Slot q:
-// in block 0 decodes A fragment q of this chunk from the wave's A slice (the
-// previous chunk's last MFMA reading that fragment has issued), reads the B
+// in block 0 decodes A fragment q + 1 of this chunk from the wave's A slice (the
+// previous chunk's last MFMA reading that fragment has issued; fragment 0 was
+// decoded in the previous chunk's last slot, from this chunk's slice), reads the B
 // fragment of slot q + kFragAhead, issues one MFMA into the block's partial
 // (blocks alternate between two partials), promotes two or three elements of
 // the previous block at K-steps 2-7 (block 3 of the previous chunk during
@@ -374,22 +375,26 @@ struct FmtsMixB {
 // so every chunk runs all steps.
 template <class FM, int kFragAhead, class FETCH_A, class SYNC>
 __device__ __forceinline__ void chunk(Smem& sm, const Ctx& t, int it, bool aseg1, bool bseg1, half8_t (&af)[8],
-                                      half8_t (&bf)[frag_ring(kFragAhead)], float (&acc)[4][16], float16v_t (&part)[2], Slice& a,
-                                      const Slice& nb, FETCH_A&& fetch_a, SYNC&& sync) {
+                                      half2_t (&sga)[4], half8_t (&bf)[frag_ring(kFragAhead)], float (&acc)[4][16],
+                                      float16v_t (&part)[2], Slice& a, const Slice& nb, FETCH_A&& fetch_a,
+                                      SYNC&& sync) {
   const _Float16* bb = sm.b[it & 1] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
   const _Float16* bn = sm.b[(it + 1) & 1] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
   _Float16* bdst = sm.b[(it + 1) & 1] + (threadIdx.x >> 2) * LDS_STRIDE + t.bq * 32;
   const float* sa_row = &sm.sa[0][t.w * 32 + 4 * (t.lane >> 5)];
   constexpr int kFragRing = frag_ring(kFragAhead);
   Scl scl;
-  half2_t sga[4], sgb[4];
-  FM::prep_a(a, sga);
+  half2_t sgb[4];
   sm.sa[it & 3][t.w * 32 + (t.lane & 31)] = a.S;  // read back by this wave only
   static_for<32>([&](auto qc) __attribute__((always_inline)) {
     constexpr int q = decltype(qc)::value;
     constexpr int tn = q / 8, ks = q % 8;
-    if constexpr (q < 8) af[q] = FM::template frag_a<q>(a, sga, aseg1);
+    // A fragment q + 1 is decoded in slot q, one slot before its first MFMA;
+    // fragment 0 of the next chunk in slot 31 (after its last use in slot 24)
+    if constexpr (q < 7) af[q + 1] = FM::template frag_a<q + 1>(a, sga, aseg1);
     if constexpr (q == 8) fetch_a(a);
+    if constexpr (q == 30) FM::prep_a(a, sga);  // the next chunk's slice
+    if constexpr (q == 31) af[0] = FM::template frag_a<0>(a, sga, aseg1);
     if constexpr (q == 32 - kFragAhead) sync();
     constexpr int qf = q + kFragAhead;  // fragment read in this slot
     if constexpr (qf < 32) bf[qf % kFragRing] = ld8(bb + (qf / 8) * 32 * LDS_STRIDE + (qf % 8) * 8);
@@ -534,6 +539,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     using FM = std::conditional_t<MIXB, FmtsMixB, Fmts<FA0, FB0, F_NONE, F_NONE>>;
     Slice a, b1, b2;
     half8_t af[8];
+    half2_t sga[4];
     float16v_t part[2];
     part[1] = float16v_t{};
     // ring slot 3 stands for "chunk -1": zero scales for the first chunk's promotion of part[1]
@@ -560,6 +566,8 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     F::fetch_a(p, t, 0, s1, a);
     __builtin_amdgcn_sched_barrier(0);
     F::fetch_b(p, t, 2, s1, b2);
+    FM::prep_a(a, sga);
+    af[0] = FM::template frag_a<0>(a, sga, false);
     barrier_lds();
     constexpr int kFragAhead = kFragAheadFor<MIXB>;
     half8_t bf[frag_ring(kFragAhead)];
@@ -579,7 +587,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
         F::fetch_b(p, t, it + 3, s1, nb);
         barrier_lds();  // chunk it+1's B staged; this chunk's stage may be refilled
       };
-      chunk<FM, kFragAhead>(sm, t, it, false, t.b8, af, bf, acc, part, a, nb, fa, sync);
+      chunk<FM, kFragAhead>(sm, t, it, false, t.b8, af, sga, bf, acc, part, a, nb, fa, sync);
     };
     int it = 0;
     for (; it + 1 < s1; it += 2) {
