@@ -83,6 +83,14 @@ def test_linear_with_outliers_partial_blocks():
     _check_linear(128, 256, K, seed=4, rht=True, plan_idx=outl, offset=24)
 
 
+@pytest.mark.parametrize("K", [9216, 16896])
+def test_linear_wide_rows_with_outliers(K):
+    """Rows wider than the forward split kernel stages (fp32 W rows past 32 KB at K = 9216; bf16 X rows
+    too at K = 16896): those tensors go through the two gathering row quantizations instead."""
+    outl = calib.select_outliers(np.exp(np.random.default_rng(K).standard_normal(K) * 1.5), 0.1)
+    _check_linear(32, 64, K, seed=6, rht=True, plan_idx=outl, offset=40)
+
+
 def _state_to_dev(st):
     return [H.f32_to_device(a) for a in (st.W_prev, st.Q_prev, st.dQ, st.dM)]
 
