@@ -730,23 +730,32 @@ GemmKernel pick_kernel(const GemmParams& p) {
 
 }  // namespace
 
-// K splits of a product: one workgroup per CU at a time (256 CUs), so the time
-// is about (rounds of workgroups) x (chunks per workgroup); a split adds about
-// one chunk's worth of time per workgroup for its fp32 partial tile (written
-// here, read by the reduction).  The smallest split with the least estimated
-// time wins; splits keep at least four chunks each.
+// K splits of a product: one workgroup per CU at a time (256 CUs).  Estimated
+// time in units of one chunk's main loop: rounds of workgroups x (chunks per
+// workgroup + kRoundChunks), plus the reduction's HBM traffic for a split
+// ((split + 1) fp32 copies of the output, kReduceBytesPerChunk per unit).
+// kRoundChunks covers a workgroup's prologue, epilogue and partial tile and
+// the loss of a partly filled or repeated round; it is fitted to measured
+// products of the weight-gradient shapes (3072x1024, 1024x1024, 4096x1024 and
+// 1024x4096 outputs over 16384 tokens), for which it picks the measured best
+// split (2, 8, 2, 2).  The smallest split with the least estimated time wins;
+// splits keep at least four chunks each.
 int gemm_split(int64_t I, int64_t J, int64_t nchunks) {
   constexpr int64_t kCUs = 256;
+  constexpr double kRoundChunks = 10.0;
+  constexpr double kReduceBytesPerChunk = 12.1e6;
   const int64_t tiles = ((I + BM - 1) / BM) * ((J + BN - 1) / BN);
   if (tiles >= kCUs || nchunks < 8) return 1;
-  int64_t best = 1, best_cost = -1;
+  int64_t best = 1;
+  double best_cost = -1.0;
   for (int64_t s = 1; s <= 64 && nchunks / s >= 4; ++s) {
     const int64_t cps = (nchunks + s - 1) / s;
     const int64_t splits = (nchunks + cps - 1) / cps;  // as launched: no empty splits
     if (splits != s) continue;
     const int64_t rounds = (tiles * s + kCUs - 1) / kCUs;
-    const int64_t cost = rounds * (cps + (s > 1 ? 1 : 0));
-    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = s; }
+    const double cost = (double)rounds * ((double)cps + kRoundChunks) +
+                        (s > 1 ? (double)(s + 1) * (double)I * (double)J * 4.0 / kReduceBytesPerChunk : 0.0);
+    if (best_cost < 0.0 || cost < best_cost) { best_cost = cost; best = s; }
   }
   return (int)best;
 }
