@@ -213,11 +213,10 @@ struct Op<TJ2_FP8> {
 __device__ __forceinline__ half8_t ld8(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
 
 // B fragments are read D MFMA slots before use, in a ring of frag_ring(D)
-// registers (32 % ring == 0 so ring positions carry over between chunks):
-// D = 5 in general, 3 for outlier-column products (fewer registers).
+// registers (32 % ring == 0 so ring positions carry over between chunks).
+// D = 5 (3 to 7 measure the same).
 constexpr int frag_ring(int d) { return d < 4 ? 4 : 8; }
-template <bool MIXB>
-constexpr int kFragAheadFor = MIXB ? 5 : 5;
+constexpr int kFragAheadSlots = 5;
 
 typedef float float16v_t __attribute__((ext_vector_type(16)));
 
@@ -569,7 +568,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     FM::prep_a(a, sga);
     af[0] = FM::template frag_a<0>(a, sga, false);
     barrier_lds();
-    constexpr int kFragAhead = kFragAheadFor<MIXB>;
+    constexpr int kFragAhead = kFragAheadSlots;
     half8_t bf[frag_ring(kFragAhead)];
     {
       const _Float16* bb = sm.b[0] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;

@@ -6,15 +6,21 @@
 // weight groups whose transpose is re-grouped) and section 2.C (Hadamard
 // transform on the backward operands; FP8 outlier channels).
 //
-// Two kernels, both HBM-bound streaming passes with no global reduction:
+// Single-pass kernels with no global reduction (the double block's purpose):
 //  * quant_row: groups along the contiguous dimension.  One lane owns one
 //    16-element group; the 8 lanes of an outer block reduce its amax with DPP.
-//  * quant_col: groups along rows, output stored transposed.  One lane owns a
-//    16-row x 8-column patch (8 groups, one per column); the 8 lanes stacked
-//    along rows form a 128-row outer block.  A row of the patch is one 16-byte
-//    (bf16) load, so lanes with neighbouring column patches read contiguous
-//    128-byte segments.  Stochastic draws follow the output position, so each
-//    16-element group uses two whole Philox blocks generated on the spot.
+//  * quant_col: groups along rows, output stored transposed.  A workgroup
+//    stages a 128-row x 64-column input tile in LDS with coalesced row reads;
+//    a lane takes two columns x 16 rows (one group per column) and the 8 lanes
+//    stacked along rows form a 128-row outer block.  Packed NVFP4 / FP8 inputs
+//    (the forward's operands, re-grouped for the backward) are decoded from the
+//    tile.  quant_col_multi runs several such problems in one launch.
+//  * quant_split: the forward's one read of X (or W) into its NVFP4 rest
+//    columns and FP8 outlier columns, whole rows staged in LDS.
+// Stochastic draws follow the output position (Philox blocks of 8 elements,
+// generated on the spot).  Round-to-nearest passes are bound by HBM; with
+// stochastic rounding and the Hadamard transform the arithmetic (Philox,
+// butterflies) bounds them.
 #include <algorithm>
 #include <cstring>
 
