@@ -271,6 +271,17 @@ def library_gemm_reference(M, shapes, reps=10):
     return res, flops / secs / 1e12
 
 
+def mfma_reference(reps=3):
+    """Achievable dense f16 MFMA rate of the part: the library's MFMA-only measurement loop
+    (four independent v_mfma_f32_32x32x16_f16 chains per wave, 2048 workgroups), TFLOP/s."""
+    import torch
+    import bit_fully_quantized_amd as tj2
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    flops = tj2.mfma_peak_probe(out, 1024)
+    t = time_launches(lambda: tj2.mfma_peak_probe(out, 1024), reps)
+    return flops / t / 1e12
+
+
 def cpu_baseline(M=8192, K=1024, N=3072, p=0.10):
     """The oracle (fp64 products, numpy quantizers) on one QKV-shaped linear with M tokens."""
     import numpy as np
@@ -381,6 +392,8 @@ def main():
     del lins, ws
     torch.cuda.empty_cache()
 
+    log("MFMA-only reference loop")
+    mfma_ach = mfma_reference()
     log("library bf16 product reference")
     lib_ref, lib_all = library_gemm_reference(M, [(f"{spec.name}.fwd", spec.K, spec.N) for spec in wl.linears])
     sweep, sweep_bytes = ({}, 0) if args.no_sweep else quant_sweep(tj2)
@@ -414,6 +427,9 @@ def main():
             "algorithmic_bytes_per_launch": round(g_bytes / g_launches),
             "avg_launch_us": round(g_time / g_launches * 1e6, 2), "launches_per_step": g_launches,
             "gemm_share_of_step": round(g_time / step_s, 3), "per_launch": per,
+            "achievable_mfma": {"what": "MFMA-only loop (v_mfma_f32_32x32x16_f16, register operands) on this part",
+                                "TFLOP_s": round(mfma_ach, 1), "frac_of_peak": round(mfma_ach / MFMA_F16_PEAK_TFLOPS, 3),
+                                "products_frac_of_it": round(achieved / mfma_ach, 3)},
             "library_bf16_reference": {"what": "torch.mm bf16 (hipBLASLt) on plain operands of each linear's "
                                                "forward shape, TFLOP/s: the achievable dense rate as a vendor "
                                                "library reaches it, without decode or per-128 promotion",

@@ -18,7 +18,7 @@ from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI
                    SR, Tj2Error, check, lib)
 
 __all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "gemm_workspace", "linear_fwd", "linear_bwd", "linear_bwd_workspace",
-           "osci_reset_step", "master_update_step", "channel_sumsq", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
+           "osci_reset_step", "master_update_step", "channel_sumsq", "mfma_peak_probe", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
            "GROUP_ROW", "GROUP_COL", "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END", "RISK_BINS"]
 
 
@@ -274,6 +274,16 @@ def master_update_step(W, m, v, grad, Q_prev, dQ, dM, *, lr: float, bias_correct
                                   ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count),
                                   _diag(flips, risk_hist), _stream())
     check("master_update_step", st)
+
+
+def mfma_peak_probe(out: torch.Tensor, iters: int) -> float:
+    """Measurement helper (not part of the path): an MFMA-only loop in out.numel() // 256
+    workgroups; returns the flops it performs (the caller times it on the current stream)."""
+    wgs = out.numel() // 256
+    if not out.is_cuda or out.dtype != torch.float32 or wgs < 1:
+        raise ValueError("out must be a device float32 tensor of at least 256 elements")
+    check("tj2_mfma_peak_probe", lib().tj2_mfma_peak_probe(wgs, iters, _ptr(out), _stream()))
+    return float(wgs) * 4 * iters * 4 * 32768
 
 
 def channel_sumsq(X: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:

@@ -86,6 +86,7 @@ SIGNATURES = {
     "master_update_step": (I32, [P, P, P, P, P, P, P, I64, I64, ctypes.POINTER(AdamWC), I32, ctypes.c_float, I32,
                                  QP, P, ctypes.POINTER(OsciDiagC), P]),
     "tj2_channel_sumsq": (I32, [P, I64, I64, P, P]),
+    "tj2_mfma_peak_probe": (I32, [I64, I32, P, P]),
 }
 
 

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libtj2.so")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "osci.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "osci.hip", "probe.hip"]
 
 # -ffp-contract=off keeps every fp32 step a single IEEE operation (bit-exact
 # quantizers); packed fp32 instructions are disabled.

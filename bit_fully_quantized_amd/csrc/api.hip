@@ -552,4 +552,12 @@ tj2_status tj2_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, vo
   return ok();
 }
 
+tj2_status tj2_mfma_peak_probe(int64_t workgroups, int32_t iters, float* out, void* stream) {
+  if (!out) return fail(TJ2_ERR_ARG, "out is required");
+  if (workgroups < 1 || workgroups > ((int64_t)1 << 20)) return fail(TJ2_ERR_ARG, "workgroups out of range");
+  if (iters < 1 || iters > (1 << 20)) return fail(TJ2_ERR_ARG, "iters out of range");
+  TJ2_TRY(hip_check(launch_mfma_peak(workgroups, iters, out, (hipStream_t)stream), "mfma probe launch"));
+  return ok();
+}
+
 }  // extern "C"

@@ -140,4 +140,7 @@ hipError_t launch_master(const MasterParams& p, hipStream_t s);
 
 hipError_t launch_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, hipStream_t s);
 
+// measurement helper: MFMA-only loop (see tj2_mfma_peak_probe)
+hipError_t launch_mfma_peak(int64_t workgroups, int32_t iters, float* out, hipStream_t s);
+
 }  // namespace tj2

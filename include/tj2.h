@@ -320,6 +320,18 @@ tj2_status master_update_step(float* W, float* m, float* v, const float* grad, f
  */
 tj2_status tj2_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, void* stream);
 
+/*
+ * Measurement helper, not part of the path: the achievable dense f16 MFMA rate
+ * of the part.  Runs `workgroups` workgroups of 256 threads (4 waves); each wave
+ * runs `iters` rounds of four independent v_mfma_f32_32x32x16_f16 accumulation
+ * chains on register operands (every element 0.0625, so each thread's result,
+ * written to out[workgroup * 256 + thread], is 0.25 * iters exactly).  Work:
+ * workgroups * 4 * iters * 4 * 32768 flops; the caller times the call on its
+ * stream.  out: device, workgroups * 256 floats, caller-owned.  Errors:
+ * TJ2_ERR_ARG (NULL out, workgroups outside [1, 2^20], iters outside [1, 2^20]).
+ */
+tj2_status tj2_mfma_peak_probe(int64_t workgroups, int32_t iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

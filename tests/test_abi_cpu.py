@@ -163,3 +163,10 @@ def test_diag_counter_alignment(L):
     d = _lib.OsciDiagC(None, 0x5002)
     assert L.osci_reset_step(*p[:5], 16, 128, _lib.OSCI_WINDOW_END, f4, 1, None, None, ctypes.byref(d),
                              None) == _lib.TJ2_ERR_ALIGN
+
+
+def test_mfma_probe_argument_errors(L):
+    from bit_fully_quantized_amd import _lib
+    assert L.tj2_mfma_peak_probe(16, 8, None, None) == _lib.TJ2_ERR_ARG
+    assert L.tj2_mfma_peak_probe(0, 8, 0x1000, None) == _lib.TJ2_ERR_ARG
+    assert L.tj2_mfma_peak_probe(16, 0, 0x1000, None) == _lib.TJ2_ERR_ARG

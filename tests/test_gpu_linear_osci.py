@@ -162,3 +162,12 @@ def test_channel_sumsq():
     np.testing.assert_allclose(acc.cpu().numpy(), ref, rtol=1e-5)
     got = calib.select_outliers(acc.cpu().numpy().astype(np.float64), 0.1)
     assert len(np.intersect1d(got, calib.select_outliers(ref, 0.1))) >= 110
+
+
+def test_mfma_peak_probe_result():
+    """The measurement helper's MFMA-only loop: every thread's sum is 0.25 * iters exactly."""
+    out = torch.full((8 * 256,), -1.0, dtype=torch.float32, device="cuda")
+    flops = tj2.mfma_peak_probe(out, 100)
+    torch.cuda.synchronize()
+    assert flops == 8 * 4 * 100 * 4 * 32768
+    assert torch.all(out == 25.0)
