@@ -54,6 +54,8 @@ tj2_status check_qtensor(const tj2_qtensor* q, const char* name, int fmt, int64_
                 (long long)q->len, (long long)rows, (long long)len);
   if (len <= 0 || len % 16) return fail(TJ2_ERR_SHAPE, "%s: len %lld is not a positive multiple of 16", name, (long long)len);
   if (rows <= 0) return fail(TJ2_ERR_SHAPE, "%s: rows must be positive", name);
+  // the products index 128-element blocks (row * blocks per row) in 32 bits
+  if (rows * ((len + 127) / 128) >= ((int64_t)1 << 32)) return fail(TJ2_ERR_SHAPE, "%s: too many 128-element blocks", name);
   if (!q->codes || !q->scale128 || (fmt == TJ2_NVFP4 && !q->scale16))
     return fail(TJ2_ERR_ARG, "%s: NULL array", name);
   if (!aligned16(q->codes) || !aligned16(q->scale128) || (fmt == TJ2_NVFP4 && !aligned16(q->scale16)))

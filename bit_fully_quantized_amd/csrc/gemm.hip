@@ -91,19 +91,21 @@ struct Op;
 
 template <>
 struct Op<TJ2_NVFP4> {
-  // rn = row * (outer blocks per row): codes at rn * 64 bytes, inner scales at rn * 8, outer at rn
+  // rn = row * (outer blocks per row), below 2^32 for any operand that fits in memory (rows x
+  // len / 128): codes at rn * 64 bytes (64-bit offsets: an operand's codes may exceed 4 GB),
+  // inner scales at rn * 8, outer at rn
   static __device__ __forceinline__ void load_half(const OperandK& o, uint32_t rn, int kc, int half, Slice& s) {
-    const uint8_t* cp = o.codes + (size_t)kc * 64 + (rn * 64 + half * 32);
+    const uint8_t* cp = o.codes + (size_t)kc * 64 + ((size_t)rn * 64 + half * 32);
     s.q[0] = *reinterpret_cast<const uint4*>(cp);
     s.q[1] = *reinterpret_cast<const uint4*>(cp + 16);
-    s.q[2].x = *reinterpret_cast<const uint32_t*>(o.s16 + (size_t)kc * 8 + (rn * 8 + half * 4));
+    s.q[2].x = *reinterpret_cast<const uint32_t*>(o.s16 + (size_t)kc * 8 + ((size_t)rn * 8 + half * 4));
     s.S = (o.s128 + kc)[rn];
   }
   static __device__ __forceinline__ void load_quarter(const OperandK& o, uint32_t rn, int kc, int qt, Slice& s) {
-    s.q[0] = *reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 64 + (rn * 64 + qt * 16));
+    s.q[0] = *reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 64 + ((size_t)rn * 64 + qt * 16));
     // the aligned word holding this quarter's two inner scales, and its shift: a
     // full-word load lands in the slice's own register (no extension on use)
-    s.q[1].x = *reinterpret_cast<const uint32_t*>(o.s16 + (size_t)kc * 8 + (rn * 8 + (qt >> 1) * 4));
+    s.q[1].x = *reinterpret_cast<const uint32_t*>(o.s16 + (size_t)kc * 8 + ((size_t)rn * 8 + (qt >> 1) * 4));
     s.q[1].y = (uint32_t)(qt & 1) * 16u;
     s.S = (o.s128 + kc)[rn];
   }
@@ -164,13 +166,13 @@ template <>
 struct Op<TJ2_FP8> {
   // rn = row * (outer blocks per row): codes at rn * 128 bytes, outer scales at rn
   static __device__ __forceinline__ void load_half(const OperandK& o, uint32_t rn, int kc, int half, Slice& s) {
-    const uint4* p = reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 128 + (rn * 128 + half * 64));
+    const uint4* p = reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 128 + ((size_t)rn * 128 + half * 64));
 #pragma unroll
     for (int i = 0; i < 4; ++i) s.q[i] = p[i];
     s.S = (o.s128 + kc)[rn];
   }
   static __device__ __forceinline__ void load_quarter(const OperandK& o, uint32_t rn, int kc, int qt, Slice& s) {
-    const uint4* p = reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 128 + (rn * 128 + qt * 32));
+    const uint4* p = reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 128 + ((size_t)rn * 128 + qt * 32));
     s.q[0] = p[0];
     s.q[1] = p[1];
     s.S = (o.s128 + kc)[rn];
@@ -269,12 +271,12 @@ struct FmtMixB {
   // are read from valid addresses and ignored).
   static __device__ __forceinline__ void fetch_b(const GemmKArgs& p, const Ctx& t, int it, int n, Slice& b) {
     const int g = t.c_begin + min(it, n - 1);
-    const uint8_t* c4 = p.seg[0].b.codes + (size_t)g * 64 + (t.brn[0] * 64 + t.bq * 16);
-    const uint8_t* c8 = p.b8.codes + (size_t)g * 128 + (t.brn[1] * 128 + t.bq * 32);
+    const uint8_t* c4 = p.seg[0].b.codes + (size_t)g * 64 + ((size_t)t.brn[0] * 64 + t.bq * 16);
+    const uint8_t* c8 = p.b8.codes + (size_t)g * 128 + ((size_t)t.brn[1] * 128 + t.bq * 32);
     const uint8_t* c = t.b8 ? c8 : c4;
     b.q[0] = *reinterpret_cast<const uint4*>(c);
     b.q[1] = *reinterpret_cast<const uint4*>(t.b8 ? c8 + 16 : c4);
-    b.q[2].x = *reinterpret_cast<const uint32_t*>(p.seg[0].b.s16 + (size_t)g * 8 + (t.brn[0] * 8 + (t.bq >> 1) * 4));
+    b.q[2].x = *reinterpret_cast<const uint32_t*>(p.seg[0].b.s16 + (size_t)g * 8 + ((size_t)t.brn[0] * 8 + (t.bq >> 1) * 4));
     b.q[2].y = (uint32_t)(t.bq & 1) * 16u;
     b.S = t.b8 ? (p.b8.s128 + g)[t.brn[1]] : (p.seg[0].b.s128 + g)[t.brn[0]];
   }

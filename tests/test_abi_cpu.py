@@ -170,3 +170,12 @@ def test_mfma_probe_argument_errors(L):
     assert L.tj2_mfma_peak_probe(16, 8, None, None) == _lib.TJ2_ERR_ARG
     assert L.tj2_mfma_peak_probe(0, 8, 0x1000, None) == _lib.TJ2_ERR_ARG
     assert L.tj2_mfma_peak_probe(16, 0, 0x1000, None) == _lib.TJ2_ERR_ARG
+
+
+def test_qtensor_block_count_limit(L):
+    # operands are indexed by 128-element block in 32 bits; larger ones are rejected on the host
+    from bit_fully_quantized_amd import _lib
+    out = _lib.QTensorC(0x10000, 0x20000, 0x30000, 1 << 30, 1 << 30, _lib.NVFP4, 0)
+    assert L.nvfp4_quantize(0x1000, _lib.BF16, None, 1 << 30, 1 << 30, None, 0, 0, 0, 0, 0, 0, 0, ctypes.byref(out),
+                            None) == _lib.TJ2_ERR_SHAPE
+    assert b"128-element blocks" in L.tj2_last_error()

@@ -141,3 +141,36 @@ def test_gemm_outlier_cols(name, I, J, K, outl):
     out = torch.from_numpy(c).cuda()
     tj2.gemm_outlier_cols(ga, gb, gb8, plan, out=out, accumulate=True)
     assert H.rel_fro(out.cpu().numpy(), 2 * ref) < 1e-5
+
+
+def test_gemm_operand_codes_beyond_4gb():
+    """An A operand whose packed codes exceed 4 GB (4096 rows x 2.1 M elements): rows past the 4 GB
+    mark are addressed with 64-bit offsets.  Random packed operands (any byte is a pair of E2M1
+    codes; E4M3 inner scales 2^-3..2^3; positive outer scales), seeded on the device; sampled
+    outputs, including the last row, against the oracle's fp64 product of the same bytes."""
+    I, J, K = 4096, 16, (1 << 21) + (1 << 14)
+    nb = K // 128
+    assert (I - 1) * nb * 64 >= (1 << 32)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+
+    def operand(rows):
+        q = tj2.QTensor(tj2.NVFP4, rows, K)
+        q.codes.random_(0, 256, generator=g)
+        q.scale16.random_(0x20, 0x51, generator=g)
+        q.scale128.copy_(torch.rand(q.scale128.shape, generator=g, device="cuda") * 0.5 + 0.5)
+        return q
+
+    def host(q, rows):
+        idx = torch.tensor(rows, device="cuda")
+        return quant.QTensor("nvfp4", q.codes[idx].cpu().numpy(), q.scale128[idx].cpu().numpy(),
+                             q.scale16[idx].cpu().numpy(), len(rows), K)
+
+    A, B = operand(I), operand(J)
+    C = tj2.gemm(A, B, workspace=tj2.gemm_workspace(I, J, K)).cpu().numpy()
+    rows, cols = [0, 2047, I - 1], [0, J - 1]
+    ra, rb = host(A, rows), host(B, cols)
+    del A, B
+    torch.cuda.empty_cache()
+    ref = ogemm.gemm_nt_f64(ra, rb)
+    assert H.rel_fro(C[np.ix_(rows, cols)], ref) <= H.GEMM_TOL
