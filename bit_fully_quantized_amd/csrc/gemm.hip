@@ -11,7 +11,11 @@
 // significant bits and lies in [2^-10, 2688], so it is exact in f16; the FP32
 // outer scales cannot be folded into the elements without rounding, so each
 // 128-wide K chunk is reduced on MFMA into a fresh f32 partial and promoted
-// into the accumulator with one multiply-add by S_A * S_B.  CDNA4's
+// into the accumulator with one multiply-add by S_A * S_B.  The products
+// S_A * S_B of a chunk come from the fp32 outer-product MFMA
+// (v_mfma_f32_32x32x1_2b_f32: two 32x32 blocks of a[i] * b[j] in fp32)
+// straight in the accumulator layout, which leaves one VALU instruction per
+// element and chunk.  CDNA4's
 // block-scaled MFMA takes E8M0 scales per 32 elements, which cannot express an
 // E4M3 scale per 16, hence the f16 decode.
 //
@@ -29,7 +33,9 @@
 // format branches); rows past the edge are clamped to the last row (their
 // results are never stored), so loads never diverge.  Workgroups are numbered
 // so that each of the 8 XCDs (own L2) gets a contiguous range of output tiles,
-// N-fastest: consecutive tiles on one XCD share their A rows.
+// N-fastest: consecutive tiles on one XCD share their A rows.  Results leave
+// through LDS as 16-byte row pieces where the tile's columns are contiguous
+// and aligned in the output (element stores otherwise).
 #include "tj2_device.h"
 #include "tj2_internal.h"
 
@@ -221,6 +227,7 @@ constexpr int frag_ring(int d) { return d < 4 ? 4 : 8; }
 constexpr int kFragAheadSlots = 5;
 
 typedef float float16v_t __attribute__((ext_vector_type(16)));
+typedef float float32v_t __attribute__((ext_vector_type(32)));
 
 // Shared memory: two decoded f16 stages of the B tile and four-deep rings of
 // the outer scales of both operands (a chunk's scales are read one chunk later).
@@ -228,6 +235,15 @@ struct Smem {
   _Float16 b[2][BN * LDS_STRIDE];
   float sa[4][BM];
   float sb[4][BN];
+};
+
+// Output staging after the K loop, in the same memory: each wave's 32x128 fp32
+// results (rows padded to 136 words: the two lane halves, four rows apart,
+// write disjoint bank halves).
+constexpr int OUT_STRIDE = BN + 8;
+union SmemAll {
+  Smem loop;
+  float out[BM / 32][32][OUT_STRIDE];
 };
 
 // Per-thread roles.  Wave w owns output rows 32w..32w+31 of the 256x128 tile
@@ -362,13 +378,13 @@ struct FmtsMixB {
 // fragment of slot q + kFragAhead, issues one MFMA into the block's partial
 // (blocks alternate between two partials), promotes two or three elements of
 // the previous block at K-steps 2-7 (block 3 of the previous chunk during
-// block 0; before the first chunk that partial and its scales are zero), and
+// block 0; before the first chunk that partial and its scales are zero) with
+// the scale products of blocks 0-1 and 2-3 issued at slots 8 and 24, and
 // stages the next chunk's B quarter into the other LDS stage at slots 9, 15,
 // 20, 25, away from block 0's A decode, and its B outer scales at slot 3
 // (after the last chunk this writes unused data).  At slot 8 the A
-// slice is refilled with the next chunk (fetch_a).  The promotion reads S_B of
-// the block at its step 0 and the lane's 16 S_A values at steps 0-1 of blocks
-// 0 (previous chunk) and 1 (this chunk).  The workgroup barrier (sync) sits in
+// slice is refilled with the next chunk (fetch_a); its S_A was kept from the
+// chunk start.  The workgroup barrier (sync) sits in
 // slot 32 - kFragAhead, once the next stage is written and this chunk's last
 // fragment read has been issued, so the last slots already read the next
 // chunk's first fragments.  A scheduling barrier after each slot keeps this
@@ -377,16 +393,15 @@ struct FmtsMixB {
 template <class FM, int kFragAhead, class FETCH_A, class SYNC>
 __device__ __forceinline__ void chunk(Smem& sm, const Ctx& t, int it, bool aseg1, bool bseg1, half8_t (&af)[8],
                                       half2_t (&sga)[4], half8_t (&bf)[frag_ring(kFragAhead)], float (&acc)[4][16],
-                                      float16v_t (&part)[2], Slice& a, const Slice& nb, FETCH_A&& fetch_a,
-                                      SYNC&& sync) {
+                                      float16v_t (&part)[2], float32v_t& smat, Slice& a, const Slice& nb,
+                                      FETCH_A&& fetch_a, SYNC&& sync) {
   const _Float16* bb = sm.b[it & 1] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
   const _Float16* bn = sm.b[(it + 1) & 1] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
   _Float16* bdst = sm.b[(it + 1) & 1] + (threadIdx.x >> 2) * LDS_STRIDE + t.bq * 32;
-  const float* sa_row = &sm.sa[0][t.w * 32 + 4 * (t.lane >> 5)];
   constexpr int kFragRing = frag_ring(kFragAhead);
-  Scl scl;
   half2_t sgb[4];
-  sm.sa[it & 3][t.w * 32 + (t.lane & 31)] = a.S;  // read back by this wave only
+  const float sa = a.S;  // S_A of this lane's row (both lane halves load the same row)
+  float sbp = 0.0f;
   static_for<32>([&](auto qc) __attribute__((always_inline)) {
     constexpr int q = decltype(qc)::value;
     constexpr int tn = q / 8, ks = q % 8;
@@ -400,24 +415,22 @@ __device__ __forceinline__ void chunk(Smem& sm, const Ctx& t, int it, bool aseg1
     constexpr int qf = q + kFragAhead;  // fragment read in this slot
     if constexpr (qf < 32) bf[qf % kFragRing] = ld8(bb + (qf / 8) * 32 * LDS_STRIDE + (qf % 8) * 8);
     else bf[qf % kFragRing] = ld8(bn + (qf - 32) * 8);
+    // S_B of the column pair's two blocks: lanes 0-31 block 2p, lanes 32-63 block 2p + 1
+    if constexpr (q == 4 || q == 20) sbp = sm.sb[it & 3][(q == 4 ? 0 : 64) + t.lane];
+    // outer-scale products S_A[row] * S_B[col] of blocks 0-1 (slot 8) and 2-3 (slot 24) in the
+    // accumulator layout: the 2-block fp32 outer product (block b in elements 16b..16b+15)
+    if constexpr (q == 8 || q == 24) smat = __builtin_amdgcn_mfma_f32_32x32x1f32(sa, sbp, float32v_t{}, 0, 0, 0);
     part[tn & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks], bf[q % kFragRing], ks == 0 ? float16v_t{} : part[tn & 1],
                                                           0, 0, 0);
-    {
-      // the previous block's elements are promoted over steps 2-7 (its last MFMA has completed)
+    if constexpr (ks >= 2) {
+      // elements [lo, hi) of the previous block at K-step ks (2..7): 3,3,3,3,2,2 (its last MFMA
+      // has completed; block 3 of the previous chunk during block 0)
       constexpr int pb = tn > 0 ? tn - 1 : 3;
-      if constexpr (ks == 0) scl.rb = sm.sb[tn > 0 ? it & 3 : (it - 1) & 3][pb * 32 + (t.lane & 31)];
-      if constexpr (tn <= 1 && ks <= 1) {
-        const float* src = sa_row + (tn == 0 ? (it - 1) & 3 : it & 3) * BM;
-        scl.ra[2 * ks] = *reinterpret_cast<const float4*>(src + 16 * ks);
-        scl.ra[2 * ks + 1] = *reinterpret_cast<const float4*>(src + 16 * ks + 8);
-      }
-      if constexpr (ks >= 2) {
-        // elements [lo, hi) of the previous block at K-step ks (2..7): 3,3,3,3,2,2
-        constexpr int lo = ks <= 6 ? 3 * (ks - 2) : 14, hi = ks < 6 ? lo + 3 : lo + 2;
-        static_for<hi - lo>([&](auto i) __attribute__((always_inline)) {
-          promote_elem<lo + decltype(i)::value>(scl, part[pb & 1], acc[pb]);
-        });
-      }
+      constexpr int lo = ks <= 6 ? 3 * (ks - 2) : 14, hi = ks < 6 ? lo + 3 : lo + 2;
+      static_for<hi - lo>([&](auto i) __attribute__((always_inline)) {
+        constexpr int e = lo + decltype(i)::value;
+        acc[pb][e] = fmaf(part[pb & 1][e], smat[16 * (pb & 1) + e], acc[pb][e]);
+      });
     }
     if constexpr (q == 1) FM::prep_b(nb, sgb);
     if constexpr (q == 9 || q == 15 || q == 20 || q == 25) {
@@ -481,7 +494,8 @@ __device__ __forceinline__ int lower_bound(const int32_t* a, int n, int v) {
 
 template <int FA0, int FB0, int FA1, int FB1, bool MIXB>
 __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+  __shared__ __attribute__((aligned(16))) SmemAll smem;
+  Smem& sm = smem.loop;
 
   // XCD-aware numbering: workgroup id w runs on XCD w % 8; give each XCD a
   // contiguous range of (tile, split) indices, tiles N-fastest.
@@ -543,9 +557,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     half2_t sga[4];
     float16v_t part[2];
     part[1] = float16v_t{};
-    // ring slot 3 stands for "chunk -1": zero scales for the first chunk's promotion of part[1]
-    sm.sb[3][threadIdx.x >> 2] = 0.0f;
-    sm.sa[3][t.w * 32 + (t.lane & 31)] = 0.0f;
+    float32v_t smat = float32v_t{};  // "chunk -1": the first chunk's promotion of part[1] adds 0 * 0
     F::fetch_b(p, t, 0, s1, b1);
     if constexpr (MIXB) {
       half2_t sg[4];
@@ -588,7 +600,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
         F::fetch_b(p, t, it + 3, s1, nb);
         barrier_lds();  // chunk it+1's B staged; this chunk's stage may be refilled
       };
-      chunk<FM, kFragAhead>(sm, t, it, false, t.b8, af, sga, bf, acc, part, a, nb, fa, sync);
+      chunk<FM, kFragAhead>(sm, t, it, false, t.b8, af, sga, bf, acc, part, smat, a, nb, fa, sync);
     };
     int it = 0;
     for (; it + 1 < s1; it += 2) {
@@ -596,10 +608,9 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
       run(it + 1, b2);
     }
     if (it < s1) run(it, b1);
-    Scl scl;
-    read_scl(sm, t, (s1 - 1) & 3, 3, scl);
     static_for<16>([&](auto e) __attribute__((always_inline)) {
-      promote_elem<decltype(e)::value>(scl, part[1], acc[3]);
+      constexpr int i = decltype(e)::value;
+      acc[3][i] = fmaf(part[1][i], smat[16 + i], acc[3][i]);
     });
   }
   if constexpr (FA1 != F_NONE) {
@@ -610,6 +621,63 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
   // 32 rows, column tn*32 + (lane & 31) of block tn (staged LDS row; for
   // outlier-column products mapped back to the original column).
   const int lane = t.lane;
+  // Tiles whose 128 columns are contiguous and 16-byte aligned in the output go
+  // through LDS and leave as 16-byte row pieces (8 bf16 or 4 fp32 per store)
+  // instead of one 2- or 4-byte store per element.
+  if constexpr (!MIXB) {
+    const bool to_partial = p.partial != nullptr;
+    const int64_t ld = to_partial ? p.J : p.ldc;
+    const bool bf = !to_partial && p.c_bf16;
+    const uintptr_t base_addr = to_partial ? (uintptr_t)p.partial : (uintptr_t)p.C;
+    if (n0 + BN <= p.J && (to_partial || !p.col_map) && (ld & (bf ? 7 : 3)) == 0 && (base_addr & 15) == 0) {
+      barrier_lds();  // every wave is done with the last chunk's B stage
+      float(&st)[32][OUT_STRIDE] = smem.out[t.w];
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st[8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][tn * 32 + (lane & 31)] = acc[tn][e];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's writes are visible to its lanes
+      __builtin_amdgcn_wave_barrier();
+      const int64_t row0 = m0 + t.w * 32;
+      if (bf) {
+        // lane: 8 columns of one of four rows per pass
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int row = 4 * r + (lane >> 4), c0 = (lane & 15) * 8;
+          const float4 u = *reinterpret_cast<const float4*>(&st[row][c0]);
+          const float4 v = *reinterpret_cast<const float4*>(&st[row][c0 + 4]);
+          uint4 o;
+          o.x = f32_to_bf16(u.x) | (f32_to_bf16(u.y) << 16);
+          o.y = f32_to_bf16(u.z) | (f32_to_bf16(u.w) << 16);
+          o.z = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
+          o.w = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
+          if (row0 + row < p.I)
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + (row0 + row) * ld + n0 + c0) = o;
+        }
+      } else {
+        float* base = to_partial ? p.partial + (int64_t)z * p.I * p.J : reinterpret_cast<float*>(p.C);
+        const bool add = !to_partial && p.accumulate;
+        // lane: 4 columns of one of two rows per pass
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 2 * r + (lane >> 5), c0 = (lane & 31) * 4;
+          float4 v = *reinterpret_cast<const float4*>(&st[row][c0]);
+          if (row0 + row < p.I) {
+            float4* dst = reinterpret_cast<float4*>(base + (row0 + row) * ld + n0 + c0);
+            if (add) {
+              const float4 o = *dst;
+              v.x = o.x + v.x;
+              v.y = o.y + v.y;
+              v.z = o.z + v.z;
+              v.w = o.w + v.w;
+            }
+            *dst = v;
+          }
+        }
+      }
+      return;
+    }
+  }
   const int64_t rw = m0 + t.w * 32 + 4 * (lane >> 5);
   const bool full_rows = m0 + BM <= p.I;
   int64_t ocol[4];

@@ -84,6 +84,36 @@ def test_gemm_heterogeneous_scales():
     assert H.rel_fro(c, ogemm.gemm_nt_f64(ra, rb)) < 1e-5
 
 
+@pytest.mark.parametrize("I,J,ld,off", [(200, 300, 300, 0), (200, 256, 264, 8), (136, 256, 260, 2),
+                                         (136, 256, 256, 1), (96, 128, 136, 4)])
+def test_gemm_output_views(I, J, ld, off):
+    """Outputs written into views of a wider buffer: ragged rows and columns, and leading dimensions and
+    offsets that do (whole 16-byte row pieces) and do not (element stores) keep rows 16-byte aligned.
+    Nothing outside the view changes; accumulation adds to what the view held."""
+    ga, gb, ra, rb = _operands(I, J, 384, seed=I + J + ld + off)
+    ref = ogemm.gemm_nt_f64(ra, rb)
+    for dt in (torch.float32, torch.bfloat16):
+        buf = torch.full((I * ld + off + 64,), 3.0, dtype=dt, device="cuda")
+        out = buf[off:off + I * ld].view(I, ld)[:, :J]
+        tj2.gemm(ga, gb, out=out, split_k=False)
+        got = out.float().cpu().numpy()
+        if dt == torch.float32:
+            assert H.rel_fro(got, ref) < 1e-5
+        else:
+            assert H.bf16_ulp_ok(out, ref)
+        rest = buf.float().cpu().numpy().copy()
+        rest[off:off + I * ld].reshape(I, ld)[:, :J] = 3.0
+        assert np.all(rest == 3.0), "write outside the output view"
+    base = np.random.default_rng(off).standard_normal((I, ld)).astype(np.float32)
+    buf = torch.zeros(I * ld + off + 64, dtype=torch.float32, device="cuda")
+    view = buf[off:off + I * ld].view(I, ld)
+    view.copy_(torch.from_numpy(base).cuda())
+    tj2.gemm(ga, gb, out=view[:, :J], accumulate=True, split_k=False)
+    got = view.cpu().numpy()
+    assert H.rel_fro(got[:, :J] - base[:, :J], ref) < 1e-5
+    np.testing.assert_array_equal(got[:, J:], base[:, J:])
+
+
 @pytest.mark.parametrize("I,J,K", [(256, 128, 8192), (200, 112, 4096), (16384 // 8, 112, 3072)])
 def test_gemm_split_k(I, J, K):
     """Few output tiles and a long reduction: K is split over workgroups, partials reduced in order."""
