@@ -621,21 +621,44 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
   // 32 rows, column tn*32 + (lane & 31) of block tn (staged LDS row; for
   // outlier-column products mapped back to the original column).
   const int lane = t.lane;
+  const int64_t rw = m0 + t.w * 32 + 4 * (lane >> 5);
+  const bool full_rows = m0 + BM <= p.I;
+  int64_t ocol[4];
+  bool ok[4];
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
+    const int rho = tn * 32 + (lane & 31);
+    if constexpr (MIXB) {
+      ok[tn] = rho < ncols;
+      ocol[tn] = !ok[tn] ? 0 : rho < c1 ? (int64_t)p.rest[r0 + rho] : (int64_t)p.outl[lo + rho - c1];
+    } else {
+      ocol[tn] = n0 + rho;
+      ok[tn] = ocol[tn] < p.J;
+    }
+  }
   // Tiles whose 128 columns are contiguous and 16-byte aligned in the output go
   // through LDS and leave as 16-byte row pieces (8 bf16 or 4 fp32 per store)
-  // instead of one 2- or 4-byte store per element.
-  if constexpr (!MIXB) {
+  // instead of one 2- or 4-byte store per element.  An outlier-column tile's
+  // columns are the full range [n0, n0 + 128) in another order (its non-outlier
+  // columns and its outlier columns, both ascending), so its results are
+  // placed in output order on the way into LDS.
+  {
     const bool to_partial = p.partial != nullptr;
     const int64_t ld = to_partial ? p.J : p.ldc;
     const bool bf = !to_partial && p.c_bf16;
     const uintptr_t base_addr = to_partial ? (uintptr_t)p.partial : (uintptr_t)p.C;
-    if (n0 + BN <= p.J && (to_partial || !p.col_map) && (ld & (bf ? 7 : 3)) == 0 && (base_addr & 15) == 0) {
+    if (n0 + BN <= p.J && (MIXB || to_partial || !p.col_map) && (ld & (bf ? 7 : 3)) == 0 &&
+        (base_addr & 15) == 0) {
       barrier_lds();  // every wave is done with the last chunk's B stage
       float(&st)[32][OUT_STRIDE] = smem.out[t.w];
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn)
+      for (int tn = 0; tn < 4; ++tn) {
+        // output column within the tile (clamped: a plan that breaks its contract cannot
+        // move a write outside the wave's staging rows)
+        const int lc = MIXB ? min(max((int)(ocol[tn] - n0), 0), BN - 1) : tn * 32 + (lane & 31);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) st[8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][tn * 32 + (lane & 31)] = acc[tn][e];
+        for (int e = 0; e < 16; ++e) st[8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][lc] = acc[tn][e];
+      }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's writes are visible to its lanes
       __builtin_amdgcn_wave_barrier();
       const int64_t row0 = m0 + t.w * 32;
@@ -676,21 +699,6 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
         }
       }
       return;
-    }
-  }
-  const int64_t rw = m0 + t.w * 32 + 4 * (lane >> 5);
-  const bool full_rows = m0 + BM <= p.I;
-  int64_t ocol[4];
-  bool ok[4];
-#pragma unroll
-  for (int tn = 0; tn < 4; ++tn) {
-    const int rho = tn * 32 + (lane & 31);
-    if constexpr (MIXB) {
-      ok[tn] = rho < ncols;
-      ocol[tn] = !ok[tn] ? 0 : rho < c1 ? (int64_t)p.rest[r0 + rho] : (int64_t)p.outl[lo + rho - c1];
-    } else {
-      ocol[tn] = n0 + rho;
-      ok[tn] = ocol[tn] < p.J;
     }
   }
   if (p.partial) {
