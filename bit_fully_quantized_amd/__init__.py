@@ -18,7 +18,7 @@ from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI
                    SR, Tj2Error, check, lib)
 
 __all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "gemm_workspace", "linear_fwd", "linear_bwd", "linear_bwd_workspace",
-           "osci_reset_step", "master_update_step", "channel_sumsq", "mfma_peak_probe", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
+           "osci_reset_step", "osci_reset_step_multi", "OsciBatch", "master_update_step", "channel_sumsq", "mfma_peak_probe", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
            "GROUP_ROW", "GROUP_COL", "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END", "RISK_BINS"]
 
 
@@ -256,6 +256,36 @@ def osci_reset_step(W, W_prev, Q_prev, dQ, dM, *, mode: int, tau: float = 4.0, r
                                ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count),
                                _diag(flips, risk_hist), _stream())
     check("osci_reset_step", st)
+
+
+class OsciBatch:
+    """Descriptors of several OsciReset problems, built once: [(W, W_prev, Q_prev, dQ, dM, Wq_out or None), ...]
+    (the tensors must stay alive and in place while the batch is used)."""
+
+    def __init__(self, tensors):
+        self.tensors = list(tensors)
+        self._wq = []  # codes descriptors the array points to
+        self.arr = (_lib.OsciTensorC * len(self.tensors))()
+        for i, (W, W_prev, Q_prev, dQ, dM, wq) in enumerate(self.tensors):
+            N, K = W.shape
+            wqc = wq.c() if wq is not None else None
+            self._wq.append(wqc)
+            self.arr[i] = _lib.OsciTensorC(_ptr(W), _ptr(W_prev), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K,
+                                           ctypes.pointer(wqc) if wqc is not None else None)
+
+    def __len__(self):
+        return len(self.tensors)
+
+
+def osci_reset_step_multi(tensors, *, mode: int, tau: float = 4.0, reset_enabled: bool = False,
+                          reset_count: torch.Tensor | None = None, flips: torch.Tensor | None = None,
+                          risk_hist: torch.Tensor | None = None) -> None:
+    """osci_reset_step on several matrices at once (an OsciBatch, or the list it takes); the counters
+    accumulate over all of them."""
+    batch = tensors if isinstance(tensors, OsciBatch) else OsciBatch(tensors)
+    st = lib().osci_reset_step_multi(batch.arr, len(batch), mode, ctypes.c_float(tau), 1 if reset_enabled else 0,
+                                     _ptr(reset_count), _diag(flips, risk_hist), _stream())
+    check("osci_reset_step_multi", st)
 
 
 def master_update_step(W, m, v, grad, Q_prev, dQ, dM, *, lr: float, bias_correction1: float,

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <string>
+#include <vector>
 
 #include "tj2_internal.h"
 
@@ -518,9 +519,14 @@ tj2_status master_update_step(float* W, float* m, float* v, const float* grad, f
   return ok();
 }
 
-tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N, int64_t K,
-                           int32_t mode, float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
-                           const tj2_osci_diag* diag, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checked launch parameters of one OsciReset problem (osci_reset_step's argument rules).
+tj2_status osci_params(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N, int64_t K,
+                       int32_t mode, float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
+                       const tj2_osci_diag* diag, OsciParams* out) {
   if (!W || !W_prev || !Q_prev || !dQ || !dM) return fail(TJ2_ERR_ARG, "W and the state arrays are required");
   if (!aligned16(W) || !aligned16(W_prev) || !aligned16(Q_prev) || !aligned16(dQ) || !aligned16(dM))
     return fail(TJ2_ERR_ALIGN, "arrays must be 16-byte aligned");
@@ -530,7 +536,7 @@ tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, fl
   if (!(tau >= 0.0f)) return fail(TJ2_ERR_ARG, "tau must be >= 0");
   const int64_t nb = (K + 127) / 128;
   if (N * nb * 16 >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
-  OsciParams p;
+  OsciParams& p = *out;
   memset(&p, 0, sizeof(p));
   p.W = W; p.W_prev = W_prev; p.Q_prev = Q_prev; p.dQ = dQ; p.dM = dM;
   p.N = N; p.K = K; p.mode = mode; p.tau = tau; p.reset_enabled = reset_enabled ? 1 : 0;
@@ -541,7 +547,37 @@ tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, fl
   }
   p.reset_count = reinterpret_cast<unsigned long long*>(reset_count);
   TJ2_TRY(diag_pointers(diag, &p.flips, &p.risk_hist));
+  return TJ2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N, int64_t K,
+                           int32_t mode, float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
+                           const tj2_osci_diag* diag, void* stream) {
+  OsciParams p;
+  TJ2_TRY(osci_params(W, W_prev, Q_prev, dQ, dM, N, K, mode, tau, reset_enabled, Wq_out, reset_count, diag, &p));
   TJ2_TRY(hip_check(launch_osci(p, (hipStream_t)stream), "osci launch"));
+  return ok();
+}
+
+tj2_status osci_reset_step_multi(const tj2_osci_tensor* tensors, int32_t n, int32_t mode, float tau,
+                                 int32_t reset_enabled, uint64_t* reset_count, const tj2_osci_diag* diag,
+                                 void* stream) {
+  if (!tensors || n < 1) return fail(TJ2_ERR_ARG, "tensors must list at least one matrix");
+  std::vector<OsciParams> ps((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const tj2_osci_tensor& x = tensors[i];
+    const tj2_status st = osci_params(x.W, x.W_prev, x.Q_prev, x.dQ, x.dM, x.N, x.K, mode, tau, reset_enabled,
+                                      x.Wq_out, reset_count, diag, &ps[(size_t)i]);
+    if (st != TJ2_OK) return fail(st, "tensors[%d]: %s", i, std::string(tj2_last_error()).c_str());
+  }
+  for (int32_t i = 0; i < n; i += kOsciMultiMax) {
+    const int m = n - i < kOsciMultiMax ? n - i : kOsciMultiMax;
+    TJ2_TRY(hip_check(launch_osci_multi(ps.data() + i, m, (hipStream_t)stream), "osci launch"));
+  }
   return ok();
 }
 

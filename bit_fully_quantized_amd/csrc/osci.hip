@@ -19,6 +19,8 @@
 // counters with one atomic per workgroup and counter.
 //
 // Calibration (section 2.C): per-channel sum of squares of the activations.
+#include <cstring>
+
 #include "tj2_device.h"
 #include "tj2_internal.h"
 
@@ -141,9 +143,7 @@ __device__ __forceinline__ void add_diag(DiagSmem& sm, unsigned long long* flips
 // before the quantization work.  Lanes past the last row stay (no early exit,
 // the diagnostics use workgroup barriers) but touch no memory.
 template <bool DIAG>
-__global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_per_row) {
-  __shared__ DiagSmem dsm;
-  const uint32_t g = blockIdx.x * 256u + threadIdx.x;
+__device__ __forceinline__ void osci_body(const OsciParams& p, int32_t halves_per_row, uint32_t g, DiagSmem& dsm) {
   const uint32_t row = g / (uint32_t)halves_per_row;
   const bool live = row < (uint32_t)p.N;  // whole outer blocks are live or not
   const uint32_t jh = g - row * (uint32_t)halves_per_row;
@@ -231,6 +231,30 @@ __global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_
   }
   if (p.reset_count && n_reset) atomicAdd(p.reset_count, (unsigned long long)n_reset);
   if constexpr (DIAG) add_diag(dsm, p.flips, want_bins ? p.risk_hist : nullptr, n_flip, want_bins && valid, bins);
+}
+
+template <bool DIAG>
+__global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_per_row) {
+  __shared__ DiagSmem dsm;
+  osci_body<DIAG>(p, halves_per_row, blockIdx.x * 256u + threadIdx.x, dsm);
+}
+
+// Several problems per launch (a model's weight matrices after one optimizer
+// step), so that small matrices do not each pay a launch.
+struct OsciMulti {
+  OsciParams p[kOsciMultiMax];
+  uint32_t begin[kOsciMultiMax + 1];
+  int32_t hpr[kOsciMultiMax];
+  int n;
+};
+static_assert(sizeof(OsciMulti) <= 4096, "kernel arguments stay within 4 KB");
+
+template <bool DIAG>
+__global__ __launch_bounds__(256) void osci_multi_kernel(OsciMulti m) {
+  __shared__ DiagSmem dsm;
+  int i = 0;
+  while (i + 1 < m.n && blockIdx.x >= m.begin[i + 1]) ++i;  // uniform per workgroup
+  osci_body<DIAG>(m.p[i], m.hpr[i], (blockIdx.x - m.begin[i]) * 256u + threadIdx.x, dsm);
 }
 
 // Fused master-weight pass (one read of the masters, their AdamW moments and the
@@ -388,6 +412,30 @@ hipError_t launch_osci(const OsciParams& p, hipStream_t s) {
     hipLaunchKernelGGL(osci_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
   else
     hipLaunchKernelGGL(osci_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_osci_multi(const OsciParams* ps, int n, hipStream_t s) {
+  if (n < 1 || n > kOsciMultiMax) return hipErrorInvalidValue;
+  OsciMulti m;
+  memset(&m, 0, sizeof(m));
+  m.n = n;
+  int64_t total = 0;
+  bool diag = false;
+  for (int i = 0; i < n; ++i) {
+    m.p[i] = ps[i];
+    const int64_t hpr = (ps[i].K + 127) / 128 * 16;  // half groups per row
+    m.hpr[i] = (int32_t)hpr;
+    m.begin[i] = (uint32_t)total;
+    total += (ps[i].N * hpr + 255) / 256;
+    diag = diag || ps[i].flips || ps[i].risk_hist;
+  }
+  if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  m.begin[n] = (uint32_t)total;
+  if (diag)
+    hipLaunchKernelGGL(osci_multi_kernel<true>, dim3((uint32_t)total), dim3(256), 0, s, m);
+  else
+    hipLaunchKernelGGL(osci_multi_kernel<false>, dim3((uint32_t)total), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 

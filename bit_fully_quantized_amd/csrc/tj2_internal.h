@@ -118,6 +118,11 @@ constexpr int kRiskBins = 32;
 
 hipError_t launch_osci(const OsciParams& p, hipStream_t s);
 
+// Several OsciReset problems (same mode, tau, switches and counters) in one
+// launch: workgroups [begin[i], begin[i+1]) take problem i.
+constexpr int kOsciMultiMax = 16;
+hipError_t launch_osci_multi(const OsciParams* ps, int n, hipStream_t s);
+
 // Fused master-weight pass: AdamW on the masters, then OsciReset (ACCUM or
 // WINDOW_END) with the pre-update master as W_prev, then the forward codes.
 struct MasterParams {

@@ -281,6 +281,34 @@ tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, fl
                            void* stream);
 
 /*
+ * One OsciReset problem of osci_reset_step_multi: W [N, K], its state arrays
+ * (all fp32 [N, K], caller-owned device memory) and optional codes Wq_out.
+ */
+typedef struct {
+  float* W;
+  float* W_prev;
+  float* Q_prev;
+  float* dQ;
+  float* dM;
+  int64_t N;
+  int64_t K;
+  tj2_qtensor* Wq_out; /* host descriptor, may be NULL */
+} tj2_osci_tensor;
+
+/*
+ * osci_reset_step (section 2.B) on n independent weight matrices with one mode,
+ * tau, reset switch and set of counters, in as few launches as possible (up to
+ * 16 matrices per launch) instead of one per matrix: the step that follows an
+ * optimizer update of a whole model.  Results equal n osci_reset_step calls.
+ * `tensors` is a host array of n (>= 1) descriptors, read during the call;
+ * every member is checked as in osci_reset_step before anything is enqueued.
+ * reset_count and diag accumulate over all matrices.
+ */
+tj2_status osci_reset_step_multi(const tj2_osci_tensor* tensors, int32_t n, int32_t mode, float tau,
+                                 int32_t reset_enabled, uint64_t* reset_count, const tj2_osci_diag* diag,
+                                 void* stream);
+
+/*
  * AdamW hyper-parameters of one optimizer step on the fp32 masters (the pages
  * train with fp32 masters but do not name the optimizer; AdamW with decoupled
  * weight decay is this library's choice).  bias_correction1 = 1 - beta1^t and

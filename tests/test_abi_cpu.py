@@ -31,7 +31,7 @@ def L():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_outlier_cols", "nvfp4_linear_fwd", "nvfp4_linear_bwd", "osci_reset_step",
-              "master_update_step", "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes"]:
+              "osci_reset_step_multi", "master_update_step", "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes"]:
         assert n in names
 
 
@@ -131,6 +131,23 @@ def test_osci_argument_errors(L):
     assert L.osci_reset_step(*p, 16, 128, 1, ctypes.c_float(-1.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
     assert L.osci_reset_step(None, *p[1:], 16, 128, 1, ctypes.c_float(4.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
     assert L.tj2_channel_sumsq(0x1000, 64, 100, 0x2000, None) == _lib.TJ2_ERR_SHAPE
+
+
+def test_osci_multi_argument_errors(L):
+    from bit_fully_quantized_amd import _lib
+    def tensor(i, N=16, K=128, align=0):
+        return _lib.OsciTensorC(*[0x1000 * (5 * i + j + 1) + align for j in range(5)], N, K, None)
+    good = [tensor(i) for i in range(3)]
+    arr = (_lib.OsciTensorC * 3)(*good)
+    assert L.osci_reset_step_multi(None, 3, 1, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step_multi(arr, 0, 1, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step_multi(arr, 3, 7, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step_multi(arr, 3, 1, ctypes.c_float(-1.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    # one bad member (K not a multiple of 16, a misaligned array) rejects the whole call, named by index
+    for bad, code in ((tensor(1, K=100), _lib.TJ2_ERR_SHAPE), (tensor(1, align=4), _lib.TJ2_ERR_ALIGN)):
+        arr = (_lib.OsciTensorC * 3)(good[0], bad, good[2])
+        assert L.osci_reset_step_multi(arr, 3, 1, ctypes.c_float(4.0), 1, None, None, None) == code
+        assert b"tensors[1]" in L.tj2_last_error()
 
 
 def test_master_update_argument_errors(L):
