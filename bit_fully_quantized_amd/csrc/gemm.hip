@@ -467,12 +467,20 @@ __device__ __forceinline__ void tail_chunk(const GemmKArgs& p, Smem& sm, const C
   const _Float16* bb = sm.b[0] + (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
   Scl scl;
   read_scl(sm, t, 0, 0, scl);
+  // B fragments are read one block ahead of their MFMAs
+  half8_t bfr[2][BK / 16];
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) bfr[0][ks] = ld8(bb + ks * 8);
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn) {
+    if (tn < 3) {
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) bfr[(tn + 1) & 1][ks] = ld8(bb + (tn + 1) * 32 * LDS_STRIDE + ks * 8);
+    }
     float16v_t part = float16v_t{};
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks)
-      part = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks], ld8(bb + tn * 32 * LDS_STRIDE + ks * 8), part, 0, 0, 0);
+      part = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks], bfr[tn & 1][ks], part, 0, 0, 0);
     scl.rb = sm.sb[0][tn * 32 + (t.lane & 31)];
     static_for<16>([&](auto e) __attribute__((always_inline)) {
       promote_elem<decltype(e)::value>(scl, part, acc[tn]);
