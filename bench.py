@@ -377,9 +377,10 @@ def main():
     log("fused master-weight pass")
     for li in lins:
         li.m, li.v = torch.zeros_like(li.W), torch.zeros_like(li.W)
-    master_t = time_launches(lambda: [tj2.master_update_step(li.W, li.m, li.v, li.dW, *li.state[1:], lr=1e-6,
-                                                             bias_correction1=0.1, bias_correction2=0.05,
-                                                             mode=tj2.OSCI_ACCUM, tau=4.0) for li in lins], 3)
+    master_batch = tj2.MasterBatch([(li.W, li.m, li.v, li.dW, *li.state[1:], None) for li in lins])
+    master_t = time_launches(lambda: tj2.master_update_step_multi(master_batch, lr=1e-6, bias_correction1=0.1,
+                                                                  bias_correction2=0.05, mode=tj2.OSCI_ACCUM,
+                                                                  tau=4.0), 3)
     # read W, m, v, grad, Q_prev, dQ, dM; write W, m, v, Q_prev, dQ, dM (fp32)
     master_bytes = n_params * 52.0
     log("oscillation diagnostics")
@@ -387,9 +388,8 @@ def main():
     hist = torch.zeros(tj2.RISK_BINS, dtype=torch.int64, device="cuda")
 
     def master_diag(mode, h):
-        for li in lins:
-            tj2.master_update_step(li.W, li.m, li.v, li.dW, *li.state[1:], lr=1e-6, bias_correction1=0.1,
-                                   bias_correction2=0.05, mode=mode, tau=4.0, flips=flips, risk_hist=h)
+        tj2.master_update_step_multi(master_batch, lr=1e-6, bias_correction1=0.1, bias_correction2=0.05, mode=mode,
+                                     tau=4.0, flips=flips, risk_hist=h)
 
     diag_accum_t = time_launches(lambda: master_diag(tj2.OSCI_ACCUM, None), 3)
     flips.zero_()
@@ -454,7 +454,8 @@ def main():
                        "GB_s": round(osci_bytes / osci_t / 1e9, 1),
                        "frac_hbm": round(osci_bytes / osci_t / 1e9 / HBM_PEAK_GBS, 3),
                        "ms_per_step": round(osci_t * 1e3, 3), "params": n_params},
-        "master_update": {"what": "fused AdamW + OsciReset accumulate over all masters (52 B/param)",
+        "master_update": {"what": "fused AdamW + OsciReset accumulate over all masters through "
+                                  "master_update_step_multi (16 weight matrices per launch; 52 B/param)",
                           "GB_s": round(master_bytes / master_t / 1e9, 1),
                           "frac_hbm": round(master_bytes / master_t / 1e9 / HBM_PEAK_GBS, 3),
                           "ms_per_step": round(master_t * 1e3, 3), "params": n_params},

@@ -18,7 +18,7 @@ from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI
                    SR, Tj2Error, check, lib)
 
 __all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "gemm_workspace", "linear_fwd", "linear_bwd", "linear_bwd_workspace",
-           "osci_reset_step", "osci_reset_step_multi", "OsciBatch", "master_update_step", "channel_sumsq", "mfma_peak_probe", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
+           "osci_reset_step", "osci_reset_step_multi", "OsciBatch", "master_update_step", "master_update_step_multi", "MasterBatch", "channel_sumsq", "mfma_peak_probe", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
            "GROUP_ROW", "GROUP_COL", "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END", "RISK_BINS"]
 
 
@@ -305,6 +305,40 @@ def master_update_step(W, m, v, grad, Q_prev, dQ, dM, *, lr: float, bias_correct
                                   _diag(flips, risk_hist), _stream())
     check("master_update_step", st)
 
+
+
+class MasterBatch:
+    """Descriptors of several fused master-weight problems, built once:
+    [(W, m, v, grad, Q_prev, dQ, dM, Wq_out or None), ...] (the tensors must stay alive and in place)."""
+
+    def __init__(self, tensors):
+        self.tensors = list(tensors)
+        self._wq = []
+        self.arr = (_lib.MasterTensorC * len(self.tensors))()
+        for i, (W, m, v, g, Q_prev, dQ, dM, wq) in enumerate(self.tensors):
+            N, K = W.shape
+            wqc = wq.c() if wq is not None else None
+            self._wq.append(wqc)
+            self.arr[i] = _lib.MasterTensorC(_ptr(W), _ptr(m), _ptr(v), _ptr(g), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K,
+                                             ctypes.pointer(wqc) if wqc is not None else None)
+
+    def __len__(self):
+        return len(self.tensors)
+
+
+def master_update_step_multi(tensors, *, lr: float, bias_correction1: float, bias_correction2: float,
+                             beta1: float = 0.9, beta2: float = 0.95, eps: float = 1e-8, weight_decay: float = 0.1,
+                             mode: int = OSCI_ACCUM, tau: float = 4.0, reset_enabled: bool = False,
+                             reset_count: torch.Tensor | None = None, flips: torch.Tensor | None = None,
+                             risk_hist: torch.Tensor | None = None) -> None:
+    """master_update_step on several matrices at once (a MasterBatch, or the list it takes); the counters
+    accumulate over all of them."""
+    batch = tensors if isinstance(tensors, MasterBatch) else MasterBatch(tensors)
+    ap = _lib.AdamWC(lr, beta1, beta2, eps, weight_decay, bias_correction1, bias_correction2)
+    st = lib().master_update_step_multi(batch.arr, len(batch), ctypes.byref(ap), mode, ctypes.c_float(tau),
+                                        1 if reset_enabled else 0, _ptr(reset_count), _diag(flips, risk_hist),
+                                        _stream())
+    check("master_update_step_multi", st)
 
 def mfma_peak_probe(out: torch.Tensor, iters: int) -> float:
     """Measurement helper (not part of the path): an MFMA-only loop in out.numel() // 256

@@ -72,6 +72,11 @@ RISK_BINS = 32
 class OsciTensorC(ctypes.Structure):
     _fields_ = [("W", P), ("W_prev", P), ("Q_prev", P), ("dQ", P), ("dM", P), ("N", I64), ("K", I64), ("Wq_out", QP)]
 
+
+class MasterTensorC(ctypes.Structure):
+    _fields_ = [("W", P), ("m", P), ("v", P), ("grad", P), ("Q_prev", P), ("dQ", P), ("dM", P), ("N", I64), ("K", I64),
+                ("Wq_out", QP)]
+
 SIGNATURES = {
     "tj2_last_error": (ctypes.c_char_p, []),
     "tj2_version": (ctypes.c_char_p, []),
@@ -89,6 +94,8 @@ SIGNATURES = {
                               P]),
     "osci_reset_step_multi": (I32, [ctypes.POINTER(OsciTensorC), I32, I32, ctypes.c_float, I32, P,
                                     ctypes.POINTER(OsciDiagC), P]),
+    "master_update_step_multi": (I32, [ctypes.POINTER(MasterTensorC), I32, ctypes.POINTER(AdamWC), I32,
+                                       ctypes.c_float, I32, P, ctypes.POINTER(OsciDiagC), P]),
     "master_update_step": (I32, [P, P, P, P, P, P, P, I64, I64, ctypes.POINTER(AdamWC), I32, ctypes.c_float, I32,
                                  QP, P, ctypes.POINTER(OsciDiagC), P]),
     "tj2_channel_sumsq": (I32, [P, I64, I64, P, P]),

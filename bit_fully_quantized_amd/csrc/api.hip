@@ -484,10 +484,15 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
   return ok();
 }
 
-tj2_status master_update_step(float* W, float* m, float* v, const float* grad, float* Q_prev, float* dQ, float* dM,
-                              int64_t N, int64_t K, const tj2_adamw_params* adam, int32_t mode, float tau,
-                              int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
-                              const tj2_osci_diag* diag, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checked launch parameters of one fused master-weight problem (master_update_step's argument rules).
+tj2_status master_params(float* W, float* m, float* v, const float* grad, float* Q_prev, float* dQ, float* dM,
+                         int64_t N, int64_t K, const tj2_adamw_params* adam, int32_t mode, float tau,
+                         int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
+                         const tj2_osci_diag* diag, MasterParams* out) {
   if (!W || !m || !v || !grad || !Q_prev || !dQ || !dM) return fail(TJ2_ERR_ARG, "W, m, v, grad and the state arrays are required");
   if (!adam) return fail(TJ2_ERR_ARG, "adam parameters are required");
   if (!aligned16(W) || !aligned16(m) || !aligned16(v) || !aligned16(grad) || !aligned16(Q_prev) || !aligned16(dQ) ||
@@ -499,7 +504,7 @@ tj2_status master_update_step(float* W, float* m, float* v, const float* grad, f
   if (!(tau >= 0.0f)) return fail(TJ2_ERR_ARG, "tau must be >= 0");
   const int64_t nb = (K + 127) / 128;
   if (N * nb * 16 >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
-  MasterParams p;
+  MasterParams& p = *out;
   memset(&p, 0, sizeof(p));
   p.W = W; p.m = m; p.v = v; p.grad = grad; p.Q_prev = Q_prev; p.dQ = dQ; p.dM = dM;
   p.N = N; p.K = K;
@@ -515,7 +520,40 @@ tj2_status master_update_step(float* W, float* m, float* v, const float* grad, f
   }
   p.reset_count = reinterpret_cast<unsigned long long*>(reset_count);
   TJ2_TRY(diag_pointers(diag, &p.flips, &p.risk_hist));
+  return TJ2_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+tj2_status master_update_step(float* W, float* m, float* v, const float* grad, float* Q_prev, float* dQ, float* dM,
+                              int64_t N, int64_t K, const tj2_adamw_params* adam, int32_t mode, float tau,
+                              int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
+                              const tj2_osci_diag* diag, void* stream) {
+  MasterParams p;
+  TJ2_TRY(master_params(W, m, v, grad, Q_prev, dQ, dM, N, K, adam, mode, tau, reset_enabled, Wq_out, reset_count,
+                        diag, &p));
   TJ2_TRY(hip_check(launch_master(p, (hipStream_t)stream), "master update launch"));
+  return ok();
+}
+
+tj2_status master_update_step_multi(const tj2_master_tensor* tensors, int32_t n, const tj2_adamw_params* adam,
+                                    int32_t mode, float tau, int32_t reset_enabled, uint64_t* reset_count,
+                                    const tj2_osci_diag* diag, void* stream) {
+  if (!tensors || n < 1) return fail(TJ2_ERR_ARG, "tensors must list at least one matrix");
+  std::vector<MasterParams> ps((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const tj2_master_tensor& x = tensors[i];
+    const tj2_status st = master_params(x.W, x.m, x.v, x.grad, x.Q_prev, x.dQ, x.dM, x.N, x.K, adam, mode, tau,
+                                        reset_enabled, x.Wq_out, reset_count, diag, &ps[(size_t)i]);
+    if (st != TJ2_OK) return fail(st, "tensors[%d]: %s", i, std::string(tj2_last_error()).c_str());
+  }
+  for (int32_t i = 0; i < n; i += kOsciMultiMax) {
+    const int cnt = n - i < kOsciMultiMax ? n - i : kOsciMultiMax;
+    TJ2_TRY(hip_check(launch_master_multi(ps.data() + i, cnt, (hipStream_t)stream), "master update launch"));
+  }
   return ok();
 }
 

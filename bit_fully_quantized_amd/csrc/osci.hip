@@ -265,9 +265,8 @@ __global__ __launch_bounds__(256) void osci_multi_kernel(OsciMulti m) {
 // W_prev (the distance the master travels is the update), then the forward
 // codes.  Lane layout as osci_kernel.
 template <bool DIAG>
-__global__ __launch_bounds__(256) void master_kernel(MasterParams p, int32_t halves_per_row) {
-  __shared__ DiagSmem dsm;
-  const uint32_t g = blockIdx.x * 256u + threadIdx.x;
+__device__ __forceinline__ void master_body(const MasterParams& p, int32_t halves_per_row, uint32_t g,
+                                            DiagSmem& dsm) {
   const uint32_t row = g / (uint32_t)halves_per_row;
   const bool live = row < (uint32_t)p.N;  // as osci_kernel: no early exit
   const uint32_t jh = g - row * (uint32_t)halves_per_row;
@@ -356,6 +355,29 @@ __global__ __launch_bounds__(256) void master_kernel(MasterParams p, int32_t hal
   if constexpr (DIAG) add_diag(dsm, p.flips, want_bins ? p.risk_hist : nullptr, n_flip, want_bins && valid, bins);
 }
 
+template <bool DIAG>
+__global__ __launch_bounds__(256) void master_kernel(MasterParams p, int32_t halves_per_row) {
+  __shared__ DiagSmem dsm;
+  master_body<DIAG>(p, halves_per_row, blockIdx.x * 256u + threadIdx.x, dsm);
+}
+
+// Several weight matrices per launch, as osci_multi_kernel.
+struct MasterMulti {
+  MasterParams p[kOsciMultiMax];
+  uint32_t begin[kOsciMultiMax + 1];
+  int32_t hpr[kOsciMultiMax];
+  int n;
+};
+static_assert(sizeof(MasterMulti) <= 4096, "kernel arguments stay within 4 KB");
+
+template <bool DIAG>
+__global__ __launch_bounds__(256) void master_multi_kernel(MasterMulti m) {
+  __shared__ DiagSmem dsm;
+  int i = 0;
+  while (i + 1 < m.n && blockIdx.x >= m.begin[i + 1]) ++i;  // uniform per workgroup
+  master_body<DIAG>(m.p[i], m.hpr[i], (blockIdx.x - m.begin[i]) * 256u + threadIdx.x, dsm);
+}
+
 // acc[k] += sum_m X[m, k]^2.  Thread: 8 columns x 64 rows; 8 row slices per block
 // are reduced in LDS, then one atomic per column per block.
 __global__ __launch_bounds__(256) void sumsq_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
@@ -401,6 +423,30 @@ hipError_t launch_master(const MasterParams& p, hipStream_t s) {
     hipLaunchKernelGGL(master_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
   else
     hipLaunchKernelGGL(master_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_master_multi(const MasterParams* ps, int n, hipStream_t s) {
+  if (n < 1 || n > kOsciMultiMax) return hipErrorInvalidValue;
+  MasterMulti m;
+  memset(&m, 0, sizeof(m));
+  m.n = n;
+  int64_t total = 0;
+  bool diag = false;
+  for (int i = 0; i < n; ++i) {
+    m.p[i] = ps[i];
+    const int64_t hpr = (ps[i].K + 127) / 128 * 16;  // half groups per row
+    m.hpr[i] = (int32_t)hpr;
+    m.begin[i] = (uint32_t)total;
+    total += (ps[i].N * hpr + 255) / 256;
+    diag = diag || ps[i].flips || ps[i].risk_hist;
+  }
+  if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  m.begin[n] = (uint32_t)total;
+  if (diag)
+    hipLaunchKernelGGL(master_multi_kernel<true>, dim3((uint32_t)total), dim3(256), 0, s, m);
+  else
+    hipLaunchKernelGGL(master_multi_kernel<false>, dim3((uint32_t)total), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 

@@ -142,6 +142,7 @@ struct MasterParams {
 };
 
 hipError_t launch_master(const MasterParams& p, hipStream_t s);
+hipError_t launch_master_multi(const MasterParams* ps, int n, hipStream_t s);  // up to kOsciMultiMax
 
 hipError_t launch_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, hipStream_t s);
 

@@ -342,6 +342,37 @@ tj2_status master_update_step(float* W, float* m, float* v, const float* grad, f
                               const tj2_osci_diag* diag, void* stream);
 
 /*
+ * One weight matrix of master_update_step_multi: the masters W [N, K], moments
+ * m, v, gradient grad and OsciReset state Q_prev, dQ, dM (all fp32 [N, K],
+ * caller-owned device memory) and optional codes Wq_out.
+ */
+typedef struct {
+  float* W;
+  float* m;
+  float* v;
+  const float* grad;
+  float* Q_prev;
+  float* dQ;
+  float* dM;
+  int64_t N;
+  int64_t K;
+  tj2_qtensor* Wq_out; /* host descriptor, may be NULL */
+} tj2_master_tensor;
+
+/*
+ * master_update_step on n weight matrices with one set of AdamW parameters,
+ * mode, tau, reset switch and counters, up to 16 matrices per launch (the
+ * optimizer step of a whole model).  Results equal n master_update_step calls.
+ * `tensors` is a host array of n (>= 1) descriptors, read during the call;
+ * every member is checked as in master_update_step before anything is
+ * enqueued (the error names the first bad index).  reset_count and diag
+ * accumulate over all matrices.
+ */
+tj2_status master_update_step_multi(const tj2_master_tensor* tensors, int32_t n, const tj2_adamw_params* adam,
+                                    int32_t mode, float tau, int32_t reset_enabled, uint64_t* reset_count,
+                                    const tj2_osci_diag* diag, void* stream);
+
+/*
  * OutControl calibration helper (section 2.C: top p% channels from a short
  * calibration window): acc[k] += sum over rows of X[m, k]^2 (fp32, bf16 input
  * [M, K]).  The caller zeroes acc once and ranks the channels on the host.

@@ -31,7 +31,7 @@ def L():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_outlier_cols", "nvfp4_linear_fwd", "nvfp4_linear_bwd", "osci_reset_step",
-              "osci_reset_step_multi", "master_update_step", "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes"]:
+              "osci_reset_step_multi", "master_update_step", "master_update_step_multi", "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes"]:
         assert n in names
 
 
@@ -148,6 +148,23 @@ def test_osci_multi_argument_errors(L):
         arr = (_lib.OsciTensorC * 3)(good[0], bad, good[2])
         assert L.osci_reset_step_multi(arr, 3, 1, ctypes.c_float(4.0), 1, None, None, None) == code
         assert b"tensors[1]" in L.tj2_last_error()
+
+
+def test_master_multi_argument_errors(L):
+    from bit_fully_quantized_amd import _lib
+    def tensor(i, N=16, K=128, align=0):
+        return _lib.MasterTensorC(*[0x1000 * (7 * i + j + 1) + align for j in range(7)], N, K, None)
+    ap = _lib.AdamWC(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
+    good = [tensor(i) for i in range(3)]
+    arr = (_lib.MasterTensorC * 3)(*good)
+    assert L.master_update_step_multi(None, 3, ctypes.byref(ap), 1, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.master_update_step_multi(arr, 0, ctypes.byref(ap), 1, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.master_update_step_multi(arr, 3, None, 1, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.master_update_step_multi(arr, 3, ctypes.byref(ap), 0, ctypes.c_float(4.0), 1, None, None, None) == _lib.TJ2_ERR_ARG
+    for bad, code in ((tensor(2, K=100), _lib.TJ2_ERR_SHAPE), (tensor(2, align=4), _lib.TJ2_ERR_ALIGN)):
+        arr = (_lib.MasterTensorC * 3)(good[0], good[1], bad)
+        assert L.master_update_step_multi(arr, 3, ctypes.byref(ap), 1, ctypes.c_float(4.0), 1, None, None, None) == code
+        assert b"tensors[2]" in L.tj2_last_error()
 
 
 def test_master_update_argument_errors(L):
