@@ -420,7 +420,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4",
+        "dtype": "f16",  # MFMA arithmetic on exactly decoded NVFP4/FP8 operands, fp32 accumulation
         "data": "synthetic",
         "config": {
             "workload": "OLMo-2-370M-style linears: d_model 1024, SwiGLU ffn 4096, 16 layers x "
