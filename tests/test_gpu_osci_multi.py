@@ -93,6 +93,7 @@ def test_master_multi_trajectory():
     batch = tj2.MasterBatch(dev)
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
     flips = torch.zeros(1, dtype=torch.int64, device="cuda")
+    hist = torch.zeros(tj2.RISK_BINS, dtype=torch.int64, device="cuda")
     osc = [rng.random(s) < 0.05 for s in shapes]
     total_resets = 0
     for t in range(1, 5):
@@ -105,11 +106,12 @@ def test_master_multi_trajectory():
             grads.append(gr)
         bc1, bc2 = opt.bias_corrections(t)
         flips.zero_()
+        hist.zero_()
         tj2.master_update_step_multi(batch, lr=opt.lr, bias_correction1=float(bc1), bias_correction2=float(bc2),
                                      beta1=opt.beta1, beta2=opt.beta2, eps=opt.eps, weight_decay=opt.weight_decay,
                                      mode=tj2.OSCI_WINDOW_END if end else tj2.OSCI_ACCUM, tau=0.5, reset_enabled=end,
-                                     reset_count=cnt, flips=flips)
-        want_flips = 0
+                                     reset_count=cnt, flips=flips, risk_hist=hist)
+        want_flips, want_hist = 0, np.zeros(tj2.RISK_BINS, np.int64)
         for i in range(len(shapes)):
             W, mo, vo, Qp, dQo, dMo = ref[i]
             diag = {}
@@ -119,6 +121,8 @@ def test_master_multi_trajectory():
             ref[i] = [W, mo, vo, Qp, dQo, dMo]
             total_resets += n_reset
             want_flips += diag["flips"]
+            if end:
+                want_hist += diag["risk_hist"]
             Wd, m, v, _, Qd, dQd, dMd, wq = dev[i]
             for name, got, r in (("W", Wd, W), ("m", m, mo), ("v", v, vo), ("Q_prev", Qd, Qp), ("dQ", dQd, dQo),
                                  ("dM", dMd, dMo)):
@@ -128,4 +132,5 @@ def test_master_multi_trajectory():
                 H.assert_q_equal(wq, wq_ref, what=f"step {t}, matrix {i} codes")
         torch.cuda.synchronize()
         assert int(flips.item()) == want_flips, f"step {t}: flips"
+        np.testing.assert_array_equal(hist.cpu().numpy(), want_hist, err_msg=f"step {t}: histogram")
     assert int(cnt.item()) == total_resets
