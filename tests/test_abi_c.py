@@ -1,0 +1,69 @@
+"""The C ABI used from C: a program compiled against include/tj2.h and linked with libtj2.so calls the
+host-only entry points and the argument checks of the device entry points (no device work), so the header's
+declarations and the library's exported functions are checked by a C compiler and linker, not only through
+ctypes.  Expected values: the oracle's Philox (RHT sign masks) and the header's storage table."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from oracle import philox
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB_DIR = os.path.join(ROOT, "bit_fully_quantized_amd")
+
+PROGRAM = r"""
+#include <stdio.h>
+#include <inttypes.h>
+#include "tj2.h"
+
+int main(void) {
+  printf("version %s\n", tj2_version());
+  const uint64_t seeds[4][2] = {{0, 0}, {0, 2}, {1234, 8}, {9223372036854775813ull, 1099511627779ull}};
+  for (int i = 0; i < 4; ++i) printf("signs %u\n", tj2_rht_signs(seeds[i][0], seeds[i][1]));
+  size_t c = 0, s16 = 0, s128 = 0;
+  tj2_status st = tj2_qtensor_bytes(TJ2_NVFP4, 3, 144, &c, &s16, &s128);
+  printf("nvfp4 %d %zu %zu %zu\n", st, c, s16, s128);
+  st = tj2_qtensor_bytes(TJ2_FP8, 2, 128, &c, &s16, &s128);
+  printf("fp8 %d %zu %zu %zu\n", st, c, s16, s128);
+  printf("bad_len %d\n", tj2_qtensor_bytes(TJ2_NVFP4, 2, 100, &c, &s16, &s128));
+  /* argument checks happen before any device work */
+  tj2_osci_tensor t = {0};
+  printf("osci_multi_empty %d\n", osci_reset_step_multi(&t, 0, TJ2_OSCI_ACCUM, 4.0f, 0, NULL, NULL, NULL));
+  tj2_adamw_params ap = {1e-3f, 0.9f, 0.95f, 1e-8f, 0.1f, 0.1f, 0.05f};
+  tj2_master_tensor m = {0};
+  printf("master_multi_null %d\n", master_update_step_multi(&m, 1, &ap, TJ2_OSCI_ACCUM, 4.0f, 0, NULL, NULL, NULL));
+  printf("last_error %s\n", tj2_last_error());
+  return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="no C compiler")
+def test_c_program_against_header_and_library(tmp_path):
+    if not os.path.exists(os.path.join(LIB_DIR, "libtj2.so")):
+        pytest.fail("libtj2.so is not built (run __graft_entry__.build())")
+    src = tmp_path / "abi.c"
+    src.write_text(PROGRAM)
+    exe = tmp_path / "abi"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-L", LIB_DIR,
+                    "-ltj2", "-Wl,-rpath," + LIB_DIR, "-o", str(exe)], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines()
+    kv = {}
+    signs = []
+    for line in out:
+        key, _, rest = line.partition(" ")
+        if key == "signs":
+            signs.append(int(rest))
+        else:
+            kv[key] = rest
+    assert "gfx950" in kv["version"]
+    want = [philox.rht_signs(s, o) for s, o in [(0, 0), (0, 2), (1234, 8), (2 ** 63 + 5, 2 ** 40 + 3)]]
+    assert signs == want
+    assert kv["nvfp4"].split() == ["0", str(3 * 2 * 64), str(3 * 2 * 8), str(3 * 2 * 4)]
+    assert kv["fp8"].split() == ["0", "256", "0", "8"]
+    assert kv["bad_len"] == "2"                   # TJ2_ERR_SHAPE
+    assert kv["osci_multi_empty"] == "1"          # TJ2_ERR_ARG
+    assert kv["master_multi_null"] == "1"         # null arrays: TJ2_ERR_ARG, named by index
+    assert "tensors[0]" in kv["last_error"]
