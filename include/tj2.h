@@ -8,7 +8,8 @@
  *
  * Conventions for every entry point
  *  - Tensor pointers are DEVICE pointers owned by the caller; the library never
- *    allocates device memory.  Host-side descriptors (tj2_qtensor, tj2_outlier_plan)
+ *    allocates device memory.  Host-side descriptors (tj2_qtensor, tj2_outlier_plan,
+ *    the tj2_osci_tensor / tj2_master_tensor arrays of the _multi entry points)
  *    are read during the call only.
  *  - Dense tensors are row-major and contiguous.  bf16 is passed as raw 16-bit
  *    words.  Device pointers must be 16-byte aligned.
