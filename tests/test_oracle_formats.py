@@ -76,13 +76,34 @@ def test_e2m1_sr_unbiased(x):
     mean = out.mean()
     gap = 2.0 if abs(x) >= 4 else 1.0 if abs(x) >= 2 else 0.5
     sigma = 0.5 * gap / np.sqrt(n)
-    # 16-bit draws bias the mean upward by at most gap/65536
+    # 16-bit draws round up with probability floor(65536 p)/65536, so the mean sits below x
+    # (towards zero) by less than gap/65536
     assert abs(mean - np.float32(x)) <= 5 * sigma + gap / 65536
 
 
+def test_e2m1_sr_up_probability_within_draw_resolution():
+    """Over all 65536 draws, the fraction rounded up differs from the exact position p of the
+    value inside its grid gap (fp64, from the E2M1 grid) by less than 2^-16 and never exceeds
+    it: E[SR(x)] = x up to the resolution of a 16-bit draw, with any bias towards zero."""
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    u = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = np.random.default_rng(9).uniform(0.0, 6.0, size=40).astype(np.float32)
+    vals = np.concatenate([vals, np.float32([0.25, 1.25, 2.5, 5.0, 0.0001, 5.9999])])
+    for v in vals:
+        out = formats.e2m1_decode(formats.e2m1_sr(np.full(65536, v), u)).astype(np.float64)
+        k = np.searchsorted(grid, float(v), side="right") - 1
+        lo, hi = grid[k], grid[min(k + 1, 7)]
+        assert set(np.unique(out)) <= {lo, hi}
+        if hi == lo:
+            continue
+        p = (float(v) - lo) / (hi - lo)
+        frac = np.count_nonzero(out == hi) / 65536.0
+        assert p - 2.0 ** -16 < frac <= p, (float(v), frac, p)
+
+
 def test_e2m1_sr_exact_probability():
-    # with all 65536 draws the up-fraction equals floor(t)/65536 exactly, and the draws that
-    # round up are the largest ones (u >= 65536 - floor(t))
+    # with all 65536 draws the draws that round up are the largest ones (u >= 65536 - floor(t)),
+    # the form gfx950's stochastic conversion takes its random operand in
     u = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     v = np.float32(1.2)  # between 1 and 1.5; fraction 0.4 -> t = 26214.4
     out = formats.e2m1_decode(formats.e2m1_sr(np.full(65536, v), u))

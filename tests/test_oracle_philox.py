@@ -47,14 +47,7 @@ def test_scalar_matches_vectorised():
 
 
 def test_against_rocrand(tmp_path):
-    inc = "/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"
-    if not (shutil.which("g++") and os.path.exists(inc)):
-        pytest.skip("rocrand header or g++ not available")
-    src = tmp_path / "rr.cpp"
-    src.write_text(ROCRAND_SRC)
-    exe = tmp_path / "rr"
-    subprocess.run(["g++", "-O1", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", str(src), "-o", str(exe)],
-                   check=True, capture_output=True)
+    exe = _rocrand_exe(tmp_path)
     blk = random_blocks(2000, seed=5)
     blk[:10, :4] = 0
     blk[10:20, :4] = 0xFFFFFFFF
@@ -93,3 +86,32 @@ def test_rht_signs_distinct_per_offset():
     masks = {philox.rht_signs(0, o) for o in range(0, 64, 2)}
     assert len(masks) > 24
     assert all(0 <= m < 65536 for m in masks)
+
+
+def _rocrand_exe(tmp_path):
+    inc = "/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"
+    if not (shutil.which("g++") and os.path.exists(inc)):
+        pytest.skip("rocrand header or g++ not available")
+    src = tmp_path / "rr.cpp"
+    src.write_text(ROCRAND_SRC)
+    exe = tmp_path / "rr"
+    subprocess.run(["g++", "-O1", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    return exe
+
+
+def test_rht_signs_against_rocrand(tmp_path):
+    """The sign mask of one product pair is the low 16 bits of word 0 of the Philox4x32-10 block
+    with counter (0xFFFFFFFF, 0xFFFFFFFF, lo offset, hi offset) and key (lo seed, hi seed),
+    computed here by rocrand's generator (a wrong counter word, word or half fails)."""
+    exe = _rocrand_exe(tmp_path)
+    cases = [(0, 0), (0, 2), (0, 8), (1, 0), (0x123456789ABCDEF0, 77), ((1 << 64) - 1, (1 << 64) - 1),
+             (42, (1 << 32) + 3), (7, 1 << 40)]
+    rows = []
+    for seed, off in cases:
+        rows.append((0xFFFFFFFF, 0xFFFFFFFF, off & 0xFFFFFFFF, off >> 32, seed & 0xFFFFFFFF, seed >> 32))
+    text = "\n".join(" ".join(str(x) for x in r) for r in rows) + "\n"
+    out = subprocess.run([str(exe)], input=text, capture_output=True, text=True, check=True).stdout.split("\n")
+    for (seed, off), line in zip(cases, out):
+        word0 = int(line.split()[0])
+        assert philox.rht_signs(seed, off) == word0 & 0xFFFF, (seed, off)

@@ -48,3 +48,15 @@ def test_transform_cancels_in_product():
     # a different mask on one side does not cancel
     TB2 = rht.rht_along_last(B, 0x3C5B).astype(np.float64)
     assert np.abs(TA @ TB2.T - ref).max() > 1e-2
+
+
+@pytest.mark.parametrize("j", range(16))
+def test_sign_bit_order_one_hot(j):
+    """Bit j of the mask negates position j of each 16-chunk, i.e. column j of (1/4) H16: built
+    from scipy's Hadamard matrix, so a reversed or shifted bit-to-position map fails."""
+    ref = hadamard(16) / 4.0
+    ref[:, j] = -ref[:, j]
+    np.testing.assert_array_equal(rht.rht_matrix_f64(1 << j), ref)
+    # the fp32 butterfly on small integers is exact: it must equal the scipy product
+    x = np.arange(1, 17, dtype=np.float32) * np.float32(3.0) - np.float32(20.0)
+    np.testing.assert_array_equal(rht.fwht16_f32(x, 1 << j).astype(np.float64), ref @ x.astype(np.float64))
