@@ -17,9 +17,11 @@ from . import _lib
 from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI_INIT, OSCI_WINDOW_END, RISK_BINS, RTN,
                    SR, Tj2Error, check, lib)
 
-__all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "gemm_workspace", "linear_fwd", "linear_bwd", "linear_bwd_workspace",
-           "osci_reset_step", "osci_reset_step_multi", "OsciBatch", "master_update_step", "master_update_step_multi", "MasterBatch", "channel_sumsq", "mfma_peak_probe", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32",
-           "GROUP_ROW", "GROUP_COL", "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END", "RISK_BINS"]
+__all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "gemm_workspace", "linear_fwd", "linear_fwd_workspace",
+           "linear_bwd", "linear_bwd_workspace", "osci_reset_step", "osci_reset_step_multi", "OsciBatch",
+           "master_update_step", "master_update_step_multi", "MasterBatch", "channel_sumsq", "select_outliers",
+           "mfma_peak_probe", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32", "GROUP_ROW", "GROUP_COL",
+           "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END", "RISK_BINS"]
 
 
 def _stream():
@@ -28,6 +30,36 @@ def _stream():
 
 def _ptr(t):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _dense(t, name: str, dtypes, shape=None, optional: bool = False):
+    """A tensor argument the library reads or writes whole: on the GPU, of one of `dtypes`,
+    contiguous (the library assumes row-major rows of the logical width), of `shape` if given."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _matrix_out(t, name: str, dtypes, rows: int, cols: int):
+    """An output matrix written with a leading dimension: rows x >= cols, unit column stride."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype not in dtypes or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D CUDA tensor of dtype {dtypes}")
+    if t.stride(1) != 1 or t.shape[0] != rows or t.shape[1] < cols or (rows > 1 and t.stride(0) < cols):
+        raise ValueError(f"{name} must be [{rows}, >= {cols}] with unit column stride")
+
+
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
 
 
 class QTensor:
@@ -104,8 +136,12 @@ def quantize(x, *, grouping: int = GROUP_ROW, rounding: int = RTN, rht: bool = F
         rows, cols = x.rows, x.len
         xp, xd, xq = None, x.fmt, ctypes.byref(x.c())
     else:
+        _dense(x, "x", (torch.bfloat16, torch.float32))
+        if x.dim() != 2:
+            raise ValueError("x must be 2-D")
         rows, cols = x.shape
         xp, xd, xq = x, _dtype_code(x), None
+    _dense(col_idx, "col_idx", _I32, optional=True)
     n = int(col_idx.numel()) if col_idx is not None else cols
     if out is None:
         out = QTensor(out_fmt, rows, n) if grouping == GROUP_ROW else QTensor(out_fmt, cols, rows)
@@ -116,8 +152,9 @@ def quantize(x, *, grouping: int = GROUP_ROW, rounding: int = RTN, rht: bool = F
     return out
 
 
-def gemm_workspace(I: int, J: int, K: int, device="cuda") -> torch.Tensor | None:
-    n = int(lib().nvfp4_gemm_workspace_size(I, J, K))
+def gemm_workspace(I: int, J: int, K: int, K2: int = 0, device="cuda") -> torch.Tensor | None:
+    """Split-K workspace of an I x J product over K (+ K2 for a second segment), or None."""
+    n = int(lib().nvfp4_gemm_workspace_size(I, J, K, K2))
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
@@ -130,8 +167,11 @@ def gemm(A: QTensor, B: QTensor, A2: QTensor | None = None, B2: QTensor | None =
     for one (nvfp4_gemm_workspace_size); pass `workspace` to reuse a buffer."""
     if out is None:
         out = torch.empty((A.rows, B.rows), dtype=out_dtype, device=A.codes.device)
+    _matrix_out(out, "out", (torch.float32, torch.bfloat16), A.rows, 1 if col_map is not None else B.rows)
+    _dense(col_map, "col_map", _I32, optional=True)
+    _dense(workspace, "workspace", (torch.uint8,), optional=True)
     if workspace is None and split_k:
-        workspace = gemm_workspace(A.rows, B.rows, A.len + (A2.len if A2 is not None else 0), A.codes.device)
+        workspace = gemm_workspace(A.rows, B.rows, A.len, A2.len if A2 is not None else 0, device=A.codes.device)
     ac, bc = A.c(), B.c()
     a2 = ctypes.byref(A2.c()) if A2 is not None else None
     b2 = ctypes.byref(B2.c()) if B2 is not None else None
@@ -149,8 +189,10 @@ def gemm_outlier_cols(A: QTensor, B: QTensor, B8: QTensor, plan: "OutlierPlan", 
     J = B.rows + B8.rows
     if out is None:
         out = torch.empty((A.rows, J), dtype=out_dtype, device=A.codes.device)
+    _matrix_out(out, "out", (torch.float32, torch.bfloat16), A.rows, J)
+    _dense(workspace, "workspace", (torch.uint8,), optional=True)
     if workspace is None:
-        workspace = gemm_workspace(A.rows, J, A.len, A.codes.device)
+        workspace = gemm_workspace(A.rows, J, A.len, device=A.codes.device)
     ac, bc, b8c, pc = A.c(), B.c(), B8.c(), plan.c()
     st = lib().nvfp4_gemm_outlier_cols(ctypes.byref(ac), ctypes.byref(bc), ctypes.byref(b8c), ctypes.byref(pc),
                                        _ptr(out), _dtype_code(out), out.stride(0), 1 if accumulate else 0,
@@ -159,13 +201,25 @@ def gemm_outlier_cols(A: QTensor, B: QTensor, B8: QTensor, plan: "OutlierPlan", 
     return out
 
 
+def linear_fwd_workspace(M: int, N: int, K: int, n_outliers: int = 0, device="cuda") -> torch.Tensor | None:
+    n = int(lib().nvfp4_linear_fwd_workspace_size(M, N, K, n_outliers))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def linear_fwd(X: torch.Tensor, W_master: torch.Tensor | None, N: int, *, Wq: QTensor | None = None,
                W8: QTensor | None = None, plan: OutlierPlan | None = None, y_dtype=torch.bfloat16,
-               Y: torch.Tensor | None = None, Xq: QTensor | None = None, X8: QTensor | None = None):
+               Y: torch.Tensor | None = None, Xq: QTensor | None = None, X8: QTensor | None = None,
+               workspace: torch.Tensor | None = None):
     """Y = X W^T with NVFP4 operands; returns (Y, saved) with saved = dict(Xq, X8, Wq, W8).
 
-    Output / saved buffers may be passed in (Y, Xq, X8, Wq, W8) to avoid allocations."""
+    Output / saved buffers may be passed in (Y, Xq, X8, Wq, W8, workspace) to avoid allocations."""
+    _dense(X, "X", _BF16)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
     M, K = X.shape
+    _dense(W_master, "W_master", _F32, shape=(N, K), optional=True)
+    if W_master is None and Wq is None:
+        raise ValueError("W_master or Wq is required")
     K1 = K - (plan.n if plan else 0)
     if Xq is None:
         Xq = QTensor(NVFP4, M, K1)
@@ -177,6 +231,10 @@ def linear_fwd(X: torch.Tensor, W_master: torch.Tensor | None, N: int, *, Wq: QT
         W8 = QTensor(FP8, N, plan.n)
     if Y is None:
         Y = torch.empty((M, N), dtype=y_dtype, device=X.device)
+    _dense(Y, "Y", (torch.bfloat16, torch.float32), shape=(M, N))
+    if workspace is None:
+        workspace = linear_fwd_workspace(M, N, K, plan.n if plan else 0, device=X.device)
+    _dense(workspace, "workspace", (torch.uint8,), optional=True)
     pc = plan.c() if plan else None
     w8c = W8.c() if W8 is not None else None
     x8c = X8.c() if X8 is not None else None
@@ -184,7 +242,8 @@ def linear_fwd(X: torch.Tensor, W_master: torch.Tensor | None, N: int, *, Wq: QT
     st = lib().nvfp4_linear_fwd(_ptr(X), M, K, N, _ptr(W_master), ctypes.byref(wqc),
                                 ctypes.byref(w8c) if w8c is not None else None,
                                 ctypes.byref(pc) if pc is not None else None, ctypes.byref(xqc),
-                                ctypes.byref(x8c) if x8c is not None else None, _ptr(Y), _dtype_code(Y), _stream())
+                                ctypes.byref(x8c) if x8c is not None else None, _ptr(Y), _dtype_code(Y),
+                                _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
     check("nvfp4_linear_fwd", st)
     return Y, {"Xq": Xq, "X8": X8, "Wq": Wq, "W8": W8}
 
@@ -199,6 +258,9 @@ def linear_bwd(dY: torch.Tensor, saved: dict, K: int, *, seed: int, offset: int,
                workspace: torch.Tensor | None = None, dX: torch.Tensor | None = None,
                dW: torch.Tensor | None = None):
     """Returns (dX, dW, operands-or-None)."""
+    _dense(dY, "dY", _BF16)
+    if dY.dim() != 2:
+        raise ValueError("dY must be 2-D")
     M, N = dY.shape
     no = plan.n if plan else 0
     K1 = K - no
@@ -206,6 +268,9 @@ def linear_bwd(dY: torch.Tensor, saved: dict, K: int, *, seed: int, offset: int,
         dX = torch.empty((M, K), dtype=dx_dtype, device=dY.device)
     if dW is None:
         dW = torch.empty((N, K), dtype=torch.float32, device=dY.device)
+    _dense(dX, "dX", (torch.bfloat16, torch.float32), shape=(M, K))
+    _dense(dW, "dW", _F32, shape=(N, K))
+    _dense(workspace, "workspace", (torch.uint8,), optional=True)
     ops = None
     opsc = None
     if keep_operands:
@@ -249,7 +314,11 @@ def osci_reset_step(W, W_prev, Q_prev, dQ, dM, *, mode: int, tau: float = 4.0, r
     """OsciReset step; flips / risk_hist (optional device counters) receive the oscillation
     diagnostics: the number of elements whose quantized value changed, and at a window end the
     risk histogram (RISK_BINS bins, see include/tj2.h)."""
+    _dense(W, "W", _F32)
     N, K = W.shape
+    for name, t in (("W_prev", W_prev), ("Q_prev", Q_prev), ("dQ", dQ), ("dM", dM)):
+        _dense(t, name, _F32, shape=(N, K))
+    _dense(reset_count, "reset_count", (torch.int64, torch.uint64), optional=True)
     wqc = Wq_out.c() if Wq_out is not None else None
     st = lib().osci_reset_step(_ptr(W), _ptr(W_prev), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K, mode,
                                ctypes.c_float(tau), 1 if reset_enabled else 0,
@@ -267,7 +336,10 @@ class OsciBatch:
         self._wq = []  # codes descriptors the array points to
         self.arr = (_lib.OsciTensorC * len(self.tensors))()
         for i, (W, W_prev, Q_prev, dQ, dM, wq) in enumerate(self.tensors):
+            _dense(W, f"tensors[{i}].W", _F32)
             N, K = W.shape
+            for name, t in (("W_prev", W_prev), ("Q_prev", Q_prev), ("dQ", dQ), ("dM", dM)):
+                _dense(t, f"tensors[{i}].{name}", _F32, shape=(N, K))
             wqc = wq.c() if wq is not None else None
             self._wq.append(wqc)
             self.arr[i] = _lib.OsciTensorC(_ptr(W), _ptr(W_prev), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K,
@@ -296,7 +368,11 @@ def master_update_step(W, m, v, grad, Q_prev, dQ, dM, *, lr: float, bias_correct
                        risk_hist: torch.Tensor | None = None) -> None:
     """Fused master-weight pass: AdamW on W, then OsciReset (ACCUM / WINDOW_END) with the
     pre-update master as W_prev, then the forward codes (Wq_out); diagnostics as osci_reset_step."""
+    _dense(W, "W", _F32)
     N, K = W.shape
+    for name, t in (("m", m), ("v", v), ("grad", grad), ("Q_prev", Q_prev), ("dQ", dQ), ("dM", dM)):
+        _dense(t, name, _F32, shape=(N, K))
+    _dense(reset_count, "reset_count", (torch.int64, torch.uint64), optional=True)
     ap = _lib.AdamWC(lr, beta1, beta2, eps, weight_decay, bias_correction1, bias_correction2)
     wqc = Wq_out.c() if Wq_out is not None else None
     st = lib().master_update_step(_ptr(W), _ptr(m), _ptr(v), _ptr(grad), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K,
@@ -316,7 +392,10 @@ class MasterBatch:
         self._wq = []
         self.arr = (_lib.MasterTensorC * len(self.tensors))()
         for i, (W, m, v, g, Q_prev, dQ, dM, wq) in enumerate(self.tensors):
+            _dense(W, f"tensors[{i}].W", _F32)
             N, K = W.shape
+            for name, t in (("m", m), ("v", v), ("grad", g), ("Q_prev", Q_prev), ("dQ", dQ), ("dM", dM)):
+                _dense(t, f"tensors[{i}].{name}", _F32, shape=(N, K))
             wqc = wq.c() if wq is not None else None
             self._wq.append(wqc)
             self.arr[i] = _lib.MasterTensorC(_ptr(W), _ptr(m), _ptr(v), _ptr(g), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K,
@@ -341,19 +420,45 @@ def master_update_step_multi(tensors, *, lr: float, bias_correction1: float, bia
     check("master_update_step_multi", st)
 
 def mfma_peak_probe(out: torch.Tensor, iters: int) -> float:
-    """Measurement helper (not part of the path): an MFMA-only loop in out.numel() // 256
-    workgroups; returns the flops it performs (the caller times it on the current stream)."""
+    """Measurement helper from libtj2_measure (not part of the path): an MFMA-only loop in
+    out.numel() // 256 workgroups; returns the flops it performs (the caller times it on the
+    current stream)."""
     wgs = out.numel() // 256
     if not out.is_cuda or out.dtype != torch.float32 or wgs < 1:
         raise ValueError("out must be a device float32 tensor of at least 256 elements")
-    check("tj2_mfma_peak_probe", lib().tj2_mfma_peak_probe(wgs, iters, _ptr(out), _stream()))
+    st = _lib.measure_lib().tj2_mfma_peak_probe(wgs, iters, _ptr(out), _stream())
+    if st != 0:
+        raise Tj2Error("tj2_mfma_peak_probe", st, "bad arguments or launch error")
     return float(wgs) * 4 * iters * 4 * 32768
 
 
-def channel_sumsq(X: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:
+def channel_sumsq(X: torch.Tensor, acc: torch.Tensor, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """acc[k] += sum_m X[m, k]^2 (fp64, fixed summation order); acc: device float64 [K]."""
+    _dense(X, "X", _BF16)
     M, K = X.shape
-    check("tj2_channel_sumsq", lib().tj2_channel_sumsq(_ptr(X), M, K, _ptr(acc), _stream()))
+    _dense(acc, "acc", (torch.float64,), shape=(K,))
+    n = int(lib().tj2_channel_sumsq_workspace_size(M, K))
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=X.device)
+    _dense(workspace, "workspace", (torch.uint8,))
+    check("tj2_channel_sumsq", lib().tj2_channel_sumsq(_ptr(X), M, K, _ptr(acc), _ptr(workspace), workspace.numel(),
+                                                        _stream()))
     return acc
+
+
+def select_outliers(scores, p: float, device="cuda") -> OutlierPlan:
+    """Static outlier plan from host or device channel scores (fp64 [K]) by tj2_select_outliers:
+    the ceil(p K / 16) * 16 largest scores, ties to the lower channel, both lists ascending."""
+    sc = scores.detach().to("cpu", torch.float64).contiguous() if isinstance(scores, torch.Tensor) else \
+        torch.as_tensor(scores, dtype=torch.float64).contiguous()
+    K = int(sc.numel())
+    outl = torch.empty(K, dtype=torch.int32)
+    rest = torch.empty(K, dtype=torch.int32)
+    n = ctypes.c_int32(0)
+    check("tj2_select_outliers", lib().tj2_select_outliers(_ptr(sc), K, ctypes.c_double(p), _ptr(outl), _ptr(rest),
+                                                            ctypes.byref(n)))
+    n = n.value
+    return OutlierPlan(outl[:n].to(device), rest[: K - n].contiguous().to(device))
 
 
 def n_outliers(K: int, p: float) -> int:

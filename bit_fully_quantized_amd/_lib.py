@@ -12,6 +12,7 @@ import os
 import torch  # noqa: F401  (loads the HIP runtime before libtj2)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtj2.so")
+MEASURE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtj2_measure.so")
 
 TJ2_OK, TJ2_ERR_ARG, TJ2_ERR_SHAPE, TJ2_ERR_ALIGN, TJ2_ERR_HIP, TJ2_ERR_UNSUPPORTED = range(6)
 BF16, F32, NVFP4, FP8 = 0, 1, 2, 3
@@ -81,12 +82,13 @@ SIGNATURES = {
     "tj2_last_error": (ctypes.c_char_p, []),
     "tj2_version": (ctypes.c_char_p, []),
     "tj2_qtensor_bytes": (I32, [I32, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
-    "tj2_rht_signs": (U32, [U64, U64]),
+    "tj2_rht_signs": (ctypes.c_uint16, [U64, U64]),
     "nvfp4_quantize": (I32, [P, I32, QP, I64, I64, P, I64, I32, I32, I32, U32, U64, U64, QP, P]),
     "nvfp4_gemm": (I32, [QP, QP, QP, QP, P, I32, I64, P, I32, P, SZ, P]),
-    "nvfp4_gemm_workspace_size": (SZ, [I64, I64, I64]),
+    "nvfp4_gemm_workspace_size": (SZ, [I64, I64, I64, I64]),
     "nvfp4_gemm_outlier_cols": (I32, [QP, QP, QP, ctypes.POINTER(PlanC), P, I32, I64, I32, P, SZ, P]),
-    "nvfp4_linear_fwd": (I32, [P, I64, I64, I64, P, QP, QP, ctypes.POINTER(PlanC), QP, QP, P, I32, P]),
+    "nvfp4_linear_fwd": (I32, [P, I64, I64, I64, P, QP, QP, ctypes.POINTER(PlanC), QP, QP, P, I32, P, SZ, P]),
+    "nvfp4_linear_fwd_workspace_size": (SZ, [I64, I64, I64, I32]),
     "nvfp4_linear_bwd": (I32, [P, I64, I64, I64, QP, QP, QP, QP, ctypes.POINTER(PlanC), I32, U64, U64, P, I32, P,
                                ctypes.POINTER(BwdOperandsC), P, SZ, P]),
     "nvfp4_linear_bwd_workspace_size": (SZ, [I64, I64, I64, I32]),
@@ -98,8 +100,9 @@ SIGNATURES = {
                                        ctypes.c_float, I32, P, ctypes.POINTER(OsciDiagC), P]),
     "master_update_step": (I32, [P, P, P, P, P, P, P, I64, I64, ctypes.POINTER(AdamWC), I32, ctypes.c_float, I32,
                                  QP, P, ctypes.POINTER(OsciDiagC), P]),
-    "tj2_channel_sumsq": (I32, [P, I64, I64, P, P]),
-    "tj2_mfma_peak_probe": (I32, [I64, I32, P, P]),
+    "tj2_channel_sumsq_workspace_size": (SZ, [I64, I64]),
+    "tj2_channel_sumsq": (I32, [P, I64, I64, P, P, SZ, P]),
+    "tj2_select_outliers": (I32, [P, I64, ctypes.c_double, P, P, ctypes.POINTER(I32)]),
 }
 
 
@@ -116,6 +119,22 @@ def lib():
             f.argtypes = args
         _lib = L
     return _lib
+
+
+_mlib = None
+
+
+def measure_lib():
+    """The measurement helpers (libtj2_measure.so, include/tj2_measure.h): not part of the path."""
+    global _mlib
+    if _mlib is None:
+        if not os.path.exists(MEASURE_LIB_PATH):
+            raise RuntimeError(f"{MEASURE_LIB_PATH} is missing: build it with `python -m bit_fully_quantized_amd.build`")
+        L = ctypes.CDLL(MEASURE_LIB_PATH)
+        L.tj2_mfma_peak_probe.restype = I32
+        L.tj2_mfma_peak_probe.argtypes = [I64, I32, P, P]
+        _mlib = L
+    return _mlib
 
 
 def check(fn: str, status: int) -> None:

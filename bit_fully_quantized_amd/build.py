@@ -1,4 +1,5 @@
-"""Build libtj2.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Build libtj2.so (HIP kernels + C ABI) and libtj2_measure.so (the benchmark's
+measurement helpers) for gfx950 with hipcc, in-tree.
 
 Usage: python -m bit_fully_quantized_amd.build
 """
@@ -15,7 +16,9 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libtj2.so")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "osci.hip", "probe.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "osci.hip"]
+MEASURE_LIB_PATH = os.path.join(HERE, "libtj2_measure.so")
+MEASURE_SOURCES = ["measure.hip"]
 
 # -ffp-contract=off keeps every fp32 step a single IEEE operation (bit-exact
 # quantizers); packed fp32 instructions are disabled.
@@ -42,18 +45,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + MEASURE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB_PATH)
+    _link([objs[s] for s in MEASURE_SOURCES], MEASURE_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {MEASURE_LIB_PATH}")
     return LIB_PATH
 
 

@@ -2,6 +2,7 @@
 // orchestration of the linear layer's forward and backward passes over the
 // quantizer, product and OsciReset kernels.  All device work is enqueued on
 // the caller's stream; no device memory is allocated here.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -91,6 +92,9 @@ size_t qbytes(int fmt, int64_t rows, int64_t len, size_t* c, size_t* s16, size_t
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// 128-element chunks of a product's reduction over one or two segments.
+int64_t gemm_chunks(int64_t K, int64_t K2) { return (K + 127) / 128 + (K2 + 127) / 128; }
 
 // Carve a tj2_qtensor out of a workspace cursor.
 tj2_qtensor carve(uint8_t*& cur, int fmt, int64_t rows, int64_t len) {
@@ -277,7 +281,7 @@ tj2_status tj2_qtensor_bytes(int32_t fmt, int64_t rows, int64_t len, size_t* cod
   return ok();
 }
 
-uint32_t tj2_rht_signs(uint64_t seed, uint64_t offset) { return philox_word0(seed, offset) & 0xFFFFu; }
+uint16_t tj2_rht_signs(uint64_t seed, uint64_t offset) { return (uint16_t)(philox_word0(seed, offset) & 0xFFFFu); }
 
 tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q, int64_t rows, int64_t cols,
                           const int32_t* col_idx, int64_t n_idx, int32_t grouping, int32_t rounding, int32_t rht,
@@ -318,9 +322,9 @@ tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q
                    offset, out, (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
 }
 
-size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K) {
-  if (I <= 0 || J <= 0 || K <= 0) return 0;
-  return gemm_workspace_bytes(I, J, (K + 127) / 128);
+size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K, int64_t K2) {
+  if (I <= 0 || J <= 0 || K <= 0 || K2 < 0) return 0;
+  return gemm_workspace_bytes(I, J, gemm_chunks(K, K2));
 }
 
 tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2, const tj2_qtensor* B2,
@@ -341,6 +345,10 @@ tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qten
   if (!col_map && ldc < B->rows) return fail(TJ2_ERR_SHAPE, "ldc < J");
   if (ldc <= 0) return fail(TJ2_ERR_SHAPE, "ldc must be positive");
   if (A->rows > ((int64_t)1 << 24) * 128 || B->rows > ((int64_t)1 << 24) * 128) return fail(TJ2_ERR_SHAPE, "too many rows");
+  if (workspace) {
+    const size_t need = gemm_workspace_bytes(A->rows, B->rows, gemm_chunks(A->len, A2 ? A2->len : 0));
+    if (ws_bytes < need) return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  }
   return run_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate, workspace, workspace ? ws_bytes : 0,
                   (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
 }
@@ -363,13 +371,22 @@ tj2_status nvfp4_gemm_outlier_cols(const tj2_qtensor* A, const tj2_qtensor* B, c
   if (accumulate && c_dtype != TJ2_F32) return fail(TJ2_ERR_UNSUPPORTED, "accumulate needs an fp32 output");
   if (ldc < J) return fail(TJ2_ERR_SHAPE, "ldc < J");
   if (A->rows > ((int64_t)1 << 24) * 128 || J > ((int64_t)1 << 24) * 128) return fail(TJ2_ERR_SHAPE, "too many rows");
+  if (workspace) {
+    const size_t need = gemm_workspace_bytes(A->rows, J, gemm_chunks(A->len, 0));
+    if (ws_bytes < need) return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  }
   return run_gemm_outl(A, B, B8, plan, C, c_dtype, ldc, accumulate, workspace, workspace ? ws_bytes : 0,
                        (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
 }
 
+size_t nvfp4_linear_fwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers) {
+  if (M <= 0 || N <= 0 || K <= 0 || n_outliers < 0 || n_outliers >= K) return 0;
+  return gemm_workspace_bytes(M, N, gemm_chunks(K - n_outliers, n_outliers));
+}
+
 tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, const float* W_master, tj2_qtensor* Wq,
                             tj2_qtensor* W8, const tj2_outlier_plan* plan, tj2_qtensor* Xq, tj2_qtensor* X8, void* Y,
-                            int32_t y_dtype, void* stream) {
+                            int32_t y_dtype, void* workspace, size_t ws_bytes, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   TJ2_TRY(check_dims(M, "M"));
   TJ2_TRY(check_dims(K, "K"));
@@ -386,6 +403,11 @@ tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, cons
     TJ2_TRY(check_qtensor(X8, "X8", TJ2_FP8, M, no));
     TJ2_TRY(check_qtensor(W8, "W8", TJ2_FP8, N, no));
   }
+  if (workspace) {
+    if (!aligned16(workspace)) return fail(TJ2_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t need = nvfp4_linear_fwd_workspace_size(M, N, K, (int32_t)no);
+    if (ws_bytes < need) return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  }
   if (plan) {
     TJ2_TRY(run_split(X, TJ2_BF16, M, K, plan, Xq, X8, s));
     if (W_master) TJ2_TRY(run_split(W_master, TJ2_F32, N, K, plan, Wq, W8, s));
@@ -393,7 +415,8 @@ tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, cons
     TJ2_TRY(run_quant(X, TJ2_BF16, nullptr, M, K, nullptr, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Xq, s));
     if (W_master) TJ2_TRY(run_quant(W_master, TJ2_F32, nullptr, N, K, nullptr, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Wq, s));
   }
-  TJ2_TRY(run_gemm(Xq, Wq, plan ? X8 : nullptr, plan ? W8 : nullptr, Y, y_dtype, N, nullptr, 0, nullptr, 0, s));
+  TJ2_TRY(run_gemm(Xq, Wq, plan ? X8 : nullptr, plan ? W8 : nullptr, Y, y_dtype, N, nullptr, 0, workspace,
+                   workspace ? ws_bytes : 0, s));
   return ok();
 }
 
@@ -619,20 +642,48 @@ tj2_status osci_reset_step_multi(const tj2_osci_tensor* tensors, int32_t n, int3
   return ok();
 }
 
-tj2_status tj2_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, void* stream) {
-  if (!X || !acc) return fail(TJ2_ERR_ARG, "X and acc are required");
-  if (!aligned16(X)) return fail(TJ2_ERR_ALIGN, "X must be 16-byte aligned");
-  if (M <= 0) return fail(TJ2_ERR_SHAPE, "M must be positive");
+size_t tj2_channel_sumsq_workspace_size(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  return sumsq_workspace_bytes(M, K);
+}
+
+tj2_status tj2_channel_sumsq(const void* X, int64_t M, int64_t K, double* acc, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  if (!X || !acc || !workspace) return fail(TJ2_ERR_ARG, "X, acc and workspace are required");
+  if (!aligned16(X) || !aligned16(acc) || !aligned16(workspace)) return fail(TJ2_ERR_ALIGN, "X, acc and workspace must be 16-byte aligned");
+  if (M <= 0 || M > ((int64_t)1 << 30)) return fail(TJ2_ERR_SHAPE, "M must be positive");
   TJ2_TRY(check_dims(K, "K"));
-  TJ2_TRY(hip_check(launch_channel_sumsq(X, M, K, acc, (hipStream_t)stream), "sumsq launch"));
+  const size_t need = sumsq_workspace_bytes(M, K);
+  if (ws_bytes < need) return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  TJ2_TRY(hip_check(launch_channel_sumsq(X, M, K, acc, reinterpret_cast<double*>(workspace), (hipStream_t)stream),
+                    "sumsq launch"));
   return ok();
 }
 
-tj2_status tj2_mfma_peak_probe(int64_t workgroups, int32_t iters, float* out, void* stream) {
-  if (!out) return fail(TJ2_ERR_ARG, "out is required");
-  if (workgroups < 1 || workgroups > ((int64_t)1 << 20)) return fail(TJ2_ERR_ARG, "workgroups out of range");
-  if (iters < 1 || iters > (1 << 20)) return fail(TJ2_ERR_ARG, "iters out of range");
-  TJ2_TRY(hip_check(launch_mfma_peak(workgroups, iters, out, (hipStream_t)stream), "mfma probe launch"));
+tj2_status tj2_select_outliers(const double* scores, int64_t K, double p, int32_t* outliers, int32_t* rest,
+                               int32_t* n_outliers) {
+  if (!scores || !outliers || !rest || !n_outliers) return fail(TJ2_ERR_ARG, "scores, outliers, rest and n_outliers are required");
+  TJ2_TRY(check_dims(K, "K"));
+  if (!(p > 0.0 && p < 1.0)) return fail(TJ2_ERR_ARG, "p must lie in (0, 1)");
+  for (int64_t k = 0; k < K; ++k)
+    if (!(scores[k] >= 0.0) || scores[k] > 1.79e308) return fail(TJ2_ERR_ARG, "score %lld is negative or not finite", (long long)k);
+  const int64_t n = (int64_t)ceil(p * (double)K / 16.0) * 16;
+  if (n <= 0 || n >= K) return fail(TJ2_ERR_SHAPE, "%lld outlier channels of K = %lld leave no NVFP4 channel", (long long)n, (long long)K);
+  std::vector<int32_t> order((size_t)K);
+  for (int64_t k = 0; k < K; ++k) order[(size_t)k] = (int32_t)k;
+  // descending score, ties to the lower channel index: a strict weak order, so the
+  // selection does not depend on the sort's implementation
+  std::sort(order.begin(), order.end(), [scores](int32_t a, int32_t b) {
+    return scores[a] > scores[b] || (scores[a] == scores[b] && a < b);
+  });
+  std::vector<uint8_t> is_out((size_t)K, 0);
+  for (int64_t i = 0; i < n; ++i) is_out[(size_t)order[(size_t)i]] = 1;
+  int64_t no = 0, nr = 0;
+  for (int64_t k = 0; k < K; ++k) {
+    if (is_out[(size_t)k]) outliers[no++] = (int32_t)k;
+    else rest[nr++] = (int32_t)k;
+  }
+  *n_outliers = (int32_t)n;
   return ok();
 }
 

@@ -18,7 +18,8 @@
 // the window's risk dQ / dM, reduced per workgroup in LDS and added to device
 // counters with one atomic per workgroup and counter.
 //
-// Calibration (section 2.C): per-channel sum of squares of the activations.
+// Calibration (section 2.C): per-channel sum of squares of the activations, in
+// fp64 and a fixed summation order (two passes, no atomics).
 #include <cstring>
 
 #include "tj2_device.h"
@@ -378,26 +379,30 @@ __global__ __launch_bounds__(256) void master_multi_kernel(MasterMulti m) {
   master_body<DIAG>(m.p[i], m.hpr[i], (blockIdx.x - m.begin[i]) * 256u + threadIdx.x, dsm);
 }
 
-// acc[k] += sum_m X[m, k]^2.  Thread: 8 columns x 64 rows; 8 row slices per block
-// are reduced in LDS, then one atomic per column per block.
-__global__ __launch_bounds__(256) void sumsq_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                    float* __restrict__ acc) {
-  __shared__ float red[8][256];
+// Per-channel sums of squares, in a fixed order so that the result does not
+// depend on scheduling: kSumsqRows-row slabs of a 256-column tile, each thread 8
+// columns x kSumsqRows/8 rows, squares and sums in fp64 (a bf16 square is exact
+// in fp64); the 8 row slices of a slab are added in LDS in slice order and the
+// slab's sums written to partial[slab][k].
+__global__ __launch_bounds__(256) void sumsq_partial_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                            double* __restrict__ partial) {
+  __shared__ double red[8][256];
   const int cgp = threadIdx.x & 31, slice = threadIdx.x >> 5;
   const int64_t c0 = (int64_t)blockIdx.x * 256 + cgp * 8;
-  const int64_t rbeg = (int64_t)blockIdx.y * 512 + slice * 64;
-  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  constexpr int kRowsPerSlice = kSumsqRows / 8;
+  const int64_t rbeg = (int64_t)blockIdx.y * kSumsqRows + slice * kRowsPerSlice;
+  double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (c0 < K) {
-    for (int r = 0; r < 64; ++r) {
+    for (int r = 0; r < kRowsPerSlice; ++r) {
       const int64_t row = rbeg + r;
       if (row >= M) break;
-      uint4 a = *reinterpret_cast<const uint4*>(X + row * K + c0);
-      uint32_t w[4] = {a.x, a.y, a.z, a.w};
+      const uint4 a = *reinterpret_cast<const uint4*>(X + row * K + c0);
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
-        s[2 * i] = fmaf(lo, lo, s[2 * i]);
-        s[2 * i + 1] = fmaf(hi, hi, s[2 * i + 1]);
+        const double lo = (double)__uint_as_float(w[i] << 16), hi = (double)__uint_as_float(w[i] & 0xFFFF0000u);
+        s[2 * i] = s[2 * i] + lo * lo;
+        s[2 * i + 1] = s[2 * i + 1] + hi * hi;
       }
     }
   }
@@ -406,11 +411,21 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const uint16_t* __restrict__
   __syncthreads();
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (col < K) {
-    float t = 0.0f;
+    double t = red[0][threadIdx.x];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t += red[i][threadIdx.x];
-    atomicAdd(acc + col, t);
+    for (int i = 1; i < 8; ++i) t = t + red[i][threadIdx.x];
+    partial[(int64_t)blockIdx.y * K + col] = t;
   }
+}
+
+// acc[k] += the slabs' sums of channel k, added in slab order.
+__global__ __launch_bounds__(256) void sumsq_finish_kernel(const double* __restrict__ partial, int64_t slabs,
+                                                           int64_t K, double* __restrict__ acc) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= K) return;
+  double t = partial[col];
+  for (int64_t z = 1; z < slabs; ++z) t = t + partial[z * K + col];
+  acc[col] = acc[col] + t;
 }
 
 }  // namespace
@@ -485,9 +500,17 @@ hipError_t launch_osci_multi(const OsciParams* ps, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, hipStream_t s) {
-  dim3 grid((uint32_t)((K + 255) / 256), (uint32_t)((M + 511) / 512));
-  hipLaunchKernelGGL(sumsq_kernel, grid, dim3(256), 0, s, reinterpret_cast<const uint16_t*>(X), M, K, acc);
+size_t sumsq_workspace_bytes(int64_t M, int64_t K) {
+  return (size_t)((M + kSumsqRows - 1) / kSumsqRows) * (size_t)K * sizeof(double);
+}
+
+hipError_t launch_channel_sumsq(const void* X, int64_t M, int64_t K, double* acc, double* partial, hipStream_t s) {
+  const int64_t slabs = (M + kSumsqRows - 1) / kSumsqRows;
+  const dim3 grid((uint32_t)((K + 255) / 256), (uint32_t)slabs);
+  hipLaunchKernelGGL(sumsq_partial_kernel, grid, dim3(256), 0, s, reinterpret_cast<const uint16_t*>(X), M, K, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sumsq_finish_kernel, dim3((uint32_t)((K + 255) / 256)), dim3(256), 0, s, partial, slabs, K, acc);
   return hipGetLastError();
 }
 

@@ -144,9 +144,10 @@ struct MasterParams {
 hipError_t launch_master(const MasterParams& p, hipStream_t s);
 hipError_t launch_master_multi(const MasterParams* ps, int n, hipStream_t s);  // up to kOsciMultiMax
 
-hipError_t launch_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, hipStream_t s);
-
-// measurement helper: MFMA-only loop (see tj2_mfma_peak_probe)
-hipError_t launch_mfma_peak(int64_t workgroups, int32_t iters, float* out, hipStream_t s);
+// Calibration sums: rows per slab of the first pass; the second pass adds the
+// slabs' fp64 partial sums (workspace [ceil(M / kSumsqRows)][K]) in slab order.
+constexpr int kSumsqRows = 512;
+size_t sumsq_workspace_bytes(int64_t M, int64_t K);
+hipError_t launch_channel_sumsq(const void* X, int64_t M, int64_t K, double* acc, double* partial, hipStream_t s);
 
 }  // namespace tj2

@@ -127,8 +127,9 @@ tj2_status tj2_qtensor_bytes(int32_t fmt, int64_t rows, int64_t len, size_t* cod
  * = position j of every 16-chunk is negated).  Host function, no device work:
  * low 16 bits of word 0 of Philox4x32-10 with key (lo seed, hi seed) and counter
  * (0xFFFFFFFF, 0xFFFFFFFF, lo offset, hi offset).  (Section 2.C: RHT on dX, dW.)
+ * Entry points that take a mask take it as uint32_t and use its low 16 bits.
  */
-uint32_t tj2_rht_signs(uint64_t seed, uint64_t offset);
+uint16_t tj2_rht_signs(uint64_t seed, uint64_t offset);
 
 /*
  * Double-block quantizer (section 2.A; FP8 output for the OutControl channels,
@@ -169,14 +170,21 @@ tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q
  * The result is accumulated in fp32 with one FP32 promotion per 128-element
  * outer block.  c_dtype TJ2_F32 or TJ2_BF16 (round to nearest even); ldc in
  * elements.  col_map (optional, device int32[J]) gives the output column of B
- * row j.  accumulate != 0 adds into C (TJ2_F32 only).  workspace may be NULL
- * when nvfp4_gemm_workspace_size() returns 0.
+ * row j.  accumulate != 0 adds into C (TJ2_F32 only).
+ * workspace: fp32 partial sums of a K split, nvfp4_gemm_workspace_size(I, J,
+ * A->len, A2 ? A2->len : 0) bytes (0 for most shapes: the library splits K only
+ * when the output has too few 256x128 tiles to fill the GPU).  NULL runs the
+ * product without a split; a non-NULL workspace smaller than the size asked
+ * for is an error (TJ2_ERR_ARG).
  */
 tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2,
                       const tj2_qtensor* B2, void* C, int32_t c_dtype, int64_t ldc,
                       const int32_t* col_map, int32_t accumulate, void* workspace, size_t ws_bytes,
                       void* stream);
-size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K);
+/* Workspace of nvfp4_gemm for I x J outputs over reductions of K (and K2 for a
+ * second segment, else 0) elements; the same for nvfp4_gemm_outlier_cols with
+ * K2 = 0.  Returns 0 for invalid sizes. */
+size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K, int64_t K2);
 
 /*
  * Product whose output columns are split by a static outlier plan (OutControl,
@@ -189,7 +197,7 @@ size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K);
  * A [I, K] NVFP4; B [J - n, K] NVFP4; B8 [n, K] FP8 with n = plan->n_outliers;
  * plan arrays sorted ascending, device int32, 16-byte aligned, rest listing the
  * J - n columns not in outliers.  C, ldc (>= J), c_dtype, accumulate and the
- * workspace (nvfp4_gemm_workspace_size(I, J, K) bytes) as for nvfp4_gemm.
+ * workspace (nvfp4_gemm_workspace_size(I, J, K, 0) bytes) as for nvfp4_gemm.
  */
 tj2_status nvfp4_gemm_outlier_cols(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* B8,
                                    const tj2_outlier_plan* plan, void* C, int32_t c_dtype, int64_t ldc,
@@ -206,11 +214,15 @@ tj2_status nvfp4_gemm_outlier_cols(const tj2_qtensor* A, const tj2_qtensor* B, c
  *     outlier channels in FP8 (round to nearest even); Y adds both products.
  * Xq/X8 are saved for the backward and stay owned by the caller.
  * Y [M, N]: y_dtype TJ2_BF16 or TJ2_F32.  M, K, N multiples of 16.
+ * workspace: split-K partial sums of the product (few output tiles, e.g. a
+ * small M), nvfp4_linear_fwd_workspace_size(M, N, K, n_outliers) bytes; NULL
+ * runs the product unsplit; a smaller non-NULL workspace is TJ2_ERR_ARG.
  */
 tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, const float* W_master,
                             tj2_qtensor* Wq, tj2_qtensor* W8, const tj2_outlier_plan* plan,
                             tj2_qtensor* Xq, tj2_qtensor* X8, void* Y, int32_t y_dtype,
-                            void* stream);
+                            void* workspace, size_t ws_bytes, void* stream);
+size_t nvfp4_linear_fwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers);
 
 /*
  * Backward of the NVFP4 linear layer (sections 2.A and 2.C).  Uses the forward's
@@ -374,23 +386,33 @@ tj2_status master_update_step_multi(const tj2_master_tensor* tensors, int32_t n,
                                     const tj2_osci_diag* diag, void* stream);
 
 /*
- * OutControl calibration helper (section 2.C: top p% channels from a short
- * calibration window): acc[k] += sum over rows of X[m, k]^2 (fp32, bf16 input
- * [M, K]).  The caller zeroes acc once and ranks the channels on the host.
+ * OutControl calibration (technical summary, section 2.C: the top p% channels
+ * are chosen once from a short calibration window and stay in FP8).
+ *
+ * tj2_channel_sumsq: acc[k] += sum over rows m of X[m, k]^2 for a bf16 X [M, K]
+ * (device), acc a device fp64 [K] array that the caller zeroes once and passes
+ * for every calibration batch.  Squares and sums are fp64 in a fixed order
+ * (per 512-row slab, then slab by slab), so a result does not depend on
+ * scheduling.  workspace: device, tj2_channel_sumsq_workspace_size(M, K)
+ * bytes, 16-byte aligned.  K a multiple of 16.
  */
-tj2_status tj2_channel_sumsq(const void* X, int64_t M, int64_t K, float* acc, void* stream);
+size_t tj2_channel_sumsq_workspace_size(int64_t M, int64_t K);
+tj2_status tj2_channel_sumsq(const void* X, int64_t M, int64_t K, double* acc, void* workspace, size_t ws_bytes,
+                             void* stream);
 
 /*
- * Measurement helper, not part of the path: the achievable dense f16 MFMA rate
- * of the part.  Runs `workgroups` workgroups of 256 threads (4 waves); each wave
- * runs `iters` rounds of four independent v_mfma_f32_32x32x16_f16 accumulation
- * chains on register operands (every element 0.0625, so each thread's result,
- * written to out[workgroup * 256 + thread], is 0.25 * iters exactly).  Work:
- * workgroups * 4 * iters * 4 * 32768 flops; the caller times the call on its
- * stream.  out: device, workgroups * 256 floats, caller-owned.  Errors:
- * TJ2_ERR_ARG (NULL out, workgroups outside [1, 2^20], iters outside [1, 2^20]).
+ * tj2_select_outliers: the static plan from the channel scores (host function,
+ * no device work).  n = ceil(p * K / 16) * 16 channels with the largest scores
+ * (ties to the lower channel index) are the outliers; every other channel is
+ * in rest.  scores: host double [K] (non-negative, finite); outliers: host
+ * int32 [n] and rest: host int32 [K - n], both written in ascending order
+ * (size them for p, e.g. K entries each); *n_outliers receives n.  The caller
+ * copies both lists to the device for a tj2_outlier_plan.  Errors: TJ2_ERR_ARG
+ * (NULL pointer, p outside (0, 1), a negative or non-finite score),
+ * TJ2_ERR_SHAPE (K not a positive multiple of 16, or n >= K).
  */
-tj2_status tj2_mfma_peak_probe(int64_t workgroups, int32_t iters, float* out, void* stream);
+tj2_status tj2_select_outliers(const double* scores, int64_t K, double p, int32_t* outliers, int32_t* rest,
+                               int32_t* n_outliers);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,32 @@
+/*
+ * tj2_measure.h -- C ABI of libtj2_measure, the measurement helpers that the
+ * benchmark times beside the products.  They are not part of the quantized
+ * linear layer and live in a library of their own (libtj2_measure.so); the
+ * product library libtj2.so exports none of them.
+ */
+#ifndef TJ2_MEASURE_H_
+#define TJ2_MEASURE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * The achievable dense f16 MFMA rate of the part.  Runs `workgroups`
+ * workgroups of 256 threads (4 waves); each wave runs `iters` rounds of four
+ * independent v_mfma_f32_32x32x16_f16 accumulation chains on register
+ * operands (every element 0.0625, so each thread's result, written to
+ * out[workgroup * 256 + thread], is 0.25 * iters exactly).  Work: workgroups *
+ * 4 * iters * 4 * 32768 flops; the caller times the call on its stream.
+ * out: device, workgroups * 256 floats, caller-owned.  Returns 0, 1 (NULL out,
+ * workgroups outside [1, 2^20] or iters outside [1, 2^20]; nothing enqueued)
+ * or 4 (launch error).
+ */
+int32_t tj2_mfma_peak_probe(int64_t workgroups, int32_t iters, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TJ2_MEASURE_H_ */

@@ -35,6 +35,18 @@ int main(void) {
   tj2_master_tensor m = {0};
   printf("master_multi_null %d\n", master_update_step_multi(&m, 1, &ap, TJ2_OSCI_ACCUM, 4.0f, 0, NULL, NULL, NULL));
   printf("last_error %s\n", tj2_last_error());
+  /* OutControl plan from host scores */
+  double scores[32];
+  for (int i = 0; i < 32; ++i) scores[i] = (double)((i * 7) % 32);
+  int32_t outl[32], rest[32], n = 0;
+  st = tj2_select_outliers(scores, 32, 0.25, outl, rest, &n);
+  printf("plan %d %d", st, (int)n);
+  for (int i = 0; i < n; ++i) printf(" %d", (int)outl[i]);
+  printf("\n");
+  printf("fwd_ws %zu %zu\n", nvfp4_linear_fwd_workspace_size(16384, 4096, 1024, 112),
+         nvfp4_linear_fwd_workspace_size(128, 128, 16384, 0));
+  printf("gemm_ws %zu\n", nvfp4_gemm_workspace_size(256, 128, 912, 112));
+  printf("sumsq_ws %zu\n", tj2_channel_sumsq_workspace_size(1024, 256));
   return 0;
 }
 """
@@ -67,3 +79,11 @@ def test_c_program_against_header_and_library(tmp_path):
     assert kv["osci_multi_empty"] == "1"          # TJ2_ERR_ARG
     assert kv["master_multi_null"] == "1"         # null arrays: TJ2_ERR_ARG, named by index
     assert "tensors[0]" in kv["last_error"]
+    # (i * 7) % 32 is a permutation of 0..31: the 16 largest scores (16..31) sit at these channels
+    plan = [int(x) for x in kv["plan"].split()]
+    assert plan[:2] == [0, 16]
+    assert plan[2:] == sorted(i for i in range(32) if (i * 7) % 32 >= 16)
+    fwd = [int(x) for x in kv["fwd_ws"].split()]
+    assert fwd[0] == 0 and fwd[1] > 0  # many output tiles: no split; one tile over a long K: split
+    assert int(kv["gemm_ws"]) > 0
+    assert int(kv["sumsq_ws"]) == 2 * 256 * 8

@@ -31,7 +31,9 @@ def L():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_outlier_cols", "nvfp4_linear_fwd", "nvfp4_linear_bwd", "osci_reset_step",
-              "osci_reset_step_multi", "master_update_step", "master_update_step_multi", "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes"]:
+              "osci_reset_step_multi", "master_update_step", "master_update_step_multi", "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes",
+              "tj2_select_outliers", "tj2_channel_sumsq_workspace_size", "nvfp4_linear_fwd_workspace_size",
+              "nvfp4_gemm_workspace_size", "nvfp4_linear_bwd_workspace_size"]:
         assert n in names
 
 
@@ -111,11 +113,19 @@ def test_gemm_and_linear_argument_errors(L):
     Wq = fake_q(_lib.NVFP4, 32, 128)
     # M not a multiple of 16
     assert L.nvfp4_linear_fwd(0x1000, 60, 128, 32, None, ctypes.byref(Wq), None, None, ctypes.byref(Xq), None,
-                              0x9000, _lib.BF16, None) == _lib.TJ2_ERR_SHAPE
+                              0x9000, _lib.BF16, None, 0, None) == _lib.TJ2_ERR_SHAPE
     # plan with a bad outlier count
     plan = _lib.PlanC(0x7000, 0x8000, 8, 0)
     assert L.nvfp4_linear_fwd(0x1000, 64, 128, 32, None, ctypes.byref(Wq), None, ctypes.byref(plan),
-                              ctypes.byref(Xq), None, 0x9000, _lib.BF16, None) == _lib.TJ2_ERR_SHAPE
+                              ctypes.byref(Xq), None, 0x9000, _lib.BF16, None, 0, None) == _lib.TJ2_ERR_SHAPE
+    # a workspace smaller than the forward's split asks for (a small M: few output tiles)
+    need = L.nvfp4_linear_fwd_workspace_size(64, 32, 128 * 64, 0)
+    assert need > 0 and L.nvfp4_linear_fwd_workspace_size(16384, 4096, 1024, 0) == 0
+    Xb = fake_q(_lib.NVFP4, 64, 128 * 64)
+    Wb = fake_q(_lib.NVFP4, 32, 128 * 64)
+    assert L.nvfp4_linear_fwd(0x1000, 64, 128 * 64, 32, None, ctypes.byref(Wb), None, None, ctypes.byref(Xb), None,
+                              0x9000, _lib.BF16, 0xB000, need - 1, None) == _lib.TJ2_ERR_ARG
+    assert b"workspace" in L.tj2_last_error()
     # backward without workspace
     assert L.nvfp4_linear_bwd(0x1000, 64, 32, 128, ctypes.byref(Xq), None, ctypes.byref(Wq), None, None, 1, 0, 0,
                               0x9000, _lib.BF16, 0xA000, None, None, 0, None) == _lib.TJ2_ERR_ARG
@@ -130,7 +140,11 @@ def test_osci_argument_errors(L):
     assert L.osci_reset_step(*p, 16, 128, 7, ctypes.c_float(4.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
     assert L.osci_reset_step(*p, 16, 128, 1, ctypes.c_float(-1.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
     assert L.osci_reset_step(None, *p[1:], 16, 128, 1, ctypes.c_float(4.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
-    assert L.tj2_channel_sumsq(0x1000, 64, 100, 0x2000, None) == _lib.TJ2_ERR_SHAPE
+    assert L.tj2_channel_sumsq(0x1000, 64, 100, 0x2000, 0x3000, 1 << 20, None) == _lib.TJ2_ERR_SHAPE
+    assert L.tj2_channel_sumsq(0x1000, 64, 128, 0x2000, None, 0, None) == _lib.TJ2_ERR_ARG
+    need = L.tj2_channel_sumsq_workspace_size(1000, 128)
+    assert need == 2 * 128 * 8  # two 512-row slabs of fp64 partial sums
+    assert L.tj2_channel_sumsq(0x1000, 1000, 128, 0x2000, 0x3000, need - 8, None) == _lib.TJ2_ERR_ARG
 
 
 def test_osci_multi_argument_errors(L):
@@ -199,11 +213,65 @@ def test_diag_counter_alignment(L):
                              None) == _lib.TJ2_ERR_ALIGN
 
 
-def test_mfma_probe_argument_errors(L):
+def test_measurement_helpers_live_outside_the_product_library(L):
+    # the benchmark's MFMA-only loop is in libtj2_measure.so, declared by include/tj2_measure.h
     from bit_fully_quantized_amd import _lib
-    assert L.tj2_mfma_peak_probe(16, 8, None, None) == _lib.TJ2_ERR_ARG
-    assert L.tj2_mfma_peak_probe(0, 8, 0x1000, None) == _lib.TJ2_ERR_ARG
-    assert L.tj2_mfma_peak_probe(16, 0, 0x1000, None) == _lib.TJ2_ERR_ARG
+    assert not hasattr(L, "tj2_mfma_peak_probe")
+    M = _lib.measure_lib()
+    assert M.tj2_mfma_peak_probe(16, 8, None, None) == 1
+    assert M.tj2_mfma_peak_probe(0, 8, 0x1000, None) == 1
+    assert M.tj2_mfma_peak_probe(16, 0, 0x1000, None) == 1
+    text = open(os.path.join(ROOT, "include", "tj2_measure.h")).read()
+    assert "tj2_mfma_peak_probe" in text
+
+
+def _plan_from_library(L, scores, p):
+    import numpy as np
+    sc = np.ascontiguousarray(scores, dtype=np.float64)
+    K = sc.size
+    o = np.zeros(K, np.int32)
+    r = np.zeros(K, np.int32)
+    n = ctypes.c_int32(-1)
+    st = L.tj2_select_outliers(sc.ctypes.data, K, ctypes.c_double(p), o.ctypes.data, r.ctypes.data, ctypes.byref(n))
+    return st, o[: n.value], r[: K - n.value]
+
+
+def test_select_outliers_matches_oracle(L):
+    """tj2_select_outliers against the oracle's top-p selection (and its brute force pin): random
+    scores, many exact ties, the lognormal channel gains of the 370M-style inputs."""
+    import numpy as np
+    from oracle import calib
+    rng = np.random.default_rng(3)
+    cases = [(rng.random(1024), 0.10), (np.floor(rng.random(4096) * 7.0), 0.10), (np.ones(128), 0.10),
+             (np.exp(1.5 * rng.standard_normal(4096)) ** 2, 0.10), (rng.random(512), 0.03), (rng.random(96), 0.5)]
+    for scores, p in cases:
+        st, o, r = _plan_from_library(L, scores, p)
+        assert st == 0
+        want = calib.select_outliers(scores, p)
+        np.testing.assert_array_equal(o, want)
+        np.testing.assert_array_equal(np.sort(np.concatenate([o, r])), np.arange(scores.size))
+        assert np.all(np.diff(r) > 0)
+
+
+def test_select_outliers_errors(L):
+    import numpy as np
+    from bit_fully_quantized_amd import _lib
+    assert _plan_from_library(L, np.ones(100), 0.1)[0] == _lib.TJ2_ERR_SHAPE  # K not a multiple of 16
+    assert _plan_from_library(L, np.ones(128), 0.0)[0] == _lib.TJ2_ERR_ARG
+    assert _plan_from_library(L, np.ones(128), 1.0)[0] == _lib.TJ2_ERR_ARG
+    assert _plan_from_library(L, np.ones(16), 0.5)[0] == _lib.TJ2_ERR_SHAPE  # 16 of 16 channels: none left
+    bad = np.ones(128)
+    bad[5] = -1.0
+    assert _plan_from_library(L, bad, 0.1)[0] == _lib.TJ2_ERR_ARG
+    bad[5] = np.nan
+    assert _plan_from_library(L, bad, 0.1)[0] == _lib.TJ2_ERR_ARG
+
+
+def test_gemm_workspace_counts_both_segments(L):
+    # a two-segment product splits over the chunks of both segments
+    one = L.nvfp4_gemm_workspace_size(256, 128, 1024, 0)
+    two = L.nvfp4_gemm_workspace_size(256, 128, 912, 112)
+    assert two >= one > 0
 
 
 def test_qtensor_block_count_limit(L):

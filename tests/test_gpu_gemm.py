@@ -114,6 +114,34 @@ def test_gemm_output_views(I, J, ld, off):
     np.testing.assert_array_equal(got[:, J:], base[:, J:])
 
 
+@pytest.mark.parametrize("I,J,K1,K2,fmt2", [(256, 128, 912, 112, "fp8"), (200, 112, 4096, 4096, "nvfp4"),
+                                             (256, 256, 3968, 1024, "fp8")])
+def test_gemm_two_segments_split_k(I, J, K1, K2, fmt2):
+    """A two-segment product (NVFP4 x NVFP4 + a second segment) over few output tiles: the K split
+    runs over the chunks of both segments (a split boundary inside a segment, splits that lie in one
+    segment), with the workspace sized by both reductions."""
+    ga, gb, ra, rb = _operands(I, J, K1, seed=K1 + K2)
+    a_bits = synthetic.normal_bf16((I, K2), 1.0, 70)
+    b_f = synthetic.normal_f32((J, K2), 0.02, 71)
+    f2 = tj2.FP8 if fmt2 == "fp8" else tj2.NVFP4
+    a2 = tj2.quantize(H.bf16_to_device(a_bits), out_fmt=f2)
+    b2 = tj2.quantize(H.f32_to_device(b_f), out_fmt=f2)
+    ra2 = quant.quantize(H.bf16_values(a_bits), fmt=fmt2)
+    rb2 = quant.quantize(b_f, fmt=fmt2)
+    H.assert_q_equal(a2, ra2, what="A2")
+    H.assert_q_equal(b2, rb2, what="B2")
+    ws = tj2.gemm_workspace(I, J, K1, K2)
+    assert ws is not None and ws.numel() >= tj2.lib().nvfp4_gemm_workspace_size(I, J, K1 + K2, 0)
+    ref = ogemm.gemm_nt_f64(ra, rb) + ogemm.gemm_nt_f64(ra2, rb2)
+    c = tj2.gemm(ga, gb, a2, b2, workspace=ws).cpu().numpy()
+    assert H.rel_fro(c, ref) < 1e-5
+    c1 = tj2.gemm(ga, gb, a2, b2, split_k=False).cpu().numpy()
+    assert H.rel_fro(c1, ref) < 1e-5
+    # a workspace too small for the split is refused, not silently ignored
+    with pytest.raises(tj2.Tj2Error):
+        tj2.gemm(ga, gb, a2, b2, workspace=ws[: ws.numel() - 256])
+
+
 @pytest.mark.parametrize("I,J,K", [(256, 128, 8192), (200, 112, 4096), (16384 // 8, 112, 3072)])
 def test_gemm_split_k(I, J, K):
     """Few output tiles and a long reduction: K is split over workgroups, partials reduced in order."""

@@ -153,15 +153,33 @@ def test_osci_single_linear_config():
 
 
 def test_channel_sumsq():
+    """fp64 sums in a fixed order: within a few fp64 roundings of the oracle's sums, and the
+    same bits on a second run."""
     M, K = 1000, 1024
     gains = synthetic.lognormal_channel_gains(K, 1.5, 5)
     bits = synthetic.heavy_tailed_acts_bf16(M, gains, 6)
-    acc = torch.zeros(K, dtype=torch.float32, device="cuda")
-    tj2.channel_sumsq(H.bf16_to_device(bits), acc)
+    x = H.bf16_to_device(bits)
+    acc = torch.zeros(K, dtype=torch.float64, device="cuda")
+    tj2.channel_sumsq(x, acc)
     ref = calib.channel_scores([H.bf16_values(bits)])
-    np.testing.assert_allclose(acc.cpu().numpy(), ref, rtol=1e-5)
-    got = calib.select_outliers(acc.cpu().numpy().astype(np.float64), 0.1)
-    assert len(np.intersect1d(got, calib.select_outliers(ref, 0.1))) >= 110
+    np.testing.assert_allclose(acc.cpu().numpy(), ref, rtol=1e-13)
+    acc2 = torch.zeros(K, dtype=torch.float64, device="cuda")
+    tj2.channel_sumsq(x, acc2)
+    assert torch.equal(acc, acc2)
+
+
+@pytest.mark.parametrize("K,M", [(1024, 2048), (4096, 1024)])
+def test_calibrate_plan_equals_oracle(K, M):
+    """OutControl calibration through the library (GPU sums over 8 batches, tj2_select_outliers)
+    picks exactly the oracle's top 10% channels on the 370M-style heavy-tailed activations."""
+    from bit_fully_quantized_amd import outcontrol
+    gains = synthetic.lognormal_channel_gains(K, 1.5, 11)
+    batches = [synthetic.heavy_tailed_acts_bf16(M, gains, 100 + b) for b in range(8)]
+    plan = outcontrol.calibrate([H.bf16_to_device(b) for b in batches], 0.10)
+    want = calib.select_outliers(calib.channel_scores([H.bf16_values(b) for b in batches]), 0.10)
+    np.testing.assert_array_equal(plan.outliers.cpu().numpy(), want)
+    rest = plan.rest.cpu().numpy()
+    np.testing.assert_array_equal(np.sort(np.concatenate([want, rest])), np.arange(K))
 
 
 def test_mfma_peak_probe_result():
