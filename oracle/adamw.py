@@ -64,11 +64,12 @@ def adamw_step(W, m, v, g, opt: AdamW, bc1, bc2):
 
 
 def master_step(W, m, v, g, Q_prev, dQ, dM, opt: AdamW, bc1, bc2, tau: float, window_end: bool,
-                reset_enabled: bool, diag: dict | None = None):
+                reset_enabled: bool, diag: dict | None = None, plan=None):
     """Fused pass: AdamW, then OsciReset with W_prev = the pre-update master (oscillation
-    diagnostics as oracle.osci.osci_step).  Returns (W, m, v, Q_prev, dQ, dM, Wq, number of resets)."""
+    diagnostics and the OutControl plan as oracle.osci.osci_step).  Returns (W, m, v, Q_prev, dQ,
+    dM, codes, number of resets)."""
     W = np.asarray(W, dtype=f32)
     W1, m1, v1 = adamw_step(W, m, v, g, opt, bc1, bc2)
     st = OsciState(W.copy(), np.asarray(Q_prev, dtype=f32), np.asarray(dQ, dtype=f32), np.asarray(dM, dtype=f32))
-    W2, st2, Wq, n = osci_step(W1, st, tau, window_end, reset_enabled, diag)
+    W2, st2, Wq, n = osci_step(W1, st, tau, window_end, reset_enabled, diag, plan)
     return W2, m1, v1, st2.Q_prev, st2.dQ, st2.dM, Wq, n
