@@ -86,6 +86,7 @@ SIGNATURES = {
     "nvfp4_quantize": (I32, [P, I32, QP, I64, I64, P, I64, I32, I32, I32, U32, U64, U64, QP, P]),
     "nvfp4_gemm": (I32, [QP, QP, QP, QP, P, I32, I64, P, I32, P, SZ, P]),
     "nvfp4_gemm_workspace_size": (SZ, [I64, I64, I64, I64]),
+    "nvfp4_gemm_noalloc": (I32, [QP, QP, QP, QP, P, I32, I64, P, I32, P]),
     "nvfp4_gemm_outlier_cols": (I32, [QP, QP, QP, ctypes.POINTER(PlanC), P, I32, I64, I32, P, SZ, P]),
     "nvfp4_linear_fwd": (I32, [P, I64, I64, I64, P, QP, QP, ctypes.POINTER(PlanC), QP, QP, P, I32, P, SZ, P]),
     "nvfp4_linear_fwd_workspace_size": (SZ, [I64, I64, I64, I32]),

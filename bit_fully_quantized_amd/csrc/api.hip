@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -261,6 +262,52 @@ tj2_status check_plan(const tj2_outlier_plan* plan, int64_t K) {
   return TJ2_OK;
 }
 
+// Argument rules of nvfp4_gemm (and its no-allocation form).
+tj2_status check_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2, const tj2_qtensor* B2,
+                      const void* C, int32_t c_dtype, int64_t ldc, const int32_t* col_map, int32_t accumulate) {
+  if (!A || !B) return fail(TJ2_ERR_ARG, "A and B are required");
+  if ((A2 == nullptr) != (B2 == nullptr)) return fail(TJ2_ERR_ARG, "A2 and B2 must be given together");
+  TJ2_TRY(check_qtensor(A, "A", A->fmt, A->rows, A->len));
+  TJ2_TRY(check_qtensor(B, "B", B->fmt, B->rows, A->len));
+  if (A2) {
+    TJ2_TRY(check_qtensor(A2, "A2", A2->fmt, A->rows, A2->len));
+    TJ2_TRY(check_qtensor(B2, "B2", B2->fmt, B->rows, A2->len));
+  }
+  if (!C) return fail(TJ2_ERR_ARG, "C is NULL");
+  if (c_dtype != TJ2_F32 && c_dtype != TJ2_BF16) return fail(TJ2_ERR_ARG, "c_dtype must be TJ2_F32 or TJ2_BF16");
+  if (accumulate && c_dtype != TJ2_F32) return fail(TJ2_ERR_UNSUPPORTED, "accumulate needs an fp32 output");
+  if (!col_map && ldc < B->rows) return fail(TJ2_ERR_SHAPE, "ldc < J");
+  if (ldc <= 0) return fail(TJ2_ERR_SHAPE, "ldc must be positive");
+  if (A->rows > ((int64_t)1 << 24) * 128 || B->rows > ((int64_t)1 << 24) * 128) return fail(TJ2_ERR_SHAPE, "too many rows");
+  return TJ2_OK;
+}
+
+// Scratch of nvfp4_gemm_noalloc: the split-K partial sums of one product, in a
+// file-scope device array (each GPU the library runs on holds its own copy
+// until the process ends).  Host code never passes the array's name to a
+// kernel: it stands for a host-side shadow, not a device address.  The device
+// address is looked up once per device, with that device current, and kept.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+tj2_status scratch_address(void** out) {
+  int dev = -1;
+  TJ2_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TJ2_ERR_UNSUPPORTED, "device %d is beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    TJ2_TRY(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p) return fail(TJ2_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TJ2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -330,26 +377,27 @@ size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K, int64_t K2) {
 tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2, const tj2_qtensor* B2,
                       void* C, int32_t c_dtype, int64_t ldc, const int32_t* col_map, int32_t accumulate,
                       void* workspace, size_t ws_bytes, void* stream) {
-  if (!A || !B) return fail(TJ2_ERR_ARG, "A and B are required");
-  if (workspace && !aligned16(workspace)) return fail(TJ2_ERR_ALIGN, "workspace must be 16-byte aligned");
-  if ((A2 == nullptr) != (B2 == nullptr)) return fail(TJ2_ERR_ARG, "A2 and B2 must be given together");
-  TJ2_TRY(check_qtensor(A, "A", A->fmt, A->rows, A->len));
-  TJ2_TRY(check_qtensor(B, "B", B->fmt, B->rows, A->len));
-  if (A2) {
-    TJ2_TRY(check_qtensor(A2, "A2", A2->fmt, A->rows, A2->len));
-    TJ2_TRY(check_qtensor(B2, "B2", B2->fmt, B->rows, A2->len));
-  }
-  if (!C) return fail(TJ2_ERR_ARG, "C is NULL");
-  if (c_dtype != TJ2_F32 && c_dtype != TJ2_BF16) return fail(TJ2_ERR_ARG, "c_dtype must be TJ2_F32 or TJ2_BF16");
-  if (accumulate && c_dtype != TJ2_F32) return fail(TJ2_ERR_UNSUPPORTED, "accumulate needs an fp32 output");
-  if (!col_map && ldc < B->rows) return fail(TJ2_ERR_SHAPE, "ldc < J");
-  if (ldc <= 0) return fail(TJ2_ERR_SHAPE, "ldc must be positive");
-  if (A->rows > ((int64_t)1 << 24) * 128 || B->rows > ((int64_t)1 << 24) * 128) return fail(TJ2_ERR_SHAPE, "too many rows");
+  TJ2_TRY(check_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate));
   if (workspace) {
+    if (!aligned16(workspace)) return fail(TJ2_ERR_ALIGN, "workspace must be 16-byte aligned");
     const size_t need = gemm_workspace_bytes(A->rows, B->rows, gemm_chunks(A->len, A2 ? A2->len : 0));
     if (ws_bytes < need) return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
   }
   return run_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate, workspace, workspace ? ws_bytes : 0,
+                  (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
+}
+
+tj2_status nvfp4_gemm_noalloc(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2,
+                              const tj2_qtensor* B2, void* C, int32_t c_dtype, int64_t ldc, const int32_t* col_map,
+                              int32_t accumulate, void* stream) {
+  TJ2_TRY(check_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate));
+  const size_t need = gemm_workspace_bytes(A->rows, B->rows, gemm_chunks(A->len, A2 ? A2->len : 0));
+  if (need > kScratchBytes)
+    return fail(TJ2_ERR_SHAPE, "the K split of this product needs %zu bytes of scratch; nvfp4_gemm_noalloc holds %zu",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need) TJ2_TRY(scratch_address(&ws));
+  return run_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate, ws, ws ? kScratchBytes : 0,
                   (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
 }
 

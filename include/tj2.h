@@ -187,6 +187,25 @@ tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qten
 size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K, int64_t K2);
 
 /*
+ * nvfp4_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, kernels and results as nvfp4_gemm with a workspace of
+ * nvfp4_gemm_workspace_size(...) bytes, but the split-K partial sums live in a
+ * static device array of the library (32 MiB, one per GPU, held until the
+ * process ends), so the call allocates nothing.  A product whose K split needs
+ * more than 32 MiB of partial sums is refused with TJ2_ERR_SHAPE before any
+ * work (the 370M-style weight gradients need at most 32 MiB).  The array's
+ * device address is looked up on the first call on each device (the current
+ * device must be the stream's).  Every call on one GPU shares that array:
+ * calls that overlap on one GPU (different streams, or host threads) race and
+ * must be ordered by the caller.  Nothing in the array needs clearing: each
+ * split writes every partial sum before the reduction reads it.
+ */
+tj2_status nvfp4_gemm_noalloc(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2,
+                              const tj2_qtensor* B2, void* C, int32_t c_dtype, int64_t ldc,
+                              const int32_t* col_map, int32_t accumulate, void* stream);
+
+/*
  * Product whose output columns are split by a static outlier plan (OutControl,
  * TetraJet-v2 technical summary, section 2.C), in one launch: with
  * J = B->rows + B8->rows output columns,

@@ -281,3 +281,17 @@ def test_qtensor_block_count_limit(L):
     assert L.nvfp4_quantize(0x1000, _lib.BF16, None, 1 << 30, 1 << 30, None, 0, 0, 0, 0, 0, 0, 0, ctypes.byref(out),
                             None) == _lib.TJ2_ERR_SHAPE
     assert b"128-element blocks" in L.tj2_last_error()
+
+
+def test_noalloc_refuses_products_beyond_its_scratch(L):
+    # a 2048 x 3072 output over 16384 tokens splits 4 ways: 96 MiB of partial sums, more than the
+    # library's 32 MiB scratch; refused on the host before any device work
+    from bit_fully_quantized_amd import _lib
+    A = fake_q(_lib.NVFP4, 2048, 16384)
+    B = fake_q(_lib.NVFP4, 3072, 16384)
+    assert L.nvfp4_gemm_workspace_size(2048, 3072, 16384, 0) == 4 * 2048 * 3072 * 4
+    assert L.nvfp4_gemm_noalloc(ctypes.byref(A), ctypes.byref(B), None, None, 0x9000, _lib.F32, 3072, None, 0,
+                                None) == _lib.TJ2_ERR_SHAPE
+    assert b"scratch" in L.tj2_last_error()
+    assert L.nvfp4_gemm_noalloc(ctypes.byref(A), None, None, None, 0x9000, _lib.F32, 3072, None, 0,
+                                None) == _lib.TJ2_ERR_ARG
