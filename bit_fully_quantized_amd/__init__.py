@@ -19,7 +19,8 @@ from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI
 
 __all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "gemm_workspace", "linear_fwd", "linear_fwd_workspace",
            "linear_bwd", "linear_bwd_workspace", "osci_reset_step", "osci_reset_step_multi", "OsciBatch",
-           "master_update_step", "master_update_step_multi", "MasterBatch", "channel_sumsq", "select_outliers",
+           "master_update_step", "master_update_step_multi", "MasterBatch", "NextBwd", "bwd_operands", "channel_sumsq",
+           "select_outliers",
            "mfma_peak_probe", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32", "GROUP_ROW", "GROUP_COL",
            "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END", "RISK_BINS"]
 
@@ -253,17 +254,32 @@ def linear_bwd_workspace(M: int, N: int, K: int, n_outliers: int = 0, device="cu
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def bwd_operands(M: int, N: int, K: int, plan: OutlierPlan | None = None, device="cuda") -> dict:
+    """Buffers for the backward operands of one linear (tj2_bwd_operands): dYq, dYt, Wt, Xt (+ W8t, X8t)."""
+    no = plan.n if plan else 0
+    K1 = K - no
+    ops = {"dYq": QTensor(NVFP4, M, N, device), "dYt": QTensor(NVFP4, N, M, device),
+           "Wt": QTensor(NVFP4, K1, N, device), "Xt": QTensor(NVFP4, K1, M, device)}
+    if plan:
+        ops["W8t"] = QTensor(FP8, no, N, device)
+        ops["X8t"] = QTensor(FP8, no, M, device)
+    return ops
+
+
 def linear_bwd(dY: torch.Tensor, saved: dict, K: int, *, seed: int, offset: int, rht: bool = True,
                plan: OutlierPlan | None = None, dx_dtype=torch.bfloat16, keep_operands: bool = False,
-               workspace: torch.Tensor | None = None, dX: torch.Tensor | None = None,
-               dW: torch.Tensor | None = None):
-    """Returns (dX, dW, operands-or-None)."""
+               operands: dict | None = None, w_given: bool = False, workspace: torch.Tensor | None = None,
+               dX: torch.Tensor | None = None, dW: torch.Tensor | None = None):
+    """Returns (dX, dW, operands-or-None).
+
+    operands: buffers from bwd_operands() to hold the backward operands (returned); keep_operands
+    allocates them.  w_given: operands["Wt"] (and ["W8t"]) already hold this call's re-grouped
+    weights (written by master_update_step's next-backward output) and are used as they are."""
     _dense(dY, "dY", _BF16)
     if dY.dim() != 2:
         raise ValueError("dY must be 2-D")
     M, N = dY.shape
     no = plan.n if plan else 0
-    K1 = K - no
     if dX is None:
         dX = torch.empty((M, K), dtype=dx_dtype, device=dY.device)
     if dW is None:
@@ -271,17 +287,15 @@ def linear_bwd(dY: torch.Tensor, saved: dict, K: int, *, seed: int, offset: int,
     _dense(dX, "dX", (torch.bfloat16, torch.float32), shape=(M, K))
     _dense(dW, "dW", _F32, shape=(N, K))
     _dense(workspace, "workspace", (torch.uint8,), optional=True)
-    ops = None
+    if w_given and operands is None:
+        raise ValueError("w_given needs the operands holding Wt (and W8t)")
+    ops = operands if operands is not None else (bwd_operands(M, N, K, plan, dY.device) if keep_operands else None)
     opsc = None
-    if keep_operands:
-        ops = {"dYq": QTensor(NVFP4, M, N), "dYt": QTensor(NVFP4, N, M), "Wt": QTensor(NVFP4, K1, N),
-               "Xt": QTensor(NVFP4, K1, M)}
-        if plan:
-            ops["W8t"] = QTensor(FP8, no, N)
-            ops["X8t"] = QTensor(FP8, no, M)
+    if ops is not None:
         empty = _lib.QTensorC()
         opsc = _lib.BwdOperandsC(ops["dYq"].c(), ops["dYt"].c(), ops["Wt"].c(), ops["Xt"].c(),
-                                 ops["W8t"].c() if plan else empty, ops["X8t"].c() if plan else empty)
+                                 ops["W8t"].c() if plan else empty, ops["X8t"].c() if plan else empty,
+                                 1 if w_given else 0, 0)
     if workspace is None:
         workspace = linear_bwd_workspace(M, N, K, no, dY.device)
     pc = plan.c() if plan else None
@@ -308,42 +322,55 @@ def _diag(flips: torch.Tensor | None, risk_hist: torch.Tensor | None):
     return ctypes.byref(_lib.OsciDiagC(_ptr(flips), _ptr(risk_hist)))
 
 
+def _qref(q):
+    return ctypes.byref(q) if q is not None else None
+
+
 def osci_reset_step(W, W_prev, Q_prev, dQ, dM, *, mode: int, tau: float = 4.0, reset_enabled: bool = False,
                     Wq_out: QTensor | None = None, reset_count: torch.Tensor | None = None,
-                    flips: torch.Tensor | None = None, risk_hist: torch.Tensor | None = None) -> None:
+                    flips: torch.Tensor | None = None, risk_hist: torch.Tensor | None = None,
+                    plan: OutlierPlan | None = None, W8_out: QTensor | None = None) -> None:
     """OsciReset step; flips / risk_hist (optional device counters) receive the oscillation
     diagnostics: the number of elements whose quantized value changed, and at a window end the
-    risk histogram (RISK_BINS bins, see include/tj2.h)."""
+    risk histogram (RISK_BINS bins, see include/tj2.h).  With an outlier plan, Q(w) quantizes the
+    outlier channels to FP8 as the forward does; Wq_out is then [N, K - n] and W8_out [N, n]."""
     _dense(W, "W", _F32)
     N, K = W.shape
     for name, t in (("W_prev", W_prev), ("Q_prev", Q_prev), ("dQ", dQ), ("dM", dM)):
         _dense(t, name, _F32, shape=(N, K))
     _dense(reset_count, "reset_count", (torch.int64, torch.uint64), optional=True)
     wqc = Wq_out.c() if Wq_out is not None else None
+    w8c = W8_out.c() if W8_out is not None else None
+    pc = plan.c() if plan is not None else None
     st = lib().osci_reset_step(_ptr(W), _ptr(W_prev), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K, mode,
-                               ctypes.c_float(tau), 1 if reset_enabled else 0,
-                               ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count),
-                               _diag(flips, risk_hist), _stream())
+                               ctypes.c_float(tau), 1 if reset_enabled else 0, _qref(pc), _qref(wqc), _qref(w8c),
+                               _ptr(reset_count), _diag(flips, risk_hist), _stream())
     check("osci_reset_step", st)
 
 
 class OsciBatch:
-    """Descriptors of several OsciReset problems, built once: [(W, W_prev, Q_prev, dQ, dM, Wq_out or None), ...]
-    (the tensors must stay alive and in place while the batch is used)."""
+    """Descriptors of several OsciReset problems, built once: [(W, W_prev, Q_prev, dQ, dM, Wq_out or None
+    [, plan, W8_out]), ...] (the tensors must stay alive and in place while the batch is used)."""
 
     def __init__(self, tensors):
         self.tensors = list(tensors)
-        self._wq = []  # codes descriptors the array points to
+        self._keep = []  # descriptors the array points to
         self.arr = (_lib.OsciTensorC * len(self.tensors))()
-        for i, (W, W_prev, Q_prev, dQ, dM, wq) in enumerate(self.tensors):
+        for i, entry in enumerate(self.tensors):
+            W, W_prev, Q_prev, dQ, dM, wq = entry[:6]
+            plan, w8 = (entry[6], entry[7]) if len(entry) > 6 else (None, None)
             _dense(W, f"tensors[{i}].W", _F32)
             N, K = W.shape
             for name, t in (("W_prev", W_prev), ("Q_prev", Q_prev), ("dQ", dQ), ("dM", dM)):
                 _dense(t, f"tensors[{i}].{name}", _F32, shape=(N, K))
             wqc = wq.c() if wq is not None else None
-            self._wq.append(wqc)
+            w8c = w8.c() if w8 is not None else None
+            pc = plan.c() if plan is not None else None
+            self._keep += [wqc, w8c, pc]
             self.arr[i] = _lib.OsciTensorC(_ptr(W), _ptr(W_prev), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K,
-                                           ctypes.pointer(wqc) if wqc is not None else None)
+                                           ctypes.pointer(wqc) if wqc is not None else None,
+                                           ctypes.pointer(pc) if pc is not None else None,
+                                           ctypes.pointer(w8c) if w8c is not None else None)
 
     def __len__(self):
         return len(self.tensors)
@@ -360,14 +387,33 @@ def osci_reset_step_multi(tensors, *, mode: int, tau: float = 4.0, reset_enabled
     check("osci_reset_step_multi", st)
 
 
+@dataclass
+class NextBwd:
+    """The next backward's re-grouped weight operands that a master pass forms (tj2_next_bwd):
+    Wt [K1, N] NVFP4 and, with a plan, W8t [n, N] FP8, for nvfp4_linear_bwd at (seed, offset)."""
+    Wt: QTensor
+    W8t: QTensor | None
+    seed: int
+    offset: int
+    rht: bool = True
+
+    def c(self):
+        self._wt = self.Wt.c()
+        self._w8t = self.W8t.c() if self.W8t is not None else None
+        return _lib.NextBwdC(ctypes.pointer(self._wt), ctypes.pointer(self._w8t) if self._w8t is not None else None,
+                             self.seed, self.offset, 1 if self.rht else 0, 0)
+
+
 def master_update_step(W, m, v, grad, Q_prev, dQ, dM, *, lr: float, bias_correction1: float,
                        bias_correction2: float, beta1: float = 0.9, beta2: float = 0.95, eps: float = 1e-8,
                        weight_decay: float = 0.1, mode: int = OSCI_ACCUM, tau: float = 4.0,
                        reset_enabled: bool = False, Wq_out: QTensor | None = None,
                        reset_count: torch.Tensor | None = None, flips: torch.Tensor | None = None,
-                       risk_hist: torch.Tensor | None = None) -> None:
+                       risk_hist: torch.Tensor | None = None, plan: OutlierPlan | None = None,
+                       W8_out: QTensor | None = None, next_bwd: NextBwd | None = None) -> None:
     """Fused master-weight pass: AdamW on W, then OsciReset (ACCUM / WINDOW_END) with the
-    pre-update master as W_prev, then the forward codes (Wq_out); diagnostics as osci_reset_step."""
+    pre-update master as W_prev, then the forward codes (Wq_out, W8_out with a plan) and, with
+    next_bwd, the next backward's re-grouped weights; diagnostics as osci_reset_step."""
     _dense(W, "W", _F32)
     N, K = W.shape
     for name, t in (("m", m), ("v", v), ("grad", grad), ("Q_prev", Q_prev), ("dQ", dQ), ("dM", dM)):
@@ -375,31 +421,48 @@ def master_update_step(W, m, v, grad, Q_prev, dQ, dM, *, lr: float, bias_correct
     _dense(reset_count, "reset_count", (torch.int64, torch.uint64), optional=True)
     ap = _lib.AdamWC(lr, beta1, beta2, eps, weight_decay, bias_correction1, bias_correction2)
     wqc = Wq_out.c() if Wq_out is not None else None
+    w8c = W8_out.c() if W8_out is not None else None
+    pc = plan.c() if plan is not None else None
+    nx = next_bwd.c() if next_bwd is not None else None
     st = lib().master_update_step(_ptr(W), _ptr(m), _ptr(v), _ptr(grad), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K,
-                                  ctypes.byref(ap), mode, ctypes.c_float(tau), 1 if reset_enabled else 0,
-                                  ctypes.byref(wqc) if wqc is not None else None, _ptr(reset_count),
-                                  _diag(flips, risk_hist), _stream())
+                                  ctypes.byref(ap), mode, ctypes.c_float(tau), 1 if reset_enabled else 0, _qref(pc),
+                                  _qref(wqc), _qref(w8c), _qref(nx), _ptr(reset_count), _diag(flips, risk_hist),
+                                  _stream())
     check("master_update_step", st)
-
 
 
 class MasterBatch:
     """Descriptors of several fused master-weight problems, built once:
-    [(W, m, v, grad, Q_prev, dQ, dM, Wq_out or None), ...] (the tensors must stay alive and in place)."""
+    [(W, m, v, grad, Q_prev, dQ, dM, Wq_out or None [, plan, W8_out, NextBwd or None]), ...]
+    (the tensors must stay alive and in place)."""
 
     def __init__(self, tensors):
         self.tensors = list(tensors)
-        self._wq = []
+        self._keep = []
         self.arr = (_lib.MasterTensorC * len(self.tensors))()
-        for i, (W, m, v, g, Q_prev, dQ, dM, wq) in enumerate(self.tensors):
+        for i, entry in enumerate(self.tensors):
+            W, m, v, g, Q_prev, dQ, dM, wq = entry[:8]
+            plan, w8, nxt = (entry[8], entry[9], entry[10]) if len(entry) > 8 else (None, None, None)
             _dense(W, f"tensors[{i}].W", _F32)
             N, K = W.shape
             for name, t in (("m", m), ("v", v), ("grad", g), ("Q_prev", Q_prev), ("dQ", dQ), ("dM", dM)):
                 _dense(t, f"tensors[{i}].{name}", _F32, shape=(N, K))
             wqc = wq.c() if wq is not None else None
-            self._wq.append(wqc)
-            self.arr[i] = _lib.MasterTensorC(_ptr(W), _ptr(m), _ptr(v), _ptr(g), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N, K,
-                                             ctypes.pointer(wqc) if wqc is not None else None)
+            w8c = w8.c() if w8 is not None else None
+            pc = plan.c() if plan is not None else None
+            nx = nxt.c() if nxt is not None else None
+            self._keep += [wqc, w8c, pc, nx, nxt]
+            self.arr[i] = _lib.MasterTensorC(_ptr(W), _ptr(m), _ptr(v), _ptr(g), _ptr(Q_prev), _ptr(dQ), _ptr(dM), N,
+                                             K, ctypes.pointer(wqc) if wqc is not None else None,
+                                             ctypes.pointer(pc) if pc is not None else None,
+                                             ctypes.pointer(w8c) if w8c is not None else None,
+                                             ctypes.pointer(nx) if nx is not None else None)
+
+    def set_next_offsets(self, offsets):
+        """Re-point the next-backward operands at new Philox offsets (one per matrix, in order)."""
+        for i, off in enumerate(offsets):
+            if self.arr[i].next:
+                self.arr[i].next.contents.offset = off
 
     def __len__(self):
         return len(self.tensors)
@@ -418,6 +481,7 @@ def master_update_step_multi(tensors, *, lr: float, bias_correction1: float, bia
                                         1 if reset_enabled else 0, _ptr(reset_count), _diag(flips, risk_hist),
                                         _stream())
     check("master_update_step_multi", st)
+
 
 def mfma_peak_probe(out: torch.Tensor, iters: int) -> float:
     """Measurement helper from libtj2_measure (not part of the path): an MFMA-only loop in

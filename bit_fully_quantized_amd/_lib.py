@@ -37,7 +37,7 @@ class PlanC(ctypes.Structure):
 
 class BwdOperandsC(ctypes.Structure):
     _fields_ = [("dYq", QTensorC), ("dYt", QTensorC), ("Wt", QTensorC), ("Xt", QTensorC), ("W8t", QTensorC),
-                ("X8t", QTensorC)]
+                ("X8t", QTensorC), ("w_given", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Tj2Error(RuntimeError):
@@ -70,13 +70,21 @@ class OsciDiagC(ctypes.Structure):
 RISK_BINS = 32
 
 
+PLANP = ctypes.POINTER(PlanC)
+
+
+class NextBwdC(ctypes.Structure):
+    _fields_ = [("Wt", QP), ("W8t", QP), ("seed", U64), ("offset", U64), ("rht", I32), ("reserved", I32)]
+
+
 class OsciTensorC(ctypes.Structure):
-    _fields_ = [("W", P), ("W_prev", P), ("Q_prev", P), ("dQ", P), ("dM", P), ("N", I64), ("K", I64), ("Wq_out", QP)]
+    _fields_ = [("W", P), ("W_prev", P), ("Q_prev", P), ("dQ", P), ("dM", P), ("N", I64), ("K", I64), ("Wq_out", QP),
+                ("plan", PLANP), ("W8_out", QP)]
 
 
 class MasterTensorC(ctypes.Structure):
     _fields_ = [("W", P), ("m", P), ("v", P), ("grad", P), ("Q_prev", P), ("dQ", P), ("dM", P), ("N", I64), ("K", I64),
-                ("Wq_out", QP)]
+                ("Wq_out", QP), ("plan", PLANP), ("W8_out", QP), ("next", ctypes.POINTER(NextBwdC))]
 
 SIGNATURES = {
     "tj2_last_error": (ctypes.c_char_p, []),
@@ -93,14 +101,14 @@ SIGNATURES = {
     "nvfp4_linear_bwd": (I32, [P, I64, I64, I64, QP, QP, QP, QP, ctypes.POINTER(PlanC), I32, U64, U64, P, I32, P,
                                ctypes.POINTER(BwdOperandsC), P, SZ, P]),
     "nvfp4_linear_bwd_workspace_size": (SZ, [I64, I64, I64, I32]),
-    "osci_reset_step": (I32, [P, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, QP, P, ctypes.POINTER(OsciDiagC),
-                              P]),
+    "osci_reset_step": (I32, [P, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, PLANP, QP, QP, P,
+                              ctypes.POINTER(OsciDiagC), P]),
     "osci_reset_step_multi": (I32, [ctypes.POINTER(OsciTensorC), I32, I32, ctypes.c_float, I32, P,
                                     ctypes.POINTER(OsciDiagC), P]),
     "master_update_step_multi": (I32, [ctypes.POINTER(MasterTensorC), I32, ctypes.POINTER(AdamWC), I32,
                                        ctypes.c_float, I32, P, ctypes.POINTER(OsciDiagC), P]),
     "master_update_step": (I32, [P, P, P, P, P, P, P, I64, I64, ctypes.POINTER(AdamWC), I32, ctypes.c_float, I32,
-                                 QP, P, ctypes.POINTER(OsciDiagC), P]),
+                                 PLANP, QP, QP, ctypes.POINTER(NextBwdC), P, ctypes.POINTER(OsciDiagC), P]),
     "tj2_channel_sumsq_workspace_size": (SZ, [I64, I64]),
     "tj2_channel_sumsq": (I32, [P, I64, I64, P, P, SZ, P]),
     "tj2_select_outliers": (I32, [P, I64, ctypes.c_double, P, P, ctypes.POINTER(I32)]),

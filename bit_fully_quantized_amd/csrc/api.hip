@@ -509,6 +509,7 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
     uint8_t* cur = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
     gemm_ws = gws ? cur : nullptr;
     cur += gws;
+    memset(&local, 0, sizeof(local));
     local.dYq = carve(cur, TJ2_NVFP4, M, N);
     local.dYt = carve(cur, TJ2_NVFP4, N, M);
     local.Wt = carve(cur, TJ2_NVFP4, K1, N);
@@ -537,11 +538,14 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
   // the small FP8 slices first so their latency hides behind the large problems
   QuantParams cols[kColMultiMax];
   int nc = 0;
+  const bool w_given = ops && ops->w_given;  // the re-grouped weights come from the master pass
   if (plan) {
     cols[nc++] = quant_params(nullptr, TJ2_FP8, X8, M, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 5, &o->X8t);
-    cols[nc++] = quant_params(nullptr, TJ2_FP8, W8, N, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 4, &o->W8t);
+    if (!w_given)
+      cols[nc++] = quant_params(nullptr, TJ2_FP8, W8, N, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 4, &o->W8t);
   }
-  cols[nc++] = quant_params(nullptr, TJ2_NVFP4, Wq, N, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 1, &o->Wt);
+  if (!w_given)
+    cols[nc++] = quant_params(nullptr, TJ2_NVFP4, Wq, N, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 1, &o->Wt);
   cols[nc++] = quant_params(nullptr, TJ2_NVFP4, Xq, M, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 3, &o->Xt);
   cols[nc++] = quant_params(dY, TJ2_BF16, nullptr, M, N, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 2, &o->dYt);
   TJ2_TRY(hip_check(launch_quant_col_multi(cols, nc, s), "column quantize launch"));
@@ -559,41 +563,105 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
 
 namespace {
 
-// Checked launch parameters of one fused master-weight problem (master_update_step's argument rules).
-tj2_status master_params(float* W, float* m, float* v, const float* grad, float* Q_prev, float* dQ, float* dM,
-                         int64_t N, int64_t K, const tj2_adamw_params* adam, int32_t mode, float tau,
-                         int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
-                         const tj2_osci_diag* diag, MasterParams* out) {
-  if (!W || !m || !v || !grad || !Q_prev || !dQ || !dM) return fail(TJ2_ERR_ARG, "W, m, v, grad and the state arrays are required");
-  if (!adam) return fail(TJ2_ERR_ARG, "adam parameters are required");
-  if (!aligned16(W) || !aligned16(m) || !aligned16(v) || !aligned16(grad) || !aligned16(Q_prev) || !aligned16(dQ) ||
-      !aligned16(dM))
+// Checked per-matrix parameters of OsciReset / the fused master pass.
+tj2_status osci_problem(float* W, float* W_prev, float* m, float* v, const float* grad, float* Q_prev, float* dQ,
+                        float* dM, int64_t N, int64_t K, bool master, const tj2_outlier_plan* plan,
+                        tj2_qtensor* Wq_out, tj2_qtensor* W8_out, OsciProblem* out) {
+  if (!W || !Q_prev || !dQ || !dM || (master ? (!m || !v || !grad) : !W_prev))
+    return fail(TJ2_ERR_ARG, master ? "W, m, v, grad and the state arrays are required"
+                                    : "W and the state arrays are required");
+  if (!aligned16(W) || !aligned16(Q_prev) || !aligned16(dQ) || !aligned16(dM) ||
+      (master ? (!aligned16(m) || !aligned16(v) || !aligned16(grad)) : !aligned16(W_prev)))
     return fail(TJ2_ERR_ALIGN, "arrays must be 16-byte aligned");
   if (N <= 0 || N > ((int64_t)1 << 30)) return fail(TJ2_ERR_SHAPE, "N must be positive");
   TJ2_TRY(check_dims(K, "K"));
-  if (mode != TJ2_OSCI_ACCUM && mode != TJ2_OSCI_WINDOW_END) return fail(TJ2_ERR_ARG, "mode must be ACCUM or WINDOW_END");
-  if (!(tau >= 0.0f)) return fail(TJ2_ERR_ARG, "tau must be >= 0");
-  const int64_t nb = (K + 127) / 128;
-  if (N * nb * 16 >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
-  MasterParams& p = *out;
+  TJ2_TRY(check_plan(plan, K));
+  const int64_t no = plan ? plan->n_outliers : 0, K1 = K - no;
+  const int64_t hpr1 = (K1 + 127) / 128 * 16, hpr = hpr1 + (no + 127) / 128 * 16;  // half groups per row
+  if (N * hpr >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
+  if (W8_out && !plan) return fail(TJ2_ERR_ARG, "W8_out needs an outlier plan");
+  OsciProblem& p = *out;
   memset(&p, 0, sizeof(p));
-  p.W = W; p.m = m; p.v = v; p.grad = grad; p.Q_prev = Q_prev; p.dQ = dQ; p.dM = dM;
-  p.N = N; p.K = K;
-  p.lr = adam->lr; p.beta1 = adam->beta1; p.beta2 = adam->beta2; p.eps = adam->eps;
-  p.weight_decay = adam->weight_decay; p.bc1 = adam->bias_correction1; p.bc2 = adam->bias_correction2;
-  p.window_end = mode == TJ2_OSCI_WINDOW_END ? 1 : 0;
-  p.tau = tau;
-  p.reset_enabled = reset_enabled ? 1 : 0;
-  if (Wq_out) {
-    TJ2_TRY(check_qtensor(Wq_out, "Wq_out", TJ2_NVFP4, N, K));
-    p.wq = make_view(*Wq_out);
-    p.have_wq = 1;
-  }
-  p.reset_count = reinterpret_cast<unsigned long long*>(reset_count);
-  TJ2_TRY(diag_pointers(diag, &p.flips, &p.risk_hist));
+  p.W = W; p.W_prev = W_prev; p.Q_prev = Q_prev; p.dQ = dQ; p.dM = dM;
+  p.m = m; p.v = v; p.grad = grad;
+  p.N = (int32_t)N; p.K = (int32_t)K;
+  p.rest = plan ? plan->rest : nullptr;
+  p.outl = plan ? plan->outliers : nullptr;
+  p.K1 = (int32_t)K1; p.no = (int32_t)no;
+  p.hpr = (int32_t)hpr; p.hpr1 = (int32_t)hpr1;
+  if (Wq_out) TJ2_TRY(check_qtensor(Wq_out, "Wq_out", TJ2_NVFP4, N, K1));
+  if (W8_out) TJ2_TRY(check_qtensor(W8_out, "W8_out", TJ2_FP8, N, no));
+  p.wq = make_qout(Wq_out);
+  p.w8 = make_qout(W8_out);
   return TJ2_OK;
 }
 
+tj2_status osci_shared(int32_t mode, float tau, int32_t reset_enabled, bool master, uint64_t* reset_count,
+                       const tj2_osci_diag* diag, const tj2_adamw_params* adam, OsciShared* out) {
+  if (master) {
+    if (!adam) return fail(TJ2_ERR_ARG, "adam parameters are required");
+    if (mode != TJ2_OSCI_ACCUM && mode != TJ2_OSCI_WINDOW_END) return fail(TJ2_ERR_ARG, "mode must be ACCUM or WINDOW_END");
+  } else if (mode != TJ2_OSCI_INIT && mode != TJ2_OSCI_ACCUM && mode != TJ2_OSCI_WINDOW_END) {
+    return fail(TJ2_ERR_ARG, "bad mode %d", mode);
+  }
+  if (!(tau >= 0.0f)) return fail(TJ2_ERR_ARG, "tau must be >= 0");
+  OsciShared& c = *out;
+  memset(&c, 0, sizeof(c));
+  c.mode = mode;
+  c.tau = tau;
+  c.reset_enabled = reset_enabled ? 1 : 0;
+  if (master) {
+    c.lr = adam->lr; c.beta1 = adam->beta1; c.beta2 = adam->beta2; c.eps = adam->eps;
+    c.weight_decay = adam->weight_decay; c.bc1 = adam->bias_correction1; c.bc2 = adam->bias_correction2;
+  }
+  c.reset_count = reinterpret_cast<unsigned long long*>(reset_count);
+  return diag_pointers(diag, &c.flips, &c.risk_hist);
+}
+
+// The next backward's re-grouped weight operands from the codes the pass wrote:
+// W-hat grouped along N (RHT with the dX mask, SR at offset + 1) and its FP8
+// outlier rows (offset + 4), exactly as nvfp4_linear_bwd would form them.
+tj2_status check_next(const tj2_next_bwd* nx, const OsciProblem& p, const tj2_qtensor* Wq_out,
+                      const tj2_qtensor* W8_out) {
+  if (!nx) return TJ2_OK;
+  if (!nx->Wt) return fail(TJ2_ERR_ARG, "next->Wt is required");
+  if (!Wq_out || (p.rest && !W8_out)) return fail(TJ2_ERR_ARG, "next needs Wq_out (and W8_out with a plan)");
+  if (p.N % 16) return fail(TJ2_ERR_SHAPE, "next: N = %d must be a multiple of 16 for the re-grouping", p.N);
+  TJ2_TRY(check_qtensor(nx->Wt, "next->Wt", TJ2_NVFP4, p.K1, p.N));
+  if (p.rest) TJ2_TRY(check_qtensor(nx->W8t, "next->W8t", TJ2_FP8, p.no, p.N));
+  return TJ2_OK;
+}
+
+tj2_status launch_next(const std::vector<const tj2_next_bwd*>& nexts, const std::vector<const tj2_qtensor*>& wqs,
+                       const std::vector<const tj2_qtensor*>& w8s, hipStream_t s) {
+  std::vector<QuantParams> qp[2];  // by Hadamard switch (one launch shares it)
+  for (size_t i = 0; i < nexts.size(); ++i) {
+    const tj2_next_bwd* nx = nexts[i];
+    if (!nx) continue;
+    const int r = nx->rht ? 1 : 0;
+    const uint32_t mdx = r ? tj2_rht_signs(nx->seed, nx->offset + 0) : 0u;
+    const tj2_qtensor* wq = wqs[i];
+    qp[r].push_back(quant_params(nullptr, TJ2_NVFP4, wq, wq->rows, wq->len, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx,
+                                 nx->seed, nx->offset + 1, nx->Wt));
+    if (w8s[i])
+      qp[r].push_back(quant_params(nullptr, TJ2_FP8, w8s[i], w8s[i]->rows, w8s[i]->len, nullptr, 0, TJ2_GROUP_COL,
+                                   TJ2_SR, r, mdx, nx->seed, nx->offset + 4, nx->W8t));
+  }
+  for (int r = 0; r < 2; ++r)
+    for (size_t i = 0; i < qp[r].size(); i += kColMultiMax) {
+      const int cnt = (int)std::min<size_t>(kColMultiMax, qp[r].size() - i);
+      TJ2_TRY(hip_check(launch_quant_col_multi(qp[r].data() + i, cnt, s), "re-grouping launch"));
+    }
+  return TJ2_OK;
+}
+
+tj2_status run_osci(const OsciShared& c, const std::vector<OsciProblem>& ps, bool master, hipStream_t s) {
+  for (size_t i = 0; i < ps.size(); i += kOsciMultiMax) {
+    const int cnt = (int)std::min<size_t>(kOsciMultiMax, ps.size() - i);
+    TJ2_TRY(hip_check(launch_osci_multi(c, ps.data() + i, cnt, master, s), master ? "master update launch" : "osci launch"));
+  }
+  return TJ2_OK;
+}
 
 }  // namespace
 
@@ -601,92 +669,71 @@ extern "C" {
 
 tj2_status master_update_step(float* W, float* m, float* v, const float* grad, float* Q_prev, float* dQ, float* dM,
                               int64_t N, int64_t K, const tj2_adamw_params* adam, int32_t mode, float tau,
-                              int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
+                              int32_t reset_enabled, const tj2_outlier_plan* plan, tj2_qtensor* Wq_out,
+                              tj2_qtensor* W8_out, const tj2_next_bwd* next, uint64_t* reset_count,
                               const tj2_osci_diag* diag, void* stream) {
-  MasterParams p;
-  TJ2_TRY(master_params(W, m, v, grad, Q_prev, dQ, dM, N, K, adam, mode, tau, reset_enabled, Wq_out, reset_count,
-                        diag, &p));
-  TJ2_TRY(hip_check(launch_master(p, (hipStream_t)stream), "master update launch"));
-  return ok();
+  tj2_master_tensor t;
+  memset(&t, 0, sizeof(t));
+  t.W = W; t.m = m; t.v = v; t.grad = grad; t.Q_prev = Q_prev; t.dQ = dQ; t.dM = dM; t.N = N; t.K = K;
+  t.Wq_out = Wq_out; t.plan = plan; t.W8_out = W8_out; t.next = next;
+  const tj2_status st = master_update_step_multi(&t, 1, adam, mode, tau, reset_enabled, reset_count, diag, stream);
+  if (st != TJ2_OK && strncmp(tj2_last_error(), "tensors[0]: ", 12) == 0) g_err = g_err.substr(12);
+  return st;
 }
 
 tj2_status master_update_step_multi(const tj2_master_tensor* tensors, int32_t n, const tj2_adamw_params* adam,
                                     int32_t mode, float tau, int32_t reset_enabled, uint64_t* reset_count,
                                     const tj2_osci_diag* diag, void* stream) {
   if (!tensors || n < 1) return fail(TJ2_ERR_ARG, "tensors must list at least one matrix");
-  std::vector<MasterParams> ps((size_t)n);
+  OsciShared c;
+  TJ2_TRY(osci_shared(mode, tau, reset_enabled, true, reset_count, diag, adam, &c));
+  std::vector<OsciProblem> ps((size_t)n);
+  std::vector<const tj2_next_bwd*> nexts((size_t)n);
+  std::vector<const tj2_qtensor*> wqs((size_t)n), w8s((size_t)n);
+  bool any_next = false;
   for (int32_t i = 0; i < n; ++i) {
     const tj2_master_tensor& x = tensors[i];
-    const tj2_status st = master_params(x.W, x.m, x.v, x.grad, x.Q_prev, x.dQ, x.dM, x.N, x.K, adam, mode, tau,
-                                        reset_enabled, x.Wq_out, reset_count, diag, &ps[(size_t)i]);
+    tj2_status st = osci_problem(x.W, nullptr, x.m, x.v, x.grad, x.Q_prev, x.dQ, x.dM, x.N, x.K, true, x.plan,
+                                 x.Wq_out, x.W8_out, &ps[(size_t)i]);
+    if (st == TJ2_OK) st = check_next(x.next, ps[(size_t)i], x.Wq_out, x.W8_out);
     if (st != TJ2_OK) return fail(st, "tensors[%d]: %s", i, std::string(tj2_last_error()).c_str());
+    nexts[(size_t)i] = x.next;
+    wqs[(size_t)i] = x.Wq_out;
+    w8s[(size_t)i] = x.plan ? x.W8_out : nullptr;
+    any_next = any_next || x.next;
   }
-  for (int32_t i = 0; i < n; i += kOsciMultiMax) {
-    const int cnt = n - i < kOsciMultiMax ? n - i : kOsciMultiMax;
-    TJ2_TRY(hip_check(launch_master_multi(ps.data() + i, cnt, (hipStream_t)stream), "master update launch"));
-  }
+  TJ2_TRY(run_osci(c, ps, true, (hipStream_t)stream));
+  if (any_next) TJ2_TRY(launch_next(nexts, wqs, w8s, (hipStream_t)stream));
   return ok();
 }
-
-}  // extern "C"
-
-namespace {
-
-// Checked launch parameters of one OsciReset problem (osci_reset_step's argument rules).
-tj2_status osci_params(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N, int64_t K,
-                       int32_t mode, float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
-                       const tj2_osci_diag* diag, OsciParams* out) {
-  if (!W || !W_prev || !Q_prev || !dQ || !dM) return fail(TJ2_ERR_ARG, "W and the state arrays are required");
-  if (!aligned16(W) || !aligned16(W_prev) || !aligned16(Q_prev) || !aligned16(dQ) || !aligned16(dM))
-    return fail(TJ2_ERR_ALIGN, "arrays must be 16-byte aligned");
-  if (N <= 0 || N > ((int64_t)1 << 30)) return fail(TJ2_ERR_SHAPE, "N must be positive");
-  TJ2_TRY(check_dims(K, "K"));
-  if (mode != TJ2_OSCI_INIT && mode != TJ2_OSCI_ACCUM && mode != TJ2_OSCI_WINDOW_END) return fail(TJ2_ERR_ARG, "bad mode %d", mode);
-  if (!(tau >= 0.0f)) return fail(TJ2_ERR_ARG, "tau must be >= 0");
-  const int64_t nb = (K + 127) / 128;
-  if (N * nb * 16 >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
-  OsciParams& p = *out;
-  memset(&p, 0, sizeof(p));
-  p.W = W; p.W_prev = W_prev; p.Q_prev = Q_prev; p.dQ = dQ; p.dM = dM;
-  p.N = N; p.K = K; p.mode = mode; p.tau = tau; p.reset_enabled = reset_enabled ? 1 : 0;
-  if (Wq_out) {
-    TJ2_TRY(check_qtensor(Wq_out, "Wq_out", TJ2_NVFP4, N, K));
-    p.wq = make_view(*Wq_out);
-    p.have_wq = 1;
-  }
-  p.reset_count = reinterpret_cast<unsigned long long*>(reset_count);
-  TJ2_TRY(diag_pointers(diag, &p.flips, &p.risk_hist));
-  return TJ2_OK;
-}
-
-}  // namespace
-
-extern "C" {
 
 tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N, int64_t K,
-                           int32_t mode, float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
+                           int32_t mode, float tau, int32_t reset_enabled, const tj2_outlier_plan* plan,
+                           tj2_qtensor* Wq_out, tj2_qtensor* W8_out, uint64_t* reset_count,
                            const tj2_osci_diag* diag, void* stream) {
-  OsciParams p;
-  TJ2_TRY(osci_params(W, W_prev, Q_prev, dQ, dM, N, K, mode, tau, reset_enabled, Wq_out, reset_count, diag, &p));
-  TJ2_TRY(hip_check(launch_osci(p, (hipStream_t)stream), "osci launch"));
-  return ok();
+  tj2_osci_tensor t;
+  memset(&t, 0, sizeof(t));
+  t.W = W; t.W_prev = W_prev; t.Q_prev = Q_prev; t.dQ = dQ; t.dM = dM; t.N = N; t.K = K;
+  t.Wq_out = Wq_out; t.plan = plan; t.W8_out = W8_out;
+  const tj2_status st = osci_reset_step_multi(&t, 1, mode, tau, reset_enabled, reset_count, diag, stream);
+  if (st != TJ2_OK && strncmp(tj2_last_error(), "tensors[0]: ", 12) == 0) g_err = g_err.substr(12);
+  return st;
 }
 
 tj2_status osci_reset_step_multi(const tj2_osci_tensor* tensors, int32_t n, int32_t mode, float tau,
                                  int32_t reset_enabled, uint64_t* reset_count, const tj2_osci_diag* diag,
                                  void* stream) {
   if (!tensors || n < 1) return fail(TJ2_ERR_ARG, "tensors must list at least one matrix");
-  std::vector<OsciParams> ps((size_t)n);
+  OsciShared c;
+  TJ2_TRY(osci_shared(mode, tau, reset_enabled, false, reset_count, diag, nullptr, &c));
+  std::vector<OsciProblem> ps((size_t)n);
   for (int32_t i = 0; i < n; ++i) {
     const tj2_osci_tensor& x = tensors[i];
-    const tj2_status st = osci_params(x.W, x.W_prev, x.Q_prev, x.dQ, x.dM, x.N, x.K, mode, tau, reset_enabled,
-                                      x.Wq_out, reset_count, diag, &ps[(size_t)i]);
+    const tj2_status st = osci_problem(x.W, x.W_prev, nullptr, nullptr, nullptr, x.Q_prev, x.dQ, x.dM, x.N, x.K,
+                                       false, x.plan, x.Wq_out, x.W8_out, &ps[(size_t)i]);
     if (st != TJ2_OK) return fail(st, "tensors[%d]: %s", i, std::string(tj2_last_error()).c_str());
   }
-  for (int32_t i = 0; i < n; i += kOsciMultiMax) {
-    const int m = n - i < kOsciMultiMax ? n - i : kOsciMultiMax;
-    TJ2_TRY(hip_check(launch_osci_multi(ps.data() + i, m, (hipStream_t)stream), "osci launch"));
-  }
+  TJ2_TRY(run_osci(c, ps, false, (hipStream_t)stream));
   return ok();
 }
 

@@ -53,20 +53,25 @@ __device__ __forceinline__ float max16_lanes(float x) {
   return __uint_as_float(xi);
 }
 
-// Forward quantization of this lane's half (8 elements) of a 16-element group:
-// the group's amax pairs the two lanes, the outer block's spans 16 lanes.
-// Returns the lane's 8 codes (one word), the group's E4M3 code and S, and the
-// dequantized values Q(w).
-__device__ __forceinline__ void fwd_quant8(const float w[8], bool valid, uint32_t* code, uint32_t* s_code, float* S,
-                                           float q[8]) {
+// Amaxes of this lane's half (8 elements) of a 16-element group: the group's
+// (the lane pair) and the 128-element outer block's (16 lanes).  Called in
+// uniform control flow (DPP reads the neighbouring lanes).
+__device__ __forceinline__ void half_amax(const float w[8], bool valid, float* a_j, float* a_o) {
   float a_h = 0.0f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) a_h = fmaxf(a_h, fabsf(w[t]));
   if (!valid) a_h = 0.0f;
   uint32_t ai = __float_as_uint(a_h);
   ai = max(ai, (uint32_t)__builtin_amdgcn_mov_dpp((int)ai, 0xB1, 0xF, 0xF, false));  // the group's other half
-  const float a_j = __uint_as_float(ai);
-  const float a_o = max16_lanes(a_j);
+  *a_j = __uint_as_float(ai);
+  *a_o = max16_lanes(*a_j);
+}
+
+// Forward NVFP4 quantization of this lane's 8 elements given the amaxes:
+// the lane's 8 codes (one word), the group's E4M3 code and S, and the
+// dequantized values Q(w).
+__device__ __forceinline__ void nvfp4_encode8(const float w[8], bool valid, float a_j, float a_o, uint32_t* code,
+                                              uint32_t* s_code, float* S, float q[8]) {
   GroupScale g = nvfp4_group_scale(a_o, a_j);
   const float s = e4m3_decode(g.s_code);
   float y[8];
@@ -92,6 +97,54 @@ __device__ __forceinline__ void fwd_quant8(const float w[8], bool valid, uint32_
   *S = g.S;
 }
 
+// Forward FP8 quantization (OutControl channels, technical summary section
+// 2.C: E4M3, one FP32 scale a_o / 448 per 128 elements, round to nearest
+// even) of this lane's 8 elements: two words of codes (element t in byte t)
+// and the dequantized values e * S8.
+__device__ __forceinline__ void fp8_encode8(const float w[8], bool valid, float a_o, uint32_t code[2], float* S,
+                                            float q[8]) {
+  typedef short short2_t __attribute__((ext_vector_type(2)));
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  float S8 = 0.0f, inv = 0.0f;
+  if (a_o >= kTiny) {
+    S8 = a_o / kFp8Div;
+    inv = 1.0f / S8;
+  }
+  float y[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) y[t] = fp8_scaled(valid ? w[t] : 0.0f, inv);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    short2_t d = {0, 0};
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(d, y[4 * h + 0], y[4 * h + 1], 1.0f, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(d, y[4 * h + 2], y[4 * h + 3], 1.0f, true);
+    code[h] = __builtin_bit_cast(uint32_t, d);
+    const float2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(code[h], 1.0f, false);  // exact E4M3 values
+    const float2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(code[h], 1.0f, true);
+    q[4 * h + 0] = lo.x * S8;
+    q[4 * h + 1] = lo.y * S8;
+    q[4 * h + 2] = hi.x * S8;
+    q[4 * h + 3] = hi.y * S8;
+  }
+  *S = S8;
+}
+
+// The forward quantization of this lane's 8 elements in its segment: NVFP4
+// (fp8 == false: codes[0], s_code) or FP8 (codes[0..1]).  Amaxes in uniform
+// control flow, then the per-lane encode.
+__device__ __forceinline__ void fwd_quant8(const float w[8], bool valid, bool fp8, uint32_t codes[2],
+                                           uint32_t* s_code, float* S, float q[8]) {
+  float a_j, a_o;
+  half_amax(w, valid, &a_j, &a_o);
+  if (fp8) {
+    fp8_encode8(w, valid, a_o, codes, S, q);
+    *s_code = 0u;
+  } else {
+    nvfp4_encode8(w, valid, a_j, a_o, &codes[0], s_code, S, q);
+    codes[1] = 0u;
+  }
+}
+
 // Risk bin of one element from its window distances: 0 if dq == 0, 31 if only
 // dm == 0, else the binary exponent e of r = dq / dm (fp32, correctly rounded)
 // as min(max(e + 16, 1), 30).
@@ -111,6 +164,20 @@ __device__ __forceinline__ uint32_t code_flips(uint32_t c, uint32_t cp) {
   for (int t = 0; t < 8; ++t) {
     const uint32_t a = (c >> (4 * t)) & 15u, b = (cp >> (4 * t)) & 15u;
     n += (a != b && ((a | b) & 7u) != 0u) ? 1u : 0u;
+  }
+  return n;
+}
+
+// Bin changes between the 8 E4M3 codes of two words pairs; +0 and -0 are one bin.
+__device__ __forceinline__ uint32_t code_flips_fp8(const uint32_t c[2], const uint32_t cp[2]) {
+  uint32_t n = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t a = (c[h] >> (8 * t)) & 0xFFu, b = (cp[h] >> (8 * t)) & 0xFFu;
+      n += (a != b && ((a | b) & 0x7Fu) != 0u) ? 1u : 0u;
+    }
   }
   return n;
 }
@@ -139,244 +206,203 @@ __device__ __forceinline__ void add_diag(DiagSmem& sm, unsigned long long* flips
     atomicAdd(hist + threadIdx.x, (unsigned long long)sm.hist[threadIdx.x]);
 }
 
-// One lane per half group (8 consecutive elements of a row); the 16 lanes of
-// a 128-element outer block are consecutive.  All loads of the lane are issued
-// before the quantization work.  Lanes past the last row stay (no early exit,
-// the diagnostics use workgroup barriers) but touch no memory.
-template <bool DIAG>
-__device__ __forceinline__ void osci_body(const OsciParams& p, int32_t halves_per_row, uint32_t g, DiagSmem& dsm) {
-  const uint32_t row = g / (uint32_t)halves_per_row;
-  const bool live = row < (uint32_t)p.N;  // whole outer blocks are live or not
-  const uint32_t jh = g - row * (uint32_t)halves_per_row;
-  const uint32_t j = jh >> 1;  // 16-element group
-  const bool valid = live && (int64_t)j * 16 < p.K;
-  const int64_t base = (int64_t)row * p.K + (int64_t)jh * 8;
+// Element access of one lane: 8 consecutive elements of a row, or with an
+// outlier plan 8 consecutive positions of the row's compacted rest channels or
+// of its outlier channels (gathered through the plan's index lists).
+template <bool PLAN>
+struct Lane8 {
+  int64_t idx[8];
+  __device__ __forceinline__ void init(const OsciProblem& q, uint32_t row, uint32_t jl, bool fp8) {
+    const int64_t base = (int64_t)row * q.K;
+    if (PLAN) {
+      const int4* ip = reinterpret_cast<const int4*>((fp8 ? q.outl : q.rest) + jl * 8u);
+      const int4 c0 = ip[0], c1 = ip[1];
+      idx[0] = base + c0.x; idx[1] = base + c0.y; idx[2] = base + c0.z; idx[3] = base + c0.w;
+      idx[4] = base + c1.x; idx[5] = base + c1.y; idx[6] = base + c1.z; idx[7] = base + c1.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) idx[t] = base + (int64_t)jl * 8 + t;
+    }
+  }
+  __device__ __forceinline__ void load(const float* a, float v[8]) const {
+    if (PLAN) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = a[idx[t]];
+    } else {
+      load8f(a + idx[0], v);
+    }
+  }
+  __device__ __forceinline__ void store(float* a, const float v[8]) const {
+    if (PLAN) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) a[idx[t]] = v[t];
+    } else {
+      store8f(a + idx[0], v);
+    }
+  }
+};
 
-  float w[8], q[8], wp[8], qp[8], dq[8], dm[8];
+// Codes of the final W: NVFP4 (the rest channels, or all of them without a plan)
+// or FP8 (the outlier channels), padding included.
+__device__ __forceinline__ void store_codes(const OsciProblem& q, uint32_t row, uint32_t jl, bool fp8,
+                                            const uint32_t codes[2], uint32_t s_code, float S) {
+  if (fp8) {
+    const QOut& o = q.w8;
+    if (!o.codes) return;
+    *reinterpret_cast<uint2*>(o.codes + (int64_t)row * o.ld_codes + jl * 8u) = make_uint2(codes[0], codes[1]);
+    if ((jl & 15u) == 0u) o.s128[(int64_t)row * o.ld_s128 + (jl >> 4)] = S;
+  } else {
+    const QOut& o = q.wq;
+    if (!o.codes) return;
+    *reinterpret_cast<uint32_t*>(o.codes + (int64_t)row * o.ld_codes + jl * 4u) = codes[0];
+    if ((jl & 1u) == 0u) o.s16[(int64_t)row * o.ld_s16 + (jl >> 1)] = (uint8_t)s_code;
+    if ((jl & 15u) == 0u) o.s128[(int64_t)row * o.ld_s128 + (jl >> 4)] = S;
+  }
+}
+
+// One lane per half group; the 16 lanes of a 128-element outer block are
+// consecutive, and an outer block lies in one segment (rest or outliers: each
+// segment is padded to whole outer blocks).  All loads of the lane are issued
+// before the quantization work.  Lanes past the last row stay (no early exit:
+// the DPP reductions and the diagnostics' barriers need every lane) but touch
+// no memory.
+//
+// MASTER == false: OsciReset (section 2.B) of the masters as given.
+// MASTER == true:  AdamW on the masters first (fp32, one rounded operation at a
+//                  time; the pages use fp32 masters and apply OsciReset after
+//                  the update without naming the optimizer), then OsciReset of
+//                  the new masters with the pre-update master as W_prev.
+template <bool MASTER, bool DIAG, bool PLAN>
+__device__ __forceinline__ void osci_body(const OsciShared& c, const OsciProblem& q, uint32_t g, DiagSmem& dsm) {
+  const uint32_t row = g / (uint32_t)q.hpr;
+  const bool live = row < (uint32_t)q.N;  // whole outer blocks are live or not
+  const uint32_t jh = g - row * (uint32_t)q.hpr;
+  const bool fp8 = PLAN && jh >= (uint32_t)q.hpr1;         // uniform over an outer block
+  const uint32_t jl = fp8 ? jh - (uint32_t)q.hpr1 : jh;    // half group within the segment
+  const int32_t len = fp8 ? q.no : q.K1;
+  const bool valid = live && (int32_t)(jl >> 1) * 16 < len;
+  const bool init = !MASTER && c.mode == TJ2_OSCI_INIT;
+  const bool window_end = c.mode == TJ2_OSCI_WINDOW_END;
+
+  Lane8<PLAN> L;
+  float w[8], wp[8], qp[8], dq[8], dm[8], m[8], v[8], gr[8];
   if (valid) {
-    load8f(p.W + base, w);
-    if (p.mode != TJ2_OSCI_INIT) {
-      load8f(p.W_prev + base, wp);
-      load8f(p.Q_prev + base, qp);
-      load8f(p.dQ + base, dq);
-      load8f(p.dM + base, dm);
+    L.init(q, row, jl, fp8);
+    L.load(q.W, w);
+    if (MASTER) {
+      L.load(q.m, m);
+      L.load(q.v, v);
+      L.load(q.grad, gr);
+    }
+    if (!init) {
+      if (!MASTER) L.load(q.W_prev, wp);
+      L.load(q.Q_prev, qp);
+      L.load(q.dQ, dq);
+      L.load(q.dM, dm);
     }
   } else {
 #pragma unroll
     for (int t = 0; t < 8; ++t) w[t] = 0.0f;
   }
-  uint32_t code, s_code;
-  float S;
-  fwd_quant8(w, valid, &code, &s_code, &S, q);
-  uint32_t code_prev = 0;  // diagnostics: the previous master's codes (a flip is a change of bin)
-  if (DIAG && p.mode != TJ2_OSCI_INIT) {
+  if (MASTER) {
+    // AdamW: wp is the pre-update master, w the new one
+    const float omb1 = 1.0f - c.beta1, omb2 = 1.0f - c.beta2;
+    const float decay = 1.0f - c.lr * c.weight_decay;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float m1 = c.beta1 * m[t] + omb1 * gr[t];
+      const float v1 = c.beta2 * v[t] + omb2 * (gr[t] * gr[t]);
+      const float u = (m1 / c.bc1) / (sqrtf(v1 / c.bc2) + c.eps);
+      wp[t] = w[t];
+      w[t] = valid ? w[t] * decay - c.lr * u : 0.0f;
+      m[t] = m1;
+      v[t] = v1;
+    }
+  }
+  uint32_t codes[2], s_code;
+  float S, qv[8];
+  fwd_quant8(w, valid, fp8, codes, &s_code, &S, qv);
+  uint32_t codes_prev[2] = {0u, 0u};  // diagnostics: the previous master's codes (a flip is a change of bin)
+  if (DIAG && !init) {
     float x[8], qx[8], Sx;
     uint32_t sx;
 #pragma unroll
     for (int t = 0; t < 8; ++t) x[t] = valid ? wp[t] : 0.0f;
-    fwd_quant8(x, valid, &code_prev, &sx, &Sx, qx);
+    fwd_quant8(x, valid, fp8, codes_prev, &sx, &Sx, qx);
   }
 
   uint32_t n_reset = 0, n_flip = 0;
   uint32_t bins[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const bool want_bins = DIAG && p.risk_hist && p.mode == TJ2_OSCI_WINDOW_END;
+  const bool want_bins = DIAG && c.risk_hist && window_end;
   if (valid) {
-    if (p.mode == TJ2_OSCI_INIT) {
+    if (init) {
       float z[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) z[t] = 0.0f;
-      store8f(p.W_prev + base, w);
-      store8f(p.Q_prev + base, q);
-      store8f(p.dQ + base, z);
-      store8f(p.dM + base, z);
+      L.store(q.W_prev, w);
+      L.store(q.Q_prev, qv);
+      L.store(q.dQ, z);
+      L.store(q.dM, z);
     } else {
-      if (DIAG) n_flip = code_flips(code, code_prev);
+      if (DIAG) n_flip = fp8 ? code_flips_fp8(codes, codes_prev) : code_flips(codes[0], codes_prev[0]);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        dq[t] = dq[t] + fabsf(q[t] - qp[t]);
+        dq[t] = dq[t] + fabsf(qv[t] - qp[t]);
         dm[t] = dm[t] + fabsf(w[t] - wp[t]);
         wp[t] = w[t];
       }
-      if (p.mode == TJ2_OSCI_WINDOW_END) {
+      bool wrote_w = MASTER;  // the master pass always writes the new masters
+      if (window_end) {
         if (want_bins) {
 #pragma unroll
           for (int t = 0; t < 8; ++t) bins[t] = risk_bin(dq[t], dm[t]);
         }
-        if (p.reset_enabled) {
+        if (c.reset_enabled) {
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
-            if (dq[t] > p.tau * dm[t]) {
-              w[t] = q[t];
-              wp[t] = q[t];
+            if (dq[t] > c.tau * dm[t]) {
+              w[t] = qv[t];
+              wp[t] = qv[t];
               ++n_reset;
             }
           }
-          if (n_reset) store8f(p.W + base, w);
+          wrote_w = wrote_w || n_reset != 0;
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t) { dq[t] = 0.0f; dm[t] = 0.0f; }
       }
-      store8f(p.W_prev + base, wp);
-      store8f(p.Q_prev + base, q);
-      store8f(p.dQ + base, dq);
-      store8f(p.dM + base, dm);
+      if (wrote_w) L.store(q.W, w);
+      if (MASTER) {
+        L.store(q.m, m);
+        L.store(q.v, v);
+      } else {
+        L.store(q.W_prev, wp);
+      }
+      L.store(q.Q_prev, qv);
+      L.store(q.dQ, dq);
+      L.store(q.dM, dm);
     }
   }
   const bool any_reset = max16_lanes(n_reset ? 1.0f : 0.0f) > 0.0f;  // uniform over the outer block
-  if (p.have_wq && live) {
-    if (any_reset) fwd_quant8(w, valid, &code, &s_code, &S, q);  // scales may change after a reset
-    const QView& o = p.wq;
-    *reinterpret_cast<uint32_t*>(o.codes + (int64_t)row * o.ld_codes + jh * 4u) = code;
-    if ((jh & 1u) == 0u) o.s16[(int64_t)row * o.ld_s16 + j] = (uint8_t)s_code;
-    if ((jh & 15u) == 0u) o.s128[(int64_t)row * o.ld_s128 + (j >> 3)] = S;
-  }
-  if (p.reset_count && n_reset) atomicAdd(p.reset_count, (unsigned long long)n_reset);
-  if constexpr (DIAG) add_diag(dsm, p.flips, want_bins ? p.risk_hist : nullptr, n_flip, want_bins && valid, bins);
+  if (any_reset) fwd_quant8(w, valid, fp8, codes, &s_code, &S, qv);  // scales may change after a reset
+  if (live) store_codes(q, row, jl, fp8, codes, s_code, S);
+  if (c.reset_count && n_reset) atomicAdd(c.reset_count, (unsigned long long)n_reset);
+  if constexpr (DIAG) add_diag(dsm, c.flips, want_bins ? c.risk_hist : nullptr, n_flip, want_bins && valid, bins);
 }
 
-template <bool DIAG>
-__global__ __launch_bounds__(256) void osci_kernel(OsciParams p, int32_t halves_per_row) {
-  __shared__ DiagSmem dsm;
-  osci_body<DIAG>(p, halves_per_row, blockIdx.x * 256u + threadIdx.x, dsm);
-}
-
-// Several problems per launch (a model's weight matrices after one optimizer
-// step), so that small matrices do not each pay a launch.
-struct OsciMulti {
-  OsciParams p[kOsciMultiMax];
-  uint32_t begin[kOsciMultiMax + 1];
-  int32_t hpr[kOsciMultiMax];
-  int n;
-};
-static_assert(sizeof(OsciMulti) <= 4096, "kernel arguments stay within 4 KB");
-
-template <bool DIAG>
-__global__ __launch_bounds__(256) void osci_multi_kernel(OsciMulti m) {
+// Up to kOsciMultiMax weight matrices per launch (a model's matrices after one
+// optimizer step), so that small matrices do not each pay a launch:
+// workgroups [begin[i], begin[i+1]) take problem i.  Problems with and
+// without an outlier plan may share a launch (the branch is uniform per
+// workgroup).
+template <bool MASTER, bool DIAG>
+__global__ __launch_bounds__(256) void osci_multi_kernel(OsciLaunch L) {
   __shared__ DiagSmem dsm;
   int i = 0;
-  while (i + 1 < m.n && blockIdx.x >= m.begin[i + 1]) ++i;  // uniform per workgroup
-  osci_body<DIAG>(m.p[i], m.hpr[i], (blockIdx.x - m.begin[i]) * 256u + threadIdx.x, dsm);
-}
-
-// Fused master-weight pass (one read of the masters, their AdamW moments and the
-// OsciReset state): AdamW with decoupled weight decay in fp32, one rounded
-// operation at a time (the builder's optimizer: the pages use fp32 masters and
-// apply OsciReset after the update, section 2.B, without naming the optimizer),
-// then the OsciReset update of the new masters with the pre-update master as
-// W_prev (the distance the master travels is the update), then the forward
-// codes.  Lane layout as osci_kernel.
-template <bool DIAG>
-__device__ __forceinline__ void master_body(const MasterParams& p, int32_t halves_per_row, uint32_t g,
-                                            DiagSmem& dsm) {
-  const uint32_t row = g / (uint32_t)halves_per_row;
-  const bool live = row < (uint32_t)p.N;  // as osci_kernel: no early exit
-  const uint32_t jh = g - row * (uint32_t)halves_per_row;
-  const uint32_t j = jh >> 1;
-  const bool valid = live && (int64_t)j * 16 < p.K;
-  const int64_t base = (int64_t)row * p.K + (int64_t)jh * 8;
-
-  float w[8], m[8], v[8], gr[8], qp[8], dq[8], dm[8];
-  if (valid) {
-    load8f(p.W + base, w);
-    load8f(p.m + base, m);
-    load8f(p.v + base, v);
-    load8f(p.grad + base, gr);
-    load8f(p.Q_prev + base, qp);
-    load8f(p.dQ + base, dq);
-    load8f(p.dM + base, dm);
-  } else {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) w[t] = 0.0f;
-  }
-  const float omb1 = 1.0f - p.beta1, omb2 = 1.0f - p.beta2;
-  const float decay = 1.0f - p.lr * p.weight_decay;
-  float w1[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const float m1 = p.beta1 * m[t] + omb1 * gr[t];
-    const float v1 = p.beta2 * v[t] + omb2 * (gr[t] * gr[t]);
-    const float u = (m1 / p.bc1) / (sqrtf(v1 / p.bc2) + p.eps);
-    w1[t] = valid ? w[t] * decay - p.lr * u : 0.0f;
-    m[t] = m1;
-    v[t] = v1;
-  }
-  uint32_t code, s_code;
-  float S;
-  float q[8];
-  fwd_quant8(w1, valid, &code, &s_code, &S, q);
-  uint32_t code_prev = 0;  // diagnostics: codes of the pre-update master
-  if (DIAG) {
-    float qx[8], Sx;
-    uint32_t sx;
-    fwd_quant8(w, valid, &code_prev, &sx, &Sx, qx);
-  }
-  uint32_t n_reset = 0, n_flip = 0;
-  uint32_t bins[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const bool want_bins = DIAG && p.risk_hist && p.window_end;
-  if (valid) {
-    if (DIAG) n_flip = code_flips(code, code_prev);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      dq[t] = dq[t] + fabsf(q[t] - qp[t]);
-      dm[t] = dm[t] + fabsf(w1[t] - w[t]);
-    }
-    if (p.window_end) {
-      if (want_bins) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) bins[t] = risk_bin(dq[t], dm[t]);
-      }
-      if (p.reset_enabled) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          if (dq[t] > p.tau * dm[t]) {
-            w1[t] = q[t];
-            ++n_reset;
-          }
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) { dq[t] = 0.0f; dm[t] = 0.0f; }
-    }
-    store8f(p.W + base, w1);
-    store8f(p.m + base, m);
-    store8f(p.v + base, v);
-    store8f(p.Q_prev + base, q);
-    store8f(p.dQ + base, dq);
-    store8f(p.dM + base, dm);
-  }
-  const bool any_reset = max16_lanes(n_reset ? 1.0f : 0.0f) > 0.0f;  // uniform over the outer block
-  if (p.have_wq && live) {
-    if (any_reset) fwd_quant8(w1, valid, &code, &s_code, &S, q);  // scales may change after a reset
-    const QView& o = p.wq;
-    *reinterpret_cast<uint32_t*>(o.codes + (int64_t)row * o.ld_codes + jh * 4u) = code;
-    if ((jh & 1u) == 0u) o.s16[(int64_t)row * o.ld_s16 + j] = (uint8_t)s_code;
-    if ((jh & 15u) == 0u) o.s128[(int64_t)row * o.ld_s128 + (j >> 3)] = S;
-  }
-  if (p.reset_count && n_reset) atomicAdd(p.reset_count, (unsigned long long)n_reset);
-  if constexpr (DIAG) add_diag(dsm, p.flips, want_bins ? p.risk_hist : nullptr, n_flip, want_bins && valid, bins);
-}
-
-template <bool DIAG>
-__global__ __launch_bounds__(256) void master_kernel(MasterParams p, int32_t halves_per_row) {
-  __shared__ DiagSmem dsm;
-  master_body<DIAG>(p, halves_per_row, blockIdx.x * 256u + threadIdx.x, dsm);
-}
-
-// Several weight matrices per launch, as osci_multi_kernel.
-struct MasterMulti {
-  MasterParams p[kOsciMultiMax];
-  uint32_t begin[kOsciMultiMax + 1];
-  int32_t hpr[kOsciMultiMax];
-  int n;
-};
-static_assert(sizeof(MasterMulti) <= 4096, "kernel arguments stay within 4 KB");
-
-template <bool DIAG>
-__global__ __launch_bounds__(256) void master_multi_kernel(MasterMulti m) {
-  __shared__ DiagSmem dsm;
-  int i = 0;
-  while (i + 1 < m.n && blockIdx.x >= m.begin[i + 1]) ++i;  // uniform per workgroup
-  master_body<DIAG>(m.p[i], m.hpr[i], (blockIdx.x - m.begin[i]) * 256u + threadIdx.x, dsm);
+  while (i + 1 < L.n && blockIdx.x >= L.begin[i + 1]) ++i;  // uniform per workgroup
+  const uint32_t g = (blockIdx.x - L.begin[i]) * 256u + threadIdx.x;
+  if (L.p[i].rest) osci_body<MASTER, DIAG, true>(L.c, L.p[i], g, dsm);
+  else osci_body<MASTER, DIAG, false>(L.c, L.p[i], g, dsm);
 }
 
 // Per-channel sums of squares, in a fixed order so that the result does not
@@ -430,73 +456,29 @@ __global__ __launch_bounds__(256) void sumsq_finish_kernel(const double* __restr
 
 }  // namespace
 
-hipError_t launch_master(const MasterParams& p, hipStream_t s) {
-  const int64_t nb = (p.K + 127) / 128;
-  const int64_t hpr = nb * 16;  // half groups per row
-  const int64_t blocks = (p.N * hpr + 255) / 256;
-  if (p.flips || p.risk_hist)
-    hipLaunchKernelGGL(master_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
-  else
-    hipLaunchKernelGGL(master_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
-  return hipGetLastError();
-}
-
-hipError_t launch_master_multi(const MasterParams* ps, int n, hipStream_t s) {
+hipError_t launch_osci_multi(const OsciShared& c, const OsciProblem* ps, int n, bool master, hipStream_t s) {
   if (n < 1 || n > kOsciMultiMax) return hipErrorInvalidValue;
-  MasterMulti m;
-  memset(&m, 0, sizeof(m));
-  m.n = n;
+  OsciLaunch L;
+  memset(&L, 0, sizeof(L));
+  L.c = c;
+  L.n = n;
   int64_t total = 0;
-  bool diag = false;
   for (int i = 0; i < n; ++i) {
-    m.p[i] = ps[i];
-    const int64_t hpr = (ps[i].K + 127) / 128 * 16;  // half groups per row
-    m.hpr[i] = (int32_t)hpr;
-    m.begin[i] = (uint32_t)total;
-    total += (ps[i].N * hpr + 255) / 256;
-    diag = diag || ps[i].flips || ps[i].risk_hist;
+    L.p[i] = ps[i];
+    L.begin[i] = (uint32_t)total;
+    total += ((int64_t)ps[i].N * ps[i].hpr + 255) / 256;
   }
   if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  m.begin[n] = (uint32_t)total;
-  if (diag)
-    hipLaunchKernelGGL(master_multi_kernel<true>, dim3((uint32_t)total), dim3(256), 0, s, m);
-  else
-    hipLaunchKernelGGL(master_multi_kernel<false>, dim3((uint32_t)total), dim3(256), 0, s, m);
-  return hipGetLastError();
-}
-
-hipError_t launch_osci(const OsciParams& p, hipStream_t s) {
-  const int64_t nb = (p.K + 127) / 128;
-  const int64_t hpr = nb * 16;  // half groups per row
-  const int64_t blocks = (p.N * hpr + 255) / 256;
-  if (p.flips || p.risk_hist)
-    hipLaunchKernelGGL(osci_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
-  else
-    hipLaunchKernelGGL(osci_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0, s, p, (int32_t)hpr);
-  return hipGetLastError();
-}
-
-hipError_t launch_osci_multi(const OsciParams* ps, int n, hipStream_t s) {
-  if (n < 1 || n > kOsciMultiMax) return hipErrorInvalidValue;
-  OsciMulti m;
-  memset(&m, 0, sizeof(m));
-  m.n = n;
-  int64_t total = 0;
-  bool diag = false;
-  for (int i = 0; i < n; ++i) {
-    m.p[i] = ps[i];
-    const int64_t hpr = (ps[i].K + 127) / 128 * 16;  // half groups per row
-    m.hpr[i] = (int32_t)hpr;
-    m.begin[i] = (uint32_t)total;
-    total += (ps[i].N * hpr + 255) / 256;
-    diag = diag || ps[i].flips || ps[i].risk_hist;
+  L.begin[n] = (uint32_t)total;
+  const bool diag = c.flips || c.risk_hist;
+  const dim3 grid((uint32_t)total);
+  if (master) {
+    if (diag) hipLaunchKernelGGL((osci_multi_kernel<true, true>), grid, dim3(256), 0, s, L);
+    else hipLaunchKernelGGL((osci_multi_kernel<true, false>), grid, dim3(256), 0, s, L);
+  } else {
+    if (diag) hipLaunchKernelGGL((osci_multi_kernel<false, true>), grid, dim3(256), 0, s, L);
+    else hipLaunchKernelGGL((osci_multi_kernel<false, false>), grid, dim3(256), 0, s, L);
   }
-  if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  m.begin[n] = (uint32_t)total;
-  if (diag)
-    hipLaunchKernelGGL(osci_multi_kernel<true>, dim3((uint32_t)total), dim3(256), 0, s, m);
-  else
-    hipLaunchKernelGGL(osci_multi_kernel<false>, dim3((uint32_t)total), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 

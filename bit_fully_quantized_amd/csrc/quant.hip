@@ -367,6 +367,7 @@ struct ColMulti {
   uint32_t begin[kColMultiMax + 1];
   int n;
 };
+static_assert(sizeof(ColMulti) <= 4096, "kernel arguments stay within 4 KB");
 
 template <bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_col_multi_kernel(ColMulti m) {

@@ -52,7 +52,7 @@ hipError_t launch_quant(const QuantParams& p, hipStream_t s);
 // Up to kColMultiMax column (16x1, transposed) quantizations in one launch; every
 // problem shares rounding and the Hadamard switch, and is bf16 -> NVFP4,
 // NVFP4 -> NVFP4 or FP8 -> FP8.
-constexpr int kColMultiMax = 6;
+constexpr int kColMultiMax = 12;
 hipError_t launch_quant_col_multi(const QuantParams* ps, int n, hipStream_t s);
 
 // Forward split of a dense row-major input with an outlier plan: the columns
@@ -101,48 +101,66 @@ size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t nchunks);
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
-struct OsciParams {
-  float *W, *W_prev, *Q_prev, *dQ, *dM;
-  int64_t N, K;
-  int mode;
+// OsciReset and the fused master-weight pass (AdamW, then OsciReset), on up to
+// kOsciMultiMax weight matrices per launch.  Parameters shared by the
+// matrices of a call:
+struct OsciShared {
+  int mode;  // TJ2_OSCI_INIT / ACCUM / WINDOW_END (the master pass: ACCUM or WINDOW_END)
   float tau;
   int reset_enabled;
-  QView wq;          // codes.rows==0 -> no codes output
-  int have_wq;
+  float lr, beta1, beta2, eps, weight_decay, bc1, bc2;  // master pass only
   unsigned long long* reset_count;
   unsigned long long* flips;      // oscillation diagnostics, NULL = off
   unsigned long long* risk_hist;  // [kRiskBins], WINDOW_END only
 };
 
-constexpr int kRiskBins = 32;
-
-hipError_t launch_osci(const OsciParams& p, hipStream_t s);
-
-// Several OsciReset problems (same mode, tau, switches and counters) in one
-// launch: workgroups [begin[i], begin[i+1]) take problem i.
-constexpr int kOsciMultiMax = 16;
-hipError_t launch_osci_multi(const OsciParams* ps, int n, hipStream_t s);
-
-// Fused master-weight pass: AdamW on the masters, then OsciReset (ACCUM or
-// WINDOW_END) with the pre-update master as W_prev, then the forward codes.
-struct MasterParams {
-  float *W, *m, *v;
-  const float* grad;
-  float *Q_prev, *dQ, *dM;
-  int64_t N, K;
-  float lr, beta1, beta2, eps, weight_decay, bc1, bc2;
-  int window_end;
-  float tau;
-  int reset_enabled;
-  QView wq;
-  int have_wq;
-  unsigned long long* reset_count;
-  unsigned long long* flips;      // as OsciParams
-  unsigned long long* risk_hist;
+// Codes written by the pass (codes == NULL: none), row strides in bytes / floats.
+struct QOut {
+  uint8_t* codes;
+  uint8_t* s16;
+  float* s128;
+  int32_t ld_codes, ld_s16, ld_s128, pad;
 };
 
-hipError_t launch_master(const MasterParams& p, hipStream_t s);
-hipError_t launch_master_multi(const MasterParams* ps, int n, hipStream_t s);  // up to kOsciMultiMax
+inline QOut make_qout(const tj2_qtensor* q) {
+  QOut o;
+  o.codes = nullptr; o.s16 = nullptr; o.s128 = nullptr;
+  o.ld_codes = o.ld_s16 = o.ld_s128 = o.pad = 0;
+  if (!q) return o;
+  const QView v = make_view(*q);
+  o.codes = v.codes; o.s16 = v.s16; o.s128 = v.s128;
+  o.ld_codes = (int32_t)v.ld_codes; o.ld_s16 = (int32_t)v.ld_s16; o.ld_s128 = (int32_t)v.ld_s128;
+  return o;
+}
+
+// One weight matrix [N, K] and its state arrays (fp32, row-major).  With an
+// outlier plan (rest != NULL) the lanes of a row cover its K1 compacted rest
+// channels (NVFP4, hpr1 half groups) and then its `no` outlier channels (FP8),
+// each segment padded to whole 128-element blocks; without one, K1 = K.
+struct OsciProblem {
+  float *W, *W_prev, *Q_prev, *dQ, *dM;  // W_prev: OsciReset only
+  float *m, *v;                          // master pass only
+  const float* grad;                     // master pass only
+  int32_t N, K;
+  const int32_t* rest;
+  const int32_t* outl;
+  int32_t K1, no;
+  int32_t hpr, hpr1;  // half groups (8 elements) per row: all segments, the rest segment
+  QOut wq, w8;        // forward codes of the final W: NVFP4 [N, K1], FP8 [N, no]
+};
+
+constexpr int kRiskBins = 32;
+constexpr int kOsciMultiMax = 16;
+
+struct OsciLaunch {
+  OsciShared c;
+  OsciProblem p[kOsciMultiMax];
+  uint32_t begin[kOsciMultiMax + 1];
+  int n;
+};
+static_assert(sizeof(OsciLaunch) <= 4096, "kernel arguments stay within 4 KB");
+
+hipError_t launch_osci_multi(const OsciShared& c, const OsciProblem* ps, int n, bool master, hipStream_t s);
 
 // Calibration sums: rows per slab of the first pass; the second pass adds the
 // slabs' fp64 partial sums (workspace [ceil(M / kSumsqRows)][K]) in slab order.

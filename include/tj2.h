@@ -98,7 +98,13 @@ typedef struct {
   int32_t reserved;
 } tj2_outlier_plan;
 
-/* Buffers for the backward operands (optional argument of nvfp4_linear_bwd). */
+/*
+ * Buffers for the backward operands (optional argument of nvfp4_linear_bwd).
+ * w_given != 0: Wt (and W8t with a plan) already hold this call's re-grouped
+ * weight operands (the dX mask, SR at offset + 1 / offset + 4), e.g. written
+ * by master_update_step's `next` output, and the call reads them instead of
+ * forming them from Wq / W8.
+ */
 typedef struct {
   tj2_qtensor dYq;  /* [M, N] NVFP4, groups along N (RHT_N, SR)       */
   tj2_qtensor dYt;  /* [N, M] NVFP4, groups along M (RHT_M, SR)       */
@@ -106,6 +112,8 @@ typedef struct {
   tj2_qtensor Xt;   /* [K1, M] NVFP4, re-grouped dequantized inputs   */
   tj2_qtensor W8t;  /* [n_outliers, N] FP8 (plan only)                */
   tj2_qtensor X8t;  /* [n_outliers, M] FP8 (plan only)                */
+  int32_t w_given;
+  int32_t reserved;
 } tj2_bwd_operands;
 
 /* Message describing the last error of the calling thread ("" if none). */
@@ -296,25 +304,37 @@ typedef struct {
 
 /*
  * OsciReset (section 2.B) on fp32 masters W [N, K] and its state arrays (all
- * fp32 [N, K], caller-owned).  Q(w) is the forward quantizer (RTN, 1x16 along K)
- * dequantized in fp32.
+ * fp32 [N, K], caller-owned).  Q(w) is the forward quantizer dequantized in
+ * fp32: RTN NVFP4 in 1x16 groups along K; with an outlier plan (section 2.C)
+ * NVFP4 over the compacted rest channels and FP8 (E4M3, per-128 FP32 scale,
+ * round to nearest even) over the outlier channels, as nvfp4_linear_fwd
+ * quantizes the masters, so an outlier weight is reset to its FP8 point.
  *   TJ2_OSCI_INIT:       W_prev = W, Q_prev = Q(W), dQ = dM = 0.
  *   TJ2_OSCI_ACCUM:      dQ += |Q(W) - Q_prev|, dM += |W - W_prev|, Q_prev = Q(W), W_prev = W.
  *   TJ2_OSCI_WINDOW_END: as ACCUM; then where reset_enabled and dQ > tau*dM:
  *                        W = Q(W), W_prev = Q(W); then dQ = dM = 0.
- * Wq_out (optional, NVFP4 [N, K]): forward codes of the final W.
+ * plan (optional): device index lists as for nvfp4_linear_fwd.
+ * Wq_out (optional, NVFP4 [N, K1], K1 = K - n_outliers): forward codes of the
+ * final W; W8_out (optional, plan only, FP8 [N, n_outliers]): its FP8 codes.
+ * Together they are the forward's weight operands (nvfp4_linear_fwd with
+ * W_master == NULL).
  * reset_count (optional, device uint64): incremented by the number of resets.
- * diag (optional): oscillation diagnostics (tj2_osci_diag).
+ * diag (optional): oscillation diagnostics (tj2_osci_diag; a flip of an
+ * outlier weight is a change of its E4M3 code).
  * K must be a multiple of 16.
+ * The pages give the risk threshold and the window as parameters without
+ * values: tau is an argument and the window is the caller's count of calls
+ * between TJ2_OSCI_INIT / TJ2_OSCI_WINDOW_END.
  */
 tj2_status osci_reset_step(float* W, float* W_prev, float* Q_prev, float* dQ, float* dM, int64_t N,
                            int64_t K, int32_t mode, float tau, int32_t reset_enabled,
-                           tj2_qtensor* Wq_out, uint64_t* reset_count, const tj2_osci_diag* diag,
-                           void* stream);
+                           const tj2_outlier_plan* plan, tj2_qtensor* Wq_out, tj2_qtensor* W8_out,
+                           uint64_t* reset_count, const tj2_osci_diag* diag, void* stream);
 
 /*
  * One OsciReset problem of osci_reset_step_multi: W [N, K], its state arrays
- * (all fp32 [N, K], caller-owned device memory) and optional codes Wq_out.
+ * (all fp32 [N, K], caller-owned device memory), an optional plan and optional
+ * codes Wq_out / W8_out (host descriptors), as for osci_reset_step.
  */
 typedef struct {
   float* W;
@@ -324,7 +344,9 @@ typedef struct {
   float* dM;
   int64_t N;
   int64_t K;
-  tj2_qtensor* Wq_out; /* host descriptor, may be NULL */
+  tj2_qtensor* Wq_out;
+  const tj2_outlier_plan* plan;
+  tj2_qtensor* W8_out;
 } tj2_osci_tensor;
 
 /*
@@ -351,6 +373,25 @@ typedef struct {
 } tj2_adamw_params;
 
 /*
+ * The next backward's weight operands, formed by the master pass from the codes
+ * it writes (section 2.A: the backward re-groups the forward's quantized
+ * weights W-hat in 16x1 groups along N): Wt [K1, N] NVFP4 = SR of the
+ * Hadamard-transformed W-hat along N at offset + 1, W8t [n_outliers, N] FP8
+ * (plan only) at offset + 4, both with the dX mask tj2_rht_signs(seed,
+ * offset + 0) (rht == 0: no transform) -- bit for bit what nvfp4_linear_bwd
+ * with this seed and offset forms from the same Wq / W8.  Pass them to that
+ * call with tj2_bwd_operands.w_given.  Host descriptor, read during the call.
+ */
+typedef struct {
+  tj2_qtensor* Wt;
+  tj2_qtensor* W8t;
+  uint64_t seed;
+  uint64_t offset;
+  int32_t rht;
+  int32_t reserved;
+} tj2_next_bwd;
+
+/*
  * Fused master-weight pass: one AdamW step on the fp32 masters W [N, K], then
  * OsciReset (section 2.B) of the updated masters, then their forward codes, in
  * one pass over W, the moments m, v, the gradient grad and the OsciReset state
@@ -362,21 +403,23 @@ typedef struct {
  *   then OsciReset on W' with W_prev = W (the pre-update master, so no W_prev
  *   array): mode TJ2_OSCI_ACCUM or TJ2_OSCI_WINDOW_END as in osci_reset_step
  *   (TJ2_OSCI_INIT is osci_reset_step's; its W_prev is not read here).
- * Wq_out (optional, NVFP4 [N, K]): forward codes of the final W.
- * reset_count (optional, device uint64): incremented by the number of resets.
- * diag (optional): oscillation diagnostics of the updated masters (tj2_osci_diag).
+ * plan, Wq_out, W8_out, reset_count, diag: as in osci_reset_step.
+ * next (optional): also form the next backward's weight operands from the
+ * written codes (needs Wq_out, and W8_out with a plan; N a multiple of 16).
  * K must be a multiple of 16; arrays 16-byte aligned.  Errors: TJ2_ERR_ARG
  * (NULL array or params, bad mode, tau < 0), TJ2_ERR_SHAPE, TJ2_ERR_ALIGN.
  */
 tj2_status master_update_step(float* W, float* m, float* v, const float* grad, float* Q_prev, float* dQ,
                               float* dM, int64_t N, int64_t K, const tj2_adamw_params* adam, int32_t mode,
-                              float tau, int32_t reset_enabled, tj2_qtensor* Wq_out, uint64_t* reset_count,
-                              const tj2_osci_diag* diag, void* stream);
+                              float tau, int32_t reset_enabled, const tj2_outlier_plan* plan,
+                              tj2_qtensor* Wq_out, tj2_qtensor* W8_out, const tj2_next_bwd* next,
+                              uint64_t* reset_count, const tj2_osci_diag* diag, void* stream);
 
 /*
  * One weight matrix of master_update_step_multi: the masters W [N, K], moments
  * m, v, gradient grad and OsciReset state Q_prev, dQ, dM (all fp32 [N, K],
- * caller-owned device memory) and optional codes Wq_out.
+ * caller-owned device memory), and the optional plan, codes and next-backward
+ * operands of master_update_step (host descriptors).
  */
 typedef struct {
   float* W;
@@ -388,7 +431,10 @@ typedef struct {
   float* dM;
   int64_t N;
   int64_t K;
-  tj2_qtensor* Wq_out; /* host descriptor, may be NULL */
+  tj2_qtensor* Wq_out;
+  const tj2_outlier_plan* plan;
+  tj2_qtensor* W8_out;
+  const tj2_next_bwd* next;
 } tj2_master_tensor;
 
 /*

@@ -136,10 +136,10 @@ def test_gemm_and_linear_argument_errors(L):
 def test_osci_argument_errors(L):
     from bit_fully_quantized_amd import _lib
     p = [0x1000 * (i + 1) for i in range(5)]
-    assert L.osci_reset_step(*p, 16, 100, 1, ctypes.c_float(4.0), 1, None, None, None, None) == _lib.TJ2_ERR_SHAPE
-    assert L.osci_reset_step(*p, 16, 128, 7, ctypes.c_float(4.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
-    assert L.osci_reset_step(*p, 16, 128, 1, ctypes.c_float(-1.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
-    assert L.osci_reset_step(None, *p[1:], 16, 128, 1, ctypes.c_float(4.0), 1, None, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step(*p, 16, 100, 1, ctypes.c_float(4.0), 1, None, None, None, None, None, None) == _lib.TJ2_ERR_SHAPE
+    assert L.osci_reset_step(*p, 16, 128, 7, ctypes.c_float(4.0), 1, None, None, None, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step(*p, 16, 128, 1, ctypes.c_float(-1.0), 1, None, None, None, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.osci_reset_step(None, *p[1:], 16, 128, 1, ctypes.c_float(4.0), 1, None, None, None, None, None, None) == _lib.TJ2_ERR_ARG
     assert L.tj2_channel_sumsq(0x1000, 64, 100, 0x2000, 0x3000, 1 << 20, None) == _lib.TJ2_ERR_SHAPE
     assert L.tj2_channel_sumsq(0x1000, 64, 128, 0x2000, None, 0, None) == _lib.TJ2_ERR_ARG
     need = L.tj2_channel_sumsq_workspace_size(1000, 128)
@@ -186,16 +186,16 @@ def test_master_update_argument_errors(L):
     p = [0x1000 * (i + 1) for i in range(7)]
     ap = _lib.AdamWC(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
     f4 = ctypes.c_float(4.0)
-    assert L.master_update_step(*p, 16, 100, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None, None) == _lib.TJ2_ERR_SHAPE
-    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_INIT, f4, 0, None, None, None, None) == _lib.TJ2_ERR_ARG
-    assert L.master_update_step(*p, 16, 128, None, _lib.OSCI_ACCUM, f4, 0, None, None, None, None) == _lib.TJ2_ERR_ARG
-    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, ctypes.c_float(-1.0), 0, None, None,
+    assert L.master_update_step(*p, 16, 100, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None, None, None, None, None) == _lib.TJ2_ERR_SHAPE
+    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_INIT, f4, 0, None, None, None, None, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.master_update_step(*p, 16, 128, None, _lib.OSCI_ACCUM, f4, 0, None, None, None, None, None, None, None) == _lib.TJ2_ERR_ARG
+    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, ctypes.c_float(-1.0), 0, None, None, None, None, None,
                                 None, None) == _lib.TJ2_ERR_ARG
-    assert L.master_update_step(None, *p[1:], 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None,
+    assert L.master_update_step(None, *p[1:], 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None, None, None,
                                 None, None) == _lib.TJ2_ERR_ARG
     q = list(p)
     q[3] = 0x3008  # grad not 16-byte aligned
-    assert L.master_update_step(*q, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None, None) == _lib.TJ2_ERR_ALIGN
+    assert L.master_update_step(*q, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None, None, None, None, None) == _lib.TJ2_ERR_ALIGN
 
 
 def test_diag_counter_alignment(L):
@@ -205,11 +205,11 @@ def test_diag_counter_alignment(L):
     ap = _lib.AdamWC(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
     f4 = ctypes.c_float(4.0)
     d = _lib.OsciDiagC(0x5004, None)
-    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, ctypes.byref(d),
+    assert L.master_update_step(*p, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None, None, None, ctypes.byref(d),
                                 None) == _lib.TJ2_ERR_ALIGN
     assert b"8-byte" in L.tj2_last_error()
     d = _lib.OsciDiagC(None, 0x5002)
-    assert L.osci_reset_step(*p[:5], 16, 128, _lib.OSCI_WINDOW_END, f4, 1, None, None, ctypes.byref(d),
+    assert L.osci_reset_step(*p[:5], 16, 128, _lib.OSCI_WINDOW_END, f4, 1, None, None, None, None, ctypes.byref(d),
                              None) == _lib.TJ2_ERR_ALIGN
 
 
@@ -295,3 +295,25 @@ def test_noalloc_refuses_products_beyond_its_scratch(L):
     assert b"scratch" in L.tj2_last_error()
     assert L.nvfp4_gemm_noalloc(ctypes.byref(A), None, None, None, 0x9000, _lib.F32, 3072, None, 0,
                                 None) == _lib.TJ2_ERR_ARG
+
+
+def test_osci_plan_argument_errors(L):
+    from bit_fully_quantized_amd import _lib
+    p = [0x1000 * (i + 1) for i in range(5)]
+    f4 = ctypes.c_float(4.0)
+    plan = _lib.PlanC(0x7000, 0x8000, 16, 0)
+    w8 = fake_q(_lib.FP8, 16, 16)
+    # FP8 codes without a plan
+    assert L.osci_reset_step(*p, 16, 128, 1, f4, 1, None, None, ctypes.byref(w8), None, None, None) == _lib.TJ2_ERR_ARG
+    # with a plan the NVFP4 codes cover the K - n rest channels
+    wq_full = fake_q(_lib.NVFP4, 16, 128)
+    assert L.osci_reset_step(*p, 16, 128, 1, f4, 1, ctypes.byref(plan), ctypes.byref(wq_full), ctypes.byref(w8),
+                             None, None, None) == _lib.TJ2_ERR_SHAPE
+    # next-backward operands need the codes they are formed from
+    q7 = [0x1000 * (i + 1) for i in range(7)]
+    ap = _lib.AdamWC(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
+    wt = fake_q(_lib.NVFP4, 128, 16)
+    nxt = _lib.NextBwdC(ctypes.pointer(wt), None, 0, 0, 1, 0)
+    assert L.master_update_step(*q7, 16, 128, ctypes.byref(ap), _lib.OSCI_ACCUM, f4, 0, None, None, None,
+                                ctypes.byref(nxt), None, None, None) == _lib.TJ2_ERR_ARG
+    assert b"Wq_out" in L.tj2_last_error()
