@@ -85,6 +85,13 @@ class QTensor:
         return _lib.QTensorC(self.codes.data_ptr(), 0 if self.scale16 is None else self.scale16.data_ptr(),
                              self.scale128.data_ptr(), self.rows, self.len, self.fmt, 0)
 
+    def clone(self) -> "QTensor":
+        q = QTensor.__new__(QTensor)
+        q.fmt, q.rows, q.len, q.nb = self.fmt, self.rows, self.len, self.nb
+        q.codes, q.scale128 = self.codes.clone(), self.scale128.clone()
+        q.scale16 = self.scale16.clone() if self.scale16 is not None else None
+        return q
+
     # host views of the unpadded content (for tests)
     def host(self):
         codes = self.codes.cpu().numpy()
