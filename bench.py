@@ -51,28 +51,36 @@ def make_gen(seed):
 
 
 class LinearState:
-    """Device buffers of one linear layer of the workload."""
+    """Device buffers of one linear layer of the workload.  370M-style (p_outliers > 0): X[t, c] =
+    z * g_c with lognormal gains and a static plan from 8 calibration batches; 70M-style
+    (p_outliers == 0): X ~ N(0, 1) with 0.5% of the channels x32, no plan."""
 
     def __init__(self, tj2, layer, spec, M, p_outliers, seed):
         import torch
         self.name, self.K, self.N = spec.name, spec.K, spec.N
         K, N = self.K, self.N
         g = make_gen(seed)
-        self.gains = torch.exp(1.5 * torch.randn(K, generator=g, device="cuda"))
+        if p_outliers > 0:
+            self.gains = torch.exp(1.5 * torch.randn(K, generator=g, device="cuda"))
+        else:
+            self.gains = torch.ones(K, device="cuda")
+            self.gains[torch.randperm(K, generator=g, device="cuda")[: max(1, round(0.005 * K))]] = 32.0
         self.X = (torch.randn(M, K, generator=g, device="cuda") * self.gains).to(torch.bfloat16)
         self.W = (torch.randn(N, K, generator=g, device="cuda") * 0.02).float().contiguous()
         self.dY = (torch.randn(M, N, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
-        # static outlier channels from 8 calibration batches (fresh z, same gains)
-        from bit_fully_quantized_amd import outcontrol
-        calib = ((torch.randn(M // 8, K, generator=g, device="cuda") * self.gains).to(torch.bfloat16)
-                 for _ in range(8))
-        self.plan = outcontrol.calibrate(calib, p_outliers)
-        no = self.plan.n
+        self.plan = None
+        if p_outliers > 0:
+            # static outlier channels from 8 calibration batches (fresh z, same gains)
+            from bit_fully_quantized_amd import outcontrol
+            calib = ((torch.randn(M // 8, K, generator=g, device="cuda") * self.gains).to(torch.bfloat16)
+                     for _ in range(8))
+            self.plan = outcontrol.calibrate(calib, p_outliers)
+        no = self.plan.n if self.plan is not None else 0
         self.K1 = K - no
         self.Xq = tj2.QTensor(tj2.NVFP4, M, self.K1)
-        self.X8 = tj2.QTensor(tj2.FP8, M, no)
+        self.X8 = tj2.QTensor(tj2.FP8, M, no) if no else None
         self.Wq = tj2.QTensor(tj2.NVFP4, N, self.K1)
-        self.W8 = tj2.QTensor(tj2.FP8, N, no)
+        self.W8 = tj2.QTensor(tj2.FP8, N, no) if no else None
         self.Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
         self.dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
         self.dW = torch.empty(N, K, dtype=torch.float32, device="cuda")
@@ -133,15 +141,8 @@ def gemm_roofline(tj2, lins, layers, M, ws, reps=10):
     for li in lins[:5]:
         _, _, ops = tj2.linear_bwd(li.dY, li.saved, li.K, seed=SEED, offset=0, plan=li.plan, dX=li.dX, dW=li.dW,
                                    keep_operands=True)
-        no, K1, K, N = li.plan.n, li.K1, li.K, li.N
-        calls = [
-            ("fwd", 2.0 * M * N * K, q_bytes(li.Xq) + q_bytes(li.Wq) + q_bytes(li.X8) + q_bytes(li.W8) + 2 * M * N,
-             lambda: tj2.gemm(li.Xq, li.Wq, li.X8, li.W8, out=li.Y)),
-            ("dX", 2.0 * M * K * N, q_bytes(ops["dYq"]) + q_bytes(ops["Wt"]) + q_bytes(ops["W8t"]) + 2 * M * K,
-             lambda: tj2.gemm_outlier_cols(ops["dYq"], ops["Wt"], ops["W8t"], li.plan, out=li.dX, workspace=ws)),
-            ("dW", 2.0 * N * K * M, q_bytes(ops["dYt"]) + q_bytes(ops["Xt"]) + q_bytes(ops["X8t"]) + 4 * N * K,
-             lambda: tj2.gemm_outlier_cols(ops["dYt"], ops["Xt"], ops["X8t"], li.plan, out=li.dW, workspace=ws)),
-        ]
+        K, N = li.K, li.N
+        calls = product_calls(tj2, li, ops, M, ws)
         for name, fl, by, fn in calls:
             t = time_launches(fn, reps)
             per[f"{li.name}.{name}"] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 1)}
@@ -150,6 +151,196 @@ def gemm_roofline(tj2, lins, layers, M, ws, reps=10):
             tot_bytes += by * layers
             launches += layers
     return tot_flops, tot_time, tot_bytes, launches, per
+
+
+def product_calls(tj2, li, ops, M, ws):
+    """The three product launches of one linear's step (as the linear calls issue them):
+    (name, flops, algorithmic bytes, launch)."""
+    K, N = li.K, li.N
+    qb = lambda q: q_bytes(q) if q is not None else 0.0  # noqa: E731
+    if li.plan is None:
+        return [
+            ("fwd", 2.0 * M * N * K, qb(li.Xq) + qb(li.Wq) + 2 * M * N, lambda: tj2.gemm(li.Xq, li.Wq, out=li.Y)),
+            ("dX", 2.0 * M * K * N, qb(ops["dYq"]) + qb(ops["Wt"]) + 2 * M * K,
+             lambda: tj2.gemm(ops["dYq"], ops["Wt"], out=li.dX, workspace=ws)),
+            ("dW", 2.0 * N * K * M, qb(ops["dYt"]) + qb(ops["Xt"]) + 4 * N * K,
+             lambda: tj2.gemm(ops["dYt"], ops["Xt"], out=li.dW, workspace=ws)),
+        ]
+    return [
+        ("fwd", 2.0 * M * N * K, qb(li.Xq) + qb(li.Wq) + qb(li.X8) + qb(li.W8) + 2 * M * N,
+         lambda: tj2.gemm(li.Xq, li.Wq, li.X8, li.W8, out=li.Y)),
+        ("dX", 2.0 * M * K * N, qb(ops["dYq"]) + qb(ops["Wt"]) + qb(ops["W8t"]) + 2 * M * K,
+         lambda: tj2.gemm_outlier_cols(ops["dYq"], ops["Wt"], ops["W8t"], li.plan, out=li.dX, workspace=ws)),
+        ("dW", 2.0 * N * K * M, qb(ops["dYt"]) + qb(ops["Xt"]) + qb(ops["X8t"]) + 4 * N * K,
+         lambda: tj2.gemm_outlier_cols(ops["dYt"], ops["Xt"], ops["X8t"], li.plan, out=li.dW, workspace=ws)),
+    ]
+
+
+def quantizers_in_step(tj2, lins, layers, M, ws, reps=10):
+    """Quantizer rates in the step's own launch configuration, from one layer's linears (weighted by
+    the number of layers): the forward's quantization of X = (nvfp4_linear_fwd with given weight codes)
+    - (its product alone); the backward's quantizers (the dY row pass and the launch of all column
+    re-groupings) = nvfp4_linear_bwd - (its two products alone).  Algorithmic bytes: inputs read once,
+    packed outputs written once."""
+    import torch
+    per = 0.5 + 1 / 16 + 4 / 128  # NVFP4 bytes per element
+    p8 = 1 + 4 / 128              # FP8
+    fwd_t = fwd_b = bwd_t = bwd_b = 0.0
+    for li in lins[:5]:
+        M_, K, N = M, li.K, li.N
+        no = li.plan.n if li.plan is not None else 0
+        K1 = K - no
+        ops = tj2.bwd_operands(M_, N, K, li.plan)
+        _, saved = tj2.linear_fwd(li.X, None, N, Wq=li.Wq, W8=li.W8, plan=li.plan, Y=li.Y, Xq=li.Xq, X8=li.X8)
+        t_fwd = time_launches(lambda: tj2.linear_fwd(li.X, None, N, Wq=li.Wq, W8=li.W8, plan=li.plan, Y=li.Y,
+                                                     Xq=li.Xq, X8=li.X8), reps)
+        calls = product_calls(tj2, li, ops, M_, ws)
+        t_prod_fwd = time_launches(calls[0][3], reps)
+        t_bwd = time_launches(lambda: tj2.linear_bwd(li.dY, saved, K, seed=SEED, offset=0, plan=li.plan, dX=li.dX,
+                                                     dW=li.dW, operands=ops, workspace=ws), reps)
+        t_prod_bwd = time_launches(calls[1][3], reps) + time_launches(calls[2][3], reps)
+        fwd_t += layers * max(t_fwd - t_prod_fwd, 0.0)
+        fwd_b += layers * (2.0 * M_ * K + M_ * K1 * per + M_ * no * p8)
+        bwd_t += layers * max(t_bwd - t_prod_bwd, 0.0)
+        # dY rows; dY columns, W-hat, X-hat (and the FP8 slices) re-grouped: read packed, write packed
+        bwd_b += layers * (2 * (2.0 * M_ * N + M_ * N * per) + 2 * N * K1 * per + 2 * M_ * K1 * per
+                           + 2 * (N + M_) * no * p8)
+        del ops
+    torch.cuda.empty_cache()
+    out = {}
+    for name, t, b in (("forward_X", fwd_t, fwd_b), ("backward_all", bwd_t, bwd_b)):
+        gbs = b / t / 1e9 if t > 0 else 0.0
+        out[name] = {"ms_per_step": round(t * 1e3, 3), "GB_per_step": round(b / 1e9, 2), "GB_s": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 3)}
+    return out
+
+
+def single_linear_latency(tj2, reps=50):
+    """The single-linear workload (X 256x512, W 512x512 fp32 masters, dY 256x512; RHT on, seed 0): latency
+    of the forward (quantizers + product), the backward and one OsciReset window-end step, in us."""
+    import torch
+    import synthetic
+    wl = synthetic.SINGLE_LINEAR
+    M, K, N = wl.M, wl.linears[0].K, wl.linears[0].N
+    g = make_gen(3)
+    X = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
+    W = (torch.randn(N, K, generator=g, device="cuda") * 0.02).contiguous()
+    dY = (torch.randn(M, N, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Xq, Wq = tj2.QTensor(tj2.NVFP4, M, K), tj2.QTensor(tj2.NVFP4, N, K)
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty(N, K, dtype=torch.float32, device="cuda")
+    ws = tj2.linear_bwd_workspace(M, N, K)
+    fws = tj2.linear_fwd_workspace(M, N, K)
+    _, saved = tj2.linear_fwd(X, W, N, Y=Y, Xq=Xq, Wq=Wq, workspace=fws)
+    t_fwd = time_launches(lambda: tj2.linear_fwd(X, W, N, Y=Y, Xq=Xq, Wq=Wq, workspace=fws), reps)
+    t_bwd = time_launches(lambda: tj2.linear_bwd(dY, saved, K, seed=0, offset=0, dX=dX, dW=dW, workspace=ws), reps)
+    st = [torch.empty_like(W) for _ in range(4)]
+    Wm = W.clone()
+    tj2.osci_reset_step(Wm, *st, mode=tj2.OSCI_INIT)
+    t_osci = time_launches(lambda: tj2.osci_reset_step(Wm, *st, mode=tj2.OSCI_WINDOW_END, tau=4.0,
+                                                       reset_enabled=True, Wq_out=Wq), reps)
+    flops = 2.0 * M * N * K
+    return {"workload": wl.name, "fwd_us": round(t_fwd * 1e6, 2), "bwd_us": round(t_bwd * 1e6, 2),
+            "osci_reset_window_end_us": round(t_osci * 1e6, 2),
+            "fwd_bwd_tflops": round(3 * flops / (t_fwd + t_bwd) / 1e12, 2)}
+
+
+def olmo70m_rates(tj2, reps=10, steps=5):
+    """OLMo-2-70M-style linears (8 layers x QKV/O/gate/up/down, d 512, ffn 2048, 16384 tokens, no plan):
+    whole-step TFLOP/s (forward + backward of all 40 linears) and per-product TFLOP/s."""
+    import torch
+    import synthetic
+    wl = synthetic.OLMO70M
+    M, layers = wl.M, wl.layers
+    lins = [LinearState(tj2, l, spec, M, 0.0, seed=500 + 10 * l + j)
+            for l in range(layers) for j, spec in enumerate(wl.linears)]
+    ws = torch.empty(max(int(tj2.lib().nvfp4_linear_bwd_workspace_size(M, li.N, li.K, 0)) for li in lins),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(it):
+        for li in lins:
+            _, li.saved = tj2.linear_fwd(li.X, li.W, li.N, Wq=li.Wq, Y=li.Y, Xq=li.Xq)
+        for idx in range(len(lins) - 1, -1, -1):
+            li = lins[idx]
+            tj2.linear_bwd(li.dY, li.saved, li.K, seed=SEED, offset=8 * (it * len(lins) + idx), dX=li.dX, dW=li.dW,
+                           workspace=ws)
+
+    step(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for it in range(steps):
+        step(1 + it)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    flops = wl.gemm_flops_per_step()
+    per = {}
+    g_flops = g_time = 0.0
+    for li in lins[:5]:
+        _, _, ops = tj2.linear_bwd(li.dY, li.saved, li.K, seed=SEED, offset=0, dX=li.dX, dW=li.dW,
+                                   keep_operands=True, workspace=ws)
+        for name, fl, _, fn in product_calls(tj2, li, ops, M, ws):
+            t = time_launches(fn, reps)
+            per[f"{li.name}.{name}"] = round(fl / t / 1e12, 1)
+            g_flops += fl * layers
+            g_time += t * layers
+    del lins, ws
+    torch.cuda.empty_cache()
+    return {"workload": "OLMo-2-70M-style linears: d_model 512, SwiGLU ffn 2048, 8 layers x (QKV, O, gate, up, "
+                        "down), 16384 tokens/step, 0.5% channels x32, no outlier plan",
+            "ms_per_step": round(step_s * 1e3, 3), "tflops_step": round(flops / step_s / 1e12, 1),
+            "gemm_tflop_per_step": round(flops / 1e12, 3), "products_tflops": round(g_flops / g_time / 1e12, 1),
+            "products_frac_of_peak": round(g_flops / g_time / 1e12 / MFMA_F16_PEAK_TFLOPS, 3),
+            "per_product_tflops": per}
+
+
+def decoder_stack(steps=3, warmup=2):
+    """The 370M-style decoder stack (vocab 50304, 8 x 2048 random tokens, 16 layers; all linears NVFP4 with
+    OutControl plans; fused master pass with OsciReset, window 50, LR decaying 1e-4 -> 1e-6), ms per training
+    step, and the same stack with bf16 linears (torch.mm / hipBLASLt, AdamW on the masters) as comparator."""
+    import torch
+    from bit_fully_quantized_amd import decoder
+    out = {}
+    for kind in ("nvfp4", "bf16"):
+        cfg = decoder.DecoderConfig(linear=kind)
+        stack = decoder.Decoder(cfg)
+        stack.calibrate([decoder.random_tokens(cfg, 100 + b)[0] for b in range(2)])
+        batches = [decoder.random_tokens(cfg, b) for b in range(steps + warmup)]
+        for b in range(warmup):
+            stack.train_step(*batches[b])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for b in range(warmup, warmup + steps):
+            loss = stack.train_step(*batches[b])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        r = {"ms_per_step": round(ms, 2), "loss": round(float(loss), 4),
+             "linear_tflops_over_step": round(cfg.linear_flops_per_step() / (ms * 1e-3) / 1e12, 1)}
+        if kind == "nvfp4":
+            lr = cfg.lr(stack.step)
+            t = time_launches(lambda: tj2_master_pass(stack, lr), 2)
+            n = stack.linear_params()
+            r.update({"master_pass_ms": round(t * 1e3, 3), "linear_params": n,
+                      "master_pass_GB_s": round(n * 52.0 / t / 1e9, 1),
+                      "resets": int(stack.reset_count.item())})
+        out[kind] = r
+        del stack, batches
+        torch.cuda.empty_cache()
+    out["workload"] = ("OLMo-2-370M-style decoder stack: vocab 50304, d_model 1024, 16 layers, 16 heads, SwiGLU ffn "
+                       "4096, 8 x 2048 random tokens; pre-norm RMSNorm, RoPE, causal bf16 flash attention, "
+                       "cross-entropy; every linear NVFP4 with top-10% FP8 channels; AdamW + OsciReset (window 50)")
+    out["linear_tflop_per_step"] = round(decoder.DecoderConfig().linear_flops_per_step() / 1e12, 3)
+    out["bf16_over_nvfp4_step_time"] = round(out["bf16"]["ms_per_step"] / out["nvfp4"]["ms_per_step"], 3)
+    return out
+
+
+def tj2_master_pass(stack, lr):
+    """One fused master pass over the stack's linears (ACCUM), as its training step issues it."""
+    import bit_fully_quantized_amd as tj2
+    c = stack.cfg
+    tj2.master_update_step_multi(stack.master_batch, lr=lr, bias_correction1=0.5, bias_correction2=0.5,
+                                 beta1=c.beta1, beta2=c.beta2, eps=c.eps, weight_decay=c.weight_decay,
+                                 mode=tj2.OSCI_ACCUM, tau=c.tau)
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
@@ -323,6 +514,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU figures are not produced",
@@ -368,6 +560,8 @@ def main():
     log("product roofline pass")
     g_flops, g_time, g_bytes, g_launches, per = gemm_roofline(tj2, lins, layers, M, ws)
     achieved = g_flops / g_time / 1e12
+    log("quantizers in the step's launch configuration")
+    q_in_step = quantizers_in_step(tj2, lins, layers, M, ws)
     copy_calibration()
     log("OsciReset pass")
     n_params = sum(li.N * li.K for li in lins)
@@ -402,6 +596,14 @@ def main():
     del lins, ws
     torch.cuda.empty_cache()
 
+    log("single-linear latency")
+    single = single_linear_latency(tj2)
+    log("70M-style linears")
+    olmo70 = olmo70m_rates(tj2)
+    stack = None
+    if not args.no_stack:
+        log("370M-style decoder stack (NVFP4 linears, then bf16 comparator)")
+        stack = decoder_stack()
     log("MFMA-only reference loop")
     mfma_ach = mfma_reference()
     log("library bf16 product reference")
@@ -447,6 +649,11 @@ def main():
                                        "frac_of_peak": round(lib_all / MFMA_F16_PEAK_TFLOPS, 3),
                                        "products_frac_of_it": round(achieved / lib_all, 3)},
         },
+        "quantizers_in_step": {"what": "370M-style step, quantizer time from the step's own calls (linear call "
+                                       "minus its products), algorithmic bytes", **q_in_step},
+        "single_linear": single,
+        "olmo70m_linears": olmo70,
+        "stack": stack,
         "quantizer_sweep": {"tensor": "bf16 8192x4096 N(0,1), 1% columns x64", "algorithmic_MB_per_call":
                             round(sweep_bytes / 1e6, 2), "hbm_peak_GB_s": HBM_PEAK_GBS, **sweep},
         "osci_reset": {"what": "OsciReset accumulate over all masters through osci_reset_step_multi (16 weight "

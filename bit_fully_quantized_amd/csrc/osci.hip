@@ -206,12 +206,17 @@ __device__ __forceinline__ void add_diag(DiagSmem& sm, unsigned long long* flips
     atomicAdd(hist + threadIdx.x, (unsigned long long)sm.hist[threadIdx.x]);
 }
 
-// Element access of one lane: 8 consecutive elements of a row, or with an
-// outlier plan 8 consecutive positions of the row's compacted rest channels or
-// of its outlier channels (gathered through the plan's index lists).
+// Element access of one lane: 8 consecutive elements of a row.  With an
+// outlier plan the lane covers 8 consecutive positions of the row's compacted
+// channel order (the rest channels, then the outlier channels): the masters W
+// and the gradient, which are in channel order, are gathered through the
+// plan's index lists; the pass's own state arrays (W_prev, Q_prev, dQ, dM and
+// the moments m, v) are kept in the compacted order, so their accesses stay
+// contiguous.
 template <bool PLAN>
 struct Lane8 {
-  int64_t idx[8];
+  int64_t idx[8];  // channel-order positions (W, grad)
+  int64_t cpos;    // first compacted position (state arrays)
   __device__ __forceinline__ void init(const OsciProblem& q, uint32_t row, uint32_t jl, bool fp8) {
     const int64_t base = (int64_t)row * q.K;
     if (PLAN) {
@@ -219,27 +224,33 @@ struct Lane8 {
       const int4 c0 = ip[0], c1 = ip[1];
       idx[0] = base + c0.x; idx[1] = base + c0.y; idx[2] = base + c0.z; idx[3] = base + c0.w;
       idx[4] = base + c1.x; idx[5] = base + c1.y; idx[6] = base + c1.z; idx[7] = base + c1.w;
+      cpos = base + (fp8 ? q.K1 : 0) + (int64_t)jl * 8;
     } else {
+      cpos = base + (int64_t)jl * 8;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) idx[t] = base + (int64_t)jl * 8 + t;
+      for (int t = 0; t < 8; ++t) idx[t] = cpos + t;
     }
   }
-  __device__ __forceinline__ void load(const float* a, float v[8]) const {
+  // W and grad (channel order)
+  __device__ __forceinline__ void load_ch(const float* a, float v[8]) const {
     if (PLAN) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) v[t] = a[idx[t]];
     } else {
-      load8f(a + idx[0], v);
+      load8f(a + cpos, v);
     }
   }
-  __device__ __forceinline__ void store(float* a, const float v[8]) const {
+  __device__ __forceinline__ void store_ch(float* a, const float v[8]) const {
     if (PLAN) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) a[idx[t]] = v[t];
     } else {
-      store8f(a + idx[0], v);
+      store8f(a + cpos, v);
     }
   }
+  // state arrays (compacted order under a plan): contiguous, 16-byte aligned (K1 and K are multiples of 16)
+  __device__ __forceinline__ void load(const float* a, float v[8]) const { load8f(a + cpos, v); }
+  __device__ __forceinline__ void store(float* a, const float v[8]) const { store8f(a + cpos, v); }
 };
 
 // Codes of the final W: NVFP4 (the rest channels, or all of them without a plan)
@@ -288,11 +299,11 @@ __device__ __forceinline__ void osci_body(const OsciShared& c, const OsciProblem
   float w[8], wp[8], qp[8], dq[8], dm[8], m[8], v[8], gr[8];
   if (valid) {
     L.init(q, row, jl, fp8);
-    L.load(q.W, w);
+    L.load_ch(q.W, w);
     if (MASTER) {
       L.load(q.m, m);
       L.load(q.v, v);
-      L.load(q.grad, gr);
+      L.load_ch(q.grad, gr);
     }
     if (!init) {
       if (!MASTER) L.load(q.W_prev, wp);
@@ -371,7 +382,7 @@ __device__ __forceinline__ void osci_body(const OsciShared& c, const OsciProblem
 #pragma unroll
         for (int t = 0; t < 8; ++t) { dq[t] = 0.0f; dm[t] = 0.0f; }
       }
-      if (wrote_w) L.store(q.W, w);
+      if (wrote_w) L.store_ch(q.W, w);
       if (MASTER) {
         L.store(q.m, m);
         L.store(q.v, v);

@@ -313,7 +313,11 @@ typedef struct {
  *   TJ2_OSCI_ACCUM:      dQ += |Q(W) - Q_prev|, dM += |W - W_prev|, Q_prev = Q(W), W_prev = W.
  *   TJ2_OSCI_WINDOW_END: as ACCUM; then where reset_enabled and dQ > tau*dM:
  *                        W = Q(W), W_prev = Q(W); then dQ = dM = 0.
- * plan (optional): device index lists as for nvfp4_linear_fwd.
+ * plan (optional): device index lists as for nvfp4_linear_fwd.  With a plan,
+ * the state arrays W_prev, Q_prev, dQ, dM hold each row in the plan's
+ * compacted channel order (position p < K1 is channel rest[p], position
+ * K1 + i is channel outliers[i]), so the pass reads them contiguously; W
+ * stays in channel order.  A plan must be the same from INIT on.
  * Wq_out (optional, NVFP4 [N, K1], K1 = K - n_outliers): forward codes of the
  * final W; W8_out (optional, plan only, FP8 [N, n_outliers]): its FP8 codes.
  * Together they are the forward's weight operands (nvfp4_linear_fwd with
@@ -403,7 +407,9 @@ typedef struct {
  *   then OsciReset on W' with W_prev = W (the pre-update master, so no W_prev
  *   array): mode TJ2_OSCI_ACCUM or TJ2_OSCI_WINDOW_END as in osci_reset_step
  *   (TJ2_OSCI_INIT is osci_reset_step's; its W_prev is not read here).
- * plan, Wq_out, W8_out, reset_count, diag: as in osci_reset_step.
+ * plan, Wq_out, W8_out, reset_count, diag: as in osci_reset_step; with a plan
+ * the moments m, v are kept in the compacted channel order as well (W and
+ * grad stay in channel order).
  * next (optional): also form the next backward's weight operands from the
  * written codes (needs Wq_out, and W8_out with a plan; N a multiple of 16).
  * K must be a multiple of 16; arrays 16-byte aligned.  Errors: TJ2_ERR_ARG

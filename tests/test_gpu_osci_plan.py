@@ -26,6 +26,21 @@ def _bits(t):
     return t.cpu().numpy().view(np.uint32)
 
 
+def _chan(t, oplan):
+    """A state array of the library (compacted channel order under a plan: rest channels, then
+    outlier channels) in channel order."""
+    a = t.cpu().numpy() if isinstance(t, torch.Tensor) else np.asarray(t)
+    if oplan is None:
+        return a
+    out = np.empty_like(a)
+    out[:, np.concatenate([oplan.rest, oplan.outliers])] = a
+    return out
+
+
+def _state_bits(t, oplan):
+    return _chan(t, oplan).view(np.uint32)
+
+
 def _check_codes(wq, w8, ref, what):
     H.assert_q_equal(wq, ref[0], what=f"{what} Wq")
     H.assert_q_equal(w8, ref[1], what=f"{what} W8")
@@ -66,7 +81,7 @@ def test_osci_plan_trajectory(N, K, n):
         n_reset_total += nr
         torch.cuda.synchronize()
         for d, r, name in zip(dev, (st.W_prev, st.Q_prev, st.dQ, st.dM), ("W_prev", "Q_prev", "dQ", "dM")):
-            np.testing.assert_array_equal(_bits(d), r.view(np.uint32), err_msg=f"step {t}: {name}")
+            np.testing.assert_array_equal(_state_bits(d, oplan), r.view(np.uint32), err_msg=f"step {t}: {name}")
         np.testing.assert_array_equal(_bits(Wd), W.view(np.uint32), err_msg=f"step {t}: W")
         _check_codes(wq, w8, codes, f"step {t}")
         assert int(flips.item()) == diag["flips"], f"step {t}: flips"
@@ -103,7 +118,8 @@ def test_osci_multi_mixed_plans():
             m["W"], m["st"], codes, _ = oosci.osci_step(m["W"], m["st"], tau=1.0, window_end=end, reset_enabled=True,
                                                         plan=m["plans"][0])
             np.testing.assert_array_equal(_bits(m["Wd"]), m["W"].view(np.uint32), err_msg=f"{i} step {t}: W")
-            np.testing.assert_array_equal(_bits(m["dev"][2]), m["st"].dQ.view(np.uint32), err_msg=f"{i}: dQ")
+            np.testing.assert_array_equal(_state_bits(m["dev"][2], m["plans"][0]), m["st"].dQ.view(np.uint32),
+                                          err_msg=f"{i}: dQ")
             if m["w8"] is not None:
                 _check_codes(m["wq"], m["w8"], codes, f"matrix {i} step {t}")
             else:
@@ -145,9 +161,9 @@ def test_master_plan_and_next_backward_operands(N, K, n):
         n_reset_total += nr
         st = oosci.OsciState(W, Qp, dQo, dMo)
         torch.cuda.synchronize()
-        for name, got, ref in (("W", Wd, W), ("m", m, mo), ("v", v, vo), ("Q_prev", Q_prev, Qp), ("dQ", dQ, dQo),
-                               ("dM", dM, dMo)):
-            np.testing.assert_array_equal(_bits(got), ref.view(np.uint32), err_msg=f"step {t}: {name}")
+        np.testing.assert_array_equal(_bits(Wd), W.view(np.uint32), err_msg=f"step {t}: W")
+        for name, got, ref in (("m", m, mo), ("v", v, vo), ("Q_prev", Q_prev, Qp), ("dQ", dQ, dQo), ("dM", dM, dMo)):
+            np.testing.assert_array_equal(_state_bits(got, oplan), ref.view(np.uint32), err_msg=f"step {t}: {name}")
         if n:
             _check_codes(wq, w8, codes, f"step {t}")
             ref_wq, ref_w8 = codes

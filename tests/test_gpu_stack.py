@@ -28,6 +28,13 @@ def _bits(t):
     return t.detach().cpu().numpy().view(np.uint32)
 
 
+def _chan(a, oplan):
+    """A master-pass state array (compacted channel order: rest, then outlier channels) in channel order."""
+    out = np.empty_like(a)
+    out[:, np.concatenate([oplan.rest, oplan.outliers])] = a
+    return out
+
+
 def _check_capture(stack, lin, cap, rng):
     """Re-run the captured call through the library, compare with the stack, then with the oracle."""
     X, W, dY = cap["X"], cap["W"], cap["dY"]
@@ -105,14 +112,17 @@ def test_small_stack_linears_and_master_pass():
             for L in st.linears:
                 if L.name not in names:
                     continue
-                W, m, v, g, Qp, dQ, dM = before[L.name]
                 oplan = olinear.Plan.from_outliers(L.K, L.plan.outliers.cpu().numpy())
+                W, g = before[L.name][0], before[L.name][3]
+                m, v, Qp, dQ, dM = (_chan(before[L.name][i], oplan) for i in (1, 2, 4, 5, 6))
                 W2, m2, v2, Qp2, dQ2, dM2, (wq, w8), n = oadamw.master_step(
                     W, m, v, g, Qp, dQ, dM, opt, bc1, bc2, tau=c.tau, window_end=True, reset_enabled=True,
                     plan=oplan)
-                for name, got, ref in (("W", L.W, W2), ("m", L.m, m2), ("v", L.v, v2), ("Q_prev", L.Q_prev, Qp2),
-                                       ("dQ", L.dQ, dQ2), ("dM", L.dM, dM2)):
-                    np.testing.assert_array_equal(_bits(got), ref.view(np.uint32), err_msg=f"{L.name}: {name}")
+                np.testing.assert_array_equal(_bits(L.W), W2.view(np.uint32), err_msg=f"{L.name}: W")
+                for name, got, ref in (("m", L.m, m2), ("v", L.v, v2), ("Q_prev", L.Q_prev, Qp2), ("dQ", L.dQ, dQ2),
+                                       ("dM", L.dM, dM2)):
+                    np.testing.assert_array_equal(_chan(got.detach().cpu().numpy(), oplan).view(np.uint32),
+                                                  ref.view(np.uint32), err_msg=f"{L.name}: {name}")
                 H.assert_q_equal(L.Wq, wq, what=f"{L.name} Wq")
                 H.assert_q_equal(L.W8, w8, what=f"{L.name} W8")
                 off = st.offset(L.idx, t + 1)
