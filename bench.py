@@ -483,6 +483,21 @@ def mfma_reference(reps=3):
     return flops / t / 1e12
 
 
+def decode_placement(reps=3):
+    """The product's inner loop (no global memory) with B decoded once per workgroup into f16 LDS
+    (the product kernel's placement) and with packed B in LDS decoded by every wave after its LDS
+    reads: MFMA TFLOP/s of each (libtj2_measure's tj2_decode_probe, 1024 workgroups)."""
+    import torch
+    import bit_fully_quantized_amd as tj2
+    out = torch.empty(1024 * 512, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, packed in (("b_f16_in_lds", False), ("b_packed_in_lds", True)):
+        flops = tj2.decode_probe(out, 256, packed)
+        t = time_launches(lambda: tj2.decode_probe(out, 256, packed), reps)
+        res[name] = round(flops / t / 1e12, 1)
+    return res
+
+
 def cpu_baseline(M=8192, K=1024, N=3072, p=0.10):
     """The oracle (fp64 products, numpy quantizers) on one QKV-shaped linear with M tokens."""
     import numpy as np
@@ -606,6 +621,8 @@ def main():
         stack = decoder_stack()
     log("MFMA-only reference loop")
     mfma_ach = mfma_reference()
+    log("decode placement probe")
+    placement = decode_placement()
     log("library bf16 product reference")
     lib_ref, lib_all = library_gemm_reference(M, [(f"{spec.name}.fwd", spec.K, spec.N) for spec in wl.linears])
     sweep, sweep_bytes = ({}, 0) if args.no_sweep else quant_sweep(tj2)
@@ -642,6 +659,9 @@ def main():
             "achievable_mfma": {"what": "MFMA-only loop (v_mfma_f32_32x32x16_f16, register operands) on this part",
                                 "TFLOP_s": round(mfma_ach, 1), "frac_of_peak": round(mfma_ach / MFMA_F16_PEAK_TFLOPS, 3),
                                 "products_frac_of_it": round(achieved / mfma_ach, 3)},
+            "decode_placement": {"what": "the products' inner loop without global memory (tj2_decode_probe), MFMA "
+                                         "TFLOP/s with B decoded once per workgroup into f16 LDS vs packed B in "
+                                         "LDS decoded by every wave", **placement},
             "library_bf16_reference": {"what": "torch.mm bf16 (hipBLASLt) on plain operands of each linear's "
                                                "forward shape, TFLOP/s: the achievable dense rate as a vendor "
                                                "library reaches it, without decode or per-128 promotion",

@@ -503,6 +503,19 @@ def mfma_peak_probe(out: torch.Tensor, iters: int) -> float:
     return float(wgs) * 4 * iters * 4 * 32768
 
 
+def decode_probe(out: torch.Tensor, iters: int, packed_b: bool) -> float:
+    """Measurement helper from libtj2_measure (not part of the path): the product's inner loop with B
+    decoded once per workgroup into f16 LDS (packed_b False) or by every wave from packed LDS
+    (packed_b True); out.numel() // 512 workgroups; returns the MFMA flops it performs."""
+    wgs = out.numel() // 512
+    if not out.is_cuda or out.dtype != torch.float32 or wgs < 1:
+        raise ValueError("out must be a device float32 tensor of at least 512 elements")
+    st = _lib.measure_lib().tj2_decode_probe(1 if packed_b else 0, wgs, iters, _ptr(out), _stream())
+    if st != 0:
+        raise Tj2Error("tj2_decode_probe", st, "bad arguments or launch error")
+    return float(wgs) * 8 * iters * 32 * 32768
+
+
 def channel_sumsq(X: torch.Tensor, acc: torch.Tensor, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """acc[k] += sum_m X[m, k]^2 (fp64, fixed summation order); acc: device float64 [K]."""
     _dense(X, "X", _BF16)

@@ -142,6 +142,8 @@ def measure_lib():
         L = ctypes.CDLL(MEASURE_LIB_PATH)
         L.tj2_mfma_peak_probe.restype = I32
         L.tj2_mfma_peak_probe.argtypes = [I64, I32, P, P]
+        L.tj2_decode_probe.restype = I32
+        L.tj2_decode_probe.argtypes = [I32, I64, I32, P, P]
         _mlib = L
     return _mlib
 

@@ -26,6 +26,20 @@ extern "C" {
  */
 int32_t tj2_mfma_peak_probe(int64_t workgroups, int32_t iters, float* out, void* stream);
 
+/*
+ * Where the B operand of a packed product is decoded: the product kernel's
+ * inner loop without global memory (per 128-K chunk: barrier, B stage written
+ * to LDS, barrier, 8 A fragments decoded in registers per wave, 32
+ * v_mfma_f32_32x32x16_f16 per wave), with B decoded once per workgroup into
+ * f16 in LDS (packed_b == 0) or staged packed (E2M1 codes + E4M3 scales) and
+ * decoded by every wave after its LDS reads (packed_b != 0).  Synthetic data,
+ * changed every chunk.  `workgroups` workgroups of 512 threads; work:
+ * workgroups * 8 * iters * 32 * 32768 flops.  out: device, workgroups * 512
+ * floats (finite values; their content is not meaningful).  Returns 0, 1 (bad
+ * arguments; nothing enqueued) or 4 (launch error).
+ */
+int32_t tj2_decode_probe(int32_t packed_b, int64_t workgroups, int32_t iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
