@@ -530,6 +530,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the timed 370M-style steps and the product roofline pass (for a kernel trace whose "
+                         "product launches are exactly the headline workload's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU figures are not produced",
@@ -575,6 +578,14 @@ def main():
     log("product roofline pass")
     g_flops, g_time, g_bytes, g_launches, per = gemm_roofline(tj2, lins, layers, M, ws)
     achieved = g_flops / g_time / 1e12
+    if args.headline_only:
+        print(json.dumps({"metric": "NVFP4 linear fwd+bwd TFLOP/s at 370M shapes", "value": round(flops_step / step_s / 1e12, 2),
+                          "unit": "TFLOP/s", "ms_per_step": round(step_s * 1e3, 3), "steps": args.steps,
+                          "roofline_achieved_tflops": round(achieved, 1),
+                          "roofline_frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                          "avg_launch_us": round(g_time / g_launches * 1e6, 2),
+                          "gemm_gflop_per_launch": round(g_flops / g_launches / 1e9, 3)}), flush=True)
+        return
     log("quantizers in the step's launch configuration")
     q_in_step = quantizers_in_step(tj2, lins, layers, M, ws)
     copy_calibration()

@@ -12,6 +12,11 @@ layouts below are the OCP ones:
   mantissa; exponent 0 is subnormal (m * 2^-9); 0x7F / 0xFF are NaN; no
   infinities; largest finite 448.
 
+* E2M3 (6 bits, the FP6 operand of the FP6 x FP4 variant the pages name as
+  future work): bit 5 sign, bits 4..3 exponent (bias 1), bits 2..0 mantissa;
+  exponent 0 is subnormal (value = m * 0.125); largest value 7.5.  Every
+  E2M3 value is an E4M3FN value, which is how the library stores them.
+
 Element rounding rules (readings where the pages are silent):
 * round-to-nearest (forward pass): nearest grid value, a tie goes to the code
   whose mantissa bit is 0 (IEEE-style ties-to-even); the sign of the input is
@@ -136,3 +141,64 @@ def e4m3_sr(v, u16) -> np.ndarray:
     up = np.asarray(u16, dtype=np.uint16).astype(np.int64) + np.floor(t).astype(np.int64) >= 65536
     idx = np.where(up, hi, lo).astype(np.uint8)
     return idx | (np.signbit(v).astype(np.uint8) << 7)
+
+
+# ---------------------------------------------------------------------------
+# E2M3 (FP6)
+# ---------------------------------------------------------------------------
+
+
+def e2m3_decode(code) -> np.ndarray:
+    """Value (fp64) of 6-bit E2M3 codes, from the bit fields."""
+    c = np.asarray(code).astype(np.int64) & 0x3F
+    s = (c >> 5) & 1
+    e = (c >> 3) & 3
+    m = c & 7
+    mag = np.where(e == 0, m * 0.125, np.ldexp(1.0 + m / 8.0, np.maximum(e - 1, 0)))
+    return np.where(s == 1, -mag, mag)
+
+
+#: magnitudes of codes 0..31 in code order (ascending): 0, 0.125, ..., 7.5
+E2M3_MAG = e2m3_decode(np.arange(32))
+
+
+def _e2m3_floor_index(a64: np.ndarray) -> np.ndarray:
+    return np.clip(np.searchsorted(E2M3_MAG, a64, side="right") - 1, 0, 31)
+
+
+def e2m3_rtn(v) -> np.ndarray:
+    """Round fp32 values (|v| <= 7.5) to E2M3 codes, nearest with ties to even mantissa; sign kept."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v).astype(np.float64)
+    lo = _e2m3_floor_index(a)
+    hi = np.minimum(lo + 1, 31)
+    d_lo = a - E2M3_MAG[lo]
+    d_hi = E2M3_MAG[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi != lo) & (hi % 2 == 0))
+    idx = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return idx | (np.signbit(v).astype(np.uint8) << 5)
+
+
+def e2m3_sr(v, u16) -> np.ndarray:
+    """Stochastic rounding of fp32 values (|v| <= 7.5) onto the E2M3 grid (same rule as E2M1)."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v)
+    lo = _e2m3_floor_index(a.astype(np.float64))
+    hi = np.minimum(lo + 1, 31)
+    lo_v = E2M3_MAG[lo].astype(np.float32)
+    gap = (E2M3_MAG[hi] - E2M3_MAG[lo]).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(gap > 0, (a - lo_v) / np.where(gap > 0, gap, np.float32(1)), np.float32(0)).astype(np.float32)
+    t = (p * np.float32(65536.0)).astype(np.float32)
+    up = np.asarray(u16, dtype=np.uint16).astype(np.int64) + np.floor(t).astype(np.int64) >= 65536
+    idx = np.where(up, hi, lo).astype(np.uint8)
+    return idx | (np.signbit(v).astype(np.uint8) << 5)
+
+
+def e2m3_to_e4m3(code6) -> np.ndarray:
+    """The E4M3FN byte of the same value as each E2M3 code (the library's storage of FP6 elements)."""
+    c = np.asarray(code6).astype(np.int64) & 0x3F
+    mag = e2m3_decode(c & 0x1F)
+    idx = np.searchsorted(E4M3_POS, mag)
+    assert np.all(E4M3_POS[idx] == mag)
+    return (idx | ((c >> 5) << 7)).astype(np.uint8)

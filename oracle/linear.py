@@ -21,6 +21,11 @@ Both operands of one product share one sign mask (rht_signs(seed, offset+0)
 for dX, rht_signs(seed, offset+2) for dW), so the transforms cancel in the
 exact product.
 
+FP6 x FP4 (the mixed-precision strategy the pages name as future work,
+section 5; reading: the gradient operand gets the wider element): with
+grad_fmt="nvfp6" the two dY operands are double-block NVFP6 (E2M3 elements,
+same scales, offsets, masks and SR rule) while W-hat and X-hat stay NVFP4.
+
 OutControl (section 2.C): a static, sorted list O of input channels (the top
 p% from calibration) stays in FP8 in forward and backward; the remaining
 channels O-bar (sorted) are compacted and quantized to NVFP4 over the
@@ -73,8 +78,9 @@ def linear_fwd(X: np.ndarray, W: np.ndarray, plan: Plan | None = None) -> dict:
 
 
 def linear_bwd(dY: np.ndarray, saved: dict, seed: int, offset: int, rht: bool = True,
-               plan: Plan | None = None) -> dict:
-    """dY fp32 [M, N] (values of the bf16 gradient); saved = linear_fwd's result."""
+               plan: Plan | None = None, grad_fmt: str = "nvfp4") -> dict:
+    """dY fp32 [M, N] (values of the bf16 gradient); saved = linear_fwd's result; grad_fmt "nvfp4"
+    or "nvfp6" (the format of the two dY operands)."""
     dY = np.asarray(dY, dtype=np.float32)
     Xq: QTensor = saved["Xq"]
     Wq: QTensor = saved["Wq"]
@@ -82,10 +88,10 @@ def linear_bwd(dY: np.ndarray, saved: dict, seed: int, offset: int, rht: bool = 
     mask_dx = philox.rht_signs(seed, offset + 0) if rht else None
     mask_dw = philox.rht_signs(seed, offset + 2) if rht else None
 
-    dYq = quantize(dY, grouping="row", fmt="nvfp4", rounding="sr", rht_mask=mask_dx, seed=seed, offset=offset + 0)
+    dYq = quantize(dY, grouping="row", fmt=grad_fmt, rounding="sr", rht_mask=mask_dx, seed=seed, offset=offset + 0)
     Wt = quantize(dequantize(Wq), grouping="col", fmt="nvfp4", rounding="sr", rht_mask=mask_dx,
                   seed=seed, offset=offset + 1)
-    dYt = quantize(dY, grouping="col", fmt="nvfp4", rounding="sr", rht_mask=mask_dw, seed=seed, offset=offset + 2)
+    dYt = quantize(dY, grouping="col", fmt=grad_fmt, rounding="sr", rht_mask=mask_dw, seed=seed, offset=offset + 2)
     Xt = quantize(dequantize(Xq), grouping="col", fmt="nvfp4", rounding="sr", rht_mask=mask_dw,
                   seed=seed, offset=offset + 3)
     out = {"dYq": dYq, "Wt": Wt, "dYt": dYt, "Xt": Xt,

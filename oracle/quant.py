@@ -22,6 +22,12 @@ Readings where the pages are silent (all fp32, one IEEE operation at a time):
   round-to-nearest (forward) or stochastic (backward) E2M1 rule.
 * dequantized value: (q * s) * S, the product q * s being exact.
 
+NVFP6 (the FP6 x FP4 variant the pages name as future work, section 5): the
+same double block with E2M3 elements (largest 7.5): S = a_o / 3360 (7.5 * 448),
+s = the smallest E4M3FN value >= min(a_j / (7.5 * S), 448), v = clamp(y * inv,
+-7.5, 7.5), then the E2M3 round-to-nearest or stochastic rule; each element
+is stored as the E4M3FN byte of its E2M3 value (one byte per element).
+
 FP8 outlier channels (section 2.C, "e.g. FP8"): OCP E4M3FN elements with one
 FP32 scale per 128 elements along the grouping dimension: S8 = a_o / 448,
 v = clamp(y * (1 / S8), -448, 448), round-to-nearest-even (forward) or the
@@ -42,6 +48,7 @@ from . import formats, philox, rht
 
 TINY = np.float32(2.0 ** -100)
 NVFP4_OUTER_DIV = np.float32(2688.0)  # 6 * 448
+NVFP6_OUTER_DIV = np.float32(3360.0)  # 7.5 * 448
 FP8_OUTER_DIV = np.float32(448.0)
 
 
@@ -78,17 +85,27 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
 
 def nvfp4_quantize_rows(y: np.ndarray, rounding: str = "rtn", u16=None) -> QTensor:
     """Double-block NVFP4 quantization of fp32 y [rows, L] along its last axis."""
+    return _double_block_rows(y, rounding, u16, fp6=False)
+
+
+def nvfp6_quantize_rows(y: np.ndarray, rounding: str = "rtn", u16=None) -> QTensor:
+    """Double-block NVFP6 (E2M3 elements) quantization of fp32 y [rows, L] along its last axis."""
+    return _double_block_rows(y, rounding, u16, fp6=True)
+
+
+def _double_block_rows(y: np.ndarray, rounding: str, u16, fp6: bool) -> QTensor:
     y = np.asarray(y, dtype=np.float32)
     rows, L = y.shape
     assert L % 16 == 0 and L > 0
+    emax = np.float32(7.5 if fp6 else 6.0)
     a = np.abs(y)
     a_o, nb = _outer_amax(a, L)
     empty_o = a_o < TINY
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        S = np.where(empty_o, np.float32(0), a_o / NVFP4_OUTER_DIV).astype(np.float32)
+        S = np.where(empty_o, np.float32(0), a_o / (NVFP6_OUTER_DIV if fp6 else NVFP4_OUTER_DIV)).astype(np.float32)
         a_j = a.reshape(rows, L // 16, 16).max(axis=-1)
         S_j = S[:, np.arange(L // 16) // 8]
-        six_S = (np.float32(6.0) * S_j).astype(np.float32)
+        six_S = (emax * S_j).astype(np.float32)
         r = np.where(six_S > 0, a_j / np.where(six_S > 0, six_S, np.float32(1)), np.float32(0)).astype(np.float32)
         r = np.minimum(r, np.float32(formats.E4M3_MAX))
         empty_j = (a_j == 0) | (S_j == 0)
@@ -98,15 +115,15 @@ def nvfp4_quantize_rows(y: np.ndarray, rounding: str = "rtn", u16=None) -> QTens
         inv = np.where(d > 0, np.float32(1.0) / np.where(d > 0, d, np.float32(1)), np.float32(0)).astype(np.float32)
         inv_e = np.repeat(inv, 16, axis=1)
         v = (y * inv_e).astype(np.float32)
-    v = np.minimum(np.maximum(v, np.float32(-6.0)), np.float32(6.0))
+    v = np.minimum(np.maximum(v, -emax), emax)
     empty_e = np.repeat(empty_j, 16, axis=1)
     v = np.where(empty_e, np.copysign(np.float32(0), y), v).astype(np.float32)
-    if rounding == "rtn":
-        q = formats.e2m1_rtn(v)
-    elif rounding == "sr":
-        q = formats.e2m1_sr(v, u16)
-    else:
+    if rounding not in ("rtn", "sr"):
         raise ValueError(rounding)
+    if fp6:
+        q = formats.e2m3_rtn(v) if rounding == "rtn" else formats.e2m3_sr(v, u16)
+        return QTensor("nvfp6", formats.e2m3_to_e4m3(q), S, s_code, rows, L)
+    q = formats.e2m1_rtn(v) if rounding == "rtn" else formats.e2m1_sr(v, u16)
     return QTensor("nvfp4", pack_nibbles(q), S, s_code, rows, L)
 
 
@@ -138,8 +155,9 @@ def dequantize(q: QTensor) -> np.ndarray:
     """fp32 dequantized values: (q * s) * S for NVFP4, e * S8 for FP8."""
     rows, L = q.rows, q.L
     S_e = np.repeat(q.s128, 128, axis=1)[:, :L].astype(np.float32)
-    if q.fmt == "nvfp4":
-        qv = formats.e2m1_decode(unpack_nibbles(q.codes)).astype(np.float32)
+    if q.fmt in ("nvfp4", "nvfp6"):
+        qv = (formats.e2m1_decode(unpack_nibbles(q.codes)) if q.fmt == "nvfp4" else
+              formats.e4m3_decode(q.codes)).astype(np.float32)
         s_e = np.repeat(formats.e4m3_decode(q.s16).astype(np.float32), 16, axis=1)
         return ((qv * s_e).astype(np.float32) * S_e).astype(np.float32)
     ev = formats.e4m3_decode(q.codes).astype(np.float32)
@@ -150,8 +168,8 @@ def dequantize_f64(q: QTensor) -> np.ndarray:
     """Exact fp64 value q * s * S (the operand value of the reference products)."""
     L = q.L
     S_e = np.repeat(q.s128.astype(np.float64), 128, axis=1)[:, :L]
-    if q.fmt == "nvfp4":
-        qv = formats.e2m1_decode(unpack_nibbles(q.codes))
+    if q.fmt in ("nvfp4", "nvfp6"):
+        qv = formats.e2m1_decode(unpack_nibbles(q.codes)) if q.fmt == "nvfp4" else formats.e4m3_decode(q.codes)
         s_e = np.repeat(formats.e4m3_decode(q.s16), 16, axis=1)
         return qv * s_e * S_e
     return formats.e4m3_decode(q.codes) * S_e
@@ -180,6 +198,8 @@ def quantize(x: np.ndarray, *, grouping: str = "row", fmt: str = "nvfp4", roundi
     u16 = philox.sr_draws_for_shape(y.shape, seed, offset) if rounding == "sr" else None
     if fmt == "nvfp4":
         return nvfp4_quantize_rows(y, rounding, u16)
+    if fmt == "nvfp6":
+        return nvfp6_quantize_rows(y, rounding, u16)
     if fmt == "fp8":
         return fp8_quantize_rows(y, rounding, u16)
     raise ValueError(fmt)
