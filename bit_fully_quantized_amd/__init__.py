@@ -14,14 +14,14 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, OSCI_ACCUM, OSCI_INIT, OSCI_WINDOW_END, RISK_BINS, RTN,
+from ._lib import (BF16, F32, FP8, GROUP_COL, GROUP_ROW, NVFP4, NVFP6, OSCI_ACCUM, OSCI_INIT, OSCI_WINDOW_END, RISK_BINS, RTN,
                    SR, Tj2Error, check, lib)
 
 __all__ = ["QTensor", "OutlierPlan", "quantize", "gemm", "gemm_workspace", "linear_fwd", "linear_fwd_workspace",
            "linear_bwd", "linear_bwd_workspace", "osci_reset_step", "osci_reset_step_multi", "OsciBatch",
            "master_update_step", "master_update_step_multi", "MasterBatch", "NextBwd", "bwd_operands", "channel_sumsq",
            "select_outliers",
-           "mfma_peak_probe", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "BF16", "F32", "GROUP_ROW", "GROUP_COL",
+           "mfma_peak_probe", "rht_signs", "lib", "Tj2Error", "NVFP4", "FP8", "NVFP6", "BF16", "F32", "GROUP_ROW", "GROUP_COL",
            "RTN", "SR", "OSCI_INIT", "OSCI_ACCUM", "OSCI_WINDOW_END", "RISK_BINS"]
 
 
@@ -66,8 +66,8 @@ _I32 = (torch.int32,)
 class QTensor:
     """A quantized operand of `rows` x `len` elements grouped along `len` (device storage).
 
-    codes    uint8 [rows, nb*64] (NVFP4) or [rows, nb*128] (FP8), nb = ceil(len/128)
-    scale16  uint8 [rows, nb*8] E4M3 (NVFP4 only)
+    codes    uint8 [rows, nb*64] (NVFP4) or [rows, nb*128] (FP8, NVFP6), nb = ceil(len/128)
+    scale16  uint8 [rows, nb*8] E4M3 (NVFP4, NVFP6)
     scale128 float32 [rows, nb]
     """
 
@@ -78,7 +78,7 @@ class QTensor:
         nb = (length + 127) // 128
         self.nb = nb
         self.codes = torch.empty((rows, nb * (64 if fmt == NVFP4 else 128)), dtype=torch.uint8, device=device)
-        self.scale16 = torch.empty((rows, nb * 8), dtype=torch.uint8, device=device) if fmt == NVFP4 else None
+        self.scale16 = torch.empty((rows, nb * 8), dtype=torch.uint8, device=device) if fmt != FP8 else None
         self.scale128 = torch.empty((rows, nb), dtype=torch.float32, device=device)
 
     def c(self) -> _lib.QTensorC:
@@ -98,6 +98,8 @@ class QTensor:
         if self.fmt == NVFP4:
             return (codes[:, : self.len // 2], self.scale16.cpu().numpy()[:, : self.len // 16],
                     self.scale128.cpu().numpy())
+        if self.fmt == NVFP6:
+            return codes[:, : self.len], self.scale16.cpu().numpy()[:, : self.len // 16], self.scale128.cpu().numpy()
         return codes[:, : self.len], None, self.scale128.cpu().numpy()
 
 
@@ -256,16 +258,18 @@ def linear_fwd(X: torch.Tensor, W_master: torch.Tensor | None, N: int, *, Wq: QT
     return Y, {"Xq": Xq, "X8": X8, "Wq": Wq, "W8": W8}
 
 
-def linear_bwd_workspace(M: int, N: int, K: int, n_outliers: int = 0, device="cuda") -> torch.Tensor:
-    n = int(lib().nvfp4_linear_bwd_workspace_size(M, N, K, n_outliers))
-    return torch.empty(n, dtype=torch.uint8, device=device)
+def linear_bwd_workspace(M: int, N: int, K: int, n_outliers: int = 0, device="cuda",
+                         grad_fmt: int = NVFP4) -> torch.Tensor:
+    f = lib().nvfp6x4_linear_bwd_workspace_size if grad_fmt == NVFP6 else lib().nvfp4_linear_bwd_workspace_size
+    return torch.empty(int(f(M, N, K, n_outliers)), dtype=torch.uint8, device=device)
 
 
-def bwd_operands(M: int, N: int, K: int, plan: OutlierPlan | None = None, device="cuda") -> dict:
-    """Buffers for the backward operands of one linear (tj2_bwd_operands): dYq, dYt, Wt, Xt (+ W8t, X8t)."""
+def bwd_operands(M: int, N: int, K: int, plan: OutlierPlan | None = None, device="cuda", grad_fmt: int = NVFP4) -> dict:
+    """Buffers for the backward operands of one linear (tj2_bwd_operands): dYq, dYt (in grad_fmt), Wt, Xt
+    (+ W8t, X8t)."""
     no = plan.n if plan else 0
     K1 = K - no
-    ops = {"dYq": QTensor(NVFP4, M, N, device), "dYt": QTensor(NVFP4, N, M, device),
+    ops = {"dYq": QTensor(grad_fmt, M, N, device), "dYt": QTensor(grad_fmt, N, M, device),
            "Wt": QTensor(NVFP4, K1, N, device), "Xt": QTensor(NVFP4, K1, M, device)}
     if plan:
         ops["W8t"] = QTensor(FP8, no, N, device)
@@ -276,8 +280,9 @@ def bwd_operands(M: int, N: int, K: int, plan: OutlierPlan | None = None, device
 def linear_bwd(dY: torch.Tensor, saved: dict, K: int, *, seed: int, offset: int, rht: bool = True,
                plan: OutlierPlan | None = None, dx_dtype=torch.bfloat16, keep_operands: bool = False,
                operands: dict | None = None, w_given: bool = False, workspace: torch.Tensor | None = None,
-               dX: torch.Tensor | None = None, dW: torch.Tensor | None = None):
-    """Returns (dX, dW, operands-or-None).
+               dX: torch.Tensor | None = None, dW: torch.Tensor | None = None, grad_fmt: int = NVFP4):
+    """Returns (dX, dW, operands-or-None).  grad_fmt NVFP6: the FP6 x FP4 backward (nvfp6x4_linear_bwd),
+    the two dY operands in NVFP6.
 
     operands: buffers from bwd_operands() to hold the backward operands (returned); keep_operands
     allocates them.  w_given: operands["Wt"] (and ["W8t"]) already hold this call's re-grouped
@@ -296,7 +301,10 @@ def linear_bwd(dY: torch.Tensor, saved: dict, K: int, *, seed: int, offset: int,
     _dense(workspace, "workspace", (torch.uint8,), optional=True)
     if w_given and operands is None:
         raise ValueError("w_given needs the operands holding Wt (and W8t)")
-    ops = operands if operands is not None else (bwd_operands(M, N, K, plan, dY.device) if keep_operands else None)
+    if grad_fmt not in (NVFP4, NVFP6):
+        raise ValueError("grad_fmt must be NVFP4 or NVFP6")
+    ops = operands if operands is not None else (bwd_operands(M, N, K, plan, dY.device, grad_fmt) if keep_operands
+                                                 else None)
     opsc = None
     if ops is not None:
         empty = _lib.QTensorC()
@@ -304,17 +312,18 @@ def linear_bwd(dY: torch.Tensor, saved: dict, K: int, *, seed: int, offset: int,
                                  ops["W8t"].c() if plan else empty, ops["X8t"].c() if plan else empty,
                                  1 if w_given else 0, 0)
     if workspace is None:
-        workspace = linear_bwd_workspace(M, N, K, no, dY.device)
+        workspace = linear_bwd_workspace(M, N, K, no, dY.device, grad_fmt)
     pc = plan.c() if plan else None
     xqc, wqc = saved["Xq"].c(), saved["Wq"].c()
     x8c = saved["X8"].c() if saved.get("X8") is not None else None
     w8c = saved["W8"].c() if saved.get("W8") is not None else None
-    st = lib().nvfp4_linear_bwd(_ptr(dY), M, N, K, ctypes.byref(xqc), ctypes.byref(x8c) if x8c else None,
+    fn = lib().nvfp6x4_linear_bwd if grad_fmt == NVFP6 else lib().nvfp4_linear_bwd
+    st = fn(_ptr(dY), M, N, K, ctypes.byref(xqc), ctypes.byref(x8c) if x8c else None,
                                 ctypes.byref(wqc), ctypes.byref(w8c) if w8c else None,
                                 ctypes.byref(pc) if pc else None, 1 if rht else 0, seed, offset, _ptr(dX),
                                 _dtype_code(dX), _ptr(dW), ctypes.byref(opsc) if opsc is not None else None,
                                 _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
-    check("nvfp4_linear_bwd", st)
+    check("nvfp6x4_linear_bwd" if grad_fmt == NVFP6 else "nvfp4_linear_bwd", st)
     return dX, dW, ops
 
 

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtj2.so")
 MEASURE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtj2_measure.so")
 
 TJ2_OK, TJ2_ERR_ARG, TJ2_ERR_SHAPE, TJ2_ERR_ALIGN, TJ2_ERR_HIP, TJ2_ERR_UNSUPPORTED = range(6)
-BF16, F32, NVFP4, FP8 = 0, 1, 2, 3
+BF16, F32, NVFP4, FP8, NVFP6 = 0, 1, 2, 3, 4
 GROUP_ROW, GROUP_COL = 0, 1
 RTN, SR = 0, 1
 OSCI_INIT, OSCI_ACCUM, OSCI_WINDOW_END = 0, 1, 2
@@ -101,6 +101,9 @@ SIGNATURES = {
     "nvfp4_linear_bwd": (I32, [P, I64, I64, I64, QP, QP, QP, QP, ctypes.POINTER(PlanC), I32, U64, U64, P, I32, P,
                                ctypes.POINTER(BwdOperandsC), P, SZ, P]),
     "nvfp4_linear_bwd_workspace_size": (SZ, [I64, I64, I64, I32]),
+    "nvfp6x4_linear_bwd": (I32, [P, I64, I64, I64, QP, QP, QP, QP, ctypes.POINTER(PlanC), I32, U64, U64, P, I32, P,
+                                 ctypes.POINTER(BwdOperandsC), P, SZ, P]),
+    "nvfp6x4_linear_bwd_workspace_size": (SZ, [I64, I64, I64, I32]),
     "osci_reset_step": (I32, [P, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, PLANP, QP, QP, P,
                               ctypes.POINTER(OsciDiagC), P]),
     "osci_reset_step_multi": (I32, [ctypes.POINTER(OsciTensorC), I32, I32, ctypes.c_float, I32, P,

@@ -59,9 +59,11 @@ tj2_status check_qtensor(const tj2_qtensor* q, const char* name, int fmt, int64_
   if (rows <= 0) return fail(TJ2_ERR_SHAPE, "%s: rows must be positive", name);
   // the products index 128-element blocks (row * blocks per row) in 32 bits
   if (rows * ((len + 127) / 128) >= ((int64_t)1 << 32)) return fail(TJ2_ERR_SHAPE, "%s: too many 128-element blocks", name);
-  if (!q->codes || !q->scale128 || (fmt == TJ2_NVFP4 && !q->scale16))
+  if (fmt != TJ2_NVFP4 && fmt != TJ2_FP8 && fmt != TJ2_NVFP6) return fail(TJ2_ERR_ARG, "%s: bad format %d", name, fmt);
+  const bool has_s16 = fmt != TJ2_FP8;
+  if (!q->codes || !q->scale128 || (has_s16 && !q->scale16))
     return fail(TJ2_ERR_ARG, "%s: NULL array", name);
-  if (!aligned16(q->codes) || !aligned16(q->scale128) || (fmt == TJ2_NVFP4 && !aligned16(q->scale16)))
+  if (!aligned16(q->codes) || !aligned16(q->scale128) || (has_s16 && !aligned16(q->scale16)))
     return fail(TJ2_ERR_ALIGN, "%s: arrays must be 16-byte aligned", name);
   return TJ2_OK;
 }
@@ -86,7 +88,7 @@ tj2_status check_dims(int64_t v, const char* name) {
 
 size_t qbytes(int fmt, int64_t rows, int64_t len, size_t* c, size_t* s16, size_t* s128) {
   const int64_t nb = (len + 127) / 128;
-  *c = (size_t)(rows * nb * (fmt == TJ2_FP8 ? 128 : 64));
+  *c = (size_t)(rows * nb * (fmt == TJ2_NVFP4 ? 64 : 128));
   *s16 = fmt == TJ2_FP8 ? 0 : (size_t)(rows * nb * 8);
   *s128 = (size_t)(rows * nb * 4);
   return *c + *s16 + *s128;
@@ -253,6 +255,16 @@ size_t bwd_gemm_ws(int64_t M, int64_t N, int64_t K1, int64_t no) {
   return align256(w);
 }
 
+// Workspace of the backward with the two dY operands in format gfmt.
+size_t bwd_workspace_size(int gfmt, int64_t M, int64_t N, int64_t K, int32_t n_outliers) {
+  if (M <= 0 || N <= 0 || K <= 0 || n_outliers < 0 || n_outliers >= K) return 0;
+  const int64_t K1 = K - n_outliers;
+  size_t t = carve_size(gfmt, M, N) + carve_size(gfmt, N, M) + carve_size(TJ2_NVFP4, K1, N) +
+             carve_size(TJ2_NVFP4, K1, M);
+  if (n_outliers) t += carve_size(TJ2_FP8, n_outliers, N) + carve_size(TJ2_FP8, n_outliers, M);
+  return t + 256 + bwd_gemm_ws(M, N, K1, n_outliers);
+}
+
 tj2_status check_plan(const tj2_outlier_plan* plan, int64_t K) {
   if (!plan) return TJ2_OK;
   if (!plan->outliers || !plan->rest) return fail(TJ2_ERR_ARG, "plan arrays are NULL");
@@ -318,7 +330,8 @@ const char* tj2_version(void) { return "tj2 0.1.0 gfx950"; }
 
 tj2_status tj2_qtensor_bytes(int32_t fmt, int64_t rows, int64_t len, size_t* codes_bytes, size_t* scale16_bytes,
                              size_t* scale128_bytes) {
-  if (fmt != TJ2_NVFP4 && fmt != TJ2_FP8) return fail(TJ2_ERR_ARG, "format must be TJ2_NVFP4 or TJ2_FP8");
+  if (fmt != TJ2_NVFP4 && fmt != TJ2_FP8 && fmt != TJ2_NVFP6)
+    return fail(TJ2_ERR_ARG, "format must be TJ2_NVFP4, TJ2_FP8 or TJ2_NVFP6");
   if (rows <= 0 || len <= 0 || len % 16) return fail(TJ2_ERR_SHAPE, "rows > 0 and len a positive multiple of 16 required");
   size_t c, s16, s128;
   qbytes(fmt, rows, len, &c, &s16, &s128);
@@ -336,7 +349,8 @@ tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q
   if (grouping != TJ2_GROUP_ROW && grouping != TJ2_GROUP_COL) return fail(TJ2_ERR_ARG, "bad grouping %d", grouping);
   if (rounding != TJ2_RTN && rounding != TJ2_SR) return fail(TJ2_ERR_ARG, "bad rounding %d", rounding);
   if (!out) return fail(TJ2_ERR_ARG, "out is NULL");
-  if (out->fmt != TJ2_NVFP4 && out->fmt != TJ2_FP8) return fail(TJ2_ERR_ARG, "out format must be NVFP4 or FP8");
+  if (out->fmt != TJ2_NVFP4 && out->fmt != TJ2_FP8 && out->fmt != TJ2_NVFP6)
+    return fail(TJ2_ERR_ARG, "out format must be NVFP4, FP8 or NVFP6");
   if (rows <= 0 || cols <= 0) return fail(TJ2_ERR_SHAPE, "rows and cols must be positive");
   if (rows > (int64_t)1 << 30 || cols > (int64_t)1 << 30) return fail(TJ2_ERR_SHAPE, "dimension too large");
   const bool dense = x_dtype == TJ2_BF16 || x_dtype == TJ2_F32;
@@ -348,7 +362,9 @@ tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q
   } else {
     return fail(TJ2_ERR_ARG, "bad x_dtype %d", x_dtype);
   }
+  if (out->fmt == TJ2_NVFP6 && !dense) return fail(TJ2_ERR_UNSUPPORTED, "NVFP6 output needs a dense (bf16 / fp32) input");
   if (col_idx) {
+    if (out->fmt == TJ2_NVFP6) return fail(TJ2_ERR_UNSUPPORTED, "col_idx with an NVFP6 output is not implemented");
     if (grouping != TJ2_GROUP_ROW || !dense) return fail(TJ2_ERR_UNSUPPORTED, "col_idx needs row grouping and a dense input");
     if (!aligned16(col_idx)) return fail(TJ2_ERR_ALIGN, "col_idx must be 16-byte aligned");
     if (n_idx <= 0 || n_idx % 16 || n_idx > cols) return fail(TJ2_ERR_SHAPE, "n_idx must be a positive multiple of 16 <= cols");
@@ -406,12 +422,12 @@ tj2_status nvfp4_gemm_outlier_cols(const tj2_qtensor* A, const tj2_qtensor* B, c
                                    int32_t accumulate, void* workspace, size_t ws_bytes, void* stream) {
   if (!A || !B || !B8 || !plan) return fail(TJ2_ERR_ARG, "A, B, B8 and plan are required");
   if (workspace && !aligned16(workspace)) return fail(TJ2_ERR_ALIGN, "workspace must be 16-byte aligned");
-  if (A->fmt != TJ2_NVFP4 || B->fmt != TJ2_NVFP4 || B8->fmt != TJ2_FP8)
-    return fail(TJ2_ERR_UNSUPPORTED, "A and B must be NVFP4, B8 FP8");
+  if ((A->fmt != TJ2_NVFP4 && A->fmt != TJ2_NVFP6) || B->fmt != TJ2_NVFP4 || B8->fmt != TJ2_FP8)
+    return fail(TJ2_ERR_UNSUPPORTED, "A must be NVFP4 or NVFP6, B NVFP4, B8 FP8");
   const int64_t J = B->rows + B8->rows;
   TJ2_TRY(check_plan(plan, J));
   if (plan->n_outliers != B8->rows) return fail(TJ2_ERR_SHAPE, "B8 rows (%lld) != n_outliers (%d)", (long long)B8->rows, plan->n_outliers);
-  TJ2_TRY(check_qtensor(A, "A", TJ2_NVFP4, A->rows, A->len));
+  TJ2_TRY(check_qtensor(A, "A", A->fmt, A->rows, A->len));
   TJ2_TRY(check_qtensor(B, "B", TJ2_NVFP4, B->rows, A->len));
   TJ2_TRY(check_qtensor(B8, "B8", TJ2_FP8, B8->rows, A->len));
   if (!C) return fail(TJ2_ERR_ARG, "C is NULL");
@@ -469,19 +485,20 @@ tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, cons
 }
 
 size_t nvfp4_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers) {
-  if (M <= 0 || N <= 0 || K <= 0 || n_outliers < 0 || n_outliers >= K) return 0;
-  const int64_t K1 = K - n_outliers;
-  size_t t = carve_size(TJ2_NVFP4, M, N) + carve_size(TJ2_NVFP4, N, M) + carve_size(TJ2_NVFP4, K1, N) +
-             carve_size(TJ2_NVFP4, K1, M);
-  if (n_outliers) t += carve_size(TJ2_FP8, n_outliers, N) + carve_size(TJ2_FP8, n_outliers, M);
-  return t + 256 + bwd_gemm_ws(M, N, K1, n_outliers);
+  return bwd_workspace_size(TJ2_NVFP4, M, N, K, n_outliers);
 }
 
-tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, const tj2_qtensor* Xq,
-                            const tj2_qtensor* X8, const tj2_qtensor* Wq, const tj2_qtensor* W8,
-                            const tj2_outlier_plan* plan, int32_t rht, uint64_t seed, uint64_t offset, void* dX,
-                            int32_t dx_dtype, float* dW, tj2_bwd_operands* ops, void* workspace, size_t ws_bytes,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward of nvfp4_linear_bwd with the two dY operands in format gfmt
+// (TJ2_NVFP4, or TJ2_NVFP6 for the FP6 x FP4 variant).
+tj2_status linear_bwd_impl(int gfmt, const void* dY, int64_t M, int64_t N, int64_t K, const tj2_qtensor* Xq,
+                           const tj2_qtensor* X8, const tj2_qtensor* Wq, const tj2_qtensor* W8,
+                           const tj2_outlier_plan* plan, int32_t rht, uint64_t seed, uint64_t offset, void* dX,
+                           int32_t dx_dtype, float* dW, tj2_bwd_operands* ops, void* workspace, size_t ws_bytes,
+                           void* stream) {
   hipStream_t s = (hipStream_t)stream;
   TJ2_TRY(check_dims(M, "M"));
   TJ2_TRY(check_dims(K, "K"));
@@ -503,15 +520,15 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
   const size_t gws = bwd_gemm_ws(M, N, K1, no);
   void* gemm_ws = nullptr;
   if (!o) {
-    const size_t need = nvfp4_linear_bwd_workspace_size(M, N, K, (int32_t)no);
+    const size_t need = bwd_workspace_size(gfmt, M, N, K, (int32_t)no);
     if (!workspace || ws_bytes < need)
       return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
     uint8_t* cur = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
     gemm_ws = gws ? cur : nullptr;
     cur += gws;
     memset(&local, 0, sizeof(local));
-    local.dYq = carve(cur, TJ2_NVFP4, M, N);
-    local.dYt = carve(cur, TJ2_NVFP4, N, M);
+    local.dYq = carve(cur, gfmt, M, N);
+    local.dYt = carve(cur, gfmt, N, M);
     local.Wt = carve(cur, TJ2_NVFP4, K1, N);
     local.Xt = carve(cur, TJ2_NVFP4, K1, M);
     if (plan) {
@@ -521,8 +538,8 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
     o = &local;
   } else {
     if (workspace && ws_bytes >= gws && aligned16(workspace)) gemm_ws = gws ? workspace : nullptr;
-    TJ2_TRY(check_qtensor(&o->dYq, "ops.dYq", TJ2_NVFP4, M, N));
-    TJ2_TRY(check_qtensor(&o->dYt, "ops.dYt", TJ2_NVFP4, N, M));
+    TJ2_TRY(check_qtensor(&o->dYq, "ops.dYq", gfmt, M, N));
+    TJ2_TRY(check_qtensor(&o->dYt, "ops.dYt", gfmt, N, M));
     TJ2_TRY(check_qtensor(&o->Wt, "ops.Wt", TJ2_NVFP4, K1, N));
     TJ2_TRY(check_qtensor(&o->Xt, "ops.Xt", TJ2_NVFP4, K1, M));
     if (plan) {
@@ -557,6 +574,32 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
   TJ2_TRY(run_gemm_outl(&o->dYq, &o->Wt, &o->W8t, plan, dX, dx_dtype, K, 0, gemm_ws, gws, s));
   TJ2_TRY(run_gemm_outl(&o->dYt, &o->Xt, &o->X8t, plan, dW, TJ2_F32, K, 0, gemm_ws, gws, s));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, const tj2_qtensor* Xq,
+                            const tj2_qtensor* X8, const tj2_qtensor* Wq, const tj2_qtensor* W8,
+                            const tj2_outlier_plan* plan, int32_t rht, uint64_t seed, uint64_t offset, void* dX,
+                            int32_t dx_dtype, float* dW, tj2_bwd_operands* ops, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  return linear_bwd_impl(TJ2_NVFP4, dY, M, N, K, Xq, X8, Wq, W8, plan, rht, seed, offset, dX, dx_dtype, dW, ops,
+                         workspace, ws_bytes, stream);
+}
+
+size_t nvfp6x4_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers) {
+  return bwd_workspace_size(TJ2_NVFP6, M, N, K, n_outliers);
+}
+
+tj2_status nvfp6x4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, const tj2_qtensor* Xq,
+                              const tj2_qtensor* X8, const tj2_qtensor* Wq, const tj2_qtensor* W8,
+                              const tj2_outlier_plan* plan, int32_t rht, uint64_t seed, uint64_t offset, void* dX,
+                              int32_t dx_dtype, float* dW, tj2_bwd_operands* ops, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  return linear_bwd_impl(TJ2_NVFP6, dY, M, N, K, Xq, X8, Wq, W8, plan, rht, seed, offset, dX, dx_dtype, dW, ops,
+                         workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

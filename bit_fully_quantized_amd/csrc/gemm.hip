@@ -89,7 +89,8 @@ struct GemmKArgs {
 //    scales) and q[1].y (their bit offset in it); FP8 q[0..1].
 struct Slice {
   uint4 q[4];
-  float S;  // outer scale of the chunk
+  float S;      // outer scale of the chunk
+  uint32_t sc;  // NVFP6 A slice: its four inner scales
 };
 
 template <int F>
@@ -218,6 +219,29 @@ struct Op<TJ2_FP8> {
   }
 };
 
+// NVFP6 A operand of the FP6 x FP4 products: E2M3 elements stored as E4M3FN
+// bytes (rn * 128 bytes per row block, like FP8) under E4M3 inner scales per 16
+// (rn * 8, like NVFP4).  The fp8 -> f16 conversion is exact on them, and an
+// E2M3 value (4 significant bits) times an E4M3 scale (4) is exact in f16.
+template <>
+struct Op<TJ2_NVFP6> {
+  static __device__ __forceinline__ void load_half(const OperandK& o, uint32_t rn, int kc, int half, Slice& s) {
+    const uint4* p = reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 128 + ((size_t)rn * 128 + half * 64));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s.q[i] = p[i];
+    s.sc = *reinterpret_cast<const uint32_t*>(o.s16 + (size_t)kc * 8 + ((size_t)rn * 8 + half * 4));
+    s.S = (o.s128 + kc)[rn];
+  }
+  static __device__ __forceinline__ void prep_a(const Slice& s, half2_t (&sg)[4]) { Op<TJ2_NVFP4>::scales(s.sc, sg); }
+  template <int F>
+  static __device__ __forceinline__ half8_t frag_a(const Slice& s, const half2_t (&sg)[4]) {
+    const uint4& v = s.q[F >> 1];
+    const half8_t e = (F & 1) ? Op<TJ2_FP8>::dec8(v.z, v.w) : Op<TJ2_FP8>::dec8(v.x, v.y);
+    const _Float16 c = sg[F >> 1][0];
+    return e * half8_t{c, c, c, c, c, c, c, c};
+  }
+};
+
 __device__ __forceinline__ half8_t ld8(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
 
 // B fragments are read D MFMA slots before use, in a ring of frag_ring(D)
@@ -277,10 +301,11 @@ struct Fmt {
   }
 };
 
-// Outlier-column products: A NVFP4; B rows NVFP4 (seg[0].b) or FP8 (b8) per thread.
+// Outlier-column products: A NVFP4 (or NVFP6); B rows NVFP4 (seg[0].b) or FP8 (b8) per thread.
+template <int FA>
 struct FmtMixB {
   static __device__ __forceinline__ void fetch_a(const GemmKArgs& p, const Ctx& t, int it, int n, Slice& a) {
-    Op<TJ2_NVFP4>::load_half(p.seg[0].a, t.arn[0], t.c_begin + min(it, n - 1), t.ah, a);
+    Op<FA>::load_half(p.seg[0].a, t.arn[0], t.c_begin + min(it, n - 1), t.ah, a);
   }
   // Branch-free: every thread issues the same loads from addresses selected by its
   // format (an NVFP4 thread's second 16 bytes and an FP8 thread's inner scales
@@ -352,15 +377,16 @@ struct Fmts {
   }
 };
 
+template <int FA>
 struct FmtsMixB {
-  static __device__ __forceinline__ void prep_a(const Slice& a, half2_t (&sg)[4]) { Op<TJ2_NVFP4>::prep_a(a, sg); }
+  static __device__ __forceinline__ void prep_a(const Slice& a, half2_t (&sg)[4]) { Op<FA>::prep_a(a, sg); }
   // the NVFP4 inner scales sit in q[2].x of a B slice here (q[1] holds FP8 codes)
   static __device__ __forceinline__ void prep_b(const Slice& b, half2_t (&sg)[4]) {
     Op<TJ2_NVFP4>::scales(b.q[2].x >> b.q[2].y, sg);
   }
   template <int F>
   static __device__ __forceinline__ half8_t frag_a(const Slice& a, const half2_t (&sg)[4], bool) {
-    return Op<TJ2_NVFP4>::template frag_a<F>(a, sg);
+    return Op<FA>::template frag_a<F>(a, sg);
   }
   // both decodes, selected per lane (no divergent branch)
   template <int U>
@@ -558,8 +584,8 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
   // chunks [0, s1) of the range are segment 0 (pipelined), [s1, n) segment 1
   const int s1 = FA1 == F_NONE ? n : min(max(t.n0c - t.c_begin, 0), n);
   if (s1 > 0) {
-    using F = std::conditional_t<MIXB, FmtMixB, Fmt<FA0, FB0, F_NONE, F_NONE>>;
-    using FM = std::conditional_t<MIXB, FmtsMixB, Fmts<FA0, FB0, F_NONE, F_NONE>>;
+    using F = std::conditional_t<MIXB, FmtMixB<FA0>, Fmt<FA0, FB0, F_NONE, F_NONE>>;
+    using FM = std::conditional_t<MIXB, FmtsMixB<FA0>, Fmts<FA0, FB0, F_NONE, F_NONE>>;
     Slice a, b1, b2;
     half8_t af[8];
     half2_t sga[4];
@@ -797,6 +823,8 @@ GemmKernel pick_kernel(const GemmParams& p) {
   if (p.outl) {
     if (p.nseg == 1 && fa == TJ2_NVFP4 && fb == TJ2_NVFP4 && p.b8.fmt == TJ2_FP8)
       return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, F_NONE, F_NONE, true>;
+    if (p.nseg == 1 && fa == TJ2_NVFP6 && fb == TJ2_NVFP4 && p.b8.fmt == TJ2_FP8)
+      return gemm_nt_kernel<TJ2_NVFP6, TJ2_NVFP4, F_NONE, F_NONE, true>;
     return nullptr;
   }
   if (p.nseg == 2) {
@@ -807,6 +835,7 @@ GemmKernel pick_kernel(const GemmParams& p) {
     return nullptr;
   }
   if (fa == TJ2_NVFP4 && fb == TJ2_NVFP4) return gemm_nt_kernel<TJ2_NVFP4, TJ2_NVFP4, F_NONE, F_NONE, false>;
+  if (fa == TJ2_NVFP6 && fb == TJ2_NVFP4) return gemm_nt_kernel<TJ2_NVFP6, TJ2_NVFP4, F_NONE, F_NONE, false>;
   if (fa == TJ2_NVFP4 && fb == TJ2_FP8) return gemm_nt_kernel<TJ2_NVFP4, TJ2_FP8, F_NONE, F_NONE, false>;
   if (fa == TJ2_FP8 && fb == TJ2_NVFP4) return gemm_nt_kernel<TJ2_FP8, TJ2_NVFP4, F_NONE, F_NONE, false>;
   if (fa == TJ2_FP8 && fb == TJ2_FP8) return gemm_nt_kernel<TJ2_FP8, TJ2_FP8, F_NONE, F_NONE, false>;

@@ -71,22 +71,35 @@ struct Dense<TJ2_F32> {
 // ----------------------------------------------------------------------------
 // Per-group quantization of 16 values v (already transformed if RHT), given
 // the outer amax a_o and, for SR, the draws r (top-aligned 16-bit).  Writes 8
-// bytes (NVFP4) or 16 bytes (FP8) of codes.
+// bytes (NVFP4) or 16 bytes (FP8, NVFP6) of codes.
 // ----------------------------------------------------------------------------
-template <bool FP8OUT, bool SR>
+template <int OF, bool SR>
 __device__ __forceinline__ void quantize_group(const float v[16], float a_o, float a_j, const uint32_t r[16],
                                                uint32_t codes[4], uint32_t* s_code, float* S_out) {
-  if (!FP8OUT) {
-    GroupScale g = nvfp4_group_scale(a_o, a_j);
+  if constexpr (OF == TJ2_NVFP4 || OF == TJ2_NVFP6) {
+    GroupScale g = OF == TJ2_NVFP4 ? nvfp4_group_scale(a_o, a_j) : nvfp6_group_scale(a_o, a_j);
     *s_code = g.s_code;
     *S_out = g.S;
-    // both conversions saturate at +-6 and y * 0 keeps the sign of y, so an
-    // empty group (inv = 0) encodes signed zeros
     float y[16];
+    if constexpr (OF == TJ2_NVFP4) {
+      // both conversions saturate at +-6 and y * 0 keeps the sign of y, so an
+      // empty group (inv = 0) encodes signed zeros
 #pragma unroll
-    for (int t = 0; t < 16; ++t) y[t] = v[t] * g.inv;
-    if (SR) e2m1_sr16(y, r, codes);
-    else e2m1_rtn16(y, codes);
+      for (int t = 0; t < 16; ++t) y[t] = v[t] * g.inv;
+      if (SR) e2m1_sr16(y, r, codes);
+      else e2m1_rtn16(y, codes);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) y[t] = fminf(fmaxf(v[t] * g.inv, -7.5f), 7.5f);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t c = 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          c |= (SR ? e2m3_sr_e4m3(y[4 * w + b], r[4 * w + b]) : e2m3_rtn_e4m3(y[4 * w + b])) << (8 * b);
+        codes[w] = c;
+      }
+    }
   } else {
     float S = 0.0f, inv = 0.0f;
     if (a_o >= kTiny) {
@@ -106,10 +119,22 @@ __device__ __forceinline__ void quantize_group(const float v[16], float a_o, flo
   }
 }
 
+// Codes and scales of one 16-element group of row `row` (group j of the row).
+template <int OF>
+__device__ __forceinline__ void store_group(const QView& o, int64_t row, int64_t j, const uint32_t codes[4],
+                                            uint32_t s_code) {
+  if constexpr (OF == TJ2_NVFP4) {
+    *reinterpret_cast<uint2*>(o.codes + row * o.ld_codes + j * 8) = make_uint2(codes[0], codes[1]);
+  } else {
+    *reinterpret_cast<uint4*>(o.codes + row * o.ld_codes + j * 16) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+  }
+  if constexpr (OF != TJ2_FP8) o.s16[row * o.ld_s16 + j] = (uint8_t)s_code;
+}
+
 // ----------------------------------------------------------------------------
 // Row grouping: one lane per 16-element group.
 // ----------------------------------------------------------------------------
-template <int IN, bool GATHER, bool FP8OUT, bool SR, bool RHT>
+template <int IN, bool GATHER, int OF, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_row_kernel(const typename Dense<IN>::T* __restrict__ x,
                                                         int64_t ld_x, const int32_t* __restrict__ idx,
                                                         int32_t rows, int32_t L, int32_t groups_per_row,
@@ -158,15 +183,8 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const typename Dense<IN>
   }
   uint32_t codes[4], s_code;
   float S;
-  quantize_group<FP8OUT, SR>(v, a_o, a_j, u, codes, &s_code, &S);
-
-  if (!FP8OUT) {
-    *reinterpret_cast<uint2*>(out.codes + (int64_t)row * out.ld_codes + j * 8u) = make_uint2(codes[0], codes[1]);
-    out.s16[(int64_t)row * out.ld_s16 + j] = (uint8_t)s_code;
-  } else {
-    *reinterpret_cast<uint4*>(out.codes + (int64_t)row * out.ld_codes + j * 16u) =
-        make_uint4(codes[0], codes[1], codes[2], codes[3]);
-  }
+  quantize_group<OF, SR>(v, a_o, a_j, u, codes, &s_code, &S);
+  store_group<OF>(out, row, j, codes, s_code);
   if ((j & 7u) == 0u) out.s128[(int64_t)row * out.ld_s128 + (j >> 3)] = S;
 }
 
@@ -295,7 +313,7 @@ struct ColTile<TJ2_FP8> {
 };
 
 // One 128-row x 64-column tile (number `bid` of the problem's tiles).
-template <int IN, bool FP8OUT, bool SR, bool RHT>
+template <int IN, int OF, bool SR, bool RHT>
 __device__ __forceinline__ void col_tile(const QuantParams& p, uint32_t bid, ColTile<IN>& tile) {
   // Packed inputs: row blocks fastest, so the column tiles of one row block run
   // on one XCD (and its L2) close together and a cache line holding several of
@@ -340,28 +358,23 @@ __device__ __forceinline__ void col_tile(const QuantParams& p, uint32_t bid, Col
     }
     uint32_t codes[4], s_code;
     float S;
-    quantize_group<FP8OUT, SR>(v, a_o, a_j, u, codes, &s_code, &S);
+    quantize_group<OF, SR>(v, a_o, a_j, u, codes, &s_code, &S);
     // groups past the last row are the zero padding of the output's last block
-    if (!FP8OUT) {
-      *reinterpret_cast<uint2*>(o.codes + orow * o.ld_codes + (r0 >> 1)) = make_uint2(codes[0], codes[1]);
-      o.s16[orow * o.ld_s16 + (r0 >> 4)] = (uint8_t)s_code;
-    } else {
-      *reinterpret_cast<uint4*>(o.codes + orow * o.ld_codes + r0) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
-    }
+    store_group<OF>(o, orow, r0 >> 4, codes, s_code);
     if (rs == 0) o.s128[orow * o.ld_s128 + rbi] = S;
   });
 }
 
-template <int IN, bool FP8OUT, bool SR, bool RHT>
+template <int IN, int OF, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_col_kernel(QuantParams p) {
   __shared__ ColTile<IN> tile;
-  col_tile<IN, FP8OUT, SR, RHT>(p, blockIdx.x, tile);
+  col_tile<IN, OF, SR, RHT>(p, blockIdx.x, tile);
 }
 
 // Several independent column quantizations in one launch (the backward's
 // re-grouped operands): workgroups [begin[i], begin[i+1]) take problem i, so
 // small, latency-bound problems run beside the large ones instead of after
-// them.  Combinations: bf16 -> NVFP4, NVFP4 -> NVFP4, FP8 -> FP8.
+// them.  Combinations: bf16 -> NVFP4 or NVFP6, NVFP4 -> NVFP4, FP8 -> FP8.
 struct ColMulti {
   QuantParams p[kColMultiMax];
   uint32_t begin[kColMultiMax + 1];
@@ -380,55 +393,64 @@ __global__ __launch_bounds__(256) void quant_col_multi_kernel(ColMulti m) {
   while (i + 1 < m.n && blockIdx.x >= m.begin[i + 1]) ++i;  // uniform per workgroup
   const QuantParams& p = m.p[i];
   const uint32_t bid = blockIdx.x - m.begin[i];
-  if (p.in_dtype == TJ2_BF16) col_tile<TJ2_BF16, false, SR, RHT>(p, bid, tile.b);
-  else if (p.in_dtype == TJ2_NVFP4) col_tile<TJ2_NVFP4, false, SR, RHT>(p, bid, tile.n);
-  else col_tile<TJ2_FP8, true, SR, RHT>(p, bid, tile.e);
+  if (p.in_dtype == TJ2_BF16) {
+    if (p.out.fmt == TJ2_NVFP6) col_tile<TJ2_BF16, TJ2_NVFP6, SR, RHT>(p, bid, tile.b);
+    else col_tile<TJ2_BF16, TJ2_NVFP4, SR, RHT>(p, bid, tile.b);
+  } else if (p.in_dtype == TJ2_NVFP4) {
+    col_tile<TJ2_NVFP4, TJ2_NVFP4, SR, RHT>(p, bid, tile.n);
+  } else {
+    col_tile<TJ2_FP8, TJ2_FP8, SR, RHT>(p, bid, tile.e);
+  }
 }
 
-template <int IN, bool GATHER, bool FP8OUT, bool SR, bool RHT>
+template <int IN, bool GATHER, int OF, bool SR, bool RHT>
 hipError_t run_row(const QuantParams& p, hipStream_t s) {
   const int64_t L = p.out.len;
   const int64_t gpr = p.out.nb * 8;
   const int64_t threads = p.rows * gpr;
   const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL((quant_row_kernel<IN, GATHER, FP8OUT, SR, RHT>), dim3((uint32_t)blocks), dim3(256), 0, s,
+  hipLaunchKernelGGL((quant_row_kernel<IN, GATHER, OF, SR, RHT>), dim3((uint32_t)blocks), dim3(256), 0, s,
                      reinterpret_cast<const typename Dense<IN>::T*>(p.x), p.ld_x, p.idx, (int32_t)p.rows,
                      (int32_t)L, (int32_t)gpr, p.out, p.rht_mask, p.seed, p.offset);
   return hipGetLastError();
 }
 
-template <int IN, bool FP8OUT, bool SR, bool RHT>
+template <int IN, int OF, bool SR, bool RHT>
 hipError_t run_col(const QuantParams& p, hipStream_t s) {
   const int64_t blocks = (p.cols + 63) / 64 * ((p.rows + 127) / 128);
   if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((quant_col_kernel<IN, FP8OUT, SR, RHT>), dim3((uint32_t)blocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((quant_col_kernel<IN, OF, SR, RHT>), dim3((uint32_t)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-template <int IN, bool GATHER, bool FP8OUT>
+template <int IN, bool GATHER, int OF>
 hipError_t dispatch_row_rs(const QuantParams& p, hipStream_t s) {
   const bool sr = p.rounding == TJ2_SR, rht = p.rht != 0;
-  if (sr) return rht ? run_row<IN, GATHER, FP8OUT, true, true>(p, s) : run_row<IN, GATHER, FP8OUT, true, false>(p, s);
-  return rht ? run_row<IN, GATHER, FP8OUT, false, true>(p, s) : run_row<IN, GATHER, FP8OUT, false, false>(p, s);
+  if (sr) return rht ? run_row<IN, GATHER, OF, true, true>(p, s) : run_row<IN, GATHER, OF, true, false>(p, s);
+  return rht ? run_row<IN, GATHER, OF, false, true>(p, s) : run_row<IN, GATHER, OF, false, false>(p, s);
 }
 
-template <int IN, bool FP8OUT>
+template <int IN, int OF>
 hipError_t dispatch_col_rs(const QuantParams& p, hipStream_t s) {
   const bool sr = p.rounding == TJ2_SR, rht = p.rht != 0;
-  if (sr) return rht ? run_col<IN, FP8OUT, true, true>(p, s) : run_col<IN, FP8OUT, true, false>(p, s);
-  return rht ? run_col<IN, FP8OUT, false, true>(p, s) : run_col<IN, FP8OUT, false, false>(p, s);
+  if (sr) return rht ? run_col<IN, OF, true, true>(p, s) : run_col<IN, OF, true, false>(p, s);
+  return rht ? run_col<IN, OF, false, true>(p, s) : run_col<IN, OF, false, false>(p, s);
 }
 
 template <int IN>
 hipError_t dispatch_row(const QuantParams& p, hipStream_t s) {
-  const bool fp8 = p.out.fmt == TJ2_FP8;
-  if (p.idx) return fp8 ? dispatch_row_rs<IN, true, true>(p, s) : dispatch_row_rs<IN, true, false>(p, s);
-  return fp8 ? dispatch_row_rs<IN, false, true>(p, s) : dispatch_row_rs<IN, false, false>(p, s);
+  const int of = p.out.fmt;
+  if (p.idx) return of == TJ2_FP8 ? dispatch_row_rs<IN, true, TJ2_FP8>(p, s) : dispatch_row_rs<IN, true, TJ2_NVFP4>(p, s);
+  if (of == TJ2_NVFP6) return dispatch_row_rs<IN, false, TJ2_NVFP6>(p, s);
+  return of == TJ2_FP8 ? dispatch_row_rs<IN, false, TJ2_FP8>(p, s) : dispatch_row_rs<IN, false, TJ2_NVFP4>(p, s);
 }
 
 template <int IN>
 hipError_t dispatch_col(const QuantParams& p, hipStream_t s) {
-  return p.out.fmt == TJ2_FP8 ? dispatch_col_rs<IN, true>(p, s) : dispatch_col_rs<IN, false>(p, s);
+  if constexpr (IN == TJ2_BF16 || IN == TJ2_F32) {
+    if (p.out.fmt == TJ2_NVFP6) return dispatch_col_rs<IN, TJ2_NVFP6>(p, s);
+  }
+  return p.out.fmt == TJ2_FP8 ? dispatch_col_rs<IN, TJ2_FP8>(p, s) : dispatch_col_rs<IN, TJ2_NVFP4>(p, s);
 }
 
 }  // namespace
@@ -502,13 +524,13 @@ __global__ __launch_bounds__(256) void quant_split_kernel(SplitParams p, int R) 
     uint32_t codes[4], s_code;
     float S;
     if (!fp8) {
-      quantize_group<false, false>(v, a_o, a_j, nullptr, codes, &s_code, &S);
+      quantize_group<TJ2_NVFP4, false>(v, a_o, a_j, nullptr, codes, &s_code, &S);
       const QView& o = p.q4;
       *reinterpret_cast<uint2*>(o.codes + orow * o.ld_codes + jj * 8) = make_uint2(codes[0], codes[1]);
       o.s16[orow * o.ld_s16 + jj] = (uint8_t)s_code;
       if ((jj & 7) == 0) o.s128[orow * o.ld_s128 + (jj >> 3)] = S;
     } else {
-      quantize_group<true, false>(v, a_o, a_j, nullptr, codes, &s_code, &S);
+      quantize_group<TJ2_FP8, false>(v, a_o, a_j, nullptr, codes, &s_code, &S);
       const QView& o = p.q8;
       *reinterpret_cast<uint4*>(o.codes + orow * o.ld_codes + jj * 16) =
           make_uint4(codes[0], codes[1], codes[2], codes[3]);
@@ -554,7 +576,7 @@ hipError_t launch_quant_col_multi(const QuantParams* ps, int n, hipStream_t s) {
   for (int i = 0; i < n; ++i) {
     const QuantParams& p = ps[i];
     const bool ok = p.grouping == TJ2_GROUP_COL && (p.rounding == TJ2_SR) == sr && (p.rht != 0) == rht &&
-                    ((p.in_dtype == TJ2_BF16 && p.out.fmt == TJ2_NVFP4) ||
+                    ((p.in_dtype == TJ2_BF16 && (p.out.fmt == TJ2_NVFP4 || p.out.fmt == TJ2_NVFP6)) ||
                      (p.in_dtype == TJ2_NVFP4 && p.out.fmt == TJ2_NVFP4) ||
                      (p.in_dtype == TJ2_FP8 && p.out.fmt == TJ2_FP8));
     if (!ok) return hipErrorInvalidValue;

@@ -32,6 +32,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kTiny = 0x1p-100f;     // outer blocks with amax below this are empty
 constexpr float kNvfp4Div = 2688.0f;   // 6 * 448: outer max -> E2M1 max * E4M3 max
+constexpr float kNvfp6Div = 3360.0f;   // 7.5 * 448: outer max -> E2M3 max * E4M3 max
 constexpr float kFp8Div = 448.0f;      // outer max -> E4M3 max
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
@@ -258,12 +259,16 @@ __device__ __forceinline__ float max8_lanes(float x) {
 // ---------------------------------------------------------------------------
 struct GroupScale { float S; float inv; uint32_t s_code; };
 
-__device__ __forceinline__ GroupScale nvfp4_group_scale(float a_o, float a_j) {
+// The element grid's largest value EMAX and the outer divisor EMAX * 448: E2M1 (6, 2688) or E2M3 (7.5, 3360).
+template <int FP6>
+__device__ __forceinline__ GroupScale double_block_scale(float a_o, float a_j) {
+  constexpr float kDiv = FP6 ? kNvfp6Div : kNvfp4Div;
+  constexpr float kEmax = FP6 ? 7.5f : 6.0f;
   GroupScale g;
   if (a_o < kTiny) { g.S = 0.0f; g.inv = 0.0f; g.s_code = 0u; return g; }
-  g.S = a_o / kNvfp4Div;
+  g.S = a_o / kDiv;
   if (a_j == 0.0f) { g.inv = 0.0f; g.s_code = 0u; return g; }
-  float six_s = 6.0f * g.S;
+  float six_s = kEmax * g.S;
   float r = fminf(a_j / six_s, 448.0f);
   uint32_t code;
   float s = e4m3_round_up(r, &code);
@@ -271,6 +276,54 @@ __device__ __forceinline__ GroupScale nvfp4_group_scale(float a_o, float a_j) {
   g.inv = 1.0f / d;
   g.s_code = code;
   return g;
+}
+
+__device__ __forceinline__ GroupScale nvfp4_group_scale(float a_o, float a_j) { return double_block_scale<0>(a_o, a_j); }
+__device__ __forceinline__ GroupScale nvfp6_group_scale(float a_o, float a_j) { return double_block_scale<1>(a_o, a_j); }
+
+// ---------------------------------------------------------------------------
+// E2M3 element rounding (|v| <= 7.5), the FP6 elements of the FP6 x FP4
+// variant, returned as the E4M3FN byte of the E2M3 value (every E2M3 value
+// is an E4M3 value: 0 and k/8 below 1, three mantissa bits from 1 to 7.5).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_byte_of(float r, uint32_t sign) {
+  // r is 0 or an E4M3 normal value (>= 2^-3 here)
+  return r == 0.0f ? sign : sign | ((__float_as_uint(r) >> 20) - 960u);
+}
+
+// nearest, ties to even mantissa, sign kept
+__device__ __forceinline__ uint32_t e2m3_rtn_e4m3(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  float r;
+  if (a < 1.0f) {
+    r = rintf(a * 8.0f) * 0.125f;  // grid k/8, ties to even k
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;  // RNE to 3 mantissa bits
+    r = __uint_as_float(b);
+  }
+  return e4m3_byte_of(r, sign);
+}
+
+// stochastic: with lo <= |v| < hi the neighbouring grid values and
+// t = 65536 (|v| - lo) / (hi - lo) (exact), round up iff u + floor(t) >= 65536,
+// u the 16-bit draw in the top half of rnd
+__device__ __forceinline__ uint32_t e2m3_sr_e4m3(float v, uint32_t rnd) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  float lo, gap;
+  if (a < 1.0f) {
+    lo = floorf(a * 8.0f) * 0.125f;
+    gap = 0.125f;
+  } else {
+    const uint32_t b = __float_as_uint(a) & 0xFFF00000u;  // truncate to 3 mantissa bits
+    lo = __uint_as_float(b);
+    gap = __uint_as_float((b & 0x7F800000u) - (3u << 23));  // 2^(e - 3)
+  }
+  const float t = ((a - lo) / gap) * 65536.0f;  // exact
+  const bool up = lo < 7.5f && (rnd >> 16) + (uint32_t)t >= 65536u;
+  return e4m3_byte_of(up ? lo + gap : lo, sign);
 }
 
 // Scaled element: clamp(y * inv, -6, 6).  An empty group has inv = 0, and

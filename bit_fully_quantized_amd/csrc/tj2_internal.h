@@ -27,7 +27,7 @@ inline QView make_view(const tj2_qtensor& q) {
   v.len = q.len;
   v.nb = (q.len + 127) / 128;
   v.fmt = q.fmt;
-  v.ld_codes = q.fmt == TJ2_FP8 ? v.nb * 128 : v.nb * 64;
+  v.ld_codes = q.fmt == TJ2_NVFP4 ? v.nb * 64 : v.nb * 128;  // FP8 / NVFP6: one byte per element
   v.ld_s16 = v.nb * 8;
   v.ld_s128 = v.nb;
   return v;

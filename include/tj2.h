@@ -45,6 +45,7 @@ typedef int32_t tj2_status;
 #define TJ2_F32 1
 #define TJ2_NVFP4 2
 #define TJ2_FP8 3
+#define TJ2_NVFP6 4 /* E2M3 elements in the NVFP4 double block (the FP6 x FP4 variant) */
 
 /* grouping of a quantizer */
 #define TJ2_GROUP_ROW 0 /* 1x16 groups along the contiguous (column) dimension   */
@@ -71,6 +72,10 @@ typedef int32_t tj2_status;
  *   TJ2_FP8:   codes    uint8 [rows][nb*128] E4M3FN
  *              scale16  unused (may be NULL)
  *              scale128 float [rows][nb]
+ *   TJ2_NVFP6: codes    uint8 [rows][nb*128] E2M3 values, each stored as the
+ *                                            E4M3FN byte of that value
+ *              scale16  uint8 [rows][nb*8]   E4M3FN, one per 16 elements
+ *              scale128 float [rows][nb]     one per 128 elements (amax / 3360)
  * Element positions beyond `len` in each row are padding; producers write
  * them as zero.  `len` must be a positive multiple of 16.
  * E2M1 code: bit 3 sign, bits 2..0 index into {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
@@ -162,8 +167,11 @@ uint16_t tj2_rht_signs(uint64_t seed, uint64_t offset);
  * Philox4x32-10 block e>>3 (counter (lo, hi of e>>3, lo, hi of offset), key seed),
  * word (e>>1)&3, half e&1 (0 = low half).
  *
- * out->fmt selects NVFP4 (scale = amax/2688 per 128, E4M3 round-up per 16) or FP8
- * (E4M3FN elements, scale = amax/448 per 128).  out->rows/len must match.
+ * out->fmt selects NVFP4 (scale = amax/2688 per 128, E4M3 round-up per 16), FP8
+ * (E4M3FN elements, scale = amax/448 per 128) or NVFP6 (E2M3 elements, largest
+ * 7.5, scale = amax/3360 per 128, E4M3 round-up per 16; dense input only; the
+ * FP6 operand of the FP6 x FP4 variant the pages name as future work, section
+ * 5).  out->rows/len must match.
  */
 tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q, int64_t rows,
                           int64_t cols, const int32_t* col_idx, int64_t n_idx, int32_t grouping,
@@ -221,7 +229,7 @@ tj2_status nvfp4_gemm_noalloc(const tj2_qtensor* A, const tj2_qtensor* B, const 
  *   C[i, plan->outliers[j]] = sum_k A[i,k] B8[j,k]   (B8 FP8, j < n_outliers)
  * This is how the backward forms dX (B = re-grouped W-hat of the non-outlier
  * channels, B8 = its FP8 outlier channels) and dW (B, B8 = re-grouped X-hat).
- * A [I, K] NVFP4; B [J - n, K] NVFP4; B8 [n, K] FP8 with n = plan->n_outliers;
+ * A [I, K] NVFP4 (or NVFP6); B [J - n, K] NVFP4; B8 [n, K] FP8 with n = plan->n_outliers;
  * plan arrays sorted ascending, device int32, 16-byte aligned, rest listing the
  * J - n columns not in outliers.  C, ldc (>= J), c_dtype, accumulate and the
  * workspace (nvfp4_gemm_workspace_size(I, J, K, 0) bytes) as for nvfp4_gemm.
@@ -275,6 +283,24 @@ tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, con
                             uint64_t offset, void* dX, int32_t dx_dtype, float* dW,
                             tj2_bwd_operands* ops, void* workspace, size_t ws_bytes, void* stream);
 size_t nvfp4_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers);
+
+/*
+ * The FP6 x FP4 backward (technical summary, section 5 names FP6 x FP4 mixed
+ * precision as a future direction; reading: the gradient operand takes the
+ * wider element): nvfp4_linear_bwd with the two dY operands (ops->dYq [M, N],
+ * ops->dYt [N, M]) in TJ2_NVFP6 -- E2M3 elements under the same E4M3 inner and
+ * FP32 outer scales, the same Hadamard masks, Philox offsets and stochastic
+ * rounding rule -- while the re-grouped W-hat and X-hat stay NVFP4 (and FP8
+ * under a plan).  Arguments, outputs and errors as for nvfp4_linear_bwd; the
+ * workspace (ops == NULL) holds nvfp6x4_linear_bwd_workspace_size(M, N, K,
+ * n_outliers) bytes.
+ */
+tj2_status nvfp6x4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, const tj2_qtensor* Xq,
+                              const tj2_qtensor* X8, const tj2_qtensor* Wq, const tj2_qtensor* W8,
+                              const tj2_outlier_plan* plan, int32_t rht, uint64_t seed, uint64_t offset,
+                              void* dX, int32_t dx_dtype, float* dW, tj2_bwd_operands* ops, void* workspace,
+                              size_t ws_bytes, void* stream);
+size_t nvfp6x4_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers);
 
 /*
  * Oscillation diagnostics (optional in osci_reset_step and master_update_step).

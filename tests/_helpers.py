@@ -25,7 +25,7 @@ def bf16_values(bits: np.ndarray) -> np.ndarray:
 def oracle_qtensor_from_gpu(q) -> quant.QTensor:
     """Oracle-side QTensor holding the GPU's (unpadded) bytes."""
     codes, s16, s128 = q.host()
-    fmt = "nvfp4" if q.fmt == 2 else "fp8"
+    fmt = {2: "nvfp4", 3: "fp8", 4: "nvfp6"}[q.fmt]
     return quant.QTensor(fmt, codes.copy(), s128.copy(), None if s16 is None else s16.copy(), q.rows, q.len)
 
 
@@ -34,7 +34,7 @@ def assert_q_equal(gpu_q, ref: quant.QTensor, rows=None, what=""):
     codes, s16, s128 = gpu_q.host()
     sel = slice(None) if rows is None else rows
     np.testing.assert_array_equal(s128[sel].view(np.uint32), ref.s128.view(np.uint32), err_msg=f"{what}: scale128")
-    if ref.fmt == "nvfp4":
+    if ref.fmt in ("nvfp4", "nvfp6"):
         np.testing.assert_array_equal(s16[sel], ref.s16, err_msg=f"{what}: scale16")
     np.testing.assert_array_equal(codes[sel], ref.codes, err_msg=f"{what}: codes")
 
@@ -67,6 +67,8 @@ def oracle_rows(y_rows: np.ndarray, row_ids, n_cols_total: int, fmt: str, roundi
         u16 = philox.sr_draws_u16(idx, seed, offset)
     if fmt == "nvfp4":
         return quant.nvfp4_quantize_rows(y, rounding, u16)
+    if fmt == "nvfp6":
+        return quant.nvfp6_quantize_rows(y, rounding, u16)
     return quant.fp8_quantize_rows(y, rounding, u16)
 
 
@@ -88,6 +90,8 @@ def oracle_cols(x_cols: np.ndarray, col_ids, n_cols_total: int, fmt: str, roundi
         u16 = philox.sr_draws_u16(idx, seed, offset)
     if fmt == "nvfp4":
         return quant.nvfp4_quantize_rows(y, rounding, u16)
+    if fmt == "nvfp6":
+        return quant.nvfp6_quantize_rows(y, rounding, u16)
     return quant.fp8_quantize_rows(y, rounding, u16)
 
 
