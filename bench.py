@@ -215,6 +215,25 @@ def quantizers_in_step(tj2, lins, layers, M, ws, reps=10):
     return out
 
 
+def fp6_backward(tj2, lins, layers, M, ws, reps=5):
+    """The FP6 x FP4 variant at the 370M shapes: the backward of one layer's five linears (weighted by
+    the number of layers) with FP4 and with FP6 gradient operands (nvfp6x4_linear_bwd), ms per step."""
+    import torch
+    out = {}
+    for name, fmt in (("fp4_grads", tj2.NVFP4), ("fp6_grads", tj2.NVFP6)):
+        t = 0.0
+        for li in lins[:5]:
+            ops = tj2.bwd_operands(M, li.N, li.K, li.plan, grad_fmt=fmt)
+            t += layers * time_launches(lambda: tj2.linear_bwd(li.dY, li.saved, li.K, seed=SEED, offset=0, plan=li.plan,
+                                                               dX=li.dX, dW=li.dW, operands=ops, workspace=ws,
+                                                               grad_fmt=fmt), reps)
+            del ops
+        out[name] = {"bwd_ms_per_step": round(t * 1e3, 3)}
+    torch.cuda.empty_cache()
+    out["fp6_over_fp4_time"] = round(out["fp6_grads"]["bwd_ms_per_step"] / out["fp4_grads"]["bwd_ms_per_step"], 3)
+    return out
+
+
 def single_linear_latency(tj2, reps=50):
     """The single-linear workload (X 256x512, W 512x512 fp32 masters, dY 256x512; RHT on, seed 0): latency
     of the forward (quantizers + product), the backward and one OsciReset window-end step, in us."""
@@ -588,6 +607,8 @@ def main():
         return
     log("quantizers in the step's launch configuration")
     q_in_step = quantizers_in_step(tj2, lins, layers, M, ws)
+    log("FP6 x FP4 backward")
+    fp6 = fp6_backward(tj2, lins, layers, M, ws)
     copy_calibration()
     log("OsciReset pass")
     n_params = sum(li.N * li.K for li in lins)
@@ -682,6 +703,8 @@ def main():
         },
         "quantizers_in_step": {"what": "370M-style step, quantizer time from the step's own calls (linear call "
                                        "minus its products), algorithmic bytes", **q_in_step},
+        "fp6x4_backward": {"what": "backward of the 370M-style linears with FP4 vs FP6 (E2M3, NVFP6) gradient "
+                                   "operands, the FP6 x FP4 variant", **fp6},
         "single_linear": single,
         "olmo70m_linears": olmo70,
         "stack": stack,
