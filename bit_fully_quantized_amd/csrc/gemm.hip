@@ -592,27 +592,34 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     float16v_t part[2];
     part[1] = float16v_t{};
     float32v_t smat = float32v_t{};  // "chunk -1": the first chunk's promotion of part[1] adds 0 * 0
-    F::fetch_b(p, t, 0, s1, b1);
-    if constexpr (MIXB) {
-      half2_t sg[4];
-      FM::prep_b(b1, sg);
-      half8_t* out = reinterpret_cast<half8_t*>(sm.b[0] + (threadIdx.x >> 2) * LDS_STRIDE + t.bq * 32);
-      out[0] = FM::template unit_b<0>(b1, sg, t.b8);
-      out[1] = FM::template unit_b<1>(b1, sg, t.b8);
-      out[2] = FM::template unit_b<2>(b1, sg, t.b8);
-      out[3] = FM::template unit_b<3>(b1, sg, t.b8);
-      sm.sb[0][threadIdx.x >> 2] = b1.S;
-    } else {
-      stage_first_b<FB0>(sm, t, b1);
+    // All first loads are in flight together (one memory latency before the first
+    // chunk): the B slice of chunk 0, staged below, then those the loop keeps in
+    // flight, in its order (the B slice staged next, the A slice, the B slice
+    // after), so the wait counts the compiler derives for the loop body hold on
+    // its first pass too.
+    {
+      Slice b0;
+      F::fetch_b(p, t, 0, s1, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      F::fetch_b(p, t, 1, s1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      F::fetch_a(p, t, 0, s1, a);
+      __builtin_amdgcn_sched_barrier(0);
+      F::fetch_b(p, t, 2, s1, b2);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MIXB) {
+        half2_t sg[4];
+        FM::prep_b(b0, sg);
+        half8_t* out = reinterpret_cast<half8_t*>(sm.b[0] + (threadIdx.x >> 2) * LDS_STRIDE + t.bq * 32);
+        out[0] = FM::template unit_b<0>(b0, sg, t.b8);
+        out[1] = FM::template unit_b<1>(b0, sg, t.b8);
+        out[2] = FM::template unit_b<2>(b0, sg, t.b8);
+        out[3] = FM::template unit_b<3>(b0, sg, t.b8);
+        sm.sb[0][threadIdx.x >> 2] = b0.S;
+      } else {
+        stage_first_b<FB0>(sm, t, b0);
+      }
     }
-    // loads in flight enter the loop in the order the loop keeps them (the B
-    // slice staged next, the A slice, the B slice after), so the wait counts
-    // the compiler derives for the loop body hold on its first pass too
-    F::fetch_b(p, t, 1, s1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    F::fetch_a(p, t, 0, s1, a);
-    __builtin_amdgcn_sched_barrier(0);
-    F::fetch_b(p, t, 2, s1, b2);
     FM::prep_a(a, sga);
     af[0] = FM::template frag_a<0>(a, sga, false);
     barrier_lds();

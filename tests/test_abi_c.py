@@ -45,7 +45,7 @@ int main(void) {
   printf("\n");
   printf("fwd_ws %zu %zu\n", nvfp4_linear_fwd_workspace_size(16384, 4096, 1024, 112),
          nvfp4_linear_fwd_workspace_size(128, 128, 16384, 0));
-  printf("gemm_ws %zu\n", nvfp4_gemm_workspace_size(256, 128, 912, 112));
+  printf("gemm_ws %zu\n", nvfp4_gemm_workspace_size(256, 128, 880, 112));
   printf("sumsq_ws %zu\n", tj2_channel_sumsq_workspace_size(1024, 256));
   return 0;
 }

@@ -270,7 +270,7 @@ def test_select_outliers_errors(L):
 def test_gemm_workspace_counts_both_segments(L):
     # a two-segment product splits over the chunks of both segments
     one = L.nvfp4_gemm_workspace_size(256, 128, 1024, 0)
-    two = L.nvfp4_gemm_workspace_size(256, 128, 912, 112)
+    two = L.nvfp4_gemm_workspace_size(256, 128, 880, 112)
     assert two >= one > 0
 
 

@@ -114,7 +114,7 @@ def test_gemm_output_views(I, J, ld, off):
     np.testing.assert_array_equal(got[:, J:], base[:, J:])
 
 
-@pytest.mark.parametrize("I,J,K1,K2,fmt2", [(256, 128, 912, 112, "fp8"), (200, 112, 4096, 4096, "nvfp4"),
+@pytest.mark.parametrize("I,J,K1,K2,fmt2", [(256, 128, 880, 112, "fp8"), (200, 112, 4096, 4096, "nvfp4"),
                                              (256, 256, 3968, 1024, "fp8")])
 def test_gemm_two_segments_split_k(I, J, K1, K2, fmt2):
     """A two-segment product (NVFP4 x NVFP4 + a second segment) over few output tiles: the K split
@@ -232,3 +232,51 @@ def test_gemm_operand_codes_beyond_4gb():
     torch.cuda.empty_cache()
     ref = ogemm.gemm_nt_f64(ra, rb)
     assert H.rel_fro(C[np.ix_(rows, cols)], ref) <= H.GEMM_TOL
+
+
+@pytest.mark.parametrize("I,J,K", [(8192, 1280, 128), (8192, 1152, 384), (8400, 1040, 640)])
+def test_gemm_persistent_item_sequences(I, J, K):
+    """More work items (256x128 output tiles) than compute units: each workgroup runs several
+    items as one stream of chunks, here items of 1, 3 and 5 chunks (the B prefetch, three
+    chunks ahead, crosses one or more item boundaries) and ragged last row and column tiles;
+    fp32 and bf16 outputs."""
+    ga, gb, ra, rb = _operands(I, J, K, seed=I + J + K)
+    ref = ogemm.gemm_nt_f64(ra, rb)
+    c = tj2.gemm(ga, gb).cpu().numpy()
+    assert H.rel_fro(c, ref) < 1e-5
+    cb = tj2.gemm(ga, gb, out_dtype=torch.bfloat16)
+    assert H.bf16_ulp_ok(cb, ref)
+
+
+def test_gemm_persistent_two_segments_and_outlier_cols():
+    """Many work items through the two-segment product (NVFP4 chunks, then an FP8 chunk, in
+    one pipelined stream: segment changes inside and across items) and through the
+    outlier-column product (B rows staged in output column order from the column map)."""
+    I, J, K1, K2 = 8192, 1152, 256, 112
+    ga, gb, ra, rb = _operands(I, J, K1, seed=31)
+    a8_bits = synthetic.normal_bf16((I, K2), 1.0, 32)
+    b8_f = synthetic.normal_f32((J, K2), 0.02, 33)
+    a8 = tj2.quantize(H.bf16_to_device(a8_bits), out_fmt=tj2.FP8)
+    b8 = tj2.quantize(H.f32_to_device(b8_f), out_fmt=tj2.FP8)
+    ra8 = quant.quantize(H.bf16_values(a8_bits), fmt="fp8")
+    rb8 = quant.quantize(b8_f, fmt="fp8")
+    ref = ogemm.gemm_nt_f64(ra, rb) + ogemm.gemm_nt_f64(ra8, rb8)
+    cb = tj2.gemm(ga, gb, a8, b8, out_dtype=torch.bfloat16)
+    assert H.bf16_ulp_ok(cb, ref)
+    assert H.rel_fro(tj2.gemm(ga, gb, a8, b8).cpu().numpy(), ref) < 1e-5
+
+    outl = np.sort(np.random.default_rng(34).choice(J, 96, replace=False))
+    rest = np.setdiff1d(np.arange(J), outl)
+    b = synthetic.normal_f32((J, K1), 0.02, 35)
+    gb4 = tj2.quantize(H.f32_to_device(b[rest]))
+    gb8 = tj2.quantize(H.f32_to_device(b[outl]), out_fmt=tj2.FP8)
+    rb4 = quant.quantize(np.ascontiguousarray(b[rest]))
+    rb8o = quant.quantize(np.ascontiguousarray(b[outl]), fmt="fp8")
+    H.assert_q_equal(gb4, rb4, what="B")
+    H.assert_q_equal(gb8, rb8o, what="B8")
+    ref2 = np.zeros((I, J))
+    ref2[:, rest] = ogemm.gemm_nt_f64(ra, rb4)
+    ref2[:, outl] = ogemm.gemm_nt_f64(ra, rb8o)
+    plan = tj2.OutlierPlan.from_indices(J, outl)
+    cb2 = tj2.gemm_outlier_cols(ga, gb4, gb8, plan, out_dtype=torch.bfloat16)
+    assert H.bf16_ulp_ok(cb2, ref2)
