@@ -235,11 +235,10 @@ def test_gemm_operand_codes_beyond_4gb():
 
 
 @pytest.mark.parametrize("I,J,K", [(8192, 1280, 128), (8192, 1152, 384), (8400, 1040, 640)])
-def test_gemm_persistent_item_sequences(I, J, K):
-    """More work items (256x128 output tiles) than compute units: each workgroup runs several
-    items as one stream of chunks, here items of 1, 3 and 5 chunks (the B prefetch, three
-    chunks ahead, crosses one or more item boundaries) and ragged last row and column tiles;
-    fp32 and bf16 outputs."""
+def test_gemm_many_tiles_short_reductions(I, J, K):
+    """More 256x128 output tiles than compute units (several rounds of workgroups) over
+    reductions of 1, 3 and 5 chunks (the prefetches of the first chunks run past the last
+    one), with ragged last row and column tiles; fp32 and bf16 outputs."""
     ga, gb, ra, rb = _operands(I, J, K, seed=I + J + K)
     ref = ogemm.gemm_nt_f64(ra, rb)
     c = tj2.gemm(ga, gb).cpu().numpy()
@@ -248,10 +247,9 @@ def test_gemm_persistent_item_sequences(I, J, K):
     assert H.bf16_ulp_ok(cb, ref)
 
 
-def test_gemm_persistent_two_segments_and_outlier_cols():
-    """Many work items through the two-segment product (NVFP4 chunks, then an FP8 chunk, in
-    one pipelined stream: segment changes inside and across items) and through the
-    outlier-column product (B rows staged in output column order from the column map)."""
+def test_gemm_many_tiles_two_segments_and_outlier_cols():
+    """Many output tiles through the two-segment product (NVFP4 chunks, then an FP8 chunk)
+    and through the outlier-column product (NVFP4 and FP8 B rows in one tile)."""
     I, J, K1, K2 = 8192, 1152, 256, 112
     ga, gb, ra, rb = _operands(I, J, K1, seed=31)
     a8_bits = synthetic.normal_bf16((I, K2), 1.0, 32)
