@@ -179,8 +179,8 @@ def product_calls(tj2, li, ops, M, ws):
 def quantizers_in_step(tj2, lins, layers, M, ws, reps=10):
     """Quantizer rates in the step's own launch configuration, from one layer's linears (weighted by
     the number of layers): the forward's quantization of X = (nvfp4_linear_fwd with given weight codes)
-    - (its product alone); the backward's quantizers (the dY row pass and the launch of all column
-    re-groupings) = nvfp4_linear_bwd - (its two products alone).  Algorithmic bytes: inputs read once,
+    - (its product alone); the backward's quantizers (the fused two-grouping pass of dY and the
+    launch of the other column re-groupings) = nvfp4_linear_bwd - (its two products alone).  Algorithmic bytes: inputs read once,
     packed outputs written once."""
     import torch
     per = 0.5 + 1 / 16 + 4 / 128  # NVFP4 bytes per element
@@ -202,8 +202,9 @@ def quantizers_in_step(tj2, lins, layers, M, ws, reps=10):
         fwd_t += layers * max(t_fwd - t_prod_fwd, 0.0)
         fwd_b += layers * (2.0 * M_ * K + M_ * K1 * per + M_ * no * p8)
         bwd_t += layers * max(t_bwd - t_prod_bwd, 0.0)
-        # dY rows; dY columns, W-hat, X-hat (and the FP8 slices) re-grouped: read packed, write packed
-        bwd_b += layers * (2 * (2.0 * M_ * N + M_ * N * per) + 2 * N * K1 * per + 2 * M_ * K1 * per
+        # dY read once into both groupings; W-hat, X-hat (and the FP8 slices) re-grouped: read
+        # packed, write packed
+        bwd_b += layers * (2.0 * M_ * N + 2 * M_ * N * per + 2 * N * K1 * per + 2 * M_ * K1 * per
                            + 2 * (N + M_) * no * p8)
         del ops
     torch.cuda.empty_cache()
@@ -451,6 +452,23 @@ def quant_sweep(tj2, reps=24, nbuf=8):
         t = time_launches(fn, reps)
         gbs = bytes_per_call / t / 1e9
         res[name] = {"us": round(t * 1e6, 2), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 3)}
+    # the fused pass of the backward's output gradient: both groupings (SR + RHT) from one read;
+    # algorithmic bytes: one read, both outputs written
+    state = {"i": 0}
+
+    def dual_fn():
+        i = state["i"] % nbuf
+        state["i"] += 1
+        tj2.quantize_dual(xs[i], rht=True, seed=0, row_offset=2 * i, col_offset=2 * i + 1, row_out=outs_r[i],
+                          col_out=outs_c[i])
+
+    t = time_launches(dual_fn, reps)
+    dual_bytes = R * C * (2 + 2 * (0.5 + 1 / 16 + 4 / 128))
+    gbs = dual_bytes / t / 1e9
+    sep = res["row_sr_rht"]["us"] + res["col_sr_rht"]["us"]
+    res["dual_sr_rht"] = {"what": "both groupings (SR + RHT) from one read, as the backward quantizes dY",
+                          "us": round(t * 1e6, 2), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 3),
+                          "separate_row_plus_col_us": round(sep, 2)}
     # achievable reference on the same rotated buffers: a plain elementwise copy (bf16 negation,
     # 64 MiB read + 64 MiB written per call), and each variant's rate as a fraction of it
     ys = [torch.empty_like(xs[0]) for _ in range(2)]
@@ -465,7 +483,7 @@ def quant_sweep(tj2, reps=24, nbuf=8):
     copy_gbs = 2 * xs[0].numel() * 2 / t / 1e9
     res["copy_reference"] = {"what": "torch bf16 negation on the same buffers (read + write)", "us": round(t * 1e6, 2),
                              "GB_s": round(copy_gbs, 1), "frac_hbm": round(copy_gbs / HBM_PEAK_GBS, 3)}
-    for name in variants:
+    for name in list(variants) + ["dual_sr_rht"]:
         res[name]["frac_of_copy"] = round(res[name]["GB_s"] / copy_gbs, 3)
     del xs, ys, outs_r, outs_c
     torch.cuda.empty_cache()

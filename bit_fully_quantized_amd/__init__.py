@@ -162,6 +162,26 @@ def quantize(x, *, grouping: int = GROUP_ROW, rounding: int = RTN, rht: bool = F
     return out
 
 
+def quantize_dual(x: torch.Tensor, *, rht: bool = True, seed: int = 0, row_offset: int = 0, col_offset: int = 2,
+                  out_fmt: int = NVFP4, row_out: QTensor | None = None,
+                  col_out: QTensor | None = None) -> tuple[QTensor, QTensor]:
+    """Both stochastic groupings of a bf16 tensor [rows, cols] from one read: along cols
+    (signs and draws of row_offset) and along rows, stored transposed (col_offset)."""
+    _dense(x, "x", (torch.bfloat16,))
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    if row_out is None:
+        row_out = QTensor(out_fmt, rows, cols)
+    if col_out is None:
+        col_out = QTensor(out_fmt, cols, rows)
+    rc, cc = row_out.c(), col_out.c()
+    st = lib().nvfp4_quantize_dual(_ptr(x), rows, cols, 1 if rht else 0, seed, row_offset, col_offset,
+                                   ctypes.byref(rc), ctypes.byref(cc), _stream())
+    check("nvfp4_quantize_dual", st)
+    return row_out, col_out
+
+
 def gemm_workspace(I: int, J: int, K: int, K2: int = 0, device="cuda") -> torch.Tensor | None:
     """Split-K workspace of an I x J product over K (+ K2 for a second segment), or None."""
     n = int(lib().nvfp4_gemm_workspace_size(I, J, K, K2))

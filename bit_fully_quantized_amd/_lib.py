@@ -92,6 +92,7 @@ SIGNATURES = {
     "tj2_qtensor_bytes": (I32, [I32, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
     "tj2_rht_signs": (ctypes.c_uint16, [U64, U64]),
     "nvfp4_quantize": (I32, [P, I32, QP, I64, I64, P, I64, I32, I32, I32, U32, U64, U64, QP, P]),
+    "nvfp4_quantize_dual": (I32, [P, I64, I64, I32, U64, U64, U64, QP, QP, P]),
     "nvfp4_gemm": (I32, [QP, QP, QP, QP, P, I32, I64, P, I32, P, SZ, P]),
     "nvfp4_gemm_workspace_size": (SZ, [I64, I64, I64, I64]),
     "nvfp4_gemm_noalloc": (I32, [QP, QP, QP, QP, P, I32, I64, P, I32, P]),

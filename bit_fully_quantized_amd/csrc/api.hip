@@ -343,6 +343,41 @@ tj2_status tj2_qtensor_bytes(int32_t fmt, int64_t rows, int64_t len, size_t* cod
 
 uint16_t tj2_rht_signs(uint64_t seed, uint64_t offset) { return (uint16_t)(philox_word0(seed, offset) & 0xFFFFu); }
 
+tj2_status run_quant_dual(const void* x, int64_t rows, int64_t cols, int rht, uint64_t seed, uint64_t row_offset,
+                          uint64_t col_offset, const tj2_qtensor* row_out, const tj2_qtensor* col_out, hipStream_t s) {
+  DualParams d;
+  d.x = reinterpret_cast<const uint16_t*>(x);
+  d.rows = rows;
+  d.cols = cols;
+  d.row_out = make_view(*row_out);
+  d.col_out = make_view(*col_out);
+  d.row_mask = rht ? tj2_rht_signs(seed, row_offset) & 0xFFFFu : 0u;
+  d.col_mask = rht ? tj2_rht_signs(seed, col_offset) & 0xFFFFu : 0u;
+  d.seed = seed;
+  d.row_offset = row_offset;
+  d.col_offset = col_offset;
+  d.rht = rht ? 1 : 0;
+  return hip_check(launch_quant_dual(d, s), "dual quantize launch");
+}
+
+tj2_status nvfp4_quantize_dual(const void* x, int64_t rows, int64_t cols, int32_t rht, uint64_t seed,
+                               uint64_t row_offset, uint64_t col_offset, tj2_qtensor* row_out, tj2_qtensor* col_out,
+                               void* stream) {
+  if (!x || !row_out || !col_out) return fail(TJ2_ERR_ARG, "x, row_out and col_out are required");
+  if (!aligned16(x)) return fail(TJ2_ERR_ALIGN, "x must be 16-byte aligned");
+  if (rows <= 0 || cols <= 0) return fail(TJ2_ERR_SHAPE, "rows and cols must be positive");
+  if (rows > (int64_t)1 << 30 || cols > (int64_t)1 << 30) return fail(TJ2_ERR_SHAPE, "dimension too large");
+  if (rows % 16 || cols % 16) return fail(TJ2_ERR_SHAPE, "rows and cols must be multiples of 16");
+  if (row_out->fmt != TJ2_NVFP4 && row_out->fmt != TJ2_NVFP6)
+    return fail(TJ2_ERR_ARG, "outputs must be NVFP4 or NVFP6");
+  if (col_out->fmt != row_out->fmt) return fail(TJ2_ERR_ARG, "row_out and col_out must have the same format");
+  TJ2_TRY(check_qtensor(row_out, "row_out", row_out->fmt, rows, cols));
+  TJ2_TRY(check_qtensor(col_out, "col_out", col_out->fmt, cols, rows));
+  if (((rows + 127) / 128) * ((cols + 127) / 128) >= ((int64_t)1 << 31)) return fail(TJ2_ERR_SHAPE, "tensor too large for one launch");
+  return run_quant_dual(x, rows, cols, rht, seed, row_offset, col_offset, row_out, col_out, (hipStream_t)stream) == TJ2_OK
+             ? ok() : TJ2_ERR_HIP;
+}
+
 tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q, int64_t rows, int64_t cols,
                           const int32_t* col_idx, int64_t n_idx, int32_t grouping, int32_t rounding, int32_t rht,
                           uint32_t rht_signs, uint64_t seed, uint64_t offset, tj2_qtensor* out, void* stream) {
@@ -550,9 +585,11 @@ tj2_status linear_bwd_impl(int gfmt, const void* dY, int64_t M, int64_t N, int64
   const int r = rht ? 1 : 0;
   const uint32_t mdx = r ? tj2_rht_signs(seed, offset + 0) : 0u;
   const uint32_t mdw = r ? tj2_rht_signs(seed, offset + 2) : 0u;
-  TJ2_TRY(run_quant(dY, TJ2_BF16, nullptr, M, N, nullptr, 0, TJ2_GROUP_ROW, TJ2_SR, r, mdx, seed, offset + 0, &o->dYq, s));
-  // the column (re-grouped, transposed) operands of both products in one launch,
-  // the small FP8 slices first so their latency hides behind the large problems
+  // dY once into both groupings: dYq along N (dX signs, draws at offset + 0) and
+  // dY^T q along M (dW signs, offset + 2)
+  TJ2_TRY(run_quant_dual(dY, M, N, r, seed, offset + 0, offset + 2, &o->dYq, &o->dYt, s));
+  // the other column (re-grouped, transposed) operands of both products in one
+  // launch, the small FP8 slices first so their latency hides behind the large ones
   QuantParams cols[kColMultiMax];
   int nc = 0;
   const bool w_given = ops && ops->w_given;  // the re-grouped weights come from the master pass
@@ -564,7 +601,6 @@ tj2_status linear_bwd_impl(int gfmt, const void* dY, int64_t M, int64_t N, int64
   if (!w_given)
     cols[nc++] = quant_params(nullptr, TJ2_NVFP4, Wq, N, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 1, &o->Wt);
   cols[nc++] = quant_params(nullptr, TJ2_NVFP4, Xq, M, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 3, &o->Xt);
-  cols[nc++] = quant_params(dY, TJ2_BF16, nullptr, M, N, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 2, &o->dYt);
   TJ2_TRY(hip_check(launch_quant_col_multi(cols, nc, s), "column quantize launch"));
   if (!plan) {
     TJ2_TRY(run_gemm(&o->dYq, &o->Wt, nullptr, nullptr, dX, dx_dtype, K, nullptr, 0, gemm_ws, gws, s));

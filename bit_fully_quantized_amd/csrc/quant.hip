@@ -453,7 +453,131 @@ hipError_t dispatch_col(const QuantParams& p, hipStream_t s) {
   return p.out.fmt == TJ2_FP8 ? dispatch_col_rs<IN, TJ2_FP8>(p, s) : dispatch_col_rs<IN, TJ2_NVFP4>(p, s);
 }
 
+// ----------------------------------------------------------------------------
+// Both backward groupings of the output gradient from one read (TetraJet-v2
+// technical summary, sections 2.A and 2.C: dY enters dX = Q(dY) Q(W^T) grouped
+// along N and dW = Q(dY^T) Q(X^T) grouped along M, each with its own Hadamard
+// signs and draws).  A workgroup stages a 128 x 128 tile of dY (rows m,
+// columns n) in LDS with coalesced reads.  Its rows are 8 row groups each, one
+// outer block along N, quantized as quant_row does (one lane per group, the 8
+// lanes of an outer block consecutive); its columns are 8 column groups each,
+// one outer block along M, quantized as quant_col does (a lane takes two
+// columns x 16 rows).  Codes, scales and draws equal those of the two separate
+// passes.
+// ----------------------------------------------------------------------------
+template <int OF, bool RHT>
+__global__ __launch_bounds__(256) void quant_dual_kernel(DualParams p) {
+  constexpr int kW = 64 + 1;  // a tile row: 128 bf16 as 64 words, padded
+  __shared__ uint32_t tile[128 * kW];
+  const uint32_t nbC = (uint32_t)((p.cols + 127) / 128);
+  const int64_t rb = (int64_t)(blockIdx.x / nbC) * 128, cb = (int64_t)(blockIdx.x % nbC) * 128;
+  {
+    // 128 rows x 16 pieces of 16 bytes, eight per lane, all in flight before the LDS writes
+    uint4 t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = (int)threadIdx.x + 256 * i, row = idx >> 4, seg = idx & 15;
+      const int64_t r = rb + row, c = cb + seg * 8;
+      t[i] = (r < p.rows && c < p.cols) ? *reinterpret_cast<const uint4*>(p.x + r * p.cols + c)
+                                          : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = (int)threadIdx.x + 256 * i, row = idx >> 4, seg = idx & 15;
+      uint32_t* d = tile + row * kW + seg * 4;
+      d[0] = t[i].x; d[1] = t[i].y; d[2] = t[i].z; d[3] = t[i].w;
+    }
+  }
+  __syncthreads();
+
+  // row groups: 1024 per tile, four per lane
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int g = pass * 256 + (int)threadIdx.x, row = g >> 3, j = g & 7;
+    const int64_t R = rb + row;
+    if (R < p.rows) {  // the 8 lanes of a row exit together
+      const bool valid = cb + j * 16 < p.cols;
+      float v[16];
+      const uint32_t* w = tile + row * kW + j * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b = valid ? w[i] : 0u;
+        v[2 * i] = __uint_as_float(b << 16);
+        v[2 * i + 1] = __uint_as_float(b & 0xFFFF0000u);
+      }
+      if (RHT && valid) rht16(v, p.row_mask);
+      float a_j = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
+      const float a_o = max8_lanes(a_j);
+      uint32_t u[16];
+      const uint64_t e0 = (uint64_t)R * (uint64_t)p.cols + (uint64_t)(cb + j * 16);
+      draws8(e0 >> 3, p.seed, p.row_offset, u);
+      draws8((e0 >> 3) + 1, p.seed, p.row_offset, u + 8);
+      uint32_t codes[4], s_code;
+      float S;
+      quantize_group<OF, true>(v, a_o, a_j, u, codes, &s_code, &S);
+      store_group<OF>(p.row_out, R, (cb >> 4) + j, codes, s_code);
+      if (j == 0) p.row_out.s128[R * p.row_out.ld_s128 + (cb >> 7)] = S;
+    }
+  }
+
+  // column groups: lane (cg, rs) of wave w takes tile columns 64 pass + 16w + 2cg, +1 and
+  // rows 16rs..16rs+15
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cg = lane >> 3, rs = lane & 7;
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cl = pass * 64 + wave * 16 + cg * 2;
+    const int64_t c0 = cb + cl;
+    if (c0 >= p.cols) continue;  // all 8 lanes of this column pair together
+    const int64_t r0 = rb + rs * 16;
+    const bool valid = r0 < p.rows;
+    float vv[2][16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint32_t b = tile[(rs * 16 + t) * kW + (cl >> 1)];
+      vv[0][t] = __uint_as_float(b << 16);
+      vv[1][t] = __uint_as_float(b & 0xFFFF0000u);
+    }
+    static_for<2>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      float* v = vv[k];
+      if (RHT && valid) rht16(v, p.col_mask);
+      float a_j = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
+      const float a_o = max8_lanes(a_j);
+      const int64_t orow = c0 + k;  // output row = input column
+      uint32_t u[16];
+      const uint64_t b = ((uint64_t)orow * (uint64_t)p.rows + (uint64_t)r0) >> 3;
+      draws8(b, p.seed, p.col_offset, u);
+      draws8(b + 1, p.seed, p.col_offset, u + 8);
+      uint32_t codes[4], s_code;
+      float S;
+      quantize_group<OF, true>(v, a_o, a_j, u, codes, &s_code, &S);
+      // groups past the last row are the zero padding of the output's last block
+      store_group<OF>(p.col_out, orow, r0 >> 4, codes, s_code);
+      if (rs == 0) p.col_out.s128[orow * p.col_out.ld_s128 + (rb >> 7)] = S;
+    });
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quant_dual(const DualParams& p, hipStream_t s) {
+  const int64_t tiles = ((p.rows + 127) / 128) * ((p.cols + 127) / 128);
+  if (tiles >= ((int64_t)1 << 31) || (p.cols % 16) != 0) return hipErrorInvalidValue;
+  const dim3 grid((uint32_t)tiles);
+  if (p.row_out.fmt == TJ2_NVFP6) {
+    if (p.rht) hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP6, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP6, false>), grid, dim3(256), 0, s, p);
+  } else {
+    if (p.rht) hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP4, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP4, false>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
 
 // ----------------------------------------------------------------------------
 // Forward split with an outlier plan (TetraJet-v2 technical summary, section

@@ -69,6 +69,21 @@ struct SplitParams {
 
 hipError_t launch_quant_split(const SplitParams& p, hipStream_t s);
 
+// Both backward groupings of a bf16 [rows, cols] gradient from one read, with
+// stochastic rounding: row_out [rows, cols] grouped along cols (signs row_mask,
+// draws at row_offset) and col_out [cols, rows] grouped along rows (col_mask,
+// col_offset); NVFP4 or NVFP6 (both outputs the same format).
+struct DualParams {
+  const uint16_t* x;
+  int64_t rows, cols;
+  QView row_out, col_out;
+  uint32_t row_mask, col_mask;
+  uint64_t seed, row_offset, col_offset;
+  int rht;
+};
+
+hipError_t launch_quant_dual(const DualParams& p, hipStream_t s);
+
 struct GemmSeg {
   QView a, b;  // a: [I, K], b: [J, K] grouped along K
   int64_t K;

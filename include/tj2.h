@@ -179,6 +179,23 @@ tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q
                           uint64_t offset, tj2_qtensor* out, void* stream);
 
 /*
+ * The output gradient's two backward operands from one read (section 2.A: dY
+ * enters dX grouped along N and dW grouped along M; section 2.C: each with a
+ * 16-wide random Hadamard transform): x bf16 [rows, cols] row-major (16-byte
+ * aligned, rows and cols multiples of 16) -> row_out [rows, cols] grouped along cols
+ * (Hadamard signs tj2_rht_signs(seed, row_offset), stochastic draws at
+ * row_offset) and col_out [cols, rows] grouped along rows, stored transposed
+ * (signs tj2_rht_signs(seed, col_offset), draws at col_offset).  Both outputs
+ * TJ2_NVFP4, or both TJ2_NVFP6; rht = 0 skips the transforms.  The codes,
+ * scales and draws equal those of two nvfp4_quantize calls (TJ2_SR, the same
+ * signs and offsets); nvfp4_linear_bwd quantizes dY with it (row_offset =
+ * offset, col_offset = offset + 2).
+ */
+tj2_status nvfp4_quantize_dual(const void* x, int64_t rows, int64_t cols, int32_t rht, uint64_t seed,
+                               uint64_t row_offset, uint64_t col_offset, tj2_qtensor* row_out,
+                               tj2_qtensor* col_out, void* stream);
+
+/*
  * Product on packed operands (section 2: every linear-layer product runs on the
  * quantized tensors).  C[i, col(j)] (+)= sum_k A[i,k] B[j,k] + sum_k A2[i,k] B2[j,k]
  * with A [I, K] and B [J, K] grouped along K, each NVFP4 or FP8; the optional

@@ -30,7 +30,7 @@ def L():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_outlier_cols", "nvfp4_linear_fwd", "nvfp4_linear_bwd", "osci_reset_step",
+    for n in ["nvfp4_quantize", "nvfp4_quantize_dual", "nvfp4_gemm", "nvfp4_gemm_outlier_cols", "nvfp4_linear_fwd", "nvfp4_linear_bwd", "osci_reset_step",
               "osci_reset_step_multi", "master_update_step", "master_update_step_multi", "tj2_channel_sumsq", "tj2_rht_signs", "tj2_last_error", "tj2_qtensor_bytes",
               "tj2_select_outliers", "tj2_channel_sumsq_workspace_size", "nvfp4_linear_fwd_workspace_size",
               "nvfp4_gemm_workspace_size", "nvfp4_linear_bwd_workspace_size"]:
@@ -86,6 +86,22 @@ def test_quantize_argument_errors(L):
     assert b"expected" in L.tj2_last_error()
     # gather with column grouping is unsupported
     assert q(0x1000, _lib.BF16, None, 32, 64, 0x3000, 16, 1, 0, 0, 0, 0, 0, ctypes.byref(out), None) == _lib.TJ2_ERR_UNSUPPORTED
+
+
+def test_quantize_dual_argument_errors(L):
+    from bit_fully_quantized_amd import _lib
+    r, c = fake_q(_lib.NVFP4, 32, 64), fake_q(_lib.NVFP4, 64, 32, base=0x20000)
+    q = lambda x, rows, cols, ro, co: L.nvfp4_quantize_dual(x, rows, cols, 1, 0, 0, 2, ro, co, None)
+    assert q(0x1000, 32, 64, None, ctypes.byref(c)) == _lib.TJ2_ERR_ARG
+    assert q(0x1002, 32, 64, ctypes.byref(r), ctypes.byref(c)) == _lib.TJ2_ERR_ALIGN
+    assert q(0x1000, 32, 40, ctypes.byref(r), ctypes.byref(c)) == _lib.TJ2_ERR_SHAPE
+    # col_out is [cols, rows]
+    assert q(0x1000, 32, 64, ctypes.byref(r), ctypes.byref(r)) == _lib.TJ2_ERR_SHAPE
+    # FP8 outputs, or mixed formats, are refused
+    r8, c8 = fake_q(_lib.FP8, 32, 64), fake_q(_lib.FP8, 64, 32, base=0x20000)
+    assert q(0x1000, 32, 64, ctypes.byref(r8), ctypes.byref(c8)) == _lib.TJ2_ERR_ARG
+    c6 = fake_q(_lib.NVFP6, 64, 32, base=0x20000)
+    assert q(0x1000, 32, 64, ctypes.byref(r), ctypes.byref(c6)) == _lib.TJ2_ERR_ARG
 
 
 def test_gemm_and_linear_argument_errors(L):
