@@ -47,6 +47,12 @@ int main(void) {
          nvfp4_linear_fwd_workspace_size(128, 128, 16384, 0));
   printf("gemm_ws %zu\n", nvfp4_gemm_workspace_size(256, 128, 880, 112));
   printf("sumsq_ws %zu\n", tj2_channel_sumsq_workspace_size(1024, 256));
+  /* the fused two-grouping quantizer refuses mismatched outputs before any device work */
+  tj2_qtensor r = {0}, q = {0};
+  r.rows = 32; r.len = 64; r.fmt = TJ2_NVFP4;
+  q.rows = 64; q.len = 32; q.fmt = TJ2_NVFP6;
+  printf("dual_fmt %d\n", nvfp4_quantize_dual((const void*)0x1000, 32, 64, 1, 0, 0, 2, &r, &q, NULL));
+  printf("dual_shape %d\n", nvfp4_quantize_dual((const void*)0x1000, 32, 40, 1, 0, 0, 2, &r, &r, NULL));
   return 0;
 }
 """
@@ -86,4 +92,6 @@ def test_c_program_against_header_and_library(tmp_path):
     fwd = [int(x) for x in kv["fwd_ws"].split()]
     assert fwd[0] == 0 and fwd[1] > 0  # many output tiles: no split; one tile over a long K: split
     assert int(kv["gemm_ws"]) > 0
+    assert kv["dual_fmt"] == "1"      # TJ2_ERR_ARG: NVFP4 rows, NVFP6 columns
+    assert kv["dual_shape"] == "2"    # TJ2_ERR_SHAPE: cols not a multiple of 16
     assert int(kv["sumsq_ws"]) == 2 * 256 * 8
