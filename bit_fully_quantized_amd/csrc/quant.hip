@@ -457,7 +457,7 @@ hipError_t dispatch_col(const QuantParams& p, hipStream_t s) {
 // Both backward groupings of the output gradient from one read (TetraJet-v2
 // technical summary, sections 2.A and 2.C: dY enters dX = Q(dY) Q(W^T) grouped
 // along N and dW = Q(dY^T) Q(X^T) grouped along M, each with its own Hadamard
-// signs and draws).  A workgroup stages a 128 x 128 tile of dY (rows m,
+// signs and draws).  A workgroup of 512 lanes stages a 128 x 128 tile of dY (rows m,
 // columns n) in LDS with coalesced reads.  Its rows are 8 row groups each, one
 // outer block along N, quantized as quant_row does (one lane per group, the 8
 // lanes of an outer block consecutive); its columns are 8 column groups each,
@@ -465,35 +465,39 @@ hipError_t dispatch_col(const QuantParams& p, hipStream_t s) {
 // columns x 16 rows).  Codes, scales and draws equal those of the two separate
 // passes.
 // ----------------------------------------------------------------------------
+// 512 lanes: two row groups and two column groups per lane; 70 VGPRs and 33 KB
+// of LDS allow six waves per SIMD (256 lanes: four, 4-8% slower).
+constexpr int kDualThreads = 512;
 template <int OF, bool RHT>
-__global__ __launch_bounds__(256) void quant_dual_kernel(DualParams p) {
+__global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) {
+  constexpr int kT = kDualThreads;
   constexpr int kW = 64 + 1;  // a tile row: 128 bf16 as 64 words, padded
   __shared__ uint32_t tile[128 * kW];
   const uint32_t nbC = (uint32_t)((p.cols + 127) / 128);
   const int64_t rb = (int64_t)(blockIdx.x / nbC) * 128, cb = (int64_t)(blockIdx.x % nbC) * 128;
   {
-    // 128 rows x 16 pieces of 16 bytes, eight per lane, all in flight before the LDS writes
-    uint4 t[8];
+    // 128 rows x 16 pieces of 16 bytes, all of a lane's in flight before the LDS writes
+    uint4 t[2048 / kT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = (int)threadIdx.x + 256 * i, row = idx >> 4, seg = idx & 15;
+    for (int i = 0; i < 2048 / kT; ++i) {
+      const int idx = (int)threadIdx.x + kT * i, row = idx >> 4, seg = idx & 15;
       const int64_t r = rb + row, c = cb + seg * 8;
       t[i] = (r < p.rows && c < p.cols) ? *reinterpret_cast<const uint4*>(p.x + r * p.cols + c)
                                           : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = (int)threadIdx.x + 256 * i, row = idx >> 4, seg = idx & 15;
+    for (int i = 0; i < 2048 / kT; ++i) {
+      const int idx = (int)threadIdx.x + kT * i, row = idx >> 4, seg = idx & 15;
       uint32_t* d = tile + row * kW + seg * 4;
       d[0] = t[i].x; d[1] = t[i].y; d[2] = t[i].z; d[3] = t[i].w;
     }
   }
   __syncthreads();
 
-  // row groups: 1024 per tile, four per lane
+  // row groups: 1024 per tile
 #pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int g = pass * 256 + (int)threadIdx.x, row = g >> 3, j = g & 7;
+  for (int pass = 0; pass < 1024 / kT; ++pass) {
+    const int g = pass * kT + (int)threadIdx.x, row = g >> 3, j = g & 7;
     const int64_t R = rb + row;
     if (R < p.rows) {  // the 8 lanes of a row exit together
       const bool valid = cb + j * 16 < p.cols;
@@ -522,13 +526,13 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(DualParams p) {
     }
   }
 
-  // column groups: lane (cg, rs) of wave w takes tile columns 64 pass + 16w + 2cg, +1 and
-  // rows 16rs..16rs+15
+  // column groups: lane (cg, rs) of wave w takes tile columns 16 (kT / 64) pass + 16w + 2cg, +1
+  // and rows 16rs..16rs+15
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cg = lane >> 3, rs = lane & 7;
 #pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    const int cl = pass * 64 + wave * 16 + cg * 2;
+  for (int pass = 0; pass < 128 * 64 / (16 * kT); ++pass) {
+    const int cl = pass * (kT / 4) + wave * 16 + cg * 2;
     const int64_t c0 = cb + cl;
     if (c0 >= p.cols) continue;  // all 8 lanes of this column pair together
     const int64_t r0 = rb + rs * 16;
@@ -570,11 +574,11 @@ hipError_t launch_quant_dual(const DualParams& p, hipStream_t s) {
   if (tiles >= ((int64_t)1 << 31) || (p.cols % 16) != 0) return hipErrorInvalidValue;
   const dim3 grid((uint32_t)tiles);
   if (p.row_out.fmt == TJ2_NVFP6) {
-    if (p.rht) hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP6, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP6, false>), grid, dim3(256), 0, s, p);
+    if (p.rht) hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP6, true>), grid, dim3(kDualThreads), 0, s, p);
+    else hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP6, false>), grid, dim3(kDualThreads), 0, s, p);
   } else {
-    if (p.rht) hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP4, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP4, false>), grid, dim3(256), 0, s, p);
+    if (p.rht) hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP4, true>), grid, dim3(kDualThreads), 0, s, p);
+    else hipLaunchKernelGGL((quant_dual_kernel<TJ2_NVFP4, false>), grid, dim3(kDualThreads), 0, s, p);
   }
   return hipGetLastError();
 }
