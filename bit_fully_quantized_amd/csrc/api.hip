@@ -176,9 +176,46 @@ tj2_status run_split(const void* x, int x_dtype, int64_t rows, int64_t K, const 
   return hip_check(launch_quant_split(p, s), "split quantize launch");
 }
 
+// B image of a product (scratch for its f16 decode; ready = already written by
+// B's producer).
+struct GemmImage {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  int ready = 0;
+};
+
+// Image bytes of a one-segment product of I x J over K (0 when it would not pay).
+size_t image_bytes(int64_t I, int64_t J, int64_t K) {
+  return gemm_image_pays(I) ? align256(gemm_image_bytes(J, (K + 127) / 128)) : 0;
+}
+
+// The image part of a product's workspace: after its split-K partials (need
+// bytes, 256-aligned) when the workspace holds img_bytes more (else none).
+GemmImage workspace_image(void* workspace, size_t ws_bytes, size_t need, size_t img_bytes) {
+  GemmImage g;
+  const uintptr_t base = reinterpret_cast<uintptr_t>(workspace);
+  const size_t at = ((base + need + 255) & ~(uintptr_t)255) - base;
+  if (img_bytes && ws_bytes >= at + img_bytes) {
+    g.ptr = reinterpret_cast<uint8_t*>(workspace) + at;
+    g.bytes = img_bytes;
+  }
+  return g;
+}
+
+// Point the column quantization q at the B image `img` of a product over K
+// with J output columns: q's output row i is image row rows[i] (NULL: i).
+void set_image(QuantParams& q, uint8_t* img, int64_t J, int64_t K, const int32_t* rows) {
+  const int64_t tiles = (J + 127) / 128, nch = (K + 127) / 128;
+  q.img = img;
+  q.img_rows = rows;
+  q.img_nch = nch;
+  q.img_ld = tiles * 128;
+  q.img_sc = reinterpret_cast<float*>(img + (size_t)tiles * (size_t)nch * kImgChunkBytes);
+}
+
 tj2_status run_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2, const tj2_qtensor* B2,
                     void* C, int c_dtype, int64_t ldc, const int32_t* col_map, int accumulate, void* ws,
-                    size_t ws_bytes, hipStream_t s) {
+                    size_t ws_bytes, hipStream_t s, const GemmImage& img = GemmImage{}) {
   GemmParams p;
   memset(&p, 0, sizeof(p));
   p.seg[0].a = make_view(*A);
@@ -200,13 +237,16 @@ tj2_status run_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtenso
   p.accumulate = accumulate;
   p.partial = reinterpret_cast<float*>(ws);
   p.partial_bytes = ws ? ws_bytes : 0;
+  p.bimg = img.ptr;
+  p.bimg_bytes = img.bytes;
+  p.bimg_ready = img.ready;
   return hip_check(launch_gemm(p, s), "gemm launch");
 }
 
 // C[:, rest[j]] = A . B[j]^T and C[:, outliers[i]] = A . B8[i]^T in one product.
 tj2_status run_gemm_outl(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* B8,
                          const tj2_outlier_plan* plan, void* C, int c_dtype, int64_t ldc, int accumulate, void* ws,
-                         size_t ws_bytes, hipStream_t s) {
+                         size_t ws_bytes, hipStream_t s, const GemmImage& img = GemmImage{}) {
   GemmParams p;
   memset(&p, 0, sizeof(p));
   p.seg[0].a = make_view(*A);
@@ -225,6 +265,9 @@ tj2_status run_gemm_outl(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_q
   p.accumulate = accumulate;
   p.partial = reinterpret_cast<float*>(ws);
   p.partial_bytes = ws ? ws_bytes : 0;
+  p.bimg = img.ptr;
+  p.bimg_bytes = img.bytes;
+  p.bimg_ready = img.ready;
   return hip_check(launch_gemm(p, s), "gemm launch");
 }
 
@@ -262,7 +305,8 @@ size_t bwd_workspace_size(int gfmt, int64_t M, int64_t N, int64_t K, int32_t n_o
   size_t t = carve_size(gfmt, M, N) + carve_size(gfmt, N, M) + carve_size(TJ2_NVFP4, K1, N) +
              carve_size(TJ2_NVFP4, K1, M);
   if (n_outliers) t += carve_size(TJ2_FP8, n_outliers, N) + carve_size(TJ2_FP8, n_outliers, M);
-  return t + 256 + bwd_gemm_ws(M, N, K1, n_outliers);
+  // the B images of dX (over N) and dW (over M), where they pay
+  return t + 256 + bwd_gemm_ws(M, N, K1, n_outliers) + image_bytes(M, K, N) + image_bytes(N, K, M);
 }
 
 tj2_status check_plan(const tj2_outlier_plan* plan, int64_t K) {
@@ -422,20 +466,24 @@ tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q
 
 size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K, int64_t K2) {
   if (I <= 0 || J <= 0 || K <= 0 || K2 < 0) return 0;
-  return gemm_workspace_bytes(I, J, gemm_chunks(K, K2));
+  const size_t part = gemm_workspace_bytes(I, J, gemm_chunks(K, K2));
+  const size_t img = K2 == 0 ? image_bytes(I, J, K) : 0;
+  return img ? align256(part) + img : part;
 }
 
 tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2, const tj2_qtensor* B2,
                       void* C, int32_t c_dtype, int64_t ldc, const int32_t* col_map, int32_t accumulate,
                       void* workspace, size_t ws_bytes, void* stream) {
   TJ2_TRY(check_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate));
+  GemmImage img;
   if (workspace) {
     if (!aligned16(workspace)) return fail(TJ2_ERR_ALIGN, "workspace must be 16-byte aligned");
     const size_t need = gemm_workspace_bytes(A->rows, B->rows, gemm_chunks(A->len, A2 ? A2->len : 0));
     if (ws_bytes < need) return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    img = workspace_image(workspace, ws_bytes, need, A2 ? 0 : image_bytes(A->rows, B->rows, A->len));
   }
   return run_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate, workspace, workspace ? ws_bytes : 0,
-                  (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
+                  (hipStream_t)stream, img) == TJ2_OK ? ok() : TJ2_ERR_HIP;
 }
 
 tj2_status nvfp4_gemm_noalloc(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2,
@@ -470,12 +518,14 @@ tj2_status nvfp4_gemm_outlier_cols(const tj2_qtensor* A, const tj2_qtensor* B, c
   if (accumulate && c_dtype != TJ2_F32) return fail(TJ2_ERR_UNSUPPORTED, "accumulate needs an fp32 output");
   if (ldc < J) return fail(TJ2_ERR_SHAPE, "ldc < J");
   if (A->rows > ((int64_t)1 << 24) * 128 || J > ((int64_t)1 << 24) * 128) return fail(TJ2_ERR_SHAPE, "too many rows");
+  GemmImage img;
   if (workspace) {
     const size_t need = gemm_workspace_bytes(A->rows, J, gemm_chunks(A->len, 0));
     if (ws_bytes < need) return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    img = workspace_image(workspace, ws_bytes, need, image_bytes(A->rows, J, A->len));
   }
   return run_gemm_outl(A, B, B8, plan, C, c_dtype, ldc, accumulate, workspace, workspace ? ws_bytes : 0,
-                       (hipStream_t)stream) == TJ2_OK ? ok() : TJ2_ERR_HIP;
+                       (hipStream_t)stream, img) == TJ2_OK ? ok() : TJ2_ERR_HIP;
 }
 
 size_t nvfp4_linear_fwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers) {
@@ -553,7 +603,17 @@ tj2_status linear_bwd_impl(int gfmt, const void* dY, int64_t M, int64_t N, int64
   tj2_bwd_operands local;
   tj2_bwd_operands* o = ops;
   const size_t gws = bwd_gemm_ws(M, N, K1, no);
+  // B images of the two products (dX: Wt / W8t over N; dW: Xt / X8t over M),
+  // written by the column quantization below
+  const size_t idx_bytes = image_bytes(M, K, N), idw_bytes = image_bytes(N, K, M);
   void* gemm_ws = nullptr;
+  GemmImage img_dx, img_dw;
+  auto carve_images = [&](uint8_t*& cur) {
+    if (idx_bytes) img_dx = GemmImage{cur, idx_bytes, 1};
+    cur += idx_bytes;
+    if (idw_bytes) img_dw = GemmImage{cur, idw_bytes, 1};
+    cur += idw_bytes;
+  };
   if (!o) {
     const size_t need = bwd_workspace_size(gfmt, M, N, K, (int32_t)no);
     if (!workspace || ws_bytes < need)
@@ -561,6 +621,7 @@ tj2_status linear_bwd_impl(int gfmt, const void* dY, int64_t M, int64_t N, int64
     uint8_t* cur = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
     gemm_ws = gws ? cur : nullptr;
     cur += gws;
+    carve_images(cur);
     memset(&local, 0, sizeof(local));
     local.dYq = carve(cur, gfmt, M, N);
     local.dYt = carve(cur, gfmt, N, M);
@@ -573,6 +634,13 @@ tj2_status linear_bwd_impl(int gfmt, const void* dY, int64_t M, int64_t N, int64
     o = &local;
   } else {
     if (workspace && ws_bytes >= gws && aligned16(workspace)) gemm_ws = gws ? workspace : nullptr;
+    // images too when the workspace holds them after the split-K partials
+    const uintptr_t base = reinterpret_cast<uintptr_t>(workspace);
+    const uintptr_t img0 = (base + gws + 255) & ~(uintptr_t)255;
+    if (workspace && aligned16(workspace) && img0 + idx_bytes + idw_bytes <= base + ws_bytes) {
+      uint8_t* cur = reinterpret_cast<uint8_t*>(img0);
+      carve_images(cur);
+    }
     TJ2_TRY(check_qtensor(&o->dYq, "ops.dYq", gfmt, M, N));
     TJ2_TRY(check_qtensor(&o->dYt, "ops.dYt", gfmt, N, M));
     TJ2_TRY(check_qtensor(&o->Wt, "ops.Wt", TJ2_NVFP4, K1, N));
@@ -593,22 +661,38 @@ tj2_status linear_bwd_impl(int gfmt, const void* dY, int64_t M, int64_t N, int64
   QuantParams cols[kColMultiMax];
   int nc = 0;
   const bool w_given = ops && ops->w_given;  // the re-grouped weights come from the master pass
+  // the images: output row i of Wt / Xt is column rest[i] of the products'
+  // outputs, row i of W8t / X8t column outliers[i]
+  const int32_t* rest_rows = plan ? plan->rest : nullptr;
+  const int32_t* outl_rows = plan ? plan->outliers : nullptr;
   if (plan) {
-    cols[nc++] = quant_params(nullptr, TJ2_FP8, X8, M, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 5, &o->X8t);
-    if (!w_given)
-      cols[nc++] = quant_params(nullptr, TJ2_FP8, W8, N, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 4, &o->W8t);
+    cols[nc] = quant_params(nullptr, TJ2_FP8, X8, M, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 5, &o->X8t);
+    if (img_dw.ptr) set_image(cols[nc], (uint8_t*)img_dw.ptr, K, M, outl_rows);
+    ++nc;
+    if (!w_given) {
+      cols[nc] = quant_params(nullptr, TJ2_FP8, W8, N, no, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 4, &o->W8t);
+      if (img_dx.ptr) set_image(cols[nc], (uint8_t*)img_dx.ptr, K, N, outl_rows);
+      ++nc;
+    }
   }
-  if (!w_given)
-    cols[nc++] = quant_params(nullptr, TJ2_NVFP4, Wq, N, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 1, &o->Wt);
-  cols[nc++] = quant_params(nullptr, TJ2_NVFP4, Xq, M, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 3, &o->Xt);
+  if (!w_given) {
+    cols[nc] = quant_params(nullptr, TJ2_NVFP4, Wq, N, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdx, seed, offset + 1, &o->Wt);
+    if (img_dx.ptr) set_image(cols[nc], (uint8_t*)img_dx.ptr, K, N, rest_rows);
+    ++nc;
+  } else {
+    img_dx.ready = 0;  // the re-grouped weights were given: the product decodes its image
+  }
+  cols[nc] = quant_params(nullptr, TJ2_NVFP4, Xq, M, K1, nullptr, 0, TJ2_GROUP_COL, TJ2_SR, r, mdw, seed, offset + 3, &o->Xt);
+  if (img_dw.ptr) set_image(cols[nc], (uint8_t*)img_dw.ptr, K, M, rest_rows);
+  ++nc;
   TJ2_TRY(hip_check(launch_quant_col_multi(cols, nc, s), "column quantize launch"));
   if (!plan) {
-    TJ2_TRY(run_gemm(&o->dYq, &o->Wt, nullptr, nullptr, dX, dx_dtype, K, nullptr, 0, gemm_ws, gws, s));
-    TJ2_TRY(run_gemm(&o->dYt, &o->Xt, nullptr, nullptr, dW, TJ2_F32, K, nullptr, 0, gemm_ws, gws, s));
+    TJ2_TRY(run_gemm(&o->dYq, &o->Wt, nullptr, nullptr, dX, dx_dtype, K, nullptr, 0, gemm_ws, gws, s, img_dx));
+    TJ2_TRY(run_gemm(&o->dYt, &o->Xt, nullptr, nullptr, dW, TJ2_F32, K, nullptr, 0, gemm_ws, gws, s, img_dw));
     return ok();
   }
-  TJ2_TRY(run_gemm_outl(&o->dYq, &o->Wt, &o->W8t, plan, dX, dx_dtype, K, 0, gemm_ws, gws, s));
-  TJ2_TRY(run_gemm_outl(&o->dYt, &o->Xt, &o->X8t, plan, dW, TJ2_F32, K, 0, gemm_ws, gws, s));
+  TJ2_TRY(run_gemm_outl(&o->dYq, &o->Wt, &o->W8t, plan, dX, dx_dtype, K, 0, gemm_ws, gws, s, img_dx));
+  TJ2_TRY(run_gemm_outl(&o->dYt, &o->Xt, &o->X8t, plan, dW, TJ2_F32, K, 0, gemm_ws, gws, s, img_dw));
   return ok();
 }
 

@@ -79,6 +79,12 @@ struct GemmKArgs {
   const int32_t* outl;
   const int32_t* rest;
   int n_outl;
+  // image products: B decoded once into f16 chunk images laid out as the LDS
+  // stage ([tiles_n][nchunks] images of kImgChunkBytes) and its outer scales
+  // S_B as [nchunks][bsc_ld] floats (bsc_ld = tiles_n * 128)
+  const uint8_t* bimg;
+  const float* bsc;
+  int64_t bsc_ld;
 };
 
 // Packed slice of one thread, in a layout shared by both formats:
@@ -98,6 +104,7 @@ struct Op;
 
 template <>
 struct Op<TJ2_NVFP4> {
+  static constexpr int kHalfLoads = 4;  // vector-memory instructions of load_half
   // rn = row * (outer blocks per row), below 2^32 for any operand that fits in memory (rows x
   // len / 128): codes at rn * 64 bytes (64-bit offsets: an operand's codes may exceed 4 GB),
   // inner scales at rn * 8, outer at rn
@@ -171,6 +178,7 @@ struct Op<TJ2_NVFP4> {
 
 template <>
 struct Op<TJ2_FP8> {
+  static constexpr int kHalfLoads = 5;
   // rn = row * (outer blocks per row): codes at rn * 128 bytes, outer scales at rn
   static __device__ __forceinline__ void load_half(const OperandK& o, uint32_t rn, int kc, int half, Slice& s) {
     const uint4* p = reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 128 + ((size_t)rn * 128 + half * 64));
@@ -225,6 +233,7 @@ struct Op<TJ2_FP8> {
 // E2M3 value (4 significant bits) times an E4M3 scale (4) is exact in f16.
 template <>
 struct Op<TJ2_NVFP6> {
+  static constexpr int kHalfLoads = 6;
   static __device__ __forceinline__ void load_half(const OperandK& o, uint32_t rn, int kc, int half, Slice& s) {
     const uint4* p = reinterpret_cast<const uint4*>(o.codes + (size_t)kc * 128 + ((size_t)rn * 128 + half * 64));
 #pragma unroll
@@ -526,6 +535,129 @@ __device__ __forceinline__ int lower_bound(const int32_t* a, int n, int v) {
   return lo;
 }
 
+// Output of one 256x128 tile from the accumulators (MIXB: the outlier-column
+// mapping of the staged rows: lo, c1, r0, ncols as set up by the kernel).
+template <bool MIXB>
+__device__ __forceinline__ void store_tile(const GemmKArgs& p, float (*out)[32][OUT_STRIDE], const Ctx& t, int64_t m0,
+                                           int64_t n0, uint32_t z, const float (&acc)[4][16], int lo, int c1, int r0,
+                                           int ncols) {
+  // Output: lane holds rows 8g + 4*(lane/32) + q (element 4g + q) of the wave's
+  // 32 rows, column tn*32 + (lane & 31) of block tn (staged LDS row; for
+  // outlier-column products mapped back to the original column).
+  const int lane = t.lane;
+  const int64_t rw = m0 + t.w * 32 + 4 * (lane >> 5);
+  const bool full_rows = m0 + BM <= p.I;
+  int64_t ocol[4];
+  bool ok[4];
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
+    const int rho = tn * 32 + (lane & 31);
+    if constexpr (MIXB) {
+      ok[tn] = rho < ncols;
+      ocol[tn] = !ok[tn] ? 0 : rho < c1 ? (int64_t)p.rest[r0 + rho] : (int64_t)p.outl[lo + rho - c1];
+    } else {
+      ocol[tn] = n0 + rho;
+      ok[tn] = ocol[tn] < p.J;
+    }
+  }
+  // Tiles whose 128 columns are contiguous and 16-byte aligned in the output go
+  // through LDS and leave as 16-byte row pieces (8 bf16 or 4 fp32 per store)
+  // instead of one 2- or 4-byte store per element.  An outlier-column tile's
+  // columns are the full range [n0, n0 + 128) in another order (its non-outlier
+  // columns and its outlier columns, both ascending), so its results are
+  // placed in output order on the way into LDS.
+  {
+    const bool to_partial = p.partial != nullptr;
+    const int64_t ld = to_partial ? p.J : p.ldc;
+    const bool bf = !to_partial && p.c_bf16;
+    const uintptr_t base_addr = to_partial ? (uintptr_t)p.partial : (uintptr_t)p.C;
+    if (n0 + BN <= p.J && (MIXB || to_partial || !p.col_map) && (ld & (bf ? 7 : 3)) == 0 &&
+        (base_addr & 15) == 0) {
+      barrier_lds();  // every wave is done with the last chunk's B stage
+      float(&st)[32][OUT_STRIDE] = out[t.w];
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) {
+        // output column within the tile (clamped: a plan that breaks its contract cannot
+        // move a write outside the wave's staging rows)
+        const int lc = MIXB ? min(max((int)(ocol[tn] - n0), 0), BN - 1) : tn * 32 + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st[8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][lc] = acc[tn][e];
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's writes are visible to its lanes
+      __builtin_amdgcn_wave_barrier();
+      const int64_t row0 = m0 + t.w * 32;
+      if (bf) {
+        // lane: 8 columns of one of four rows per pass
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int row = 4 * r + (lane >> 4), c0 = (lane & 15) * 8;
+          const float4 u = *reinterpret_cast<const float4*>(&st[row][c0]);
+          const float4 v = *reinterpret_cast<const float4*>(&st[row][c0 + 4]);
+          uint4 o;
+          o.x = f32_to_bf16(u.x) | (f32_to_bf16(u.y) << 16);
+          o.y = f32_to_bf16(u.z) | (f32_to_bf16(u.w) << 16);
+          o.z = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
+          o.w = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
+          if (row0 + row < p.I)
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + (row0 + row) * ld + n0 + c0) = o;
+        }
+      } else {
+        float* base = to_partial ? p.partial + (int64_t)z * p.I * p.J : reinterpret_cast<float*>(p.C);
+        const bool add = !to_partial && p.accumulate;
+        // lane: 4 columns of one of two rows per pass
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 2 * r + (lane >> 5), c0 = (lane & 31) * 4;
+          float4 v = *reinterpret_cast<const float4*>(&st[row][c0]);
+          if (row0 + row < p.I) {
+            float4* dst = reinterpret_cast<float4*>(base + (row0 + row) * ld + n0 + c0);
+            if (add) {
+              const float4 o = *dst;
+              v.x = o.x + v.x;
+              v.y = o.y + v.y;
+              v.z = o.z + v.z;
+              v.w = o.w + v.w;
+            }
+            *dst = v;
+          }
+        }
+      }
+      return;
+    }
+  }
+  if (p.partial) {
+    float* base = p.partial + (int64_t)z * p.I * p.J + rw * p.J;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      if (!ok[tn]) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int dr = 8 * (e >> 2) + (e & 3);
+        if (full_rows || rw + dr < p.I) base[dr * p.J + ocol[tn]] = acc[tn][e];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
+    if (!ok[tn]) continue;
+    const int64_t ccol = (!MIXB && p.col_map) ? (int64_t)p.col_map[ocol[tn]] : ocol[tn];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int dr = 8 * (e >> 2) + (e & 3);
+      if (!full_rows && rw + dr >= p.I) continue;
+      const int64_t off = (rw + dr) * p.ldc + ccol;
+      const float v = acc[tn][e];
+      if (p.c_bf16) {
+        reinterpret_cast<uint16_t*>(p.C)[off] = (uint16_t)f32_to_bf16(v);
+      } else {
+        float* cp = reinterpret_cast<float*>(p.C) + off;
+        *cp = p.accumulate ? *cp + v : v;
+      }
+    }
+  }
+}
+
 template <int FA0, int FB0, int FA1, int FB1, bool MIXB>
 __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
   __shared__ __attribute__((aligned(16))) SmemAll smem;
@@ -658,120 +790,343 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_kernel(GemmKArgs p) {
     for (int it = s1; it < n; ++it) tail_chunk<FA1, FB1>(p, sm, t, t.c_begin + it - t.n0c, acc);
   }
 
-  // Output: lane holds rows 8g + 4*(lane/32) + q (element 4g + q) of the wave's
-  // 32 rows, column tn*32 + (lane & 31) of block tn (staged LDS row; for
-  // outlier-column products mapped back to the original column).
-  const int lane = t.lane;
-  const int64_t rw = m0 + t.w * 32 + 4 * (lane >> 5);
-  const bool full_rows = m0 + BM <= p.I;
-  int64_t ocol[4];
-  bool ok[4];
-#pragma unroll
-  for (int tn = 0; tn < 4; ++tn) {
-    const int rho = tn * 32 + (lane & 31);
-    if constexpr (MIXB) {
-      ok[tn] = rho < ncols;
-      ocol[tn] = !ok[tn] ? 0 : rho < c1 ? (int64_t)p.rest[r0 + rho] : (int64_t)p.outl[lo + rho - c1];
-    } else {
-      ocol[tn] = n0 + rho;
-      ok[tn] = ocol[tn] < p.J;
+  store_tile<MIXB>(p, smem.out, t, m0, n0, z, acc, lo, c1, r0, ncols);
+}
+
+// ---------------------------------------------------------------------------
+// Image products: B decoded once per product.
+//
+// Every row tile of the output reads the whole B operand (a 16384-row forward
+// reads the weights 64 times), and the kernel above decodes B again in each of
+// them (decode, LDS writes and the packed B slices in registers: about a sixth
+// of its time).  Here bimage_kernel first decodes B once into f16 chunk images
+// laid out exactly as the kernel's LDS stage (128 rows of LDS_STRIDE halfs per
+// 128-K chunk and column tile, outlier-column products already in output-column
+// order), and gemm_img_kernel copies each image into LDS with
+// global_load_lds_dwordx4, which moves the bytes without registers or VALU.
+// The cost is one extra pass over B (0.56 B read and 2.1 B written per
+// element, small next to the product for weights) and 3.9 times the B bytes
+// per tile, served from L2.
+static_assert(kImgChunkBytes == BN * LDS_STRIDE * 2 && kImgRowBytes == LDS_STRIDE * 2, "image = LDS stage");
+// row tiles from which the image pays for its extra pass (each row tile would
+// otherwise decode B again)
+constexpr int kImgMinRowTiles = 8;
+static_assert(kImgChunkBytes % 1024 == 0 && kImgChunkBytes / 1024 == 34, "image chunk of 34 1 KB blocks");
+
+struct SmemImg {
+  _Float16 b[2][BN * LDS_STRIDE];
+};
+union SmemImgAll {
+  SmemImg loop;
+  float out[BM / 32][32][OUT_STRIDE];
+};
+
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Copy one chunk image (kImgChunkBytes at src, 16-byte aligned) into the LDS
+// stage whose block `w` starts at lds_w, if `on` (wave-uniform): wave w moves
+// the 1 KB blocks w, w + 8, w + 16, w + 24 (waves 0 and 1 also w + 32), 16
+// bytes per lane (voff = 16 * lane + 1024 * w).  The copy is asynchronous: it
+// has landed once this wave's vector-memory counter is zero, and the other
+// waves may read it after a barrier that follows that wait.  Written in
+// assembly because the compiler's own form makes the next LDS read of any
+// stage wait for every outstanding copy (here the chunk's barrier carries the
+// wait), and with its two conditions inside the block: a branch around it
+// splits the chunk's straight-line code, and the register allocation of the
+// chunk then spills.  m0 (the LDS destination) is restored afterwards; the
+// first s_nop covers an SGPR operand written by a vector instruction just
+// before, the others the m0 write before each copy.
+__device__ __forceinline__ void dma_chunk(const uint8_t* src, uint32_t lds_w, uint32_t voff, int w, int on) {
+  uint32_t save;
+  asm volatile(
+      "s_cmp_eq_u32 %[on], 0\n\t"
+      "s_cbranch_scc1 2f\n\t"
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[v], %[b0]\n\t"
+      "s_mov_b32 m0, %[m1]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[v], %[b1]\n\t"
+      "s_mov_b32 m0, %[m2]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[v], %[b2]\n\t"
+      "s_mov_b32 m0, %[m3]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[v], %[b3]\n\t"
+      "s_cmp_lt_u32 %[w], 2\n\t"
+      "s_cbranch_scc0 1f\n\t"
+      "s_mov_b32 m0, %[m4]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[v], %[b4]\n"
+      "1:\n\t"
+      "s_mov_b32 m0, %[sv]\n"
+      "2:\n"
+      : [sv] "=&s"(save)
+      : [on] "s"(__builtin_amdgcn_readfirstlane(on)), [w] "s"(__builtin_amdgcn_readfirstlane(w)), [m0] "s"(lds_w), [m1] "s"(lds_w + 8192u), [m2] "s"(lds_w + 16384u),
+        [m3] "s"(lds_w + 24576u), [m4] "s"(lds_w + 32768u), [v] "v"(voff), [b0] "s"(src), [b1] "s"(src + 8192),
+        [b2] "s"(src + 16384), [b3] "s"(src + 24576), [b4] "s"(src + 32768)
+      : "memory", "scc");
+}
+
+// Every outstanding load and LDS access of this wave has completed (the
+// stage copies included), then the workgroup barrier.
+__device__ __forceinline__ void barrier_all() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int F>
+struct FmtTag {
+  static constexpr int value = F;
+};
+
+// One chunk of an image product: the slots of chunk() above without the B
+// staging.  The A fragments come from this chunk's slice `a` (format FA); at
+// slot 7 the next chunk's S_B is requested (fetch_sb) and at slot 8 the slice
+// of the chunk after next (fetch_a, into `a`, whose fragments are decoded by
+// then); the next chunk's slice `an`, requested one chunk earlier, is prepared
+// at slot 30 and its fragment 0 decoded at slot 31.  sync (slot
+// 32 - kFragAhead) waits for every load and copy except the slice just
+// requested, crosses the barrier (the next stage has landed for all waves,
+// this stage is no longer read) and starts the copy of the chunk after next
+// into this stage.  sbc holds S_B of this chunk's column pairs (lanes 0-31
+// columns of block 2p, lanes 32-63 of block 2p + 1).
+template <int FA, int kFragAhead, class FETCH_SB, class FETCH_A, class SYNC>
+__device__ __forceinline__ void chunk_img(const _Float16* bb, const _Float16* bn, half8_t (&af)[8],
+                                          half2_t (&sga)[4], half8_t (&bf)[frag_ring(kFragAhead)],
+                                          float (&acc)[4][16], float16v_t (&part)[2], float32v_t& smat, Slice& a,
+                                          const Slice& an, const float2& sbc, FETCH_SB&& fetch_sb, FETCH_A&& fetch_a,
+                                          SYNC&& sync) {
+  constexpr int kFragRing = frag_ring(kFragAhead);
+  // S_A of this chunk in a register of its own (an opaque copy): the slice's
+  // register is refilled at slot 8 while S_A is still needed at slot 24, and
+  // without the copy the compiler carries the refilled value into the loop's
+  // register with a move at the back edge, which waits for every load in
+  // flight (the stage copy included)
+  float sa;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(sa) : "v"(a.S));
+  static_for<32>([&](auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    constexpr int tn = q / 8, ks = q % 8;
+    if constexpr (q < 7) af[q + 1] = Op<FA>::template frag_a<q + 1>(a, sga);
+    if constexpr (q == 7) fetch_sb();
+    if constexpr (q == 8) {
+      // the scale products of blocks 0-1 before the slice (and S_A) is refilled
+      smat = __builtin_amdgcn_mfma_f32_32x32x1f32(sa, sbc.x, float32v_t{}, 0, 0, 0);
+      fetch_a(a);
     }
-  }
-  // Tiles whose 128 columns are contiguous and 16-byte aligned in the output go
-  // through LDS and leave as 16-byte row pieces (8 bf16 or 4 fp32 per store)
-  // instead of one 2- or 4-byte store per element.  An outlier-column tile's
-  // columns are the full range [n0, n0 + 128) in another order (its non-outlier
-  // columns and its outlier columns, both ascending), so its results are
-  // placed in output order on the way into LDS.
+    if constexpr (q == 30) Op<FA>::prep_a(an, sga);
+    if constexpr (q == 31) af[0] = Op<FA>::template frag_a<0>(an, sga);
+    if constexpr (q == 32 - kFragAhead) sync();
+    constexpr int qf = q + kFragAhead;
+    if constexpr (qf < 32) bf[qf % kFragRing] = ld8(bb + (qf / 8) * 32 * LDS_STRIDE + (qf % 8) * 8);
+    else bf[qf % kFragRing] = ld8(bn + (qf - 32) * 8);
+    if constexpr (q == 24) smat = __builtin_amdgcn_mfma_f32_32x32x1f32(sa, sbc.y, float32v_t{}, 0, 0, 0);
+    part[tn & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks], bf[q % kFragRing], ks == 0 ? float16v_t{} : part[tn & 1],
+                                                          0, 0, 0);
+    if constexpr (ks >= 2) {
+      constexpr int pb = tn > 0 ? tn - 1 : 3;
+      constexpr int lo = ks <= 6 ? 3 * (ks - 2) : 14, hi = ks < 6 ? lo + 3 : lo + 2;
+      static_for<hi - lo>([&](auto i) __attribute__((always_inline)) {
+        constexpr int e = lo + decltype(i)::value;
+        acc[pb][e] = fmaf(part[pb & 1][e], smat[16 * (pb & 1) + e], acc[pb][e]);
+      });
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// Workgroup: 512 threads (8 waves), one 256x128 output tile, the chunk range of
+// split z; A in format FA (one K segment); B from the chunk images.  Chunk it
+// reads stage it & 1; the copy of chunk it + 2 into the same stage starts once
+// every wave is past the chunk's barrier.
+template <int FA>
+__global__ __launch_bounds__(512, 1) void gemm_img_kernel(GemmKArgs p) {
+  __shared__ __attribute__((aligned(16))) SmemImgAll smem;
+  SmemImg& sm = smem.loop;
+
+  const uint32_t nwg = gridDim.x;
+  uint32_t id = blockIdx.x;
+  const uint32_t per_xcd = nwg / 8;
+  if (id < per_xcd * 8) id = (id % 8) * per_xcd + id / 8;
+  const uint32_t tiles = (uint32_t)(p.tiles_m * p.tiles_n);
+  const uint32_t tile = id % tiles, z = id / tiles;
+  const uint32_t tj = tile % (uint32_t)p.tiles_n;
+  const int64_t m0 = (int64_t)(tile / p.tiles_n) * BM, n0 = (int64_t)tj * BN;
+
+  Ctx t;
+  t.lane = threadIdx.x & 63;
+  t.w = threadIdx.x >> 6;
+  t.ah = t.lane >> 5;
+  t.bq = 0;
+  t.b8 = false;
+  const uint32_t arow = (uint32_t)min(m0 + t.w * 32 + (t.lane & 31), p.I - 1);
+  t.arn[0] = t.arn[1] = arow * (uint32_t)p.seg[0].a.ld_s128;
+  t.brn[0] = t.brn[1] = 0;
+  t.n0c = p.seg[0].nchunks;
+  t.c_begin = (int)z * p.chunks_per_split;
+  const int n = min(t.c_begin + p.chunks_per_split, p.nchunks) - t.c_begin;
+
+  const uint8_t* img = p.bimg + ((size_t)tj * (size_t)p.nchunks + (size_t)t.c_begin) * kImgChunkBytes;
+  const float* sbl = p.bsc + (size_t)t.c_begin * (size_t)p.bsc_ld + n0 + t.lane;
+  const uint32_t lds_w = __builtin_amdgcn_readfirstlane(lds_addr(sm.b[0]) + (uint32_t)t.w * 1024u);
+  const uint32_t voff = (uint32_t)t.lane * 16u + (uint32_t)t.w * 1024u;
+  // copy the image of chunk c into stage st if c < n
+  auto dma = [&](int c, int st) __attribute__((always_inline)) {
+    dma_chunk(img + (size_t)min(c, n - 1) * kImgChunkBytes, lds_w + (uint32_t)st * (uint32_t)kImgChunkBytes, voff,
+              t.w, c < n ? 1 : 0);
+  };
+  auto load_sb = [&](int it, float2& sb) __attribute__((always_inline)) {
+    const float* q = sbl + (size_t)min(it, n - 1) * (size_t)p.bsc_ld;
+    sb.x = q[0];
+    sb.y = q[64];
+  };
+
+  float acc[4][16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+
+  Slice as[2];
+  float2 sbc, sbn;
+  // Prologue: chunk 0's A slice, S_B and image; once they have landed, the copy
+  // of chunk 1 and the slice of chunk 1 are requested.
+  Op<FA>::load_half(p.seg[0].a, t.arn[0], t.c_begin, t.ah, as[0]);
+  load_sb(0, sbc);
+  dma(0, 0);
+  barrier_all();
+  dma(1, 1);
+
   {
-    const bool to_partial = p.partial != nullptr;
-    const int64_t ld = to_partial ? p.J : p.ldc;
-    const bool bf = !to_partial && p.c_bf16;
-    const uintptr_t base_addr = to_partial ? (uintptr_t)p.partial : (uintptr_t)p.C;
-    if (n0 + BN <= p.J && (MIXB || to_partial || !p.col_map) && (ld & (bf ? 7 : 3)) == 0 &&
-        (base_addr & 15) == 0) {
-      barrier_lds();  // every wave is done with the last chunk's B stage
-      float(&st)[32][OUT_STRIDE] = smem.out[t.w];
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-        // output column within the tile (clamped: a plan that breaks its contract cannot
-        // move a write outside the wave's staging rows)
-        const int lc = MIXB ? min(max((int)(ocol[tn] - n0), 0), BN - 1) : tn * 32 + (lane & 31);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st[8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][lc] = acc[tn][e];
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's writes are visible to its lanes
-      __builtin_amdgcn_wave_barrier();
-      const int64_t row0 = m0 + t.w * 32;
-      if (bf) {
-        // lane: 8 columns of one of four rows per pass
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int row = 4 * r + (lane >> 4), c0 = (lane & 15) * 8;
-          const float4 u = *reinterpret_cast<const float4*>(&st[row][c0]);
-          const float4 v = *reinterpret_cast<const float4*>(&st[row][c0 + 4]);
-          uint4 o;
-          o.x = f32_to_bf16(u.x) | (f32_to_bf16(u.y) << 16);
-          o.y = f32_to_bf16(u.z) | (f32_to_bf16(u.w) << 16);
-          o.z = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
-          o.w = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
-          if (row0 + row < p.I)
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + (row0 + row) * ld + n0 + c0) = o;
-        }
-      } else {
-        float* base = to_partial ? p.partial + (int64_t)z * p.I * p.J : reinterpret_cast<float*>(p.C);
-        const bool add = !to_partial && p.accumulate;
-        // lane: 4 columns of one of two rows per pass
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 2 * r + (lane >> 5), c0 = (lane & 31) * 4;
-          float4 v = *reinterpret_cast<const float4*>(&st[row][c0]);
-          if (row0 + row < p.I) {
-            float4* dst = reinterpret_cast<float4*>(base + (row0 + row) * ld + n0 + c0);
-            if (add) {
-              const float4 o = *dst;
-              v.x = o.x + v.x;
-              v.y = o.y + v.y;
-              v.z = o.z + v.z;
-              v.w = o.w + v.w;
-            }
-            *dst = v;
-          }
-        }
-      }
-      return;
+    Op<FA>::load_half(p.seg[0].a, t.arn[0], t.c_begin + min(1, n - 1), t.ah, as[1]);
+    half8_t af[8];
+    half2_t sga[4];
+    float16v_t part[2];
+    part[1] = float16v_t{};
+    float32v_t smat = float32v_t{};  // "chunk -1": the first chunk's promotion of part[1] adds 0 * 0
+    constexpr int kFragAhead = kFragAheadSlots;
+    half8_t bf[frag_ring(kFragAhead)];
+    const int lane_off = (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
+    Op<FA>::prep_a(as[0], sga);
+    af[0] = Op<FA>::template frag_a<0>(as[0], sga);
+    {
+      const _Float16* bb = sm.b[0] + lane_off;
+      static_for<kFragAhead>([&](auto f) __attribute__((always_inline)) {
+        bf[decltype(f)::value] = ld8(bb + decltype(f)::value * 8);
+      });
     }
+    // chunk it in stage ST with slice as[ST] (requests past the range reload
+    // the last chunk); S_B alternates between two register pairs.  The barrier's
+    // wait leaves only the slice requested at slot 8 in flight (it was issued
+    // after the S_B request of slot 7 and after the copy it waits for).
+    auto run = [&](auto st, int it) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st)::value;
+      float2& cur = ST ? sbn : sbc;
+      float2& nxt = ST ? sbc : sbn;
+      auto fetch_sb = [&]() __attribute__((always_inline)) { load_sb(it + 1, nxt); };
+      auto fetch_a = [&](Slice& sl) __attribute__((always_inline)) {
+        Op<FA>::load_half(p.seg[0].a, t.arn[0], t.c_begin + min(it + 2, n - 1), t.ah, sl);
+      };
+      auto sync = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0070 | Op<FA>::kHalfLoads);  // vmcnt(slice loads) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        dma(it + 2, ST);
+      };
+      chunk_img<FA, kFragAhead>(sm.b[ST] + lane_off, sm.b[ST ^ 1] + lane_off, af, sga, bf, acc, part, smat, as[ST],
+                                 as[ST ^ 1], cur, fetch_sb, fetch_a, sync);
+    };
+    int it = 0;
+    for (; it + 1 < n; it += 2) {
+      run(FmtTag<0>{}, it);
+      run(FmtTag<1>{}, it + 1);
+    }
+    if (it < n) run(FmtTag<0>{}, it);
+    static_for<16>([&](auto e) __attribute__((always_inline)) {
+      constexpr int i = decltype(e)::value;
+      acc[3][i] = fmaf(part[1][i], smat[16 + i], acc[3][i]);
+    });
   }
-  if (p.partial) {
-    float* base = p.partial + (int64_t)z * p.I * p.J + rw * p.J;
+
+  store_tile<false>(p, smem.out, t, m0, n0, z, acc, 0, BN, 0, BN);
+}
+
+// B decode into chunk images: a workgroup of 256 threads per (chunk g, 64
+// source rows); thread (unit u = t % 16, rows v = 64 * slab + 16k + t / 16,
+// k = 0..3) decodes K elements 8u..8u+7 of the chunk in four rows into 16-byte
+// pieces of the image (the 16 threads of a row write its 256 bytes; u = 15
+// also writes the row's pad, u = 0 its S_B).  Source rows are B's rows in
+// order; for outlier-column products rows [0, J - n_outl) are B's NVFP4 rows,
+// placed at image row (output column) rest[v], and rows [J - n_outl, J) are
+// b8's FP8 rows, placed at outl[v - (J - n_outl)], so every destination is
+// known from one load.  Rows J and above of the last column tile are zero.
+struct ImgArgs {
+  OperandK b;
+  int fmt;
+  int nchunks;
+  OperandK b8;
+  const int32_t* outl;
+  const int32_t* rest;
+  int n_outl;
+  int64_t J, Jpad;
+  uint8_t* img;
+  float* bsc;
+  int64_t bsc_ld;
+};
+
+__global__ __launch_bounds__(256) void bimage_kernel(ImgArgs p) {
+  const int g = blockIdx.x;
+  const int u = threadIdx.x & 15;
+  const bool plan = p.outl != nullptr;
+  const int64_t nrest = plan ? p.J - p.n_outl : p.J;
+  const bool b_fp8 = p.fmt == TJ2_FP8;
+  half8_t f[4];
+  float S[4];
+  int64_t dest[4];
+  // Branch-free: every load is issued for all four rows from addresses chosen
+  // per row (a divergent branch would make the compiler wait for each load at
+  // its join), then the stores.
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-      if (!ok[tn]) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int dr = 8 * (e >> 2) + (e & 3);
-        if (full_rows || rw + dr < p.I) base[dr * p.J + ocol[tn]] = acc[tn][e];
-      }
-    }
-    return;
+  for (int k = 0; k < 4; ++k) {
+    const int64_t v = (int64_t)blockIdx.y * 64 + k * 16 + (threadIdx.x >> 4);
+    const bool real = v < p.J;
+    const bool is8 = plan && real && v >= nrest;                // an FP8 row of b8
+    const int64_t r8 = is8 ? v - nrest : 0;
+    const int64_t r4 = real && !is8 ? v : 0;
+    // the row's destination: loaded for every row from a valid address (without
+    // a plan, the first word of B's codes, unused)
+    const int32_t* ip = !plan ? reinterpret_cast<const int32_t*>(p.b.codes)
+                        : is8 ? p.outl + r8 : nrest > 0 ? p.rest + min(v, nrest - 1) : p.outl;
+    const int32_t at = *ip;
+    dest[k] = plan && real ? (int64_t)at : v;
+    const bool fp8 = is8 || b_fp8;
+    const size_t rn = (size_t)(is8 ? r8 * p.b8.ld_s128 : r4 * p.b.ld_s128);
+    const uint8_t* c4 = p.b.codes + (size_t)g * 64 + rn * 64 + u * 4;    // NVFP4 codes
+    const uint8_t* c8 = (is8 ? p.b8.codes : p.b.codes) + (size_t)g * 128 + rn * 128 + u * 8;  // FP8 codes
+    const uint8_t* cw = fp8 ? c8 : c4;
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(cw);
+    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(fp8 ? cw + 4 : cw);
+    const uint32_t sb = *(fp8 ? cw : p.b.s16 + (size_t)g * 8 + rn * 8 + (u >> 1));
+    const float s128 = ((is8 ? p.b8.s128 : p.b.s128) + g)[rn];
+    const half2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+    const half8_t v8 = Op<TJ2_FP8>::dec8(w0, w1);
+    const half8_t v4 = Op<TJ2_NVFP4>::dec8(w0, half2_t{s2[0], s2[0]});
+    f[k] = !real ? half8_t{} : fp8 ? v8 : v4;
+    S[k] = real ? s128 : 0.0f;
   }
 #pragma unroll
-  for (int tn = 0; tn < 4; ++tn) {
-    if (!ok[tn]) continue;
-    const int64_t ccol = (!MIXB && p.col_map) ? (int64_t)p.col_map[ocol[tn]] : ocol[tn];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int dr = 8 * (e >> 2) + (e & 3);
-      if (!full_rows && rw + dr >= p.I) continue;
-      const int64_t off = (rw + dr) * p.ldc + ccol;
-      const float v = acc[tn][e];
-      if (p.c_bf16) {
-        reinterpret_cast<uint16_t*>(p.C)[off] = (uint16_t)f32_to_bf16(v);
-      } else {
-        float* cp = reinterpret_cast<float*>(p.C) + off;
-        *cp = p.accumulate ? *cp + v : v;
-      }
-    }
+  for (int k = 0; k < 4; ++k) {
+    const int64_t d = dest[k];
+    if (d < 0 || d >= p.Jpad) continue;  // past the padded rows (or a plan entry out of range)
+    uint8_t* dst = p.img + ((size_t)(d / BN) * (size_t)p.nchunks + (size_t)g) * kImgChunkBytes +
+                   (size_t)(d % BN) * (LDS_STRIDE * 2);
+    *reinterpret_cast<half8_t*>(dst + u * 16) = f[k];
+    if (u == 0) p.bsc[(size_t)g * (size_t)p.bsc_ld + (size_t)d] = S[k];
   }
 }
 
@@ -849,7 +1204,29 @@ GemmKernel pick_kernel(const GemmParams& p) {
   return nullptr;
 }
 
+typedef void (*ImgKernel)(GemmKArgs);
+
+ImgKernel pick_img_kernel(const GemmParams& p) {
+  if (p.nseg != 1) return nullptr;
+  const int fa = p.seg[0].a.fmt, fb = p.seg[0].b.fmt;
+  if (fb != TJ2_NVFP4 && fb != TJ2_FP8) return nullptr;
+  if (p.outl && (fb != TJ2_NVFP4 || p.b8.fmt != TJ2_FP8)) return nullptr;
+  if (fa == TJ2_NVFP4) return gemm_img_kernel<TJ2_NVFP4>;
+  if (fa == TJ2_NVFP6) return gemm_img_kernel<TJ2_NVFP6>;
+  if (fa == TJ2_FP8) return gemm_img_kernel<TJ2_FP8>;
+  return nullptr;
+}
+
 }  // namespace
+
+bool gemm_image_pays(int64_t I) { return (I + BM - 1) / BM >= kImgMinRowTiles; }
+
+size_t gemm_image_bytes(int64_t J, int64_t nchunks) {
+  const int64_t tn = (J + BN - 1) / BN;
+  const size_t img = (size_t)tn * (size_t)nchunks * (size_t)kImgChunkBytes;
+  const size_t sc = (size_t)nchunks * (size_t)tn * BN * sizeof(float);
+  return img + ((sc + 255) & ~(size_t)255);
+}
 
 // K splits of a product: one workgroup per CU at a time (256 CUs).  Estimated
 // time in units of one chunk's main loop: rounds of workgroups x (chunks per
@@ -890,6 +1267,9 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   GemmKernel kern = pick_kernel(p);
   if (!kern) return hipErrorInvalidValue;
   GemmKArgs k;
+  k.bimg = nullptr;
+  k.bsc = nullptr;
+  k.bsc_ld = 0;
   k.nchunks = 0;
   for (int i = 0; i < 2; ++i) {
     if (i < p.nseg) {
@@ -923,6 +1303,36 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   k.tiles_n = (int)((p.J + BN - 1) / BN);
   k.split = split;
   const uint32_t nwg = (uint32_t)k.tiles_m * (uint32_t)k.tiles_n * (uint32_t)split;
+  // B is decoded once into chunk images when it is read by many row tiles and
+  // the caller gave room for them
+  ImgKernel ikern = p.bimg && gemm_image_pays(p.I) ? pick_img_kernel(p) : nullptr;
+  if (ikern && p.bimg_bytes >= gemm_image_bytes(p.J, k.nchunks) && (reinterpret_cast<uintptr_t>(p.bimg) & 255) == 0) {
+    ImgArgs ia;
+    ia.b = k.seg[0].b;
+    ia.fmt = p.seg[0].b.fmt;
+    ia.nchunks = k.nchunks;
+    ia.b8 = k.b8;
+    ia.outl = p.outl;
+    ia.rest = p.rest;
+    ia.n_outl = p.n_outl;
+    ia.J = p.J;
+    ia.Jpad = (int64_t)k.tiles_n * BN;
+    ia.img = reinterpret_cast<uint8_t*>(p.bimg);
+    ia.bsc_ld = ia.Jpad;
+    ia.bsc = reinterpret_cast<float*>(ia.img + (size_t)k.tiles_n * (size_t)k.nchunks * kImgChunkBytes);
+    if (!p.bimg_ready) {
+      hipLaunchKernelGGL(bimage_kernel, dim3((uint32_t)k.nchunks, (uint32_t)(ia.Jpad / 64)), dim3(256), 0, s, ia);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    k.bimg = ia.img;
+    k.bsc = ia.bsc;
+    k.bsc_ld = ia.bsc_ld;
+    k.outl = nullptr;
+    k.rest = nullptr;
+    k.n_outl = 0;
+    kern = ikern;
+  }
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(512), 0, s, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split == 1) return e;

@@ -312,6 +312,37 @@ struct ColTile<TJ2_FP8> {
   }
 };
 
+// The image of a product's B operand (its f16 decode, laid out as the
+// product's LDS stage; see kImgRowBytes): this group's 16 values, decoded
+// exactly as the product would (E2M1 times its E4M3 scale, or the E4M3 value;
+// the outer scale S stays a separate float), go to image row img_rows[orow]
+// (or orow), chunk g, elements 16 rs .. 16 rs + 15; lane rs = 0 writes S.
+template <int OF>
+__device__ __forceinline__ void store_image_group(const QuantParams& p, int64_t orow, uint32_t g, int rs,
+                                                  const uint32_t codes[4], uint32_t s_code, float S) {
+  const int64_t d = p.img_rows ? (int64_t)p.img_rows[orow] : orow;
+  uint8_t* dst = p.img + ((size_t)(d >> 7) * (size_t)p.img_nch + g) * kImgChunkBytes + (size_t)(d & 127) * kImgRowBytes +
+                 rs * 32;
+  uint32_t h[8];
+  if constexpr (OF == TJ2_NVFP4) {
+    const half2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s_code, 1.0f, false);
+    const half2_t sc = half2_t{s2[0], s2[0]};
+    static_for<8>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      const half2_t q = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[i >> 2], 1.0f, i & 3) * sc;
+      h[i] = __builtin_bit_cast(uint32_t, q);
+    });
+  } else {
+    static_for<8>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      h[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[i >> 1], 1.0f, (i & 1) != 0));
+    });
+  }
+  *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<uint4*>(dst + 16) = make_uint4(h[4], h[5], h[6], h[7]);
+  if (rs == 0) p.img_sc[(size_t)g * (size_t)p.img_ld + (size_t)d] = S;
+}
+
 // One 128-row x 64-column tile (number `bid` of the problem's tiles).
 template <int IN, int OF, bool SR, bool RHT>
 __device__ __forceinline__ void col_tile(const QuantParams& p, uint32_t bid, ColTile<IN>& tile) {
@@ -362,6 +393,9 @@ __device__ __forceinline__ void col_tile(const QuantParams& p, uint32_t bid, Col
     // groups past the last row are the zero padding of the output's last block
     store_group<OF>(o, orow, r0 >> 4, codes, s_code);
     if (rs == 0) o.s128[orow * o.ld_s128 + rbi] = S;
+    if constexpr (OF == TJ2_NVFP4 || OF == TJ2_FP8) {
+      if (p.img) store_image_group<OF>(p, orow, rbi, rs, codes, s_code, S);
+    }
   });
 }
 

@@ -33,6 +33,16 @@ inline QView make_view(const tj2_qtensor& q) {
   return v;
 }
 
+// B operand image of a product (the f16 decode of a packed B, laid out as the
+// product kernel's LDS stage): for column tile t (128 output columns) and K
+// chunk g (128 elements), a block of kImgChunkBytes at (t * nchunks + g) *
+// kImgChunkBytes holds row r (output column 128t + r) at r * kImgRowBytes:
+// its 128 values as f16 (element k at 2k bytes), then 16 unused bytes (the
+// row pitch keeps the product's fragment reads free of bank conflicts).  The
+// outer scales follow the images: float S_B[g][Jpad], Jpad = 128 * tiles.
+constexpr int kImgRowBytes = 272;
+constexpr int kImgChunkBytes = 128 * kImgRowBytes;
+
 struct QuantParams {
   int in_dtype;          // TJ2_BF16, TJ2_F32, TJ2_NVFP4, TJ2_FP8
   const void* x;         // dense input (BF16/F32), row-major [rows, ld_x]
@@ -45,6 +55,13 @@ struct QuantParams {
   uint32_t rht_mask;
   uint64_t seed, offset;
   QView out;
+  // column grouping only, NVFP4 or FP8 output: also write the output's B image
+  // (img != NULL): output row i is image row img_rows[i] (NULL: i), chunks of
+  // img_nch, outer scales at img_sc[g * img_ld + image row]
+  uint8_t* img;
+  float* img_sc;
+  const int32_t* img_rows;
+  int64_t img_ld, img_nch;
 };
 
 hipError_t launch_quant(const QuantParams& p, hipStream_t s);
@@ -107,12 +124,25 @@ struct GemmParams {
   const int32_t* outl;
   const int32_t* rest;
   int n_outl;
+  // image products: scratch for B decoded once into f16 chunk images
+  // (gemm_image_bytes); NULL -> B is decoded inside the product kernel.
+  // bimg_ready: the image was written by B's producer (no decode pass)
+  void* bimg;
+  size_t bimg_bytes;
+  int bimg_ready;
 };
 
 // Number of K splits used for a product of I x J outputs over nchunks 128-element
 // chunks, and the workspace it needs (0 when no split).
 int gemm_split(int64_t I, int64_t J, int64_t nchunks);
 size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t nchunks);
+
+// Scratch of an image product: the f16 chunk images of a J-row B operand over
+// nchunks 128-element chunks, and their outer scales.
+size_t gemm_image_bytes(int64_t J, int64_t nchunks);
+// Whether a product of I rows decodes its B into an image (given the room):
+// only when enough row tiles would otherwise decode B again.
+bool gemm_image_pays(int64_t I);
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 

@@ -290,6 +290,21 @@ def test_gemm_workspace_counts_both_segments(L):
     assert two >= one > 0
 
 
+def test_gemm_workspace_holds_the_b_image(L):
+    # one-segment products of at least 8 row tiles (2048 rows) also take room for B decoded once:
+    # per 128-column tile and 128-element chunk, 128 rows of 272 bytes, then the fp32 outer scales
+    # [chunks][columns padded to 128]; the split-K partials come first (256-byte aligned)
+    I, J, K = 2048, 3072, 16384
+    part = 4 * I * J * 4  # four K splits of fp32 partial sums
+    img = (J // 128) * (K // 128) * 128 * 272 + (K // 128) * J * 4
+    assert L.nvfp4_gemm_workspace_size(I, J, K, 0) == part + img
+    # 300 columns: 3 column tiles, scales padded to 384 columns
+    assert L.nvfp4_gemm_workspace_size(16384, 300, 1024, 0) == 3 * 8 * 128 * 272 + 8 * 384 * 4
+    # fewer row tiles (7), or a second K segment: no image (7 chunks: no split either)
+    assert L.nvfp4_gemm_workspace_size(1792, 300, 896, 0) == 0
+    assert L.nvfp4_gemm_workspace_size(16384, 300, 768, 128) == 0
+
+
 def test_qtensor_block_count_limit(L):
     # operands are indexed by 128-element block in 32 bits; larger ones are rejected on the host
     from bit_fully_quantized_amd import _lib
@@ -305,7 +320,7 @@ def test_noalloc_refuses_products_beyond_its_scratch(L):
     from bit_fully_quantized_amd import _lib
     A = fake_q(_lib.NVFP4, 2048, 16384)
     B = fake_q(_lib.NVFP4, 3072, 16384)
-    assert L.nvfp4_gemm_workspace_size(2048, 3072, 16384, 0) == 4 * 2048 * 3072 * 4
+    assert L.nvfp4_gemm_workspace_size(2048, 3072, 16384, 0) >= 4 * 2048 * 3072 * 4
     assert L.nvfp4_gemm_noalloc(ctypes.byref(A), ctypes.byref(B), None, None, 0x9000, _lib.F32, 3072, None, 0,
                                 None) == _lib.TJ2_ERR_SHAPE
     assert b"scratch" in L.tj2_last_error()

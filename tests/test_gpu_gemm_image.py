@@ -1,0 +1,168 @@
+"""GPU parity of the image products: B decoded once into f16 chunk images (by a
+decode pass, or written by the column quantization that produces B) and copied
+into the product's LDS stages, used for one-segment products of at least 8 row
+tiles (2048 rows) when the workspace holds the image.
+
+Each case checks the product against the oracle's fp64 product of the same
+dequantized operands (relative Frobenius < 1e-5: fp32 accumulation of exact
+f16 products), and, where the reduction is not split, bit for bit against the
+product kernel that decodes B itself (same K order, same promotions)."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import gemm as ogemm, quant
+
+import _helpers as H
+from _linear_check import check_linear_sampled
+
+pytestmark = pytest.mark.gpu
+
+tj2 = pytest.importorskip("bit_fully_quantized_amd")
+
+
+def _ops(I, J, K, seed, fmt_a="nvfp4", fmt_b="nvfp4"):
+    a_bits = synthetic.normal_bf16((I, K), 1.0, seed)
+    b = synthetic.normal_f32((J, K), 0.02, seed + 1)
+    code = {"nvfp4": tj2.NVFP4, "fp8": tj2.FP8, "nvfp6": tj2.NVFP6}
+    ga = tj2.quantize(H.bf16_to_device(a_bits), out_fmt=code[fmt_a])
+    gb = tj2.quantize(H.f32_to_device(b), out_fmt=code[fmt_b])
+    ra = quant.quantize(H.bf16_values(a_bits), fmt=fmt_a)
+    rb = quant.quantize(b, fmt=fmt_b)
+    H.assert_q_equal(ga, ra, what="A")
+    H.assert_q_equal(gb, rb, what="B")
+    return ga, gb, ra, rb
+
+
+def _image_workspace(I, J, K):
+    n = int(tj2.lib().nvfp4_gemm_workspace_size(I, J, K, 0))
+    assert n > 0, "the image path applies to this shape"
+    return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("I,J,K", [(2100, 300, 880), (2048, 128, 128), (4096, 1040, 384), (2304, 16, 400)])
+def test_image_product_bit_identical(I, J, K):
+    """Ragged row, column and chunk tiles, one to seven chunks (no K split): the image product
+    equals the direct product bit for bit, fp32 and bf16 outputs."""
+    print(f"[image] plain {I}x{J}x{K}", flush=True)
+    ga, gb, ra, rb = _ops(I, J, K, seed=I + J + K)
+    ws = _image_workspace(I, J, K)
+    for dtype in (torch.float32, torch.bfloat16):
+        img = tj2.gemm(ga, gb, out_dtype=dtype, workspace=ws)
+        direct = tj2.gemm(ga, gb, out_dtype=dtype, split_k=False)
+        torch.cuda.synchronize()
+        assert torch.equal(img, direct), dtype
+    c = tj2.gemm(ga, gb, workspace=ws).cpu().numpy()
+    assert H.rel_fro(c, ogemm.gemm_nt_f64(ra, rb)) < 1e-5
+
+
+@pytest.mark.parametrize("I,J,K", [(2048, 200, 4096), (2304, 136, 8192)])
+def test_image_product_split_k(I, J, K):
+    """Few output tiles over a long reduction: the chunk ranges of the K splits read their
+    images from the middle of the chunk sequence."""
+    print(f"[image] split-K {I}x{J}x{K}", flush=True)
+    ga, gb, ra, rb = _ops(I, J, K, seed=7 + K)
+    c = tj2.gemm(ga, gb, workspace=_image_workspace(I, J, K)).cpu().numpy()
+    assert H.rel_fro(c, ogemm.gemm_nt_f64(ra, rb)) < 1e-5
+
+
+@pytest.mark.parametrize("fmt_a,fmt_b", [("nvfp4", "fp8"), ("fp8", "nvfp4"), ("nvfp6", "nvfp4")])
+def test_image_product_formats(fmt_a, fmt_b):
+    """FP8 B rows decoded into the image; FP8 and NVFP6 A operands against an image."""
+    I, J, K = 2048, 256, 512
+    print(f"[image] {fmt_a} x {fmt_b}", flush=True)
+    ga, gb, ra, rb = _ops(I, J, K, seed=40, fmt_a=fmt_a, fmt_b=fmt_b)
+    img = tj2.gemm(ga, gb, workspace=_image_workspace(I, J, K))
+    direct = tj2.gemm(ga, gb, split_k=False)
+    torch.cuda.synchronize()
+    assert torch.equal(img, direct)
+    assert H.rel_fro(img.cpu().numpy(), ogemm.gemm_nt_f64(ra, rb)) < 1e-5
+
+
+def _outlier_case(I, J, K, outl, seed):
+    outl = np.asarray(outl, dtype=np.int64)
+    rest = np.setdiff1d(np.arange(J), outl)
+    a_bits = synthetic.normal_bf16((I, K), 1.0, seed)
+    b = synthetic.normal_f32((J, K), 0.02, seed + 1)
+    ga = tj2.quantize(H.bf16_to_device(a_bits))
+    gb = tj2.quantize(H.f32_to_device(b[rest]))
+    gb8 = tj2.quantize(H.f32_to_device(b[outl]), out_fmt=tj2.FP8)
+    ra = quant.quantize(H.bf16_values(a_bits))
+    rb = quant.quantize(np.ascontiguousarray(b[rest]))
+    rb8 = quant.quantize(np.ascontiguousarray(b[outl]), fmt="fp8")
+    H.assert_q_equal(gb, rb, what="B")
+    H.assert_q_equal(gb8, rb8, what="B8")
+    ref = np.zeros((I, J))
+    ref[:, rest] = ogemm.gemm_nt_f64(ra, rb)
+    ref[:, outl] = ogemm.gemm_nt_f64(ra, rb8)
+    return ga, gb, gb8, tj2.OutlierPlan.from_indices(J, outl), ref
+
+
+def _outlier_cases():
+    rng = np.random.default_rng(23)
+    return [
+        ("random", 2304, 400, 896, np.sort(rng.choice(400, 48, replace=False))),
+        ("tile-of-outliers", 2048, 384, 384, np.concatenate([np.arange(128), np.arange(368, 384)])),
+        ("edges", 2100, 272, 128, np.concatenate([np.arange(8), np.arange(264, 272)])),
+    ]
+
+
+@pytest.mark.parametrize("name,I,J,K,outl", _outlier_cases(), ids=[c[0] for c in _outlier_cases()])
+def test_image_outlier_cols(name, I, J, K, outl):
+    """Outlier-column products: the image holds each output column's row (NVFP4 or FP8) in
+    output order.  Equal bit for bit to the direct product, and to the oracle."""
+    print(f"[image] outlier columns {name} {I}x{J}x{K}", flush=True)
+    ga, gb, gb8, plan, ref = _outlier_case(I, J, K, outl, seed=50 + J)
+    ws = _image_workspace(I, J, K)
+    img = tj2.gemm_outlier_cols(ga, gb, gb8, plan, workspace=ws)
+    # a workspace too small for the image: the direct product
+    direct = tj2.gemm_outlier_cols(ga, gb, gb8, plan, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(img, direct)
+    assert H.rel_fro(img.cpu().numpy(), ref) < 1e-5
+
+
+def test_image_outlier_cols_split_k():
+    I, J, K = 2048, 208, 8192
+    print(f"[image] outlier columns split-K {I}x{J}x{K}", flush=True)
+    outl = np.sort(np.random.default_rng(24).choice(J, 32, replace=False))
+    ga, gb, gb8, plan, ref = _outlier_case(I, J, K, outl, seed=60)
+    c = tj2.gemm_outlier_cols(ga, gb, gb8, plan, workspace=_image_workspace(I, J, K)).cpu().numpy()
+    assert H.rel_fro(c, ref) < 1e-5
+
+
+def test_backward_images_from_the_column_quantization():
+    """The backward's dX and dW images written by the column re-grouping of W and X (with an
+    outlier plan, so the FP8 rows land at their channels): dX and dW equal bit for bit those of
+    the same backward without images (no K split at this shape), and sampled outputs match the
+    oracle.  A second call with the re-grouped weights given decodes the dX image itself."""
+    M, N, K = 2048, 2048, 4096
+    rng = np.random.default_rng(5)
+    xb = synthetic.normal_bf16((M, K), 1.0, 81)
+    W = synthetic.normal_f32((N, K), 0.02, 82)
+    dyb = synthetic.normal_bf16((M, N), 0.01, 83)
+    plan_idx = np.sort(rng.choice(K, 128, replace=False))
+    plan = tj2.OutlierPlan.from_indices(K, plan_idx)
+    print(f"[image] backward M={M} N={N} K={K} outliers=128", flush=True)
+    Y, saved = tj2.linear_fwd(H.bf16_to_device(xb), H.f32_to_device(W), N, plan=plan, y_dtype=torch.bfloat16)
+    dY = H.bf16_to_device(dyb)
+    ws = tj2.linear_bwd_workspace(M, N, K, len(plan_idx))
+    dX, dW, ops = tj2.linear_bwd(dY, saved, K, seed=3, offset=16, plan=plan, dx_dtype=torch.bfloat16,
+                                 keep_operands=True, workspace=ws)
+    ops2 = tj2.bwd_operands(M, N, K, plan)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    dX2, dW2, _ = tj2.linear_bwd(dY, saved, K, seed=3, offset=16, plan=plan, dx_dtype=torch.bfloat16,
+                                 operands=ops2, workspace=small)
+    # the re-grouped weights given (as the fused master pass provides them): dX decodes its image
+    dX3, dW3, _ = tj2.linear_bwd(dY, saved, K, seed=3, offset=16, plan=plan, dx_dtype=torch.bfloat16,
+                                 operands=ops, w_given=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dX2) and torch.equal(dW, dW2)
+    assert torch.equal(dX, dX3) and torch.equal(dW, dW3)
+    dX32, _, _ = tj2.linear_bwd(dY, saved, K, seed=3, offset=16, plan=plan, dx_dtype=torch.float32, workspace=ws)
+    Y32, _ = tj2.linear_fwd(H.bf16_to_device(xb), H.f32_to_device(W), N, plan=plan, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    gpu = dict(saved=saved, ops=ops, Y=Y, dX=dX, dW=dW, Y32=Y32, dX32=dX32)
+    err = check_linear_sampled(H.bf16_values(xb), W, H.bf16_values(dyb), plan_idx, 3, 16, gpu, rng, tag="image")
+    print(f"[image] rel_fro dX {err['dX']:.2e} dW {err['dW']:.2e}", flush=True)
