@@ -378,7 +378,7 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     torch.cuda.empty_cache()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_kernel_olmo370m_linears_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "products_olmo370m_linears_traffic.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "bit_fully_quantized_amd", "csrc", f)
                 for f in ("gemm.hip", "tj2_device.h", "tj2_internal.h")]
 
@@ -699,7 +699,9 @@ def main():
             "gemm_tflop_per_step": round(flops_step / 1e12, 3), "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "gemm_nt_kernel (packed NVFP4/FP8 products: fwd with the FP8 segment, dX and dW over all columns)",
+            "kernel": "the products (gemm_img_kernel: dX and dW of >= 2048 output rows with B from f16 images in LDS; "
+                      "gemm_nt_kernel: fwd with the FP8 segment, the other dW); a call includes its split-K reduction "
+                      "and, here, its B decode pass (in the step the column re-grouping writes the images)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",

@@ -204,19 +204,24 @@ tj2_status nvfp4_quantize_dual(const void* x, int64_t rows, int64_t cols, int32_
  * outer block.  c_dtype TJ2_F32 or TJ2_BF16 (round to nearest even); ldc in
  * elements.  col_map (optional, device int32[J]) gives the output column of B
  * row j.  accumulate != 0 adds into C (TJ2_F32 only).
- * workspace: fp32 partial sums of a K split, nvfp4_gemm_workspace_size(I, J,
- * A->len, A2 ? A2->len : 0) bytes (0 for most shapes: the library splits K only
- * when the output has too few 256x128 tiles to fill the GPU).  NULL runs the
- * product without a split; a non-NULL workspace smaller than the size asked
- * for is an error (TJ2_ERR_ARG).
+ * workspace: fp32 partial sums of a K split (the library splits K only when
+ * the output has too few 256x128 tiles to fill the GPU), then, for a
+ * one-segment product of at least 2048 rows, room for B decoded once into an
+ * f16 image that the product copies into LDS instead of decoding B again in
+ * every row tile: nvfp4_gemm_workspace_size(I, J, A->len, A2 ? A2->len : 0)
+ * bytes for both (0 when neither applies).  NULL runs the product without a
+ * split or an image; a non-NULL workspace smaller than the partial sums need is
+ * an error (TJ2_ERR_ARG); one that holds the partial sums but not the image
+ * runs without the image.  The results do not depend on the image (the same
+ * f16 values, the same order of operations).
  */
 tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qtensor* A2,
                       const tj2_qtensor* B2, void* C, int32_t c_dtype, int64_t ldc,
                       const int32_t* col_map, int32_t accumulate, void* workspace, size_t ws_bytes,
                       void* stream);
 /* Workspace of nvfp4_gemm for I x J outputs over reductions of K (and K2 for a
- * second segment, else 0) elements; the same for nvfp4_gemm_outlier_cols with
- * K2 = 0.  Returns 0 for invalid sizes. */
+ * second segment, else 0) elements, image included; the same for
+ * nvfp4_gemm_outlier_cols with K2 = 0.  Returns 0 for invalid sizes. */
 size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K, int64_t K2);
 
 /*
@@ -292,7 +297,11 @@ size_t nvfp4_linear_fwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t 
  * scattered back to their original channel positions.
  * ops (optional): caller buffers for the intermediate operands (shapes in
  * tj2_bwd_operands); NULL = carve them from `workspace`, which must then hold
- * nvfp4_linear_bwd_workspace_size(M, N, K, n_outliers) bytes.
+ * nvfp4_linear_bwd_workspace_size(M, N, K, n_outliers) bytes.  That size also
+ * covers the split-K partial sums and the B images of the two products (dX for
+ * M >= 2048, dW for N >= 2048), which the column re-grouping of W-hat and
+ * X-hat writes as it quantizes; with ops given, a workspace that holds them
+ * (NULL or smaller: products without them) is used the same way.
  */
 tj2_status nvfp4_linear_bwd(const void* dY, int64_t M, int64_t N, int64_t K, const tj2_qtensor* Xq,
                             const tj2_qtensor* X8, const tj2_qtensor* Wq, const tj2_qtensor* W8,
