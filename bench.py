@@ -111,6 +111,48 @@ def osci_batch(tj2, lins):
     return _OSCI_BATCH[key][1]
 
 
+def gpu_state_under_load(run, seconds=1.5):
+    """GPU clocks, socket power and temperatures (amd-smi, a child process) sampled while `run`
+    (untimed steps) keeps the GPU busy; None where amd-smi is missing or fails."""
+    import subprocess
+    import threading
+
+    import torch
+    res = {}
+
+    def sample():
+        time.sleep(0.6)  # under load by then
+        try:
+            out = subprocess.run(["amd-smi", "metric", "-p", "-c", "-t", "--json"], capture_output=True, text=True,
+                                 timeout=30)
+            res["data"] = json.loads(out.stdout)
+        except Exception as e:  # noqa: BLE001 - report, do not fail the benchmark
+            res["error"] = str(e)[:200]
+
+    th = threading.Thread(target=sample)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    while th.is_alive() or time.perf_counter() < t_end:
+        run()
+        torch.cuda.synchronize()
+    th.join()
+    if "data" not in res:
+        return {"error": res.get("error", "no data")}
+    try:
+        g = res["data"]["gpu_data"][0] if isinstance(res["data"], dict) else res["data"][0]
+        val = lambda x: x["value"] if isinstance(x, dict) else None  # noqa: E731
+        gfx = [val(v["clk"]) for k, v in g["clock"].items() if k.startswith("gfx_") and isinstance(v, dict)]
+        gfx = [c for c in gfx if c is not None]
+        return {"what": "amd-smi metric while untimed steps ran right after the timed ones",
+                "gfx_clk_mhz_mean": round(sum(gfx) / len(gfx), 1) if gfx else None,
+                "gfx_clk_mhz_min_max": [min(gfx), max(gfx)] if gfx else None,
+                "mem_clk_mhz": val(g["clock"].get("mem_0", {}).get("clk")) if isinstance(g["clock"].get("mem_0"), dict) else None,
+                "socket_power_w": val(g["power"].get("socket_power")),
+                "hotspot_c": val(g["temperature"].get("hotspot")), "mem_c": val(g["temperature"].get("mem"))}
+    except (KeyError, IndexError, TypeError, ValueError) as e:
+        return {"error": f"unexpected amd-smi output: {e}"[:200]}
+
+
 def time_launches(fn, reps):
     """Average duration (s) of fn() over reps launches, HIP events on the current stream."""
     import torch
@@ -611,6 +653,15 @@ def main():
     step_s = wall / args.steps
     step_ev = ev0.elapsed_time(ev1) / 1e3 / args.steps
     log(f"step {step_s * 1e3:.2f} ms (events {step_ev * 1e3:.2f} ms)")
+    gpu_state = None
+    if not args.headline_only:
+        log("clocks and power under the step's load")
+        n_extra = [0]
+
+        def extra_step():
+            run_step(tj2, lins, ws, args.warmup + args.steps + n_extra[0])
+            n_extra[0] += 1
+        gpu_state = gpu_state_under_load(extra_step)
 
     log("product roofline pass")
     g_flops, g_time, g_bytes, g_launches, per = gemm_roofline(tj2, lins, layers, M, ws)
@@ -747,6 +798,7 @@ def main():
                              "window_end_with_hist_ms": round(diag_end_t * 1e3, 3),
                              "window_end_with_hist_GB_s": round(master_bytes / diag_end_t / 1e9, 1),
                              "flips_per_pass": flips_per_pass, "risk_hist_one_window_end": risk_hist},
+        "gpu_state": gpu_state,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
