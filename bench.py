@@ -85,7 +85,7 @@ class LinearState:
         self.dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
         self.dW = torch.empty(N, K, dtype=torch.float32, device="cuda")
         self.state = [torch.empty_like(self.W) for _ in range(4)]
-        tj2.osci_reset_step(self.W, *self.state, mode=tj2.OSCI_INIT)
+        tj2.osci_reset_step(self.W, *self.state, mode=tj2.OSCI_INIT, plan=self.plan)
         self.saved = None
 
 
@@ -104,10 +104,12 @@ _OSCI_BATCH = {}
 
 
 def osci_batch(tj2, lins):
-    """The OsciReset descriptors of all linears, built once (one launch per 16 weight matrices)."""
+    """The OsciReset descriptors of all linears, built once (one launch per 16 weight matrices), with
+    each linear's outlier plan: the state arrays follow the forward's quantizer (FP8 outlier channels,
+    NVFP4 over the compacted rest)."""
     key = id(lins)
     if key not in _OSCI_BATCH:
-        _OSCI_BATCH[key] = (lins, tj2.OsciBatch([(li.W, *li.state, None) for li in lins]))
+        _OSCI_BATCH[key] = (lins, tj2.OsciBatch([(li.W, *li.state, None, li.plan, None) for li in lins]))
     return _OSCI_BATCH[key][1]
 
 
@@ -405,6 +407,23 @@ def tj2_master_pass(stack, lr):
                                  mode=tj2.OSCI_ACCUM, tau=c.tau)
 
 
+def stream_reference(n, reps=3):
+    """HBM rate (GB/s) of the OsciReset and master passes' access pattern without their arithmetic
+    (libtj2_measure's tj2_stream_probe) over n fp32 elements per array."""
+    import torch
+    import bit_fully_quantized_amd as tj2
+    bufs = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(13)]
+    res = {}
+    for name, ns, nd in (("osci_5r4w", 5, 4), ("master_7r6w", 7, 6)):
+        src, dst = bufs[:ns], bufs[7:7 + nd]
+        nbytes = tj2.stream_probe(src, dst)
+        t = time_launches(lambda: tj2.stream_probe(src, dst), reps)
+        res[name] = round(nbytes / t / 1e9, 1)
+    del bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(nbytes=1 << 30, reps=3):
     """A plain elementwise copy kernel of known size (bf16 negation, 1 GiB read + 1 GiB written per launch).
 
@@ -693,6 +712,13 @@ def main():
                                                                   tau=4.0), 3)
     # read W, m, v, grad, Q_prev, dQ, dM; write W, m, v, Q_prev, dQ, dM (fp32)
     master_bytes = n_params * 52.0
+    master_plan_batch = tj2.MasterBatch([(li.W, li.m, li.v, li.dW, *li.state[1:], None, li.plan, None, None)
+                                         for li in lins])
+    master_plan_t = time_launches(lambda: tj2.master_update_step_multi(master_plan_batch, lr=1e-6,
+                                                                       bias_correction1=0.1, bias_correction2=0.05,
+                                                                       mode=tj2.OSCI_ACCUM, tau=4.0), 3)
+    log("OsciReset / master access-pattern reference")
+    pattern = stream_reference(n_params)
     log("oscillation diagnostics")
     flips = torch.zeros(1, dtype=torch.int64, device="cuda")
     hist = torch.zeros(tj2.RISK_BINS, dtype=torch.int64, device="cuda")
@@ -782,15 +808,27 @@ def main():
         "quantizer_sweep": {"tensor": "bf16 8192x4096 N(0,1), 1% columns x64", "algorithmic_MB_per_call":
                             round(sweep_bytes / 1e6, 2), "hbm_peak_GB_s": HBM_PEAK_GBS, **sweep},
         "osci_reset": {"what": "OsciReset accumulate over all masters through osci_reset_step_multi (16 weight "
-                               "matrices per launch; 36 B/param)",
+                               "matrices per launch, each with its outlier plan; 36 B/param), as in the step",
                        "GB_s": round(osci_bytes / osci_t / 1e9, 1),
                        "frac_hbm": round(osci_bytes / osci_t / 1e9 / HBM_PEAK_GBS, 3),
+                       "access_pattern_GB_s": pattern["osci_5r4w"],
+                       "frac_of_access_pattern": round(osci_bytes / osci_t / 1e9 / pattern["osci_5r4w"], 3),
                        "ms_per_step": round(osci_t * 1e3, 3), "params": n_params},
         "master_update": {"what": "fused AdamW + OsciReset accumulate over all masters through "
-                                  "master_update_step_multi (16 weight matrices per launch; 52 B/param)",
+                                  "master_update_step_multi (16 weight matrices per launch; 52 B/param), without "
+                                  "and with the outlier plans (with a plan W and its gradient are gathered through "
+                                  "the channel lists)",
                           "GB_s": round(master_bytes / master_t / 1e9, 1),
                           "frac_hbm": round(master_bytes / master_t / 1e9 / HBM_PEAK_GBS, 3),
-                          "ms_per_step": round(master_t * 1e3, 3), "params": n_params},
+                          "access_pattern_GB_s": pattern["master_7r6w"],
+                          "frac_of_access_pattern": round(master_bytes / master_t / 1e9 / pattern["master_7r6w"], 3),
+                          "ms_per_step": round(master_t * 1e3, 3),
+                          "with_plans_GB_s": round(master_bytes / master_plan_t / 1e9, 1),
+                          "with_plans_ms_per_step": round(master_plan_t * 1e3, 3), "params": n_params},
+        "access_pattern_reference": {"what": "libtj2_measure's tj2_stream_probe: the OsciReset pass's loads and "
+                                             "stores (5 fp32 reads, 4 writes per element) and the master pass's "
+                                             "(7 reads, 6 writes), 8 consecutive elements per thread, no arithmetic, "
+                                             "over as many elements as the masters", **pattern},
         "osci_diagnostics": {"what": "fused master pass with oscillation diagnostics: per-pass flip count (ACCUM), "
                                      "window risk histogram in 32 log2 bins (WINDOW_END)",
                              "accum_with_flips_ms": round(diag_accum_t * 1e3, 3),

@@ -545,6 +545,22 @@ def decode_probe(out: torch.Tensor, iters: int, packed_b: bool) -> float:
     return float(wgs) * 8 * iters * 32 * 32768
 
 
+def stream_probe(src, dst) -> float:
+    """Measurement helper from libtj2_measure (not part of the path): the OsciReset (5 reads, 4
+    writes) or master-pass (7 reads, 6 writes) access pattern without arithmetic over equal-sized
+    contiguous float32 device tensors; returns the bytes it moves."""
+    n = src[0].numel()
+    for t in list(src) + list(dst):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+            raise ValueError("stream_probe takes contiguous device float32 tensors of one size")
+    sp = (ctypes.c_void_p * len(src))(*[t.data_ptr() for t in src])
+    dp = (ctypes.c_void_p * len(dst))(*[t.data_ptr() for t in dst])
+    st = _lib.measure_lib().tj2_stream_probe(sp, len(src), dp, len(dst), n, _stream())
+    if st != 0:
+        raise Tj2Error("tj2_stream_probe", st, "bad arguments or launch error")
+    return 4.0 * (len(src) + len(dst)) * (n - n % 8)
+
+
 def channel_sumsq(X: torch.Tensor, acc: torch.Tensor, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """acc[k] += sum_m X[m, k]^2 (fp64, fixed summation order); acc: device float64 [K]."""
     _dense(X, "X", _BF16)

@@ -148,6 +148,8 @@ def measure_lib():
         L.tj2_mfma_peak_probe.argtypes = [I64, I32, P, P]
         L.tj2_decode_probe.restype = I32
         L.tj2_decode_probe.argtypes = [I32, I64, I32, P, P]
+        L.tj2_stream_probe.restype = I32
+        L.tj2_stream_probe.argtypes = [P, I32, P, I32, I64, P]
         _mlib = L
     return _mlib
 

@@ -20,6 +20,9 @@
 //   fragment).
 // The packed data is synthetic and changes every chunk, so no decode is hoisted
 // out of the loop.
+//
+// tj2_stream_probe: the HBM rate of the OsciReset and master-weight passes'
+// access pattern (their loads and stores, no arithmetic).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -127,7 +130,61 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int32_t iters, _Float16 
   out[(int64_t)blockIdx.x * 256 + threadIdx.x] = ((c0[0] + c1[0]) + c2[0]) + c3[0];
 }
 
+// The access pattern of the OsciReset pass (NS = 5 reads, ND = 4 writes) and of
+// the fused master pass (7 reads, 6 writes) without their arithmetic: lane g
+// owns elements 8g..8g+7 of every array (two 16-byte pieces), issues all its
+// loads, then writes dst[i] = src[i] + src[NS - 1].
+struct StreamArgs {
+  const float* src[8];
+  float* dst[8];
+  int64_t n8;
+};
+
+template <int NS, int ND>
+__global__ __launch_bounds__(256) void stream_probe_kernel(StreamArgs a) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= a.n8) return;
+  float4 x[NS][2];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const float4* q = reinterpret_cast<const float4*>(a.src[i] + g * 8);
+    x[i][0] = q[0];
+    x[i][1] = q[1];
+  }
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    float4* q = reinterpret_cast<float4*>(a.dst[i] + g * 8);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4 u = x[i][h], v = x[NS - 1][h];
+      q[h] = make_float4(u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w);
+    }
+  }
+}
+
 }  // namespace
+
+extern "C" int32_t tj2_stream_probe(const float* const* src, int32_t nsrc, float* const* dst, int32_t ndst, int64_t n,
+                                    void* stream) {
+  if (!src || !dst || n < 8 || n > ((int64_t)1 << 36) || !((nsrc == 5 && ndst == 4) || (nsrc == 7 && ndst == 6)))
+    return 1;
+  StreamArgs a{};
+  for (int i = 0; i < nsrc; ++i) {
+    if (!src[i] || (reinterpret_cast<uintptr_t>(src[i]) & 15u)) return 1;
+    a.src[i] = src[i];
+  }
+  for (int i = 0; i < ndst; ++i) {
+    if (!dst[i] || (reinterpret_cast<uintptr_t>(dst[i]) & 15u)) return 1;
+    a.dst[i] = dst[i];
+  }
+  a.n8 = n / 8;
+  const dim3 grid((uint32_t)((a.n8 + 255) / 256));
+  if (nsrc == 5)
+    hipLaunchKernelGGL((stream_probe_kernel<5, 4>), grid, dim3(256), 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((stream_probe_kernel<7, 6>), grid, dim3(256), 0, (hipStream_t)stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 extern "C" int32_t tj2_decode_probe(int32_t packed_b, int64_t workgroups, int32_t iters, float* out, void* stream) {
   if (!out || workgroups < 1 || workgroups > ((int64_t)1 << 20) || iters < 1 || iters > (1 << 20)) return 1;

@@ -40,6 +40,20 @@ int32_t tj2_mfma_peak_probe(int64_t workgroups, int32_t iters, float* out, void*
  */
 int32_t tj2_decode_probe(int32_t packed_b, int64_t workgroups, int32_t iters, float* out, void* stream);
 
+/*
+ * The access pattern of the OsciReset pass (nsrc = 5 reads, ndst = 4 writes,
+ * 36 B per element) or of the fused master-weight pass (nsrc = 7, ndst = 6,
+ * 52 B per element) without their arithmetic: element-wise over n fp32
+ * elements (the first n - n % 8), 8 consecutive elements per thread, every
+ * load issued before the stores, dst[i][e] = src[i][e] + src[nsrc - 1][e].
+ * src, dst: host arrays of device pointers (16-byte aligned, n floats each,
+ * caller-owned; the destinations may not overlap the sources).  Returns 0, 1
+ * (NULL or misaligned pointer, n outside [8, 2^36], or another nsrc / ndst
+ * pair; nothing enqueued) or 4 (launch error).
+ */
+int32_t tj2_stream_probe(const float* const* src, int32_t nsrc, float* const* dst, int32_t ndst, int64_t n,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

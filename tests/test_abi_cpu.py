@@ -239,6 +239,16 @@ def test_measurement_helpers_live_outside_the_product_library(L):
     assert M.tj2_mfma_peak_probe(16, 0, 0x1000, None) == 1
     text = open(os.path.join(ROOT, "include", "tj2_measure.h")).read()
     assert "tj2_mfma_peak_probe" in text
+    # the access-pattern reference: argument checks only (they return before any launch)
+    assert not hasattr(L, "tj2_stream_probe") and "tj2_stream_probe" in text
+    five = (ctypes.c_void_p * 7)(*([0x10000] * 7))
+    four = (ctypes.c_void_p * 6)(*([0x20000] * 6))
+    assert M.tj2_stream_probe(None, 5, four, 4, 1024, None) == 1
+    assert M.tj2_stream_probe(five, 6, four, 4, 1024, None) == 1  # only 5 / 4 and 7 / 6
+    assert M.tj2_stream_probe(five, 7, four, 4, 1024, None) == 1
+    assert M.tj2_stream_probe(five, 5, four, 4, 4, None) == 1  # n below 8
+    bad = (ctypes.c_void_p * 7)(*([0x10004] + [0x10000] * 6))  # not 16-byte aligned
+    assert M.tj2_stream_probe(bad, 5, four, 4, 1024, None) == 1
 
 
 def _plan_from_library(L, scores, p):
