@@ -156,10 +156,15 @@ tj2_status run_quant(const void* x, int x_dtype, const tj2_qtensor* x_q, int64_t
 
 // One read of X (or W) into its NVFP4 rest columns and FP8 outlier columns.
 // Rows wider than 32 KB go through the two gathering row quantizations.
+// With img (the forward product's B image, rows = its output columns), the
+// split quantization also writes the rows' decoded f16 values into it: NVFP4
+// chunks first, then the FP8 chunks (the caller checks that the split kernel
+// runs: rows within 32 KB).
 tj2_status run_split(const void* x, int x_dtype, int64_t rows, int64_t K, const tj2_outlier_plan* plan,
-                     const tj2_qtensor* q4, const tj2_qtensor* q8, hipStream_t s) {
+                     const tj2_qtensor* q4, const tj2_qtensor* q8, hipStream_t s, uint8_t* img = nullptr) {
   const int64_t no = plan->n_outliers, K1 = K - no;
   if (K * (x_dtype == TJ2_BF16 ? 2 : 4) > 32768) {
+    if (img) return fail(TJ2_ERR_ARG, "the B image needs rows within 32 KB");
     TJ2_TRY(run_quant(x, x_dtype, nullptr, rows, K, plan->rest, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, q4, s));
     return run_quant(x, x_dtype, nullptr, rows, K, plan->outliers, no, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, q8, s);
   }
@@ -173,6 +178,14 @@ tj2_status run_split(const void* x, int x_dtype, int64_t rows, int64_t K, const 
   p.outl = plan->outliers;
   p.q4 = make_view(*q4);
   p.q8 = make_view(*q8);
+  if (img) {
+    const int64_t tiles = (rows + 127) / 128, n0c = (K1 + 127) / 128, nch = n0c + (no + 127) / 128;
+    p.img = img;
+    p.img_nch = (int)nch;
+    p.img_g8 = (int)n0c;
+    p.img_ld = tiles * 128;
+    p.img_sc = reinterpret_cast<float*>(img + (size_t)tiles * (size_t)nch * kImgChunkBytes);
+  }
   return hip_check(launch_quant_split(p, s), "split quantize launch");
 }
 
@@ -184,9 +197,20 @@ struct GemmImage {
   int ready = 0;
 };
 
-// Image bytes of a one-segment product of I x J over K (0 when it would not pay).
-size_t image_bytes(int64_t I, int64_t J, int64_t K) {
-  return gemm_image_pays(I) ? align256(gemm_image_bytes(J, (K + 127) / 128)) : 0;
+// Image bytes of a product of I x J over K (+ K2 for a second segment; 0 when
+// it would not pay).
+size_t image_bytes(int64_t I, int64_t J, int64_t K, int64_t K2 = 0) {
+  return gemm_image_pays(I) ? align256(gemm_image_bytes(J, gemm_chunks(K, K2))) : 0;
+}
+
+// Whether the forward's product runs from a B image that the weights' split
+// quantization writes beside Wq and W8: an outlier plan, the masters given and
+// staged whole by that quantization (K * 4 bytes within 32 KB), an NVFP4
+// segment of more than one chunk, one K split and enough row tiles.
+bool fwd_image(int64_t M, int64_t N, int64_t K, int64_t no, bool w_master) {
+  const int64_t K1 = K - no;
+  return no > 0 && w_master && K * 4 <= 32768 && K1 > 128 && gemm_image_pays(M) &&
+         gemm_split(M, N, gemm_chunks(K1, no)) == 1;
 }
 
 // The image part of a product's workspace: after its split-K partials (need
@@ -530,7 +554,9 @@ tj2_status nvfp4_gemm_outlier_cols(const tj2_qtensor* A, const tj2_qtensor* B, c
 
 size_t nvfp4_linear_fwd_workspace_size(int64_t M, int64_t N, int64_t K, int32_t n_outliers) {
   if (M <= 0 || N <= 0 || K <= 0 || n_outliers < 0 || n_outliers >= K) return 0;
-  return gemm_workspace_bytes(M, N, gemm_chunks(K - n_outliers, n_outliers));
+  const size_t part = gemm_workspace_bytes(M, N, gemm_chunks(K - n_outliers, n_outliers));
+  const size_t img = fwd_image(M, N, K, n_outliers, true) ? image_bytes(M, N, K - n_outliers, n_outliers) : 0;
+  return img ? align256(part) + img : part;
 }
 
 tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, const float* W_master, tj2_qtensor* Wq,
@@ -552,20 +578,25 @@ tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, cons
     TJ2_TRY(check_qtensor(X8, "X8", TJ2_FP8, M, no));
     TJ2_TRY(check_qtensor(W8, "W8", TJ2_FP8, N, no));
   }
+  GemmImage img;
   if (workspace) {
     if (!aligned16(workspace)) return fail(TJ2_ERR_ALIGN, "workspace must be 16-byte aligned");
-    const size_t need = nvfp4_linear_fwd_workspace_size(M, N, K, (int32_t)no);
+    // the K-split partials are required; the B image is used when there is room for it
+    const size_t need = gemm_workspace_bytes(M, N, gemm_chunks(K1, no));
     if (ws_bytes < need) return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    if (fwd_image(M, N, K, no, W_master != nullptr))
+      img = workspace_image(workspace, ws_bytes, need, image_bytes(M, N, K1, no));
   }
   if (plan) {
     TJ2_TRY(run_split(X, TJ2_BF16, M, K, plan, Xq, X8, s));
-    if (W_master) TJ2_TRY(run_split(W_master, TJ2_F32, N, K, plan, Wq, W8, s));
+    if (W_master) TJ2_TRY(run_split(W_master, TJ2_F32, N, K, plan, Wq, W8, s, static_cast<uint8_t*>(img.ptr)));
+    img.ready = img.ptr ? 1 : 0;  // written by the split quantization above
   } else {
     TJ2_TRY(run_quant(X, TJ2_BF16, nullptr, M, K, nullptr, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Xq, s));
     if (W_master) TJ2_TRY(run_quant(W_master, TJ2_F32, nullptr, N, K, nullptr, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Wq, s));
   }
   TJ2_TRY(run_gemm(Xq, Wq, plan ? X8 : nullptr, plan ? W8 : nullptr, Y, y_dtype, N, nullptr, 0, workspace,
-                   workspace ? ws_bytes : 0, s));
+                   workspace ? ws_bytes : 0, s, img));
   return ok();
 }
 

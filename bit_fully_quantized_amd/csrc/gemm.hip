@@ -36,6 +36,12 @@
 // N-fastest: consecutive tiles on one XCD share their A rows.  Results leave
 // through LDS as 16-byte row pieces where the tile's columns are contiguous
 // and aligned in the output (element stores otherwise).
+//
+// Image products (products of 2048 rows or more, when the caller gives room):
+// B is decoded once into f16 chunk images laid out as the LDS stage, by the
+// quantization that produces B or by a decode pass, and gemm_img_kernel (one
+// K segment) and gemm_img2_kernel (the forward's NVFP4 + FP8 segments) copy
+// each chunk's image into LDS with global_load_lds instead of decoding B.
 #include "tj2_device.h"
 #include "tj2_internal.h"
 
@@ -886,7 +892,9 @@ struct FmtTag {
 };
 
 // One chunk of an image product: the slots of chunk() above without the B
-// staging.  The A fragments come from this chunk's slice `a` (format FA); at
+// staging.  The A fragments come from this chunk's slice `a` (format FA; the
+// next chunk's slice `an` is in format FN, which differs from FA only where a
+// two-segment product crosses from its NVFP4 to its FP8 segment); at
 // slot 7 the next chunk's S_B is requested (fetch_sb) and at slot 8 the slice
 // of the chunk after next (fetch_a, into `a`, whose fragments are decoded by
 // then); the next chunk's slice `an`, requested one chunk earlier, is prepared
@@ -896,7 +904,7 @@ struct FmtTag {
 // this stage is no longer read) and starts the copy of the chunk after next
 // into this stage.  sbc holds S_B of this chunk's column pairs (lanes 0-31
 // columns of block 2p, lanes 32-63 of block 2p + 1).
-template <int FA, int kFragAhead, class FETCH_SB, class FETCH_A, class SYNC>
+template <int FA, int kFragAhead, int FN, class FETCH_SB, class FETCH_A, class SYNC>
 __device__ __forceinline__ void chunk_img(const _Float16* bb, const _Float16* bn, half8_t (&af)[8],
                                           half2_t (&sga)[4], half8_t (&bf)[frag_ring(kFragAhead)],
                                           float (&acc)[4][16], float16v_t (&part)[2], float32v_t& smat, Slice& a,
@@ -920,8 +928,8 @@ __device__ __forceinline__ void chunk_img(const _Float16* bb, const _Float16* bn
       smat = __builtin_amdgcn_mfma_f32_32x32x1f32(sa, sbc.x, float32v_t{}, 0, 0, 0);
       fetch_a(a);
     }
-    if constexpr (q == 30) Op<FA>::prep_a(an, sga);
-    if constexpr (q == 31) af[0] = Op<FA>::template frag_a<0>(an, sga);
+    if constexpr (q == 30) Op<FN>::prep_a(an, sga);
+    if constexpr (q == 31) af[0] = Op<FN>::template frag_a<0>(an, sga);
     if constexpr (q == 32 - kFragAhead) sync();
     constexpr int qf = q + kFragAhead;
     if constexpr (qf < 32) bf[qf % kFragRing] = ld8(bb + (qf / 8) * 32 * LDS_STRIDE + (qf % 8) * 8);
@@ -1038,7 +1046,7 @@ __global__ __launch_bounds__(512, 1) void gemm_img_kernel(GemmKArgs p) {
         __builtin_amdgcn_s_barrier();
         dma(it + 2, ST);
       };
-      chunk_img<FA, kFragAhead>(sm.b[ST] + lane_off, sm.b[ST ^ 1] + lane_off, af, sga, bf, acc, part, smat, as[ST],
+      chunk_img<FA, kFragAhead, FA>(sm.b[ST] + lane_off, sm.b[ST ^ 1] + lane_off, af, sga, bf, acc, part, smat, as[ST],
                                  as[ST ^ 1], cur, fetch_sb, fetch_a, sync);
     };
     int it = 0;
@@ -1056,6 +1064,160 @@ __global__ __launch_bounds__(512, 1) void gemm_img_kernel(GemmKArgs p) {
   store_tile<false>(p, smem.out, t, m0, n0, z, acc, 0, BN, 0, BN);
 }
 
+// The forward's two-segment product (NVFP4 x NVFP4 over the rest channels,
+// then FP8 x FP8 over the outlier channels) from one chunk image of both
+// segments' B rows: the pipelined loop runs through the segment boundary, so
+// the FP8 chunks are pipelined like the others.  Each chunk's code knows the
+// formats of its own slice, of the next chunk's (decoded at its last slots)
+// and of the one it requests (two chunks ahead): NVFP4 up to chunk n0 - 3,
+// the crossing at chunks n0 - 2 and n0 - 1, FP8 from n0 on.  P0 = n0 & 1
+// fixes the stage parity of the crossing, so stages and slices stay
+// compile-time indices.  One split (no K split); n0 >= 2, at least one FP8
+// chunk.
+template <int P0>
+__global__ __launch_bounds__(512, 1) void gemm_img2_kernel(GemmKArgs p) {
+  constexpr int N4 = TJ2_NVFP4, F8 = TJ2_FP8;
+  __shared__ __attribute__((aligned(16))) SmemImgAll smem;
+  SmemImg& sm = smem.loop;
+
+  const uint32_t nwg = gridDim.x;
+  uint32_t id = blockIdx.x;
+  const uint32_t per_xcd = nwg / 8;
+  if (id < per_xcd * 8) id = (id % 8) * per_xcd + id / 8;
+  const uint32_t tile = id;
+  const uint32_t tj = tile % (uint32_t)p.tiles_n;
+  const int64_t m0 = (int64_t)(tile / p.tiles_n) * BM, n0 = (int64_t)tj * BN;
+
+  Ctx t;
+  t.lane = threadIdx.x & 63;
+  t.w = threadIdx.x >> 6;
+  t.ah = t.lane >> 5;
+  t.bq = 0;
+  t.b8 = false;
+  const uint32_t arow = (uint32_t)min(m0 + t.w * 32 + (t.lane & 31), p.I - 1);
+  t.arn[0] = arow * (uint32_t)p.seg[0].a.ld_s128;
+  t.arn[1] = arow * (uint32_t)p.seg[1].a.ld_s128;
+  t.brn[0] = t.brn[1] = 0;
+  t.n0c = p.seg[0].nchunks;
+  t.c_begin = 0;
+  const int n = p.nchunks, nc0 = t.n0c;
+
+  const uint8_t* img = p.bimg + (size_t)tj * (size_t)n * kImgChunkBytes;
+  const float* sbl = p.bsc + n0 + t.lane;
+  const uint32_t lds_w = __builtin_amdgcn_readfirstlane(lds_addr(sm.b[0]) + (uint32_t)t.w * 1024u);
+  const uint32_t voff = (uint32_t)t.lane * 16u + (uint32_t)t.w * 1024u;
+  auto dma = [&](int c, int st) __attribute__((always_inline)) {
+    dma_chunk(img + (size_t)min(c, n - 1) * kImgChunkBytes, lds_w + (uint32_t)st * (uint32_t)kImgChunkBytes, voff,
+              t.w, c < n ? 1 : 0);
+  };
+  auto load_sb = [&](int it, float2& sb) __attribute__((always_inline)) {
+    const float* q = sbl + (size_t)min(it, n - 1) * (size_t)p.bsc_ld;
+    sb.x = q[0];
+    sb.y = q[64];
+  };
+  // the slice of chunk c in format F (chunks past the range reload the last one)
+  auto load_slice = [&](auto ft, int c, Slice& sl) __attribute__((always_inline)) {
+    constexpr int F = decltype(ft)::value;
+    if constexpr (F == N4) Op<N4>::load_half(p.seg[0].a, t.arn[0], c, t.ah, sl);
+    else Op<F8>::load_half(p.seg[1].a, t.arn[1], min(c, n - 1) - nc0, t.ah, sl);
+  };
+
+  float acc[4][16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+
+  Slice as[2];
+  float2 sbc, sbn;
+  load_slice(FmtTag<N4>{}, 0, as[0]);
+  load_sb(0, sbc);
+  dma(0, 0);
+  barrier_all();
+  dma(1, 1);
+
+  {
+    load_slice(FmtTag<N4>{}, 1, as[1]);
+    half8_t af[8];
+    half2_t sga[4];
+    float16v_t part[2];
+    part[1] = float16v_t{};
+    float32v_t smat = float32v_t{};
+    constexpr int kFragAhead = kFragAheadSlots;
+    half8_t bf[frag_ring(kFragAhead)];
+    const int lane_off = (t.lane & 31) * LDS_STRIDE + (t.lane >> 5) * 64;
+    Op<N4>::prep_a(as[0], sga);
+    af[0] = Op<N4>::template frag_a<0>(as[0], sga);
+    {
+      const _Float16* bb = sm.b[0] + lane_off;
+      static_for<kFragAhead>([&](auto f) __attribute__((always_inline)) {
+        bf[decltype(f)::value] = ld8(bb + decltype(f)::value * 8);
+      });
+    }
+    // chunk it in stage ST: its slice in format FC, the next chunk's in FN, the
+    // one requested at slot 8 (chunk it + 2) in FF
+    auto run = [&](auto st, auto fc, auto fn, auto ff, int it) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st)::value;
+      constexpr int FC = decltype(fc)::value, FN = decltype(fn)::value, FF = decltype(ff)::value;
+      float2& cur = ST ? sbn : sbc;
+      float2& nxt = ST ? sbc : sbn;
+      auto fetch_sb = [&]() __attribute__((always_inline)) { load_sb(it + 1, nxt); };
+      auto fetch_a = [&](Slice& sl) __attribute__((always_inline)) { load_slice(FmtTag<FF>{}, it + 2, sl); };
+      auto sync = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0070 | Op<FF>::kHalfLoads);  // vmcnt(slice loads) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        dma(it + 2, ST);
+      };
+      chunk_img<FC, kFragAhead, FN>(sm.b[ST] + lane_off, sm.b[ST ^ 1] + lane_off, af, sga, bf, acc, part, smat,
+                                    as[ST], as[ST ^ 1], cur, fetch_sb, fetch_a, sync);
+    };
+    using S0 = FmtTag<0>;
+    using S1 = FmtTag<1>;
+    using TN = FmtTag<N4>;
+    using TF = FmtTag<F8>;
+    int it = 0;
+    // NVFP4 chunks whose requests are NVFP4 too (it + 2 < n0)
+    for (; it + 3 < nc0; it += 2) {
+      run(S0{}, TN{}, TN{}, TN{}, it);
+      run(S1{}, TN{}, TN{}, TN{}, it + 1);
+    }
+    if constexpr (P0 == 1) {  // n0 odd: chunk n0 - 3 (stage 0) is the last of them
+      run(S0{}, TN{}, TN{}, TN{}, it);
+      ++it;
+    }
+    // the crossing: chunk n0 - 2 requests the first FP8 slice, chunk n0 - 1
+    // decodes it at its last slots
+    if constexpr (P0 == 0) {
+      run(S0{}, TN{}, TN{}, TF{}, it);
+      run(S1{}, TN{}, TF{}, TF{}, it + 1);
+    } else {
+      run(S1{}, TN{}, TN{}, TF{}, it);
+      run(S0{}, TN{}, TF{}, TF{}, it + 1);
+    }
+    it += 2;
+    // FP8 chunks, from stage n0 & 1
+    if constexpr (P0 == 0) {
+      for (; it + 1 < n; it += 2) {
+        run(S0{}, TF{}, TF{}, TF{}, it);
+        run(S1{}, TF{}, TF{}, TF{}, it + 1);
+      }
+      if (it < n) run(S0{}, TF{}, TF{}, TF{}, it);
+    } else {
+      for (; it + 1 < n; it += 2) {
+        run(S1{}, TF{}, TF{}, TF{}, it);
+        run(S0{}, TF{}, TF{}, TF{}, it + 1);
+      }
+      if (it < n) run(S1{}, TF{}, TF{}, TF{}, it);
+    }
+    static_for<16>([&](auto e) __attribute__((always_inline)) {
+      constexpr int i = decltype(e)::value;
+      acc[3][i] = fmaf(part[1][i], smat[16 + i], acc[3][i]);
+    });
+  }
+
+  store_tile<false>(p, smem.out, t, m0, n0, 0, acc, 0, BN, 0, BN);
+}
+
 // B decode into chunk images: a workgroup of 256 threads per (chunk g, 64
 // source rows); thread (unit u = t % 16, rows v = 64 * slab + 16k + t / 16,
 // k = 0..3) decodes K elements 8u..8u+7 of the chunk in four rows into 16-byte
@@ -1068,7 +1230,8 @@ __global__ __launch_bounds__(512, 1) void gemm_img_kernel(GemmKArgs p) {
 struct ImgArgs {
   OperandK b;
   int fmt;
-  int nchunks;
+  int nchunks;  // chunks of the whole image
+  int g0;       // image chunk of B's chunk 0 (a second segment's B follows the first's)
   OperandK b8;
   const int32_t* outl;
   const int32_t* rest;
@@ -1123,10 +1286,11 @@ __global__ __launch_bounds__(256) void bimage_kernel(ImgArgs p) {
   for (int k = 0; k < 4; ++k) {
     const int64_t d = dest[k];
     if (d < 0 || d >= p.Jpad) continue;  // past the padded rows (or a plan entry out of range)
-    uint8_t* dst = p.img + ((size_t)(d / BN) * (size_t)p.nchunks + (size_t)g) * kImgChunkBytes +
+    const size_t gi = (size_t)p.g0 + (size_t)g;
+    uint8_t* dst = p.img + ((size_t)(d / BN) * (size_t)p.nchunks + gi) * kImgChunkBytes +
                    (size_t)(d % BN) * (LDS_STRIDE * 2);
     *reinterpret_cast<half8_t*>(dst + u * 16) = f[k];
-    if (u == 0) p.bsc[(size_t)g * (size_t)p.bsc_ld + (size_t)d] = S[k];
+    if (u == 0) p.bsc[gi * (size_t)p.bsc_ld + (size_t)d] = S[k];
   }
 }
 
@@ -1221,6 +1385,11 @@ ImgKernel pick_img_kernel(const GemmParams& p) {
 
 bool gemm_image_pays(int64_t I) { return (I + BM - 1) / BM >= kImgMinRowTiles; }
 
+bool gemm_image_two_segments(const GemmParams& p) {
+  return p.nseg == 2 && !p.outl && p.seg[0].a.fmt == TJ2_NVFP4 && p.seg[0].b.fmt == TJ2_NVFP4 &&
+         p.seg[1].a.fmt == TJ2_FP8 && p.seg[1].b.fmt == TJ2_FP8 && p.seg[0].K > BK && p.seg[1].K > 0;
+}
+
 size_t gemm_image_bytes(int64_t J, int64_t nchunks) {
   const int64_t tn = (J + BN - 1) / BN;
   const size_t img = (size_t)tn * (size_t)nchunks * (size_t)kImgChunkBytes;
@@ -1306,11 +1475,14 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   // B is decoded once into chunk images when it is read by many row tiles and
   // the caller gave room for them
   ImgKernel ikern = p.bimg && gemm_image_pays(p.I) ? pick_img_kernel(p) : nullptr;
+  if (p.bimg && gemm_image_pays(p.I) && gemm_image_two_segments(p) && split == 1)
+    ikern = (k.seg[0].nchunks & 1) ? gemm_img2_kernel<1> : gemm_img2_kernel<0>;
   if (ikern && p.bimg_bytes >= gemm_image_bytes(p.J, k.nchunks) && (reinterpret_cast<uintptr_t>(p.bimg) & 255) == 0) {
     ImgArgs ia;
     ia.b = k.seg[0].b;
     ia.fmt = p.seg[0].b.fmt;
     ia.nchunks = k.nchunks;
+    ia.g0 = 0;
     ia.b8 = k.b8;
     ia.outl = p.outl;
     ia.rest = p.rest;
@@ -1321,9 +1493,21 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     ia.bsc_ld = ia.Jpad;
     ia.bsc = reinterpret_cast<float*>(ia.img + (size_t)k.tiles_n * (size_t)k.nchunks * kImgChunkBytes);
     if (!p.bimg_ready) {
-      hipLaunchKernelGGL(bimage_kernel, dim3((uint32_t)k.nchunks, (uint32_t)(ia.Jpad / 64)), dim3(256), 0, s, ia);
+      // one decode launch per segment (a second segment's chunks follow the first's)
+      const int n0c = p.nseg == 2 ? k.seg[0].nchunks : k.nchunks;
+      hipLaunchKernelGGL(bimage_kernel, dim3((uint32_t)n0c, (uint32_t)(ia.Jpad / 64)), dim3(256), 0, s, ia);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
+      if (p.nseg == 2) {
+        ImgArgs ib = ia;
+        ib.b = k.seg[1].b;
+        ib.fmt = p.seg[1].b.fmt;
+        ib.g0 = n0c;
+        hipLaunchKernelGGL(bimage_kernel, dim3((uint32_t)k.seg[1].nchunks, (uint32_t)(ia.Jpad / 64)), dim3(256), 0,
+                           s, ib);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
     }
     k.bimg = ia.img;
     k.bsc = ia.bsc;

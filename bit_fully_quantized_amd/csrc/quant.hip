@@ -318,10 +318,10 @@ struct ColTile<TJ2_FP8> {
 // the outer scale S stays a separate float), go to image row img_rows[orow]
 // (or orow), chunk g, elements 16 rs .. 16 rs + 15; lane rs = 0 writes S.
 template <int OF>
-__device__ __forceinline__ void store_image_group(const QuantParams& p, int64_t orow, uint32_t g, int rs,
-                                                  const uint32_t codes[4], uint32_t s_code, float S) {
-  const int64_t d = p.img_rows ? (int64_t)p.img_rows[orow] : orow;
-  uint8_t* dst = p.img + ((size_t)(d >> 7) * (size_t)p.img_nch + g) * kImgChunkBytes + (size_t)(d & 127) * kImgRowBytes +
+__device__ __forceinline__ void write_image_group(uint8_t* img, float* img_sc, int64_t img_ld, int64_t img_nch,
+                                                  int64_t d, uint32_t g, int rs, const uint32_t codes[4],
+                                                  uint32_t s_code, float S) {
+  uint8_t* dst = img + ((size_t)(d >> 7) * (size_t)img_nch + g) * kImgChunkBytes + (size_t)(d & 127) * kImgRowBytes +
                  rs * 32;
   uint32_t h[8];
   if constexpr (OF == TJ2_NVFP4) {
@@ -340,7 +340,14 @@ __device__ __forceinline__ void store_image_group(const QuantParams& p, int64_t 
   }
   *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
   *reinterpret_cast<uint4*>(dst + 16) = make_uint4(h[4], h[5], h[6], h[7]);
-  if (rs == 0) p.img_sc[(size_t)g * (size_t)p.img_ld + (size_t)d] = S;
+  if (rs == 0) img_sc[(size_t)g * (size_t)img_ld + (size_t)d] = S;
+}
+
+template <int OF>
+__device__ __forceinline__ void store_image_group(const QuantParams& p, int64_t orow, uint32_t g, int rs,
+                                                  const uint32_t codes[4], uint32_t s_code, float S) {
+  const int64_t d = p.img_rows ? (int64_t)p.img_rows[orow] : orow;
+  write_image_group<OF>(p.img, p.img_sc, p.img_ld, p.img_nch, d, g, rs, codes, s_code, S);
 }
 
 // One 128-row x 64-column tile (number `bid` of the problem's tiles).
@@ -691,12 +698,18 @@ __global__ __launch_bounds__(256) void quant_split_kernel(SplitParams p, int R) 
       *reinterpret_cast<uint2*>(o.codes + orow * o.ld_codes + jj * 8) = make_uint2(codes[0], codes[1]);
       o.s16[orow * o.ld_s16 + jj] = (uint8_t)s_code;
       if ((jj & 7) == 0) o.s128[orow * o.ld_s128 + (jj >> 3)] = S;
+      if (p.img)
+        write_image_group<TJ2_NVFP4>(p.img, p.img_sc, p.img_ld, p.img_nch, orow, (uint32_t)(jj >> 3), jj & 7, codes,
+                                     s_code, S);
     } else {
       quantize_group<TJ2_FP8, false>(v, a_o, a_j, nullptr, codes, &s_code, &S);
       const QView& o = p.q8;
       *reinterpret_cast<uint4*>(o.codes + orow * o.ld_codes + jj * 16) =
           make_uint4(codes[0], codes[1], codes[2], codes[3]);
       if ((jj & 7) == 0) o.s128[orow * o.ld_s128 + (jj >> 3)] = S;
+      if (p.img)
+        write_image_group<TJ2_FP8>(p.img, p.img_sc, p.img_ld, p.img_nch, orow, (uint32_t)(p.img_g8 + (jj >> 3)),
+                                   jj & 7, codes, s_code, S);
     }
   }
 }

@@ -82,6 +82,13 @@ struct SplitParams {
   const int32_t* rest;
   const int32_t* outl;
   QView q4, q8;
+  // optional: the forward product's B image (the rows' NVFP4 chunks, then
+  // their FP8 chunks from image chunk img_g8 on), written beside the codes
+  uint8_t* img;
+  float* img_sc;
+  int64_t img_ld;  // scale row length: the rows padded to whole 128-row tiles
+  int img_nch;     // chunks of the whole image
+  int img_g8;
 };
 
 hipError_t launch_quant_split(const SplitParams& p, hipStream_t s);
@@ -143,6 +150,9 @@ size_t gemm_image_bytes(int64_t J, int64_t nchunks);
 // Whether a product of I rows decodes its B into an image (given the room):
 // only when enough row tiles would otherwise decode B again.
 bool gemm_image_pays(int64_t I);
+// The forward's two-segment product (NVFP4 x NVFP4, then FP8 x FP8, the first
+// segment longer than one chunk) can run from a B image of both segments.
+bool gemm_image_two_segments(const GemmParams& p);
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 

@@ -272,8 +272,14 @@ tj2_status nvfp4_gemm_outlier_cols(const tj2_qtensor* A, const tj2_qtensor* B, c
  * Xq/X8 are saved for the backward and stay owned by the caller.
  * Y [M, N]: y_dtype TJ2_BF16 or TJ2_F32.  M, K, N multiples of 16.
  * workspace: split-K partial sums of the product (few output tiles, e.g. a
- * small M), nvfp4_linear_fwd_workspace_size(M, N, K, n_outliers) bytes; NULL
- * runs the product unsplit; a smaller non-NULL workspace is TJ2_ERR_ARG.
+ * small M), then, with a plan, room for the product's B image (W-hat's NVFP4
+ * chunks then W8's FP8 chunks, decoded to f16, 2.125 B per weight), which the
+ * split quantization of W_master writes beside Wq and W8 when M >= 2048, K <=
+ * 8192, K - n_outliers > 128 and the product runs unsplit;
+ * nvfp4_linear_fwd_workspace_size(M, N, K, n_outliers) bytes covers both.
+ * NULL runs the product unsplit and without the image; a workspace smaller
+ * than the partial sums is TJ2_ERR_ARG, one without room for the image runs the
+ * product without it (same result, bit for bit).
  */
 tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, const float* W_master,
                             tj2_qtensor* Wq, tj2_qtensor* W8, const tj2_outlier_plan* plan,

@@ -310,9 +310,24 @@ def test_gemm_workspace_holds_the_b_image(L):
     assert L.nvfp4_gemm_workspace_size(I, J, K, 0) == part + img
     # 300 columns: 3 column tiles, scales padded to 384 columns
     assert L.nvfp4_gemm_workspace_size(16384, 300, 1024, 0) == 3 * 8 * 128 * 272 + 8 * 384 * 4
-    # fewer row tiles (7), or a second K segment: no image (7 chunks: no split either)
+    # fewer row tiles (7): no image (7 chunks: no split either)
     assert L.nvfp4_gemm_workspace_size(1792, 300, 896, 0) == 0
+    # a second K segment: no image (the product decodes B itself)
     assert L.nvfp4_gemm_workspace_size(16384, 300, 768, 128) == 0
+
+
+def test_forward_workspace_holds_the_b_image(L):
+    # the forward with an outlier plan takes room for its product's B image, which the weights' split
+    # quantization writes: W's NVFP4 chunks, then W8's FP8 chunks
+    img = lambda J, nch: (J // 128) * nch * 128 * 272 + nch * J * 4  # noqa: E731
+    assert L.nvfp4_linear_fwd_workspace_size(16384, 4096, 1024, 112) == img(4096, 9)
+    assert L.nvfp4_linear_fwd_workspace_size(16384, 1024, 4096, 416) == img(1024, 33)
+    # no plan, fewer than 8 row tiles, rows past the quantizer's 32 KB staging (K > 8192), or a
+    # single NVFP4 chunk: no image
+    assert L.nvfp4_linear_fwd_workspace_size(16384, 4096, 1024, 0) == 0
+    assert L.nvfp4_linear_fwd_workspace_size(1792, 4096, 1024, 112) == 0
+    assert L.nvfp4_linear_fwd_workspace_size(16384, 4096, 9216, 112) == 0
+    assert L.nvfp4_linear_fwd_workspace_size(16384, 4096, 240, 112) == 0
 
 
 def test_qtensor_block_count_limit(L):

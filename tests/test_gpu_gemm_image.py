@@ -1,7 +1,8 @@
 """GPU parity of the image products: B decoded once into f16 chunk images (by a
-decode pass, or written by the column quantization that produces B) and copied
-into the product's LDS stages, used for one-segment products of at least 8 row
-tiles (2048 rows) when the workspace holds the image.
+decode pass, or written by the quantization that produces B: the backward's
+column re-grouping, the forward's split quantization of the weights) and copied
+into the product's LDS stages, used for products of at least 8 row tiles (2048
+rows) when the workspace holds the image.
 
 Each case checks the product against the oracle's fp64 product of the same
 dequantized operands (relative Frobenius < 1e-5: fp32 accumulation of exact
@@ -12,7 +13,7 @@ import pytest
 import torch
 
 import synthetic
-from oracle import gemm as ogemm, quant
+from oracle import gemm as ogemm, linear as olinear, quant
 
 import _helpers as H
 from _linear_check import check_linear_sampled
@@ -78,6 +79,44 @@ def test_image_product_formats(fmt_a, fmt_b):
     torch.cuda.synchronize()
     assert torch.equal(img, direct)
     assert H.rel_fro(img.cpu().numpy(), ogemm.gemm_nt_f64(ra, rb)) < 1e-5
+
+
+# (tokens, outputs, channels, outlier channels): at least 8 row tiles and one K split, so the
+# forward's product runs from the image; NVFP4 chunk counts 2, 3, 5, 8 and 29 (both parities of the
+# segment crossing), one to four FP8 chunks, ragged rows, columns and chunks
+_FWD_IMG = [(2112, 208, 272, 16), (2048, 256, 400, 16), (2304, 384, 768, 144), (4096, 2048, 1024, 112),
+            (4096, 2048, 4096, 416)]
+
+
+@pytest.mark.parametrize("M,N,K,no", _FWD_IMG)
+def test_forward_image_from_the_split_quantization(M, N, K, no):
+    """The forward with an outlier plan: the weights' split quantization writes the product's B image
+    (NVFP4 chunks, then FP8 chunks) and the two-segment image kernel runs the FP8 chunks inside its
+    pipelined loop.  Y equals bit for bit the forward without room for the image (the direct
+    two-segment product: same chunk order, same promotions); the weights' codes and sampled rows of
+    Y match the oracle."""
+    print(f"[image] forward {M}x{N}x{K} outliers={no}", flush=True)
+    rng = np.random.default_rng(M + K)
+    xb = synthetic.normal_bf16((M, K), 1.0, 100 + K)
+    W = synthetic.normal_f32((N, K), 0.02, 101 + K)
+    outl = np.sort(rng.choice(K, no, replace=False))
+    plan = tj2.OutlierPlan.from_indices(K, outl)
+    assert int(tj2.lib().nvfp4_linear_fwd_workspace_size(M, N, K, no)) > 0, "room for the image"
+    X, Wd = H.bf16_to_device(xb), H.f32_to_device(W)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    Y32 = saved = None
+    for dtype in (torch.float32, torch.bfloat16):
+        Y, sv = tj2.linear_fwd(X, Wd, N, plan=plan, y_dtype=dtype)
+        Yd, _ = tj2.linear_fwd(X, Wd, N, plan=plan, y_dtype=dtype, workspace=small)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Yd), dtype
+        if dtype == torch.float32:
+            Y32, saved = Y, sv
+    rows = np.unique(np.concatenate([rng.choice(M, 64, replace=False), [0, M - 1]]))
+    ref = olinear.linear_fwd(H.bf16_values(xb)[rows], W, olinear.Plan.from_outliers(K, outl))
+    H.assert_q_equal(saved["Wq"], ref["Wq"], what="Wq")
+    H.assert_q_equal(saved["W8"], ref["W8"], what="W8")
+    assert H.rel_fro(Y32.cpu().numpy()[rows], ref["Y"]) < 1e-5
 
 
 def _outlier_case(I, J, K, outl, seed):
