@@ -822,6 +822,25 @@ static_assert(kImgChunkBytes % 1024 == 0 && kImgChunkBytes / 1024 == 34, "image 
 struct SmemImg {
   _Float16 b[2][BN * LDS_STRIDE];
 };
+
+// Tile order of the image products: groups of kImgGroupRows row tiles, rows
+// fastest within a group, then the group's next column tile.  A B image is
+// 3.8 times the packed bytes and a product's image is larger than an XCD's 4 MB
+// L2, so with columns fastest the ~32 tiles an XCD runs at once (its range of
+// tile numbers is contiguous) would read the whole image and every row tile
+// would fetch it again; in groups, those tiles share 8 row blocks of A and a
+// few column tiles of the image.  A bijection of [0, tiles_m * tiles_n) for any
+// sizes (the last group may have fewer rows).
+constexpr uint32_t kImgGroupRows = 8;
+__device__ __forceinline__ void img_tile(uint32_t tile, uint32_t tiles_m, uint32_t tiles_n, uint32_t& tm,
+                                         uint32_t& tn) {
+  const uint32_t per_group = kImgGroupRows * tiles_n;
+  const uint32_t g = tile / per_group, w = tile - g * per_group;
+  const uint32_t first = g * kImgGroupRows;
+  const uint32_t rows = min(tiles_m - first, kImgGroupRows);
+  tm = first + w % rows;
+  tn = w / rows;
+}
 union SmemImgAll {
   SmemImg loop;
   float out[BM / 32][32][OUT_STRIDE];
@@ -964,8 +983,9 @@ __global__ __launch_bounds__(512, 1) void gemm_img_kernel(GemmKArgs p) {
   if (id < per_xcd * 8) id = (id % 8) * per_xcd + id / 8;
   const uint32_t tiles = (uint32_t)(p.tiles_m * p.tiles_n);
   const uint32_t tile = id % tiles, z = id / tiles;
-  const uint32_t tj = tile % (uint32_t)p.tiles_n;
-  const int64_t m0 = (int64_t)(tile / p.tiles_n) * BM, n0 = (int64_t)tj * BN;
+  uint32_t ti, tj;
+  img_tile(tile, (uint32_t)p.tiles_m, (uint32_t)p.tiles_n, ti, tj);
+  const int64_t m0 = (int64_t)ti * BM, n0 = (int64_t)tj * BN;
 
   Ctx t;
   t.lane = threadIdx.x & 63;
@@ -1084,9 +1104,9 @@ __global__ __launch_bounds__(512, 1) void gemm_img2_kernel(GemmKArgs p) {
   uint32_t id = blockIdx.x;
   const uint32_t per_xcd = nwg / 8;
   if (id < per_xcd * 8) id = (id % 8) * per_xcd + id / 8;
-  const uint32_t tile = id;
-  const uint32_t tj = tile % (uint32_t)p.tiles_n;
-  const int64_t m0 = (int64_t)(tile / p.tiles_n) * BM, n0 = (int64_t)tj * BN;
+  uint32_t ti, tj;
+  img_tile(id, (uint32_t)p.tiles_m, (uint32_t)p.tiles_n, ti, tj);
+  const int64_t m0 = (int64_t)ti * BM, n0 = (int64_t)tj * BN;
 
   Ctx t;
   t.lane = threadIdx.x & 63;
