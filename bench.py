@@ -776,9 +776,11 @@ def main():
             "gemm_tflop_per_step": round(flops_step / 1e12, 3), "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "the products (gemm_img_kernel: dX and dW of >= 2048 output rows with B from f16 images in LDS; "
-                      "gemm_nt_kernel: fwd with the FP8 segment, the other dW); a call includes its split-K reduction "
-                      "and, here, its B decode pass (in the step the column re-grouping writes the images)",
+            "kernel": "the products, each called on its own (gemm_img_kernel: dX and dW of >= 2048 output rows "
+                      "with B from f16 images in LDS; gemm_nt_kernel: fwd with the FP8 segment, the other dW); a call "
+                      "includes its split-K reduction and its B decode pass (in the step the quantizations that "
+                      "produce B write the images, and the forward runs gemm_img2_kernel from the image the "
+                      "weights' split quantization writes)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",
