@@ -213,6 +213,14 @@ bool fwd_image(int64_t M, int64_t N, int64_t K, int64_t no, bool w_master) {
          gemm_split(M, N, gemm_chunks(K1, no)) == 1;
 }
 
+// Image room of a product called on its own (nvfp4_gemm): one segment, or
+// two (the forward's NVFP4 and FP8 segments) when the product runs unsplit
+// (the two-segment image kernel has no K split).
+size_t gemm_image_room(int64_t I, int64_t J, int64_t K, int64_t K2) {
+  if (K2 > 0 && (K <= 128 || gemm_split(I, J, gemm_chunks(K, K2)) != 1)) return 0;
+  return image_bytes(I, J, K, K2);
+}
+
 // The image part of a product's workspace: after its split-K partials (need
 // bytes, 256-aligned) when the workspace holds img_bytes more (else none).
 GemmImage workspace_image(void* workspace, size_t ws_bytes, size_t need, size_t img_bytes) {
@@ -491,7 +499,7 @@ tj2_status nvfp4_quantize(const void* x, int32_t x_dtype, const tj2_qtensor* x_q
 size_t nvfp4_gemm_workspace_size(int64_t I, int64_t J, int64_t K, int64_t K2) {
   if (I <= 0 || J <= 0 || K <= 0 || K2 < 0) return 0;
   const size_t part = gemm_workspace_bytes(I, J, gemm_chunks(K, K2));
-  const size_t img = K2 == 0 ? image_bytes(I, J, K) : 0;
+  const size_t img = gemm_image_room(I, J, K, K2);
   return img ? align256(part) + img : part;
 }
 
@@ -504,7 +512,7 @@ tj2_status nvfp4_gemm(const tj2_qtensor* A, const tj2_qtensor* B, const tj2_qten
     if (!aligned16(workspace)) return fail(TJ2_ERR_ALIGN, "workspace must be 16-byte aligned");
     const size_t need = gemm_workspace_bytes(A->rows, B->rows, gemm_chunks(A->len, A2 ? A2->len : 0));
     if (ws_bytes < need) return fail(TJ2_ERR_ARG, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
-    img = workspace_image(workspace, ws_bytes, need, A2 ? 0 : image_bytes(A->rows, B->rows, A->len));
+    img = workspace_image(workspace, ws_bytes, need, gemm_image_room(A->rows, B->rows, A->len, A2 ? A2->len : 0));
   }
   return run_gemm(A, B, A2, B2, C, c_dtype, ldc, col_map, accumulate, workspace, workspace ? ws_bytes : 0,
                   (hipStream_t)stream, img) == TJ2_OK ? ok() : TJ2_ERR_HIP;

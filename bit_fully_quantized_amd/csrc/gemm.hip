@@ -1238,8 +1238,9 @@ __global__ __launch_bounds__(512, 1) void gemm_img2_kernel(GemmKArgs p) {
   store_tile<false>(p, smem.out, t, m0, n0, 0, acc, 0, BN, 0, BN);
 }
 
-// B decode into chunk images: a workgroup of 256 threads per (chunk g, 64
-// source rows); thread (unit u = t % 16, rows v = 64 * slab + 16k + t / 16,
+// B decode into chunk images: a workgroup of 256 threads per (image chunk, 64
+// source rows; a two-segment product's image holds the first segment's chunks,
+// then the second's, each chunk decoded from its own segment's B); thread (unit u = t % 16, rows v = 64 * slab + 16k + t / 16,
 // k = 0..3) decodes K elements 8u..8u+7 of the chunk in four rows into 16-byte
 // pieces of the image (the 16 threads of a row write its 256 bytes; u = 15
 // also writes the row's pad, u = 0 its S_B).  Source rows are B's rows in
@@ -1251,7 +1252,9 @@ struct ImgArgs {
   OperandK b;
   int fmt;
   int nchunks;  // chunks of the whole image
-  int g0;       // image chunk of B's chunk 0 (a second segment's B follows the first's)
+  int n0c;      // chunks of the first segment: image chunks from n0c on are the second's (b2, fmt2)
+  OperandK b2;
+  int fmt2;
   OperandK b8;
   const int32_t* outl;
   const int32_t* rest;
@@ -1263,11 +1266,14 @@ struct ImgArgs {
 };
 
 __global__ __launch_bounds__(256) void bimage_kernel(ImgArgs p) {
-  const int g = blockIdx.x;
+  const int gi = blockIdx.x;  // image chunk
+  const bool seg2 = gi >= p.n0c;  // uniform per workgroup
+  const int g = seg2 ? gi - p.n0c : gi;  // chunk of its segment's B
+  const OperandK& bop = seg2 ? p.b2 : p.b;
   const int u = threadIdx.x & 15;
   const bool plan = p.outl != nullptr;
   const int64_t nrest = plan ? p.J - p.n_outl : p.J;
-  const bool b_fp8 = p.fmt == TJ2_FP8;
+  const bool b_fp8 = (seg2 ? p.fmt2 : p.fmt) == TJ2_FP8;
   half8_t f[4];
   float S[4];
   int64_t dest[4];
@@ -1283,19 +1289,19 @@ __global__ __launch_bounds__(256) void bimage_kernel(ImgArgs p) {
     const int64_t r4 = real && !is8 ? v : 0;
     // the row's destination: loaded for every row from a valid address (without
     // a plan, the first word of B's codes, unused)
-    const int32_t* ip = !plan ? reinterpret_cast<const int32_t*>(p.b.codes)
+    const int32_t* ip = !plan ? reinterpret_cast<const int32_t*>(bop.codes)
                         : is8 ? p.outl + r8 : nrest > 0 ? p.rest + min(v, nrest - 1) : p.outl;
     const int32_t at = *ip;
     dest[k] = plan && real ? (int64_t)at : v;
     const bool fp8 = is8 || b_fp8;
-    const size_t rn = (size_t)(is8 ? r8 * p.b8.ld_s128 : r4 * p.b.ld_s128);
-    const uint8_t* c4 = p.b.codes + (size_t)g * 64 + rn * 64 + u * 4;    // NVFP4 codes
-    const uint8_t* c8 = (is8 ? p.b8.codes : p.b.codes) + (size_t)g * 128 + rn * 128 + u * 8;  // FP8 codes
+    const size_t rn = (size_t)(is8 ? r8 * p.b8.ld_s128 : r4 * bop.ld_s128);
+    const uint8_t* c4 = bop.codes + (size_t)g * 64 + rn * 64 + u * 4;    // NVFP4 codes
+    const uint8_t* c8 = (is8 ? p.b8.codes : bop.codes) + (size_t)g * 128 + rn * 128 + u * 8;  // FP8 codes
     const uint8_t* cw = fp8 ? c8 : c4;
     const uint32_t w0 = *reinterpret_cast<const uint32_t*>(cw);
     const uint32_t w1 = *reinterpret_cast<const uint32_t*>(fp8 ? cw + 4 : cw);
-    const uint32_t sb = *(fp8 ? cw : p.b.s16 + (size_t)g * 8 + rn * 8 + (u >> 1));
-    const float s128 = ((is8 ? p.b8.s128 : p.b.s128) + g)[rn];
+    const uint32_t sb = *(fp8 ? cw : bop.s16 + (size_t)g * 8 + rn * 8 + (u >> 1));
+    const float s128 = ((is8 ? p.b8.s128 : bop.s128) + g)[rn];
     const half2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
     const half8_t v8 = Op<TJ2_FP8>::dec8(w0, w1);
     const half8_t v4 = Op<TJ2_NVFP4>::dec8(w0, half2_t{s2[0], s2[0]});
@@ -1306,11 +1312,10 @@ __global__ __launch_bounds__(256) void bimage_kernel(ImgArgs p) {
   for (int k = 0; k < 4; ++k) {
     const int64_t d = dest[k];
     if (d < 0 || d >= p.Jpad) continue;  // past the padded rows (or a plan entry out of range)
-    const size_t gi = (size_t)p.g0 + (size_t)g;
-    uint8_t* dst = p.img + ((size_t)(d / BN) * (size_t)p.nchunks + gi) * kImgChunkBytes +
+    uint8_t* dst = p.img + ((size_t)(d / BN) * (size_t)p.nchunks + (size_t)gi) * kImgChunkBytes +
                    (size_t)(d % BN) * (LDS_STRIDE * 2);
     *reinterpret_cast<half8_t*>(dst + u * 16) = f[k];
-    if (u == 0) p.bsc[gi * (size_t)p.bsc_ld + (size_t)d] = S[k];
+    if (u == 0) p.bsc[(size_t)gi * (size_t)p.bsc_ld + (size_t)d] = S[k];
   }
 }
 
@@ -1502,7 +1507,9 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     ia.b = k.seg[0].b;
     ia.fmt = p.seg[0].b.fmt;
     ia.nchunks = k.nchunks;
-    ia.g0 = 0;
+    ia.n0c = p.nseg == 2 ? k.seg[0].nchunks : k.nchunks;
+    ia.b2 = k.seg[1].b;
+    ia.fmt2 = p.nseg == 2 ? p.seg[1].b.fmt : p.seg[0].b.fmt;
     ia.b8 = k.b8;
     ia.outl = p.outl;
     ia.rest = p.rest;
@@ -1513,21 +1520,10 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     ia.bsc_ld = ia.Jpad;
     ia.bsc = reinterpret_cast<float*>(ia.img + (size_t)k.tiles_n * (size_t)k.nchunks * kImgChunkBytes);
     if (!p.bimg_ready) {
-      // one decode launch per segment (a second segment's chunks follow the first's)
-      const int n0c = p.nseg == 2 ? k.seg[0].nchunks : k.nchunks;
-      hipLaunchKernelGGL(bimage_kernel, dim3((uint32_t)n0c, (uint32_t)(ia.Jpad / 64)), dim3(256), 0, s, ia);
+      // one decode launch for both segments (a second segment's chunks follow the first's)
+      hipLaunchKernelGGL(bimage_kernel, dim3((uint32_t)k.nchunks, (uint32_t)(ia.Jpad / 64)), dim3(256), 0, s, ia);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      if (p.nseg == 2) {
-        ImgArgs ib = ia;
-        ib.b = k.seg[1].b;
-        ib.fmt = p.seg[1].b.fmt;
-        ib.g0 = n0c;
-        hipLaunchKernelGGL(bimage_kernel, dim3((uint32_t)k.seg[1].nchunks, (uint32_t)(ia.Jpad / 64)), dim3(256), 0,
-                           s, ib);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
     }
     k.bimg = ia.img;
     k.bsc = ia.bsc;

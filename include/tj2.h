@@ -205,10 +205,12 @@ tj2_status nvfp4_quantize_dual(const void* x, int64_t rows, int64_t cols, int32_
  * elements.  col_map (optional, device int32[J]) gives the output column of B
  * row j.  accumulate != 0 adds into C (TJ2_F32 only).
  * workspace: fp32 partial sums of a K split (the library splits K only when
- * the output has too few 256x128 tiles to fill the GPU), then, for a
- * one-segment product of at least 2048 rows, room for B decoded once into an
- * f16 image that the product copies into LDS instead of decoding B again in
- * every row tile: nvfp4_gemm_workspace_size(I, J, A->len, A2 ? A2->len : 0)
+ * the output has too few 256x128 tiles to fill the GPU), then, for a product
+ * of at least 2048 rows (one segment, or an NVFP4 segment of more than 128
+ * followed by an FP8 one when the product runs without a split), room for B
+ * decoded once into an f16 image that the product copies into LDS instead of
+ * decoding B again in every row tile (a second segment's chunks follow the
+ * first's): nvfp4_gemm_workspace_size(I, J, A->len, A2 ? A2->len : 0)
  * bytes for both (0 when neither applies).  NULL runs the product without a
  * split or an image; a non-NULL workspace smaller than the partial sums need is
  * an error (TJ2_ERR_ARG); one that holds the partial sums but not the image

@@ -312,8 +312,12 @@ def test_gemm_workspace_holds_the_b_image(L):
     assert L.nvfp4_gemm_workspace_size(16384, 300, 1024, 0) == 3 * 8 * 128 * 272 + 8 * 384 * 4
     # fewer row tiles (7): no image (7 chunks: no split either)
     assert L.nvfp4_gemm_workspace_size(1792, 300, 896, 0) == 0
-    # a second K segment: no image (the product decodes B itself)
-    assert L.nvfp4_gemm_workspace_size(16384, 300, 768, 128) == 0
+    # a second K segment (the forward's FP8 outlier channels): its chunks follow the first's, when the
+    # product runs unsplit (here fewer than 8 chunks); a split product, or one NVFP4 chunk: none
+    assert L.nvfp4_gemm_workspace_size(16384, 300, 768, 128) == 3 * 7 * 128 * 272 + 7 * 384 * 4
+    split_only = L.nvfp4_gemm_workspace_size(2048, 256, 3680, 416)  # 16 tiles over 33 chunks: a K split
+    assert split_only > 0 and split_only % (2048 * 256 * 4) == 0  # whole fp32 partial sums, no image
+    assert L.nvfp4_gemm_workspace_size(16384, 300, 128, 128) == 0
 
 
 def test_forward_workspace_holds_the_b_image(L):

@@ -81,6 +81,49 @@ def test_image_product_formats(fmt_a, fmt_b):
     assert H.rel_fro(img.cpu().numpy(), ogemm.gemm_nt_f64(ra, rb)) < 1e-5
 
 
+def _two_segment_ops(I, J, K1, K2, seed):
+    a_bits = synthetic.normal_bf16((I, K1 + K2), 1.0, seed)
+    b = synthetic.normal_f32((J, K1 + K2), 0.02, seed + 1)
+    a_f = H.bf16_values(a_bits)
+    ga = tj2.quantize(H.bf16_to_device(np.ascontiguousarray(a_bits[:, :K1])))
+    ga8 = tj2.quantize(H.bf16_to_device(np.ascontiguousarray(a_bits[:, K1:])), out_fmt=tj2.FP8)
+    gb = tj2.quantize(H.f32_to_device(np.ascontiguousarray(b[:, :K1])))
+    gb8 = tj2.quantize(H.f32_to_device(np.ascontiguousarray(b[:, K1:])), out_fmt=tj2.FP8)
+    ra = quant.quantize(np.ascontiguousarray(a_f[:, :K1]))
+    ra8 = quant.quantize(np.ascontiguousarray(a_f[:, K1:]), fmt="fp8")
+    rb = quant.quantize(np.ascontiguousarray(b[:, :K1]))
+    rb8 = quant.quantize(np.ascontiguousarray(b[:, K1:]), fmt="fp8")
+    H.assert_q_equal(gb, rb, what="B")
+    H.assert_q_equal(gb8, rb8, what="B8")
+    ref = ogemm.gemm_nt_f64(ra, rb) + ogemm.gemm_nt_f64(ra8, rb8)
+    return ga, gb, ga8, gb8, ref
+
+
+# (rows, columns, NVFP4 length, FP8 length): fewer than 8 chunks or at least 256 output tiles, so
+# one K split; NVFP4 chunk counts 2, 3, 5, 8 and 29 (both parities of the segment crossing), one to
+# four FP8 chunks, ragged rows, columns and chunks
+_TWO_SEG = [(2100, 200, 256, 16), (2304, 384, 384, 256), (2048, 256, 640, 112), (4096, 2048, 912, 112),
+            (4096, 2048, 3680, 416)]
+
+
+@pytest.mark.parametrize("I,J,K1,K2", _TWO_SEG)
+def test_image_two_segment_product(I, J, K1, K2):
+    """A two-segment product (NVFP4, then FP8) called on its own: both segments' B rows decoded into
+    one image by one decode launch, the FP8 chunks inside the image kernel's pipelined loop.  Equal
+    bit for bit to the direct two-segment product, and to the oracle."""
+    print(f"[image] two segments {I}x{J}x({K1}+{K2})", flush=True)
+    ga, gb, ga8, gb8, ref = _two_segment_ops(I, J, K1, K2, seed=90 + K1 + K2)
+    ws = tj2.gemm_workspace(I, J, K1, K2)
+    assert ws is not None and ws.numel() > 0, "room for the image"
+    for dtype in (torch.float32, torch.bfloat16):
+        img = tj2.gemm(ga, gb, ga8, gb8, out_dtype=dtype, workspace=ws)
+        direct = tj2.gemm(ga, gb, ga8, gb8, out_dtype=dtype, split_k=False)
+        torch.cuda.synchronize()
+        assert torch.equal(img, direct), dtype
+    c = tj2.gemm(ga, gb, ga8, gb8, workspace=ws).cpu().numpy()
+    assert H.rel_fro(c, ref) < 1e-5
+
+
 # (tokens, outputs, channels, outlier channels): at least 8 row tiles and one K split, so the
 # forward's product runs from the image; NVFP4 chunk counts 2, 3, 5, 8 and 29 (both parities of the
 # segment crossing), one to four FP8 chunks, ragged rows, columns and chunks
