@@ -160,14 +160,9 @@ tj2_status run_quant(const void* x, int x_dtype, const tj2_qtensor* x_q, int64_t
 // split quantization also writes the rows' decoded f16 values into it: NVFP4
 // chunks first, then the FP8 chunks (the caller checks that the split kernel
 // runs: rows within 32 KB).
-tj2_status run_split(const void* x, int x_dtype, int64_t rows, int64_t K, const tj2_outlier_plan* plan,
-                     const tj2_qtensor* q4, const tj2_qtensor* q8, hipStream_t s, uint8_t* img = nullptr) {
+SplitParams split_params(const void* x, int x_dtype, int64_t rows, int64_t K, const tj2_outlier_plan* plan,
+                         const tj2_qtensor* q4, const tj2_qtensor* q8, uint8_t* img) {
   const int64_t no = plan->n_outliers, K1 = K - no;
-  if (K * (x_dtype == TJ2_BF16 ? 2 : 4) > 32768) {
-    if (img) return fail(TJ2_ERR_ARG, "the B image needs rows within 32 KB");
-    TJ2_TRY(run_quant(x, x_dtype, nullptr, rows, K, plan->rest, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, q4, s));
-    return run_quant(x, x_dtype, nullptr, rows, K, plan->outliers, no, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, q8, s);
-  }
   SplitParams p;
   memset(&p, 0, sizeof(p));
   p.in_dtype = x_dtype;
@@ -186,7 +181,19 @@ tj2_status run_split(const void* x, int x_dtype, int64_t rows, int64_t K, const 
     p.img_ld = tiles * 128;
     p.img_sc = reinterpret_cast<float*>(img + (size_t)tiles * (size_t)nch * kImgChunkBytes);
   }
-  return hip_check(launch_quant_split(p, s), "split quantize launch");
+  return p;
+}
+
+tj2_status run_split(const void* x, int x_dtype, int64_t rows, int64_t K, const tj2_outlier_plan* plan,
+                     const tj2_qtensor* q4, const tj2_qtensor* q8, hipStream_t s, uint8_t* img = nullptr) {
+  const int64_t no = plan->n_outliers, K1 = K - no;
+  if (K * (x_dtype == TJ2_BF16 ? 2 : 4) > 32768) {
+    if (img) return fail(TJ2_ERR_ARG, "the B image needs rows within 32 KB");
+    TJ2_TRY(run_quant(x, x_dtype, nullptr, rows, K, plan->rest, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, q4, s));
+    return run_quant(x, x_dtype, nullptr, rows, K, plan->outliers, no, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, q8, s);
+  }
+  return hip_check(launch_quant_split(split_params(x, x_dtype, rows, K, plan, q4, q8, img), s),
+                   "split quantize launch");
 }
 
 // B image of a product (scratch for its f16 decode; ready = already written by
@@ -596,8 +603,16 @@ tj2_status nvfp4_linear_fwd(const void* X, int64_t M, int64_t K, int64_t N, cons
       img = workspace_image(workspace, ws_bytes, need, image_bytes(M, N, K1, no));
   }
   if (plan) {
-    TJ2_TRY(run_split(X, TJ2_BF16, M, K, plan, Xq, X8, s));
-    if (W_master) TJ2_TRY(run_split(W_master, TJ2_F32, N, K, plan, Wq, W8, s, static_cast<uint8_t*>(img.ptr)));
+    uint8_t* wimg = static_cast<uint8_t*>(img.ptr);
+    if (W_master && K * 4 <= 32768) {
+      // X and the masters split in one launch (the masters also write the product's image)
+      TJ2_TRY(hip_check(launch_quant_split2(split_params(X, TJ2_BF16, M, K, plan, Xq, X8, nullptr),
+                                            split_params(W_master, TJ2_F32, N, K, plan, Wq, W8, wimg), s),
+                        "split quantize launch"));
+    } else {
+      TJ2_TRY(run_split(X, TJ2_BF16, M, K, plan, Xq, X8, s));
+      if (W_master) TJ2_TRY(run_split(W_master, TJ2_F32, N, K, plan, Wq, W8, s, wimg));
+    }
     img.ready = img.ptr ? 1 : 0;  // written by the split quantization above
   } else {
     TJ2_TRY(run_quant(X, TJ2_BF16, nullptr, M, K, nullptr, K1, TJ2_GROUP_ROW, TJ2_RTN, 0, 0, 0, 0, Xq, s));

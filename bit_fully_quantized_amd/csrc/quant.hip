@@ -631,11 +631,13 @@ hipError_t launch_quant_dual(const DualParams& p, hipStream_t s) {
 // per row) and gathers their columns from LDS.  Groups of one outer block are 8
 // consecutive lanes, as in the row kernel, so their amax is a DPP reduction.
 // ----------------------------------------------------------------------------
+extern __shared__ uint32_t rows_lds[];
+
+// Workgroup blk of a split quantization (rows R * blk ..).
 template <int IN>
-__global__ __launch_bounds__(256) void quant_split_kernel(SplitParams p, int R) {
-  extern __shared__ uint32_t rows_lds[];
+__device__ __forceinline__ void split_body(const SplitParams& p, int R, uint32_t blk) {
   using T = typename Dense<IN>::T;
-  const int64_t r_base = (int64_t)blockIdx.x * R;
+  const int64_t r_base = (int64_t)blk * R;
   const int nrows = (int)min((int64_t)R, p.rows - r_base);
   const int units = (int)(p.cols * (int64_t)sizeof(T) / 16);  // 16-byte units per row
   {
@@ -714,6 +716,21 @@ __global__ __launch_bounds__(256) void quant_split_kernel(SplitParams p, int R) 
   }
 }
 
+template <int IN>
+__global__ __launch_bounds__(256) void quant_split_kernel(SplitParams p, int R) {
+  split_body<IN>(p, R, blockIdx.x);
+}
+
+// The forward's two split quantizations in one launch: workgroups [0, bx)
+// take X (bf16), the others the fp32 masters W, so the smaller launch's ramp
+// and tail overlap the larger one's.
+__global__ __launch_bounds__(256) void quant_split2_kernel(SplitParams px, int rx, uint32_t bx, SplitParams pw,
+                                                           int rw) {
+  if (blockIdx.x < bx) split_body<TJ2_BF16>(px, rx, blockIdx.x);
+  else split_body<TJ2_F32>(pw, rw, blockIdx.x - bx);
+}
+
+
 // Rows per workgroup: the groups of R rows fill whole 256-lane passes as well
 // as possible, within 32 KB of LDS (several workgroups per CU).
 int split_rows_per_wg(int64_t cols, int esize, int64_t groups_per_row) {
@@ -726,6 +743,17 @@ int split_rows_per_wg(int64_t cols, int esize, int64_t groups_per_row) {
     if (eff > best_eff + 1e-9) { best_eff = eff; best = (int)r; }
   }
   return best;
+}
+
+hipError_t launch_quant_split2(const SplitParams& px, const SplitParams& pw, hipStream_t s) {
+  if (px.in_dtype != TJ2_BF16 || pw.in_dtype != TJ2_F32 || px.cols * 2 > 32768 || pw.cols * 4 > 32768)
+    return hipErrorInvalidValue;  // the kernel stages at most 32 KB per workgroup
+  const int rx = split_rows_per_wg(px.cols, 2, (px.q4.nb + px.q8.nb) * 8);
+  const int rw = split_rows_per_wg(pw.cols, 4, (pw.q4.nb + pw.q8.nb) * 8);
+  const uint32_t bx = (uint32_t)((px.rows + rx - 1) / rx), bw = (uint32_t)((pw.rows + rw - 1) / rw);
+  const size_t lds = std::max((size_t)rx * px.cols * 2, (size_t)rw * pw.cols * 4);
+  hipLaunchKernelGGL(quant_split2_kernel, dim3(bx + bw), dim3(256), lds, s, px, rx, bx, pw, rw);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_split(const SplitParams& p, hipStream_t s) {

@@ -92,6 +92,8 @@ struct SplitParams {
 };
 
 hipError_t launch_quant_split(const SplitParams& p, hipStream_t s);
+// X (bf16) and the fp32 masters W of one forward, both split, in one launch.
+hipError_t launch_quant_split2(const SplitParams& px, const SplitParams& pw, hipStream_t s);
 
 // Both backward groupings of a bf16 [rows, cols] gradient from one read, with
 // stochastic rounding: row_out [rows, cols] grouped along cols (signs row_mask,
