@@ -239,7 +239,12 @@ def quantizers_in_step(tj2, lins, layers, M, ws, reps=10):
         t_fwd = time_launches(lambda: tj2.linear_fwd(li.X, None, N, Wq=li.Wq, W8=li.W8, plan=li.plan, Y=li.Y,
                                                      Xq=li.Xq, X8=li.X8), reps)
         calls = product_calls(tj2, li, ops, M_, ws)
-        t_prod_fwd = time_launches(calls[0][3], reps)
+        # the forward product as linear_fwd runs it with the weight codes given (no masters to write an
+        # image from, so the direct kernel, without a workspace)
+        if li.plan is not None:
+            t_prod_fwd = time_launches(lambda: tj2.gemm(li.Xq, li.Wq, li.X8, li.W8, out=li.Y, split_k=False), reps)
+        else:
+            t_prod_fwd = time_launches(lambda: tj2.gemm(li.Xq, li.Wq, out=li.Y, split_k=False), reps)
         t_bwd = time_launches(lambda: tj2.linear_bwd(li.dY, saved, K, seed=SEED, offset=0, plan=li.plan, dX=li.dX,
                                                      dW=li.dW, operands=ops, workspace=ws), reps)
         t_prod_bwd = time_launches(calls[1][3], reps) + time_launches(calls[2][3], reps)
