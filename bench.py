@@ -622,7 +622,45 @@ def cpu_baseline(M=8192, K=1024, N=3072, p=0.10):
             "sample": f"one QKV-shaped linear (K={K}, N={N}) with M={M} tokens and {plan.outliers.size} FP8 "
                       f"outlier channels: forward + backward incl. every quantizer, fp64 products; "
                       f"{dt:.2f} s for {flops / 1e9:.2f} GFLOP",
-            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
+            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0)),
+            "components": cpu_components()}
+
+
+def cpu_components(rows=512):
+    """The oracle's quantizers (numpy element-wise, one thread) on a bounded sample of the quantizer
+    sweep tensor, its OsciReset accumulate step on 1024x1024 masters, and the single-linear workload end
+    to end (forward, backward, one window-end OsciReset)."""
+    import numpy as np
+    import synthetic
+    from oracle import linear as olinear, osci as oosci, quant as oquant
+    out = {}
+    C = synthetic.QUANT_SWEEP_SHAPE[1]
+    x = synthetic.bf16_bits_to_f32(synthetic.acts_with_outliers_bf16((rows, C), 1.0, 0.01, 64.0, 21))
+    for name, kw in (("row_rtn", {}), ("row_sr_rht", {"rounding": "sr", "rht_mask": 0x5A5A, "seed": 0, "offset": 0})):
+        t0 = time.perf_counter()
+        oquant.quantize(x, grouping="row", fmt="nvfp4", **kw)
+        dt = time.perf_counter() - t0
+        out[f"quantizer_{name}"] = {"elements_per_s": round(rows * C / dt), "GB_s": round(rows * C * 2.59375 / dt / 1e9, 4),
+                                    "sample": f"{rows}x{C} bf16 rows of the sweep recipe", "seconds": round(dt, 2)}
+    W = synthetic.normal_f32((1024, 1024), 0.02, 22)
+    st, _ = oosci.osci_init(W)
+    W1 = W - np.float32(1e-4) * synthetic.normal_f32((1024, 1024), 1.0, 23)
+    t0 = time.perf_counter()
+    oosci.osci_step(W1, st, 4.0, False, False)
+    dt = time.perf_counter() - t0
+    out["osci_reset_accum"] = {"params_per_s": round(W.size / dt), "GB_s": round(W.size * 36.0 / dt / 1e9, 4),
+                               "sample": "1024x1024 fp32 masters", "seconds": round(dt, 2)}
+    X = synthetic.bf16_bits_to_f32(synthetic.normal_bf16((256, 512), 1.0, 24))
+    Wm = synthetic.normal_f32((512, 512), 0.02, 25)
+    dY = synthetic.bf16_bits_to_f32(synthetic.normal_bf16((256, 512), 0.01, 26))
+    t0 = time.perf_counter()
+    fwd = olinear.linear_fwd(X, Wm)
+    bwd = olinear.linear_bwd(dY, fwd, seed=0, offset=0)
+    st0, _ = oosci.osci_init(Wm)
+    oosci.osci_step(Wm - np.float32(1e-4) * bwd["dW"], st0, 4.0, True, True)
+    out["single_linear_end_to_end_s"] = round(time.perf_counter() - t0, 3)
+    out["threads"] = "quantizers and OsciReset: numpy element-wise (one thread); products: BLAS (cores above)"
+    return out
 
 
 def main():
