@@ -626,10 +626,10 @@ def cpu_baseline(M=8192, K=1024, N=3072, p=0.10):
             "components": cpu_components()}
 
 
-def cpu_components(rows=512):
-    """The oracle's quantizers (numpy element-wise, one thread) on a bounded sample of the quantizer
-    sweep tensor, its OsciReset accumulate step on 1024x1024 masters, and the single-linear workload end
-    to end (forward, backward, one window-end OsciReset)."""
+def cpu_components(rows=8192):
+    """The oracle's quantizers (numpy element-wise, one thread) on the quantizer sweep tensor (8192
+    rows: in full), its OsciReset accumulate step on 1024x1024 masters, and the single-linear workload
+    end to end (forward, backward, one window-end OsciReset)."""
     import numpy as np
     import synthetic
     from oracle import linear as olinear, osci as oosci, quant as oquant
@@ -641,7 +641,7 @@ def cpu_components(rows=512):
         oquant.quantize(x, grouping="row", fmt="nvfp4", **kw)
         dt = time.perf_counter() - t0
         out[f"quantizer_{name}"] = {"elements_per_s": round(rows * C / dt), "GB_s": round(rows * C * 2.59375 / dt / 1e9, 4),
-                                    "sample": f"{rows}x{C} bf16 rows of the sweep recipe", "seconds": round(dt, 2)}
+                                    "sample": f"{rows}x{C} bf16 (the sweep recipe)", "seconds": round(dt, 2)}
     W = synthetic.normal_f32((1024, 1024), 0.02, 22)
     st, _ = oosci.osci_init(W)
     W1 = W - np.float32(1e-4) * synthetic.normal_f32((1024, 1024), 1.0, 23)
