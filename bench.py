@@ -229,7 +229,7 @@ def quantizers_in_step(tj2, lins, layers, M, ws, reps=10):
     import torch
     per = 0.5 + 1 / 16 + 4 / 128  # NVFP4 bytes per element
     p8 = 1 + 4 / 128              # FP8
-    fwd_t = fwd_b = bwd_t = bwd_b = 0.0
+    fwd_t = fwd_b = bwd_t = bwd_b = dual_t = dual_b = 0.0
     for li in lins[:5]:
         M_, K, N = M, li.K, li.N
         no = li.plan.n if li.plan is not None else 0
@@ -248,6 +248,10 @@ def quantizers_in_step(tj2, lins, layers, M, ws, reps=10):
         t_bwd = time_launches(lambda: tj2.linear_bwd(li.dY, saved, K, seed=SEED, offset=0, plan=li.plan, dX=li.dX,
                                                      dW=li.dW, operands=ops, workspace=ws), reps)
         t_prod_bwd = time_launches(calls[1][3], reps) + time_launches(calls[2][3], reps)
+        # the fused dY pass alone (both groupings from one read), into the step's operand buffers
+        dual_t += layers * time_launches(lambda: tj2.quantize_dual(li.dY, seed=SEED, row_offset=0, col_offset=2,
+                                                                   row_out=ops["dYq"], col_out=ops["dYt"]), reps)
+        dual_b += layers * (2.0 * M_ * N + 2 * M_ * N * per)
         fwd_t += layers * max(t_fwd - t_prod_fwd, 0.0)
         fwd_b += layers * (2.0 * M_ * K + M_ * K1 * per + M_ * no * p8)
         bwd_t += layers * max(t_bwd - t_prod_bwd, 0.0)
@@ -258,7 +262,8 @@ def quantizers_in_step(tj2, lins, layers, M, ws, reps=10):
         del ops
     torch.cuda.empty_cache()
     out = {}
-    for name, t, b in (("forward_X", fwd_t, fwd_b), ("backward_all", bwd_t, bwd_b)):
+    for name, t, b in (("forward_X", fwd_t, fwd_b), ("backward_all", bwd_t, bwd_b), ("backward_dY_dual", dual_t, dual_b),
+                       ("backward_regroupings", max(bwd_t - dual_t, 0.0), bwd_b - dual_b)):
         gbs = b / t / 1e9 if t > 0 else 0.0
         out[name] = {"ms_per_step": round(t * 1e3, 3), "GB_per_step": round(b / 1e9, 2), "GB_s": round(gbs, 1),
                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 3)}
@@ -796,6 +801,10 @@ def main():
     log("library bf16 product reference")
     lib_ref, lib_all = library_gemm_reference(M, [(f"{spec.name}.fwd", spec.K, spec.N) for spec in wl.linears])
     sweep, sweep_bytes = ({}, 0) if args.no_sweep else quant_sweep(tj2)
+    copy_ref = sweep.get("copy_reference", {}).get("GB_s")
+    for v in q_in_step.values():  # fraction of the copy reference measured on the sweep buffers
+        if isinstance(v, dict) and "GB_s" in v:
+            v["frac_of_copy"] = round(v["GB_s"] / copy_ref, 3) if copy_ref else None
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     out = {
@@ -844,7 +853,11 @@ def main():
                                        "products_frac_of_it": round(achieved / lib_all, 3)},
         },
         "quantizers_in_step": {"what": "370M-style step, quantizer time from the step's own calls (linear call "
-                                       "minus its products), algorithmic bytes", **q_in_step},
+                                       "minus its products; the fused dY pass timed alone, the re-groupings the "
+                                       "rest of the backward), algorithmic bytes (packed operands; the B images the "
+                                       "re-groupings and the forward's split also write, 2.125 B per element, are "
+                                       "the products' scratch and not counted); frac_of_copy against the copy "
+                                       "reference of the quantizer sweep", **q_in_step},
         "fp6x4_backward": {"what": "backward of the 370M-style linears with FP4 vs FP6 (E2M3, NVFP6) gradient "
                                    "operands, the FP6 x FP4 variant", **fp6},
         "single_linear": single,
