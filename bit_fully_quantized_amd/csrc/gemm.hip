@@ -1356,6 +1356,42 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// The common case of the reduction with the split count known at compile time:
+// no column map, J and ldc multiples of 4, the output 16-byte aligned.  Every
+// partial of the thread's 4 consecutive outputs is requested before the sums
+// (taken in split order, as above), and the 4 results leave in one store.
+template <int S>
+__global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __restrict__ partial, int64_t I, int64_t J,
+                                                             void* C, int64_t ldc, int c_bf16, int accumulate) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t jq = J / 4;
+  const int64_t i = q / jq;
+  if (i >= I) return;
+  const int64_t j0 = (q - i * jq) * 4;
+  const int64_t stride = I * J;
+  const float* p = partial + i * J + j0;
+  float4 v[S];
+#pragma unroll
+  for (int z = 0; z < S; ++z) v[z] = *reinterpret_cast<const float4*>(p + z * stride);
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+  for (int z = 0; z < S; ++z) {
+    s0 += v[z].x; s1 += v[z].y; s2 += v[z].z; s3 += v[z].w;
+  }
+  if (c_bf16) {
+    const uint32_t lo = f32_to_bf16(s0) | (f32_to_bf16(s1) << 16), hi = f32_to_bf16(s2) | (f32_to_bf16(s3) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + i * ldc + j0) = make_uint2(lo, hi);
+  } else {
+    float4* cp = reinterpret_cast<float4*>(reinterpret_cast<float*>(C) + i * ldc + j0);
+    if (accumulate) {
+      const float4 c = *cp;
+      *cp = make_float4(c.x + s0, c.y + s1, c.z + s2, c.w + s3);
+    } else {
+      *cp = make_float4(s0, s1, s2, s3);
+    }
+  }
+}
+
 OperandK operand_of(const QView& v) {
   OperandK o;
   o.codes = v.codes;
@@ -1537,8 +1573,19 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split == 1) return e;
   const int64_t threads = p.I * ((p.J + 3) / 4);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, s, p.partial, split,
-                     p.I, p.J, p.C, p.ldc, p.col_map, p.c_dtype == TJ2_BF16 ? 1 : 0, p.accumulate);
+  const dim3 rgrid((uint32_t)((threads + 255) / 256));
+  const int bf = p.c_dtype == TJ2_BF16 ? 1 : 0;
+  const bool vec = !p.col_map && (p.J & 3) == 0 && (p.ldc & 3) == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.C) & (bf ? 7 : 15)) == 0;
+  if (vec && split == 2)
+    hipLaunchKernelGGL(splitk_reduce4_kernel<2>, rgrid, dim3(256), 0, s, p.partial, p.I, p.J, p.C, p.ldc, bf,
+                       p.accumulate);
+  else if (vec && split == 8)
+    hipLaunchKernelGGL(splitk_reduce4_kernel<8>, rgrid, dim3(256), 0, s, p.partial, p.I, p.J, p.C, p.ldc, bf,
+                       p.accumulate);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel, rgrid, dim3(256), 0, s, p.partial, split, p.I, p.J, p.C, p.ldc,
+                       p.col_map, bf, p.accumulate);
   return hipGetLastError();
 }
 

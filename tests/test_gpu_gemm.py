@@ -278,3 +278,36 @@ def test_gemm_many_tiles_two_segments_and_outlier_cols():
     plan = tj2.OutlierPlan.from_indices(J, outl)
     cb2 = tj2.gemm_outlier_cols(ga, gb4, gb8, plan, out_dtype=torch.bfloat16)
     assert H.bf16_ulp_ok(cb2, ref2)
+
+
+@pytest.mark.parametrize("I,J,K", [(1024, 1024, 16384), (3072, 1024, 16384)])
+def test_split_k_reduction_paths(I, J, K):
+    """The weight-gradient shapes whose K split is 8 (1024 x 1024) and 2 (3072 x 1024) over 16384
+    tokens: the reduction's vector path (no column map) equals bit for bit its general path (the
+    same product with an identity column map; both sum the partials in split order), for fp32, bf16
+    and accumulating outputs; sampled rows match the oracle."""
+    print(f"[gemm] split-K reduction {I}x{J}x{K}", flush=True)
+    rng = np.random.default_rng(I + J)
+    a_bits = synthetic.normal_bf16((I, K), 0.01, I)
+    b = synthetic.normal_f32((J, K), 1.0, J + 1)
+    ga = tj2.quantize(H.bf16_to_device(a_bits))
+    gb = tj2.quantize(H.f32_to_device(b))
+    ident = torch.arange(J, dtype=torch.int32, device="cuda")
+    for dtype in (torch.float32, torch.bfloat16):
+        vec = tj2.gemm(ga, gb, out_dtype=dtype)
+        gen = tj2.gemm(ga, gb, out_dtype=dtype, col_map=ident)
+        torch.cuda.synchronize()
+        assert torch.equal(vec, gen), dtype
+    base = torch.from_numpy(rng.standard_normal((I, J)).astype(np.float32)).cuda()
+    acc_vec, acc_gen = base.clone(), base.clone()
+    tj2.gemm(ga, gb, out=acc_vec, accumulate=True)
+    tj2.gemm(ga, gb, out=acc_gen, col_map=ident, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(acc_vec, acc_gen)
+    rows = np.unique(np.concatenate([rng.choice(I, 24, replace=False), [0, I - 1]]))
+    ra = quant.quantize(np.ascontiguousarray(H.bf16_values(a_bits)[rows]))
+    rb = quant.quantize(b)
+    ref = ogemm.gemm_nt_f64(ra, rb)
+    got = tj2.gemm(ga, gb).cpu().numpy()[rows]
+    assert H.rel_fro(got, ref) < 1e-5
+    assert H.rel_fro((acc_vec - base).cpu().numpy()[rows], ref) < 1e-5
