@@ -17,12 +17,15 @@ pytestmark = pytest.mark.gpu
 tj2 = pytest.importorskip("bit_fully_quantized_amd")
 
 
-@pytest.mark.parametrize("R,C,rounding,rht", [(100, 400, "rtn", False), (33, 2048, "sr", False), (64, 256, "sr", True),
-                                              (16, 16, "sr", True), (130, 144, "rtn", False)])
-@pytest.mark.parametrize("grouping", ["row", "col"])
-def test_nvfp6_quantize(R, C, rounding, rht, grouping):
-    if grouping == "col" and R % 16:
-        pytest.skip("column grouping needs rows in multiples of 16")
+# row grouping at ragged row counts; column grouping (rows grouped by 16) at rows in multiples of 16
+_NVFP6_CASES = [("row", 100, 400, "rtn", False), ("row", 33, 2048, "sr", False), ("row", 64, 256, "sr", True),
+                ("row", 16, 16, "sr", True), ("row", 130, 144, "rtn", False),
+                ("col", 112, 400, "rtn", False), ("col", 48, 2048, "sr", False), ("col", 64, 256, "sr", True),
+                ("col", 16, 16, "sr", True), ("col", 144, 144, "rtn", False)]
+
+
+@pytest.mark.parametrize("grouping,R,C,rounding,rht", _NVFP6_CASES)
+def test_nvfp6_quantize(grouping, R, C, rounding, rht):
     bits = synthetic.normal_bf16((R, C), 1.0, R + C)
     x = H.bf16_values(bits)
     x[::5, ::7] *= 50.0  # heavy rows / columns
