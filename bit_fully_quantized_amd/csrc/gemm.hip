@@ -541,6 +541,16 @@ __device__ __forceinline__ int lower_bound(const int32_t* a, int n, int v) {
   return lo;
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to the nearest even bf16 (v_cvt_pk_bf16_f32; the
+// kernels' float mode keeps denormals), a in the low half.  Equal to
+// f32_to_bf16 on finite values.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // Output of one 256x128 tile from the accumulators (MIXB: the outlier-column
 // mapping of the staged rows: lo, c1, r0, ncols as set up by the kernel).
 template <bool MIXB>
@@ -592,31 +602,42 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, float (*out)[32][
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's writes are visible to its lanes
       __builtin_amdgcn_wave_barrier();
       const int64_t row0 = m0 + t.w * 32;
+      // rows of the wave's 32 inside the output (fewer in a last, partial row tile)
+      const int rows_here = (int)min(p.I - row0, (int64_t)32);
+      // Each lane forms its 64-bit output address once and steps it by a uniform
+      // row stride per pass (a 64-bit row x stride product per pass costs three
+      // quarter-rate multiplies), and bf16 pairs come from the hardware
+      // conversion (one instruction per two values).
       if (bf) {
         // lane: 8 columns of one of four rows per pass
+        const int rl = lane >> 4, c0 = (lane & 15) * 8;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.C) + (row0 + rl) * ld + n0 + c0;
+        const int64_t step = 4 * ld;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int row = 4 * r + (lane >> 4), c0 = (lane & 15) * 8;
+        for (int r = 0; r < 8; ++r, dst += step) {
+          const int row = 4 * r + rl;
           const float4 u = *reinterpret_cast<const float4*>(&st[row][c0]);
           const float4 v = *reinterpret_cast<const float4*>(&st[row][c0 + 4]);
           uint4 o;
-          o.x = f32_to_bf16(u.x) | (f32_to_bf16(u.y) << 16);
-          o.y = f32_to_bf16(u.z) | (f32_to_bf16(u.w) << 16);
-          o.z = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
-          o.w = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
-          if (row0 + row < p.I)
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + (row0 + row) * ld + n0 + c0) = o;
+          o.x = pk_bf16(u.x, u.y);
+          o.y = pk_bf16(u.z, u.w);
+          o.z = pk_bf16(v.x, v.y);
+          o.w = pk_bf16(v.z, v.w);
+          if (row < rows_here) *reinterpret_cast<uint4*>(dst) = o;
         }
       } else {
         float* base = to_partial ? p.partial + (int64_t)z * p.I * p.J : reinterpret_cast<float*>(p.C);
         const bool add = !to_partial && p.accumulate;
         // lane: 4 columns of one of two rows per pass
+        const int rl = lane >> 5, c0 = (lane & 31) * 4;
+        float* dst0 = base + (row0 + rl) * ld + n0 + c0;
+        const int64_t step = 2 * ld;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 2 * r + (lane >> 5), c0 = (lane & 31) * 4;
+        for (int r = 0; r < 16; ++r, dst0 += step) {
+          const int row = 2 * r + rl;
           float4 v = *reinterpret_cast<const float4*>(&st[row][c0]);
-          if (row0 + row < p.I) {
-            float4* dst = reinterpret_cast<float4*>(base + (row0 + row) * ld + n0 + c0);
+          if (row < rows_here) {
+            float4* dst = reinterpret_cast<float4*>(dst0);
             if (add) {
               const float4 o = *dst;
               v.x = o.x + v.x;

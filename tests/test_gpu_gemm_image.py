@@ -248,3 +248,21 @@ def test_backward_images_from_the_column_quantization():
     gpu = dict(saved=saved, ops=ops, Y=Y, dX=dX, dW=dW, Y32=Y32, dX32=dX32)
     err = check_linear_sampled(H.bf16_values(xb), W, H.bf16_values(dyb), plan_idx, 3, 16, gpu, rng, tag="image")
     print(f"[image] rel_fro dX {err['dX']:.2e} dW {err['dW']:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("I,J,K,img", [(4096, 1024, 1024, True), (2048, 1024, 1024, True), (2100, 300, 880, True),
+                                       (1024, 640, 512, False), (1024, 1024, 16384, False)])
+def test_bf16_output_is_rne_of_fp32_output(I, J, K, img):
+    """A product's bf16 output is its fp32 output rounded to nearest even, bit for bit: the staged
+    16-byte stores convert pairs with the hardware conversion, the ragged-tile element stores and
+    the split-K reduction in software, and all of them must agree with torch's host rounding.
+    Image products without and with a K split (the first two shapes), full and ragged tiles, a
+    direct product, and a direct product split eight ways."""
+    print(f"[image] bf16 rounding {I}x{J}x{K} image={img}", flush=True)
+    ga, gb, _, _ = _ops(I, J, K, seed=3 * I + J)
+    ws = _image_workspace(I, J, K) if img else tj2.gemm_workspace(I, J, K)
+    c32 = tj2.gemm(ga, gb, workspace=ws)
+    c16 = tj2.gemm(ga, gb, out_dtype=torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    want = c32.cpu().to(torch.bfloat16)
+    assert torch.equal(c16.cpu().view(torch.int16), want.view(torch.int16))
