@@ -119,16 +119,22 @@ __device__ __forceinline__ void quantize_group(const float v[16], float a_o, flo
   }
 }
 
-// Codes and scales of one 16-element group of row `row` (group j of the row).
+// a * b for 0 <= a, b < 2^32: one 32 x 32 -> 64-bit multiply (a 64 x 64-bit
+// product costs three quarter-rate instructions)
+__device__ __forceinline__ uint64_t mul32(int64_t a, int64_t b) { return (uint64_t)(uint32_t)a * (uint32_t)b; }
+
+// Codes and scales of one 16-element group of row `row` (group j of the row);
+// the entry points bound rows, lengths and strides by 2^30.
 template <int OF>
 __device__ __forceinline__ void store_group(const QView& o, int64_t row, int64_t j, const uint32_t codes[4],
                                             uint32_t s_code) {
   if constexpr (OF == TJ2_NVFP4) {
-    *reinterpret_cast<uint2*>(o.codes + row * o.ld_codes + j * 8) = make_uint2(codes[0], codes[1]);
+    *reinterpret_cast<uint2*>(o.codes + mul32(row, o.ld_codes) + j * 8) = make_uint2(codes[0], codes[1]);
   } else {
-    *reinterpret_cast<uint4*>(o.codes + row * o.ld_codes + j * 16) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+    *reinterpret_cast<uint4*>(o.codes + mul32(row, o.ld_codes) + j * 16) =
+        make_uint4(codes[0], codes[1], codes[2], codes[3]);
   }
-  if constexpr (OF != TJ2_FP8) o.s16[row * o.ld_s16 + j] = (uint8_t)s_code;
+  if constexpr (OF != TJ2_FP8) o.s16[mul32(row, o.ld_s16) + j] = (uint8_t)s_code;
 }
 
 // ----------------------------------------------------------------------------
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const typename Dense<IN>
 
   float v[16];
   if (valid) {
-    const typename Dense<IN>::T* xr = x + (int64_t)row * ld_x;
+    const typename Dense<IN>::T* xr = x + mul32(row, ld_x);
     if (GATHER) {
       const int4* ip = reinterpret_cast<const int4*>(idx + j * 16u);
 #pragma unroll
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const typename Dense<IN>
   // rounds to zero, and no branch keeps the draws' registers apart
   uint32_t u[16];
   if (SR) {
-    const uint64_t e0 = (uint64_t)row * (uint64_t)L + j * 16u;
+    const uint64_t e0 = mul32(row, L) + j * 16u;
     draws8(e0 >> 3, seed, offset, u);
     draws8((e0 >> 3) + 1, seed, offset, u + 8);
   }
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const typename Dense<IN>
   float S;
   quantize_group<OF, SR>(v, a_o, a_j, u, codes, &s_code, &S);
   store_group<OF>(out, row, j, codes, s_code);
-  if ((j & 7u) == 0u) out.s128[(int64_t)row * out.ld_s128 + (j >> 3)] = S;
+  if ((j & 7u) == 0u) out.s128[mul32(row, out.ld_s128) + (j >> 3)] = S;
 }
 
 // ----------------------------------------------------------------------------
@@ -211,7 +217,7 @@ struct ColTile<TJ2_BF16> {
       const int idx = threadIdx.x + 256 * i, row = idx >> 3, seg = idx & 7;
       const int64_t r = rb + row, c = c_tile + seg * 8;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < p.rows && c < p.cols) v = *reinterpret_cast<const uint4*>(x + r * p.ld_x + c);
+      if (r < p.rows && c < p.cols) v = *reinterpret_cast<const uint4*>(x + mul32(r, p.ld_x) + c);
       uint32_t* d = w + row * kRowWords + seg * 4;
       d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
@@ -234,7 +240,7 @@ struct ColTile<TJ2_F32> {
       const int idx = threadIdx.x + 256 * i, row = idx >> 4, seg = idx & 15;
       const int64_t r = rb + row, c = c_tile + seg * 4;
       float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (r < p.rows && c < p.cols) v = *reinterpret_cast<const float4*>(x + r * p.ld_x + c);
+      if (r < p.rows && c < p.cols) v = *reinterpret_cast<const float4*>(x + mul32(r, p.ld_x) + c);
       float* d = w + row * kRowWords + seg * 4;
       d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
@@ -258,14 +264,14 @@ struct ColTile<TJ2_NVFP4> {
     const int64_t r = rb + row;
     const bool in = r < p.rows;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (in) v = *reinterpret_cast<const uint4*>(q.codes + r * q.ld_codes + (c0 >> 1) + half * 16);
+    if (in) v = *reinterpret_cast<const uint4*>(q.codes + mul32(r, q.ld_codes) + (c0 >> 1) + half * 16);
     uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * kRowBytes + half * 16);
     dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
     if (half == 0) {
-      const uint32_t w = in ? *reinterpret_cast<const uint32_t*>(q.s16 + r * q.ld_s16 + (c0 >> 4)) : 0u;
+      const uint32_t w = in ? *reinterpret_cast<const uint32_t*>(q.s16 + mul32(r, q.ld_s16) + (c0 >> 4)) : 0u;
       *reinterpret_cast<uint32_t*>(s16 + row * 4) = w;
     } else {
-      S[row] = in ? q.s128[r * q.ld_s128 + (c0 >> 7)] : 0.0f;
+      S[row] = in ? q.s128[mul32(r, q.ld_s128) + (c0 >> 7)] : 0.0f;
     }
   }
   // values of tile row `row`, tile columns col, col + 1 (col even): (q * s) * S in fp32,
@@ -293,14 +299,14 @@ struct ColTile<TJ2_FP8> {
     const bool in = r < p.rows;
     uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
     if (in) {
-      const uint4* src = reinterpret_cast<const uint4*>(q.codes + r * q.ld_codes + c0 + half * 32);
+      const uint4* src = reinterpret_cast<const uint4*>(q.codes + mul32(r, q.ld_codes) + c0 + half * 32);
       v0 = src[0];
       v1 = src[1];
     }
     uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * kRowBytes + half * 32);
     dst[0] = v0.x; dst[1] = v0.y; dst[2] = v0.z; dst[3] = v0.w;
     dst[4] = v1.x; dst[5] = v1.y; dst[6] = v1.z; dst[7] = v1.w;
-    if (half == 0) S[row] = in ? q.s128[r * q.ld_s128 + (c0 >> 7)] : 0.0f;
+    if (half == 0) S[row] = in ? q.s128[mul32(r, q.ld_s128) + (c0 >> 7)] : 0.0f;
   }
   __device__ __forceinline__ void get2(int row, int col, float& v0, float& v1) const {
     typedef float float2_t __attribute__((ext_vector_type(2)));
@@ -321,8 +327,7 @@ template <int OF>
 __device__ __forceinline__ void write_image_group(uint8_t* img, float* img_sc, int64_t img_ld, int64_t img_nch,
                                                   int64_t d, uint32_t g, int rs, const uint32_t codes[4],
                                                   uint32_t s_code, float S) {
-  uint8_t* dst = img + ((size_t)(d >> 7) * (size_t)img_nch + g) * kImgChunkBytes + (size_t)(d & 127) * kImgRowBytes +
-                 rs * 32;
+  uint8_t* dst = img + (mul32(d >> 7, img_nch) + g) * kImgChunkBytes + (size_t)(d & 127) * kImgRowBytes + rs * 32;
   uint32_t h[8];
   if constexpr (OF == TJ2_NVFP4) {
     const half2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s_code, 1.0f, false);
@@ -340,7 +345,7 @@ __device__ __forceinline__ void write_image_group(uint8_t* img, float* img_sc, i
   }
   *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
   *reinterpret_cast<uint4*>(dst + 16) = make_uint4(h[4], h[5], h[6], h[7]);
-  if (rs == 0) img_sc[(size_t)g * (size_t)img_ld + (size_t)d] = S;
+  if (rs == 0) img_sc[mul32(g, img_ld) + (size_t)d] = S;
 }
 
 template <int OF>
@@ -390,7 +395,7 @@ __device__ __forceinline__ void col_tile(const QuantParams& p, uint32_t bid, Col
     const int64_t orow = c0 + k;  // output row = input column
     uint32_t u[16];
     if (SR) {  // groups past the last row are zeros: any draw keeps them zero
-      const uint64_t b = ((uint64_t)orow * (uint64_t)R + (uint64_t)r0) >> 3;
+      const uint64_t b = (mul32(orow, R) + (uint64_t)r0) >> 3;
       draws8(b, p.seed, p.offset, u);
       draws8(b + 1, p.seed, p.offset, u + 8);
     }
@@ -399,7 +404,7 @@ __device__ __forceinline__ void col_tile(const QuantParams& p, uint32_t bid, Col
     quantize_group<OF, SR>(v, a_o, a_j, u, codes, &s_code, &S);
     // groups past the last row are the zero padding of the output's last block
     store_group<OF>(o, orow, r0 >> 4, codes, s_code);
-    if (rs == 0) o.s128[orow * o.ld_s128 + rbi] = S;
+    if (rs == 0) o.s128[mul32(orow, o.ld_s128) + rbi] = S;
     if constexpr (OF == TJ2_NVFP4 || OF == TJ2_FP8) {
       if (p.img) store_image_group<OF>(p, orow, rbi, rs, codes, s_code, S);
     }
@@ -519,12 +524,14 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
   {
     // 128 rows x 16 pieces of 16 bytes, all of a lane's in flight before the LDS writes
     uint4 t[2048 / kT];
+    const int64_t r0 = rb + (threadIdx.x >> 4), c = cb + (threadIdx.x & 15) * 8;
+    const uint16_t* x0 = p.x + mul32(r0, p.cols) + c;
 #pragma unroll
     for (int i = 0; i < 2048 / kT; ++i) {
-      const int idx = (int)threadIdx.x + kT * i, row = idx >> 4, seg = idx & 15;
-      const int64_t r = rb + row, c = cb + seg * 8;
-      t[i] = (r < p.rows && c < p.cols) ? *reinterpret_cast<const uint4*>(p.x + r * p.cols + c)
-                                          : make_uint4(0u, 0u, 0u, 0u);
+      // pass i: rows r0 + (kT / 16) i
+      t[i] = (r0 + (kT / 16) * i < p.rows && c < p.cols)
+                 ? *reinterpret_cast<const uint4*>(x0 + (int64_t)(kT / 16) * i * p.cols)
+                 : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int i = 0; i < 2048 / kT; ++i) {
@@ -556,14 +563,14 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
       for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
       const float a_o = max8_lanes(a_j);
       uint32_t u[16];
-      const uint64_t e0 = (uint64_t)R * (uint64_t)p.cols + (uint64_t)(cb + j * 16);
+      const uint64_t e0 = mul32(R, p.cols) + (uint64_t)(cb + j * 16);
       draws8(e0 >> 3, p.seed, p.row_offset, u);
       draws8((e0 >> 3) + 1, p.seed, p.row_offset, u + 8);
       uint32_t codes[4], s_code;
       float S;
       quantize_group<OF, true>(v, a_o, a_j, u, codes, &s_code, &S);
       store_group<OF>(p.row_out, R, (cb >> 4) + j, codes, s_code);
-      if (j == 0) p.row_out.s128[R * p.row_out.ld_s128 + (cb >> 7)] = S;
+      if (j == 0) p.row_out.s128[mul32(R, p.row_out.ld_s128) + (cb >> 7)] = S;
     }
   }
 
@@ -595,7 +602,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
       const float a_o = max8_lanes(a_j);
       const int64_t orow = c0 + k;  // output row = input column
       uint32_t u[16];
-      const uint64_t b = ((uint64_t)orow * (uint64_t)p.rows + (uint64_t)r0) >> 3;
+      const uint64_t b = (mul32(orow, p.rows) + (uint64_t)r0) >> 3;
       draws8(b, p.seed, p.col_offset, u);
       draws8(b + 1, p.seed, p.col_offset, u + 8);
       uint32_t codes[4], s_code;
@@ -603,7 +610,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
       quantize_group<OF, true>(v, a_o, a_j, u, codes, &s_code, &S);
       // groups past the last row are the zero padding of the output's last block
       store_group<OF>(p.col_out, orow, r0 >> 4, codes, s_code);
-      if (rs == 0) p.col_out.s128[orow * p.col_out.ld_s128 + (rb >> 7)] = S;
+      if (rs == 0) p.col_out.s128[mul32(orow, p.col_out.ld_s128) + (rb >> 7)] = S;
     });
   }
 }
@@ -643,7 +650,7 @@ __device__ __forceinline__ void split_body(const SplitParams& p, int R, uint32_t
   {
     // the rows are contiguous and hold at most 32 KB: eight 16-byte loads per
     // lane, all in flight before the LDS writes
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(p.x) + r_base * p.cols);
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(p.x) + mul32(r_base, p.cols));
     uint4* dst = reinterpret_cast<uint4*>(rows_lds);
     const int n = nrows * units;
     uint4 t[8];
@@ -674,7 +681,7 @@ __device__ __forceinline__ void split_body(const SplitParams& p, int R, uint32_t
     float v[16];
     if (valid) {
       const int4* ip = reinterpret_cast<const int4*>(idx + jj * 16);
-      const T* xr = xs + (int64_t)row * p.cols;
+      const T* xr = xs + mul32(row, p.cols);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int4 c = ip[q];
@@ -697,18 +704,18 @@ __device__ __forceinline__ void split_body(const SplitParams& p, int R, uint32_t
     if (!fp8) {
       quantize_group<TJ2_NVFP4, false>(v, a_o, a_j, nullptr, codes, &s_code, &S);
       const QView& o = p.q4;
-      *reinterpret_cast<uint2*>(o.codes + orow * o.ld_codes + jj * 8) = make_uint2(codes[0], codes[1]);
-      o.s16[orow * o.ld_s16 + jj] = (uint8_t)s_code;
-      if ((jj & 7) == 0) o.s128[orow * o.ld_s128 + (jj >> 3)] = S;
+      *reinterpret_cast<uint2*>(o.codes + mul32(orow, o.ld_codes) + jj * 8) = make_uint2(codes[0], codes[1]);
+      o.s16[mul32(orow, o.ld_s16) + jj] = (uint8_t)s_code;
+      if ((jj & 7) == 0) o.s128[mul32(orow, o.ld_s128) + (jj >> 3)] = S;
       if (p.img)
         write_image_group<TJ2_NVFP4>(p.img, p.img_sc, p.img_ld, p.img_nch, orow, (uint32_t)(jj >> 3), jj & 7, codes,
                                      s_code, S);
     } else {
       quantize_group<TJ2_FP8, false>(v, a_o, a_j, nullptr, codes, &s_code, &S);
       const QView& o = p.q8;
-      *reinterpret_cast<uint4*>(o.codes + orow * o.ld_codes + jj * 16) =
+      *reinterpret_cast<uint4*>(o.codes + mul32(orow, o.ld_codes) + jj * 16) =
           make_uint4(codes[0], codes[1], codes[2], codes[3]);
-      if ((jj & 7) == 0) o.s128[orow * o.ld_s128 + (jj >> 3)] = S;
+      if ((jj & 7) == 0) o.s128[mul32(orow, o.ld_s128) + (jj >> 3)] = S;
       if (p.img)
         write_image_group<TJ2_FP8>(p.img, p.img_sc, p.img_ld, p.img_nch, orow, (uint32_t)(p.img_g8 + (jj >> 3)),
                                    jj & 7, codes, s_code, S);
