@@ -1315,7 +1315,7 @@ __global__ __launch_bounds__(256) void bimage_kernel(ImgArgs p) {
     const int32_t at = *ip;
     dest[k] = plan && real ? (int64_t)at : v;
     const bool fp8 = is8 || b_fp8;
-    const size_t rn = (size_t)(is8 ? r8 * p.b8.ld_s128 : r4 * bop.ld_s128);
+    const size_t rn = is8 ? mul32(r8, p.b8.ld_s128) : mul32(r4, bop.ld_s128);
     const uint8_t* c4 = bop.codes + (size_t)g * 64 + rn * 64 + u * 4;    // NVFP4 codes
     const uint8_t* c8 = (is8 ? p.b8.codes : bop.codes) + (size_t)g * 128 + rn * 128 + u * 8;  // FP8 codes
     const uint8_t* cw = fp8 ? c8 : c4;
@@ -1333,10 +1333,10 @@ __global__ __launch_bounds__(256) void bimage_kernel(ImgArgs p) {
   for (int k = 0; k < 4; ++k) {
     const int64_t d = dest[k];
     if (d < 0 || d >= p.Jpad) continue;  // past the padded rows (or a plan entry out of range)
-    uint8_t* dst = p.img + ((size_t)(d / BN) * (size_t)p.nchunks + (size_t)gi) * kImgChunkBytes +
-                   (size_t)(d % BN) * (LDS_STRIDE * 2);
+    uint8_t* dst = p.img + (mul32((uint64_t)d / BN, p.nchunks) + (size_t)gi) * kImgChunkBytes +
+                   ((uint64_t)d % BN) * (LDS_STRIDE * 2);
     *reinterpret_cast<half8_t*>(dst + u * 16) = f[k];
-    if (u == 0) p.bsc[(size_t)gi * (size_t)p.bsc_ld + (size_t)d] = S[k];
+    if (u == 0) p.bsc[mul32(gi, p.bsc_ld) + (size_t)d] = S[k];
   }
 }
 
@@ -1383,12 +1383,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // (taken in split order, as above), and the 4 results leave in one store.
 template <int S>
 __global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __restrict__ partial, int64_t I, int64_t J,
-                                                             void* C, int64_t ldc, int c_bf16, int accumulate) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t jq = J / 4;
-  const int64_t i = q / jq;
-  if (i >= I) return;
-  const int64_t j0 = (q - i * jq) * 4;
+                                                             void* C, int64_t ldc, int c_bf16, int accumulate,
+                                                             uint32_t bpr) {
+  // bpr workgroups per output row: the row and column come from the workgroup
+  // id (one uniform division) instead of a 64-bit division per lane
+  const uint32_t i32 = blockIdx.x / bpr;
+  const int64_t i = i32;
+  const int64_t j0 = ((int64_t)(blockIdx.x - i32 * bpr) * 256 + threadIdx.x) * 4;
+  if (j0 >= J) return;
   const int64_t stride = I * J;
   const float* p = partial + i * J + j0;
   float4 v[S];
@@ -1400,8 +1402,7 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __rest
     s0 += v[z].x; s1 += v[z].y; s2 += v[z].z; s3 += v[z].w;
   }
   if (c_bf16) {
-    const uint32_t lo = f32_to_bf16(s0) | (f32_to_bf16(s1) << 16), hi = f32_to_bf16(s2) | (f32_to_bf16(s3) << 16);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + i * ldc + j0) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + i * ldc + j0) = make_uint2(pk_bf16(s0, s1), pk_bf16(s2, s3));
   } else {
     float4* cp = reinterpret_cast<float4*>(reinterpret_cast<float*>(C) + i * ldc + j0);
     if (accumulate) {
@@ -1596,14 +1597,16 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   const int64_t threads = p.I * ((p.J + 3) / 4);
   const dim3 rgrid((uint32_t)((threads + 255) / 256));
   const int bf = p.c_dtype == TJ2_BF16 ? 1 : 0;
+  const int64_t bpr = (p.J / 4 + 255) / 256;  // vector path: workgroups per output row
   const bool vec = !p.col_map && (p.J & 3) == 0 && (p.ldc & 3) == 0 &&
-                   (reinterpret_cast<uintptr_t>(p.C) & (bf ? 7 : 15)) == 0;
+                   (reinterpret_cast<uintptr_t>(p.C) & (bf ? 7 : 15)) == 0 && p.I * bpr < ((int64_t)1 << 31);
+  const dim3 vgrid((uint32_t)(p.I * bpr));
   if (vec && split == 2)
-    hipLaunchKernelGGL(splitk_reduce4_kernel<2>, rgrid, dim3(256), 0, s, p.partial, p.I, p.J, p.C, p.ldc, bf,
-                       p.accumulate);
+    hipLaunchKernelGGL(splitk_reduce4_kernel<2>, vgrid, dim3(256), 0, s, p.partial, p.I, p.J, p.C, p.ldc, bf,
+                       p.accumulate, (uint32_t)bpr);
   else if (vec && split == 8)
-    hipLaunchKernelGGL(splitk_reduce4_kernel<8>, rgrid, dim3(256), 0, s, p.partial, p.I, p.J, p.C, p.ldc, bf,
-                       p.accumulate);
+    hipLaunchKernelGGL(splitk_reduce4_kernel<8>, vgrid, dim3(256), 0, s, p.partial, p.I, p.J, p.C, p.ldc, bf,
+                       p.accumulate, (uint32_t)bpr);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel, rgrid, dim3(256), 0, s, p.partial, split, p.I, p.J, p.C, p.ldc,
                        p.col_map, bf, p.accumulate);

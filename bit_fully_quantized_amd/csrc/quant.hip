@@ -119,10 +119,6 @@ __device__ __forceinline__ void quantize_group(const float v[16], float a_o, flo
   }
 }
 
-// a * b for 0 <= a, b < 2^32: one 32 x 32 -> 64-bit multiply (a 64 x 64-bit
-// product costs three quarter-rate instructions)
-__device__ __forceinline__ uint64_t mul32(int64_t a, int64_t b) { return (uint64_t)(uint32_t)a * (uint32_t)b; }
-
 // Codes and scales of one 16-element group of row `row` (group j of the row);
 // the entry points bound rows, lengths and strides by 2^30.
 template <int OF>

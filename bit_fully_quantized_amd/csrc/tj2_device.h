@@ -37,6 +37,10 @@ constexpr float kFp8Div = 448.0f;      // outer max -> E4M3 max
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
+// a * b for 0 <= a, b < 2^32: one 32 x 32 -> 64-bit multiply (a 64 x 64-bit
+// product costs three quarter-rate instructions)
+__device__ __forceinline__ uint64_t mul32(int64_t a, int64_t b) { return (uint64_t)(uint32_t)a * (uint32_t)b; }
+
 // Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   uint32_t b = __float_as_uint(f);
