@@ -547,13 +547,25 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
       const bool valid = cb + j * 16 < p.cols;
       float v[16];
       const uint32_t* w = tile + row * kW + j * 8;
+      if (RHT && valid) {
+        // bf16 -> fp32 with the transform's sign in one instruction per element
+        // (a shift-add, where adding 2^31 flips bit 31 only, or an and-xor), then
+        // the butterflies
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t b = valid ? w[i] : 0u;
-        v[2 * i] = __uint_as_float(b << 16);
-        v[2 * i + 1] = __uint_as_float(b & 0xFFFF0000u);
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t b = w[i];
+          v[2 * i] = __uint_as_float((b << 16) + rht_sign(p.row_mask, 2 * i));
+          v[2 * i + 1] = __uint_as_float((b & 0xFFFF0000u) ^ rht_sign(p.row_mask, 2 * i + 1));
+        }
+        hadamard16(v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t b = valid ? w[i] : 0u;
+          v[2 * i] = __uint_as_float(b << 16);
+          v[2 * i + 1] = __uint_as_float(b & 0xFFFF0000u);
+        }
       }
-      if (RHT && valid) rht16(v, p.row_mask);
       float a_j = 0.0f;
 #pragma unroll
       for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
@@ -582,16 +594,26 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
     const int64_t r0 = rb + rs * 16;
     const bool valid = r0 < p.rows;
     float vv[2][16];
+    if (RHT && valid) {
+      // as the row groups: the sign of row t in the bf16 -> fp32 step
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint32_t b = tile[(rs * 16 + t) * kW + (cl >> 1)];
-      vv[0][t] = __uint_as_float(b << 16);
-      vv[1][t] = __uint_as_float(b & 0xFFFF0000u);
+      for (int t = 0; t < 16; ++t) {
+        const uint32_t b = tile[(rs * 16 + t) * kW + (cl >> 1)];
+        vv[0][t] = __uint_as_float((b << 16) + rht_sign(p.col_mask, t));
+        vv[1][t] = __uint_as_float((b & 0xFFFF0000u) ^ rht_sign(p.col_mask, t));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const uint32_t b = tile[(rs * 16 + t) * kW + (cl >> 1)];
+        vv[0][t] = __uint_as_float(b << 16);
+        vv[1][t] = __uint_as_float(b & 0xFFFF0000u);
+      }
     }
     static_for<2>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       float* v = vv[k];
-      if (RHT && valid) rht16(v, p.col_mask);
+      if (RHT && valid) hadamard16(v);
       float a_j = 0.0f;
 #pragma unroll
       for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));

@@ -220,14 +220,13 @@ __device__ __forceinline__ void draws8(uint64_t b, uint64_t seed, uint64_t offse
   r[6] = w.w << 16; r[7] = w.w & 0xFFFF0000u;
 }
 
-// ---------------------------------------------------------------------------
-// 16-wide random Hadamard transform, in registers: negate positions whose bit
-// is set in `mask`, butterflies h = 1, 2, 4, 8 pairing (i, i+h) -> (a+b, a-b),
-// then * 0.25 (TetraJet-v2 technical summary, section 2.C).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void rht16(float v[16], uint32_t mask) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((mask >> j) & 1u) << 31));
+// The random Hadamard transform's sign on position j (bit 31 when bit j of
+// `mask` is set).
+__device__ __forceinline__ uint32_t rht_sign(uint32_t mask, int j) { return ((mask >> j) & 1u) << 31; }
+
+// Butterflies h = 1, 2, 4, 8 pairing (i, i+h) -> (a+b, a-b), then * 0.25: the
+// transform after its signs.
+__device__ __forceinline__ void hadamard16(float v[16]) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -240,6 +239,17 @@ __device__ __forceinline__ void rht16(float v[16], uint32_t mask) {
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
+}
+
+// ---------------------------------------------------------------------------
+// 16-wide random Hadamard transform, in registers: negate positions whose bit
+// is set in `mask`, butterflies h = 1, 2, 4, 8 pairing (i, i+h) -> (a+b, a-b),
+// then * 0.25 (TetraJet-v2 technical summary, section 2.C).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rht16(float v[16], uint32_t mask) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ rht_sign(mask, j));
+  hadamard16(v);
 }
 
 // ---------------------------------------------------------------------------
