@@ -287,7 +287,9 @@ __device__ __forceinline__ GroupScale double_block_scale(float a_o, float a_j) {
   uint32_t code;
   float s = e4m3_round_up(r, &code);
   float d = s * g.S;
-  g.inv = 1.0f / d;
+  // r below the fp32 range (a group under 2^-149 of its block's scale) gives
+  // s = 0: the group then encodes signed zeros, as its scale decodes it
+  g.inv = d > 0.0f ? 1.0f / d : 0.0f;
   g.s_code = code;
   return g;
 }

@@ -57,3 +57,23 @@ def test_quantize_dual_equals_two_passes_at_size():
         assert torch.equal(a.codes, b.codes), what
         assert torch.equal(a.scale16, b.scale16), what
         assert torch.equal(a.scale128, b.scale128), what
+
+
+def test_quantize_dual_extreme_magnitudes():
+    """Outer blocks near the top of the fp32 range (group sums up to about 1.6e38, the largest the
+    transform keeps finite) and of bf16 subnormals next to ordinary ones: the fused pass, which
+    takes the transform's 1/4 into the group's reciprocal, equals the oracle bit for bit."""
+    M, N = 256, 384
+    x = H.bf16_values(synthetic.normal_bf16((M, N), 1.0, 91))
+    x[:16] *= np.float32(2.5e36)
+    x[16:32] *= np.float32(1e-39)
+    x[:, 128:144] *= np.float32(1e-39)
+    bits = synthetic.f32_to_bf16_bits(x)
+    x = H.bf16_values(bits)
+    assert np.isfinite(x).all() and np.abs(x).max() > 1e36 and (np.abs(x[16:32]) < 1.2e-38).all()
+    seed, ro, co = 3, 6, 8
+    rq, cq = tj2.quantize_dual(H.bf16_to_device(bits), rht=True, seed=seed, row_offset=ro, col_offset=co)
+    ref_r = quant.quantize(x, grouping="row", rounding="sr", rht_mask=philox.rht_signs(seed, ro), seed=seed, offset=ro)
+    ref_c = quant.quantize(x, grouping="col", rounding="sr", rht_mask=philox.rht_signs(seed, co), seed=seed, offset=co)
+    H.assert_q_equal(rq, ref_r, what="dual row, extreme magnitudes")
+    H.assert_q_equal(cq, ref_c, what="dual col, extreme magnitudes")
