@@ -68,18 +68,48 @@ struct Dense<TJ2_F32> {
   static __device__ __forceinline__ float load1(const T* p) { return *p; }
 };
 
+// Butterflies h = 1, 2, 4, 8 of the 16-wide Hadamard transform without its
+// final 1/4 (the quantize_group X4 form).
+__device__ __forceinline__ void butterflies16(float v[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Per-group quantization of 16 values v (already transformed if RHT), given
 // the outer amax a_o and, for SR, the draws r (top-aligned 16-bit).  Writes 8
 // bytes (NVFP4) or 16 bytes (FP8, NVFP6) of codes.
+//
+// X4 (NVFP4 / NVFP6 only): v holds four times the values, the Hadamard
+// butterflies of bf16 input without the transform's final 1/4 (a_o and a_j
+// are those of the values).  Such sums are multiples of 2^-133, so v / 4 is
+// exact and y = (v / 4) * inv is the one rounding of v * inv / 4, which
+// v * (inv / 4) also is when inv / 4 is exact (inv >= 2^-124 or 0); otherwise
+// (outer amax above about 1e38) v is scaled first.
 // ----------------------------------------------------------------------------
-template <int OF, bool SR>
-__device__ __forceinline__ void quantize_group(const float v[16], float a_o, float a_j, const uint32_t r[16],
+template <int OF, bool SR, bool X4 = false>
+__device__ __forceinline__ void quantize_group(float v[16], float a_o, float a_j, const uint32_t r[16],
                                                uint32_t codes[4], uint32_t* s_code, float* S_out) {
   if constexpr (OF == TJ2_NVFP4 || OF == TJ2_NVFP6) {
     GroupScale g = OF == TJ2_NVFP4 ? nvfp4_group_scale(a_o, a_j) : nvfp6_group_scale(a_o, a_j);
     *s_code = g.s_code;
     *S_out = g.S;
+    if constexpr (X4) {
+      if (g.inv >= 0x1p-124f || g.inv == 0.0f) {
+        g.inv *= 0.25f;
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) v[t] *= 0.25f;
+      }
+    }
     float y[16];
     if constexpr (OF == TJ2_NVFP4) {
       // both conversions saturate at +-6 and y * 0 keeps the sign of y, so an
@@ -557,7 +587,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
           v[2 * i] = __uint_as_float((b << 16) + rht_sign(p.row_mask, 2 * i));
           v[2 * i + 1] = __uint_as_float((b & 0xFFFF0000u) ^ rht_sign(p.row_mask, 2 * i + 1));
         }
-        hadamard16(v);
+        butterflies16(v);  // four times the transformed values (zeros stay zeros)
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -569,6 +599,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
       float a_j = 0.0f;
 #pragma unroll
       for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
+      if (RHT) a_j *= 0.25f;  // exact: the amax of the transformed values
       const float a_o = max8_lanes(a_j);
       uint32_t u[16];
       const uint64_t e0 = mul32(R, p.cols) + (uint64_t)(cb + j * 16);
@@ -576,7 +607,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
       draws8((e0 >> 3) + 1, p.seed, p.row_offset, u + 8);
       uint32_t codes[4], s_code;
       float S;
-      quantize_group<OF, true>(v, a_o, a_j, u, codes, &s_code, &S);
+      quantize_group<OF, true, RHT>(v, a_o, a_j, u, codes, &s_code, &S);
       store_group<OF>(p.row_out, R, (cb >> 4) + j, codes, s_code);
       if (j == 0) p.row_out.s128[mul32(R, p.row_out.ld_s128) + (cb >> 7)] = S;
     }
@@ -613,10 +644,11 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
     static_for<2>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       float* v = vv[k];
-      if (RHT && valid) hadamard16(v);
+      if (RHT && valid) butterflies16(v);  // four times the transformed values
       float a_j = 0.0f;
 #pragma unroll
       for (int t = 0; t < 16; ++t) a_j = fmaxf(a_j, fabsf(v[t]));
+      if (RHT) a_j *= 0.25f;
       const float a_o = max8_lanes(a_j);
       const int64_t orow = c0 + k;  // output row = input column
       uint32_t u[16];
@@ -625,7 +657,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(DualParams p) 
       draws8(b + 1, p.seed, p.col_offset, u + 8);
       uint32_t codes[4], s_code;
       float S;
-      quantize_group<OF, true>(v, a_o, a_j, u, codes, &s_code, &S);
+      quantize_group<OF, true, RHT>(v, a_o, a_j, u, codes, &s_code, &S);
       // groups past the last row are the zero padding of the output's last block
       store_group<OF>(p.col_out, orow, r0 >> 4, codes, s_code);
       if (rs == 0) p.col_out.s128[mul32(orow, p.col_out.ld_s128) + (rb >> 7)] = S;
