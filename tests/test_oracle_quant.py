@@ -154,3 +154,21 @@ def test_dequantize_f64_matches_f32_within_one_rounding():
     d32 = quant.dequantize(q).astype(np.float64)
     d64 = quant.dequantize_f64(q)
     assert np.all(np.abs(d32 - d64) <= np.abs(d64) * 2.0 ** -24)
+
+
+@pytest.mark.parametrize("rounding", ["rtn", "sr"])
+def test_group_below_block_scale_range_encodes_zeros(rounding):
+    """A group more than 2^149 below its outer block's scale (its amax / (6 S) underflows fp32):
+    inner scale 0, codes the elements' signed zeros, dequantized values 0; the rest of the block
+    is quantized as usual (the block maximum takes the largest inner scale)."""
+    y = np.zeros((1, 128), np.float32)
+    y[0, :16] = np.float32(3e37) * np.sign(np.arange(16) - 7.5).astype(np.float32)
+    tiny = np.array([1e-39, -2e-39, 3e-40, -0.0, 0.0, 5e-39] + [1e-39] * 10, np.float32)
+    y[0, 16:32] = tiny
+    q = quant.quantize(y, rounding=rounding, seed=1, offset=0)
+    assert (np.float32(1e-39) / (np.float32(6) * q.s128[0, 0])) == 0  # the ratio does underflow
+    assert q.s16[0, 1] == 0 and q.s16[0, 0] == 0x7E
+    c = codes_of(q)[0, 16:32]
+    np.testing.assert_array_equal(c, np.where(np.signbit(tiny), 8, 0))
+    d = quant.dequantize_f64(q)
+    assert np.all(d[0, 16:32] == 0) and np.all(np.abs(d[0, :16]) > 1e37)
