@@ -113,13 +113,22 @@ def osci_batch(tj2, lins):
     return _OSCI_BATCH[key][1]
 
 
+def under_profiler() -> bool:
+    """True inside rocprofv3 (its tool library is preloaded into this process and its children)."""
+    return "rocprof" in os.environ.get("LD_PRELOAD", "").lower() or any(k.startswith("ROCPROF") for k in os.environ)
+
+
 def gpu_state_under_load(run, seconds=1.5):
     """GPU clocks, socket power and temperatures (amd-smi, a child process) sampled while `run`
-    (untimed steps) keeps the GPU busy; None where amd-smi is missing or fails."""
+    (untimed steps) keeps the GPU busy; None where amd-smi is missing or fails.  Skipped under a
+    profiler: amd-smi is a Python script whose interpreter would start (by exec) inside a child
+    that the preloaded profiler library has already attached to the GPU."""
     import subprocess
     import threading
 
     import torch
+    if under_profiler():
+        return {"skipped": "under a profiler (amd-smi would start inside its preloaded GPU library)"}
     res = {}
 
     def sample():
